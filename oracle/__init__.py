@@ -1,0 +1,303 @@
+"""numpy front end of the CPU oracle (oracle/cskv_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: used by tests/, the smoke check and the bench's
+CPU-baseline leg.  The product package never imports this module.
+
+The C library does the arithmetic; this module only marshals numpy arrays
+and composes the per-layer CSA2 modes [P2 "CSA2：三种模式，40 层只存 4 份"]:
+  full    - append the new token to the shared cache, score every entry with
+            its own indexer query, keep the top-k, attend;
+  reindex - score the shared indexer keys with its own indexer query, keep
+            its own top-k, attend;
+  reuse   - attend with the index list of the most recent full/reindex layer.
+Every mode appends its own window row and uses its own query.
+  P2  "DeepSeek V1 到 V4.1-Flash，单 token 的 global KV 如何从 389,000 B 压缩到 890 B的？"
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+STATUS_OVERFLOW = 1
+STATUS_ODD_ENTRY_APPEND = 2
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        _lib = C.CDLL(_build.LIB)
+        _declare(_lib)
+    return _lib
+
+
+def _p(a, ctype):
+    return None if a is None else a.ctypes.data_as(C.POINTER(ctype))
+
+
+class _Cache(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("capacity", C.c_int32), ("dim", C.c_int32),
+                ("rope_dim", C.c_int32), ("k_group", C.c_int32), ("v_group", C.c_int32),
+                ("idx_dim", C.c_int32),
+                ("k_codes", C.POINTER(C.c_uint8)), ("k_scales", C.POINTER(C.c_float)),
+                ("v_codes", C.POINTER(C.c_uint8)), ("v_scales", C.POINTER(C.c_float)),
+                ("idx_keys", C.POINTER(C.c_uint16)), ("n_tokens", C.POINTER(C.c_int32)),
+                ("pending", C.POINTER(C.c_float)), ("status", C.POINTER(C.c_int32))]
+
+
+def _declare(L):
+    u64, i32, i64, f64 = C.c_uint64, C.c_int32, C.c_int64, C.c_double
+    P = C.POINTER
+    L.orc_kv_bytes.restype = u64
+    L.orc_kv_bytes.argtypes = [u64] * 5
+    L.orc_fp4_row_bytes.restype = f64
+    L.orc_fp4_row_bytes.argtypes = [C.c_int, C.c_int, f64]
+    L.orc_global_kv_per_token.restype = f64
+    L.orc_global_kv_per_token.argtypes = [C.c_int, P(C.c_int), f64, f64]
+    L.orc_e2m1_value.restype = f64
+    L.orc_e2m1_value.argtypes = [C.c_uint]
+    L.orc_e2m1_encode.restype = C.c_uint
+    L.orc_e2m1_encode.argtypes = [C.c_float]
+    L.orc_bf16_from_f32.restype = C.c_uint16
+    L.orc_bf16_from_f32.argtypes = [C.c_float]
+    L.orc_bf16_value.restype = f64
+    L.orc_bf16_value.argtypes = [C.c_uint16]
+    L.orc_compress_pair.restype = None
+    L.orc_compress_pair.argtypes = [P(C.c_float)] * 3 + [C.c_int, P(C.c_float)]
+    L.orc_quantize_row.restype = None
+    L.orc_quantize_row.argtypes = [P(C.c_float), C.c_int, C.c_int, P(C.c_uint8), P(C.c_float)]
+    L.orc_dequantize_row.restype = None
+    L.orc_dequantize_row.argtypes = [P(C.c_uint8), P(C.c_float), C.c_int, C.c_int, P(f64)]
+    L.orc_kv_append.restype = None
+    L.orc_kv_append.argtypes = [P(_Cache), P(C.c_float), P(i32), P(C.c_float), P(C.c_uint16)]
+    L.orc_swa_append.restype = None
+    L.orc_swa_append.argtypes = [P(C.c_uint16), C.c_int, C.c_int, C.c_int, P(C.c_float),
+                                 P(i32), P(i32)]
+    L.orc_indexer_scores.restype = None
+    L.orc_indexer_scores.argtypes = [P(C.c_uint16), i64, C.c_int, P(C.c_uint16), C.c_int,
+                                     P(C.c_float), P(f64)]
+    L.orc_topk.restype = None
+    L.orc_topk.argtypes = [P(f64), i64, C.c_int, P(i32)]
+    L.orc_indexer_topk.restype = None
+    L.orc_indexer_topk.argtypes = [P(_Cache), P(C.c_uint16), C.c_int, P(C.c_float), C.c_int,
+                                   P(i32)]
+    L.orc_sparse_attn.restype = None
+    L.orc_sparse_attn.argtypes = [P(_Cache), P(C.c_float), C.c_int, P(i32), C.c_int,
+                                  P(C.c_uint16), C.c_int, P(i32), f64, P(f64), P(f64)]
+
+
+# ------------------------------------------------------------------ scalars
+
+def kv_bytes(layers, tokens, heads, head_dim, elem_bytes) -> int:
+    return int(lib().orc_kv_bytes(layers, tokens, heads, head_dim, elem_bytes))
+
+
+def fp4_row_bytes(dims, group, scale_bytes) -> float:
+    return float(lib().orc_fp4_row_bytes(dims, group, scale_bytes))
+
+
+def global_kv_per_token(ratios, main_entry_bytes, idx_entry_bytes) -> float:
+    r = (C.c_int * len(ratios))(*ratios)
+    return float(lib().orc_global_kv_per_token(len(ratios), r, main_entry_bytes, idx_entry_bytes))
+
+
+def e2m1_value(code: int) -> float:
+    return float(lib().orc_e2m1_value(code))
+
+
+def e2m1_encode(v: float) -> int:
+    return int(lib().orc_e2m1_encode(v))
+
+
+def bf16_from_f32(x: float) -> int:
+    return int(lib().orc_bf16_from_f32(x))
+
+
+def bf16_value(h: int) -> float:
+    return float(lib().orc_bf16_value(h))
+
+
+# ------------------------------------------------------------------ arrays
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def compress_pair(W, x_even, x_odd) -> np.ndarray:
+    W, xe, xo = _f32(W), _f32(x_even), _f32(x_odd)
+    D = xe.shape[0]
+    assert W.shape == (D, 2 * D)
+    e = np.empty(D, np.float32)
+    lib().orc_compress_pair(_p(W, C.c_float), _p(xe, C.c_float), _p(xo, C.c_float), D,
+                            _p(e, C.c_float))
+    return e
+
+
+def quantize_row(x, group):
+    x = _f32(x)
+    n = x.shape[0]
+    packed = np.empty(n // 2, np.uint8)
+    scales = np.empty(n // group, np.float32)
+    lib().orc_quantize_row(_p(x, C.c_float), n, group, _p(packed, C.c_uint8),
+                           _p(scales, C.c_float))
+    return packed, scales
+
+
+def dequantize_row(packed, scales, n, group) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, np.uint8)
+    scales = _f32(scales)
+    out = np.empty(n, np.float64)
+    lib().orc_dequantize_row(_p(packed, C.c_uint8), _p(scales, C.c_float), n, group,
+                             _p(out, C.c_double))
+    return out
+
+
+def indexer_scores(keys, q, head_w=None) -> np.ndarray:
+    keys = np.ascontiguousarray(keys, np.uint16)
+    q = np.ascontiguousarray(q, np.uint16)
+    E, Di = keys.shape
+    H = q.shape[0]
+    hw = None if head_w is None else _f32(head_w)
+    out = np.empty(E, np.float64)
+    lib().orc_indexer_scores(_p(keys, C.c_uint16), E, Di, _p(q, C.c_uint16), H,
+                             _p(hw, C.c_float), _p(out, C.c_double))
+    return out
+
+
+def topk(scores, k) -> np.ndarray:
+    s = np.ascontiguousarray(scores, np.float64)
+    out = np.empty(k, np.int32)
+    lib().orc_topk(_p(s, C.c_double), s.shape[0], k, _p(out, C.c_int32))
+    return out
+
+
+# ------------------------------------------------------------------ cache
+
+@dataclass
+class Cache:
+    """Host mirror of the device cache planes."""
+    batch: int
+    capacity: int
+    dim: int
+    rope_dim: int
+    k_group: int
+    v_group: int
+    idx_dim: int
+    k_codes: np.ndarray
+    k_scales: np.ndarray
+    v_codes: Optional[np.ndarray]
+    v_scales: Optional[np.ndarray]
+    idx_keys: np.ndarray
+    n_tokens: np.ndarray
+    pending: np.ndarray
+    status: np.ndarray
+
+    @classmethod
+    def empty(cls, batch, capacity, dim=576, rope_dim=64, k_group=32, v_group=0, idx_dim=128):
+        Dv = dim - rope_dim
+        return cls(batch, capacity, dim, rope_dim, k_group, v_group, idx_dim,
+                   np.zeros((batch, capacity, dim // 2), np.uint8),
+                   np.zeros((batch, capacity, dim // k_group), np.float32),
+                   np.zeros((batch, capacity, Dv // 2), np.uint8) if v_group else None,
+                   np.zeros((batch, capacity, Dv // v_group), np.float32) if v_group else None,
+                   np.zeros((batch, capacity, idx_dim), np.uint16),
+                   np.zeros(batch, np.int32), np.zeros((batch, dim), np.float32),
+                   np.zeros(1, np.int32))
+
+    def _c(self) -> _Cache:
+        return _Cache(self.batch, self.capacity, self.dim, self.rope_dim, self.k_group,
+                      self.v_group, self.idx_dim,
+                      _p(self.k_codes, C.c_uint8), _p(self.k_scales, C.c_float),
+                      _p(self.v_codes, C.c_uint8), _p(self.v_scales, C.c_float),
+                      _p(self.idx_keys, C.c_uint16), _p(self.n_tokens, C.c_int32),
+                      _p(self.pending, C.c_float), _p(self.status, C.c_int32))
+
+    def entries(self) -> np.ndarray:
+        return np.clip(self.n_tokens // 2, 0, self.capacity)
+
+
+def kv_append(cache: Cache, tokens, cu_new, w_comp, idx_rows) -> None:
+    tokens = _f32(tokens).reshape(-1, cache.dim)
+    cu = np.ascontiguousarray(cu_new, np.int32)
+    assert cu.shape == (cache.batch + 1,)
+    irows = np.ascontiguousarray(idx_rows, np.uint16).reshape(-1, cache.idx_dim)
+    W = None if w_comp is None else _f32(w_comp)
+    c = cache._c()
+    lib().orc_kv_append(C.byref(c), _p(tokens, C.c_float), _p(cu, C.c_int32),
+                        _p(W, C.c_float), _p(irows, C.c_uint16))
+
+
+def swa_append(ring, rows, cu_new, end_pos) -> None:
+    """ring: bf16 bits [B, W, dim] updated in place."""
+    assert ring.dtype == np.uint16 and ring.flags.c_contiguous
+    B, W, D = ring.shape
+    rows = _f32(rows).reshape(-1, D)
+    cu = np.ascontiguousarray(cu_new, np.int32)
+    ep = np.ascontiguousarray(end_pos, np.int32)
+    lib().orc_swa_append(_p(ring, C.c_uint16), B, W, D, _p(rows, C.c_float), _p(cu, C.c_int32),
+                         _p(ep, C.c_int32))
+
+
+def indexer_topk(cache: Cache, q_idx, k, head_w=None) -> np.ndarray:
+    q = np.ascontiguousarray(q_idx, np.uint16)
+    H = q.shape[1]
+    hw = None if head_w is None else _f32(head_w)
+    out = np.empty((cache.batch, k), np.int32)
+    c = cache._c()
+    lib().orc_indexer_topk(C.byref(c), _p(q, C.c_uint16), H, _p(hw, C.c_float), k,
+                           _p(out, C.c_int32))
+    return out
+
+
+def sparse_attn(cache: Cache, q, idx, swa, scale, swa_len=None):
+    q = _f32(q)
+    B, H, D = q.shape
+    idx = np.ascontiguousarray(idx, np.int32)
+    k = idx.shape[1]
+    swa = np.ascontiguousarray(swa, np.uint16)
+    W = swa.shape[1]
+    sl = None if swa_len is None else np.ascontiguousarray(swa_len, np.int32)
+    out = np.empty((B, H, cache.dim - cache.rope_dim), np.float64)
+    lse = np.empty((B, H), np.float64)
+    c = cache._c()
+    lib().orc_sparse_attn(C.byref(c), _p(q, C.c_float), H, _p(idx, C.c_int32), k,
+                          _p(swa, C.c_uint16), W, _p(sl, C.c_int32), float(scale),
+                          _p(out, C.c_double), _p(lse, C.c_double))
+    return out, lse
+
+
+def layer_group_decode(cache: Cache, modes, new_token, new_idx_row, w_comp, q, q_idx,
+                       swa_rings, swa_rows, k, scale, head_w=None):
+    """One CSA2 layer-group decode step over a shared cache.
+
+    new_token fp32 [B, dim] (appended by the full layer, or None);
+    q / q_idx / swa_rings / swa_rows: per-layer lists (q_idx None for reuse).
+    swa_rings are updated in place.  Returns (outs, lses, idx_lists) per layer.
+    """
+    B = cache.batch
+    cu = np.arange(B + 1, dtype=np.int32)
+    outs, lses, idxs = [], [], []
+    last_idx = None
+    for li, mode in enumerate(modes):
+        if mode == "full" and new_token is not None:
+            kv_append(cache, new_token, cu, w_comp, new_idx_row)
+        swa_append(swa_rings[li], swa_rows[li], cu, cache.n_tokens)
+        if mode in ("full", "reindex"):
+            hw = None if head_w is None else head_w[li]
+            last_idx = indexer_topk(cache, q_idx[li], k, hw)
+        elif last_idx is None:
+            raise ValueError("reuse layer with no preceding full/reindex layer")
+        o, l = sparse_attn(cache, q[li], last_idx, swa_rings[li], scale)
+        outs.append(o)
+        lses.append(l)
+        idxs.append(last_idx)
+    return outs, lses, idxs

@@ -1,0 +1,350 @@
+/*
+ * cskv_oracle.c -- plain CPU oracle of the CSA2 FP4 sparse-decode path.
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the tests, the smoke check and the
+ * bench's CPU-baseline leg, never by the product path.  Shares no code with
+ * the HIP library.  Each function follows the passage cited in
+ * cskv_oracle.h; the code is written for checking by eye, not for speed.
+ * The only parallelism is an OpenMP loop over independent sequences.
+ */
+#include "cskv_oracle.h"
+
+#include <assert.h>
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------ accounting */
+
+uint64_t orc_kv_bytes(uint64_t layers, uint64_t tokens, uint64_t heads,
+                      uint64_t head_dim, uint64_t elem_bytes)
+{
+    return 2u * layers * tokens * heads * head_dim * elem_bytes;
+}
+
+double orc_fp4_row_bytes(int dims, int group, double scale_bytes)
+{
+    return dims * 0.5 + (double)(dims / group) * scale_bytes;
+}
+
+double orc_global_kv_per_token(int n_copies, const int *ratio,
+                               double main_entry_bytes, double idx_entry_bytes)
+{
+    double total = 0.0;
+    for (int i = 0; i < n_copies; ++i)
+        total += (main_entry_bytes + idx_entry_bytes) / ratio[i];
+    return total;
+}
+
+/* ------------------------------------------------------------ E2M1, bf16 */
+
+double orc_e2m1_value(unsigned code)
+{
+    unsigned sign = (code >> 3) & 1u, expo = (code >> 1) & 3u, mant = code & 1u;
+    double mag;
+    if (expo == 0)
+        mag = 0.5 * mant;                               /* subnormal: m x 2^(1-bias) x 0.5 */
+    else
+        mag = ldexp(1.0 + 0.5 * mant, (int)expo - 1);   /* normal: 2^(e-1) x (1 + m/2) */
+    return sign ? -mag : mag;
+}
+
+unsigned orc_e2m1_encode(float v)
+{
+    assert(isfinite(v));
+    double mag = fabs((double)v);
+    unsigned sign = signbit(v) ? 8u : 0u;
+    /* at or past the largest grid value the nearest point is 6 (saturation);
+       handled first because for huge inputs the fp64 distances to 4 and 6
+       round to the same number */
+    if (mag >= 6.0) return 7u | sign;
+    unsigned best = 0;
+    double best_d = INFINITY;
+    for (unsigned c = 0; c < 8; ++c) {
+        double d = fabs(mag - orc_e2m1_value(c));
+        /* strictly closer wins; on an exact tie the even code wins (the two
+           candidates of a tie are neighbours, so exactly one is even) */
+        if (d < best_d || (d == best_d && (c & 1u) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    /* below 6 every distance is exact in fp64: an fp32 input and a grid value
+       of at most 3 significant bits differ by a number of at most ~30 bits */
+    return best | sign;
+}
+
+static uint32_t f32_bits(float x) { uint32_t u; memcpy(&u, &x, 4); return u; }
+static float bits_f32(uint32_t u) { float x; memcpy(&x, &u, 4); return x; }
+
+double orc_bf16_value(uint16_t h)
+{
+    return (double)bits_f32((uint32_t)h << 16);
+}
+
+uint16_t orc_bf16_from_f32(float x)
+{
+    assert(isfinite(x));
+    uint32_t u = f32_bits(x);
+    uint16_t lo = (uint16_t)(u >> 16);           /* truncation toward zero */
+    uint16_t hi = (uint16_t)(lo + 1);            /* next bf16 away from zero */
+    double xd = fabs((double)x);
+    double vlo = fabs(orc_bf16_value(lo));
+    /* the successor of the largest finite bf16 is infinity; for rounding it
+       sits where the next binade would start */
+    double vhi = ((hi & 0x7FFFu) == 0x7F80u) ? ldexp(1.0, 128) : fabs(orc_bf16_value(hi));
+    double dlo = xd - vlo, dhi = vhi - xd;
+    if (dlo < dhi) return lo;
+    if (dhi < dlo) return hi;
+    return (lo & 1u) ? hi : lo;                  /* tie: even mantissa */
+}
+
+/* ------------------------------------------------------------ compress */
+
+void orc_compress_pair(const float *W, const float *x_even, const float *x_odd,
+                       int dim, float *e)
+{
+    for (int r = 0; r < dim; ++r) {
+        float acc = 0.0f;
+        for (int j = 0; j < 2 * dim; ++j) {
+            float u = (j < dim) ? x_even[j] : x_odd[j - dim];
+            acc = fmaf(W[(size_t)r * 2 * dim + j], u, acc);
+        }
+        e[r] = acc;
+    }
+}
+
+/* ------------------------------------------------------------ quantise */
+
+void orc_quantize_row(const float *x, int n, int group, uint8_t *packed, float *scales)
+{
+    assert(n % group == 0 && n % 2 == 0);
+    unsigned *code = (unsigned *)malloc(sizeof(unsigned) * (size_t)n);
+    for (int g0 = 0; g0 < n; g0 += group) {
+        float a = 0.0f;
+        for (int c = g0; c < g0 + group; ++c) {
+            assert(isfinite(x[c]));
+            a = fmaxf(a, fabsf(x[c]));
+        }
+        float s = a / 6.0f;
+        if (s == 0.0f) {
+            scales[g0 / group] = 0.0f;
+            for (int c = g0; c < g0 + group; ++c) code[c] = 0;
+        } else {
+            scales[g0 / group] = s;
+            for (int c = g0; c < g0 + group; ++c) code[c] = orc_e2m1_encode(x[c] / s);
+        }
+    }
+    for (int t = 0; t < n / 2; ++t)
+        packed[t] = (uint8_t)(code[2 * t] | (code[2 * t + 1] << 4));
+    free(code);
+}
+
+void orc_dequantize_row(const uint8_t *packed, const float *scales, int n, int group,
+                        double *out)
+{
+    for (int c = 0; c < n; ++c) {
+        unsigned code = (c & 1) ? (packed[c / 2] >> 4) : (packed[c / 2] & 0xFu);
+        out[c] = orc_e2m1_value(code) * (double)scales[c / group];
+    }
+}
+
+/* ------------------------------------------------------------ cache append */
+
+static void store_entry(orc_cache *c, int b, int64_t i, const float *e, const uint16_t *idx_row)
+{
+    const int D = c->dim, Dv = c->dim - c->rope_dim;
+    size_t row = (size_t)b * c->capacity + (size_t)i;
+    orc_quantize_row(e, D, c->k_group, c->k_codes + row * (D / 2),
+                     c->k_scales + row * (D / c->k_group));
+    if (c->v_group > 0)
+        orc_quantize_row(e, Dv, c->v_group, c->v_codes + row * (Dv / 2),
+                         c->v_scales + row * (Dv / c->v_group));
+    memcpy(c->idx_keys + row * c->idx_dim, idx_row, sizeof(uint16_t) * (size_t)c->idx_dim);
+}
+
+void orc_kv_append(orc_cache *c, const float *tokens, const int32_t *cu_new,
+                   const float *w_comp, const uint16_t *idx_rows)
+{
+    const int D = c->dim;
+    float *e = (float *)malloc(sizeof(float) * (size_t)D);
+    for (int b = 0; b < c->batch; ++b) {
+        int64_t p = c->n_tokens[b];
+        int64_t m = cu_new[b + 1] - cu_new[b];
+        const float *rows = tokens + (size_t)cu_new[b] * D;
+        const uint16_t *irows = idx_rows + (size_t)cu_new[b] * c->idx_dim;
+        if (m == 0) continue;
+        if (w_comp == NULL) {
+            if (p % 2 != 0) { c->status[0] |= ORC_STATUS_ODD_ENTRY_APPEND; continue; }
+            if (p / 2 + m > c->capacity) { c->status[0] |= ORC_STATUS_OVERFLOW; continue; }
+            for (int64_t q = 0; q < m; ++q)
+                store_entry(c, b, p / 2 + q, rows + q * D, irows + q * c->idx_dim);
+            c->n_tokens[b] = (int32_t)(p + 2 * m);
+        } else {
+            if ((p + m) / 2 > c->capacity) { c->status[0] |= ORC_STATUS_OVERFLOW; continue; }
+            for (int64_t q = 0; q < m; ++q) {
+                int64_t pos = p + q;
+                if (pos % 2 == 0) continue;            /* first half of a pair */
+                const float *x_even = (q > 0) ? rows + (q - 1) * D : c->pending + (size_t)b * D;
+                orc_compress_pair(w_comp, x_even, rows + q * D, D, e);
+                store_entry(c, b, pos / 2, e, irows + q * c->idx_dim);
+            }
+            if ((p + m) % 2 != 0)
+                memcpy(c->pending + (size_t)b * D, rows + (m - 1) * D, sizeof(float) * (size_t)D);
+            c->n_tokens[b] = (int32_t)(p + m);
+        }
+    }
+    free(e);
+}
+
+void orc_swa_append(uint16_t *ring, int batch, int W, int dim, const float *rows,
+                    const int32_t *cu_new, const int32_t *end_pos)
+{
+    for (int b = 0; b < batch; ++b) {
+        int64_t m = cu_new[b + 1] - cu_new[b];
+        for (int64_t q = 0; q < m; ++q) {
+            int64_t pos = (int64_t)end_pos[b] - m + q;
+            if (pos < 0 || pos < (int64_t)end_pos[b] - W) continue;
+            const float *x = rows + (size_t)(cu_new[b] + q) * dim;
+            uint16_t *dst = ring + ((size_t)b * W + (size_t)(pos % W)) * dim;
+            for (int d = 0; d < dim; ++d) dst[d] = orc_bf16_from_f32(x[d]);
+        }
+    }
+}
+
+/* ------------------------------------------------------------ indexer */
+
+void orc_indexer_scores(const uint16_t *keys, int64_t E, int idx_dim,
+                        const uint16_t *q, int heads, const float *head_w,
+                        double *scores)
+{
+    for (int64_t j = 0; j < E; ++j) {
+        double s = 0.0;
+        for (int h = 0; h < heads; ++h) {
+            double dot = 0.0;
+            for (int d = 0; d < idx_dim; ++d)
+                dot += orc_bf16_value(q[(size_t)h * idx_dim + d]) *
+                       orc_bf16_value(keys[(size_t)j * idx_dim + d]);
+            double w = head_w ? (double)head_w[h] : 1.0;
+            s += w * (dot > 0.0 ? dot : 0.0);
+        }
+        scores[j] = s;
+    }
+}
+
+typedef struct { double score; int64_t index; } scored;
+
+static int by_score_then_index(const void *a, const void *b)
+{
+    const scored *x = (const scored *)a, *y = (const scored *)b;
+    if (x->score > y->score) return -1;
+    if (x->score < y->score) return 1;
+    return (x->index < y->index) ? -1 : (x->index > y->index);
+}
+
+static int by_int32(const void *a, const void *b)
+{
+    int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+void orc_topk(const double *scores, int64_t E, int k, int32_t *out)
+{
+    scored *all = (scored *)malloc(sizeof(scored) * (size_t)(E > 0 ? E : 1));
+    for (int64_t j = 0; j < E; ++j) { all[j].score = scores[j]; all[j].index = j; }
+    qsort(all, (size_t)E, sizeof(scored), by_score_then_index);
+    int64_t n = E < k ? E : k;
+    for (int64_t i = 0; i < n; ++i) out[i] = (int32_t)all[i].index;
+    qsort(out, (size_t)n, sizeof(int32_t), by_int32);
+    for (int64_t i = n; i < k; ++i) out[i] = -1;
+    free(all);
+}
+
+static int64_t entries_of(const orc_cache *c, int b)
+{
+    int64_t e = c->n_tokens[b] / 2;
+    if (e < 0) e = 0;
+    if (e > c->capacity) e = c->capacity;
+    return e;
+}
+
+void orc_indexer_topk(const orc_cache *c, const uint16_t *q, int heads,
+                      const float *head_w, int k, int32_t *out)
+{
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < c->batch; ++b) {
+        int64_t E = entries_of(c, b);
+        double *s = (double *)malloc(sizeof(double) * (size_t)(E > 0 ? E : 1));
+        orc_indexer_scores(c->idx_keys + (size_t)b * c->capacity * c->idx_dim, E, c->idx_dim,
+                           q + (size_t)b * heads * c->idx_dim, heads,
+                           head_w ? head_w + (size_t)b * heads : NULL, s);
+        orc_topk(s, E, k, out + (size_t)b * k);
+        free(s);
+    }
+}
+
+/* ------------------------------------------------------------ attention */
+
+void orc_sparse_attn(const orc_cache *c, const float *q, int heads, const int32_t *idx,
+                     int k, const uint16_t *swa, int W, const int32_t *swa_len,
+                     double scale, double *out, double *lse)
+{
+    const int D = c->dim, Dv = c->dim - c->rope_dim;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < c->batch; ++b) {
+        int64_t E = entries_of(c, b);
+        int64_t nswa = swa_len ? swa_len[b] : (c->n_tokens[b] < W ? c->n_tokens[b] : W);
+        if (nswa < 0) nswa = 0;
+        if (nswa > W) nswa = W;
+        int64_t nk = 0, cap = k + nswa;
+        double *K = (double *)malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1) * D);
+        double *V = (double *)malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1) * Dv);
+        /* keys from the compressed cache: dequantise (exact in fp64) */
+        for (int t = 0; t < k; ++t) {
+            int64_t j = idx[(size_t)b * k + t];
+            if (j < 0 || j >= E) continue;
+            size_t row = (size_t)b * c->capacity + (size_t)j;
+            orc_dequantize_row(c->k_codes + row * (D / 2), c->k_scales + row * (D / c->k_group),
+                               D, c->k_group, K + nk * D);
+            if (c->v_group > 0)
+                orc_dequantize_row(c->v_codes + row * (Dv / 2),
+                                   c->v_scales + row * (Dv / c->v_group), Dv, c->v_group,
+                                   V + nk * Dv);
+            else
+                memcpy(V + nk * Dv, K + nk * D, sizeof(double) * (size_t)Dv);
+            ++nk;
+        }
+        /* keys from the sliding window (bf16 rows; values are the first Dv dims) */
+        for (int64_t s = 0; s < nswa; ++s) {
+            const uint16_t *r = swa + ((size_t)b * W + (size_t)s) * D;
+            for (int d = 0; d < D; ++d) K[nk * D + d] = orc_bf16_value(r[d]);
+            memcpy(V + nk * Dv, K + nk * D, sizeof(double) * (size_t)Dv);
+            ++nk;
+        }
+        double *logit = (double *)malloc(sizeof(double) * (size_t)(nk > 0 ? nk : 1));
+        for (int h = 0; h < heads; ++h) {
+            const float *qh = q + ((size_t)b * heads + h) * D;
+            double *o = out + ((size_t)b * heads + h) * Dv;
+            for (int d = 0; d < Dv; ++d) o[d] = 0.0;
+            if (nk == 0) { lse[(size_t)b * heads + h] = -INFINITY; continue; }
+            double mx = -INFINITY;
+            for (int64_t j = 0; j < nk; ++j) {
+                double dot = 0.0;
+                for (int d = 0; d < D; ++d) dot += (double)qh[d] * K[j * D + d];
+                logit[j] = scale * dot;
+                if (logit[j] > mx) mx = logit[j];
+            }
+            double l = 0.0;
+            for (int64_t j = 0; j < nk; ++j) {
+                double p = exp(logit[j] - mx);
+                l += p;
+                for (int d = 0; d < Dv; ++d) o[d] += p * V[j * Dv + d];
+            }
+            for (int d = 0; d < Dv; ++d) o[d] /= l;
+            lse[(size_t)b * heads + h] = mx + log(l);
+        }
+        free(logit);
+        free(K);
+        free(V);
+    }
+}

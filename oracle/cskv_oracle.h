@@ -1,0 +1,168 @@
+/*
+ * cskv_oracle.h -- plain CPU oracle of the CSA2 FP4 sparse-decode path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library is the slow, obviously-correct
+ * reference that the HIP library is checked against.  Only the test suite,
+ * the smoke check and the bench's CPU-baseline leg may load it; the product
+ * path never links, loads or calls it, and it shares no code with the HIP
+ * sources.
+ *
+ * Arithmetic: fp64 for every floating-point result that has a plain
+ * mathematical definition (indexer scores, attention); fp32 where the method
+ * is an encoding whose decisions are defined in fp32 (group scale, the
+ * division by it, the stand-in compressor's fused multiply-add chain).
+ *
+ * Sources cited as [P1]/[P2]/[P3] (page title, then the section):
+ *   P1  "DeepSeek V4.1 Flash KV Cache压缩实战：FP4+CSA2+CED将显存降至1/4"
+ *   P2  "DeepSeek V1 到 V4.1-Flash，单 token 的 global KV 如何从 389,000 B 压缩到 890 B的？"
+ *   P3  "KV Cache 瘦身 437 倍：DeepSeek V4.1-Flash 的推理效率革命"
+ *
+ * Parity status per function is stated at each declaration.
+ */
+#ifndef CSKV_ORACLE_H
+#define CSKV_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------- byte accounting ---------------------------------------- */
+
+/* KV bytes = 2 x layers x tokens x heads x head_dim x bytes per element; the 2
+ * counts K and V [P1 §1; P2 "KV Cache 到底有多大"].
+ * Pinned: the pages' own worked numbers (95-layer BF16 model per token; the
+ * L=60 H=64 D=128 64K FP16 estimate; 128K / 1M context sizes). */
+uint64_t orc_kv_bytes(uint64_t layers, uint64_t tokens, uint64_t heads,
+                      uint64_t head_dim, uint64_t elem_bytes);
+
+/* Bytes of one group-quantised FP4 row: dims/2 code bytes + one scale of
+ * scale_bytes per group [P1 §3.1; P2 "890 字节是怎么算出来的"].
+ * Pinned: 512-dim main entry with 16-channel 1-byte scales = 288 B; 128-dim
+ * indexer key = 72 B (both printed on P2). */
+double orc_fp4_row_bytes(int dims, int group, double scale_bytes);
+
+/* Per-token global KV of a CSA2 model: sum over cache copies of
+ * (main entry + indexer key bytes) / compression ratio
+ * [P2 "890 字节是怎么算出来的", "CSA2：三种模式，40 层只存 4 份"].
+ * Pinned: 3 encoder copies at ratio 2 + 1 decoder copy at ratio 1 = 900 B. */
+double orc_global_kv_per_token(int n_copies, const int *ratio,
+                               double main_entry_bytes, double idx_entry_bytes);
+
+/* ---------------- E2M1 (FP4) and bf16 ------------------------------------ */
+
+/* Value of a 4-bit E2M1 code: 1 sign, 2 exponent (bias 1), 1 mantissa bit
+ * [P1 §3.1; P2 "P4 main KV"].  Pinned: the 16 codes give exactly
+ * {0, +-0.5, +-1, +-1.5, +-2, +-3, +-4, +-6}. */
+double orc_e2m1_value(unsigned code);
+
+/* Nearest E2M1 code to v (compared in fp64), ties to the even code, values
+ * past 6 saturate to 6, sign bit = signbit(v).  v must be finite.
+ * Pinned: exhaustive comparison over all fp32 inputs with the midpoint table
+ * (tests/native), plus round-trip and monotonicity. */
+unsigned orc_e2m1_encode(float v);
+
+/* Nearest bf16 to x, ties to even mantissa; overflow past the largest finite
+ * bf16 (by more than half an ulp) gives infinity.  x must be finite.
+ * Pinned: exhaustive comparison with the integer round-half-even trick. */
+uint16_t orc_bf16_from_f32(float x);
+double orc_bf16_value(uint16_t h);
+
+/* ---------------- compress, quantise, append ----------------------------- */
+
+/* Stand-in for the learned 2->1 compressor [P2 "突破四"; P1 §3.2]:
+ * e[r] = sum_j W[r][j] * u[j], u = x_even || x_odd, accumulated in fp32 from
+ * j = 0 upward with one fused multiply-add per term, starting from +0.
+ * The pages' compressor is trained and not given: parity with it is
+ * unpinned.  The fp32 chain itself is pinned against an fp64 evaluation
+ * within the forward-error bound of a length-2D dot product. */
+void orc_compress_pair(const float *W, const float *x_even, const float *x_odd,
+                       int dim, float *e);
+
+/* Group FP4 quantisation of one row [P1 §3.1, §4.3; P2 "P4 main KV"]:
+ * per contiguous group of `group` channels, a = max|x|, s = a/6 (fp32 IEEE
+ * division), codes = E2M1(x/s) with x/s an fp32 IEEE division; s == 0 stores
+ * scale +0 and all-zero codes.  Two codes per byte, low nibble first.
+ * Pinned: decode error bound, "every non-zero group holds a +-6 code",
+ * zero groups, sign of tiny negatives, exact round trip. */
+void orc_quantize_row(const float *x, int n, int group, uint8_t *packed, float *scales);
+void orc_dequantize_row(const uint8_t *packed, const float *scales, int n, int group,
+                        double *out);
+
+/* Host mirror of the device cache (same layout as the HIP library's). */
+typedef struct {
+    int32_t batch, capacity, dim, rope_dim, k_group, v_group, idx_dim;
+    uint8_t *k_codes;   /* [B][cap][dim/2]                 */
+    float *k_scales;    /* [B][cap][dim/k_group]           */
+    uint8_t *v_codes;   /* [B][cap][(dim-rope)/2] or NULL  */
+    float *v_scales;    /* [B][cap][(dim-rope)/v_group]    */
+    uint16_t *idx_keys; /* [B][cap][idx_dim] bf16          */
+    int32_t *n_tokens;  /* [B] tokens seen                 */
+    float *pending;     /* [B][dim] odd token awaiting its pair */
+    int32_t *status;    /* [1] bit flags                   */
+} orc_cache;
+
+#define ORC_STATUS_OVERFLOW 1
+#define ORC_STATUS_ODD_ENTRY_APPEND 2
+
+/* Append new rows to every sequence (2 tokens -> 1 entry, [P2 "突破四"]).
+ * tokens fp32 [total][dim]; cu_new [B+1] prefix sums of rows per sequence.
+ * w_comp != NULL: rows are tokens, paired by absolute position (2i, 2i+1);
+ *   an odd trailing token waits in pending[b]; entry i takes the indexer-key
+ *   row of the token that completes it.
+ * w_comp == NULL: rows are already entries (n_tokens += 2 per row); requires
+ *   an even token count.
+ * A sequence whose entries would pass capacity is left untouched and raises
+ * ORC_STATUS_OVERFLOW. */
+void orc_kv_append(orc_cache *c, const float *tokens, const int32_t *cu_new,
+                   const float *w_comp, const uint16_t *idx_rows);
+
+/* Write the window rows of a step: for each new row of sequence b at absolute
+ * position pos (the rows end at end_pos[b]), rows inside the last W positions
+ * go to ring slot pos % W as bf16 [P2 "突破四"; "CSA2：三种模式"]. */
+void orc_swa_append(uint16_t *ring, int batch, int W, int dim, const float *rows,
+                    const int32_t *cu_new, const int32_t *end_pos);
+
+/* ---------------- indexer + top-k ---------------------------------------- */
+
+/* s_j = sum_h w_h * max(0, sum_d q[h][d] K[j][d]) in fp64, over j < E
+ * [P2 "突破四" (lightweight indexer scoring all history),
+ *  "CSA2：三种模式" (per-layer indexer Q, per-entry indexer K)].
+ * The formula is not printed on the pages; parity with the model's indexer
+ * is unpinned.  Pinned: exact integer identities and brute-force cases. */
+void orc_indexer_scores(const uint16_t *keys, int64_t E, int idx_dim,
+                        const uint16_t *q, int heads, const float *head_w,
+                        double *scores);
+
+/* Exact top-k: order by (score descending, index ascending), take the first
+ * min(k, E), output them ascending by index, pad with -1 [P2 "突破四": keep
+ * the 512 highest].  Pinned: brute force over all subsets on tiny inputs,
+ * threshold invariants, forced ties. */
+void orc_topk(const double *scores, int64_t E, int k, int32_t *out);
+
+/* Whole-batch indexer + top-k on a cache: sequence b scores its first
+ * n_tokens[b]/2 entries (capped at capacity). q [B][H][Di], head_w [B][H]
+ * or NULL, out [B][k]. */
+void orc_indexer_topk(const orc_cache *c, const uint16_t *q, int heads,
+                      const float *head_w, int k, int32_t *out);
+
+/* ---------------- attention ---------------------------------------------- */
+
+/* One joint softmax per query head over the selected compressed entries and
+ * the window rows [P2 "突破四"; "突破二" (one shared latent for all heads)]:
+ * l = scale * q.k; out = sum softmax(l) * v[0:dim-rope]; lse = log sum exp l.
+ * Keys: K = dequantised key plane (all dim dims); values: the value plane if
+ * present, else K's first dim-rope dims.  Indices < 0 or >= the sequence's
+ * entry count are skipped.  No keys: out = 0, lse = -inf.
+ * q fp32 [B][Hq][dim]; idx [B][k]; swa bf16 [B][W][dim]; swa_len [B]
+ * (NULL: min(n_tokens, W)); out [B][Hq][dim-rope]; lse [B][Hq].
+ * Pinned: equal logits -> mean of values, a dominant logit -> its value,
+ * single key, LSE merge of the two branches, permutation invariance. */
+void orc_sparse_attn(const orc_cache *c, const float *q, int heads, const int32_t *idx,
+                     int k, const uint16_t *swa, int W, const int32_t *swa_len,
+                     double scale, double *out, double *lse);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

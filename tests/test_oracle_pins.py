@@ -1,0 +1,526 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these tests uses the HIP library.  Each pin is chosen so that a
+plausible mistake in the oracle (a dropped term, a wrong sign or index, a
+transposed operand, a wrong rounding or tie rule) fails at least one of them.
+"""
+import json
+import math
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLD = json.load(open(os.path.join(HERE, "golden", "page_numbers.json"), encoding="utf-8"))
+GIB = 1 << 30
+
+
+# ---------------------------------------------------------------- byte accounting
+
+def test_first_generation_bytes_per_token(orc):
+    g = GOLD["first_gen_bytes_per_token"]
+    b = orc.kv_bytes(g["layers"], 1, g["kv_heads"], g["head_dim"], g["elem_bytes"])
+    assert b == 389120
+    assert abs(b - g["approx_bytes"]) / g["approx_bytes"] < g["rel_tol"]
+
+
+def test_first_generation_context_sizes(orc):
+    g = GOLD["first_gen_context_sizes"]
+    per_tok = orc.kv_bytes(95, 1, 8, 128, 2)
+    # the pages' "GB" here are binary GiB: 47.5 -> "48", 380.0 -> "380"
+    assert per_tok * g["tokens_128k"] / GIB == pytest.approx(47.5)
+    assert round(per_tok * g["tokens_128k"] / GIB) == g["printed_128k_gb"]
+    assert per_tok * g["tokens_1m"] / GIB == pytest.approx(g["printed_1m_gb"])
+    assert orc.kv_bytes(95, g["tokens_1m"], 8, 128, 2) == per_tok * g["tokens_1m"]
+
+
+def test_fp16_64k_estimate(orc):
+    g = GOLD["fp16_64k_estimate"]
+    b = orc.kv_bytes(g["layers"], g["tokens"], g["heads"], g["head_dim"], g["elem_bytes"])
+    assert b == 128849018880
+    assert b / 1e11 == pytest.approx(g["printed_bytes_approx"] / 1e11, abs=0.005)
+    assert b / GIB == g["printed_gb"]
+    assert b / 4 / GIB == g["printed_quarter_gb"]
+    half = orc.kv_bytes(g["layers"], g["tokens"] // 2, g["heads"], g["head_dim"], g["elem_bytes"])
+    assert half / 4 / GIB == g["printed_32k_quarter_gb"]
+
+
+def test_fp4_is_4x_fp16_before_scales(orc):
+    g = GOLD["fp4_vs_fp16_ratio_before_scales"]
+    d = 576
+    fp16 = d * g["fp16_bits"] / 8
+    fp4_no_scale = orc.fp4_row_bytes(d, d, 0.0)
+    assert fp16 / fp4_no_scale == g["printed_ratio"]
+    # with fp32 group scales the ratio is 16 / (4 + 32/g)
+    for grp, ratio in ((32, 3.2), (64, 16 / 4.5)):
+        assert fp16 / orc.fp4_row_bytes(d, grp, 4.0) == pytest.approx(ratio)
+
+
+def test_mla_entry_dims():
+    g = GOLD["mla_numbers_per_layer_token"]
+    assert g["latent"] + g["rope"] == g["printed_total"] == 576
+
+
+def test_fp4_entry_and_indexer_key_bytes(orc):
+    m, i = GOLD["fp4_main_entry"], GOLD["fp4_indexer_key"]
+    assert orc.fp4_row_bytes(m["dims"], m["scale_group"], m["scale_bytes"]) == m["printed_bytes"]
+    assert orc.fp4_row_bytes(i["dims"], i["scale_group"], i["scale_bytes"]) == i["printed_bytes"]
+
+
+def test_global_kv_per_token_900(orc):
+    g = GOLD["global_kv_per_token"]
+    ratios = [g["encoder_ratio"]] * g["encoder_copies"] + [g["decoder_ratio"]] * g["decoder_copies"]
+    enc = orc.global_kv_per_token(ratios[:3], 288, 72)
+    dec = orc.global_kv_per_token(ratios[3:], 288, 72)
+    assert enc == g["printed_encoder_bytes"]
+    assert dec == g["printed_decoder_bytes"]
+    tot = orc.global_kv_per_token(ratios, 288, 72)
+    assert tot == g["printed_estimate"]
+    assert abs(tot - g["printed_reported"]) / g["printed_reported"] < 0.02
+    first_gen = orc.kv_bytes(95, 1, 8, 128, 2)
+    assert round(first_gen / g["printed_reported"]) == GOLD["reduction_factor"]["printed"]
+
+
+def test_csa2_schedule_counts():
+    g = GOLD["csa2_full_layers"]
+    sched = g["encoder_group"] * g["encoder_groups"] + g["decoder_first"] + \
+        g["decoder_rest"] * g["decoder_rest_groups"]
+    assert sched.count("full") == g["printed_full"]
+    # the pages' own group sizes add up to 38 of the 40 layers they state
+    assert len(sched) == 38
+
+
+# ---------------------------------------------------------------- E2M1 / bf16
+
+def test_e2m1_value_set(orc):
+    vals = [orc.e2m1_value(c) for c in range(16)]
+    assert sorted(set(abs(v) for v in vals)) == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    assert vals[:8] == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    assert vals[8:] == [-v for v in vals[:8]]
+    assert math.copysign(1, vals[8]) == -1          # code 8 is -0
+
+
+def test_e2m1_encode_round_trip_and_ties(orc):
+    for c in range(16):
+        assert orc.e2m1_encode(orc.e2m1_value(c)) == c
+    ties = {0.25: 0, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6, 5.0: 6}
+    for v, c in ties.items():
+        assert orc.e2m1_encode(v) == c and orc.e2m1_encode(-v) == c | 8
+    assert orc.e2m1_encode(1e30) == 7 and orc.e2m1_encode(-7.0) == 15
+    assert orc.e2m1_encode(-1e-30) == 8 and orc.e2m1_encode(0.0) == 0
+
+
+def test_e2m1_monotone(orc):
+    xs = np.linspace(-8, 8, 4001)
+    vals = [orc.e2m1_value(orc.e2m1_encode(float(x))) for x in xs]
+    assert all(a <= b for a, b in zip(vals, vals[1:]))
+
+
+def test_bf16_matches_torch_on_samples(orc):
+    torch = pytest.importorskip("torch")
+    g = np.random.default_rng(7)
+    x = np.concatenate([g.standard_normal(2000).astype(np.float32) * np.float32(10.0) ** g.integers(-30, 30, 2000),
+                        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8)], np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    got = np.array([orc.bf16_from_f32(float(v)) for v in x], np.uint16)
+    assert np.array_equal(ref, got)
+
+
+@pytest.fixture(scope="module")
+def exhaustive_bin(tmp_path_factory):
+    out = tmp_path_factory.mktemp("native") / "exhaustive"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-o", str(out),
+                    os.path.join(HERE, "native", "exhaustive.c"), "-ldl", "-lm"], check=True)
+    return str(out)
+
+
+def test_encoders_exhaustive_all_fp32(orc, exhaustive_bin):
+    """Every finite fp32 pattern: E2M1 encode vs the threshold table and bf16
+    rounding vs the integer formulation."""
+    import oracle.build as ob
+    r = subprocess.run([exhaustive_bin, ob.LIB, "0", str(1 << 32)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "e2m1_mismatch=0 bf16_mismatch=0" in r.stdout
+
+
+# ---------------------------------------------------------------- quantiser
+
+def _codes(packed):
+    return np.stack([packed & 0xF, packed >> 4], axis=-1).reshape(*packed.shape[:-1], -1)
+
+
+@pytest.mark.parametrize("group", [32, 64])
+def test_quantize_error_bound_and_full_scale_code(orc, group):
+    g = np.random.default_rng(group)
+    for law in ("normal", "t3"):
+        x = g.standard_normal(576).astype(np.float32) if law == "normal" else \
+            (g.standard_t(3, 576)).astype(np.float32)
+        packed, scales = orc.quantize_row(x, group)
+        deq = orc.dequantize_row(packed, scales, 576, group)
+        s = np.repeat(scales.astype(np.float64), group)
+        err = np.abs(x.astype(np.float64) - deq)
+        assert np.all(err <= s * (1 + 2 ** -20))
+        small = np.abs(x.astype(np.float64)) <= 2 * s
+        assert np.all(err[small] <= s[small] * (0.25 + 2 ** -21))
+        codes = _codes(packed).reshape(-1, group)
+        assert np.all((codes & 7).max(axis=1) == 7)
+        # the scale is absmax / 6 in fp32
+        a = np.abs(x).reshape(-1, group).max(axis=1)
+        assert np.array_equal(scales, (a / np.float32(6.0)).astype(np.float32))
+
+
+def test_quantize_zero_group_and_signs(orc):
+    x = np.zeros(64, np.float32)
+    x[32:] = np.float32(1.0)
+    x[33] = np.float32(-1e-3)      # rounds to zero magnitude but keeps its sign
+    x[34] = np.float32(-0.0)
+    packed, scales = orc.quantize_row(x, 32)
+    codes = _codes(packed)
+    assert scales[0] == 0 and not np.signbit(scales[0]) and np.all(codes[:32] == 0)
+    assert scales[1] == np.float32(1.0) / np.float32(6.0)
+    assert codes[33] == 8 and codes[34] == 8 and codes[32] == 7
+
+
+def test_quantize_pack_order_low_nibble_first(orc):
+    x = np.zeros(32, np.float32)
+    x[0], x[1] = 6.0, -3.0          # codes 7 and 13
+    packed, _ = orc.quantize_row(x, 32)
+    assert packed[0] == 7 | (13 << 4)
+
+
+def test_quantize_uses_true_division(orc):
+    """x/s is an IEEE division, not a multiplication by a reciprocal: find an
+    input where the two differ in the chosen code and check the division wins."""
+    g = np.random.default_rng(3)
+    found = 0
+    for _ in range(20000):
+        a = np.float32(g.uniform(0.5, 4.0))
+        s = a / np.float32(6.0)
+        mid = np.float32(g.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]))
+        x = np.float32(mid * s)
+        for cand in (x, np.nextafter(x, np.float32(0)), np.nextafter(x, np.float32(10))):
+            q_div = np.float32(cand / s)
+            q_rcp = np.float32(cand * (np.float32(1.0) / s))
+            if q_div != q_rcp:
+                row = np.zeros(32, np.float32)
+                row[0], row[1] = a, cand
+                packed, scales = orc.quantize_row(row, 32)
+                assert scales[0] == s
+                assert _codes(packed)[1] == orc.e2m1_encode(float(q_div))
+                found += 1
+    assert found > 0
+
+
+# ---------------------------------------------------------------- compressor
+
+def test_compress_selects_rows():
+    import oracle as orc
+    D = 576
+    g = np.random.default_rng(1)
+    xe, xo = g.standard_normal(D).astype(np.float32), g.standard_normal(D).astype(np.float32)
+    W = np.zeros((D, 2 * D), np.float32)
+    W[np.arange(D), np.arange(D)] = 1
+    assert np.array_equal(orc.compress_pair(W, xe, xo), xe)
+    W[:] = 0
+    W[np.arange(D), D + np.arange(D)] = 1
+    assert np.array_equal(orc.compress_pair(W, xe, xo), xo)
+    W[:] = 0
+    W[3, 7], W[3, D + 7] = 2.0, -1.0
+    e = orc.compress_pair(W, xe, xo)
+    assert e[3] == np.float32(np.float32(2 * xe[7]) - xo[7]) and np.all(np.delete(e, 3) == 0)
+
+
+def test_compress_sequential_fma_order():
+    """The fold runs j = 0..2D-1 in order: 1e8 + 1 rounds to 1e8 in fp32, so
+    (1e8 + 1) - 1e8 = 0, while any regrouping that adds 1 last gives 1."""
+    import oracle as orc
+    D = 4
+    W = np.zeros((D, 2 * D), np.float32)
+    W[0, :3] = 1.0
+    xe = np.array([1e8, 1.0, -1e8, 0.0], np.float32)
+    assert orc.compress_pair(W, xe, np.zeros(D, np.float32))[0] == 0.0
+    W[1, [0, 2, 1]] = 1.0
+    xe2 = np.array([1e8, 1.0, -1e8, 0], np.float32)
+    assert orc.compress_pair(W, xe2, np.zeros(D, np.float32))[1] == 0.0
+    # a single rounding per term: after acc = -1, fma(1/3f, 3, acc) keeps the
+    # product's low bits (a separate multiply would round 3 * (1/3f) to 1 first)
+    W[:] = 0
+    W[2, 0], W[2, 1] = -1.0, np.float32(1.0 / 3.0)
+    xe3 = np.array([1.0, 3.0, 0, 0], np.float32)
+    exact = np.float64(np.float32(1.0 / 3.0)) * 3.0 - 1.0
+    assert orc.compress_pair(W, xe3, np.zeros(D, np.float32))[2] == np.float32(exact)
+
+
+def test_compress_within_forward_error_bound():
+    import oracle as orc
+    D = 576
+    g = np.random.default_rng(2)
+    W = (g.standard_normal((D, 2 * D)) * 0.02).astype(np.float32)
+    xe, xo = g.standard_normal(D).astype(np.float32), g.standard_normal(D).astype(np.float32)
+    e = orc.compress_pair(W, xe, xo).astype(np.float64)
+    u = np.concatenate([xe, xo]).astype(np.float64)
+    ref = W.astype(np.float64) @ u
+    n, uu = 2 * D, 2.0 ** -24
+    gamma = n * uu / (1 - n * uu)
+    bound = gamma * (np.abs(W.astype(np.float64)) @ np.abs(u))
+    assert np.all(np.abs(e - ref) <= bound)
+
+
+# ---------------------------------------------------------------- append state machine
+
+def _small_cache(orc, B=3, cap=40, k_group=32, v_group=0, idx_dim=64):
+    return orc.Cache.empty(B, cap, 576, 64, k_group, v_group, idx_dim)
+
+
+def test_append_pairs_and_pending(orc):
+    D = 576
+    g = np.random.default_rng(4)
+    W = (g.standard_normal((D, 2 * D)) * 0.02).astype(np.float32)
+    lens = [7, 4, 1]
+    toks = [g.standard_normal((n, D)).astype(np.float32) for n in lens]
+    irow = [g.integers(-8, 9, (n, 64)).astype(np.float32).view(np.uint32) >> 16 for n in lens]
+    irow = [r.astype(np.uint16) for r in irow]
+    # one call with all rows
+    c1 = _small_cache(orc)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    orc.kv_append(c1, np.concatenate(toks), cu, W, np.concatenate(irow))
+    # token by token
+    c2 = _small_cache(orc)
+    for t in range(max(lens)):
+        rows, irs, cu2 = [], [], [0]
+        for b in range(3):
+            if t < lens[b]:
+                rows.append(toks[b][t]); irs.append(irow[b][t])
+            cu2.append(len(rows))
+        orc.kv_append(c2, np.array(rows), np.array(cu2, np.int32), W, np.array(irs))
+    for f in ("k_codes", "k_scales", "idx_keys", "n_tokens"):
+        assert np.array_equal(getattr(c1, f), getattr(c2, f)), f
+    assert np.array_equal(c1.pending[[0, 2]], c2.pending[[0, 2]])
+    assert list(c1.n_tokens) == lens and list(c1.entries()) == [3, 2, 0]
+    assert np.array_equal(c1.pending[0], toks[0][6]) and np.array_equal(c1.pending[2], toks[2][0])
+    # entry i of sequence 0 is the compressed pair (2i, 2i+1) with the key row of token 2i+1
+    e = orc.compress_pair(W, toks[0][2], toks[0][3])
+    pk, sc = orc.quantize_row(e, 32)
+    assert np.array_equal(c1.k_codes[0, 1], pk) and np.array_equal(c1.k_scales[0, 1], sc)
+    assert np.array_equal(c1.idx_keys[0, 1], irow[0][3])
+    assert c1.status[0] == 0
+
+
+def test_append_entries_mode_and_split_planes(orc):
+    g = np.random.default_rng(5)
+    c = _small_cache(orc, B=2, cap=8, k_group=32, v_group=128)
+    rows = g.standard_normal((5, 576)).astype(np.float32)
+    irs = np.zeros((5, 64), np.uint16)
+    orc.kv_append(c, rows, np.array([0, 3, 5], np.int32), None, irs)
+    assert list(c.n_tokens) == [6, 4]
+    pk, sc = orc.quantize_row(rows[4], 32)
+    assert np.array_equal(c.k_codes[1, 1], pk) and np.array_equal(c.k_scales[1, 1], sc)
+    pv, sv = orc.quantize_row(rows[4][:512], 128)
+    assert np.array_equal(c.v_codes[1, 1], pv) and np.array_equal(c.v_scales[1, 1], sv)
+    assert sv.shape == (4,)
+
+
+def test_append_overflow_and_odd_are_rejected(orc):
+    c = _small_cache(orc, B=2, cap=2)
+    rows = np.ones((4, 576), np.float32)
+    irs = np.zeros((4, 64), np.uint16)
+    orc.kv_append(c, rows, np.array([0, 3, 4], np.int32), None, irs)
+    assert list(c.n_tokens) == [0, 2] and c.status[0] == orc.STATUS_OVERFLOW
+    c.status[0] = 0
+    c.n_tokens[1] = 3
+    orc.kv_append(c, rows[:1], np.array([0, 0, 1], np.int32), None, irs[:1])
+    assert c.status[0] == orc.STATUS_ODD_ENTRY_APPEND and c.n_tokens[1] == 3
+
+
+def test_swa_ring_positions(orc):
+    g = np.random.default_rng(6)
+    B, W, D = 2, 4, 576
+    ring = np.zeros((B, W, D), np.uint16)
+    rows = g.standard_normal((7, D)).astype(np.float32)
+    cu = np.array([0, 6, 7], np.int32)
+    end = np.array([10, 2], np.int32)
+    orc.swa_append(ring, rows, cu, end)
+    # sequence 0: rows are positions 4..9, the last 4 (6..9) land in slots 2,3,0,1
+    for q, pos in ((2, 6), (3, 7), (4, 8), (5, 9)):
+        want = np.array([orc.bf16_from_f32(float(v)) for v in rows[q]], np.uint16)
+        assert np.array_equal(ring[0, pos % W], want)
+    assert np.array_equal(ring[1, 1], np.array([orc.bf16_from_f32(float(v)) for v in rows[6]],
+                                               np.uint16))
+    assert np.all(ring[1, [0, 2, 3]] == 0)
+
+
+# ---------------------------------------------------------------- indexer + top-k
+
+def _bf16_int(a):
+    return (np.asarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_indexer_special_cases(orc):
+    g = np.random.default_rng(8)
+    K = g.integers(-8, 9, (50, 64))
+    q = g.integers(-8, 9, (4, 64))
+    # zero keys score zero
+    assert np.all(orc.indexer_scores(_bf16_int(np.zeros((3, 64))), _bf16_int(q)) == 0)
+    # a unit query picks one coordinate and ReLU drops negatives
+    e = np.zeros((1, 64)); e[0, 5] = 1
+    s = orc.indexer_scores(_bf16_int(K), _bf16_int(e))
+    assert np.array_equal(s, np.maximum(K[:, 5], 0))
+    # the ReLU acts per head before the head sum: +e5 and -e5 give |K5|, not 0
+    s2 = orc.indexer_scores(_bf16_int(K), _bf16_int(np.stack([e[0], -e[0]])))
+    assert np.array_equal(s2, np.abs(K[:, 5]))
+    # q equal to a key row scores its squared norm (single head)
+    s3 = orc.indexer_scores(_bf16_int(K), _bf16_int(K[7:8]))
+    assert s3[7] == float((K[7] ** 2).sum())
+    # head weights scale heads linearly; zero weights silence a head
+    w = np.array([0, 2, 0, 0], np.float32)
+    s4 = orc.indexer_scores(_bf16_int(K), _bf16_int(q), w)
+    assert np.array_equal(s4, 2 * np.maximum(K @ q[1], 0))
+    # a transposed key layout would mix entries: entry j only depends on row j
+    K2 = K.copy(); K2[10] = 0
+    s5 = orc.indexer_scores(_bf16_int(K2), _bf16_int(q))
+    s6 = orc.indexer_scores(_bf16_int(K), _bf16_int(q))
+    assert s5[10] == 0 and np.array_equal(np.delete(s5, 10), np.delete(s6, 10))
+
+
+def _valid_topk(s, k, out):
+    E = len(s)
+    n = min(k, E)
+    sel = out[:n]
+    assert np.all(out[n:] == -1) and np.all(np.diff(sel) > 0)
+    S = set(sel.tolist())
+    for i in S:
+        for j in range(E):
+            if j not in S:
+                assert s[i] > s[j] or (s[i] == s[j] and i < j)
+
+
+def test_topk_characterisation_with_ties(orc):
+    g = np.random.default_rng(9)
+    for trial in range(300):
+        E = int(g.integers(0, 14))
+        k = int(g.integers(1, 10))
+        s = g.integers(0, 3, E).astype(np.float64) if trial % 2 else g.standard_normal(E)
+        out = orc.topk(s, k)
+        _valid_topk(s, k, out)
+
+
+def test_topk_all_equal_takes_lowest_indices(orc):
+    out = orc.topk(np.zeros(1000), 512)
+    assert np.array_equal(out, np.arange(512))
+    out = orc.topk(np.zeros(300), 512)
+    assert np.array_equal(out[:300], np.arange(300)) and np.all(out[300:] == -1)
+
+
+def test_topk_exhaustive_tiny(orc):
+    """All score vectors over {0,1,2}^6 and every k: the output is the unique
+    set allowed by the (score desc, index asc) order."""
+    import itertools
+    for s in itertools.product([0.0, 1.0, 2.0], repeat=6):
+        s = np.array(s)
+        for k in range(1, 8):
+            _valid_topk(s, k, orc.topk(s, k))
+
+
+# ---------------------------------------------------------------- attention
+
+def _attn_cache(orc, entries, group=32):
+    """Cache holding the given fp32 entries for one sequence."""
+    n = entries.shape[0]
+    c = orc.Cache.empty(1, n, 576, 64, group, 0, 64)
+    orc.kv_append(c, entries, np.array([0, n], np.int32), None, np.zeros((n, 64), np.uint16))
+    return c
+
+
+def test_attention_equal_logits_gives_mean(orc):
+    g = np.random.default_rng(10)
+    c = _attn_cache(orc, g.standard_normal((6, 576)).astype(np.float32))
+    idx = np.array([[0, 2, 5, -1]], np.int32)
+    swa = _bf16_int(g.integers(-3, 4, (1, 4, 576)))
+    out, lse = orc.sparse_attn(c, np.zeros((1, 2, 576), np.float32), idx, swa, 1 / 24,
+                               swa_len=np.array([2], np.int32))
+    vals = [orc.dequantize_row(c.k_codes[0, j], c.k_scales[0, j], 576, 32)[:512] for j in (0, 2, 5)]
+    vals += [(swa[0, s, :512].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+             for s in range(2)]
+    assert np.allclose(out[0, 0], np.mean(vals, axis=0), rtol=0, atol=1e-14)
+    assert lse[0, 1] == pytest.approx(math.log(5), abs=1e-14)
+
+
+def test_attention_single_key_and_dominant_key(orc):
+    g = np.random.default_rng(11)
+    ent = g.standard_normal((3, 576)).astype(np.float32)
+    c = _attn_cache(orc, ent)
+    deq = [orc.dequantize_row(c.k_codes[0, j], c.k_scales[0, j], 576, 32) for j in range(3)]
+    swa = np.zeros((1, 1, 576), np.uint16)
+    q = g.standard_normal((1, 1, 576)).astype(np.float32)
+    out, lse = orc.sparse_attn(c, q, np.array([[1]], np.int32), swa, 0.5,
+                               swa_len=np.array([0], np.int32))
+    assert np.array_equal(out[0, 0], deq[1][:512])
+    assert lse[0, 0] == pytest.approx(0.5 * float(q[0, 0].astype(np.float64) @ deq[1]), rel=1e-13)
+    # make key 2 dominate by > 60 in logit: the others weigh <= 2 e^-60
+    qd = (deq[2] / np.dot(deq[2], deq[2]) * 200.0).astype(np.float32)[None, None]
+    out, _ = orc.sparse_attn(c, qd, np.array([[0, 1, 2]], np.int32), swa, 1.0,
+                             swa_len=np.array([0], np.int32))
+    l = [float(qd[0, 0].astype(np.float64) @ d) for d in deq]
+    assert l[2] - max(l[0], l[1]) > 60
+    assert np.allclose(out[0, 0], deq[2][:512], rtol=0, atol=1e-24)
+
+
+def test_attention_lse_merge_and_permutation(orc):
+    g = np.random.default_rng(12)
+    c = _attn_cache(orc, g.standard_normal((20, 576)).astype(np.float32))
+    q = g.standard_normal((1, 3, 576)).astype(np.float32)
+    swa = _bf16_int(g.integers(-4, 5, (1, 8, 576)))
+    idx = np.array([[1, 4, 7, 11, 19]], np.int32)
+    joint, lj = orc.sparse_attn(c, q, idx, swa, 1 / 24, swa_len=np.array([8], np.int32))
+    sp, ls = orc.sparse_attn(c, q, idx, swa, 1 / 24, swa_len=np.array([0], np.int32))
+    sw, lw = orc.sparse_attn(c, q, np.full((1, 5), -1, np.int32), swa, 1 / 24,
+                             swa_len=np.array([8], np.int32))
+    m = np.maximum(ls, lw)
+    wa, wb = np.exp(ls - m), np.exp(lw - m)
+    merged = (sp * wa[..., None] + sw * wb[..., None]) / (wa + wb)[..., None]
+    assert np.allclose(joint, merged, rtol=1e-12, atol=1e-14)
+    assert np.allclose(lj, m + np.log(wa + wb), rtol=1e-13)
+    perm, lp = orc.sparse_attn(c, q, idx[:, ::-1].copy(), swa, 1 / 24, swa_len=np.array([8], np.int32))
+    assert np.allclose(perm, joint, rtol=1e-13, atol=1e-15) and np.allclose(lp, lj, rtol=1e-14)
+
+
+def test_attention_out_of_range_indices_skipped_and_empty(orc):
+    g = np.random.default_rng(13)
+    c = _attn_cache(orc, g.standard_normal((4, 576)).astype(np.float32))
+    q = g.standard_normal((1, 2, 576)).astype(np.float32)
+    swa = np.zeros((1, 2, 576), np.uint16)
+    a, la = orc.sparse_attn(c, q, np.array([[0, 9, -5, 2]], np.int32), swa, 0.1,
+                            swa_len=np.array([0], np.int32))
+    b, lb = orc.sparse_attn(c, q, np.array([[0, 2]], np.int32), swa, 0.1,
+                            swa_len=np.array([0], np.int32))
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+    e, le = orc.sparse_attn(c, q, np.array([[-1]], np.int32), swa, 0.1,
+                            swa_len=np.array([0], np.int32))
+    assert np.all(e == 0) and np.all(np.isneginf(le))
+
+
+# ---------------------------------------------------------------- modes
+
+def test_modes_reindex_and_reuse_reproduce_full(orc):
+    import synth
+    w = synth.scaled(synth.WORKLOADS["tiny_t4096"], batch=2, entries=300, prefill_tokens=None,
+                     entry_law="normal", layers=("full", "reindex", "reuse"))
+    cache = orc.Cache.empty(2, 310, 576, 64, 32, 0, 64)
+    ents = np.concatenate([synth.cache_entries(w, b) for b in range(2)])
+    keys = np.concatenate([synth.cache_idx_keys(w, b) for b in range(2)])
+    orc.kv_append(cache, ents, np.array([0, 300, 600], np.int32), None, keys)
+    st = synth.step_inputs(w)
+    Wc = synth.w_comp(w)
+    # give the reindex layer the full layer's indexer query, the reuse layer its q and window
+    q_idx = [st.q_idx[0], st.q_idx[0], None]
+    q = [st.q[0], st.q[1], st.q[0]]
+    rings = [st.swa_ring[0].copy(), st.swa_ring[1].copy(), st.swa_ring[0].copy()]
+    rows = [st.swa_row[0], st.swa_row[1], st.swa_row[0]]
+    outs, lses, idxs = orc.layer_group_decode(cache, w.layers, st.token, st.idx_row, Wc, q, q_idx,
+                                              rings, rows, 64, 1 / 24)
+    assert np.array_equal(idxs[0], idxs[1]) and np.array_equal(idxs[2], idxs[1])
+    assert np.array_equal(outs[2], outs[0]) and np.array_equal(lses[2], lses[0])
+    assert not np.array_equal(outs[1], outs[0])
+    assert list(cache.n_tokens) == [601, 601]
