@@ -1,0 +1,269 @@
+"""Decode-step throughput of the CSA2 FP4 sparse-decode path on one MI355X.
+
+Workload (default): 32 sequences x 64K tokens (32,768 compressed entries
+each), 576-dim E2M1 entries with group 64 and Student-t(3) values, indexer
+64 heads x 128 dims with integer values in [-8, 8], top-512, 64 query heads,
+128-token bf16 window.  One step = one Full-layer decode step for the whole
+batch: append one token per sequence (stand-in compressor + FP4 quantise),
+window append, indexer scan + exact top-512, gather/dequantise + attention.
+
+Inputs are seeded synthetic data resident in HBM before timing.  Several
+cache replicas are stepped in rotation so consecutive steps do not hit the
+last-level cache with the previous step's data.
+
+Prints one JSON line (rank 0).  --copy-probe MIB instead runs a plain
+device copy of known size, used to calibrate hardware byte counters.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA2 FP4 sparse decode: steps/s at 64K ctx; achieved % of 8 TB/s HBM"
+HBM_PEAK_GBPS = 8000.0
+PMC_FILE = os.path.join(ROOT, "profiles", "indexer_scan_decode_64k_b32_pmc.json")
+SCAN_SRC = os.path.join(ROOT, "compressed_sparse_kv_append_amd", "csrc", "indexer.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="decode_64k_b32")
+    p.add_argument("--replicas", type=int, default=2)
+    p.add_argument("--cpu-baseline-seqs", type=int, default=16)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-probe", type=int, default=0, help="MiB copied by a plain device copy")
+    return p.parse_args()
+
+
+def copy_probe(mib: int):
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+
+
+def build_replicas(ck, synth, w, cap, dev, n):
+    """Entries-mode build of n identical cache replicas, one sequence at a time
+    (each sequence's entries are drawn once and appended to every replica)."""
+    import torch
+    reps = [ck.Cache.allocate(w.batch, cap, w.k_group, w.v_group, w.idx_dim) for _ in range(n)]
+    for b in range(w.batch):
+        ents = dev(synth.cache_entries(w, b))
+        keys = dev(synth.cache_idx_keys(w, b))
+        cu = np.zeros(w.batch + 1, np.int32)
+        cu[b + 1:] = ents.shape[0]
+        cu = dev(cu)
+        for c in reps:
+            ck.kv_append_fp4(c, ents, cu, None, keys)
+    torch.cuda.synchronize()
+    return reps
+
+
+def step_bytes(w, entries: float) -> dict:
+    """Algorithmic bytes of one step (whole batch): every plane read or written
+    once by the method's definition; score arrays are not counted."""
+    B, D, Dv, Di = w.batch, w.dim, w.vdim, w.idx_dim
+    entry_fp4 = D // 2 + 4 * (D // w.k_group)
+    if w.v_group:
+        entry_fp4 += Dv // 2 + 4 * (Dv // w.v_group)
+    parts = {
+        "indexer_keys": B * entries * Di * 2,
+        "indexer_q": B * w.idx_heads * Di * 2,
+        "gather": B * min(w.topk, entries) * entry_fp4,
+        "window": B * w.window * D * 2,
+        "q": B * w.q_heads * D * 4,
+        "out": B * w.q_heads * (Dv + 1) * 4,
+        "indices": B * w.topk * 4 * 2,
+        # one token per sequence; a pair completes every other step, then the
+        # compressor weights are read and one entry + indexer key written
+        "append": B * (D * 4 * 2 + 0.5 * (entry_fp4 + Di * 2)) + 0.5 * D * 2 * D * 4,
+    }
+    parts["total"] = sum(parts.values())
+    return parts
+
+
+def cpu_baseline(synth, w, nseq: int):
+    """The oracle, as it is, on a bounded sample: nseq of the batch's sequences,
+    full-length caches, one Full-layer decode step; the cache build is untimed."""
+    import oracle as orc
+    nseq = max(1, min(nseq, w.batch))
+    seqs = list(range(nseq))
+    sub = synth.scaled(w, batch=nseq)
+    cap = w.entries + 8
+    hc = orc.Cache.empty(nseq, cap, w.dim, w.rope_dim, w.k_group, w.v_group, w.idx_dim)
+    ents = np.concatenate([synth.cache_entries(w, b) for b in seqs])
+    keys = np.concatenate([synth.cache_idx_keys(w, b) for b in seqs])
+    cu = (np.arange(nseq + 1) * w.entries).astype(np.int32)
+    t0 = time.time()
+    orc.kv_append(hc, ents, cu, None, keys)
+    log(f"cpu baseline: oracle cache build {time.time() - t0:.1f}s (untimed)")
+    del ents
+    st = synth.step_inputs(w, 0, seqs=seqs)
+    W = synth.w_comp(w)
+    rings = [r.copy() for r in st.swa_ring]
+    t0 = time.perf_counter()
+    orc.layer_group_decode(hc, sub.layers, st.token, st.idx_row, W, st.q, st.q_idx, rings,
+                           st.swa_row, w.topk, 1 / math.sqrt(w.dim))
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    per_full_step = dt * w.batch / nseq
+    return {"value": 1.0 / per_full_step, "unit": "steps/s", "cores": min(threads, nseq),
+            "kind": "oracle",
+            "sample": f"{nseq} of {w.batch} sequences at full length ({w.entries} entries), one Full-layer "
+                      f"decode step ({dt:.2f} s), scaled by {w.batch}/{nseq}; cache build untimed"}
+
+
+def pmc_traffic():
+    """HBM bytes per scan launch from the committed counter summary, if it was
+    taken on the current scan source."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    try:
+        d = json.load(open(PMC_FILE))
+        sha = hashlib.sha256(open(SCAN_SRC, "rb").read()).hexdigest()
+        if d.get("scan_source_sha256") != sha:
+            return None
+        return float(d["traffic_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              "(the batch shards by sequence with no exchange, so N GPUs run N independent copies)",
+              file=sys.stderr)
+        sys.exit(2)
+    if a.copy_probe:
+        copy_probe(a.copy_probe)
+        return
+
+    import torch
+
+    import compressed_sparse_kv_append_amd as ck
+    import synth
+
+    ck.lib()
+    w = synth.WORKLOADS[a.workload]
+    assert w.entries is not None and len(w.layers) == 1, "bench steps fixed-length single-layer workloads"
+    total_steps = a.warmup + a.steps
+    per_rep = (total_steps + a.replicas - 1) // a.replicas
+    cap = w.entries + (per_rep + 1) // 2 + 16
+
+    def dev(x):
+        x = np.ascontiguousarray(x)
+        return torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).cuda()
+
+    t0 = time.time()
+    reps = build_replicas(ck, synth, w, cap, dev, a.replicas)
+    log(f"built {a.replicas} cache replicas in {time.time() - t0:.1f}s "
+        f"({reps[0].entry_bytes()} B/entry incl. indexer key)")
+    st = synth.step_inputs(w, 0)
+    W = dev(synth.w_comp(w))
+    scale = 1 / math.sqrt(w.dim)
+    B = w.batch
+    per_rep_io = []
+    for r in range(a.replicas):
+        per_rep_io.append(dict(
+            layers=[ck.Layer(mode="full", q=dev(st.q[0]), q_idx=dev(st.q_idx[0]), swa=dev(st.swa_ring[0]),
+                             swa_row=dev(st.swa_row[0]),
+                             idx=torch.empty(B, w.topk, dtype=torch.int32, device="cuda"),
+                             out=torch.empty(B, w.q_heads, w.vdim, device="cuda"),
+                             lse=torch.empty(B, w.q_heads, device="cuda"))],
+            ws=ck.workspace(reps[r], w.topk)))
+    tok, irow = dev(st.token), dev(st.idx_row)
+
+    def step(i):
+        r = i % a.replicas
+        io = per_rep_io[r]
+        ck.layer_group_decode(reps[r], io["layers"], tok, W, irow, w.topk, w.window, scale, ws=io["ws"])
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    kinds = {"append": ck.KERNEL_APPEND, "swa_append": ck.KERNEL_SWA_APPEND,
+             "indexer_scan": ck.KERNEL_INDEXER_SCAN, "topk_select": ck.KERNEL_TOPK_SELECT,
+             "attention": ck.KERNEL_ATTENTION}
+    for kd in kinds.values():
+        ck.timer_enable(kd, a.steps)
+    ent_before = np.mean([r.n_tokens.float().mean().item() for r in reps]) / 2
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(a.warmup, total_steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    kern = {}
+    for name, kd in kinds.items():
+        tot, n = ck.timer_read(kd)
+        kern[name] = {"avg_us": 1000 * tot / max(n, 1), "launches": n}
+    ck.timer_disable_all()
+    status = [int(r.status[0].item()) for r in reps]
+    assert all(s == 0 for s in status), f"cache status flags raised: {status}"
+
+    # mean entries per sequence over the timed steps
+    ent_after = np.mean([r.n_tokens.float().mean().item() for r in reps]) / 2
+    entries_mean = float(0.5 * (ent_before + ent_after))
+    sb = step_bytes(w, entries_mean)
+    scan_bytes = sb["indexer_keys"] + sb["indexer_q"]
+    scan_us = kern["indexer_scan"]["avg_us"]
+    achieved = scan_bytes / (scan_us * 1e-6) / 1e9
+    steps_per_s = 1000.0 / ms
+    result = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; Student-t(3) cache entries, integer indexer inputs)",
+        "config": {"workload": w.name, "batch": B, "context_tokens": 2 * w.entries,
+                   "entries_per_seq": w.entries, "k_group": w.k_group, "storage": "e2m1+fp32 scales",
+                   "idx_heads": w.idx_heads, "idx_dim": w.idx_dim, "q_heads": w.q_heads,
+                   "topk": w.topk, "window": w.window, "replicas": a.replicas,
+                   "tokens_per_s": round(steps_per_s * B, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": pmc_traffic(), "kernel": "indexer_scan",
+                     "bytes_per_launch": round(scan_bytes), "avg_us": round(scan_us, 2)},
+        "step_bytes": round(sb["total"]),
+        "step_hbm_frac": round(sb["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
+    }
+    if not a.no_cpu_baseline:
+        log("timing the oracle on a CPU sample ...")
+        result["cpu_baseline"] = cpu_baseline(synth, w, a.cpu_baseline_seqs)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,297 @@
+"""Python binding of libcskv.so, the gfx950 CSA2 FP4 sparse-decode library.
+
+Argument marshalling only: each function checks tensor placement, dtype and
+shape, then calls the C entry point of the same name on the current HIP
+stream.  Every step of the path runs in the library's HIP kernels; there is
+no other code path.  If the library is not built, importing works but the
+first call raises.
+
+Tensors: device (cuda) tensors, contiguous.  bf16 data may be passed as
+torch.bfloat16 or as int16/uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+from . import _build
+
+OK = 0
+EINVAL = -1
+EUNSUPPORTED = -2
+EWORKSPACE = -3
+EHIP = -4
+STATUS_OVERFLOW = 1
+STATUS_ODD_ENTRY_APPEND = 2
+STATUS_BAD_STATE = 4
+MODE_FULL, MODE_REINDEX, MODE_REUSE = 0, 1, 2
+MODES = {"full": MODE_FULL, "reindex": MODE_REINDEX, "reuse": MODE_REUSE}
+KERNEL_APPEND, KERNEL_SWA_APPEND, KERNEL_INDEXER_SCAN, KERNEL_TOPK_SELECT, KERNEL_ATTENTION = 1, 2, 3, 4, 5
+
+EXPORTS = ("cskv_kv_append_fp4", "cskv_swa_append", "cskv_indexer_topk", "cskv_sparse_attn_decode",
+           "cskv_layer_group_decode", "cskv_workspace_bytes", "cskv_entry_bytes", "cskv_last_error",
+           "cskv_timer_enable", "cskv_timer_read", "cskv_timer_disable_all")
+
+
+class CskvError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"cskv error {code}: {msg}")
+        self.code = code
+
+
+class CacheDesc(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("capacity", C.c_int32), ("dim", C.c_int32),
+                ("rope_dim", C.c_int32), ("k_group", C.c_int32), ("v_group", C.c_int32),
+                ("idx_dim", C.c_int32),
+                ("k_codes", C.c_void_p), ("k_scales", C.c_void_p), ("v_codes", C.c_void_p),
+                ("v_scales", C.c_void_p), ("idx_keys", C.c_void_p), ("n_tokens", C.c_void_p),
+                ("pending", C.c_void_p), ("status", C.c_void_p)]
+
+
+class LayerDesc(C.Structure):
+    _fields_ = [("mode", C.c_int32), ("q", C.c_void_p), ("q_idx", C.c_void_p),
+                ("head_w", C.c_void_p), ("swa", C.c_void_p), ("swa_row", C.c_void_p),
+                ("idx", C.c_void_p), ("out", C.c_void_p), ("lse", C.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            raise RuntimeError(f"{_build.LIB} is missing: build the HIP library first "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = C.CDLL(_build.LIB)
+        vp, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
+        L.cskv_kv_append_fp4.argtypes = [vp, vp, vp, i32, vp, vp, vp]
+        L.cskv_swa_append.argtypes = [vp, i32, i32, i32, vp, vp, i32, vp, vp]
+        L.cskv_indexer_topk.argtypes = [vp, vp, i32, vp, i32, vp, vp, sz, vp]
+        L.cskv_sparse_attn_decode.argtypes = [vp, vp, i32, vp, i32, vp, i32, vp, C.c_float, vp, vp, vp]
+        L.cskv_layer_group_decode.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, C.c_float,
+                                              vp, sz, vp]
+        L.cskv_workspace_bytes.argtypes = [vp, i32]
+        L.cskv_workspace_bytes.restype = sz
+        L.cskv_entry_bytes.argtypes = [i32] * 5
+        L.cskv_entry_bytes.restype = sz
+        L.cskv_last_error.restype = C.c_char_p
+        L.cskv_timer_enable.argtypes = [i32, i32]
+        L.cskv_timer_read.argtypes = [i32, C.POINTER(C.c_double), C.POINTER(C.c_int32)]
+        for f in ("cskv_kv_append_fp4", "cskv_swa_append", "cskv_indexer_topk", "cskv_sparse_attn_decode",
+                  "cskv_layer_group_decode", "cskv_timer_enable", "cskv_timer_read", "cskv_timer_disable_all"):
+            getattr(L, f).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != OK:
+        raise CskvError(rc, lib().cskv_last_error().decode())
+
+
+def _stream(stream) -> C.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor], dtypes, name, shape=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    return C.c_void_p(t.data_ptr())
+
+
+F32 = (torch.float32,)
+I32 = (torch.int32,)
+U8 = (torch.uint8,)
+B16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+@dataclass
+class Cache:
+    """Device planes of one layer group's shared cache (torch-allocated, caller-owned)."""
+    batch: int
+    capacity: int
+    k_group: int
+    v_group: int
+    idx_dim: int
+    k_codes: torch.Tensor
+    k_scales: torch.Tensor
+    v_codes: Optional[torch.Tensor]
+    v_scales: Optional[torch.Tensor]
+    idx_keys: torch.Tensor
+    n_tokens: torch.Tensor
+    pending: torch.Tensor
+    status: torch.Tensor
+    dim: int = 576
+    rope_dim: int = 64
+
+    @classmethod
+    def allocate(cls, batch, capacity, k_group=32, v_group=0, idx_dim=128, dim=576, rope_dim=64,
+                 device="cuda"):
+        dv = dim - rope_dim
+        z = lambda *s, dt: torch.zeros(*s, dtype=dt, device=device)
+        return cls(batch, capacity, k_group, v_group, idx_dim,
+                   z(batch, capacity, dim // 2, dt=torch.uint8),
+                   z(batch, capacity, dim // k_group, dt=torch.float32),
+                   z(batch, capacity, dv // 2, dt=torch.uint8) if v_group else None,
+                   z(batch, capacity, dv // v_group, dt=torch.float32) if v_group else None,
+                   z(batch, capacity, idx_dim, dt=torch.int16),
+                   z(batch, dt=torch.int32), z(batch, dim, dt=torch.float32),
+                   z(4, dt=torch.int32), dim, rope_dim)
+
+    def desc(self) -> CacheDesc:
+        p = lambda t: None if t is None else t.data_ptr()
+        return CacheDesc(self.batch, self.capacity, self.dim, self.rope_dim, self.k_group,
+                         self.v_group, self.idx_dim, p(self.k_codes), p(self.k_scales),
+                         p(self.v_codes), p(self.v_scales), p(self.idx_keys), p(self.n_tokens),
+                         p(self.pending), p(self.status))
+
+    def entry_bytes(self) -> int:
+        return entry_bytes(self.dim, self.rope_dim, self.k_group, self.v_group, self.idx_dim)
+
+
+def workspace_bytes(cache: Cache, k: int) -> int:
+    d = cache.desc()
+    n = lib().cskv_workspace_bytes(C.byref(d), k)
+    if n == 0:
+        raise CskvError(EINVAL, lib().cskv_last_error().decode())
+    return int(n)
+
+
+def workspace(cache: Cache, k: int) -> torch.Tensor:
+    return torch.empty(workspace_bytes(cache, k), dtype=torch.uint8, device=cache.k_codes.device)
+
+
+def entry_bytes(dim, rope_dim, k_group, v_group, idx_dim) -> int:
+    return int(lib().cskv_entry_bytes(dim, rope_dim, k_group, v_group, idx_dim))
+
+
+def kv_append_fp4(cache: Cache, tokens: torch.Tensor, cu_new: Optional[torch.Tensor],
+                  w_comp: Optional[torch.Tensor], idx_rows: torch.Tensor, stream=None) -> None:
+    n = tokens.shape[0]
+    d = cache.desc()
+    _check(lib().cskv_kv_append_fp4(
+        C.byref(d), _ptr(tokens, F32, "tokens", (n, cache.dim)),
+        _ptr(cu_new, I32, "cu_new", (cache.batch + 1,)), n,
+        _ptr(w_comp, F32, "w_comp", (cache.dim, 2 * cache.dim)),
+        _ptr(idx_rows, B16, "idx_rows", (n, cache.idx_dim)), _stream(stream)))
+
+
+def swa_append(ring: torch.Tensor, rows: torch.Tensor, cu_new: Optional[torch.Tensor],
+               end_pos: torch.Tensor, stream=None) -> None:
+    B, W, D = ring.shape
+    n = rows.shape[0]
+    _check(lib().cskv_swa_append(_ptr(ring, B16, "ring"), B, W, D, _ptr(rows, F32, "rows", (n, D)),
+                                 _ptr(cu_new, I32, "cu_new", (B + 1,)), n,
+                                 _ptr(end_pos, I32, "end_pos", (B,)), _stream(stream)))
+
+
+def indexer_topk(cache: Cache, q_idx: torch.Tensor, k: int, head_w: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    B, H, Di = q_idx.shape
+    if out is None:
+        out = torch.empty(B, k, dtype=torch.int32, device=q_idx.device)
+    if ws is None:
+        ws = workspace(cache, k)
+    d = cache.desc()
+    _check(lib().cskv_indexer_topk(
+        C.byref(d), _ptr(q_idx, B16, "q_idx", (cache.batch, H, cache.idx_dim)), H,
+        _ptr(head_w, F32, "head_w", (cache.batch, H)), k, _ptr(out, I32, "out", (cache.batch, k)),
+        _ptr(ws, U8, "ws"), ws.numel(), _stream(stream)))
+    return out
+
+
+def sparse_attn_decode(cache: Cache, q: torch.Tensor, idx: torch.Tensor, swa: torch.Tensor,
+                       softmax_scale: float, swa_len: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                       stream=None):
+    B, H, D = q.shape
+    k = idx.shape[1]
+    W = swa.shape[1]
+    dv = cache.dim - cache.rope_dim
+    if out is None:
+        out = torch.empty(B, H, dv, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    d = cache.desc()
+    _check(lib().cskv_sparse_attn_decode(
+        C.byref(d), _ptr(q, F32, "q", (cache.batch, H, cache.dim)), H,
+        _ptr(idx, I32, "idx", (cache.batch, k)), k, _ptr(swa, B16, "swa", (cache.batch, W, cache.dim)), W,
+        _ptr(swa_len, I32, "swa_len", (cache.batch,)), float(softmax_scale),
+        _ptr(out, F32, "out", (cache.batch, H, dv)), _ptr(lse, F32, "lse", (cache.batch, H)),
+        _stream(stream)))
+    return out, lse
+
+
+@dataclass
+class Layer:
+    """One layer of a CSA2 group; tensors as in cskv.h's cskv_layer."""
+    mode: str
+    q: torch.Tensor
+    swa: torch.Tensor
+    out: torch.Tensor
+    q_idx: Optional[torch.Tensor] = None
+    head_w: Optional[torch.Tensor] = None
+    swa_row: Optional[torch.Tensor] = None
+    idx: Optional[torch.Tensor] = None
+    lse: Optional[torch.Tensor] = None
+
+
+def layer_group_decode(cache: Cache, layers: Sequence[Layer], new_tokens: Optional[torch.Tensor],
+                       w_comp: Optional[torch.Tensor], new_idx_rows: Optional[torch.Tensor],
+                       k: int, window: int, softmax_scale: float, ws: Optional[torch.Tensor] = None,
+                       stream=None) -> None:
+    B = cache.batch
+    n_heads = layers[0].q.shape[1]
+    n_idx_heads = next((L.q_idx.shape[1] for L in layers if L.q_idx is not None), 1)
+    if ws is None:
+        ws = workspace(cache, k)
+    arr = (LayerDesc * len(layers))()
+    for i, L in enumerate(layers):
+        dv = cache.dim - cache.rope_dim
+        arr[i] = LayerDesc(MODES[L.mode], _ptr(L.q, F32, "q", (B, n_heads, cache.dim)),
+                           _ptr(L.q_idx, B16, "q_idx", (B, n_idx_heads, cache.idx_dim)),
+                           _ptr(L.head_w, F32, "head_w", (B, n_idx_heads)),
+                           _ptr(L.swa, B16, "swa", (B, window, cache.dim)),
+                           _ptr(L.swa_row, F32, "swa_row", (B, cache.dim)),
+                           _ptr(L.idx, I32, "idx", (B, k)),
+                           _ptr(L.out, F32, "out", (B, n_heads, dv)),
+                           _ptr(L.lse, F32, "lse", (B, n_heads)))
+    d = cache.desc()
+    _check(lib().cskv_layer_group_decode(
+        C.byref(d), arr, len(layers), _ptr(new_tokens, F32, "new_tokens", (B, cache.dim)),
+        _ptr(w_comp, F32, "w_comp", (cache.dim, 2 * cache.dim)),
+        _ptr(new_idx_rows, B16, "new_idx_rows", (B, cache.idx_dim)), n_idx_heads, n_heads, k,
+        window, float(softmax_scale), _ptr(ws, U8, "ws"), ws.numel(), _stream(stream)))
+
+
+# ---------------------------------------------------------------- timers
+
+def timer_enable(kind: int, max_launches: int) -> None:
+    _check(lib().cskv_timer_enable(kind, max_launches))
+
+
+def timer_read(kind: int):
+    ms = C.c_double()
+    n = C.c_int32()
+    _check(lib().cskv_timer_read(kind, C.byref(ms), C.byref(n)))
+    return ms.value, n.value
+
+
+def timer_disable_all() -> None:
+    _check(lib().cskv_timer_disable_all())

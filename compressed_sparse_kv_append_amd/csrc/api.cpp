@@ -1,0 +1,308 @@
+// api.cpp -- the C ABI: argument checks, launch order, timers.
+//
+// Sources cited as [P2] (page title, then the section):
+//   P2  "DeepSeek V1 到 V4.1-Flash，单 token 的 global KV 如何从 389,000 B 压缩到 890 B的？"
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+#include <vector>
+
+#include "cskv.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(CSKV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+#define REQUIRE(cond, code, ...)              \
+    do {                                      \
+        if (!(cond)) return fail(code, __VA_ARGS__); \
+    } while (0)
+
+int check_cache(const cskv_cache *c)
+{
+    REQUIRE(c, CSKV_EINVAL, "cache descriptor is NULL");
+    REQUIRE(c->batch >= 1 && c->batch <= 65535, CSKV_EINVAL, "batch %d out of [1, 65535]", c->batch);
+    REQUIRE(c->capacity >= 1 && c->capacity <= (1 << 26), CSKV_EINVAL,
+            "capacity %d out of [1, 2^26]", c->capacity);
+    REQUIRE(c->dim == 576 && c->rope_dim == 64, CSKV_EUNSUPPORTED,
+            "dim %d / rope_dim %d: only 576 / 64 are built", c->dim, c->rope_dim);
+    REQUIRE(c->k_group == 32 || c->k_group == 64, CSKV_EUNSUPPORTED,
+            "k_group %d: 32 or 64 supported (must divide 576)", c->k_group);
+    REQUIRE(c->v_group == 0 || c->v_group == 32 || c->v_group == 64 || c->v_group == 128,
+            CSKV_EUNSUPPORTED, "v_group %d: 0, 32, 64 or 128 supported", c->v_group);
+    REQUIRE(c->idx_dim == 64 || c->idx_dim == 128, CSKV_EUNSUPPORTED,
+            "idx_dim %d: 64 or 128 supported", c->idx_dim);
+    REQUIRE(c->k_codes && c->k_scales && c->idx_keys && c->n_tokens && c->pending && c->status,
+            CSKV_EINVAL, "cache plane pointer is NULL");
+    REQUIRE((c->v_group > 0) == (c->v_codes != nullptr) && (c->v_group > 0) == (c->v_scales != nullptr),
+            CSKV_EINVAL, "value plane pointers must be set exactly when v_group > 0");
+    REQUIRE(aligned(c->k_codes, 16) && aligned(c->k_scales, 16) && aligned(c->idx_keys, 16) &&
+                aligned(c->n_tokens, 16) && aligned(c->pending, 16) && aligned(c->status, 4) &&
+                (!c->v_codes || aligned(c->v_codes, 16)) && (!c->v_scales || aligned(c->v_scales, 16)),
+            CSKV_EINVAL, "cache planes must be 16-byte aligned");
+    return CSKV_OK;
+}
+
+int check_rows(const void *rows, const int32_t *cu_new, int32_t total_new, int32_t batch)
+{
+    REQUIRE(total_new >= 0, CSKV_EINVAL, "total_new %d < 0", total_new);
+    REQUIRE(total_new == 0 || rows, CSKV_EINVAL, "rows are NULL");
+    REQUIRE(rows == nullptr || aligned(rows, 16), CSKV_EINVAL, "rows must be 16-byte aligned");
+    REQUIRE(cu_new || total_new == batch, CSKV_EINVAL,
+            "cu_new NULL needs total_new == batch (%d != %d)", total_new, batch);
+    return CSKV_OK;
+}
+
+int topk_args(const cskv_cache *c, const uint16_t *q_idx, int32_t heads, int32_t k,
+              const int32_t *out_idx, const void *ws, size_t ws_bytes)
+{
+    REQUIRE(q_idx && aligned(q_idx, 16), CSKV_EINVAL, "q_idx NULL or not 16-byte aligned");
+    REQUIRE(heads >= 1 && heads <= 64, CSKV_EUNSUPPORTED, "n_idx_heads %d out of [1, 64]", heads);
+    REQUIRE(k >= 1 && k <= 2048, CSKV_EUNSUPPORTED, "k %d out of [1, 2048]", k);
+    REQUIRE(out_idx, CSKV_EINVAL, "out_idx is NULL");
+    const size_t need = cskv::topk_workspace(*c).total;
+    REQUIRE(ws && aligned(ws, 256), CSKV_EWORKSPACE, "workspace NULL or not 256-byte aligned");
+    REQUIRE(ws_bytes >= need, CSKV_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    return CSKV_OK;
+}
+
+int attn_args(const float *q, int32_t heads, const int32_t *idx, bool need_idx, int32_t k,
+              const uint16_t *swa, int32_t window, const float *out)
+{
+    REQUIRE(q && out && (idx || !need_idx), CSKV_EINVAL, "q, idx or out is NULL");
+    REQUIRE(heads >= 16 && heads <= 1024 && heads % 16 == 0, CSKV_EUNSUPPORTED,
+            "n_heads %d: a multiple of 16 in [16, 1024]", heads);
+    REQUIRE(k >= 1 && k <= 65536, CSKV_EUNSUPPORTED, "k %d out of [1, 65536]", k);
+    REQUIRE(window >= 1 && window <= (1 << 20), CSKV_EINVAL, "window %d out of [1, 2^20]", window);
+    REQUIRE(swa && aligned(swa, 16), CSKV_EINVAL, "window ring NULL or not 16-byte aligned");
+    return CSKV_OK;
+}
+
+// ---------------------------------------------------------------- timers
+
+struct Timer {
+    bool on = false;
+    int max = 0, count = 0;
+    std::vector<hipEvent_t> start, stop;
+};
+Timer g_timers[8];
+
+void free_timer(Timer &T)
+{
+    for (auto e : T.start) (void)hipEventDestroy(e);
+    for (auto e : T.stop) (void)hipEventDestroy(e);
+    T = Timer();
+}
+
+}  // namespace
+
+namespace cskv {
+void timer_before(int kind, hipStream_t s)
+{
+    Timer &T = g_timers[kind];
+    if (T.on && T.count < T.max) (void)hipEventRecord(T.start[T.count], s);
+}
+void timer_after(int kind, hipStream_t s)
+{
+    Timer &T = g_timers[kind];
+    if (T.on && T.count < T.max) (void)hipEventRecord(T.stop[T.count++], s);
+}
+}  // namespace cskv
+
+extern "C" {
+
+const char *cskv_last_error(void) { return g_error.c_str(); }
+
+size_t cskv_entry_bytes(int32_t dim, int32_t rope_dim, int32_t k_group, int32_t v_group,
+                        int32_t idx_dim)
+{
+    if (dim <= 0 || k_group <= 0 || dim % k_group) return 0;
+    size_t b = (size_t)dim / 2 + 4 * (size_t)(dim / k_group) + 2 * (size_t)idx_dim;
+    if (v_group > 0) {
+        const int dv = dim - rope_dim;
+        if (dv <= 0 || dv % v_group) return 0;
+        b += (size_t)dv / 2 + 4 * (size_t)(dv / v_group);
+    }
+    return b;
+}
+
+size_t cskv_workspace_bytes(const cskv_cache *cache, int32_t k)
+{
+    (void)k;
+    if (check_cache(cache) != CSKV_OK) return 0;
+    return cskv::topk_workspace(*cache).total;
+}
+
+int cskv_kv_append_fp4(const cskv_cache *cache, const float *tokens, const int32_t *cu_new,
+                       int32_t total_new, const float *w_comp, const uint16_t *idx_rows,
+                       hipStream_t stream)
+{
+    int rc = check_cache(cache);
+    if (rc) return rc;
+    if ((rc = check_rows(tokens, cu_new, total_new, cache->batch))) return rc;
+    REQUIRE(total_new == 0 || (idx_rows && aligned(idx_rows, 4)), CSKV_EINVAL,
+            "idx_rows NULL or not 4-byte aligned");
+    REQUIRE(!w_comp || aligned(w_comp, 16), CSKV_EINVAL, "w_comp must be 16-byte aligned");
+    hipError_t e = cskv::launch_kv_append(*cache, tokens, cu_new, total_new, w_comp, idx_rows, stream);
+    return e == hipSuccess ? CSKV_OK : hip_fail(e, "kv_append_fp4 launch");
+}
+
+int cskv_swa_append(uint16_t *ring, int32_t batch, int32_t window, int32_t dim, const float *rows,
+                    const int32_t *cu_new, int32_t total_new, const int32_t *end_pos,
+                    hipStream_t stream)
+{
+    REQUIRE(ring && aligned(ring, 16), CSKV_EINVAL, "ring NULL or not 16-byte aligned");
+    REQUIRE(batch >= 1, CSKV_EINVAL, "batch %d < 1", batch);
+    REQUIRE(window >= 1 && window <= (1 << 20), CSKV_EINVAL, "window %d out of [1, 2^20]", window);
+    REQUIRE(dim > 0 && dim % 4 == 0, CSKV_EUNSUPPORTED, "dim %d must be a positive multiple of 4", dim);
+    REQUIRE(end_pos, CSKV_EINVAL, "end_pos is NULL");
+    int rc = check_rows(rows, cu_new, total_new, batch);
+    if (rc) return rc;
+    hipError_t e = cskv::launch_swa_append(ring, batch, window, dim, rows, cu_new, total_new, end_pos, stream);
+    return e == hipSuccess ? CSKV_OK : hip_fail(e, "swa_append launch");
+}
+
+int cskv_indexer_topk(const cskv_cache *cache, const uint16_t *q_idx, int32_t n_idx_heads,
+                      const float *head_w, int32_t k, int32_t *out_idx, void *ws, size_t ws_bytes,
+                      hipStream_t stream)
+{
+    int rc = check_cache(cache);
+    if (rc) return rc;
+    if ((rc = topk_args(cache, q_idx, n_idx_heads, k, out_idx, ws, ws_bytes))) return rc;
+    hipError_t e = cskv::launch_indexer_topk(*cache, q_idx, n_idx_heads, head_w, k, out_idx, ws, stream);
+    return e == hipSuccess ? CSKV_OK : hip_fail(e, "indexer_topk launch");
+}
+
+int cskv_sparse_attn_decode(const cskv_cache *cache, const float *q, int32_t n_heads,
+                            const int32_t *idx, int32_t k, const uint16_t *swa, int32_t window,
+                            const int32_t *swa_len, float softmax_scale, float *out, float *lse,
+                            hipStream_t stream)
+{
+    int rc = check_cache(cache);
+    if (rc) return rc;
+    if ((rc = attn_args(q, n_heads, idx, true, k, swa, window, out))) return rc;
+    hipError_t e = cskv::launch_sparse_attn(*cache, q, n_heads, idx, k, swa, window, swa_len,
+                                            softmax_scale, out, lse, stream);
+    return e == hipSuccess ? CSKV_OK : hip_fail(e, "sparse_attn_decode launch");
+}
+
+int cskv_layer_group_decode(const cskv_cache *cache, const cskv_layer *layers, int32_t n_layers,
+                            const float *new_tokens, const float *w_comp,
+                            const uint16_t *new_idx_rows, int32_t n_idx_heads, int32_t n_heads,
+                            int32_t k, int32_t window, float softmax_scale, void *ws,
+                            size_t ws_bytes, hipStream_t stream)
+{
+    int rc = check_cache(cache);
+    if (rc) return rc;
+    REQUIRE(layers && n_layers >= 1 && n_layers <= 256, CSKV_EINVAL, "need 1..256 layers");
+    REQUIRE(!new_tokens || (aligned(new_tokens, 16) && new_idx_rows), CSKV_EINVAL,
+            "new_tokens must be 16-byte aligned and come with new_idx_rows");
+    // check every layer before enqueueing anything [P2 四、"CSA2：三种模式"]
+    bool have_index = false;
+    for (int i = 0; i < n_layers; ++i) {
+        const cskv_layer &L = layers[i];
+        REQUIRE(L.mode == CSKV_MODE_FULL || L.mode == CSKV_MODE_REINDEX || L.mode == CSKV_MODE_REUSE,
+                CSKV_EINVAL, "layer %d: unknown mode %d", i, L.mode);
+        if ((rc = attn_args(L.q, n_heads, L.idx, L.mode != CSKV_MODE_REUSE, k, L.swa, window, L.out)))
+            return fail(rc, "layer %d: %s", i, g_error.c_str());
+        REQUIRE(!L.swa_row || aligned(L.swa_row, 16), CSKV_EINVAL, "layer %d: swa_row not 16-byte aligned", i);
+        if (L.mode == CSKV_MODE_REUSE) {
+            REQUIRE(have_index, CSKV_EINVAL, "layer %d: REUSE with no FULL/REINDEX layer before it", i);
+        } else {
+            if ((rc = topk_args(cache, L.q_idx, n_idx_heads, k, L.idx, ws, ws_bytes)))
+                return fail(rc, "layer %d: %s", i, g_error.c_str());
+            have_index = true;
+        }
+    }
+    bool appended = false;
+    const int32_t *last_idx = nullptr;
+    hipError_t e;
+    for (int i = 0; i < n_layers; ++i) {
+        const cskv_layer &L = layers[i];
+        if (L.mode == CSKV_MODE_FULL && new_tokens && !appended) {
+            e = cskv::launch_kv_append(*cache, new_tokens, nullptr, cache->batch, w_comp, new_idx_rows, stream);
+            if (e != hipSuccess) return hip_fail(e, "layer group: append");
+            appended = true;
+        }
+        if (L.swa_row) {
+            e = cskv::launch_swa_append(L.swa, cache->batch, window, cache->dim, L.swa_row, nullptr,
+                                        cache->batch, cache->n_tokens, stream);
+            if (e != hipSuccess) return hip_fail(e, "layer group: window append");
+        }
+        if (L.mode != CSKV_MODE_REUSE) {
+            e = cskv::launch_indexer_topk(*cache, L.q_idx, n_idx_heads, L.head_w, k, L.idx, ws, stream);
+            if (e != hipSuccess) return hip_fail(e, "layer group: indexer");
+            last_idx = L.idx;
+        }
+        e = cskv::launch_sparse_attn(*cache, L.q, n_heads, last_idx, k, L.swa, window, nullptr,
+                                     softmax_scale, L.out, L.lse, stream);
+        if (e != hipSuccess) return hip_fail(e, "layer group: attention");
+    }
+    return CSKV_OK;
+}
+
+int cskv_timer_enable(int32_t kind, int32_t max_launches)
+{
+    REQUIRE(kind >= 1 && kind < 8, CSKV_EINVAL, "kernel kind %d", kind);
+    REQUIRE(max_launches >= 1 && max_launches <= 1 << 16, CSKV_EINVAL, "max_launches %d", max_launches);
+    Timer &T = g_timers[kind];
+    free_timer(T);
+    T.start.resize(max_launches);
+    T.stop.resize(max_launches);
+    for (int i = 0; i < max_launches; ++i) {
+        hipError_t e1 = hipEventCreate(&T.start[i]), e2 = hipEventCreate(&T.stop[i]);
+        if (e1 != hipSuccess || e2 != hipSuccess) {
+            free_timer(T);
+            return hip_fail(e1 != hipSuccess ? e1 : e2, "hipEventCreate");
+        }
+    }
+    T.max = max_launches;
+    T.on = true;
+    return CSKV_OK;
+}
+
+int cskv_timer_read(int32_t kind, double *total_ms, int32_t *count)
+{
+    REQUIRE(kind >= 1 && kind < 8 && total_ms && count, CSKV_EINVAL, "bad timer_read arguments");
+    Timer &T = g_timers[kind];
+    double sum = 0;
+    for (int i = 0; i < T.count; ++i) {
+        hipError_t e = hipEventSynchronize(T.stop[i]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+        float ms = 0;
+        e = hipEventElapsedTime(&ms, T.start[i], T.stop[i]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+        sum += ms;
+    }
+    *total_ms = sum;
+    *count = T.count;
+    return CSKV_OK;
+}
+
+int cskv_timer_disable_all(void)
+{
+    for (auto &T : g_timers) free_timer(T);
+    return CSKV_OK;
+}
+
+}  // extern "C"

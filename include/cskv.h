@@ -1,0 +1,238 @@
+/*
+ * cskv.h -- C ABI of the MI355X (gfx950) CSA2 FP4 sparse-decode library.
+ *
+ * One decode step of CSA2-style compressed sparse attention over an FP4
+ * (E2M1) group-quantised KV cache:
+ *   1. append: every 2 tokens are compressed into 1 cache entry, quantised to
+ *      packed E2M1 codes with one fp32 scale per channel group
+ *      (cskv_kv_append_fp4), and the sliding-window rows are written
+ *      (cskv_swa_append);
+ *   2. the indexer scores every cached entry and keeps the exact top-k
+ *      (cskv_indexer_topk);
+ *   3-4. the selected entries are gathered, dequantised, and attended to by
+ *      all query heads together with the window rows in one softmax
+ *      (cskv_sparse_attn_decode);
+ *   and the Full / Reindex / Reuse layer modes of one layer group over a
+ *   shared cache (cskv_layer_group_decode).
+ *
+ * Sources cited as [P1]/[P2]/[P3] (page title, then the section):
+ *   P1  "DeepSeek V4.1 Flash KV Cache压缩实战：FP4+CSA2+CED将显存降至1/4"
+ *   P2  "DeepSeek V1 到 V4.1-Flash，单 token 的 global KV 如何从 389,000 B 压缩到 890 B的？"
+ *   P3  "KV Cache 瘦身 437 倍：DeepSeek V4.1-Flash 的推理效率革命"
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked "host".  The caller owns
+ *     every buffer and the stream; the library never allocates device memory
+ *     and never synchronises.  All work is enqueued on `stream` in order.
+ *   - Return value: CSKV_OK (0) or a negative error code.  Arguments are
+ *     checked on the host before anything is enqueued; on error nothing is
+ *     enqueued and cskv_last_error() (thread-local) describes the problem.
+ *   - Conditions only the device can see (capacity overflow, an entries-mode
+ *     append onto a pending odd token) set bits in cache->status, which the
+ *     caller reads after synchronising; the offending sequence is left
+ *     unchanged and no byte outside the cache planes is written.
+ *   - Base pointers must be 16-byte aligned.
+ */
+#ifndef CSKV_H
+#define CSKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSKV_OK 0
+#define CSKV_EINVAL (-1)        /* bad argument, null pointer, misalignment   */
+#define CSKV_EUNSUPPORTED (-2)  /* valid but outside the shapes built here     */
+#define CSKV_EWORKSPACE (-3)    /* workspace missing or too small              */
+#define CSKV_EHIP (-4)          /* a HIP launch or runtime call failed         */
+
+/* bits of *cache->status (device int32) */
+#define CSKV_STATUS_OVERFLOW 1           /* an append would pass capacity       */
+#define CSKV_STATUS_ODD_ENTRY_APPEND 2   /* entries-mode append with a pending token */
+#define CSKV_STATUS_BAD_STATE 4          /* negative n_tokens or cu_new inconsistent with total_new */
+
+/*
+ * The shared cache of one layer group (device planes, caller-owned).
+ *
+ * Entry i of sequence b holds the compressed pair of tokens (2i, 2i+1)
+ * [P2 三、"突破四：滑动窗口和稀疏注意力" (2 tokens -> 1 entry)]; its 576 numbers
+ * are one MLA latent (512) plus its RoPE part (64), shared by all query
+ * heads [P2 三、"突破二：MLA，低秩压缩"].  It is stored as E2M1 codes with one
+ * fp32 scale per group of channels [P1 §3.1, §4.3; P2 四、"P4 main KV"]:
+ *   k_codes  u8  [batch][capacity][dim/2]          two codes per byte, low nibble first
+ *   k_scales f32 [batch][capacity][dim/k_group]    scale = group absmax / 6
+ * Keys finer, values coarser [P1 §3.1, §4.3]: with v_group > 0 a second plane
+ * quantises the value dims (the first dim-rope_dim) with its own group:
+ *   v_codes  u8  [batch][capacity][(dim-rope_dim)/2]
+ *   v_scales f32 [batch][capacity][(dim-rope_dim)/v_group]
+ * otherwise values are read from the key plane (v_codes/v_scales NULL).
+ * The indexer key of each entry [P2 四、"CSA2：三种模式"] is kept in bf16:
+ *   idx_keys bf16 [batch][capacity][idx_dim]
+ * Sequence state:
+ *   n_tokens i32 [batch]  tokens appended so far; entries = n_tokens / 2
+ *   pending  f32 [batch][dim]  the odd token waiting for its pair
+ *   status   i32 [1]      CSKV_STATUS_* bits, sticky until the caller clears them
+ * Supported here: dim 576, rope_dim 64, k_group 32 or 64, v_group 0, 32, 64
+ * or 128, idx_dim 64 or 128, capacity <= 2^26.
+ */
+typedef struct cskv_cache {
+    int32_t batch, capacity, dim, rope_dim, k_group, v_group, idx_dim;
+    uint8_t *k_codes;
+    float *k_scales;
+    uint8_t *v_codes;
+    float *v_scales;
+    uint16_t *idx_keys;
+    int32_t *n_tokens;
+    float *pending;
+    int32_t *status;
+} cskv_cache;
+
+/*
+ * Append new rows to every sequence of the cache [P2 三、"突破四" (every 2
+ * tokens compressed into 1 entry); P1 §3.1 (group FP4 with one scale per
+ * group); P1 §3.2 (a trained compressor maps tokens to the compressed form)].
+ *
+ * tokens   f32 [total_new][dim]; sequence b owns rows cu_new[b]..cu_new[b+1]-1.
+ * cu_new   i32 [batch+1] prefix sums, or NULL: one row per sequence
+ *          (total_new must equal batch).
+ * w_comp   f32 [dim][2*dim] stand-in compressor, or NULL.
+ *   non-NULL: rows are tokens.  Tokens pair by absolute position (2i, 2i+1);
+ *     the entry is e[r] = sum_j w_comp[r][j] * u[j] with u = x_2i || x_2i+1,
+ *     folded in fp32 from j = 0 upward with one fused multiply-add per term.
+ *     A trailing odd token waits in pending[b].  Entry i takes the indexer-key
+ *     row of token 2i+1 (the row that completes it); other key rows are unused.
+ *   NULL: rows are already entries; each adds 2 tokens.  Requires an even
+ *     n_tokens (else CSKV_STATUS_ODD_ENTRY_APPEND, sequence untouched).
+ * idx_rows bf16 [total_new][idx_dim] indexer-key rows.
+ * Quantisation per group of g channels: a = max|e|, s = a/6 (IEEE fp32
+ * division), code = E2M1 of e/s (IEEE division) rounded to nearest with ties
+ * to the even code, saturating at 6, sign = sign of e; s == 0 stores scale +0
+ * and zero codes.
+ * A sequence whose entries would pass capacity is left untouched and sets
+ * CSKV_STATUS_OVERFLOW.
+ */
+int cskv_kv_append_fp4(const cskv_cache *cache, const float *tokens, const int32_t *cu_new,
+                       int32_t total_new, const float *w_comp, const uint16_t *idx_rows,
+                       hipStream_t stream);
+
+/*
+ * Write sliding-window rows [P2 三、"突破四" (each token sees the latest 128);
+ * P2 四、"CSA2：三种模式" (every layer keeps its own window)].
+ * ring     bf16 [batch][window][dim] (this layer's window, caller-owned)
+ * rows     f32 [total_new][dim], grouped by cu_new as in cskv_kv_append_fp4
+ *          (cu_new NULL: one row per sequence)
+ * end_pos  i32 [batch] token count of each sequence after these rows (e.g.
+ *          cache->n_tokens after the append).  The row at absolute position
+ *          pos goes to slot pos % window, as bf16 rounded to nearest even, if
+ *          it is among the last `window` positions; older rows are skipped.
+ */
+int cskv_swa_append(uint16_t *ring, int32_t batch, int32_t window, int32_t dim,
+                    const float *rows, const int32_t *cu_new, int32_t total_new,
+                    const int32_t *end_pos, hipStream_t stream);
+
+/*
+ * Indexer scoring and exact top-k [P2 三、"突破四" (a light indexer scores all
+ * history and attention keeps the 512 best); P2 四、"CSA2：三种模式" (per-layer
+ * indexer query, per-entry indexer key)].
+ * Sequence b scores entries j < min(n_tokens[b]/2, capacity):
+ *   s_j = sum_h w_h * max(0, sum_d q[b][h][d] * idx_keys[b][j][d])
+ * (fp32 accumulation; integer-valued bf16 inputs with |s| < 2^24 are exact).
+ * q_idx    bf16 [batch][n_idx_heads][idx_dim], 1 <= n_idx_heads <= 64
+ * head_w   f32 [batch][n_idx_heads] or NULL (all weights 1)
+ * out_idx  i32 [batch][k]: the k highest scores, ties to the lower index,
+ *          listed in ascending index order; -1 pads when fewer than k entries.
+ * 1 <= k <= 2048.  ws: device workspace of at least
+ * cskv_workspace_bytes(cache, k) bytes (contents need not be initialised).
+ */
+int cskv_indexer_topk(const cskv_cache *cache, const uint16_t *q_idx, int32_t n_idx_heads,
+                      const float *head_w, int32_t k, int32_t *out_idx, void *ws,
+                      size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Sparse + window attention of one decode step [P2 三、"突破四" (sparse global
+ * branch of 512 selected entries plus a 128-token window); P2 三、"突破二"
+ * (all heads share one latent entry); P2 四、"P4 main KV" (FP4 is only
+ * storage: entries are dequantised before attention)].
+ * For every head h of sequence b, one softmax over the keys
+ *   { dequantised entry idx[b][t] : 0 <= idx < entries } U { window slot s < swa_len[b] }
+ * with logits softmax_scale * q.k over all dim dims; out = sum p * v where
+ * v = the value plane (if present) or the first dim-rope_dim key dims;
+ * lse = natural log of sum exp(logit).  No keys: out = 0, lse = -inf.
+ * q        f32 [batch][n_heads][dim], n_heads a multiple of 16, <= 128
+ * idx      i32 [batch][k] (entries outside [0, entries) are skipped)
+ * swa      bf16 [batch][window][dim]
+ * swa_len  i32 [batch] valid window slots, or NULL: min(n_tokens, window)
+ * out      f32 [batch][n_heads][dim-rope_dim];  lse f32 [batch][n_heads] or NULL
+ */
+int cskv_sparse_attn_decode(const cskv_cache *cache, const float *q, int32_t n_heads,
+                            const int32_t *idx, int32_t k, const uint16_t *swa, int32_t window,
+                            const int32_t *swa_len, float softmax_scale, float *out, float *lse,
+                            hipStream_t stream);
+
+/* Layer modes [P2 四、"CSA2：三种模式，40 层只存 4 份"]. */
+#define CSKV_MODE_FULL 0     /* append, own indexer query, own top-k, attend        */
+#define CSKV_MODE_REINDEX 1  /* own indexer query over the shared indexer keys      */
+#define CSKV_MODE_REUSE 2    /* borrow the most recent FULL/REINDEX index list      */
+
+/* One layer of a group.  Every mode keeps its own query and its own window. */
+typedef struct cskv_layer {
+    int32_t mode;
+    const float *q;          /* f32 [batch][n_heads][dim]                        */
+    const uint16_t *q_idx;   /* bf16 [batch][n_idx_heads][idx_dim] (FULL/REINDEX) */
+    const float *head_w;     /* f32 [batch][n_idx_heads] or NULL                 */
+    uint16_t *swa;           /* bf16 [batch][window][dim] this layer's ring      */
+    const float *swa_row;    /* f32 [batch][dim] window row of the new token, or NULL */
+    int32_t *idx;            /* i32 [batch][k] written by FULL/REINDEX; unused by REUSE */
+    float *out;              /* f32 [batch][n_heads][dim-rope_dim]               */
+    float *lse;              /* f32 [batch][n_heads] or NULL                     */
+} cskv_layer;
+
+/*
+ * One decode step of a CSA2 layer group over its shared cache, layers in
+ * order, one new token per sequence [P2 四、"CSA2：三种模式"].
+ * new_tokens f32 [batch][dim] and new_idx_rows bf16 [batch][idx_dim] are
+ * appended by the first FULL layer (new_tokens NULL: no append).  Every layer
+ * with a swa_row writes it at position n_tokens-1 of its own ring.  A REUSE
+ * layer needs a FULL or REINDEX layer before it.  ws as for cskv_indexer_topk.
+ * layers is a host array.
+ */
+int cskv_layer_group_decode(const cskv_cache *cache, const cskv_layer *layers, int32_t n_layers,
+                            const float *new_tokens, const float *w_comp,
+                            const uint16_t *new_idx_rows, int32_t n_idx_heads, int32_t n_heads,
+                            int32_t k, int32_t window, float softmax_scale, void *ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* Device workspace bytes cskv_indexer_topk / cskv_layer_group_decode need. */
+size_t cskv_workspace_bytes(const cskv_cache *cache, int32_t k);
+
+/* Bytes one entry occupies across all planes (codes, scales, indexer key)
+ * [P2 四、"890 字节是怎么算出来的"]. */
+size_t cskv_entry_bytes(int32_t dim, int32_t rope_dim, int32_t k_group, int32_t v_group,
+                        int32_t idx_dim);
+
+/* Thread-local description of the last error (host string, never NULL). */
+const char *cskv_last_error(void);
+
+/*
+ * Kernel timers for measurement.  When enabled for a kernel kind, the library
+ * records a hipEvent pair around each of the next `max_launches` launches of
+ * that kind on the launch stream; cskv_timer_read waits for them and returns
+ * the summed milliseconds and the count.  Not thread-safe; meant for benches.
+ */
+#define CSKV_KERNEL_APPEND 1
+#define CSKV_KERNEL_SWA_APPEND 2
+#define CSKV_KERNEL_INDEXER_SCAN 3
+#define CSKV_KERNEL_TOPK_SELECT 4
+#define CSKV_KERNEL_ATTENTION 5
+int cskv_timer_enable(int32_t kernel_kind, int32_t max_launches);
+int cskv_timer_read(int32_t kernel_kind, double *total_ms, int32_t *count);
+int cskv_timer_disable_all(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

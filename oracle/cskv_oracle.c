@@ -163,25 +163,33 @@ static void store_entry(orc_cache *c, int b, int64_t i, const float *e, const ui
     memcpy(c->idx_keys + row * c->idx_dim, idx_row, sizeof(uint16_t) * (size_t)c->idx_dim);
 }
 
+static void raise_status(orc_cache *c, int32_t bit)
+{
+    #pragma omp atomic
+    c->status[0] |= bit;
+}
+
 void orc_kv_append(orc_cache *c, const float *tokens, const int32_t *cu_new,
                    const float *w_comp, const uint16_t *idx_rows)
 {
     const int D = c->dim;
-    float *e = (float *)malloc(sizeof(float) * (size_t)D);
+    /* sequences are independent: each touches only its own rows and state */
+    #pragma omp parallel for schedule(dynamic, 1)
     for (int b = 0; b < c->batch; ++b) {
+        float *e = (float *)malloc(sizeof(float) * (size_t)D);
         int64_t p = c->n_tokens[b];
         int64_t m = cu_new[b + 1] - cu_new[b];
         const float *rows = tokens + (size_t)cu_new[b] * D;
         const uint16_t *irows = idx_rows + (size_t)cu_new[b] * c->idx_dim;
-        if (m == 0) continue;
+        if (m == 0) { free(e); continue; }
         if (w_comp == NULL) {
-            if (p % 2 != 0) { c->status[0] |= ORC_STATUS_ODD_ENTRY_APPEND; continue; }
-            if (p / 2 + m > c->capacity) { c->status[0] |= ORC_STATUS_OVERFLOW; continue; }
+            if (p % 2 != 0) { raise_status(c, ORC_STATUS_ODD_ENTRY_APPEND); free(e); continue; }
+            if (p / 2 + m > c->capacity) { raise_status(c, ORC_STATUS_OVERFLOW); free(e); continue; }
             for (int64_t q = 0; q < m; ++q)
                 store_entry(c, b, p / 2 + q, rows + q * D, irows + q * c->idx_dim);
             c->n_tokens[b] = (int32_t)(p + 2 * m);
         } else {
-            if ((p + m) / 2 > c->capacity) { c->status[0] |= ORC_STATUS_OVERFLOW; continue; }
+            if ((p + m) / 2 > c->capacity) { raise_status(c, ORC_STATUS_OVERFLOW); free(e); continue; }
             for (int64_t q = 0; q < m; ++q) {
                 int64_t pos = p + q;
                 if (pos % 2 == 0) continue;            /* first half of a pair */
@@ -193,8 +201,8 @@ void orc_kv_append(orc_cache *c, const float *tokens, const int32_t *cu_new,
                 memcpy(c->pending + (size_t)b * D, rows + (m - 1) * D, sizeof(float) * (size_t)D);
             c->n_tokens[b] = (int32_t)(p + m);
         }
+        free(e);
     }
-    free(e);
 }
 
 void orc_swa_append(uint16_t *ring, int batch, int W, int dim, const float *rows,

@@ -1,0 +1,68 @@
+"""Helpers shared by the GPU parity tests: move seeded inputs to the device,
+mirror a device cache on the host, and the attention tolerance check."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import compressed_sparse_kv_append_amd as ck
+import oracle as orc
+
+TOL = 2e-3   # max_i |o_i - r_i| / max_i |r_i| per (sequence, head) row
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    a = t.detach().cpu().numpy()
+    return a.view(np.uint16) if a.dtype == np.int16 else a
+
+
+def pair(batch, capacity, k_group, v_group, idx_dim):
+    """An empty device cache and its empty host mirror with the same shape."""
+    g = ck.Cache.allocate(batch, capacity, k_group, v_group, idx_dim)
+    h = orc.Cache.empty(batch, capacity, 576, 64, k_group, v_group, idx_dim)
+    return g, h
+
+
+def assert_cache_equal(g: ck.Cache, h: orc.Cache, seqs=None, check_pending=True):
+    torch.cuda.synchronize()
+    seqs = list(range(h.batch)) if seqs is None else list(seqs)
+    nt = host(g.n_tokens)
+    assert np.array_equal(nt[seqs], h.n_tokens[seqs]), (nt[seqs], h.n_tokens[seqs])
+    for b in seqs:
+        e = int(min(h.n_tokens[b] // 2, h.capacity))
+        for name in ("k_codes", "k_scales", "v_codes", "v_scales", "idx_keys"):
+            gt = getattr(g, name)
+            if gt is None:
+                continue
+            ga = host(gt[b, :e])
+            ha = getattr(h, name)[b, :e]
+            if not np.array_equal(ga.view(np.uint8), ha.view(np.uint8)):
+                bad = np.argwhere(ga.view(np.uint8).reshape(e, -1) != ha.view(np.uint8).reshape(e, -1))
+                raise AssertionError(f"{name} differs for sequence {b}: first at {bad[:5].tolist()}")
+        if check_pending and h.n_tokens[b] % 2 == 1:
+            assert np.array_equal(host(g.pending[b]), h.pending[b]), f"pending differs, seq {b}"
+    assert int(host(g.status)[0]) == int(h.status[0])
+
+
+def attn_rel_err(out: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per-row max abs error over max abs reference value."""
+    num = np.abs(out.astype(np.float64) - ref).max(axis=-1)
+    den = np.abs(ref).max(axis=-1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1), num)
+
+
+def load_entries(g: ck.Cache, h: orc.Cache, entries_per_seq, idx_keys_per_seq):
+    """Entries-mode append of per-sequence rows on both sides."""
+    lens = [len(e) for e in entries_per_seq]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    rows = np.concatenate(entries_per_seq).astype(np.float32)
+    keys = np.concatenate(idx_keys_per_seq).astype(np.uint16)
+    ck.kv_append_fp4(g, dev(rows), dev(cu), None, dev(keys))
+    orc.kv_append(h, rows, cu, None, keys)
