@@ -1,0 +1,115 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/cskv.h declares, and its host-only parts (byte helpers, argument
+checks that reject a call before anything is enqueued) behave as declared.
+No call here reaches a kernel launch."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import compressed_sparse_kv_append_amd as ck
+from compressed_sparse_kv_append_amd import _build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cskv.h")
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cskv_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_build.LIB):
+        pytest.fail(f"{_build.LIB} not built: run __graft_entry__.build() first")
+    return ck.lib()
+
+
+def test_every_declared_function_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 10, names
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, f"declared in cskv.h but not exported: {missing}"
+    assert set(ck.EXPORTS) <= set(names), set(ck.EXPORTS) - set(names)
+
+
+def test_entry_bytes(L):
+    # 576 dims: 288 code bytes + 4 B per group scale + 2 B per indexer-key dim
+    assert ck.entry_bytes(576, 64, 32, 0, 128) == 288 + 72 + 256
+    assert ck.entry_bytes(576, 64, 64, 0, 128) == 288 + 36 + 256
+    # split value plane: 512 dims at group 128 adds 256 + 16
+    assert ck.entry_bytes(576, 64, 32, 128, 128) == 288 + 72 + 256 + 256 + 16
+    assert ck.entry_bytes(576, 64, 100, 0, 128) == 0   # group must divide dim
+
+
+def _desc(**over):
+    d = dict(batch=2, capacity=64, dim=576, rope_dim=64, k_group=32, v_group=0, idx_dim=64,
+             k_codes=0x10000, k_scales=0x20000, v_codes=None, v_scales=None, idx_keys=0x30000,
+             n_tokens=0x40000, pending=0x50000, status=0x60000)
+    d.update(over)
+    return ck.CacheDesc(*[d[f] for f, _ in ck.CacheDesc._fields_])
+
+
+def _err(L):
+    return L.cskv_last_error().decode()
+
+
+@pytest.mark.parametrize("over,code,text", [
+    (dict(dim=512), ck.EUNSUPPORTED, "dim"),
+    (dict(k_group=128), ck.EUNSUPPORTED, "k_group"),
+    (dict(v_group=48), ck.EUNSUPPORTED, "v_group"),
+    (dict(idx_dim=96), ck.EUNSUPPORTED, "idx_dim"),
+    (dict(batch=0), ck.EINVAL, "batch"),
+    (dict(capacity=0), ck.EINVAL, "capacity"),
+    (dict(k_codes=None), ck.EINVAL, "NULL"),
+    (dict(k_scales=0x20004), ck.EINVAL, "aligned"),
+    (dict(v_group=128), ck.EINVAL, "value plane"),
+])
+def test_cache_descriptor_rejected_before_launch(L, over, code, text):
+    d = _desc(**over)
+    rc = L.cskv_kv_append_fp4(C.byref(d), C.c_void_p(0x70000), None, 2, None,
+                              C.c_void_p(0x80000), None)
+    assert rc == code and text in _err(L), (rc, _err(L))
+    assert L.cskv_workspace_bytes(C.byref(d), 512) == 0
+
+
+def test_call_arguments_rejected_before_launch(L):
+    d = _desc()
+    vp = C.c_void_p
+    # cu_new NULL needs one row per sequence
+    assert L.cskv_kv_append_fp4(C.byref(d), vp(0x70000), None, 3, None, vp(0x80000), None) == ck.EINVAL
+    # top-k: k out of range, too many heads, workspace too small
+    ws = L.cskv_workspace_bytes(C.byref(d), 512)
+    assert ws > 0
+    out = vp(0x90000)
+    assert L.cskv_indexer_topk(C.byref(d), vp(0xA0000), 4, None, 0, out, vp(0xB0000), ws, None) == ck.EUNSUPPORTED
+    assert L.cskv_indexer_topk(C.byref(d), vp(0xA0000), 65, None, 512, out, vp(0xB0000), ws, None) == ck.EUNSUPPORTED
+    assert L.cskv_indexer_topk(C.byref(d), vp(0xA0000), 4, None, 512, out, vp(0xB0000), ws - 1, None) == ck.EWORKSPACE
+    assert L.cskv_indexer_topk(C.byref(d), vp(0xA0000), 4, None, 512, out, None, ws, None) == ck.EWORKSPACE
+    # attention: heads not a multiple of 16, missing window
+    assert L.cskv_sparse_attn_decode(C.byref(d), vp(0xC0000), 24, vp(0xD0000), 512, vp(0xE0000), 128,
+                                     None, C.c_float(0.04), vp(0xF0000), None, None) == ck.EUNSUPPORTED
+    assert L.cskv_sparse_attn_decode(C.byref(d), vp(0xC0000), 16, vp(0xD0000), 512, None, 128,
+                                     None, C.c_float(0.04), vp(0xF0000), None, None) == ck.EINVAL
+    # window append: dim not a multiple of 4
+    assert L.cskv_swa_append(vp(0x100000), 2, 128, 578, vp(0x70000), None, 2, vp(0x40000), None) == ck.EUNSUPPORTED
+
+
+def test_layer_group_checks_every_layer_first(L):
+    d = _desc()
+    vp = C.c_void_p
+    ws = L.cskv_workspace_bytes(C.byref(d), 512)
+    # a REUSE layer with no FULL/REINDEX before it is rejected before anything runs
+    layers = (ck.LayerDesc * 2)()
+    layers[0] = ck.LayerDesc(ck.MODE_REUSE, 0xC0000, None, None, 0x100000, None, None, 0xF0000, None)
+    layers[1] = ck.LayerDesc(ck.MODE_FULL, 0xC0000, 0xA0000, None, 0x100000, None, 0x90000, 0xF0000, None)
+    rc = L.cskv_layer_group_decode(C.byref(d), layers, 2, None, None, None, 4, 16, 512, 128,
+                                   C.c_float(0.04), vp(0xB0000), ws, None)
+    assert rc == ck.EINVAL and "REUSE" in _err(L)
+    layers[0].mode = 7
+    rc = L.cskv_layer_group_decode(C.byref(d), layers, 2, None, None, None, 4, 16, 512, 128,
+                                   C.c_float(0.04), vp(0xB0000), ws, None)
+    assert rc == ck.EINVAL and "mode" in _err(L)
