@@ -192,7 +192,7 @@ def main():
                              idx=torch.empty(B, w.topk, dtype=torch.int32, device="cuda"),
                              out=torch.empty(B, w.q_heads, w.vdim, device="cuda"),
                              lse=torch.empty(B, w.q_heads, device="cuda"))],
-            ws=ck.workspace(reps[r], w.topk)))
+            ws=ck.workspace(reps[r], w.topk, ck.OP_LAYER_GROUP, w.q_heads, w.window)))
     tok, irow = dev(st.token), dev(st.idx_row)
 
     def step(i):

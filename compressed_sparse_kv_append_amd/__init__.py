@@ -31,8 +31,9 @@ STATUS_BAD_STATE = 4
 MODE_FULL, MODE_REINDEX, MODE_REUSE = 0, 1, 2
 MODES = {"full": MODE_FULL, "reindex": MODE_REINDEX, "reuse": MODE_REUSE}
 KERNEL_APPEND, KERNEL_SWA_APPEND, KERNEL_INDEXER_SCAN, KERNEL_TOPK_SELECT, KERNEL_ATTENTION = 1, 2, 3, 4, 5
+OP_INDEXER_TOPK, OP_SPARSE_ATTN, OP_LAYER_GROUP = 1, 2, 3
 
-EXPORTS = ("cskv_kv_append_fp4", "cskv_swa_append", "cskv_indexer_topk", "cskv_sparse_attn_decode",
+EXPORTS = ("cskv_kv_append_fp4", "cskv_append_workspace_bytes", "cskv_swa_append", "cskv_indexer_topk", "cskv_sparse_attn_decode",
            "cskv_layer_group_decode", "cskv_workspace_bytes", "cskv_entry_bytes", "cskv_last_error",
            "cskv_timer_enable", "cskv_timer_read", "cskv_timer_disable_all")
 
@@ -70,13 +71,16 @@ def lib():
                                "(python -c 'import __graft_entry__ as g; g.build()')")
         L = C.CDLL(_build.LIB)
         vp, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
-        L.cskv_kv_append_fp4.argtypes = [vp, vp, vp, i32, vp, vp, vp]
+        L.cskv_kv_append_fp4.argtypes = [vp, vp, vp, i32, vp, vp, vp, sz, vp]
+        L.cskv_append_workspace_bytes.argtypes = [i32, vp]
+        L.cskv_append_workspace_bytes.restype = sz
         L.cskv_swa_append.argtypes = [vp, i32, i32, i32, vp, vp, i32, vp, vp]
         L.cskv_indexer_topk.argtypes = [vp, vp, i32, vp, i32, vp, vp, sz, vp]
-        L.cskv_sparse_attn_decode.argtypes = [vp, vp, i32, vp, i32, vp, i32, vp, C.c_float, vp, vp, vp]
+        L.cskv_sparse_attn_decode.argtypes = [vp, vp, i32, vp, i32, vp, i32, vp, C.c_float, vp, vp, vp, sz,
+                                              vp]
         L.cskv_layer_group_decode.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, C.c_float,
                                               vp, sz, vp]
-        L.cskv_workspace_bytes.argtypes = [vp, i32]
+        L.cskv_workspace_bytes.argtypes = [vp, i32, i32, i32, i32]
         L.cskv_workspace_bytes.restype = sz
         L.cskv_entry_bytes.argtypes = [i32] * 5
         L.cskv_entry_bytes.restype = sz
@@ -164,31 +168,43 @@ class Cache:
         return entry_bytes(self.dim, self.rope_dim, self.k_group, self.v_group, self.idx_dim)
 
 
-def workspace_bytes(cache: Cache, k: int) -> int:
+def workspace_bytes(cache: Cache, k: int, op: int = OP_INDEXER_TOPK, n_heads: int = 0,
+                    window: int = 0) -> int:
     d = cache.desc()
-    n = lib().cskv_workspace_bytes(C.byref(d), k)
+    n = lib().cskv_workspace_bytes(C.byref(d), op, n_heads, k, window)
     if n == 0:
         raise CskvError(EINVAL, lib().cskv_last_error().decode())
     return int(n)
 
 
-def workspace(cache: Cache, k: int) -> torch.Tensor:
-    return torch.empty(workspace_bytes(cache, k), dtype=torch.uint8, device=cache.k_codes.device)
+def workspace(cache: Cache, k: int, op: int = OP_INDEXER_TOPK, n_heads: int = 0,
+              window: int = 0) -> torch.Tensor:
+    return torch.empty(workspace_bytes(cache, k, op, n_heads, window), dtype=torch.uint8,
+                       device=cache.k_codes.device)
 
 
 def entry_bytes(dim, rope_dim, k_group, v_group, idx_dim) -> int:
     return int(lib().cskv_entry_bytes(dim, rope_dim, k_group, v_group, idx_dim))
 
 
+def append_workspace(n_rows: int, w_comp: Optional[torch.Tensor], device="cuda") -> torch.Tensor:
+    nbytes = lib().cskv_append_workspace_bytes(n_rows, None if w_comp is None else w_comp.data_ptr())
+    return torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+
+
 def kv_append_fp4(cache: Cache, tokens: torch.Tensor, cu_new: Optional[torch.Tensor],
-                  w_comp: Optional[torch.Tensor], idx_rows: torch.Tensor, stream=None) -> None:
+                  w_comp: Optional[torch.Tensor], idx_rows: torch.Tensor, ws: Optional[torch.Tensor] = None,
+                  stream=None) -> None:
     n = tokens.shape[0]
+    if ws is None and w_comp is not None:
+        ws = append_workspace(n, w_comp, tokens.device)
     d = cache.desc()
     _check(lib().cskv_kv_append_fp4(
         C.byref(d), _ptr(tokens, F32, "tokens", (n, cache.dim)),
         _ptr(cu_new, I32, "cu_new", (cache.batch + 1,)), n,
         _ptr(w_comp, F32, "w_comp", (cache.dim, 2 * cache.dim)),
-        _ptr(idx_rows, B16, "idx_rows", (n, cache.idx_dim)), _stream(stream)))
+        _ptr(idx_rows, B16, "idx_rows", (n, cache.idx_dim)),
+        _ptr(ws, U8, "ws"), 0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def swa_append(ring: torch.Tensor, rows: torch.Tensor, cu_new: Optional[torch.Tensor],
@@ -219,7 +235,7 @@ def indexer_topk(cache: Cache, q_idx: torch.Tensor, k: int, head_w: Optional[tor
 def sparse_attn_decode(cache: Cache, q: torch.Tensor, idx: torch.Tensor, swa: torch.Tensor,
                        softmax_scale: float, swa_len: Optional[torch.Tensor] = None,
                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                       stream=None):
+                       ws: Optional[torch.Tensor] = None, stream=None):
     B, H, D = q.shape
     k = idx.shape[1]
     W = swa.shape[1]
@@ -228,13 +244,15 @@ def sparse_attn_decode(cache: Cache, q: torch.Tensor, idx: torch.Tensor, swa: to
         out = torch.empty(B, H, dv, dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(cache, k, OP_SPARSE_ATTN, H, W)
     d = cache.desc()
     _check(lib().cskv_sparse_attn_decode(
         C.byref(d), _ptr(q, F32, "q", (cache.batch, H, cache.dim)), H,
         _ptr(idx, I32, "idx", (cache.batch, k)), k, _ptr(swa, B16, "swa", (cache.batch, W, cache.dim)), W,
         _ptr(swa_len, I32, "swa_len", (cache.batch,)), float(softmax_scale),
         _ptr(out, F32, "out", (cache.batch, H, dv)), _ptr(lse, F32, "lse", (cache.batch, H)),
-        _stream(stream)))
+        _ptr(ws, U8, "ws"), ws.numel(), _stream(stream)))
     return out, lse
 
 
@@ -260,7 +278,7 @@ def layer_group_decode(cache: Cache, layers: Sequence[Layer], new_tokens: Option
     n_heads = layers[0].q.shape[1]
     n_idx_heads = next((L.q_idx.shape[1] for L in layers if L.q_idx is not None), 1)
     if ws is None:
-        ws = workspace(cache, k)
+        ws = workspace(cache, k, OP_LAYER_GROUP, n_heads, window)
     arr = (LayerDesc * len(layers))()
     for i, L in enumerate(layers):
         dv = cache.dim - cache.rope_dim

@@ -80,21 +80,34 @@ int topk_args(const cskv_cache *c, const uint16_t *q_idx, int32_t heads, int32_t
     REQUIRE(heads >= 1 && heads <= 64, CSKV_EUNSUPPORTED, "n_idx_heads %d out of [1, 64]", heads);
     REQUIRE(k >= 1 && k <= 2048, CSKV_EUNSUPPORTED, "k %d out of [1, 2048]", k);
     REQUIRE(out_idx, CSKV_EINVAL, "out_idx is NULL");
-    const size_t need = cskv::topk_workspace(*c).total;
+    const size_t need = cskv::topk_workspace(*c, k).total;
     REQUIRE(ws && aligned(ws, 256), CSKV_EWORKSPACE, "workspace NULL or not 256-byte aligned");
     REQUIRE(ws_bytes >= need, CSKV_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
     return CSKV_OK;
 }
 
-int attn_args(const float *q, int32_t heads, const int32_t *idx, bool need_idx, int32_t k,
-              const uint16_t *swa, int32_t window, const float *out)
+int attn_shape(int32_t heads, int32_t k, int32_t window)
 {
-    REQUIRE(q && out && (idx || !need_idx), CSKV_EINVAL, "q, idx or out is NULL");
     REQUIRE(heads >= 16 && heads <= 1024 && heads % 16 == 0, CSKV_EUNSUPPORTED,
             "n_heads %d: a multiple of 16 in [16, 1024]", heads);
-    REQUIRE(k >= 1 && k <= 65536, CSKV_EUNSUPPORTED, "k %d out of [1, 65536]", k);
-    REQUIRE(window >= 1 && window <= (1 << 20), CSKV_EINVAL, "window %d out of [1, 2^20]", window);
+    REQUIRE(k >= 1 && k <= 2048, CSKV_EUNSUPPORTED, "k %d out of [1, 2048]", k);
+    REQUIRE(window >= 1 && window <= 1024, CSKV_EUNSUPPORTED, "window %d out of [1, 1024]", window);
+    return CSKV_OK;
+}
+
+int attn_args(const cskv_cache *c, const float *q, int32_t heads, const int32_t *idx, bool need_idx,
+              int32_t k, const uint16_t *swa, int32_t window, const float *out, const float *lse,
+              const void *ws, size_t ws_bytes)
+{
+    REQUIRE(q && out && (idx || !need_idx), CSKV_EINVAL, "q, idx or out is NULL");
+    int rc = attn_shape(heads, k, window);
+    if (rc) return rc;
+    REQUIRE(aligned(q, 16) && aligned(out, 16) && (!idx || aligned(idx, 4)) && (!lse || aligned(lse, 4)),
+            CSKV_EINVAL, "q and out must be 16-byte aligned");
     REQUIRE(swa && aligned(swa, 16), CSKV_EINVAL, "window ring NULL or not 16-byte aligned");
+    const size_t need = cskv::attn_plan(*c, heads, k, window).ws_bytes;
+    REQUIRE(need == 0 || (ws && aligned(ws, 256)), CSKV_EWORKSPACE, "workspace NULL or not 256-byte aligned");
+    REQUIRE(ws_bytes >= need, CSKV_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
     return CSKV_OK;
 }
 
@@ -146,16 +159,44 @@ size_t cskv_entry_bytes(int32_t dim, int32_t rope_dim, int32_t k_group, int32_t 
     return b;
 }
 
-size_t cskv_workspace_bytes(const cskv_cache *cache, int32_t k)
+size_t cskv_workspace_bytes(const cskv_cache *cache, int32_t op, int32_t n_heads, int32_t k,
+                            int32_t window)
 {
-    (void)k;
     if (check_cache(cache) != CSKV_OK) return 0;
-    return cskv::topk_workspace(*cache).total;
+    size_t topk = 0, attn = 0;
+    if (op == CSKV_OP_INDEXER_TOPK || op == CSKV_OP_LAYER_GROUP) {
+        if (k < 1 || k > 2048) {
+            fail(CSKV_EUNSUPPORTED, "k %d out of [1, 2048]", k);
+            return 0;
+        }
+        topk = cskv::topk_workspace(*cache, k).total;
+    }
+    if (op == CSKV_OP_SPARSE_ATTN || op == CSKV_OP_LAYER_GROUP) {
+        if (attn_shape(n_heads, k, window) != CSKV_OK) return 0;
+        attn = cskv::attn_plan(*cache, n_heads, k, window).ws_bytes;
+    }
+    if (op < CSKV_OP_INDEXER_TOPK || op > CSKV_OP_LAYER_GROUP) {
+        fail(CSKV_EINVAL, "unknown workspace op %d", op);
+        return 0;
+    }
+    size_t need = topk > attn ? topk : attn;
+    if (op == CSKV_OP_LAYER_GROUP) {
+        const size_t app = cskv::append_workspace_bytes(cache->batch);   // one new token per sequence
+        need = need > app ? need : app;
+    }
+    return need > 256 ? need : 256;
+}
+
+size_t cskv_append_workspace_bytes(int32_t total_new, const float *w_comp)
+{
+    if (!w_comp || total_new <= 0) return 256;
+    const size_t need = cskv::append_workspace_bytes(total_new);
+    return need > 256 ? need : 256;
 }
 
 int cskv_kv_append_fp4(const cskv_cache *cache, const float *tokens, const int32_t *cu_new,
                        int32_t total_new, const float *w_comp, const uint16_t *idx_rows,
-                       hipStream_t stream)
+                       void *ws, size_t ws_bytes, hipStream_t stream)
 {
     int rc = check_cache(cache);
     if (rc) return rc;
@@ -163,7 +204,12 @@ int cskv_kv_append_fp4(const cskv_cache *cache, const float *tokens, const int32
     REQUIRE(total_new == 0 || (idx_rows && aligned(idx_rows, 4)), CSKV_EINVAL,
             "idx_rows NULL or not 4-byte aligned");
     REQUIRE(!w_comp || aligned(w_comp, 16), CSKV_EINVAL, "w_comp must be 16-byte aligned");
-    hipError_t e = cskv::launch_kv_append(*cache, tokens, cu_new, total_new, w_comp, idx_rows, stream);
+    if (w_comp && total_new > 0) {
+        const size_t need = cskv::append_workspace_bytes(total_new);
+        REQUIRE(ws && aligned(ws, 256), CSKV_EWORKSPACE, "workspace NULL or not 256-byte aligned");
+        REQUIRE(ws_bytes >= need, CSKV_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    }
+    hipError_t e = cskv::launch_kv_append(*cache, tokens, cu_new, total_new, w_comp, idx_rows, ws, stream);
     return e == hipSuccess ? CSKV_OK : hip_fail(e, "kv_append_fp4 launch");
 }
 
@@ -196,13 +242,13 @@ int cskv_indexer_topk(const cskv_cache *cache, const uint16_t *q_idx, int32_t n_
 int cskv_sparse_attn_decode(const cskv_cache *cache, const float *q, int32_t n_heads,
                             const int32_t *idx, int32_t k, const uint16_t *swa, int32_t window,
                             const int32_t *swa_len, float softmax_scale, float *out, float *lse,
-                            hipStream_t stream)
+                            void *ws, size_t ws_bytes, hipStream_t stream)
 {
     int rc = check_cache(cache);
     if (rc) return rc;
-    if ((rc = attn_args(q, n_heads, idx, true, k, swa, window, out))) return rc;
+    if ((rc = attn_args(cache, q, n_heads, idx, true, k, swa, window, out, lse, ws, ws_bytes))) return rc;
     hipError_t e = cskv::launch_sparse_attn(*cache, q, n_heads, idx, k, swa, window, swa_len,
-                                            softmax_scale, out, lse, stream);
+                                            softmax_scale, out, lse, ws, stream);
     return e == hipSuccess ? CSKV_OK : hip_fail(e, "sparse_attn_decode launch");
 }
 
@@ -223,7 +269,8 @@ int cskv_layer_group_decode(const cskv_cache *cache, const cskv_layer *layers, i
         const cskv_layer &L = layers[i];
         REQUIRE(L.mode == CSKV_MODE_FULL || L.mode == CSKV_MODE_REINDEX || L.mode == CSKV_MODE_REUSE,
                 CSKV_EINVAL, "layer %d: unknown mode %d", i, L.mode);
-        if ((rc = attn_args(L.q, n_heads, L.idx, L.mode != CSKV_MODE_REUSE, k, L.swa, window, L.out)))
+        if ((rc = attn_args(cache, L.q, n_heads, L.idx, L.mode != CSKV_MODE_REUSE, k, L.swa, window, L.out,
+                            L.lse, ws, ws_bytes)))
             return fail(rc, "layer %d: %s", i, g_error.c_str());
         REQUIRE(!L.swa_row || aligned(L.swa_row, 16), CSKV_EINVAL, "layer %d: swa_row not 16-byte aligned", i);
         if (L.mode == CSKV_MODE_REUSE) {
@@ -240,7 +287,8 @@ int cskv_layer_group_decode(const cskv_cache *cache, const cskv_layer *layers, i
     for (int i = 0; i < n_layers; ++i) {
         const cskv_layer &L = layers[i];
         if (L.mode == CSKV_MODE_FULL && new_tokens && !appended) {
-            e = cskv::launch_kv_append(*cache, new_tokens, nullptr, cache->batch, w_comp, new_idx_rows, stream);
+            e = cskv::launch_kv_append(*cache, new_tokens, nullptr, cache->batch, w_comp, new_idx_rows, ws,
+                                       stream);
             if (e != hipSuccess) return hip_fail(e, "layer group: append");
             appended = true;
         }
@@ -255,7 +303,7 @@ int cskv_layer_group_decode(const cskv_cache *cache, const cskv_layer *layers, i
             last_idx = L.idx;
         }
         e = cskv::launch_sparse_attn(*cache, L.q, n_heads, last_idx, k, L.swa, window, nullptr,
-                                     softmax_scale, L.out, L.lse, stream);
+                                     softmax_scale, L.out, L.lse, ws, stream);
         if (e != hipSuccess) return hip_fail(e, "layer group: attention");
     }
     return CSKV_OK;

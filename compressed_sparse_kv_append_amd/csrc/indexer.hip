@@ -4,14 +4,22 @@
 // indexer query, per-entry indexer key)].
 //
 // Scan: s_j = sum_h w_h * relu(q_h . K_j) is a [heads x dim] x [dim x entries]
-// contraction, run on bf16 MFMA with fp32 accumulation.  Each block streams a
-// contiguous run of one sequence's keys through LDS with coalesced 16-byte
-// loads, scores them, writes an order-preserving uint32 key per entry and adds
-// the entries to a per-sequence histogram of the keys' top 11 bits.
+// contraction, run on bf16 MFMA (16x16x32) with fp32 accumulation.  The keys
+// plane is the only large read of the decode step, so the scan is built to
+// stream it: each wave pulls 16-key tiles with coalesced, non-temporal
+// loads that write straight into its own LDS ring (no registers, no block
+// barrier), reads them back in the MFMA operand layout, and keeps the query
+// in registers.  One round of blocks covers the chip.  The only output is
+// one order-preserving uint32 key per entry.
 //
-// Select: one block per sequence finds the k-th largest key by radix passes
-// (11 + 11 + 10 bits; the first histogram comes from the scan), then writes the
-// selected indices in ascending order, taking tied keys from the lowest index.
+// Select: exact top-k per sequence by radix select on those keys.  The digit
+// windows adapt to the keys' actual range (the first window starts below the
+// common prefix of the smallest and largest key).  Work is spread over the
+// chip: a sequence is cut into slices of 4096 keys, one 4-wave block each,
+// whose local top-k lists (which must contain the global top-k) are merged by
+// one block per sequence; a sequence of at most one slice is selected
+// directly.  Each block holds its keys in LDS.  The output lists the selected indices
+// in ascending order; among equal scores the lower index wins.
 //
 // Sources cited as [P2]:
 //   P2  "DeepSeek V1 到 V4.1-Flash，单 token 的 global KV 如何从 389,000 B 压缩到 890 B的？"
@@ -24,19 +32,27 @@ static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 static size_t key_stride(const cskv_cache &c) { return align_up((size_t)c.capacity, 64); }
 
-TopkWorkspace topk_workspace(const cskv_cache &c)
+int topk_slices(const cskv_cache &c) { return (int)((c.capacity + kSliceKeys - 1) / kSliceKeys); }
+
+TopkWorkspace topk_workspace(const cskv_cache &c, int k)
 {
     TopkWorkspace w;
     w.keys_off = 0;
-    w.hist_off = align_up(sizeof(uint32_t) * key_stride(c) * (size_t)c.batch, 256);
-    w.total = align_up(w.hist_off + sizeof(uint32_t) * kHistBins * (size_t)c.batch, 256);
+    w.cand_off = align_up(sizeof(uint32_t) * key_stride(c) * (size_t)c.batch, 256);
+    const size_t slices = (size_t)topk_slices(c);
+    const size_t cand = slices > 1 ? sizeof(uint32_t) * 2 * slices * (size_t)k * c.batch : 0;
+    w.total = align_up(w.cand_off + cand, 256);
     return w;
 }
 
 namespace {
 
+// ---------------------------------------------------------------- scan
+
 constexpr int kScanThreads = 256;   // 4 waves
-constexpr int kTile = 64;           // entries per LDS tile: 16 per wave
+constexpr int kScanWaves = kScanThreads / kWave;
+constexpr int kRing = 2;            // 16-key tiles in flight per wave (LDS slots)
+constexpr int kScanBlocksPerCU = 3; // what registers (<= 168) and LDS (32 KB) allow
 
 struct ScanArgs {
     const uint16_t *keys;      // idx_keys plane
@@ -44,137 +60,170 @@ struct ScanArgs {
     const uint16_t *q;         // [B][H][Di]
     const float *head_w;       // [B][H] or null
     uint32_t *out_keys;        // [B][key_stride]
-    uint32_t *hist;            // [B][kHistBins]
     int capacity, heads, chunk;
     size_t key_stride;
 };
 
-template <int DI>
-__device__ __forceinline__ int swz(int row, int ch)
-{
-    // 16-byte chunk permutation inside a key row so that the 16 rows one MFMA
-    // operand read touches fall on distinct LDS banks.
-    return DI == 128 ? (ch ^ (row & 15)) : (ch ^ ((row >> 1) & 7));
-}
+typedef __attribute__((address_space(1))) void global_void_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-template <int DI>
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8; a field at its maximum does not wait).
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (7 << 4) | (0xF << 8); }
+constexpr int kWaitLgkm0 = 0xF | (3 << 14) | (7 << 4);
+constexpr int kNonTemporal = 2;     // cache policy of the streaming loads
+
+// One block: a run of `chunk` entries of one sequence; wave w takes 16-key
+// tiles w, w + 4, ...  MT: 16-head row tiles of the query (1..4).
+template <int DI, int MT>
 __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
 {
-    constexpr int kChunks = DI / 8;        // 16-byte chunks per key row
-    constexpr int kSteps = DI / 32;        // MFMA contraction steps
-    __shared__ u32x4_t tile[kTile * kChunks];
-    __shared__ uint32_t hist[kHistBins];
+    constexpr int kSteps = DI / 32;            // MFMA contraction steps per key
+    constexpr int kRowBytes = 2 * DI;
+    constexpr int kChunks = kRowBytes / 16;    // 16-byte chunks per key row
+    constexpr int kTileBytes = 16 * kRowBytes;
+    constexpr int kInst = kTileBytes / 1024;   // loads per tile (64 lanes x 16 B)
+    __shared__ __attribute__((aligned(16))) uint8_t ring[kScanWaves][kRing][kTileBytes];
 
     const int b = blockIdx.y;
     const int64_t E = entries_of(a.n_tokens, b, a.capacity);
     const int64_t e_begin = (int64_t)blockIdx.x * a.chunk;
     if (e_begin >= E) return;
     const int64_t e_end = E < e_begin + a.chunk ? E : e_begin + a.chunk;
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    const int col = lane & 15, grp = lane >> 4;
 
-    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
-    for (int i = t; i < kHistBins; i += kScanThreads) hist[i] = 0;
-
-    // Indexer query as MFMA A operands: row = head (16 per tile), held for the
-    // whole block.  Missing heads (H not a multiple of 16) are zero rows.
-    const int mtiles = (a.heads + 15) / 16;
-    u32x4_t qa[4][kSteps];
-    float hw[4][4];
+    // Indexer query as MFMA A operands: row = head, contraction slots
+    // 8*grp..8*grp+7 of each 32-dim step.  Missing heads: zero rows, weight 0.
+    u32x4_t qa[MT][kSteps];
+    float hw[MT][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        const int head = 16 * mt + (lane & 15);
+    for (int mt = 0; mt < MT; ++mt) {
+        const int head = 16 * mt + col;
 #pragma unroll
         for (int s = 0; s < kSteps; ++s) {
             u32x4_t v = {0u, 0u, 0u, 0u};
-            if (mt < mtiles && head < a.heads)
-                v = *reinterpret_cast<const u32x4_t *>(
-                    a.q + ((size_t)b * a.heads + head) * DI + 32 * s + 8 * (lane >> 4));
+            if (head < a.heads)
+                v = *reinterpret_cast<const u32x4_t *>(a.q + ((size_t)b * a.heads + head) * DI + 32 * s + 8 * grp);
             qa[mt][s] = v;
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int hrow = 16 * mt + 4 * (lane >> 4) + v;
+            const int hrow = 16 * mt + 4 * grp + v;
             hw[mt][v] = hrow < a.heads ? (a.head_w ? a.head_w[(size_t)b * a.heads + hrow] : 1.0f) : 0.0f;
         }
     }
 
+    const int n_tiles = (int)((e_end - e_begin + 15) / 16);
+    const int my_n = n_tiles > w ? (n_tiles - w + kScanWaves - 1) / kScanWaves : 0;
     const uint8_t *kb = reinterpret_cast<const uint8_t *>(a.keys + (size_t)b * a.capacity * DI);
     uint32_t *ok = a.out_keys + (size_t)b * a.key_stride;
-    for (int64_t t0 = e_begin; t0 < e_end; t0 += kTile) {
-        __syncthreads();   // previous tile fully consumed (and hist zeroed on entry)
-        for (int ci = t; ci < kTile * kChunks; ci += kScanThreads) {
-            const int row = ci / kChunks, ch = ci % kChunks;
-            const int64_t e = t0 + row;
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (e < e_end) v = *reinterpret_cast<const u32x4_t *>(kb + (size_t)e * (2 * DI) + 16 * ch);
-            tile[row * kChunks + swz<DI>(row, ch)] = v;
-        }
-        __syncthreads();
-        const int row = 16 * w + (lane & 15);
-        f32x4_t acc[4];
+
+    // Tile i goes straight from HBM into LDS slot i % kRing with coalesced
+    // 16-byte loads (instruction s covers bytes 1024 s .. 1024 s + 1023 of the
+    // tile's 16 contiguous rows).  Lane l's bytes land at slot offset
+    // 1024 s + 16 l; the lane fetches the chunk that belongs there under an
+    // XOR swizzle (chunk c of row r at position c ^ (r % kChunks)), which
+    // makes the operand reads below bank-conflict free.  Rows past the end
+    // re-read the last valid row; their scores are dropped.
+    auto issue = [&](int i) {
+        const int64_t t0 = e_begin + (int64_t)(w + kScanWaves * i) * 16;
+        uint8_t *slot = &ring[w][i % kRing][0];
+        const bool tail = t0 + 16 > e_end;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < kInst; ++s) {
+            const int u = 64 * s + lane, r = u / kChunks, p = u % kChunks, c = p ^ (r % kChunks);
+            int64_t e = t0 + r;
+            if (tail) e = e < e_end ? e : e_end - 1;
+            __builtin_amdgcn_global_load_lds((global_void_t *)(kb + (size_t)e * kRowBytes + 16 * c),
+                                             (lds_void_t *)(slot + 1024 * s), 16, 0, kNonTemporal);
+        }
+    };
+
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) issue(i);
+    for (int i = 0; i < my_n; ++i) {
+        // tile i has landed once at most the later tiles' loads are pending
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kInst * (kRing - 1)));
+        const uint8_t *slot = &ring[w][i % kRing][0];
+        u32x4_t bop[kSteps];
 #pragma unroll
         for (int s = 0; s < kSteps; ++s) {
-            const u32x4_t bop = tile[row * kChunks + swz<DI>(row, 4 * s + (lane >> 4))];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                if (mt < mtiles) acc[mt] = mfma16x16x32(qa[mt][s], bop, acc[mt]);
+            const int p = (4 * s + grp) ^ (col % kChunks);
+            bop[s] = *reinterpret_cast<const u32x4_t *>(slot + 16 * (col * kChunks + p));
         }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);      // slot read before it is refilled
+        issue(i + kRing);
+        f32x4_t acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16x16x32(qa[mt][s], bop[s], acc[mt]);
         float part = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int v = 0; v < 4; ++v) part += hw[mt][v] * fmaxf(acc[mt][v], 0.f);
         part += __shfl_xor(part, 16);
         part += __shfl_xor(part, 32);
-        const int64_t e = t0 + row;
-        if (lane < 16 && e < e_end) {
-            const uint32_t key = score_key(part);
-            ok[e] = key;
-            atomicAdd(&hist[key >> 21], 1u);
-        }
+        const int64_t e = e_begin + (int64_t)(w + kScanWaves * i) * 16 + lane;
+        if (lane < 16 && e < e_end) ok[e] = score_key(part);
     }
-    __syncthreads();
-    uint32_t *gh = a.hist + (size_t)b * kHistBins;
-    for (int i = t; i < kHistBins; i += kScanThreads)
-        if (hist[i]) atomicAdd(&gh[i], hist[i]);
-}
-
-__global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t *p, size_t n)
-{
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-        p[i] = 0u;
+    // no LDS write may land after the block's LDS is handed to another block
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
 // ---------------------------------------------------------------- select
 
-constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / kWave;
-constexpr int kCandMax = 6144;
-constexpr int kPer = 4;                       // elements per thread per sweep
-constexpr int kSweep = kSelThreads * kPer;
+constexpr int kBins = 2048;
+constexpr int kDigit = 11;
+constexpr int kSliceThreads = 256;                      // slice blocks: 4 waves
+constexpr int kSlicePer = kSliceKeys / kSliceThreads;   // keys per thread in a slice (16)
+constexpr int kMergeThreads = 256;
+constexpr int kMergePer = 36;                           // candidates per thread per merge round
+
+// Items of one selection, in ascending index order: a contiguous key array
+// (the item at position p has index base + p; positions < n are valid), or
+// the concatenated candidate lists of the slices of one sequence (k (key,
+// index) pairs per slice; unused slots hold key 0 and are never valid).
+// Key 0 is the key of a score whose bits are all ones (a NaN), which the
+// scan cannot produce from finite inputs.
+struct Items {
+    const uint32_t *keys;   // contiguous mode
+    const uint2 *pairs;     // list mode
+    int64_t n;              // positions
+    int64_t base;           // contiguous mode: index of position 0
+};
 
 struct SelectArgs {
-    const uint32_t *keys;
-    const uint32_t *hist;
+    const uint32_t *keys;   // [B][key_stride]
+    uint2 *cand;            // [B][slices][k] (key, index) pairs
     const int32_t *n_tokens;
-    int32_t *out;
-    int capacity, k;
+    int32_t *out;           // [B][k]
+    int capacity, k, slices;
     size_t key_stride;
 };
 
+template <int THREADS, int PER>
 struct SelectSmem {
-    uint32_t bins[kHistBins];
-    uint32_t cand_key[kCandMax];
-    int32_t cand_idx[kCandMax];
-    uint32_t wave_sum[kSelWaves];
-    uint32_t found[4];
+    static constexpr int kRound = PER * THREADS;
+    static constexpr int kWaves = THREADS / kWave;
+    uint32_t keys[kRound];      // the round's keys
+    uint32_t bins[kBins];
+    uint32_t wave_sum[kWaves];
+    uint32_t red[2][kWaves];
+    uint32_t found[2];
 };
 
 // Inclusive prefix sum over the block; *total receives the block sum.
+template <int THREADS>
 __device__ uint32_t block_scan(uint32_t v, uint32_t *wave_sum, uint32_t *total)
 {
+    constexpr int kWaves = THREADS / kWave;
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+#pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
         const uint32_t n = __shfl_up(v, off);
         if (lane >= off) v += n;
@@ -182,182 +231,289 @@ __device__ uint32_t block_scan(uint32_t v, uint32_t *wave_sum, uint32_t *total)
     if (lane == kWave - 1) wave_sum[w] = v;
     __syncthreads();
     if (w == 0) {
-        uint32_t x = lane < kSelWaves ? wave_sum[lane] : 0u;
-        for (int off = 1; off < kSelWaves; off <<= 1) {
+        uint32_t x = lane < kWaves ? wave_sum[lane] : 0u;
+#pragma unroll
+        for (int off = 1; off < kWaves; off <<= 1) {
             const uint32_t n = __shfl_up(x, off);
             if (lane >= off) x += n;
         }
-        if (lane < kSelWaves) wave_sum[lane] = x;
+        if (lane < kWaves) wave_sum[lane] = x;
     }
     __syncthreads();
     const uint32_t base = w ? wave_sum[w - 1] : 0u;
-    *total = wave_sum[kSelWaves - 1];
+    *total = wave_sum[kWaves - 1];
     __syncthreads();
     return v + base;
 }
 
-// Over a histogram of n bins held in sm.bins, find the highest bin t with
-// (count of bins above t) < need <= (count of bins >= t).  Returns t and the
-// count strictly above it.
-__device__ void find_threshold_bin(SelectSmem &sm, int n, uint32_t need, uint32_t *bin,
-                                   uint32_t *above)
+// Over the histogram in sm.bins (nbins <= 2048), the highest bin t with
+// (count above t) < need <= (count at or above t).  Returns t and the count
+// strictly above it.  Requires need <= total count.
+template <int THREADS, class Smem>
+__device__ void find_threshold_bin(Smem &sm, int nbins, uint32_t need, uint32_t *bin, uint32_t *above)
 {
+    constexpr int kOwn = kBins / THREADS;         // bins per thread, in descending order
     const int t = threadIdx.x;
-    // thread t owns bins n-1-2t and n-2-2t (descending order)
-    const int b0 = n - 1 - 2 * t, b1 = n - 2 - 2 * t;
-    const uint32_t c0 = b0 >= 0 ? sm.bins[b0] : 0u, c1 = b1 >= 0 ? sm.bins[b1] : 0u;
+    uint32_t c[kOwn], sum = 0;
+#pragma unroll
+    for (int j = 0; j < kOwn; ++j) {
+        const int bn = nbins - 1 - kOwn * t - j;
+        c[j] = bn >= 0 ? sm.bins[bn] : 0u;
+        sum += c[j];
+    }
     uint32_t total;
-    const uint32_t incl = block_scan(c0 + c1, sm.wave_sum, &total);
-    const uint32_t before = incl - c0 - c1;
-    if (before < need && need <= before + c0) { sm.found[0] = (uint32_t)b0; sm.found[1] = before; }
-    if (before + c0 < need && need <= incl && b1 >= 0) { sm.found[0] = (uint32_t)b1; sm.found[1] = before + c0; }
+    uint32_t run = block_scan<THREADS>(sum, sm.wave_sum, &total) - sum;
+#pragma unroll
+    for (int j = 0; j < kOwn; ++j) {
+        const int bn = nbins - 1 - kOwn * t - j;
+        if (bn >= 0 && run < need && need <= run + c[j]) { sm.found[0] = (uint32_t)bn; sm.found[1] = run; }
+        run += c[j];
+    }
     __syncthreads();
     *bin = sm.found[0];
     *above = sm.found[1];
     __syncthreads();
 }
 
-// Elements come either from the candidate list in LDS or straight from the
-// key array in global memory; both are visited in ascending index order.
-struct FromLds {
-    const SelectSmem *sm;
-    int64_t n;
-    __device__ uint32_t key(int64_t i) const { return sm->cand_key[i]; }
-    __device__ int32_t index(int64_t i) const { return sm->cand_idx[i]; }
-};
-struct FromGlobal {
-    const uint32_t *keys;
-    int64_t n;
-    __device__ uint32_t key(int64_t i) const { return keys[i]; }
-    __device__ int32_t index(int64_t i) const { return (int32_t)i; }
-};
-
-// Histogram of `bits`-bit digit at `shift` over elements whose key >> (shift+bits)
-// equals prefix.
-template <class Src>
-__device__ void digit_histogram(SelectSmem &sm, const Src &src, int shift, int bits, uint32_t prefix)
+// Copy the keys of round r into LDS; positions past the end hold 0.  Ends
+// with a barrier.
+template <bool kList, int THREADS, int PER>
+__device__ void load_round(SelectSmem<THREADS, PER> &sm, const Items &it, int64_t r)
 {
-    const int nb = 1 << bits;
-    for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) sm.bins[i] = 0;
-    __syncthreads();
-    for (int64_t i = threadIdx.x; i < src.n; i += kSelThreads) {
-        const uint32_t k = src.key(i);
-        if ((k >> (shift + bits)) == prefix) atomicAdd(&sm.bins[(k >> shift) & (nb - 1)], 1u);
+    constexpr int kRound = SelectSmem<THREADS, PER>::kRound;
+    const int64_t p0 = r * kRound;
+    __syncthreads();                            // previous round fully consumed
+    if (!kList) {
+        constexpr int kVec = kRound / 4 / THREADS;   // uint4 per thread
+        uint4 v[kVec];
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+            const int64_t p = p0 + 4 * ((int64_t)threadIdx.x + (int64_t)THREADS * j);
+            v[j] = make_uint4(0u, 0u, 0u, 0u);
+            if (p + 3 < it.n) {
+                v[j] = *reinterpret_cast<const uint4 *>(it.keys + p);
+            } else {
+                if (p + 0 < it.n) v[j].x = it.keys[p + 0];
+                if (p + 1 < it.n) v[j].y = it.keys[p + 1];
+                if (p + 2 < it.n) v[j].z = it.keys[p + 2];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kVec; ++j)
+            reinterpret_cast<uint4 *>(sm.keys)[threadIdx.x + THREADS * j] = v[j];
+    } else {
+        uint32_t v[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int64_t p = p0 + threadIdx.x + (int64_t)THREADS * j;
+            v[j] = p < it.n ? it.pairs[p].x : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < PER; ++j) sm.keys[threadIdx.x + THREADS * j] = v[j];
     }
     __syncthreads();
 }
 
-// Exact threshold T (the k-th largest key) and the number of keys above it,
-// given the first-pass bin t1 and the count above that bin.
-template <class Src>
-__device__ void refine_threshold(SelectSmem &sm, const Src &src, uint32_t t1, uint32_t above1,
-                                 uint32_t k, uint32_t *T, uint32_t *above)
+// Validity of the item at LDS slot i of a round holding nr positions.
+template <bool kList>
+__device__ __forceinline__ bool slot_valid(uint32_t x, int i, int64_t nr)
 {
-    uint32_t t2, a2, t3, a3;
-    digit_histogram(sm, src, 10, 11, t1);
-    find_threshold_bin(sm, 2048, k - above1, &t2, &a2);
-    const uint32_t p2 = (t1 << 11) | t2;
-    digit_histogram(sm, src, 0, 10, p2);
-    find_threshold_bin(sm, 1024, k - above1 - a2, &t3, &a3);
-    *T = (p2 << 10) | t3;
-    *above = above1 + a2 + a3;
+    return kList ? x != 0u : (int64_t)i < nr;
 }
 
-// Write, in ascending index order, every element with key > T and the first
-// `ties` elements with key == T.
-template <class Src>
-__device__ void emit_selected(SelectSmem &sm, const Src &src, uint32_t T, uint32_t ties,
-                              int32_t *out, int k)
+// Exact top-k of `it`, which holds more than k valid items.  kPairsOut: write
+// the selected (key, index) pairs in index order; else the indices.  Exactly
+// k items are selected, so nothing is padded.
+template <bool kList, bool kPairsOut, int THREADS, int PER>
+__device__ void select_topk(SelectSmem<THREADS, PER> &sm, const Items &it, int k, int32_t *out_idx,
+                            uint2 *out_pairs)
 {
-    uint32_t tie_base = 0, sel_base = 0;
-    for (int64_t s0 = 0; s0 < src.n; s0 += kSweep) {
-        uint32_t key[kPer];
-        int32_t idx[kPer];
-        uint32_t nt = 0;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int64_t e = s0 + (int64_t)threadIdx.x * kPer + i;
-            const bool in = e < src.n;
-            key[i] = in ? src.key(e) : 0u;
-            idx[i] = in ? src.index(e) : -1;
-            nt += (in && key[i] == T) ? 1u : 0u;
-        }
-        uint32_t tot_t;
-        uint32_t tie_pos = tie_base + block_scan(nt, sm.wave_sum, &tot_t) - nt;
-        bool sel[kPer];
-        uint32_t ns = 0;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const bool in = idx[i] >= 0;
-            bool s = in && key[i] > T;
-            if (in && key[i] == T) { s = tie_pos < ties; ++tie_pos; }
-            sel[i] = s;
-            ns += s ? 1u : 0u;
-        }
-        uint32_t tot_s;
-        uint32_t pos = sel_base + block_scan(ns, sm.wave_sum, &tot_s) - ns;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i)
-            if (sel[i]) { if (pos < (uint32_t)k) out[pos] = idx[i]; ++pos; }
-        tie_base += tot_t;
-        sel_base += tot_s;
-    }
-    for (int i = (int)sel_base + threadIdx.x; i < k; i += kSelThreads) out[i] = -1;
-}
+    typedef SelectSmem<THREADS, PER> Smem;
+    constexpr int kRound = Smem::kRound;
+    constexpr int kWaves = Smem::kWaves;
+    const int t = threadIdx.x;
+    const int64_t rounds = (it.n + kRound - 1) / kRound;
+    if (rounds == 1) load_round<kList>(sm, it, 0);
+    auto round_n = [&](int64_t r) { return it.n - r * kRound < kRound ? it.n - r * kRound : (int64_t)kRound; };
 
-__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectArgs a)
-{
-    __shared__ SelectSmem sm;
-    const int b = blockIdx.x, t = threadIdx.x;
-    const int64_t E = entries_of(a.n_tokens, b, a.capacity);
-    int32_t *out = a.out + (size_t)b * a.k;
-    const uint32_t *keys = a.keys + (size_t)b * a.key_stride;
-    if (E <= a.k) {
-        for (int i = t; i < a.k; i += kSelThreads) out[i] = i < E ? i : -1;
-        return;
+    // ---- range of the valid keys
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for (int64_t r = 0; r < rounds; ++r) {
+        if (rounds > 1) load_round<kList>(sm, it, r);
+        const int64_t nr = round_n(r);
+        for (int i = t; i < nr; i += THREADS) {
+            const uint32_t x = sm.keys[i];
+            const bool v = slot_valid<kList>(x, i, nr);
+            lo = min(lo, v ? x : 0xFFFFFFFFu);
+            hi = max(hi, v ? x : 0u);
+        }
     }
-    // pass 1: top 11 bits, histogram built by the scan
-    for (int i = t; i < kHistBins; i += kSelThreads) sm.bins[i] = a.hist[(size_t)b * kHistBins + i];
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
+    }
+    if ((t & (kWave - 1)) == 0) { sm.red[0][t / kWave] = lo; sm.red[1][t / kWave] = hi; }
     __syncthreads();
-    uint32_t t1, above1;
-    find_threshold_bin(sm, kHistBins, (uint32_t)a.k, &t1, &above1);
-    const uint32_t floor_key = t1 << 21;
-
-    // ordered compaction of every key in bins >= t1 into the candidate list
-    uint32_t base = 0;
-    for (int64_t s0 = 0; s0 < E; s0 += kSweep) {
-        uint32_t key[kPer];
-        uint32_t n = 0;
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int64_t e = s0 + (int64_t)t * kPer + i;
-            key[i] = e < E ? keys[e] : 0u;
-            n += (e < E && key[i] >= floor_key) ? 1u : 0u;
+    for (int i = 0; i < kWaves; ++i) { lo = min(lo, sm.red[0][i]); hi = max(hi, sm.red[1][i]); }
+
+    // ---- radix passes: digit windows below the common prefix of lo and hi
+    uint32_t T = lo, above = 0;          // the k-th largest key, items above it
+    if (lo != hi) {
+        const int top = 32 - __clz((int)(lo ^ hi));      // bits [0, top) still vary
+        int shift = top > kDigit ? top - kDigit : 0;
+        uint32_t sub = lo >> shift;                      // first window: offset from lo
+        int pshift = 32;
+        uint32_t prefix = 0;
+        uint32_t mask = kBins - 1;
+        uint32_t need = (uint32_t)k;
+        while (true) {
+            const int nbins = pshift >= 32 ? kBins : 1 << (pshift - shift);
+            for (int i = t; i < kBins; i += THREADS) sm.bins[i] = 0u;
+            __syncthreads();
+            for (int64_t r = 0; r < rounds; ++r) {
+                if (rounds > 1) load_round<kList>(sm, it, r);
+                const int64_t nr = round_n(r);
+                for (int i = t; i < nr; i += THREADS) {
+                    const uint32_t x = sm.keys[i];
+                    if (slot_valid<kList>(x, i, nr) && (pshift >= 32 || (x >> (pshift & 31)) == prefix))
+                        atomicAdd(&sm.bins[((x >> shift) - sub) & mask], 1u);
+                }
+            }
+            __syncthreads();
+            uint32_t bin, a2;
+            find_threshold_bin<THREADS>(sm, nbins, need, &bin, &a2);
+            // key >> shift of the threshold key
+            prefix = pshift >= 32 ? bin + sub : (prefix << (pshift - shift)) | bin;
+            above += a2;
+            need -= a2;
+            if (shift == 0) { T = prefix; break; }
+            pshift = shift;
+            shift = shift > kDigit ? shift - kDigit : 0;
+            sub = 0;
+            mask = (1u << (pshift - shift)) - 1u;
         }
+    }
+    // The first k - above items equal to T (in index order) complete the set.
+    const uint32_t ties = (uint32_t)k - above;
+
+    // ---- ordered emission: thread t owns positions PER*t .. PER*t + PER-1
+    uint32_t gt_base = 0, eq_base = 0;
+    for (int64_t r = 0; r < rounds; ++r) {
+        if (rounds > 1) load_round<kList>(sm, it, r);
+        const int64_t nr = round_n(r);
+        const int64_t p0 = r * kRound + (int64_t)PER * t;
+        uint64_t gtm = 0, eqm = 0;
+        if ((int64_t)PER * t < nr) {
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const uint32_t x = sm.keys[PER * t + i];
+                const bool v = slot_valid<kList>(x, PER * t + i, nr);
+                gtm |= (uint64_t)(v && x > T) << i;
+                eqm |= (uint64_t)(v && x == T) << i;
+            }
+        }
+        const uint32_t ngt = __popcll(gtm), neq = __popcll(eqm);
         uint32_t tot;
-        uint32_t pos = base + block_scan(n, sm.wave_sum, &tot) - n;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int64_t e = s0 + (int64_t)t * kPer + i;
-            if (e < E && key[i] >= floor_key) {
-                if (pos < (uint32_t)kCandMax) { sm.cand_key[pos] = key[i]; sm.cand_idx[pos] = (int32_t)e; }
+        const uint32_t mine = (ngt << 16) | neq;
+        const uint32_t excl = block_scan<THREADS>(mine, sm.wave_sum, &tot) - mine;
+        // Tied items take the remaining tie slots in index order.  (Written
+        // with a running rank and a comparison: a form with an unsigned
+        // saturating difference was mis-lowered by the compiler.)
+        uint32_t eqr = eq_base + (excl & 0xFFFFu);
+        uint32_t pos = gt_base + (excl >> 16) + min(eqr, ties);
+        uint64_t m = gtm | eqm;
+        while (m) {
+            const int i = __ffsll((unsigned long long)m) - 1;
+            m &= m - 1ull;
+            bool sel = true;
+            if ((eqm >> i) & 1ull) {
+                sel = eqr < ties;
+                ++eqr;
+            }
+            if (sel) {
+                if (pos < (uint32_t)k) {
+                    const int64_t p = p0 + i;
+                    if (kList) {
+                        const uint2 pr = it.pairs[p];
+                        if (kPairsOut) out_pairs[pos] = pr;
+                        else out_idx[pos] = (int32_t)pr.y;
+                    } else {
+                        if (kPairsOut) out_pairs[pos] = make_uint2(sm.keys[PER * t + i], (uint32_t)(it.base + p));
+                        else out_idx[pos] = (int32_t)(it.base + p);
+                    }
+                }
                 ++pos;
             }
         }
-        base += tot;
+        gt_base += tot >> 16;
+        eq_base += tot & 0xFFFFu;
     }
-    __syncthreads();
+}
 
-    uint32_t T, above;
-    if (base <= (uint32_t)kCandMax) {
-        FromLds src{&sm, (int64_t)base};
-        refine_threshold(sm, src, t1, above1, (uint32_t)a.k, &T, &above);
-        emit_selected(sm, src, T, (uint32_t)a.k - above, out, a.k);
-    } else {
-        FromGlobal src{keys, E};
-        refine_threshold(sm, src, t1, above1, (uint32_t)a.k, &T, &above);
-        emit_selected(sm, src, T, (uint32_t)a.k - above, out, a.k);
+// Sequence b longer than one slice, slice s: the local top-k of keys
+// [s*kSliceKeys, (s+1)*kSliceKeys) as index-ordered (key, index) pairs; a
+// slice with at most k entries passes them all and pads its list with key 0.
+// The slices' lists contain the sequence's top-k (an entry beaten by fewer
+// than k entries overall is beaten by fewer than k in its slice).
+__global__ __launch_bounds__(kSliceThreads) void topk_slice_kernel(SelectArgs a)
+{
+    __shared__ SelectSmem<kSliceThreads, kSlicePer> sm;
+    const int b = blockIdx.y, s = blockIdx.x;
+    const int64_t E = entries_of(a.n_tokens, b, a.capacity);
+    if (E <= a.k || E <= kSliceKeys) return;         // the merge reads the keys directly
+    uint2 *out = a.cand + ((size_t)b * a.slices + s) * a.k;
+    const int64_t first = (int64_t)s * kSliceKeys;
+    if (first >= E) return;
+    const int64_t n = E - first < kSliceKeys ? E - first : kSliceKeys;
+    if (n <= a.k) {
+        for (int i = threadIdx.x; i < a.k; i += kSliceThreads)
+            out[i] = i < n ? make_uint2(a.keys[(size_t)b * a.key_stride + first + i], (uint32_t)(first + i))
+                           : make_uint2(0u, 0xFFFFFFFFu);
+        return;
     }
+    Items it{a.keys + (size_t)b * a.key_stride + first, nullptr, n, first};
+    select_topk<false, true>(sm, it, a.k, nullptr, out);
+}
+
+// Sequence b of a cache that fits one slice: the final top-k from the key
+// array.
+__global__ __launch_bounds__(kSliceThreads) void topk_select_kernel(SelectArgs a)
+{
+    __shared__ SelectSmem<kSliceThreads, kSlicePer> sm;
+    const int b = blockIdx.x;
+    const int64_t E = entries_of(a.n_tokens, b, a.capacity);
+    int32_t *out = a.out + (size_t)b * a.k;
+    if (E <= a.k) {
+        for (int i = threadIdx.x; i < a.k; i += kSliceThreads) out[i] = i < E ? i : -1;
+        return;
+    }
+    Items it{a.keys + (size_t)b * a.key_stride, nullptr, E, 0};
+    select_topk<false, false>(sm, it, a.k, out, nullptr);
+}
+
+// Sequence b of a cache whose capacity spans several slices: the final top-k
+// over the slices' candidate lists (index-ordered, so their concatenation is
+// too), or straight from the key array when the sequence fits one slice.
+__global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(SelectArgs a)
+{
+    __shared__ SelectSmem<kMergeThreads, kMergePer> sm;
+    const int b = blockIdx.x;
+    const int64_t E = entries_of(a.n_tokens, b, a.capacity);
+    int32_t *out = a.out + (size_t)b * a.k;
+    if (E <= a.k) {
+        for (int i = threadIdx.x; i < a.k; i += kMergeThreads) out[i] = i < E ? i : -1;
+        return;
+    }
+    if (E <= kSliceKeys) {
+        Items it{a.keys + (size_t)b * a.key_stride, nullptr, E, 0};
+        select_topk<false, false>(sm, it, a.k, out, nullptr);
+        return;
+    }
+    const int64_t used = (E + kSliceKeys - 1) / kSliceKeys;
+    Items it{nullptr, a.cand + (size_t)b * a.slices * a.k, used * a.k, 0};
+    select_topk<true, false>(sm, it, a.k, out, nullptr);
 }
 
 }  // namespace
@@ -366,30 +522,49 @@ hipError_t launch_indexer_topk(const cskv_cache &c, const uint16_t *q_idx, int h
                                const float *head_w, int k, int32_t *out_idx, void *ws,
                                hipStream_t s)
 {
-    const TopkWorkspace lay = topk_workspace(c);
+    const TopkWorkspace lay = topk_workspace(c, k);
     uint32_t *keys = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + lay.keys_off);
-    uint32_t *hist = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + lay.hist_off);
-    const size_t nh = (size_t)kHistBins * c.batch;
-    zero_u32_kernel<<<(unsigned)((nh + 255) / 256 < 1024 ? (nh + 255) / 256 : 1024), 256, 0, s>>>(hist, nh);
+    uint2 *cand = reinterpret_cast<uint2 *>(static_cast<char *>(ws) + lay.cand_off);
 
-    // entries per block: aim for ~2048 blocks over the batch, 256..4096, a
-    // multiple of the tile
-    size_t chunk = ((size_t)c.capacity * c.batch + 2047) / 2048;
-    chunk = (chunk + kTile - 1) / kTile * kTile;
-    chunk = chunk < 256 ? 256 : (chunk > 4096 ? 4096 : chunk);
-    ScanArgs sa{c.idx_keys, c.n_tokens, q_idx, head_w, keys, hist, c.capacity, heads, (int)chunk,
+    // One round of blocks that fills every CU: entries per block chosen so
+    // that batch x blocks-per-sequence <= resident slots, a multiple of 64.
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+    }
+    const int slots = kScanBlocksPerCU * cus;
+    const int per_seq = c.batch >= slots ? 1 : slots / c.batch;
+    size_t chunk = ((size_t)c.capacity + per_seq - 1) / per_seq;
+    chunk = (chunk + 63) / 64 * 64;
+    ScanArgs sa{c.idx_keys, c.n_tokens, q_idx, head_w, keys, c.capacity, heads, (int)chunk,
                 key_stride(c)};
     dim3 grid((unsigned)(((size_t)c.capacity + chunk - 1) / chunk), (unsigned)c.batch);
+    const int mt = (heads + 15) / 16;
     timer_before(CSKV_KERNEL_INDEXER_SCAN, s);
-    if (c.idx_dim == 128)
-        indexer_scan_kernel<128><<<grid, kScanThreads, 0, s>>>(sa);
-    else
-        indexer_scan_kernel<64><<<grid, kScanThreads, 0, s>>>(sa);
+    if (c.idx_dim == 128) {
+        if (mt == 4) indexer_scan_kernel<128, 4><<<grid, kScanThreads, 0, s>>>(sa);
+        else if (mt == 3) indexer_scan_kernel<128, 3><<<grid, kScanThreads, 0, s>>>(sa);
+        else if (mt == 2) indexer_scan_kernel<128, 2><<<grid, kScanThreads, 0, s>>>(sa);
+        else indexer_scan_kernel<128, 1><<<grid, kScanThreads, 0, s>>>(sa);
+    } else {
+        if (mt == 4) indexer_scan_kernel<64, 4><<<grid, kScanThreads, 0, s>>>(sa);
+        else if (mt == 3) indexer_scan_kernel<64, 3><<<grid, kScanThreads, 0, s>>>(sa);
+        else if (mt == 2) indexer_scan_kernel<64, 2><<<grid, kScanThreads, 0, s>>>(sa);
+        else indexer_scan_kernel<64, 1><<<grid, kScanThreads, 0, s>>>(sa);
+    }
     timer_after(CSKV_KERNEL_INDEXER_SCAN, s);
 
-    SelectArgs se{keys, hist, c.n_tokens, out_idx, c.capacity, k, key_stride(c)};
+    const int slices = topk_slices(c);
+    SelectArgs se{keys, cand, c.n_tokens, out_idx, c.capacity, k, slices, key_stride(c)};
     timer_before(CSKV_KERNEL_TOPK_SELECT, s);
-    topk_select_kernel<<<c.batch, kSelThreads, 0, s>>>(se);
+    if (slices > 1) {
+        topk_slice_kernel<<<dim3((unsigned)slices, (unsigned)c.batch), kSliceThreads, 0, s>>>(se);
+        topk_merge_kernel<<<c.batch, kMergeThreads, 0, s>>>(se);
+    } else {
+        topk_select_kernel<<<c.batch, kSliceThreads, 0, s>>>(se);
+    }
     timer_after(CSKV_KERNEL_TOPK_SELECT, s);
     return hipGetLastError();
 }

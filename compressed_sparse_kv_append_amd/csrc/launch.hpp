@@ -10,25 +10,38 @@
 
 namespace cskv {
 
-// Workspace layout of the indexer + top-k (offsets in bytes from ws).
+// Workspace layout of the indexer + top-k (offsets in bytes from ws): one
+// uint32 score key per entry, and the per-slice candidate lists of sequences
+// longer than one select round.
 struct TopkWorkspace {
-    size_t keys_off, hist_off, total;
+    size_t keys_off, cand_off, total;
 };
-constexpr int kHistBins = 2048;   // first radix pass: top 11 bits of the key
-TopkWorkspace topk_workspace(const cskv_cache &c);
+constexpr int kSliceKeys = 4096;  // keys per select slice (one block)
+TopkWorkspace topk_workspace(const cskv_cache &c, int k);
+int topk_slices(const cskv_cache &c);
 
+// Compressor output rows (fp32) staged between the compressor and the quantiser.
+size_t append_workspace_bytes(int total_new);
 hipError_t launch_kv_append(const cskv_cache &c, const float *tokens, const int32_t *cu_new,
                             int total_new, const float *w_comp, const uint16_t *idx_rows,
-                            hipStream_t s);
+                            void *ws, hipStream_t s);
 hipError_t launch_swa_append(uint16_t *ring, int batch, int window, int dim, const float *rows,
                              const int32_t *cu_new, int total_new, const int32_t *end_pos,
                              hipStream_t s);
 hipError_t launch_indexer_topk(const cskv_cache &c, const uint16_t *q_idx, int heads,
                                const float *head_w, int k, int32_t *out_idx, void *ws,
                                hipStream_t s);
+// Attention work split: chunks of 32 keys (selected entries, then window
+// rows) cut into `splits` runs of `per_split` chunks; ws_bytes of partial
+// results when splits > 1.
+struct AttnPlan {
+    int n_sparse, n_chunks, splits, per_split;
+    size_t ws_bytes;
+};
+AttnPlan attn_plan(const cskv_cache &c, int heads, int k, int window);
 hipError_t launch_sparse_attn(const cskv_cache &c, const float *q, int heads, const int32_t *idx,
                               int k, const uint16_t *swa, int window, const int32_t *swa_len,
-                              float scale, float *out, float *lse, hipStream_t s);
+                              float scale, float *out, float *lse, void *ws, hipStream_t s);
 
 // Kernel timers (api.cpp): bracket a launch with event records when enabled.
 void timer_before(int kind, hipStream_t s);

@@ -114,10 +114,17 @@ typedef struct cskv_cache {
  * and zero codes.
  * A sequence whose entries would pass capacity is left untouched and sets
  * CSKV_STATUS_OVERFLOW.
+ * ws       device workspace for the compressor's fp32 output when w_comp is
+ *          non-NULL: at least cskv_append_workspace_bytes(total_new, w_comp)
+ *          bytes, 256-byte aligned; ignored (may be NULL) when w_comp is NULL.
  */
 int cskv_kv_append_fp4(const cskv_cache *cache, const float *tokens, const int32_t *cu_new,
                        int32_t total_new, const float *w_comp, const uint16_t *idx_rows,
-                       hipStream_t stream);
+                       void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes of cskv_kv_append_fp4 (total_new * dim * 4 with a
+ * compressor, else a nominal 256). */
+size_t cskv_append_workspace_bytes(int32_t total_new, const float *w_comp);
 
 /*
  * Write sliding-window rows [P2 三、"突破四" (each token sees the latest 128);
@@ -146,7 +153,8 @@ int cskv_swa_append(uint16_t *ring, int32_t batch, int32_t window, int32_t dim,
  * out_idx  i32 [batch][k]: the k highest scores, ties to the lower index,
  *          listed in ascending index order; -1 pads when fewer than k entries.
  * 1 <= k <= 2048.  ws: device workspace of at least
- * cskv_workspace_bytes(cache, k) bytes (contents need not be initialised).
+ * cskv_workspace_bytes(cache, CSKV_OP_INDEXER_TOPK, 0, k, 0) bytes, 256-byte
+ * aligned (contents need not be initialised; they are overwritten).
  */
 int cskv_indexer_topk(const cskv_cache *cache, const uint16_t *q_idx, int32_t n_idx_heads,
                       const float *head_w, int32_t k, int32_t *out_idx, void *ws,
@@ -162,16 +170,19 @@ int cskv_indexer_topk(const cskv_cache *cache, const uint16_t *q_idx, int32_t n_
  * with logits softmax_scale * q.k over all dim dims; out = sum p * v where
  * v = the value plane (if present) or the first dim-rope_dim key dims;
  * lse = natural log of sum exp(logit).  No keys: out = 0, lse = -inf.
- * q        f32 [batch][n_heads][dim], n_heads a multiple of 16, <= 128
- * idx      i32 [batch][k] (entries outside [0, entries) are skipped)
- * swa      bf16 [batch][window][dim]
+ * q        f32 [batch][n_heads][dim], n_heads a multiple of 16 in [16, 1024]
+ * idx      i32 [batch][k], 1 <= k <= 2048 (entries outside [0, entries) are skipped)
+ * swa      bf16 [batch][window][dim], 1 <= window <= 1024
  * swa_len  i32 [batch] valid window slots, or NULL: min(n_tokens, window)
  * out      f32 [batch][n_heads][dim-rope_dim];  lse f32 [batch][n_heads] or NULL
+ * ws       device workspace for partial softmaxes: at least
+ *          cskv_workspace_bytes(cache, CSKV_OP_SPARSE_ATTN, n_heads, k, window)
+ *          bytes, 256-byte aligned (may be NULL when that size is 256 or less).
  */
 int cskv_sparse_attn_decode(const cskv_cache *cache, const float *q, int32_t n_heads,
                             const int32_t *idx, int32_t k, const uint16_t *swa, int32_t window,
                             const int32_t *swa_len, float softmax_scale, float *out, float *lse,
-                            hipStream_t stream);
+                            void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Layer modes [P2 四、"CSA2：三种模式，40 层只存 4 份"]. */
 #define CSKV_MODE_FULL 0     /* append, own indexer query, own top-k, attend        */
@@ -206,8 +217,14 @@ int cskv_layer_group_decode(const cskv_cache *cache, const cskv_layer *layers, i
                             int32_t k, int32_t window, float softmax_scale, void *ws,
                             size_t ws_bytes, hipStream_t stream);
 
-/* Device workspace bytes cskv_indexer_topk / cskv_layer_group_decode need. */
-size_t cskv_workspace_bytes(const cskv_cache *cache, int32_t k);
+/* Device workspace bytes an operation needs (at least 256); 0 on invalid
+ * arguments (see cskv_last_error).  op: CSKV_OP_INDEXER_TOPK (uses k),
+ * CSKV_OP_SPARSE_ATTN (n_heads, k, window), CSKV_OP_LAYER_GROUP (all). */
+#define CSKV_OP_INDEXER_TOPK 1
+#define CSKV_OP_SPARSE_ATTN 2
+#define CSKV_OP_LAYER_GROUP 3
+size_t cskv_workspace_bytes(const cskv_cache *cache, int32_t op, int32_t n_heads, int32_t k,
+                            int32_t window);
 
 /* Bytes one entry occupies across all planes (codes, scales, indexer key)
  * [P2 四、"890 字节是怎么算出来的"]. */

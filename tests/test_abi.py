@@ -71,29 +71,42 @@ def _err(L):
 def test_cache_descriptor_rejected_before_launch(L, over, code, text):
     d = _desc(**over)
     rc = L.cskv_kv_append_fp4(C.byref(d), C.c_void_p(0x70000), None, 2, None,
-                              C.c_void_p(0x80000), None)
+                              C.c_void_p(0x80000), None, 0, None)
     assert rc == code and text in _err(L), (rc, _err(L))
-    assert L.cskv_workspace_bytes(C.byref(d), 512) == 0
+    assert L.cskv_workspace_bytes(C.byref(d), ck.OP_INDEXER_TOPK, 0, 512, 0) == 0
 
 
 def test_call_arguments_rejected_before_launch(L):
     d = _desc()
     vp = C.c_void_p
     # cu_new NULL needs one row per sequence
-    assert L.cskv_kv_append_fp4(C.byref(d), vp(0x70000), None, 3, None, vp(0x80000), None) == ck.EINVAL
+    assert L.cskv_kv_append_fp4(C.byref(d), vp(0x70000), None, 3, None, vp(0x80000), None, 0, None) == ck.EINVAL
+    # a compressor append needs its workspace
+    need = L.cskv_append_workspace_bytes(2, vp(0x110000))
+    assert need == 2 * 576 * 4 and L.cskv_append_workspace_bytes(2, None) == 256
+    assert L.cskv_kv_append_fp4(C.byref(d), vp(0x70000), None, 2, vp(0x110000), vp(0x80000), vp(0xB0000),
+                                need - 1, None) == ck.EWORKSPACE
     # top-k: k out of range, too many heads, workspace too small
-    ws = L.cskv_workspace_bytes(C.byref(d), 512)
+    ws = L.cskv_workspace_bytes(C.byref(d), ck.OP_INDEXER_TOPK, 0, 512, 0)
     assert ws > 0
     out = vp(0x90000)
     assert L.cskv_indexer_topk(C.byref(d), vp(0xA0000), 4, None, 0, out, vp(0xB0000), ws, None) == ck.EUNSUPPORTED
     assert L.cskv_indexer_topk(C.byref(d), vp(0xA0000), 65, None, 512, out, vp(0xB0000), ws, None) == ck.EUNSUPPORTED
     assert L.cskv_indexer_topk(C.byref(d), vp(0xA0000), 4, None, 512, out, vp(0xB0000), ws - 1, None) == ck.EWORKSPACE
     assert L.cskv_indexer_topk(C.byref(d), vp(0xA0000), 4, None, 512, out, None, ws, None) == ck.EWORKSPACE
-    # attention: heads not a multiple of 16, missing window
+    # attention: heads not a multiple of 16, missing window, workspace too small
+    aws = L.cskv_workspace_bytes(C.byref(d), ck.OP_SPARSE_ATTN, 16, 512, 128)
+    assert aws > 256
     assert L.cskv_sparse_attn_decode(C.byref(d), vp(0xC0000), 24, vp(0xD0000), 512, vp(0xE0000), 128,
-                                     None, C.c_float(0.04), vp(0xF0000), None, None) == ck.EUNSUPPORTED
+                                     None, C.c_float(0.04), vp(0xF0000), None, vp(0xB0000), aws,
+                                     None) == ck.EUNSUPPORTED
     assert L.cskv_sparse_attn_decode(C.byref(d), vp(0xC0000), 16, vp(0xD0000), 512, None, 128,
-                                     None, C.c_float(0.04), vp(0xF0000), None, None) == ck.EINVAL
+                                     None, C.c_float(0.04), vp(0xF0000), None, vp(0xB0000), aws,
+                                     None) == ck.EINVAL
+    assert L.cskv_sparse_attn_decode(C.byref(d), vp(0xC0000), 16, vp(0xD0000), 512, vp(0xE0000), 128,
+                                     None, C.c_float(0.04), vp(0xF0000), None, vp(0xB0000), aws - 1,
+                                     None) == ck.EWORKSPACE
+    assert L.cskv_workspace_bytes(C.byref(d), 9, 16, 512, 128) == 0
     # window append: dim not a multiple of 4
     assert L.cskv_swa_append(vp(0x100000), 2, 128, 578, vp(0x70000), None, 2, vp(0x40000), None) == ck.EUNSUPPORTED
 
@@ -101,7 +114,7 @@ def test_call_arguments_rejected_before_launch(L):
 def test_layer_group_checks_every_layer_first(L):
     d = _desc()
     vp = C.c_void_p
-    ws = L.cskv_workspace_bytes(C.byref(d), 512)
+    ws = L.cskv_workspace_bytes(C.byref(d), ck.OP_LAYER_GROUP, 16, 512, 128)
     # a REUSE layer with no FULL/REINDEX before it is rejected before anything runs
     layers = (ck.LayerDesc * 2)()
     layers[0] = ck.LayerDesc(ck.MODE_REUSE, 0xC0000, None, None, 0x100000, None, None, 0xF0000, None)

@@ -166,6 +166,18 @@ def test_indexer_topk_exact_ragged(ck, orc, idx_dim, heads):
     _indexer_case(ck, orc, lens, idx_dim, heads, 512, seed=idx_dim + heads)
 
 
+def test_indexer_topk_long_sequences_merge_slices(ck, orc):
+    """Sequences longer than one select round (36,864 keys) go through the
+    per-slice candidate lists and the merge; short ones in the same batch
+    take the direct path."""
+    lens = [36864, 36865, 80000, 700, 0]
+    _indexer_case(ck, orc, lens, 128, 64, 512, seed=40)
+    _indexer_case(ck, orc, [50000, 36900], 64, 4, 2048, seed=41)
+    zero = lambda g, n: np.zeros((n, 64), np.uint16)
+    got = _indexer_case(ck, orc, [90000, 40000], 64, 4, 512, seed=42, key_fn=zero)
+    assert np.array_equal(got[0], np.arange(512)) and np.array_equal(got[1], np.arange(512))
+
+
 def test_indexer_topk_head_weights_and_small_k(ck, orc):
     hw = synth.head_weights_int(5, 3, 64)
     _indexer_case(ck, orc, [3000, 64, 9000], 128, 64, 512, seed=11, head_w=hw)
