@@ -78,6 +78,50 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const u32x4_t &a, const u32x4_t 
                                                     __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// ---------------------------------------------------------------- wave scans
+
+// Cross-lane steps through DPP (no LDS round trip): row_shr:n moves values n
+// lanes up inside each row of 16; row_bcast:15 / row_bcast:31 carry lane 15
+// (31) of a row into the next row(s).  Lanes without a source take `ident`.
+enum : int { kDppRowShr = 0x110, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143 };
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t ident, uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive prefix (op = add, max or min) over the 64 lanes of the wave.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_inclusive(uint32_t v, uint32_t ident, Op op)
+{
+    v = op(v, dpp_u32<kDppRowShr | 1, 0xF>(ident, v));
+    v = op(v, dpp_u32<kDppRowShr | 2, 0xF>(ident, v));
+    v = op(v, dpp_u32<kDppRowShr | 4, 0xF>(ident, v));
+    v = op(v, dpp_u32<kDppRowShr | 8, 0xF>(ident, v));
+    v = op(v, dpp_u32<kDppRowBcast15, 0xA>(ident, v));
+    v = op(v, dpp_u32<kDppRowBcast31, 0xC>(ident, v));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_scan_add(uint32_t v)
+{
+    return wave_inclusive(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
+// Reductions over the wave, the same value in every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = wave_inclusive(v, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
+{
+    v = wave_inclusive(v, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+
 // ---------------------------------------------------------------- misc
 
 // Order-preserving map of an fp32 score to uint32 (larger score -> larger key).

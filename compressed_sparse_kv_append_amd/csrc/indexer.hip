@@ -34,13 +34,16 @@ static size_t key_stride(const cskv_cache &c) { return align_up((size_t)c.capaci
 
 int topk_slices(const cskv_cache &c) { return (int)((c.capacity + kSliceKeys - 1) / kSliceKeys); }
 
+// Candidate pairs per sequence, rounded to even so each list is 16-byte aligned.
+static size_t cand_stride(const cskv_cache &c, int k) { return ((size_t)topk_slices(c) * k + 1) & ~(size_t)1; }
+
 TopkWorkspace topk_workspace(const cskv_cache &c, int k)
 {
     TopkWorkspace w;
     w.keys_off = 0;
     w.cand_off = align_up(sizeof(uint32_t) * key_stride(c) * (size_t)c.batch, 256);
     const size_t slices = (size_t)topk_slices(c);
-    const size_t cand = slices > 1 ? sizeof(uint32_t) * 2 * slices * (size_t)k * c.batch : 0;
+    const size_t cand = slices > 1 ? sizeof(uint32_t) * 2 * cand_stride(c, k) * c.batch : 0;
     w.total = align_up(w.cand_off + cand, 256);
     return w;
 }
@@ -199,167 +202,169 @@ struct Items {
 
 struct SelectArgs {
     const uint32_t *keys;   // [B][key_stride]
-    uint2 *cand;            // [B][slices][k] (key, index) pairs
+    uint2 *cand;            // [B][cand_stride]: slices x k (key, index) pairs per sequence
     const int32_t *n_tokens;
     int32_t *out;           // [B][k]
     int capacity, k, slices;
-    size_t key_stride;
+    size_t key_stride, cand_stride;
 };
 
-template <int THREADS, int PER>
+template <int THREADS>
 struct SelectSmem {
-    static constexpr int kRound = PER * THREADS;
     static constexpr int kWaves = THREADS / kWave;
-    uint32_t keys[kRound];      // the round's keys
     uint32_t bins[kBins];
     uint32_t wave_sum[kWaves];
     uint32_t red[2][kWaves];
-    uint32_t found[2];
+    uint32_t found[3];
 };
 
 // Inclusive prefix sum over the block; *total receives the block sum.
 template <int THREADS>
-__device__ uint32_t block_scan(uint32_t v, uint32_t *wave_sum, uint32_t *total)
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t *wave_sum, uint32_t *total)
 {
     constexpr int kWaves = THREADS / kWave;
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t n = __shfl_up(v, off);
-        if (lane >= off) v += n;
-    }
+    v = wave_scan_add(v);
     if (lane == kWave - 1) wave_sum[w] = v;
     __syncthreads();
-    if (w == 0) {
-        uint32_t x = lane < kWaves ? wave_sum[lane] : 0u;
+    uint32_t base = 0, tot = 0;
 #pragma unroll
-        for (int off = 1; off < kWaves; off <<= 1) {
-            const uint32_t n = __shfl_up(x, off);
-            if (lane >= off) x += n;
-        }
-        if (lane < kWaves) wave_sum[lane] = x;
+    for (int i = 0; i < kWaves; ++i) {
+        const uint32_t x = wave_sum[i];
+        base += i < w ? x : 0u;
+        tot += x;
     }
-    __syncthreads();
-    const uint32_t base = w ? wave_sum[w - 1] : 0u;
-    *total = wave_sum[kWaves - 1];
+    *total = tot;
     __syncthreads();
     return v + base;
 }
 
 // Over the histogram in sm.bins (nbins <= 2048), the highest bin t with
-// (count above t) < need <= (count at or above t).  Returns t and the count
-// strictly above it.  Requires need <= total count.
-template <int THREADS, class Smem>
-__device__ void find_threshold_bin(Smem &sm, int nbins, uint32_t need, uint32_t *bin, uint32_t *above)
+// (count above t) < need <= (count at or above t); sm.found = {t, count
+// strictly above t, count in t}.  Run by wave 0 alone: lane l owns the 32
+// bins below nbins - 32 l (read in a rotated order so that no two lanes hit
+// one LDS bank), a lane prefix sum orders the groups from the top, and the
+// lane whose group holds the threshold scans its 32 counts in registers.
+// Afterwards every bin is cleared for the next histogram.  Requires
+// need <= total count.
+template <class Smem>
+__device__ __forceinline__ void find_threshold_bin_wave0(Smem &sm, int nbins, uint32_t need)
 {
-    constexpr int kOwn = kBins / THREADS;         // bins per thread, in descending order
-    const int t = threadIdx.x;
-    uint32_t c[kOwn], sum = 0;
+    constexpr int kOwn = kBins / kWave;           // 32 bins per lane
+    const int lane = threadIdx.x;
+    const int top = nbins - 1 - kOwn * lane;      // this lane's highest bin
+    uint32_t sum = 0;
 #pragma unroll
     for (int j = 0; j < kOwn; ++j) {
-        const int bn = nbins - 1 - kOwn * t - j;
-        c[j] = bn >= 0 ? sm.bins[bn] : 0u;
-        sum += c[j];
+        const int bn = top - ((j + lane) & (kOwn - 1));
+        sum += bn >= 0 ? sm.bins[bn] : 0u;
     }
-    uint32_t total;
-    uint32_t run = block_scan<THREADS>(sum, sm.wave_sum, &total) - sum;
+    const uint32_t incl = wave_scan_add(sum);
+    uint32_t run = incl - sum;
+    if (run < need && need <= incl) {
+        uint32_t c[kOwn];
 #pragma unroll
-    for (int j = 0; j < kOwn; ++j) {
-        const int bn = nbins - 1 - kOwn * t - j;
-        if (bn >= 0 && run < need && need <= run + c[j]) { sm.found[0] = (uint32_t)bn; sm.found[1] = run; }
-        run += c[j];
-    }
-    __syncthreads();
-    *bin = sm.found[0];
-    *above = sm.found[1];
-    __syncthreads();
-}
-
-// Copy the keys of round r into LDS; positions past the end hold 0.  Ends
-// with a barrier.
-template <bool kList, int THREADS, int PER>
-__device__ void load_round(SelectSmem<THREADS, PER> &sm, const Items &it, int64_t r)
-{
-    constexpr int kRound = SelectSmem<THREADS, PER>::kRound;
-    const int64_t p0 = r * kRound;
-    __syncthreads();                            // previous round fully consumed
-    if (!kList) {
-        constexpr int kVec = kRound / 4 / THREADS;   // uint4 per thread
-        uint4 v[kVec];
+        for (int j = 0; j < kOwn; ++j) c[j] = sm.bins[top - j];
+        bool done = false;
 #pragma unroll
-        for (int j = 0; j < kVec; ++j) {
-            const int64_t p = p0 + 4 * ((int64_t)threadIdx.x + (int64_t)THREADS * j);
-            v[j] = make_uint4(0u, 0u, 0u, 0u);
-            if (p + 3 < it.n) {
-                v[j] = *reinterpret_cast<const uint4 *>(it.keys + p);
-            } else {
-                if (p + 0 < it.n) v[j].x = it.keys[p + 0];
-                if (p + 1 < it.n) v[j].y = it.keys[p + 1];
-                if (p + 2 < it.n) v[j].z = it.keys[p + 2];
+        for (int j = 0; j < kOwn; ++j) {
+            if (!done && need <= run + c[j]) {
+                sm.found[0] = (uint32_t)(top - j);
+                sm.found[1] = run;
+                sm.found[2] = c[j];
+                done = true;
             }
+            run += c[j];
         }
-#pragma unroll
-        for (int j = 0; j < kVec; ++j)
-            reinterpret_cast<uint4 *>(sm.keys)[threadIdx.x + THREADS * j] = v[j];
-    } else {
-        uint32_t v[PER];
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int64_t p = p0 + threadIdx.x + (int64_t)THREADS * j;
-            v[j] = p < it.n ? it.pairs[p].x : 0u;
-        }
-#pragma unroll
-        for (int j = 0; j < PER; ++j) sm.keys[threadIdx.x + THREADS * j] = v[j];
     }
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kOwn; ++j) sm.bins[kOwn * lane + ((j + lane) & (kOwn - 1))] = 0u;
 }
 
-// Validity of the item at LDS slot i of a round holding nr positions.
-template <bool kList>
-__device__ __forceinline__ bool slot_valid(uint32_t x, int i, int64_t nr)
+// The keys of positions [PER t, PER t + PER) of round r, held by thread t,
+// and their validity bits.  List mode: an unused slot holds key 0.
+template <bool kList, int THREADS, int PER>
+__device__ __forceinline__ uint64_t load_keys(const Items &it, int64_t r, uint32_t (&key)[PER],
+                                              uint32_t (&idx)[PER])
 {
-    return kList ? x != 0u : (int64_t)i < nr;
+    const int64_t p0 = r * (int64_t)(THREADS * PER) + (int64_t)PER * threadIdx.x;
+    uint64_t vm = 0;
+    if (!kList) {
+        static_assert(PER % 4 == 0, "contiguous keys load as uint4");
+#pragma unroll
+        for (int i = 0; i < PER; i += 4) {
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (p0 + i + 3 < it.n) {
+                v = *reinterpret_cast<const uint4 *>(it.keys + p0 + i);
+            } else {
+                if (p0 + i + 0 < it.n) v.x = it.keys[p0 + i + 0];
+                if (p0 + i + 1 < it.n) v.y = it.keys[p0 + i + 1];
+                if (p0 + i + 2 < it.n) v.z = it.keys[p0 + i + 2];
+            }
+            key[i] = v.x; key[i + 1] = v.y; key[i + 2] = v.z; key[i + 3] = v.w;
+        }
+        const int64_t nv = it.n - p0;
+        vm = nv >= PER ? (PER == 64 ? ~0ull : (1ull << PER) - 1ull) : (nv > 0 ? (1ull << nv) - 1ull : 0ull);
+    } else {
+#pragma unroll
+        for (int i = 0; i < PER; i += 2) {
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (p0 + i + 1 < it.n) v = *reinterpret_cast<const uint4 *>(it.pairs + p0 + i);
+            else if (p0 + i < it.n) { const uint2 u = it.pairs[p0 + i]; v.x = u.x; v.y = u.y; }
+            key[i] = v.x;
+            idx[i] = v.y;
+            key[i + 1] = v.z;
+            idx[i + 1] = v.w;
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) vm |= (uint64_t)(key[i] != 0u) << i;
+    }
+    return vm;
 }
 
-// Exact top-k of `it`, which holds more than k valid items.  kPairsOut: write
-// the selected (key, index) pairs in index order; else the indices.  Exactly
-// k items are selected, so nothing is padded.
+// Exact top-k of `it`, which holds more than k valid items.  Thread t holds
+// PER consecutive positions in registers.  kPairsOut: write the selected
+// (key, index) pairs in index order; else the indices.  Exactly k items are
+// selected, so nothing is padded.
 template <bool kList, bool kPairsOut, int THREADS, int PER>
-__device__ void select_topk(SelectSmem<THREADS, PER> &sm, const Items &it, int k, int32_t *out_idx,
+__device__ __forceinline__ void select_topk(SelectSmem<THREADS> &sm, const Items &it, int k, int32_t *out_idx,
                             uint2 *out_pairs)
 {
-    typedef SelectSmem<THREADS, PER> Smem;
-    constexpr int kRound = Smem::kRound;
-    constexpr int kWaves = Smem::kWaves;
+    constexpr int kRound = THREADS * PER;
+    constexpr int kWaves = THREADS / kWave;
     const int t = threadIdx.x;
     const int64_t rounds = (it.n + kRound - 1) / kRound;
-    if (rounds == 1) load_round<kList>(sm, it, 0);
-    auto round_n = [&](int64_t r) { return it.n - r * kRound < kRound ? it.n - r * kRound : (int64_t)kRound; };
+    uint32_t key[PER], idx[PER];
+    uint64_t vm = 0;
+    if (rounds == 1) vm = load_keys<kList, THREADS, PER>(it, 0, key, idx);
 
     // ---- range of the valid keys
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
     for (int64_t r = 0; r < rounds; ++r) {
-        if (rounds > 1) load_round<kList>(sm, it, r);
-        const int64_t nr = round_n(r);
-        for (int i = t; i < nr; i += THREADS) {
-            const uint32_t x = sm.keys[i];
-            const bool v = slot_valid<kList>(x, i, nr);
-            lo = min(lo, v ? x : 0xFFFFFFFFu);
-            hi = max(hi, v ? x : 0u);
+        if (rounds > 1) vm = load_keys<kList, THREADS, PER>(it, r, key, idx);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const bool v = (vm >> i) & 1ull;
+            lo = min(lo, v ? key[i] : 0xFFFFFFFFu);
+            hi = max(hi, v ? key[i] : 0u);
         }
     }
-#pragma unroll
-    for (int off = kWave / 2; off >= 1; off >>= 1) {
-        lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
-        hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
-    }
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
     if ((t & (kWave - 1)) == 0) { sm.red[0][t / kWave] = lo; sm.red[1][t / kWave] = hi; }
+    for (int i = t; i < kBins; i += THREADS) sm.bins[i] = 0u;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) { lo = min(lo, sm.red[0][i]); hi = max(hi, sm.red[1][i]); }
 
-    // ---- radix passes: digit windows below the common prefix of lo and hi
-    uint32_t T = lo, above = 0;          // the k-th largest key, items above it
+    // ---- radix passes: digit windows below the common prefix of lo and hi.
+    // After a pass, items whose key >> shift exceeds the threshold prefix are
+    // in; if the threshold bin is taken whole, it is in too and the search
+    // stops; otherwise the bin is refined by the next lower bits.  At
+    // shift 0 the prefix is the k-th largest key itself.
+    uint32_t T = lo;                 // selected: key >> tshift > T, or == T within the tie quota
+    int tshift = 0;
+    uint32_t ties = (uint32_t)k;
     if (lo != hi) {
         const int top = 32 - __clz((int)(lo ^ hi));      // bits [0, top) still vary
         int shift = top > kDigit ? top - kDigit : 0;
@@ -370,49 +375,49 @@ __device__ void select_topk(SelectSmem<THREADS, PER> &sm, const Items &it, int k
         uint32_t need = (uint32_t)k;
         while (true) {
             const int nbins = pshift >= 32 ? kBins : 1 << (pshift - shift);
-            for (int i = t; i < kBins; i += THREADS) sm.bins[i] = 0u;
-            __syncthreads();
             for (int64_t r = 0; r < rounds; ++r) {
-                if (rounds > 1) load_round<kList>(sm, it, r);
-                const int64_t nr = round_n(r);
-                for (int i = t; i < nr; i += THREADS) {
-                    const uint32_t x = sm.keys[i];
-                    if (slot_valid<kList>(x, i, nr) && (pshift >= 32 || (x >> (pshift & 31)) == prefix))
+                if (rounds > 1) vm = load_keys<kList, THREADS, PER>(it, r, key, idx);
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    const uint32_t x = key[i];
+                    if (((vm >> i) & 1ull) && (pshift >= 32 || (x >> (pshift & 31)) == prefix))
                         atomicAdd(&sm.bins[((x >> shift) - sub) & mask], 1u);
                 }
             }
             __syncthreads();
-            uint32_t bin, a2;
-            find_threshold_bin<THREADS>(sm, nbins, need, &bin, &a2);
+            if (t < kWave) find_threshold_bin_wave0(sm, nbins, need);
+            __syncthreads();
+            const uint32_t bin = sm.found[0], a2 = sm.found[1], cnt = sm.found[2];
             // key >> shift of the threshold key
             prefix = pshift >= 32 ? bin + sub : (prefix << (pshift - shift)) | bin;
-            above += a2;
             need -= a2;
-            if (shift == 0) { T = prefix; break; }
+            if (shift == 0 || cnt == need) {
+                T = prefix;
+                tshift = shift;
+                ties = need;
+                break;
+            }
             pshift = shift;
             shift = shift > kDigit ? shift - kDigit : 0;
             sub = 0;
             mask = (1u << (pshift - shift)) - 1u;
         }
     }
-    // The first k - above items equal to T (in index order) complete the set.
-    const uint32_t ties = (uint32_t)k - above;
+    // Items with key >> tshift == T: the first `ties` of them in index order
+    // complete the set (all of them when the bin was taken whole).
 
-    // ---- ordered emission: thread t owns positions PER*t .. PER*t + PER-1
+    // ---- ordered emission
     uint32_t gt_base = 0, eq_base = 0;
     for (int64_t r = 0; r < rounds; ++r) {
-        if (rounds > 1) load_round<kList>(sm, it, r);
-        const int64_t nr = round_n(r);
-        const int64_t p0 = r * kRound + (int64_t)PER * t;
+        if (rounds > 1) vm = load_keys<kList, THREADS, PER>(it, r, key, idx);
+        const int64_t p0 = r * (int64_t)kRound + (int64_t)PER * t;
         uint64_t gtm = 0, eqm = 0;
-        if ((int64_t)PER * t < nr) {
 #pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                const uint32_t x = sm.keys[PER * t + i];
-                const bool v = slot_valid<kList>(x, PER * t + i, nr);
-                gtm |= (uint64_t)(v && x > T) << i;
-                eqm |= (uint64_t)(v && x == T) << i;
-            }
+        for (int i = 0; i < PER; ++i) {
+            const bool v = (vm >> i) & 1ull;
+            const uint32_t xs = key[i] >> tshift;
+            gtm |= (uint64_t)(v && xs > T) << i;
+            eqm |= (uint64_t)(v && xs == T) << i;
         }
         const uint32_t ngt = __popcll(gtm), neq = __popcll(eqm);
         uint32_t tot;
@@ -423,28 +428,25 @@ __device__ void select_topk(SelectSmem<THREADS, PER> &sm, const Items &it, int k
         // saturating difference was mis-lowered by the compiler.)
         uint32_t eqr = eq_base + (excl & 0xFFFFu);
         uint32_t pos = gt_base + (excl >> 16) + min(eqr, ties);
-        uint64_t m = gtm | eqm;
-        while (m) {
-            const int i = __ffsll((unsigned long long)m) - 1;
-            m &= m - 1ull;
-            bool sel = true;
-            if ((eqm >> i) & 1ull) {
-                sel = eqr < ties;
-                ++eqr;
-            }
-            if (sel) {
-                if (pos < (uint32_t)k) {
-                    const int64_t p = p0 + i;
-                    if (kList) {
-                        const uint2 pr = it.pairs[p];
-                        if (kPairsOut) out_pairs[pos] = pr;
-                        else out_idx[pos] = (int32_t)pr.y;
-                    } else {
-                        if (kPairsOut) out_pairs[pos] = make_uint2(sm.keys[PER * t + i], (uint32_t)(it.base + p));
-                        else out_idx[pos] = (int32_t)(it.base + p);
+        if (gtm | eqm) {
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const bool g = (gtm >> i) & 1ull, q = (eqm >> i) & 1ull;
+                if (g || q) {
+                    bool sel = true;
+                    if (q) {
+                        sel = eqr < ties;
+                        ++eqr;
+                    }
+                    if (sel) {
+                        if (pos < (uint32_t)k) {
+                            const uint32_t ix = kList ? idx[i] : (uint32_t)(it.base + p0 + i);
+                            if (kPairsOut) out_pairs[pos] = make_uint2(key[i], ix);
+                            else out_idx[pos] = (int32_t)ix;
+                        }
+                        ++pos;
                     }
                 }
-                ++pos;
             }
         }
         gt_base += tot >> 16;
@@ -459,11 +461,11 @@ __device__ void select_topk(SelectSmem<THREADS, PER> &sm, const Items &it, int k
 // than k entries overall is beaten by fewer than k in its slice).
 __global__ __launch_bounds__(kSliceThreads) void topk_slice_kernel(SelectArgs a)
 {
-    __shared__ SelectSmem<kSliceThreads, kSlicePer> sm;
+    __shared__ SelectSmem<kSliceThreads> sm;
     const int b = blockIdx.y, s = blockIdx.x;
     const int64_t E = entries_of(a.n_tokens, b, a.capacity);
     if (E <= a.k || E <= kSliceKeys) return;         // the merge reads the keys directly
-    uint2 *out = a.cand + ((size_t)b * a.slices + s) * a.k;
+    uint2 *out = a.cand + (size_t)b * a.cand_stride + (size_t)s * a.k;
     const int64_t first = (int64_t)s * kSliceKeys;
     if (first >= E) return;
     const int64_t n = E - first < kSliceKeys ? E - first : kSliceKeys;
@@ -474,14 +476,14 @@ __global__ __launch_bounds__(kSliceThreads) void topk_slice_kernel(SelectArgs a)
         return;
     }
     Items it{a.keys + (size_t)b * a.key_stride + first, nullptr, n, first};
-    select_topk<false, true>(sm, it, a.k, nullptr, out);
+    select_topk<false, true, kSliceThreads, kSlicePer>(sm, it, a.k, nullptr, out);
 }
 
 // Sequence b of a cache that fits one slice: the final top-k from the key
 // array.
 __global__ __launch_bounds__(kSliceThreads) void topk_select_kernel(SelectArgs a)
 {
-    __shared__ SelectSmem<kSliceThreads, kSlicePer> sm;
+    __shared__ SelectSmem<kSliceThreads> sm;
     const int b = blockIdx.x;
     const int64_t E = entries_of(a.n_tokens, b, a.capacity);
     int32_t *out = a.out + (size_t)b * a.k;
@@ -490,7 +492,7 @@ __global__ __launch_bounds__(kSliceThreads) void topk_select_kernel(SelectArgs a
         return;
     }
     Items it{a.keys + (size_t)b * a.key_stride, nullptr, E, 0};
-    select_topk<false, false>(sm, it, a.k, out, nullptr);
+    select_topk<false, false, kSliceThreads, kSlicePer>(sm, it, a.k, out, nullptr);
 }
 
 // Sequence b of a cache whose capacity spans several slices: the final top-k
@@ -498,7 +500,7 @@ __global__ __launch_bounds__(kSliceThreads) void topk_select_kernel(SelectArgs a
 // too), or straight from the key array when the sequence fits one slice.
 __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(SelectArgs a)
 {
-    __shared__ SelectSmem<kMergeThreads, kMergePer> sm;
+    __shared__ SelectSmem<kMergeThreads> sm;
     const int b = blockIdx.x;
     const int64_t E = entries_of(a.n_tokens, b, a.capacity);
     int32_t *out = a.out + (size_t)b * a.k;
@@ -508,12 +510,12 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(SelectArgs a)
     }
     if (E <= kSliceKeys) {
         Items it{a.keys + (size_t)b * a.key_stride, nullptr, E, 0};
-        select_topk<false, false>(sm, it, a.k, out, nullptr);
+        select_topk<false, false, kMergeThreads, kMergePer>(sm, it, a.k, out, nullptr);
         return;
     }
     const int64_t used = (E + kSliceKeys - 1) / kSliceKeys;
-    Items it{nullptr, a.cand + (size_t)b * a.slices * a.k, used * a.k, 0};
-    select_topk<true, false>(sm, it, a.k, out, nullptr);
+    Items it{nullptr, a.cand + (size_t)b * a.cand_stride, used * a.k, 0};
+    select_topk<true, false, kMergeThreads, kMergePer>(sm, it, a.k, out, nullptr);
 }
 
 }  // namespace
@@ -557,7 +559,7 @@ hipError_t launch_indexer_topk(const cskv_cache &c, const uint16_t *q_idx, int h
     timer_after(CSKV_KERNEL_INDEXER_SCAN, s);
 
     const int slices = topk_slices(c);
-    SelectArgs se{keys, cand, c.n_tokens, out_idx, c.capacity, k, slices, key_stride(c)};
+    SelectArgs se{keys, cand, c.n_tokens, out_idx, c.capacity, k, slices, key_stride(c), cand_stride(c, k)};
     timer_before(CSKV_KERNEL_TOPK_SELECT, s);
     if (slices > 1) {
         topk_slice_kernel<<<dim3((unsigned)slices, (unsigned)c.batch), kSliceThreads, 0, s>>>(se);
