@@ -4,26 +4,28 @@
 // window); P2 三、"突破二：MLA，低秩压缩" (every head reads the same latent
 // entry); P2 四、"P4 main KV" (FP4 is storage only; dequantise before use)].
 //
-// Work decomposition.  The keys of a sequence (the k selected entries, then
-// the window rows) are cut into chunks of 32 and the chunks into S contiguous
-// splits.  One block of 4 waves takes 16 query heads and one split; a second
-// kernel merges the S partial softmaxes of each head by their log-sum-exp
-// (skipped when S = 1).  The blocks that share a split's keys (one per head
-// group) are numbered so that they land on the same XCD and read the gathered
-// rows through one L2.
+// Work decomposition.  The keys of a sequence are the k selected entries,
+// cut into chunks of 128, and the window rows, cut into chunks of 64.  A
+// split is a run of chunks of one kind; one block of 8 waves takes 16 query
+// heads and one split, and a second kernel merges the partial softmaxes of
+// each head by their log-sum-exp (skipped when there is one split).  The
+// blocks that share a split's keys (one per head group) are numbered so that
+// they land on the same XCD and read the gathered rows through one L2.
+// Keeping a block to one kind lets each loop hold its own prefetch registers
+// and makes every load in it unconditional.
 //
 // Per chunk.  The gathered rows stay E2M1 codes in LDS: the key plane row-
 // major (MFMA B operand of Q.K^T: 8 consecutive dims of one key = one 32-bit
 // word of codes) and the value plane transposed to [dim][key] nibbles (B
-// operand of P.V: 8 consecutive keys of one dim = one word).  Each operand
-// word becomes 8 bf16 values with four hardware FP4 conversions; E2M1 values
-// are exact in bf16.  Group scales stay fp32 outside the MFMA: per key group
-// on the logits, folded into the probabilities per value group.  q and the
-// scaled probabilities are each split into bf16 high and low parts, so the
-// products carry about 16 significant bits.  Window rows are bf16 already and
-// are staged row-major.  The softmax runs online in base 2 with fp32
-// statistics.  The next chunk's HBM reads are issued before the current chunk
-// is computed.
+// operand of P.V: 8 consecutive keys of one dim = one word), the transpose
+// done in registers on the way from HBM to LDS.  Each operand word becomes 8
+// bf16 values with four hardware FP4 conversions; E2M1 values are exact in
+// bf16.  Group scales stay fp32 outside the MFMA: per key group on the
+// logits, folded into the probabilities per value group.  q and the scaled
+// probabilities are each split into bf16 high and low parts, so the products
+// carry about 16 significant bits.  Window rows are bf16 already and are
+// staged row-major.  The softmax runs online in base 2 with fp32 statistics.
+// The next chunk's HBM reads are issued before the current chunk is computed.
 //
 // Sources cited as [P2]:
 //   P2  "DeepSeek V1 到 V4.1-Flash，单 token 的 global KV 如何从 389,000 B 压缩到 890 B的？"
@@ -36,31 +38,34 @@ namespace cskv {
 
 namespace {
 
-constexpr int kThreads = 512;    // 8 waves
-constexpr int kWaves = kThreads / kWave;
-constexpr int kHG = 16;          // query heads per block (one MFMA row tile)
-constexpr int kKC = 32;          // keys per chunk
+constexpr int kThreads = 512;                 // 8 waves
+constexpr int kHG = 16;                       // query heads per block (one MFMA row tile)
+constexpr int kSK = 128;                      // selected entries per chunk
+constexpr int kWK = 64;                       // window rows per chunk
 constexpr int kD = 576;
 constexpr int kDv = 512;
-constexpr int kSteps = kD / 32;  // 18 contraction steps of Q.K^T
-constexpr int kParts = 4;        // the steps are shared by 4 waves per key tile
-constexpr int kMaxPart = 5;      // steps per part: 5, 5, 4, 4
+constexpr int kSteps = kD / 32;               // 18 contraction steps of Q.K^T
+constexpr int kHalf = kSteps / 2;
 constexpr int kMaxKG = kD / 32;
 constexpr int kMaxVG = kDv / 32;
-constexpr int kCodeRow = kD / 2 + 16;     // 304 B: conflict-free 32-bit operand reads
-constexpr int kVCodeRow = kDv / 2 + 16;   // 272 B
-constexpr int kWinRow = kD + 8;           // 584 bf16 = 1168 B
-constexpr int kMaxSplitChunks = 32;       // chunk indices a block keeps in LDS
-
-__device__ __forceinline__ int part_begin(int p) { return p < 2 ? 5 * p : 10 + 4 * (p - 2); }
+// Key-code row stride in words: 72 + 2, so the 16 rows of a key tile start on
+// 16 distinct even banks and one 32-bit operand read per lane is conflict-free.
+constexpr int kKcRow = kD / 8 + 2;
+// Transposed value codes: per 32-key group, dim d's 4 words (8 keys each) sit
+// at (d / 8) * 33 + 4 * (d % 8); the odd octet stride spreads the transpose
+// writes of 32 lanes (one dim octet each) over 32 banks.
+constexpr int kVtOct = 33;
+constexpr int kVtGroup = (kDv / 8) * kVtOct;
+constexpr int kWinRow = kD + 8;               // 584 bf16 per staged window row
+constexpr int kSRow = kSK + 4;                // floats per head row of logits / probabilities
+constexpr int kMaxSplitChunks = 8;            // chunks a block keeps key sources for
 
 struct SparseStage {
-    uint8_t kc[kKC][kCodeRow];            // key-plane codes, row-major
-    uint8_t vc[kKC][kVCodeRow];           // value-plane codes (split planes only)
-    uint32_t vt[kDv][kKC / 8];            // value codes transposed: [dim][8-key word]
+    uint32_t kc[kSK * kKcRow];                // key-plane codes, row-major
+    uint32_t vt[(kSK / 32) * kVtGroup];       // value codes, [32-key group][dim][8-key word]
 };
 struct WindowStage {
-    uint16_t kr[kKC][kWinRow];            // window rows, bf16
+    uint16_t kr[kWK][kWinRow];                // window rows, bf16
 };
 
 struct AttnSmem {
@@ -68,12 +73,12 @@ struct AttnSmem {
         SparseStage sp;
         WindowStage win;
     } st;
-    float ks[kKC][kMaxKG];                // key-plane scale per key and group (1: window)
-    float vs[kKC][kMaxVG];                // value scale per key and value group
-    float spart[kParts][kHG][kKC + 1];    // logits from the 4 parts of the contraction
-    float p[kHG][kKC + 4];                // probabilities of the chunk
+    u32x4_t q[kSteps][2][kWave];              // q hi / lo: MFMA A operand per step and lane
+    float ks[kMaxKG][kSK];                    // key-plane scale per group and key
+    float vs[kMaxVG][kSK];                    // value-plane scale per group and key (split planes)
+    float s[2][kHG][kSRow];                   // logits (two contraction halves), then probabilities
     float m[kHG], l[kHG], alpha[kHG];
-    int32_t src[kMaxSplitChunks * kKC];   // entry index / window slot per key, -1 masked
+    int32_t src[kMaxSplitChunks * kSK];       // entry index / window slot per key, -1 masked
 };
 
 struct AttnArgs {
@@ -87,10 +92,18 @@ struct AttnArgs {
     float *part_o;      // [B][HG][S][16][512] unnormalised partial outputs (S > 1)
     float *part_ml;     // [B][HG][S][2][16] partial max (log2 units) and sum
     int heads, k, window;
-    int n_sparse;       // chunks of selected entries
-    int n_chunks;       // + chunks of window rows
-    int splits, per_split;
+    int n_sparse, n_win;
+    int sparse_splits, per_sparse, per_win, splits;
     float scale_log2;   // softmax_scale * log2(e)
+};
+
+// Per-block constants shared by the chunk loop.
+struct Ctx {
+    int t, lane, w, col, grp;
+    int nloc;           // chunks of this block
+    int G, kshift;      // key groups per row; contraction step -> key group shift
+    size_t row0;        // first cache row of the sequence
+    const uint16_t *ring;
 };
 
 __device__ __forceinline__ u32x4_t lds16(const void *p) { return *reinterpret_cast<const u32x4_t *>(p); }
@@ -151,16 +164,335 @@ __device__ __forceinline__ void transpose_nibbles(const uint32_t (&in)[8], uint3
     for (int d = 0; d < 8; ++d) out[d] = a[d];
 }
 
-// Registers holding one chunk's HBM reads until they are written to LDS.
-struct Prefetch {
-    u32x4_t w[5];       // 16-byte pieces (sparse: key codes 0-1, value codes 2; window: 0-4)
-    float sc[3];        // key scales 0-1, value scales 2
+// One chunk's HBM reads, held in registers until they are written to LDS.
+// Every load is issued unconditionally: a masked key reads row 0 of its
+// sequence (always inside the cache) and is zeroed or ignored on the way to
+// LDS, so no load waits behind a branch.
+struct SparseRegs {
+    uint32_t v[16];     // value-plane words of key octets w and w + 8, word = lane
+    u32x4_t k[5];       // split planes: 16-byte pieces of key codes; one plane: k[0].xy = rope words
+    float sc[9];        // key scales 0-4, value scales 5-8 (group t / 128 + 4 i, key t % 128)
+    bool valid;         // key t % 128 is present (its scales are kept)
+};
+struct WindowRegs {
+    u32x4_t p[9];       // 64 rows x 72 pieces of 16 bytes
+    uint32_t valid;     // bit i: piece i's row is present
 };
 
+template <bool SPLIT, int VGS>
+__device__ __forceinline__ void fetch_sparse(const AttnArgs &a, const AttnSmem &sm, const Ctx &x, int lc,
+                                             SparseRegs &r)
+{
+    const cskv_cache &c = a.c;
+    const int32_t *src = sm.src + lc * kSK;
+    constexpr int VG = kDv / VGS;
+    int32_t e[16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int4 s0 = *reinterpret_cast<const int4 *>(src + 8 * (x.w + 8 * i));
+        const int4 s1 = *reinterpret_cast<const int4 *>(src + 8 * (x.w + 8 * i) + 4);
+        e[8 * i + 0] = s0.x; e[8 * i + 1] = s0.y; e[8 * i + 2] = s0.z; e[8 * i + 3] = s0.w;
+        e[8 * i + 4] = s1.x; e[8 * i + 5] = s1.y; e[8 * i + 6] = s1.z; e[8 * i + 7] = s1.w;
+    }
+    const int32_t es = src[x.t & (kSK - 1)];
+    const uint32_t *vplane = reinterpret_cast<const uint32_t *>(SPLIT ? c.v_codes : c.k_codes);
+    constexpr int kVRow = SPLIT ? kDv / 8 : kD / 8;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        r.v[j] = vplane[(x.row0 + (uint32_t)max(e[j], 0)) * kVRow + x.lane];
+    const uint32_t *kplane = reinterpret_cast<const uint32_t *>(c.k_codes);
+    if (!SPLIT) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {                      // rope words 64..71 of 128 rows
+            const int task = x.t + kThreads * i;
+            const int32_t er = src[task >> 3];
+            r.k[0][i] = kplane[(x.row0 + (uint32_t)max(er, 0)) * (kD / 8) + 64 + (task & 7)];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {                      // 128 rows x 18 pieces of key codes
+            const int task = min(x.t + kThreads * i, kSK * 18 - 1), row = task / 18, p = task % 18;
+            const int32_t er = src[row];
+            r.k[i] = *reinterpret_cast<const u32x4_t *>(kplane + (x.row0 + (uint32_t)max(er, 0)) * (kD / 8) + 4 * p);
+        }
+    }
+    const size_t srow = x.row0 + (uint32_t)max(es, 0);
+    r.valid = es >= 0;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {                          // key scales: group t / 128 + 4 i
+        const int g = min((x.t >> 7) + 4 * i, x.G - 1);
+        r.sc[i] = c.k_scales[srow * x.G + g];
+    }
+    if (SPLIT) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {                      // value scales: group t / 128 + 4 i < 16
+            const int g = min((x.t >> 7) + 4 * i, VG - 1);
+            r.sc[5 + i] = c.v_scales[srow * VG + g];
+        }
+    }
+}
+
+template <bool SPLIT, int VGS>
+__device__ __forceinline__ void store_sparse(AttnSmem &sm, const Ctx &x, const SparseRegs &r)
+{
+    constexpr int VG = kDv / VGS;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int o = x.w + 8 * i;
+        uint32_t in[8], tw[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) in[j] = r.v[8 * i + j];
+        if (!SPLIT) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sm.st.sp.kc[(8 * o + j) * kKcRow + x.lane] = in[j];
+        }
+        transpose_nibbles(in, tw);
+        uint32_t *vt = sm.st.sp.vt + (o >> 2) * kVtGroup + x.lane * kVtOct + (o & 3);
+#pragma unroll
+        for (int d = 0; d < 8; ++d) vt[4 * d] = tw[d];
+    }
+    if (!SPLIT) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int task = x.t + kThreads * i;
+            sm.st.sp.kc[(task >> 3) * kKcRow + 64 + (task & 7)] = r.k[0][i];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            const int task = x.t + kThreads * i, row = task / 18, p = task % 18;
+            if (task < kSK * 18) {
+                uint2 *dst = reinterpret_cast<uint2 *>(sm.st.sp.kc + row * kKcRow + 4 * p);
+                dst[0] = make_uint2(r.k[i][0], r.k[i][1]);
+                dst[1] = make_uint2(r.k[i][2], r.k[i][3]);
+            }
+        }
+    }
+    const int key = x.t & (kSK - 1);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const int g = (x.t >> 7) + 4 * i;
+        if (g < x.G) sm.ks[g][key] = r.valid ? r.sc[i] : 0.f;
+    }
+    if (SPLIT) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int g = (x.t >> 7) + 4 * i;
+            if (g < VG) sm.vs[g][key] = r.valid ? r.sc[5 + i] : 0.f;
+        }
+    }
+}
+
+__device__ __forceinline__ void fetch_window(const AttnSmem &sm, const Ctx &x, int lc, WindowRegs &r)
+{
+    const int32_t *src = sm.src + lc * kSK;
+    uint32_t valid = 0;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+        const int task = x.t + kThreads * i, row = task / 72, p = task % 72;
+        const int32_t slot = src[row];
+        valid |= (uint32_t)(slot >= 0) << i;
+        r.p[i] = *reinterpret_cast<const u32x4_t *>(x.ring + (size_t)max(slot, 0) * kD + 8 * p);
+    }
+    r.valid = valid;
+}
+
+__device__ __forceinline__ void store_window(AttnSmem &sm, const Ctx &x, const WindowRegs &r)
+{
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+        const int task = x.t + kThreads * i, row = task / 72, p = task % 72;
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4_t *>(&sm.st.win.kr[row][8 * p]) = ((r.valid >> i) & 1u) ? r.p[i] : z;
+    }
+}
+
+// Logits of one chunk.  Wave w takes contraction half w / 4 (9 steps) of two
+// key tiles (selected entries: tiles 2 (w % 4) and 2 (w % 4) + 1 of 8) or of
+// one (window rows: tile w % 4 of 4); the halves are added in the softmax.
+template <bool SPARSE>
+__device__ __forceinline__ void chunk_logits(AttnSmem &sm, const Ctx &x)
+{
+    const int half = x.w >> 2;
+    if (SPARSE) {
+        const int j0 = 32 * (x.w & 3) + x.col, j1 = j0 + 16;
+        const uint32_t *k0 = sm.st.sp.kc + j0 * kKcRow + x.grp;
+        const uint32_t *k1 = sm.st.sp.kc + j1 * kKcRow + x.grp;
+        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < kHalf; ++s) {
+            const int step = kHalf * half + s;
+            const u32x4_t qh = sm.q[step][0][x.lane], ql = sm.q[step][1][x.lane];
+            const u32x4_t kb0 = fp4x8_to_bf16x8(k0[4 * step]);
+            const u32x4_t kb1 = fp4x8_to_bf16x8(k1[4 * step]);
+            f32x4_t p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
+            p0 = mfma16x16x32(qh, kb0, p0);
+            p1 = mfma16x16x32(qh, kb1, p1);
+            p0 = mfma16x16x32(ql, kb0, p0);
+            p1 = mfma16x16x32(ql, kb1, p1);
+            const float sc0 = sm.ks[step >> x.kshift][j0], sc1 = sm.ks[step >> x.kshift][j1];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                acc0[v] = fmaf(sc0, p0[v], acc0[v]);
+                acc1[v] = fmaf(sc1, p1[v], acc1[v]);
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            sm.s[half][4 * x.grp + v][j0] = acc0[v];
+            sm.s[half][4 * x.grp + v][j1] = acc1[v];
+        }
+    } else {
+        const int j = 16 * (x.w & 3) + x.col;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < kHalf; ++s) {
+            const int step = kHalf * half + s;
+            const u32x4_t kb = lds16(&sm.st.win.kr[j][32 * step + 8 * x.grp]);
+            acc = mfma16x16x32(sm.q[step][0][x.lane], kb, acc);
+            acc = mfma16x16x32(sm.q[step][1][x.lane], kb, acc);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sm.s[half][4 * x.grp + v][j] = acc[v];
+    }
+}
+
+// Online softmax in base 2: thread t -> head t / 32, keys t % 32 + 32 i.
+// Probabilities overwrite the first logit half; m, l and the rescale factor
+// alpha of each head are updated by its first thread.
+template <bool SPARSE>
+__device__ __forceinline__ void chunk_softmax(AttnSmem &sm, const Ctx &x, int lc, float scale_log2)
+{
+    constexpr int NQ = (SPARSE ? kSK : kWK) / 32;
+    const int h = x.t >> 5, j0 = x.t & 31;
+    const int32_t *src = sm.src + lc * kSK;
+    float sv[NQ];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        const int j = j0 + 32 * i;
+        const float v = sm.s[0][h][j] + sm.s[1][h][j];
+        sv[i] = src[j] >= 0 ? v * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sv[i]);
+    }
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float m_old = sm.m[h];
+    const float m_new = fmaxf(m_old, mx);
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        const float pj = exp2f(sv[i] - m_new);
+        sm.s[0][h][j0 + 32 * i] = pj;
+        sum += pj;
+    }
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    if (j0 == 0) {
+        const float al = exp2f(m_old - m_new);
+        sm.alpha[h] = al;
+        sm.m[h] = m_new;
+        sm.l[h] = sm.l[h] * al + sum;
+    }
+}
+
+// P.V: wave w owns value dims [64 w, 64 w + 64) = 4 tiles of 16.  The value
+// group scales of selected entries are folded into P per group.
+template <bool SPARSE, bool SPLIT, int VGS>
+__device__ __forceinline__ void chunk_pv(const AttnSmem &sm, const Ctx &x, f32x4_t (&o)[4])
+{
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const float al = sm.alpha[4 * x.grp + v];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) o[nt][v] *= al;
+    }
+    constexpr int kGroupsHere = VGS >= 64 ? 1 : 64 / VGS;   // value groups per wave
+    constexpr int kTilesPerGroup = 4 / kGroupsHere;
+    constexpr int NKK = (SPARSE ? kSK : kWK) / 32;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        const int key0 = 32 * kk + 8 * x.grp;
+        const float4 p0 = *reinterpret_cast<const float4 *>(&sm.s[0][x.col][key0]);
+        const float4 p1 = *reinterpret_cast<const float4 *>(&sm.s[0][x.col][key0 + 4]);
+        const float pr[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+        for (int gi = 0; gi < (SPARSE ? kGroupsHere : 1); ++gi) {
+            float pv[8];
+            if (SPARSE) {
+                const int gv = (64 * x.w) / VGS + gi;
+                const float *vsr = SPLIT ? &sm.vs[gv][key0] : &sm.ks[gv][key0];
+                const float4 v0 = *reinterpret_cast<const float4 *>(vsr);
+                const float4 v1 = *reinterpret_cast<const float4 *>(vsr + 4);
+                pv[0] = pr[0] * v0.x; pv[1] = pr[1] * v0.y; pv[2] = pr[2] * v0.z; pv[3] = pr[3] * v0.w;
+                pv[4] = pr[4] * v1.x; pv[5] = pr[5] * v1.y; pv[6] = pr[6] * v1.z; pv[7] = pr[7] * v1.w;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pv[i] = pr[i];
+            }
+            u32x4_t phi, plo;
+            split8(pv, phi, plo);
+            constexpr int kTiles = SPARSE ? kTilesPerGroup : 4;
+#pragma unroll
+            for (int tt = 0; tt < kTiles; ++tt) {
+                const int nt = gi * kTiles + tt;
+                const int dim = 64 * x.w + 16 * nt + x.col;
+                u32x4_t vb;
+                if (SPARSE) {
+                    vb = fp4x8_to_bf16x8(sm.st.sp.vt[kk * kVtGroup + (dim >> 3) * kVtOct + 4 * (dim & 7) + x.grp]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        vb[i] = (uint32_t)sm.st.win.kr[key0 + 2 * i][dim] |
+                                ((uint32_t)sm.st.win.kr[key0 + 2 * i + 1][dim] << 16);
+                }
+                o[nt] = mfma16x16x32(phi, vb, o[nt]);
+                o[nt] = mfma16x16x32(plo, vb, o[nt]);
+            }
+        }
+    }
+}
+
+// The chunk loop of one block: the next chunk's HBM reads are in flight
+// while the current chunk is computed.
+template <bool SPARSE, bool SPLIT, int VGS>
+__device__ __forceinline__ void run_chunks(const AttnArgs &a, AttnSmem &sm, const Ctx &x, f32x4_t (&o)[4])
+{
+    if (SPARSE) {
+        SparseRegs r;
+        fetch_sparse<SPLIT, VGS>(a, sm, x, 0, r);
+        for (int lc = 0; lc < x.nloc; ++lc) {
+            __syncthreads();                               // previous chunk fully consumed
+            store_sparse<SPLIT, VGS>(sm, x, r);
+            __syncthreads();
+            if (lc + 1 < x.nloc) fetch_sparse<SPLIT, VGS>(a, sm, x, lc + 1, r);
+            chunk_logits<true>(sm, x);
+            __syncthreads();
+            chunk_softmax<true>(sm, x, lc, a.scale_log2);
+            __syncthreads();
+            chunk_pv<true, SPLIT, VGS>(sm, x, o);
+        }
+    } else {
+        WindowRegs r;
+        fetch_window(sm, x, 0, r);
+        for (int lc = 0; lc < x.nloc; ++lc) {
+            __syncthreads();
+            store_window(sm, x, r);
+            __syncthreads();
+            if (lc + 1 < x.nloc) fetch_window(sm, x, lc + 1, r);
+            chunk_logits<false>(sm, x);
+            __syncthreads();
+            chunk_softmax<false>(sm, x, lc, a.scale_log2);
+            __syncthreads();
+            chunk_pv<false, SPLIT, VGS>(sm, x, o);
+        }
+    }
+}
+
 // VGS: the value group size in effect (the value plane's group, else the key
-// plane's): 32, 64 or 128.
-template <int VGS>
-__global__ __launch_bounds__(kThreads, 2) void sparse_attn_kernel(AttnArgs a)
+// plane's): 32, 64 or 128.  SPLIT: the cache has a separate value plane.
+template <int VGS, bool SPLIT>
+__global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a)
 {
     __shared__ AttnSmem sm;
     const cskv_cache &c = a.c;
@@ -173,239 +505,68 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_kernel(AttnArgs a)
     const int hg = rest % HG, u = (rest / HG) * 8 + xcd;
     if (u >= U) return;
     const int b = u / a.splits, split = u % a.splits;
-    const int c0 = split * a.per_split;
-    const int c1 = min(a.n_chunks, c0 + a.per_split);
+    const bool sparse = split < a.sparse_splits;
+    const int c0 = sparse ? split * a.per_sparse : (split - a.sparse_splits) * a.per_win;
+    const int c1 = sparse ? min(a.n_sparse, c0 + a.per_sparse) : min(a.n_win, c0 + a.per_win);
 
-    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
-    const int col = lane & 15, grp = lane >> 4;
+    Ctx x;
+    x.t = threadIdx.x;
+    x.lane = x.t & (kWave - 1);
+    x.w = x.t / kWave;
+    x.col = x.lane & 15;
+    x.grp = x.lane >> 4;
+    x.nloc = c1 - c0;
+    x.G = kD / c.k_group;
+    x.kshift = __builtin_ctz((unsigned)c.k_group) - 5;
+    x.row0 = (size_t)b * c.capacity;
+    x.ring = a.swa + (size_t)b * a.window * kD;
     const int64_t E = entries_of(c.n_tokens, b, c.capacity);
     int64_t nswa = a.swa_len ? (int64_t)a.swa_len[b] : (int64_t)c.n_tokens[b];
     nswa = nswa < 0 ? 0 : (nswa > a.window ? a.window : nswa);
 
-    const int kg = c.k_group, G = kD / kg;
-    const bool split_v = c.v_group > 0;
-    constexpr int VG = kDv / VGS;
-    const float *vscales = split_v ? c.v_scales : c.k_scales;
-    const int vscale_row = split_v ? VG : G;
-    const size_t row0 = (size_t)b * c.capacity;
-
     // ---- key sources of every chunk of the split
-    for (int i = t; i < (c1 - c0) * kKC; i += kThreads) {
-        const int chunk = c0 + i / kKC, j = i % kKC;
+    for (int i = x.t; i < x.nloc * kSK; i += kThreads) {
+        const int chunk = c0 + i / kSK, j = i % kSK;
         int32_t s = -1;
-        if (chunk < a.n_sparse) {
-            const int jj = chunk * kKC + j;
+        if (sparse) {
+            const int jj = chunk * kSK + j;
             const int32_t e = jj < a.k ? a.idx[(size_t)b * a.k + jj] : -1;
             s = (e >= 0 && e < E) ? e : -1;
-        } else {
-            const int64_t slot = (int64_t)(chunk - a.n_sparse) * kKC + j;
+        } else if (j < kWK) {
+            const int64_t slot = (int64_t)chunk * kWK + j;
             s = slot < nswa ? (int32_t)slot : -1;
         }
         sm.src[i] = s;
     }
-    if (t < kHG) { sm.m[t] = -1e30f; sm.l[t] = 0.f; }
-
-    // ---- query operands: wave w takes key tile kt = w & 1 and contraction
-    // steps [s0, s0 + ns) of part w >> 1; rows = heads of this group, hi + lo
-    const int kt = w & 1, part = w >> 1;
-    const int s0 = part_begin(part), ns = part_begin(part + 1) - s0;
-    u32x4_t qhi[kMaxPart], qlo[kMaxPart];
+    // ---- query operands of the 16 heads, hi + lo, per contraction step
     {
-        const float *qrow = a.q + ((size_t)b * a.heads + kHG * hg + col) * kD + 8 * grp;
-#pragma unroll
-        for (int s = 0; s < kMaxPart; ++s) {
-            const int step = s < ns ? s0 + s : s0;
-            const float4 x0 = *reinterpret_cast<const float4 *>(qrow + 32 * step);
-            const float4 x1 = *reinterpret_cast<const float4 *>(qrow + 32 * step + 4);
-            const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-            split8(x, qhi[s], qlo[s]);
+        const float *qbase = a.q + ((size_t)b * a.heads + kHG * hg) * kD;
+        for (int i = x.t; i < kSteps * kWave; i += kThreads) {
+            const int s = i / kWave, ln = i % kWave;
+            const float *qr = qbase + (size_t)(ln & 15) * kD + 32 * s + 8 * (ln >> 4);
+            const float4 x0 = *reinterpret_cast<const float4 *>(qr);
+            const float4 x1 = *reinterpret_cast<const float4 *>(qr + 4);
+            const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            u32x4_t hi, lo;
+            split8(xv, hi, lo);
+            sm.q[s][0][ln] = hi;
+            sm.q[s][1][ln] = lo;
         }
     }
+    if (x.t < kHG) { sm.m[x.t] = -1e30f; sm.l[x.t] = 0.f; }
     f32x4_t o[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) o[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     __syncthreads();
 
-    // ---- HBM reads of one chunk into registers
-    auto fetch = [&](int chunk, Prefetch &pf) {
-        const int32_t *src = sm.src + (chunk - c0) * kKC;
-        if (chunk < a.n_sparse) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {                  // 32 keys x 18 pieces of key codes
-                const int task = t + kThreads * i, j = task / 18, piece = task % 18;
-                u32x4_t v = {0u, 0u, 0u, 0u};
-                if (task < kKC * 18 && src[j] >= 0)
-                    v = *reinterpret_cast<const u32x4_t *>(c.k_codes + (row0 + src[j]) * (kD / 2) + 16 * piece);
-                pf.w[i] = v;
-            }
-            if (split_v) {                                 // 32 keys x 16 pieces of value codes
-                const int j = t / 16, piece = t % 16;
-                u32x4_t v = {0u, 0u, 0u, 0u};
-                if (src[j] >= 0)
-                    v = *reinterpret_cast<const u32x4_t *>(c.v_codes + (row0 + src[j]) * (kDv / 2) + 16 * piece);
-                pf.w[2] = v;
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {                  // key scales: 32 x G
-                const int task = t + kThreads * i, j = task / G, g = task % G;
-                pf.sc[i] = (task < kKC * G && src[j] >= 0) ? c.k_scales[(row0 + src[j]) * G + g] : 0.f;
-            }
-            {                                              // value scales: 32 x VG
-                const int j = t / VG, g = t % VG;
-                pf.sc[2] = (t < kKC * VG && src[j] >= 0) ? vscales[(row0 + src[j]) * vscale_row + g] : 0.f;
-            }
-        } else {
-            const uint16_t *ring = a.swa + (size_t)b * a.window * kD;
-#pragma unroll
-            for (int i = 0; i < 5; ++i) {                  // 32 rows x 72 pieces
-                const int task = t + kThreads * i, j = task / 72, piece = task % 72;
-                u32x4_t v = {0u, 0u, 0u, 0u};
-                if (task < kKC * 72 && src[j] >= 0)
-                    v = *reinterpret_cast<const u32x4_t *>(ring + (size_t)src[j] * kD + 8 * piece);
-                pf.w[i] = v;
-            }
-        }
-    };
-
-    auto store = [&](int chunk, const Prefetch &pf) {
-        if (chunk < a.n_sparse) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int task = t + kThreads * i, j = task / 18, piece = task % 18;
-                if (task < kKC * 18) *reinterpret_cast<u32x4_t *>(&sm.st.sp.kc[j][16 * piece]) = pf.w[i];
-            }
-            if (split_v) *reinterpret_cast<u32x4_t *>(&sm.st.sp.vc[t / 16][16 * (t % 16)]) = pf.w[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int task = t + kThreads * i;
-                if (task < kKC * G) sm.ks[task / G][task % G] = pf.sc[i];
-            }
-            if (t < kKC * VG) sm.vs[t / VG][t % VG] = pf.sc[2];
-        } else {
-#pragma unroll
-            for (int i = 0; i < 5; ++i) {
-                const int task = t + kThreads * i, j = task / 72, piece = task % 72;
-                if (task < kKC * 72) *reinterpret_cast<u32x4_t *>(&sm.st.win.kr[j][8 * piece]) = pf.w[i];
-            }
-            for (int i = t; i < kKC * kMaxKG; i += kThreads) sm.ks[i / kMaxKG][i % kMaxKG] = 1.f;
-            for (int i = t; i < kKC * kMaxVG; i += kThreads) sm.vs[i / kMaxVG][i % kMaxVG] = 1.f;
-        }
-    };
-
-    Prefetch pf;
-    if (c0 < c1) fetch(c0, pf);
-    for (int chunk = c0; chunk < c1; ++chunk) {
-        const bool sparse = chunk < a.n_sparse;
-        const int32_t *src = sm.src + (chunk - c0) * kKC;
-        __syncthreads();                                   // previous chunk fully consumed
-        store(chunk, pf);
-        __syncthreads();
-        if (chunk + 1 < c1) fetch(chunk + 1, pf);
-
-        // ---- value codes transposed to [dim][key word]: task = (key octet, dim octet)
-        if (sparse) {
-            if (t < 256) {
-                const int oct = t & 3, doct = t >> 2;      // 4 key octets x 64 dim octets
-                uint32_t in[8], outw[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    in[j] = split_v ? *reinterpret_cast<const uint32_t *>(&sm.st.sp.vc[8 * oct + j][4 * doct])
-                                    : *reinterpret_cast<const uint32_t *>(&sm.st.sp.kc[8 * oct + j][4 * doct]);
-                transpose_nibbles(in, outw);
-#pragma unroll
-                for (int d = 0; d < 8; ++d) sm.st.sp.vt[8 * doct + d][oct] = outw[d];
-            }
-            __syncthreads();
-        }
-
-        // ---- logits of key tile kt over this wave's contraction steps
-        {
-            const int j = 16 * kt + col;
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < kMaxPart; ++s) {
-                if (s < ns) {
-                    const int step = s0 + s;
-                    u32x4_t kb;
-                    if (sparse) kb = fp4x8_to_bf16x8(*reinterpret_cast<const uint32_t *>(&sm.st.sp.kc[j][16 * step + 4 * grp]));
-                    else kb = lds16(&sm.st.win.kr[j][32 * step + 8 * grp]);
-                    f32x4_t pr = {0.f, 0.f, 0.f, 0.f};
-                    pr = mfma16x16x32(qhi[s], kb, pr);
-                    pr = mfma16x16x32(qlo[s], kb, pr);
-                    const float sc = sm.ks[j][(32 * step) / kg];
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) acc[v] = fmaf(sc, pr[v], acc[v]);
-                }
-            }
-#pragma unroll
-            for (int v = 0; v < 4; ++v) sm.spart[part][4 * grp + v][j] = acc[v];
-        }
-        __syncthreads();
-
-        // ---- online softmax: thread t -> head t / 32, key t % 32
-        {
-            const int h = t >> 5, j = t & 31;
-            const float sum4 = (sm.spart[0][h][j] + sm.spart[1][h][j]) + (sm.spart[2][h][j] + sm.spart[3][h][j]);
-            const float sv = src[j] >= 0 ? sum4 * a.scale_log2 : -INFINITY;
-            float mx = sv;
-#pragma unroll
-            for (int off = 16; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-            const float m_old = sm.m[h];
-            const float m_new = fmaxf(m_old, mx);
-            const float pj = exp2f(sv - m_new);
-            float sum = pj;
-#pragma unroll
-            for (int off = 16; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-            sm.p[h][j] = pj;
-            if (j == 0) {
-                const float al = exp2f(m_old - m_new);
-                sm.alpha[h] = al;
-                sm.m[h] = m_new;
-                sm.l[h] = sm.l[h] * al + sum;
-            }
-        }
-        __syncthreads();
-
-        // ---- P.V: wave w owns value dims [64 w, 64 w + 64) = 4 tiles of 16
-        {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float al = sm.alpha[4 * grp + v];
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt) o[nt][v] *= al;
-            }
-            constexpr int kGroupsHere = VGS >= 64 ? 1 : 64 / VGS;   // value groups per wave
-            constexpr int kTilesPerGroup = 4 / kGroupsHere;
-#pragma unroll
-            for (int gi = 0; gi < kGroupsHere; ++gi) {
-                const int gv = (64 * w) / VGS + gi;
-                float pv[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) pv[i] = sm.p[col][8 * grp + i] * sm.vs[8 * grp + i][gv];
-                u32x4_t phi, plo;
-                split8(pv, phi, plo);
-#pragma unroll
-                for (int tt = 0; tt < kTilesPerGroup; ++tt) {
-                    const int nt = gi * kTilesPerGroup + tt;
-                    const int dim = 64 * w + 16 * nt + col;
-                    u32x4_t vb;
-                    if (sparse) {
-                        vb = fp4x8_to_bf16x8(sm.st.sp.vt[dim][grp]);
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            vb[i] = (uint32_t)sm.st.win.kr[8 * grp + 2 * i][dim] |
-                                    ((uint32_t)sm.st.win.kr[8 * grp + 2 * i + 1][dim] << 16);
-                    }
-                    o[nt] = mfma16x16x32(phi, vb, o[nt]);
-                    o[nt] = mfma16x16x32(plo, vb, o[nt]);
-                }
-            }
-        }
+    if (x.nloc > 0) {
+        if (sparse) run_chunks<true, SPLIT, VGS>(a, sm, x, o);
+        else run_chunks<false, SPLIT, VGS>(a, sm, x, o);
     }
     __syncthreads();
 
     // ---- results: final (one split) or partial (merged by attn_merge_kernel)
+    const int t = x.t, w = x.w, col = x.col, grp = x.grp;
     const size_t head0 = (size_t)b * a.heads + kHG * hg;
     if (a.splits == 1) {
 #pragma unroll
@@ -482,18 +643,29 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a)
 
 AttnPlan attn_plan(const cskv_cache &c, int heads, int k, int window)
 {
+    // Blocks of 8 waves, one per CU (the staging takes most of the LDS).  The
+    // split is chosen from a rough cost per block -- setup, then per chunk a
+    // fixed cost that is about twice as high for 128 entries as for 64 window
+    // rows -- times the rounds of 256 blocks, plus the merge when splitting.
     AttnPlan p;
-    p.n_sparse = (k + kKC - 1) / kKC;
-    p.n_chunks = p.n_sparse + (window + kKC - 1) / kKC;
-    const int hg = heads / kHG;
-    // about one block (8 waves) per CU
-    int splits = (256 + c.batch * hg - 1) / (c.batch * hg);
-    splits = splits < 1 ? 1 : (splits > p.n_chunks ? p.n_chunks : splits);
-    p.per_split = (p.n_chunks + splits - 1) / splits;
-    if (p.per_split > kMaxSplitChunks) p.per_split = kMaxSplitChunks;
-    p.splits = (p.n_chunks + p.per_split - 1) / p.per_split;
-    const size_t units = (size_t)c.batch * hg * p.splits;
-    p.ws_bytes = p.splits > 1 ? units * kHG * (kDv + 2) * sizeof(float) + 256 : 0;
+    p.n_sparse = (k + kSK - 1) / kSK;
+    p.n_win = (window + kWK - 1) / kWK;
+    const int units = c.batch * (heads / kHG);
+    double best = 1e300;
+    p.per_sparse = p.n_sparse;
+    p.per_win = p.n_win;
+    for (int ps = 1; ps <= p.n_sparse && ps <= kMaxSplitChunks; ++ps)
+        for (int pw = 1; pw <= p.n_win && pw <= kMaxSplitChunks; ++pw) {
+            const int ss = (p.n_sparse + ps - 1) / ps, sw = (p.n_win + pw - 1) / pw;
+            const double blocks = (double)units * (ss + sw);
+            const double rounds = ceil(blocks / 256.0);
+            const double cost = rounds * (3.0 + fmax(2.0 * ps, 1.0 * pw)) + (ss + sw > 1 ? 4.0 : 0.0);
+            if (cost < best - 1e-9) { best = cost; p.per_sparse = ps; p.per_win = pw; }
+        }
+    p.sparse_splits = (p.n_sparse + p.per_sparse - 1) / p.per_sparse;
+    p.splits = p.sparse_splits + (p.n_win + p.per_win - 1) / p.per_win;
+    const size_t parts = (size_t)units * p.splits;
+    p.ws_bytes = p.splits > 1 ? parts * kHG * (kDv + 2) * sizeof(float) + 256 : 0;
     return p;
 }
 
@@ -507,15 +679,21 @@ hipError_t launch_sparse_attn(const cskv_cache &c, const float *q, int heads, co
     float *part_o = p.splits > 1 ? static_cast<float *>(ws) : nullptr;
     float *part_ml = p.splits > 1 ? part_o + units * kHG * kDv : nullptr;
     AttnArgs a{c, q, idx, swa, swa_len, out, lse, part_o, part_ml, heads, k, window,
-               p.n_sparse, p.n_chunks, p.splits, p.per_split,
+               p.n_sparse, p.n_win, p.sparse_splits, p.per_sparse, p.per_win, p.splits,
                (float)((double)scale * 1.4426950408889634)};
     const int U = c.batch * p.splits;
     const unsigned blocks = (unsigned)(8 * hg * ((U + 7) / 8));
     const int vgs = c.v_group > 0 ? c.v_group : c.k_group;
     timer_before(CSKV_KERNEL_ATTENTION, s);
-    if (vgs == 32) sparse_attn_kernel<32><<<blocks, kThreads, 0, s>>>(a);
-    else if (vgs == 64) sparse_attn_kernel<64><<<blocks, kThreads, 0, s>>>(a);
-    else sparse_attn_kernel<128><<<blocks, kThreads, 0, s>>>(a);
+    if (c.v_group > 0) {
+        if (vgs == 32) sparse_attn_kernel<32, true><<<blocks, kThreads, 0, s>>>(a);
+        else if (vgs == 64) sparse_attn_kernel<64, true><<<blocks, kThreads, 0, s>>>(a);
+        else sparse_attn_kernel<128, true><<<blocks, kThreads, 0, s>>>(a);
+    } else {
+        if (vgs == 32) sparse_attn_kernel<32, false><<<blocks, kThreads, 0, s>>>(a);
+        else if (vgs == 64) sparse_attn_kernel<64, false><<<blocks, kThreads, 0, s>>>(a);
+        else sparse_attn_kernel<128, false><<<blocks, kThreads, 0, s>>>(a);
+    }
     if (p.splits > 1) attn_merge_kernel<<<(unsigned)(c.batch * hg), 256, 0, s>>>(a);
     timer_after(CSKV_KERNEL_ATTENTION, s);
     return hipGetLastError();

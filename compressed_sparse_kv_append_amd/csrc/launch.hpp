@@ -31,11 +31,14 @@ hipError_t launch_swa_append(uint16_t *ring, int batch, int window, int dim, con
 hipError_t launch_indexer_topk(const cskv_cache &c, const uint16_t *q_idx, int heads,
                                const float *head_w, int k, int32_t *out_idx, void *ws,
                                hipStream_t s);
-// Attention work split: chunks of 32 keys (selected entries, then window
-// rows) cut into `splits` runs of `per_split` chunks; ws_bytes of partial
-// results when splits > 1.
+// Split of the keys of one (sequence, head group) over blocks: selected
+// entries in chunks of 128, window rows in chunks of 64; a split holds chunks
+// of one kind only.  Splits [0, sparse_splits) take per_sparse entry chunks
+// each, the rest per_win window chunks each.  ws_bytes: partial results
+// when splits > 1.
 struct AttnPlan {
-    int n_sparse, n_chunks, splits, per_split;
+    int n_sparse, n_win;
+    int sparse_splits, per_sparse, per_win, splits;
     size_t ws_bytes;
 };
 AttnPlan attn_plan(const cskv_cache &c, int heads, int k, int window);

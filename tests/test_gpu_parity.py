@@ -241,7 +241,7 @@ def _attn_case(ck, orc, k_group, v_group, lens, heads, k, nswa, seed, window=128
 
 
 @pytest.mark.parametrize("k_group,v_group,law", [(32, 0, "normal"), (64, 0, "t3"), (32, 128, "normal"),
-                                                  (64, 64, "t3")])
+                                                  (64, 64, "t3"), (64, 32, "normal"), (64, 128, "t3")])
 def test_attention_parity(ck, orc, k_group, v_group, law):
     err = _attn_case(ck, orc, k_group, v_group, lens=[700, 40, 513], heads=32, k=512,
                      nswa=[128, 5, 0], seed=20 + k_group + v_group, law=law)
@@ -251,6 +251,13 @@ def test_attention_parity(ck, orc, k_group, v_group, law):
 def test_attention_edge_cases(ck, orc):
     # no keys at all, only window keys, a single key, k not a multiple of 32
     _attn_case(ck, orc, 32, 0, lens=[0, 0, 1, 100], heads=16, k=37, nswa=[0, 3, 0, 128], seed=30)
+
+
+def test_attention_longest_selection_and_window(ck, orc):
+    # k = 2048 selected entries and a 1024-row window with 64 heads: the most
+    # chunks a sequence can have, spread over several splits per head group
+    _attn_case(ck, orc, 64, 0, lens=[2600, 2100], heads=64, k=2048, nswa=[1024, 700], seed=33,
+               window=1024)
 
 
 def test_attention_invalid_indices_are_skipped(ck, orc):
