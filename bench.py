@@ -9,7 +9,14 @@ window append, indexer scan + exact top-512, gather/dequantise + attention.
 
 Inputs are seeded synthetic data resident in HBM before timing.  Several
 cache replicas are stepped in rotation so consecutive steps do not hit the
-last-level cache with the previous step's data.
+last-level cache with the previous step's data.  The timed steps are plain
+launches; the indexer scan, the kernel the roofline is quoted for, is timed
+live with HIP events on its launch stream on one timed step in
+--scan-sample-every (each event pair adds a few microseconds to its step).
+The per-kernel breakdown comes from a separate eager pass after the timed
+steps with every kernel timer on.  --graph instead captures each replica's
+step in a HIP graph and times graph replays (the scan time then comes from
+the separate pass).
 
 Prints one JSON line (rank 0).  --copy-probe MIB instead runs a plain
 device copy of known size, used to calibrate hardware byte counters.
@@ -48,6 +55,8 @@ def parse():
     p.add_argument("--replicas", type=int, default=2)
     p.add_argument("--cpu-baseline-seqs", type=int, default=16)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--graph", action="store_true", help="time HIP graph replays of the step")
+    p.add_argument("--scan-sample-every", type=int, default=4)
     p.add_argument("--copy-probe", type=int, default=0, help="MiB copied by a plain device copy")
     return p.parse_args()
 
@@ -168,7 +177,8 @@ def main():
     ck.lib()
     w = synth.WORKLOADS[a.workload]
     assert w.entries is not None and len(w.layers) == 1, "bench steps fixed-length single-layer workloads"
-    total_steps = a.warmup + a.steps
+    timer_steps = min(a.steps, 100)
+    total_steps = a.warmup + timer_steps + a.steps + a.replicas
     per_rep = (total_steps + a.replicas - 1) // a.replicas
     cap = w.entries + (per_rep + 1) // 2 + 16
 
@@ -200,23 +210,59 @@ def main():
         io = per_rep_io[r]
         ck.layer_group_decode(reps[r], io["layers"], tok, W, irow, w.topk, w.window, scale, ws=io["ws"])
 
-    for i in range(a.warmup):
-        step(i)
-    torch.cuda.synchronize()
     kinds = {"append": ck.KERNEL_APPEND, "swa_append": ck.KERNEL_SWA_APPEND,
              "indexer_scan": ck.KERNEL_INDEXER_SCAN, "topk_select": ck.KERNEL_TOPK_SELECT,
              "attention": ck.KERNEL_ATTENTION}
-    for kd in kinds.values():
-        ck.timer_enable(kd, a.steps)
+    i = 0
+    for _ in range(a.warmup):
+        step(i)
+        i += 1
+    torch.cuda.synchronize()
+
+    graphs = []
+    if a.graph:
+        for r in range(a.replicas):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(r)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for r in range(a.replicas):          # one untimed replay per replica
+            graphs[(i + r) % a.replicas].replay()
+        i += a.replicas
+        torch.cuda.synchronize()
+    every = max(1, a.scan_sample_every)
+    if not a.graph:
+        ck.timer_enable(ck.KERNEL_INDEXER_SCAN, (a.steps + every - 1) // every)
+
     ent_before = np.mean([r.n_tokens.float().mean().item() for r in reps]) / 2
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
-    for i in range(a.warmup, total_steps):
-        step(i)
+    for j in range(a.steps):
+        if a.graph:
+            graphs[(i + j) % a.replicas].replay()
+        else:
+            ck.timer_pause(ck.KERNEL_INDEXER_SCAN, j % every != 0)
+            step(i + j)
     e1.record()
     torch.cuda.synchronize()
+    i += a.steps
     ms = e0.elapsed_time(e1) / a.steps
+    live = None
+    if not a.graph:
+        tot, n = ck.timer_read(ck.KERNEL_INDEXER_SCAN)
+        live = {"avg_us": 1000 * tot / max(n, 1), "launches": n}
+        ck.timer_disable_all()
+    ent_after = np.mean([r.n_tokens.float().mean().item() for r in reps]) / 2
+
+    # per-kernel breakdown: separate eager pass with every timer on
+    for kd in kinds.values():
+        ck.timer_enable(kd, timer_steps)
+    for _ in range(timer_steps):
+        step(i)
+        i += 1
+    torch.cuda.synchronize()
     kern = {}
     for name, kd in kinds.items():
         tot, n = ck.timer_read(kd)
@@ -226,11 +272,11 @@ def main():
     assert all(s == 0 for s in status), f"cache status flags raised: {status}"
 
     # mean entries per sequence over the timed steps
-    ent_after = np.mean([r.n_tokens.float().mean().item() for r in reps]) / 2
     entries_mean = float(0.5 * (ent_before + ent_after))
     sb = step_bytes(w, entries_mean)
     scan_bytes = sb["indexer_keys"] + sb["indexer_q"]
-    scan_us = kern["indexer_scan"]["avg_us"]
+    scan = live if live is not None else kern["indexer_scan"]
+    scan_us = scan["avg_us"]
     achieved = scan_bytes / (scan_us * 1e-6) / 1e9
     steps_per_s = 1000.0 / ms
     result = {
@@ -250,11 +296,15 @@ def main():
                    "entries_per_seq": w.entries, "k_group": w.k_group, "storage": "e2m1+fp32 scales",
                    "idx_heads": w.idx_heads, "idx_dim": w.idx_dim, "q_heads": w.q_heads,
                    "topk": w.topk, "window": w.window, "replicas": a.replicas,
+                   "launch": "hip_graph" if a.graph else "eager",
                    "tokens_per_s": round(steps_per_s * B, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": pmc_traffic(), "kernel": "indexer_scan",
-                     "bytes_per_launch": round(scan_bytes), "avg_us": round(scan_us, 2)},
+                     "bytes_per_launch": round(scan_bytes), "avg_us": round(scan_us, 2),
+                     "timed_launches": scan["launches"],
+                     "timing": ("hip events in the timed region, 1 step in %d" % every) if live is not None
+                     else "hip events, separate eager pass"},
         "step_bytes": round(sb["total"]),
         "step_hbm_frac": round(sb["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},

@@ -35,7 +35,7 @@ OP_INDEXER_TOPK, OP_SPARSE_ATTN, OP_LAYER_GROUP = 1, 2, 3
 
 EXPORTS = ("cskv_kv_append_fp4", "cskv_append_workspace_bytes", "cskv_swa_append", "cskv_indexer_topk", "cskv_sparse_attn_decode",
            "cskv_layer_group_decode", "cskv_workspace_bytes", "cskv_entry_bytes", "cskv_last_error",
-           "cskv_timer_enable", "cskv_timer_read", "cskv_timer_disable_all")
+           "cskv_timer_enable", "cskv_timer_pause", "cskv_timer_read", "cskv_timer_disable_all")
 
 
 class CskvError(RuntimeError):
@@ -86,9 +86,11 @@ def lib():
         L.cskv_entry_bytes.restype = sz
         L.cskv_last_error.restype = C.c_char_p
         L.cskv_timer_enable.argtypes = [i32, i32]
+        L.cskv_timer_pause.argtypes = [i32, i32]
         L.cskv_timer_read.argtypes = [i32, C.POINTER(C.c_double), C.POINTER(C.c_int32)]
         for f in ("cskv_kv_append_fp4", "cskv_swa_append", "cskv_indexer_topk", "cskv_sparse_attn_decode",
-                  "cskv_layer_group_decode", "cskv_timer_enable", "cskv_timer_read", "cskv_timer_disable_all"):
+                  "cskv_layer_group_decode", "cskv_timer_enable", "cskv_timer_pause", "cskv_timer_read",
+                  "cskv_timer_disable_all"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -302,6 +304,10 @@ def layer_group_decode(cache: Cache, layers: Sequence[Layer], new_tokens: Option
 
 def timer_enable(kind: int, max_launches: int) -> None:
     _check(lib().cskv_timer_enable(kind, max_launches))
+
+
+def timer_pause(kind: int, paused: bool) -> None:
+    _check(lib().cskv_timer_pause(kind, int(bool(paused))))
 
 
 def timer_read(kind: int):

@@ -114,7 +114,7 @@ int attn_args(const cskv_cache *c, const float *q, int32_t heads, const int32_t 
 // ---------------------------------------------------------------- timers
 
 struct Timer {
-    bool on = false;
+    bool on = false, paused = false;
     int max = 0, count = 0;
     std::vector<hipEvent_t> start, stop;
 };
@@ -133,12 +133,12 @@ namespace cskv {
 void timer_before(int kind, hipStream_t s)
 {
     Timer &T = g_timers[kind];
-    if (T.on && T.count < T.max) (void)hipEventRecord(T.start[T.count], s);
+    if (T.on && !T.paused && T.count < T.max) (void)hipEventRecord(T.start[T.count], s);
 }
 void timer_after(int kind, hipStream_t s)
 {
     Timer &T = g_timers[kind];
-    if (T.on && T.count < T.max) (void)hipEventRecord(T.stop[T.count++], s);
+    if (T.on && !T.paused && T.count < T.max) (void)hipEventRecord(T.stop[T.count++], s);
 }
 }  // namespace cskv
 
@@ -326,6 +326,13 @@ int cskv_timer_enable(int32_t kind, int32_t max_launches)
     }
     T.max = max_launches;
     T.on = true;
+    return CSKV_OK;
+}
+
+int cskv_timer_pause(int32_t kind, int32_t paused)
+{
+    REQUIRE(kind >= 1 && kind < 8, CSKV_EINVAL, "kernel kind %d", kind);
+    g_timers[kind].paused = paused != 0;
     return CSKV_OK;
 }
 

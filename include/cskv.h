@@ -238,7 +238,10 @@ const char *cskv_last_error(void);
  * Kernel timers for measurement.  When enabled for a kernel kind, the library
  * records a hipEvent pair around each of the next `max_launches` launches of
  * that kind on the launch stream; cskv_timer_read waits for them and returns
- * the summed milliseconds and the count.  Not thread-safe; meant for benches.
+ * the summed milliseconds and the count.  cskv_timer_pause(kind, 1) stops
+ * recording for that kind (launches run untimed, no events are recorded)
+ * until cskv_timer_pause(kind, 0), so a bench can time a sample of its
+ * steps.  Not thread-safe; meant for benches.
  */
 #define CSKV_KERNEL_APPEND 1
 #define CSKV_KERNEL_SWA_APPEND 2
@@ -246,6 +249,7 @@ const char *cskv_last_error(void);
 #define CSKV_KERNEL_TOPK_SELECT 4
 #define CSKV_KERNEL_ATTENTION 5
 int cskv_timer_enable(int32_t kernel_kind, int32_t max_launches);
+int cskv_timer_pause(int32_t kernel_kind, int32_t paused);
 int cskv_timer_read(int32_t kernel_kind, double *total_ms, int32_t *count);
 int cskv_timer_disable_all(void);
 
