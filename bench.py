@@ -39,7 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "CSA2 FP4 sparse decode: steps/s at 64K ctx; achieved % of 8 TB/s HBM"
 HBM_PEAK_GBPS = 8000.0
 PMC_FILE = os.path.join(ROOT, "profiles", "indexer_scan_decode_64k_b32_pmc.json")
-SCAN_SRC = os.path.join(ROOT, "compressed_sparse_kv_append_amd", "csrc", "indexer.hip")
+SCAN_SRC = os.path.join(ROOT, "compressed_sparse_kv_append_amd", "csrc", "scan.hip")
 
 
 def log(*a):

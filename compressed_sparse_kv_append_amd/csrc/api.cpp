@@ -130,15 +130,16 @@ void free_timer(Timer &T)
 }  // namespace
 
 namespace cskv {
-void timer_before(int kind, hipStream_t s)
+TimedLaunch timer_take(int kind)
 {
     Timer &T = g_timers[kind];
-    if (T.on && !T.paused && T.count < T.max) (void)hipEventRecord(T.start[T.count], s);
-}
-void timer_after(int kind, hipStream_t s)
-{
-    Timer &T = g_timers[kind];
-    if (T.on && !T.paused && T.count < T.max) (void)hipEventRecord(T.stop[T.count++], s);
+    TimedLaunch t;
+    if (T.on && !T.paused && T.count < T.max) {
+        t.start = T.start[T.count];
+        t.stop = T.stop[T.count];
+        ++T.count;
+    }
+    return t;
 }
 }  // namespace cskv
 

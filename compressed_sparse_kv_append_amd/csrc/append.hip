@@ -296,21 +296,23 @@ hipError_t launch_kv_append(const cskv_cache &c, const float *tokens, const int3
 {
     if (total_new == 0) return hipSuccess;
     AppendArgs a{c, tokens, cu_new, w_comp, idx_rows, static_cast<float *>(ws), total_new};
-    timer_before(CSKV_KERNEL_APPEND, s);
+    const TimedLaunch tl = timer_take(CSKV_KERNEL_APPEND);
     if (w_comp) {
         // decode-sized appends: one row per wave (shortest chains); large
         // chunks: 8 rows per wave share each W row read
         if (total_new <= 1024)
-            compress_kernel<1><<<dim3((unsigned)total_new, kDim / kWave), kWave, 0, s>>>(a);
+            launch_kernel(compress_kernel<1>, dim3((unsigned)total_new, kDim / kWave), dim3(kWave), s, tl.start,
+                          nullptr, a);
         else
-            compress_kernel<8><<<dim3((unsigned)((total_new + 7) / 8), kDim / kWave), kWave, 0, s>>>(a);
-        quantize_kernel<true><<<total_new, kAppendThreads, 0, s>>>(a);
-        append_finalize_kernel<true><<<c.batch, kWave, 0, s>>>(a);
+            launch_kernel(compress_kernel<8>, dim3((unsigned)((total_new + 7) / 8), kDim / kWave), dim3(kWave), s,
+                          tl.start, nullptr, a);
+        launch_kernel(quantize_kernel<true>, dim3((unsigned)total_new), dim3(kAppendThreads), s, nullptr, nullptr, a);
+        launch_kernel(append_finalize_kernel<true>, dim3((unsigned)c.batch), dim3(kWave), s, nullptr, tl.stop, a);
     } else {
-        quantize_kernel<false><<<total_new, kAppendThreads, 0, s>>>(a);
-        append_finalize_kernel<false><<<c.batch, kWave, 0, s>>>(a);
+        launch_kernel(quantize_kernel<false>, dim3((unsigned)total_new), dim3(kAppendThreads), s, tl.start, nullptr,
+                      a);
+        launch_kernel(append_finalize_kernel<false>, dim3((unsigned)c.batch), dim3(kWave), s, nullptr, tl.stop, a);
     }
-    timer_after(CSKV_KERNEL_APPEND, s);
     return hipGetLastError();
 }
 
@@ -320,9 +322,8 @@ hipError_t launch_swa_append(uint16_t *ring, int batch, int window, int dim, con
 {
     if (total_new == 0) return hipSuccess;
     SwaArgs a{ring, batch, window, dim, rows, cu_new, end_pos, total_new};
-    timer_before(CSKV_KERNEL_SWA_APPEND, s);
-    swa_append_kernel<<<total_new, kWave, 0, s>>>(a);
-    timer_after(CSKV_KERNEL_SWA_APPEND, s);
+    const TimedLaunch tl = timer_take(CSKV_KERNEL_SWA_APPEND);
+    launch_kernel(swa_append_kernel, dim3((unsigned)total_new), dim3(kWave), s, tl.start, tl.stop, a);
     return hipGetLastError();
 }
 

@@ -684,18 +684,20 @@ hipError_t launch_sparse_attn(const cskv_cache &c, const float *q, int heads, co
     const int U = c.batch * p.splits;
     const unsigned blocks = (unsigned)(8 * hg * ((U + 7) / 8));
     const int vgs = c.v_group > 0 ? c.v_group : c.k_group;
-    timer_before(CSKV_KERNEL_ATTENTION, s);
+    const TimedLaunch tl = timer_take(CSKV_KERNEL_ATTENTION);
+    hipEvent_t stop_main = p.splits > 1 ? nullptr : tl.stop;
+    auto attn = [&](auto kernel) { launch_kernel(kernel, dim3(blocks), dim3(kThreads), s, tl.start, stop_main, a); };
     if (c.v_group > 0) {
-        if (vgs == 32) sparse_attn_kernel<32, true><<<blocks, kThreads, 0, s>>>(a);
-        else if (vgs == 64) sparse_attn_kernel<64, true><<<blocks, kThreads, 0, s>>>(a);
-        else sparse_attn_kernel<128, true><<<blocks, kThreads, 0, s>>>(a);
+        if (vgs == 32) attn(sparse_attn_kernel<32, true>);
+        else if (vgs == 64) attn(sparse_attn_kernel<64, true>);
+        else attn(sparse_attn_kernel<128, true>);
     } else {
-        if (vgs == 32) sparse_attn_kernel<32, false><<<blocks, kThreads, 0, s>>>(a);
-        else if (vgs == 64) sparse_attn_kernel<64, false><<<blocks, kThreads, 0, s>>>(a);
-        else sparse_attn_kernel<128, false><<<blocks, kThreads, 0, s>>>(a);
+        if (vgs == 32) attn(sparse_attn_kernel<32, false>);
+        else if (vgs == 64) attn(sparse_attn_kernel<64, false>);
+        else attn(sparse_attn_kernel<128, false>);
     }
-    if (p.splits > 1) attn_merge_kernel<<<(unsigned)(c.batch * hg), 256, 0, s>>>(a);
-    timer_after(CSKV_KERNEL_ATTENTION, s);
+    if (p.splits > 1)
+        launch_kernel(attn_merge_kernel, dim3((unsigned)(c.batch * hg)), dim3(256), s, nullptr, tl.stop, a);
     return hipGetLastError();
 }
 

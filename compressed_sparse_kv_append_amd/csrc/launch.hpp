@@ -2,6 +2,7 @@
 // Each returns hipSuccess or the launch error; argument checking happens in
 // api.cpp before any of these is called.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -17,6 +18,8 @@ struct TopkWorkspace {
     size_t keys_off, cand_off, total;
 };
 constexpr int kSliceKeys = 4096;  // keys per select slice (one block)
+// Score keys: one uint32 per cache row; a sequence's rows padded to 64.
+inline size_t score_key_stride(const cskv_cache &c) { return ((size_t)c.capacity + 63) / 64 * 64; }
 TopkWorkspace topk_workspace(const cskv_cache &c, int k);
 int topk_slices(const cskv_cache &c);
 
@@ -28,6 +31,10 @@ hipError_t launch_kv_append(const cskv_cache &c, const float *tokens, const int3
 hipError_t launch_swa_append(uint16_t *ring, int batch, int window, int dim, const float *rows,
                              const int32_t *cu_new, int total_new, const int32_t *end_pos,
                              hipStream_t s);
+// Indexer scan (scan.hip): one score key per valid entry into keys
+// [batch][score_key_stride].
+void launch_indexer_scan(const cskv_cache &c, const uint16_t *q_idx, int heads, const float *head_w,
+                         uint32_t *keys, hipStream_t s);
 hipError_t launch_indexer_topk(const cskv_cache &c, const uint16_t *q_idx, int heads,
                                const float *head_w, int k, int32_t *out_idx, void *ws,
                                hipStream_t s);
@@ -46,8 +53,22 @@ hipError_t launch_sparse_attn(const cskv_cache &c, const float *q, int heads, co
                               int k, const uint16_t *swa, int window, const int32_t *swa_len,
                               float scale, float *out, float *lse, void *ws, hipStream_t s);
 
-// Kernel timers (api.cpp): bracket a launch with event records when enabled.
-void timer_before(int kind, hipStream_t s);
-void timer_after(int kind, hipStream_t s);
+// Kernel timers (api.cpp).  When the timer of a kernel kind is on, one
+// launch group of that kind takes an event pair: its first kernel records
+// `start` as it begins and its last records `stop` as it ends (both through
+// hipExtLaunchKernel), so the interval covers the kernels' own execution and
+// adds no marker packets to the stream.  Both are null when the timer is off.
+struct TimedLaunch {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+TimedLaunch timer_take(int kind);
+
+template <class... P, class... A>
+inline void launch_kernel(void (*k)(P...), dim3 grid, dim3 block, hipStream_t s, hipEvent_t start,
+                          hipEvent_t stop, A... args)
+{
+    if (start || stop) hipExtLaunchKernelGGL(k, grid, block, 0, s, start, stop, 0, args...);
+    else hipLaunchKernelGGL(k, grid, block, 0, s, args...);
+}
 
 }  // namespace cskv

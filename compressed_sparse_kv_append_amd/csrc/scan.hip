@@ -1,0 +1,185 @@
+// scan.hip -- indexer scoring over every cached entry [P2 三、"突破四：滑动窗口和
+// 稀疏注意力" (a light indexer scores all history); P2 四、"CSA2：三种模式"
+// (per-layer multi-head indexer query, per-entry indexer key)].
+//
+// s_j = sum_h w_h * relu(q_h . K_j) is a [heads x dim] x [dim x entries]
+// contraction, run on bf16 MFMA (16x16x32) with fp32 accumulation.  The keys
+// plane is the only large read of the decode step, so the scan is built to
+// stream it: each wave pulls 16-key tiles with coalesced, non-temporal loads
+// that write straight into its own LDS ring (no registers, no block barrier),
+// reads them back in the MFMA operand layout, and keeps the query in
+// registers.  One round of blocks covers the chip.  The only output is one
+// order-preserving uint32 key per entry, which the top-k select consumes.
+//
+// Sources cited as [P2]:
+//   P2  "DeepSeek V1 到 V4.1-Flash，单 token 的 global KV 如何从 389,000 B 压缩到 890 B的？"
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace cskv {
+
+namespace {
+
+constexpr int kScanThreads = 256;   // 4 waves
+constexpr int kScanWaves = kScanThreads / kWave;
+constexpr int kRing = 2;            // 16-key tiles in flight per wave (LDS slots)
+constexpr int kScanBlocksPerCU = 3; // what registers (<= 168) and LDS (32 KB) allow
+
+struct ScanArgs {
+    const uint16_t *keys;      // idx_keys plane
+    const int32_t *n_tokens;
+    const uint16_t *q;         // [B][H][Di]
+    const float *head_w;       // [B][H] or null
+    uint32_t *out_keys;        // [B][key_stride]
+    int capacity, heads, chunk;
+    size_t key_stride;
+};
+
+typedef __attribute__((address_space(1))) void global_void_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8; a field at its maximum does not wait).
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (7 << 4) | (0xF << 8); }
+constexpr int kWaitLgkm0 = 0xF | (3 << 14) | (7 << 4);
+constexpr int kNonTemporal = 2;     // cache policy of the streaming loads
+
+// One block: a run of `chunk` entries of one sequence; wave w takes 16-key
+// tiles w, w + 4, ...  MT: 16-head row tiles of the query (1..4).
+template <int DI, int MT>
+__global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
+{
+    constexpr int kSteps = DI / 32;            // MFMA contraction steps per key
+    constexpr int kRowBytes = 2 * DI;
+    constexpr int kChunks = kRowBytes / 16;    // 16-byte chunks per key row
+    constexpr int kTileBytes = 16 * kRowBytes;
+    constexpr int kInst = kTileBytes / 1024;   // loads per tile (64 lanes x 16 B)
+    __shared__ __attribute__((aligned(16))) uint8_t ring[kScanWaves][kRing][kTileBytes];
+
+    const int b = blockIdx.y;
+    const int64_t E = entries_of(a.n_tokens, b, a.capacity);
+    const int64_t e_begin = (int64_t)blockIdx.x * a.chunk;
+    if (e_begin >= E) return;
+    const int64_t e_end = E < e_begin + a.chunk ? E : e_begin + a.chunk;
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    const int col = lane & 15, grp = lane >> 4;
+
+    // Indexer query as MFMA A operands: row = head, contraction slots
+    // 8*grp..8*grp+7 of each 32-dim step.  Missing heads: zero rows, weight 0.
+    u32x4_t qa[MT][kSteps];
+    float hw[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int head = 16 * mt + col;
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            if (head < a.heads)
+                v = *reinterpret_cast<const u32x4_t *>(a.q + ((size_t)b * a.heads + head) * DI + 32 * s + 8 * grp);
+            qa[mt][s] = v;
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int hrow = 16 * mt + 4 * grp + v;
+            hw[mt][v] = hrow < a.heads ? (a.head_w ? a.head_w[(size_t)b * a.heads + hrow] : 1.0f) : 0.0f;
+        }
+    }
+
+    const int n_tiles = (int)((e_end - e_begin + 15) / 16);
+    const int my_n = n_tiles > w ? (n_tiles - w + kScanWaves - 1) / kScanWaves : 0;
+    const uint8_t *kb = reinterpret_cast<const uint8_t *>(a.keys + (size_t)b * a.capacity * DI);
+    uint32_t *ok = a.out_keys + (size_t)b * a.key_stride;
+
+    // Tile i goes straight from HBM into LDS slot i % kRing with coalesced
+    // 16-byte loads (instruction s covers bytes 1024 s .. 1024 s + 1023 of the
+    // tile's 16 contiguous rows).  Lane l's bytes land at slot offset
+    // 1024 s + 16 l; the lane fetches the chunk that belongs there under an
+    // XOR swizzle (chunk c of row r at position c ^ (r % kChunks)), which
+    // makes the operand reads below bank-conflict free.  Rows past the end
+    // re-read the last valid row; their scores are dropped.
+    auto issue = [&](int i) {
+        const int64_t t0 = e_begin + (int64_t)(w + kScanWaves * i) * 16;
+        uint8_t *slot = &ring[w][i % kRing][0];
+        const bool tail = t0 + 16 > e_end;
+#pragma unroll
+        for (int s = 0; s < kInst; ++s) {
+            const int u = 64 * s + lane, r = u / kChunks, p = u % kChunks, c = p ^ (r % kChunks);
+            int64_t e = t0 + r;
+            if (tail) e = e < e_end ? e : e_end - 1;
+            __builtin_amdgcn_global_load_lds((global_void_t *)(kb + (size_t)e * kRowBytes + 16 * c),
+                                             (lds_void_t *)(slot + 1024 * s), 16, 0, kNonTemporal);
+        }
+    };
+
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) issue(i);
+    for (int i = 0; i < my_n; ++i) {
+        // tile i has landed once at most the later tiles' loads are pending
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kInst * (kRing - 1)));
+        const uint8_t *slot = &ring[w][i % kRing][0];
+        u32x4_t bop[kSteps];
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            const int p = (4 * s + grp) ^ (col % kChunks);
+            bop[s] = *reinterpret_cast<const u32x4_t *>(slot + 16 * (col * kChunks + p));
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);      // slot read before it is refilled
+        issue(i + kRing);
+        f32x4_t acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16x16x32(qa[mt][s], bop[s], acc[mt]);
+        float part = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) part += hw[mt][v] * fmaxf(acc[mt][v], 0.f);
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        const int64_t e = e_begin + (int64_t)(w + kScanWaves * i) * 16 + lane;
+        if (lane < 16 && e < e_end) ok[e] = score_key(part);
+    }
+    // no LDS write may land after the block's LDS is handed to another block
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+}
+
+}  // namespace
+
+void launch_indexer_scan(const cskv_cache &c, const uint16_t *q_idx, int heads, const float *head_w,
+                         uint32_t *keys, hipStream_t s)
+{
+    // One round of blocks that fills every CU: entries per block chosen so
+    // that batch x blocks-per-sequence <= resident slots, a multiple of 64.
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+    }
+    const int slots = kScanBlocksPerCU * cus;
+    const int per_seq = c.batch >= slots ? 1 : slots / c.batch;
+    size_t chunk = ((size_t)c.capacity + per_seq - 1) / per_seq;
+    chunk = (chunk + 63) / 64 * 64;
+    ScanArgs sa{c.idx_keys, c.n_tokens, q_idx, head_w, keys, c.capacity, heads, (int)chunk,
+                score_key_stride(c)};
+    dim3 grid((unsigned)(((size_t)c.capacity + chunk - 1) / chunk), (unsigned)c.batch);
+    const int mt = (heads + 15) / 16;
+    const TimedLaunch ts = timer_take(CSKV_KERNEL_INDEXER_SCAN);
+    auto scan = [&](auto kernel) { launch_kernel(kernel, grid, dim3(kScanThreads), s, ts.start, ts.stop, sa); };
+    if (c.idx_dim == 128) {
+        if (mt == 4) scan(indexer_scan_kernel<128, 4>);
+        else if (mt == 3) scan(indexer_scan_kernel<128, 3>);
+        else if (mt == 2) scan(indexer_scan_kernel<128, 2>);
+        else scan(indexer_scan_kernel<128, 1>);
+    } else {
+        if (mt == 4) scan(indexer_scan_kernel<64, 4>);
+        else if (mt == 3) scan(indexer_scan_kernel<64, 3>);
+        else if (mt == 2) scan(indexer_scan_kernel<64, 2>);
+        else scan(indexer_scan_kernel<64, 1>);
+    }
+}
+
+}  // namespace cskv

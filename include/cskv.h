@@ -235,13 +235,15 @@ size_t cskv_entry_bytes(int32_t dim, int32_t rope_dim, int32_t k_group, int32_t 
 const char *cskv_last_error(void);
 
 /*
- * Kernel timers for measurement.  When enabled for a kernel kind, the library
- * records a hipEvent pair around each of the next `max_launches` launches of
- * that kind on the launch stream; cskv_timer_read waits for them and returns
- * the summed milliseconds and the count.  cskv_timer_pause(kind, 1) stops
- * recording for that kind (launches run untimed, no events are recorded)
- * until cskv_timer_pause(kind, 0), so a bench can time a sample of its
- * steps.  Not thread-safe; meant for benches.
+ * Kernel timers for measurement.  When enabled for a kernel kind, each of
+ * the next `max_launches` launch groups of that kind (the one to three
+ * kernels one call launches for it) records an event as its first kernel
+ * starts and one as its last kernel ends, passed to hipExtLaunchKernel, so no
+ * marker packets are added to the stream.  cskv_timer_read waits for them
+ * and returns the summed milliseconds and the count.  cskv_timer_pause(kind,
+ * 1) stops recording for that kind (launches run untimed) until
+ * cskv_timer_pause(kind, 0), so a bench can time a sample of its steps.  Not
+ * thread-safe; meant for benches.
  */
 #define CSKV_KERNEL_APPEND 1
 #define CSKV_KERNEL_SWA_APPEND 2
