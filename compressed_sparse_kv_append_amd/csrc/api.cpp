@@ -102,6 +102,8 @@ int attn_args(const cskv_cache *c, const float *q, int32_t heads, const int32_t 
     REQUIRE(q && out && (idx || !need_idx), CSKV_EINVAL, "q, idx or out is NULL");
     int rc = attn_shape(heads, k, window);
     if (rc) return rc;
+    REQUIRE(c->capacity <= (1 << 23), CSKV_EUNSUPPORTED,
+            "capacity %d: attention supports at most 2^23 entries per sequence", c->capacity);
     REQUIRE(aligned(q, 16) && aligned(out, 16) && (!idx || aligned(idx, 4)) && (!lse || aligned(lse, 4)),
             CSKV_EINVAL, "q and out must be 16-byte aligned");
     REQUIRE(swa && aligned(swa, 16), CSKV_EINVAL, "window ring NULL or not 16-byte aligned");

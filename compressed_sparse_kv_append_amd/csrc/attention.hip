@@ -101,7 +101,7 @@ struct AttnArgs {
 struct Ctx {
     int t, lane, w, col, grp;
     int nloc;           // chunks of this block
-    int G, kshift;      // key groups per row; contraction step -> key group shift
+    int G;              // key groups per row
     size_t row0;        // first cache row of the sequence
     const uint16_t *ring;
 };
@@ -119,16 +119,23 @@ __device__ __forceinline__ u32x4_t fp4x8_to_bf16x8(uint32_t w)
     return r;
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bf16 (round to nearest even), packed low first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
+}
+
 // hi/lo bf16 split of 8 floats: x = hi + lo + O(2^-17 |x|)
 __device__ __forceinline__ void split8(const float *x, u32x4_t &hi, u32x4_t &lo)
 {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t h0 = bf16_bits_rne(x[2 * i]), h1 = bf16_bits_rne(x[2 * i + 1]);
-        const uint32_t l0 = bf16_bits_rne(x[2 * i] - bf16_bits_to_f32(h0));
-        const uint32_t l1 = bf16_bits_rne(x[2 * i + 1] - bf16_bits_to_f32(h1));
-        hi[i] = h0 | (h1 << 16);
-        lo[i] = l0 | (l1 << 16);
+        const uint32_t h = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+        hi[i] = h;
+        lo[i] = pack_bf16x2(x[2 * i] - __uint_as_float(h << 16), x[2 * i + 1] - __uint_as_float(h & 0xFFFF0000u));
     }
 }
 
@@ -165,19 +172,31 @@ __device__ __forceinline__ void transpose_nibbles(const uint32_t (&in)[8], uint3
 }
 
 // One chunk's HBM reads, held in registers until they are written to LDS.
-// Every load is issued unconditionally: a masked key reads row 0 of its
-// sequence (always inside the cache) and is zeroed or ignored on the way to
-// LDS, so no load waits behind a branch.
+// They are buffer loads against a per-sequence resource: offsets are 32-bit,
+// and a masked key is given an offset past the end of the resource, which the
+// hardware answers with zeros, so no load waits behind a branch and masked
+// keys arrive with zero codes and zero scales.
 struct SparseRegs {
     uint32_t v[16];     // value-plane words of key octets w and w + 8, word = lane
     u32x4_t k[5];       // split planes: 16-byte pieces of key codes; one plane: k[0].xy = rope words
     float sc[9];        // key scales 0-4, value scales 5-8 (group t / 128 + 4 i, key t % 128)
-    bool valid;         // key t % 128 is present (its scales are kept)
 };
 struct WindowRegs {
     u32x4_t p[9];       // 64 rows x 72 pieces of 16 bytes
-    uint32_t valid;     // bit i: piece i's row is present
 };
+
+constexpr uint32_t kMasked = 0x80000000u;    // offset past the end of every resource
+constexpr int kRsrcWord3 = 0x00020000;       // raw 32-bit buffer, gfx9 family
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ uint32_t row_off(int32_t e, uint32_t row_bytes)
+{
+    return e >= 0 ? (uint32_t)e * row_bytes : kMasked;
+}
 
 template <bool SPLIT, int VGS>
 __device__ __forceinline__ void fetch_sparse(const AttnArgs &a, const AttnSmem &sm, const Ctx &x, int lc,
@@ -186,6 +205,12 @@ __device__ __forceinline__ void fetch_sparse(const AttnArgs &a, const AttnSmem &
     const cskv_cache &c = a.c;
     const int32_t *src = sm.src + lc * kSK;
     constexpr int VG = kDv / VGS;
+    constexpr uint32_t kVRowBytes = SPLIT ? kDv / 2 : kD / 2;
+    const uint32_t cap = (uint32_t)c.capacity;
+    const __amdgpu_buffer_rsrc_t vr =
+        make_rsrc((SPLIT ? c.v_codes : c.k_codes) + x.row0 * kVRowBytes, cap * kVRowBytes);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(c.k_codes + x.row0 * (kD / 2), cap * (kD / 2));
+    const __amdgpu_buffer_rsrc_t ksr = make_rsrc(c.k_scales + x.row0 * x.G, cap * x.G * 4);
     int32_t e[16];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -195,39 +220,37 @@ __device__ __forceinline__ void fetch_sparse(const AttnArgs &a, const AttnSmem &
         e[8 * i + 4] = s1.x; e[8 * i + 5] = s1.y; e[8 * i + 6] = s1.z; e[8 * i + 7] = s1.w;
     }
     const int32_t es = src[x.t & (kSK - 1)];
-    const uint32_t *vplane = reinterpret_cast<const uint32_t *>(SPLIT ? c.v_codes : c.k_codes);
-    constexpr int kVRow = SPLIT ? kDv / 8 : kD / 8;
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-        r.v[j] = vplane[(x.row0 + (uint32_t)max(e[j], 0)) * kVRow + x.lane];
-    const uint32_t *kplane = reinterpret_cast<const uint32_t *>(c.k_codes);
+        r.v[j] = __builtin_amdgcn_raw_buffer_load_b32(vr, (int)(row_off(e[j], kVRowBytes) + 4 * x.lane), 0, 0);
     if (!SPLIT) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {                      // rope words 64..71 of 128 rows
             const int task = x.t + kThreads * i;
-            const int32_t er = src[task >> 3];
-            r.k[0][i] = kplane[(x.row0 + (uint32_t)max(er, 0)) * (kD / 8) + 64 + (task & 7)];
+            const uint32_t off = row_off(src[task >> 3], kD / 2) + 4 * (64 + (task & 7));
+            r.k[0][i] = __builtin_amdgcn_raw_buffer_load_b32(kr, (int)off, 0, 0);
         }
     } else {
 #pragma unroll
         for (int i = 0; i < 5; ++i) {                      // 128 rows x 18 pieces of key codes
             const int task = min(x.t + kThreads * i, kSK * 18 - 1), row = task / 18, p = task % 18;
-            const int32_t er = src[row];
-            r.k[i] = *reinterpret_cast<const u32x4_t *>(kplane + (x.row0 + (uint32_t)max(er, 0)) * (kD / 8) + 4 * p);
+            const uint32_t off = row_off(src[row], kD / 2) + 16 * p;
+            r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, (int)off, 0, 0);
         }
     }
-    const size_t srow = x.row0 + (uint32_t)max(es, 0);
-    r.valid = es >= 0;
+    const uint32_t so = row_off(es, 4 * x.G);
 #pragma unroll
     for (int i = 0; i < 5; ++i) {                          // key scales: group t / 128 + 4 i
         const int g = min((x.t >> 7) + 4 * i, x.G - 1);
-        r.sc[i] = c.k_scales[srow * x.G + g];
+        r.sc[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ksr, (int)(so + 4 * g), 0, 0));
     }
     if (SPLIT) {
+        const __amdgpu_buffer_rsrc_t vsr = make_rsrc(c.v_scales + x.row0 * VG, cap * VG * 4);
+        const uint32_t vo = row_off(es, 4 * VG);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {                      // value scales: group t / 128 + 4 i < 16
             const int g = min((x.t >> 7) + 4 * i, VG - 1);
-            r.sc[5 + i] = c.v_scales[srow * VG + g];
+            r.sc[5 + i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vsr, (int)(vo + 4 * g), 0, 0));
         }
     }
 }
@@ -272,29 +295,28 @@ __device__ __forceinline__ void store_sparse(AttnSmem &sm, const Ctx &x, const S
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
         const int g = (x.t >> 7) + 4 * i;
-        if (g < x.G) sm.ks[g][key] = r.valid ? r.sc[i] : 0.f;
+        if (g < x.G) sm.ks[g][key] = r.sc[i];
     }
     if (SPLIT) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int g = (x.t >> 7) + 4 * i;
-            if (g < VG) sm.vs[g][key] = r.valid ? r.sc[5 + i] : 0.f;
+            if (g < VG) sm.vs[g][key] = r.sc[5 + i];
         }
     }
 }
 
-__device__ __forceinline__ void fetch_window(const AttnSmem &sm, const Ctx &x, int lc, WindowRegs &r)
+__device__ __forceinline__ void fetch_window(const AttnArgs &a, const AttnSmem &sm, const Ctx &x, int lc,
+                                             WindowRegs &r)
 {
     const int32_t *src = sm.src + lc * kSK;
-    uint32_t valid = 0;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(x.ring, (uint32_t)a.window * (kD * 2));
 #pragma unroll
     for (int i = 0; i < 9; ++i) {
         const int task = x.t + kThreads * i, row = task / 72, p = task % 72;
-        const int32_t slot = src[row];
-        valid |= (uint32_t)(slot >= 0) << i;
-        r.p[i] = *reinterpret_cast<const u32x4_t *>(x.ring + (size_t)max(slot, 0) * kD + 8 * p);
+        const uint32_t off = row_off(src[row], kD * 2) + 16 * p;
+        r.p[i] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)off, 0, 0);
     }
-    r.valid = valid;
 }
 
 __device__ __forceinline__ void store_window(AttnSmem &sm, const Ctx &x, const WindowRegs &r)
@@ -302,46 +324,59 @@ __device__ __forceinline__ void store_window(AttnSmem &sm, const Ctx &x, const W
 #pragma unroll
     for (int i = 0; i < 9; ++i) {
         const int task = x.t + kThreads * i, row = task / 72, p = task % 72;
-        const u32x4_t z = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4_t *>(&sm.st.win.kr[row][8 * p]) = ((r.valid >> i) & 1u) ? r.p[i] : z;
+        *reinterpret_cast<u32x4_t *>(&sm.st.win.kr[row][8 * p]) = r.p[i];
     }
 }
 
 // Logits of one chunk.  Wave w takes contraction half w / 4 (9 steps) of two
 // key tiles (selected entries: tiles 2 (w % 4) and 2 (w % 4) + 1 of 8) or of
 // one (window rows: tile w % 4 of 4); the halves are added in the softmax.
-template <bool SPARSE>
-__device__ __forceinline__ void chunk_logits(AttnSmem &sm, const Ctx &x)
+// Selected entries: the MFMA accumulates the steps of one key group, whose
+// scale is then applied once in fp32.
+template <int KG, int HALF>
+__device__ __forceinline__ void sparse_logits_half(AttnSmem &sm, const Ctx &x)
 {
-    const int half = x.w >> 2;
-    if (SPARSE) {
-        const int j0 = 32 * (x.w & 3) + x.col, j1 = j0 + 16;
-        const uint32_t *k0 = sm.st.sp.kc + j0 * kKcRow + x.grp;
-        const uint32_t *k1 = sm.st.sp.kc + j1 * kKcRow + x.grp;
-        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    constexpr int kPer = KG / 32;                  // contraction steps per key group
+    const int j0 = 32 * (x.w & 3) + x.col, j1 = j0 + 16;
+    const uint32_t *k0 = sm.st.sp.kc + j0 * kKcRow + x.grp;
+    const uint32_t *k1 = sm.st.sp.kc + j1 * kKcRow + x.grp;
+    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < kHalf; ++s) {
-            const int step = kHalf * half + s;
-            const u32x4_t qh = sm.q[step][0][x.lane], ql = sm.q[step][1][x.lane];
-            const u32x4_t kb0 = fp4x8_to_bf16x8(k0[4 * step]);
-            const u32x4_t kb1 = fp4x8_to_bf16x8(k1[4 * step]);
-            f32x4_t p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
-            p0 = mfma16x16x32(qh, kb0, p0);
-            p1 = mfma16x16x32(qh, kb1, p1);
-            p0 = mfma16x16x32(ql, kb0, p0);
-            p1 = mfma16x16x32(ql, kb1, p1);
-            const float sc0 = sm.ks[step >> x.kshift][j0], sc1 = sm.ks[step >> x.kshift][j1];
+    for (int s = 0; s < kHalf; ++s) {
+        const int step = kHalf * HALF + s;
+        const u32x4_t qh = sm.q[step][0][x.lane], ql = sm.q[step][1][x.lane];
+        const u32x4_t kb0 = fp4x8_to_bf16x8(k0[4 * step]);
+        const u32x4_t kb1 = fp4x8_to_bf16x8(k1[4 * step]);
+        p0 = mfma16x16x32(qh, kb0, p0);
+        p1 = mfma16x16x32(qh, kb1, p1);
+        p0 = mfma16x16x32(ql, kb0, p0);
+        p1 = mfma16x16x32(ql, kb1, p1);
+        if ((step + 1) % kPer == 0 || s == kHalf - 1) {       // last step of a group in this half
+            const float sc0 = sm.ks[step / kPer][j0], sc1 = sm.ks[step / kPer][j1];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 acc0[v] = fmaf(sc0, p0[v], acc0[v]);
                 acc1[v] = fmaf(sc1, p1[v], acc1[v]);
             }
+            p0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            p1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
+    }
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            sm.s[half][4 * x.grp + v][j0] = acc0[v];
-            sm.s[half][4 * x.grp + v][j1] = acc1[v];
-        }
+    for (int v = 0; v < 4; ++v) {
+        sm.s[HALF][4 * x.grp + v][j0] = acc0[v];
+        sm.s[HALF][4 * x.grp + v][j1] = acc1[v];
+    }
+}
+
+template <bool SPARSE, int KG>
+__device__ __forceinline__ void chunk_logits(AttnSmem &sm, const Ctx &x)
+{
+    const int half = x.w >> 2;
+    if (SPARSE) {
+        if (half == 0) sparse_logits_half<KG, 0>(sm, x);
+        else sparse_logits_half<KG, 1>(sm, x);
     } else {
         const int j = 16 * (x.w & 3) + x.col;
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -355,6 +390,35 @@ __device__ __forceinline__ void chunk_logits(AttnSmem &sm, const Ctx &x)
 #pragma unroll
         for (int v = 0; v < 4; ++v) sm.s[half][4 * x.grp + v][j] = acc[v];
     }
+}
+
+// Reductions over the 32 lanes of a half wave, the result in every lane:
+// rotations inside each row of 16 (DPP), then the two rows of the half
+// exchange through a swizzle.
+enum : int { kDppRowRor = 0x120, kSwizzleXor16 = 0x401F };
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float half_wave_max(float v)
+{
+    v = fmaxf(v, dpp_f32<kDppRowRor | 8>(v));
+    v = fmaxf(v, dpp_f32<kDppRowRor | 4>(v));
+    v = fmaxf(v, dpp_f32<kDppRowRor | 2>(v));
+    v = fmaxf(v, dpp_f32<kDppRowRor | 1>(v));
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), kSwizzleXor16)));
+}
+
+__device__ __forceinline__ float half_wave_sum(float v)
+{
+    v += dpp_f32<kDppRowRor | 8>(v);
+    v += dpp_f32<kDppRowRor | 4>(v);
+    v += dpp_f32<kDppRowRor | 2>(v);
+    v += dpp_f32<kDppRowRor | 1>(v);
+    return v + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), kSwizzleXor16));
 }
 
 // Online softmax in base 2: thread t -> head t / 32, keys t % 32 + 32 i.
@@ -375,8 +439,7 @@ __device__ __forceinline__ void chunk_softmax(AttnSmem &sm, const Ctx &x, int lc
         sv[i] = src[j] >= 0 ? v * scale_log2 : -INFINITY;
         mx = fmaxf(mx, sv[i]);
     }
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    mx = half_wave_max(mx);
     const float m_old = sm.m[h];
     const float m_new = fmaxf(m_old, mx);
     float sum = 0.f;
@@ -386,8 +449,7 @@ __device__ __forceinline__ void chunk_softmax(AttnSmem &sm, const Ctx &x, int lc
         sm.s[0][h][j0 + 32 * i] = pj;
         sum += pj;
     }
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    sum = half_wave_sum(sum);
     if (j0 == 0) {
         const float al = exp2f(m_old - m_new);
         sm.alpha[h] = al;
@@ -455,7 +517,7 @@ __device__ __forceinline__ void chunk_pv(const AttnSmem &sm, const Ctx &x, f32x4
 
 // The chunk loop of one block: the next chunk's HBM reads are in flight
 // while the current chunk is computed.
-template <bool SPARSE, bool SPLIT, int VGS>
+template <bool SPARSE, bool SPLIT, int VGS, int KG>
 __device__ __forceinline__ void run_chunks(const AttnArgs &a, AttnSmem &sm, const Ctx &x, f32x4_t (&o)[4])
 {
     if (SPARSE) {
@@ -466,7 +528,7 @@ __device__ __forceinline__ void run_chunks(const AttnArgs &a, AttnSmem &sm, cons
             store_sparse<SPLIT, VGS>(sm, x, r);
             __syncthreads();
             if (lc + 1 < x.nloc) fetch_sparse<SPLIT, VGS>(a, sm, x, lc + 1, r);
-            chunk_logits<true>(sm, x);
+            chunk_logits<true, KG>(sm, x);
             __syncthreads();
             chunk_softmax<true>(sm, x, lc, a.scale_log2);
             __syncthreads();
@@ -474,13 +536,13 @@ __device__ __forceinline__ void run_chunks(const AttnArgs &a, AttnSmem &sm, cons
         }
     } else {
         WindowRegs r;
-        fetch_window(sm, x, 0, r);
+        fetch_window(a, sm, x, 0, r);
         for (int lc = 0; lc < x.nloc; ++lc) {
             __syncthreads();
             store_window(sm, x, r);
             __syncthreads();
-            if (lc + 1 < x.nloc) fetch_window(sm, x, lc + 1, r);
-            chunk_logits<false>(sm, x);
+            if (lc + 1 < x.nloc) fetch_window(a, sm, x, lc + 1, r);
+            chunk_logits<false, KG>(sm, x);
             __syncthreads();
             chunk_softmax<false>(sm, x, lc, a.scale_log2);
             __syncthreads();
@@ -491,7 +553,8 @@ __device__ __forceinline__ void run_chunks(const AttnArgs &a, AttnSmem &sm, cons
 
 // VGS: the value group size in effect (the value plane's group, else the key
 // plane's): 32, 64 or 128.  SPLIT: the cache has a separate value plane.
-template <int VGS, bool SPLIT>
+// KG: the key plane's group, 32 or 64.
+template <int VGS, bool SPLIT, int KG>
 __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a)
 {
     __shared__ AttnSmem sm;
@@ -516,8 +579,7 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a)
     x.col = x.lane & 15;
     x.grp = x.lane >> 4;
     x.nloc = c1 - c0;
-    x.G = kD / c.k_group;
-    x.kshift = __builtin_ctz((unsigned)c.k_group) - 5;
+    x.G = kD / KG;
     x.row0 = (size_t)b * c.capacity;
     x.ring = a.swa + (size_t)b * a.window * kD;
     const int64_t E = entries_of(c.n_tokens, b, c.capacity);
@@ -560,8 +622,8 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a)
     __syncthreads();
 
     if (x.nloc > 0) {
-        if (sparse) run_chunks<true, SPLIT, VGS>(a, sm, x, o);
-        else run_chunks<false, SPLIT, VGS>(a, sm, x, o);
+        if (sparse) run_chunks<true, SPLIT, VGS, KG>(a, sm, x, o);
+        else run_chunks<false, SPLIT, VGS, KG>(a, sm, x, o);
     }
     __syncthreads();
 
@@ -688,13 +750,18 @@ hipError_t launch_sparse_attn(const cskv_cache &c, const float *q, int heads, co
     hipEvent_t stop_main = p.splits > 1 ? nullptr : tl.stop;
     auto attn = [&](auto kernel) { launch_kernel(kernel, dim3(blocks), dim3(kThreads), s, tl.start, stop_main, a); };
     if (c.v_group > 0) {
-        if (vgs == 32) attn(sparse_attn_kernel<32, true>);
-        else if (vgs == 64) attn(sparse_attn_kernel<64, true>);
-        else attn(sparse_attn_kernel<128, true>);
+        if (c.k_group == 32) {
+            if (vgs == 32) attn(sparse_attn_kernel<32, true, 32>);
+            else if (vgs == 64) attn(sparse_attn_kernel<64, true, 32>);
+            else attn(sparse_attn_kernel<128, true, 32>);
+        } else {
+            if (vgs == 32) attn(sparse_attn_kernel<32, true, 64>);
+            else if (vgs == 64) attn(sparse_attn_kernel<64, true, 64>);
+            else attn(sparse_attn_kernel<128, true, 64>);
+        }
     } else {
-        if (vgs == 32) attn(sparse_attn_kernel<32, false>);
-        else if (vgs == 64) attn(sparse_attn_kernel<64, false>);
-        else attn(sparse_attn_kernel<128, false>);
+        if (c.k_group == 32) attn(sparse_attn_kernel<32, false, 32>);
+        else attn(sparse_attn_kernel<64, false, 64>);
     }
     if (p.splits > 1)
         launch_kernel(attn_merge_kernel, dim3((unsigned)(c.batch * hg)), dim3(256), s, nullptr, tl.stop, a);

@@ -178,6 +178,8 @@ int cskv_indexer_topk(const cskv_cache *cache, const uint16_t *q_idx, int32_t n_
  * ws       device workspace for partial softmaxes: at least
  *          cskv_workspace_bytes(cache, CSKV_OP_SPARSE_ATTN, n_heads, k, window)
  *          bytes, 256-byte aligned (may be NULL when that size is 256 or less).
+ * The gather addresses a sequence's rows with 32-bit byte offsets, so the
+ * cache capacity is limited to 2^23 entries per sequence (CSKV_EUNSUPPORTED).
  */
 int cskv_sparse_attn_decode(const cskv_cache *cache, const float *q, int32_t n_heads,
                             const int32_t *idx, int32_t k, const uint16_t *swa, int32_t window,

@@ -107,6 +107,12 @@ def test_call_arguments_rejected_before_launch(L):
                                      None, C.c_float(0.04), vp(0xF0000), None, vp(0xB0000), aws - 1,
                                      None) == ck.EWORKSPACE
     assert L.cskv_workspace_bytes(C.byref(d), 9, 16, 512, 128) == 0
+    # attention addresses a sequence's rows with 32-bit offsets: capacity <= 2^23
+    big = _desc(capacity=(1 << 23) + 1)
+    bws = L.cskv_workspace_bytes(C.byref(big), ck.OP_SPARSE_ATTN, 16, 512, 128)
+    assert L.cskv_sparse_attn_decode(C.byref(big), vp(0xC0000), 16, vp(0xD0000), 512, vp(0xE0000), 128,
+                                     None, C.c_float(0.04), vp(0xF0000), None, vp(0xB0000), bws,
+                                     None) == ck.EUNSUPPORTED and "capacity" in _err(L)
     # window append: dim not a multiple of 4
     assert L.cskv_swa_append(vp(0x100000), 2, 128, 578, vp(0x70000), None, 2, vp(0x40000), None) == ck.EUNSUPPORTED
 
