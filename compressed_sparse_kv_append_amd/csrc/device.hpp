@@ -122,6 +122,18 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
     return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
 }
 
+__device__ __forceinline__ uint32_t wave_or_u32(uint32_t v)
+{
+    v = wave_inclusive(v, 0u, [](uint32_t a, uint32_t b) { return a | b; });
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+
+__device__ __forceinline__ uint32_t wave_and_u32(uint32_t v)
+{
+    v = wave_inclusive(v, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return a & b; });
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+
 // ---------------------------------------------------------------- misc
 
 // Order-preserving map of an fp32 score to uint32 (larger score -> larger key).

@@ -75,7 +75,7 @@ struct SelectSmem {
     static constexpr int kWaves = THREADS / kWave;
     uint32_t bins[kBins];
     uint32_t wave_sum[kWaves];
-    uint32_t red[2][kWaves];
+    uint32_t red[4][kWaves];
     uint32_t found[3];
 };
 
@@ -104,10 +104,10 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t *wave_sum, u
 // (count above t) < need <= (count at or above t); sm.found = {t, count
 // strictly above t, count in t}.  Run by wave 0 alone: lane l owns the 32
 // bins below nbins - 32 l (read in a rotated order so that no two lanes hit
-// one LDS bank), a lane prefix sum orders the groups from the top, and the
-// lane whose group holds the threshold scans its 32 counts in registers.
-// Afterwards every bin is cleared for the next histogram.  Requires
-// need <= total count.
+// one LDS bank); a lane prefix sum and a ballot name the group that holds
+// the threshold, then lanes 0..31 take that group's bins from the top and a
+// second prefix sum and ballot name the bin.  Afterwards every bin is
+// cleared for the next histogram.  Requires need <= total count.
 template <class Smem>
 __device__ __forceinline__ void find_threshold_bin_wave0(Smem &sm, int nbins, uint32_t need)
 {
@@ -121,25 +121,19 @@ __device__ __forceinline__ void find_threshold_bin_wave0(Smem &sm, int nbins, ui
         sum += bn >= 0 ? sm.bins[bn] : 0u;
     }
     const uint32_t incl = wave_scan_add(sum);
-    uint32_t run = incl - sum;
-    if (run < need && need <= incl) {
-        uint32_t c[kOwn];
-#pragma unroll
-        for (int j = 0; j < kOwn; ++j) c[j] = sm.bins[top - j];
-        bool done = false;
-#pragma unroll
-        for (int j = 0; j < kOwn; ++j) {
-            if (!done && need <= run + c[j]) {
-                sm.found[0] = (uint32_t)(top - j);
-                sm.found[1] = run;
-                sm.found[2] = c[j];
-                done = true;
-            }
-            run += c[j];
-        }
+    const int owner = __ffsll((unsigned long long)__ballot(incl >= need)) - 1;
+    const uint32_t run = (uint32_t)__builtin_amdgcn_readlane((int)(incl - sum), owner);
+    const int otop = nbins - 1 - kOwn * owner;
+    const uint32_t c = (lane < kOwn && otop - lane >= 0) ? sm.bins[otop - lane] : 0u;
+    const uint32_t ci = wave_scan_add(c);
+    const int j = __ffsll((unsigned long long)__ballot(lane < kOwn && run + ci >= need)) - 1;
+    if (lane == j) {
+        sm.found[0] = (uint32_t)(otop - j);
+        sm.found[1] = run + ci - c;
+        sm.found[2] = c;
     }
 #pragma unroll
-    for (int j = 0; j < kOwn; ++j) sm.bins[kOwn * lane + ((j + lane) & (kOwn - 1))] = 0u;
+    for (int jj = 0; jj < kOwn; ++jj) sm.bins[kOwn * lane + ((jj + lane) & (kOwn - 1))] = 0u;
 }
 
 // The keys of positions [PER t, PER t + PER) of round r, held by thread t,
@@ -199,8 +193,8 @@ __device__ __forceinline__ void select_topk(SelectSmem<THREADS> &sm, const Items
     uint64_t vm = 0;
     if (rounds == 1) vm = load_keys<kList, THREADS, PER>(it, 0, key, idx);
 
-    // ---- range of the valid keys
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    // ---- range of the valid keys, and the bits in which any two differ
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u, orv = 0u, andv = 0xFFFFFFFFu;
     for (int64_t r = 0; r < rounds; ++r) {
         if (rounds > 1) vm = load_keys<kList, THREADS, PER>(it, r, key, idx);
 #pragma unroll
@@ -208,27 +202,45 @@ __device__ __forceinline__ void select_topk(SelectSmem<THREADS> &sm, const Items
             const bool v = (vm >> i) & 1ull;
             lo = min(lo, v ? key[i] : 0xFFFFFFFFu);
             hi = max(hi, v ? key[i] : 0u);
+            orv |= v ? key[i] : 0u;
+            andv &= v ? key[i] : 0xFFFFFFFFu;
         }
     }
     lo = wave_min_u32(lo);
     hi = wave_max_u32(hi);
-    if ((t & (kWave - 1)) == 0) { sm.red[0][t / kWave] = lo; sm.red[1][t / kWave] = hi; }
+    orv = wave_or_u32(orv);
+    andv = wave_and_u32(andv);
+    if ((t & (kWave - 1)) == 0) {
+        sm.red[0][t / kWave] = lo;
+        sm.red[1][t / kWave] = hi;
+        sm.red[2][t / kWave] = orv;
+        sm.red[3][t / kWave] = andv;
+    }
     for (int i = t; i < kBins; i += THREADS) sm.bins[i] = 0u;
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) { lo = min(lo, sm.red[0][i]); hi = max(hi, sm.red[1][i]); }
+    for (int i = 0; i < kWaves; ++i) {
+        lo = min(lo, sm.red[0][i]);
+        hi = max(hi, sm.red[1][i]);
+        orv |= sm.red[2][i];
+        andv &= sm.red[3][i];
+    }
+    // bits below `low` are the same in every valid key: they never split a tie
+    const uint32_t vary = orv ^ andv;
+    const int low = vary ? __builtin_ctz(vary) : 0;
 
-    // ---- radix passes: digit windows below the common prefix of lo and hi.
-    // After a pass, items whose key >> shift exceeds the threshold prefix are
-    // in; if the threshold bin is taken whole, it is in too and the search
-    // stops; otherwise the bin is refined by the next lower bits.  At
-    // shift 0 the prefix is the k-th largest key itself.
+    // ---- radix passes: digit windows below the common prefix of lo and hi,
+    // down to bit `low`.  After a pass, items whose key >> shift exceeds the
+    // threshold prefix are in; if the threshold bin is taken whole, it is in
+    // too and the search stops; otherwise the bin is refined by the next
+    // lower bits.  At shift `low` the prefix identifies the k-th largest key
+    // itself.
     uint32_t T = lo;                 // selected: key >> tshift > T, or == T within the tie quota
     int tshift = 0;
     uint32_t ties = (uint32_t)k;
     if (lo != hi) {
-        const int top = 32 - __clz((int)(lo ^ hi));      // bits [0, top) still vary
-        int shift = top > kDigit ? top - kDigit : 0;
+        const int top = 32 - __clz((int)(lo ^ hi));      // bits [low, top) vary
+        int shift = top - kDigit > low ? top - kDigit : low;
         uint32_t sub = lo >> shift;                      // first window: offset from lo
         int pshift = 32;
         uint32_t prefix = 0;
@@ -252,14 +264,14 @@ __device__ __forceinline__ void select_topk(SelectSmem<THREADS> &sm, const Items
             // key >> shift of the threshold key
             prefix = pshift >= 32 ? bin + sub : (prefix << (pshift - shift)) | bin;
             need -= a2;
-            if (shift == 0 || cnt == need) {
+            if (shift == low || cnt == need) {
                 T = prefix;
                 tshift = shift;
                 ties = need;
                 break;
             }
             pshift = shift;
-            shift = shift > kDigit ? shift - kDigit : 0;
+            shift = shift - kDigit > low ? shift - kDigit : low;
             sub = 0;
             mask = (1u << (pshift - shift)) - 1u;
         }
@@ -376,7 +388,10 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(SelectArgs a)
     }
     const int64_t used = (E + kSliceKeys - 1) / kSliceKeys;
     Items it{nullptr, a.cand + (size_t)b * a.cand_stride, used * a.k, 0};
-    select_topk<true, false, kMergeThreads, kMergePer>(sm, it, a.k, out, nullptr);
+    if (it.n <= kMergeThreads * kSlicePer)     // one round of 16 candidates per thread
+        select_topk<true, false, kMergeThreads, kSlicePer>(sm, it, a.k, out, nullptr);
+    else
+        select_topk<true, false, kMergeThreads, kMergePer>(sm, it, a.k, out, nullptr);
 }
 
 }  // namespace
