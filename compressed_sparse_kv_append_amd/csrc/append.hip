@@ -68,84 +68,92 @@ __device__ __forceinline__ RowInfo row_info(const AppendArgs &a, int64_t r)
 // ---------------------------------------------------------------- compressor
 
 // Stand-in 2->1 compressor [P2 三、"突破四" (2 tokens -> 1 entry); P1 §3.2]:
-// e[ch] = sum_j W[ch][j] u[j], u = x_even || x_odd, folded in fp32 from j = 0
-// upward with one fused multiply-add per term.  Each output channel is one
-// sequential chain of 2*dim dependent FMAs, so the parallelism is channels x
-// entries: one wave takes 64 channels (one per lane) of NE consecutive input
-// rows, reads its W rows once for all of them and keeps one accumulator per
-// row.  The rows' inputs u are staged in LDS and read as broadcasts.
-template <int NE>
-__global__ __launch_bounds__(kWave) void compress_kernel(AppendArgs a)
+// e[ch] = sum_j W[ch][j] u[j], u = x_even || x_odd, in a fixed fp32 order:
+// the 1152 terms are cut into 64 blocks of 18, each folded upward from +0
+// with one fused multiply-add per term, and the 64 block sums are added as a
+// pairwise tree (blocks 2i and 2i+1 first).  Lane l of a wave owns block l:
+// it keeps u's 18 terms of E input rows in registers and reads
+// W[ch][18 l .. 18 l + 17], so the wave reads each W row contiguously once
+// for all E rows.  The tree is four DPP steps inside each row of 16 lanes
+// (lane p adds lane p + w) and one scalar step over the four row sums.  A
+// wave takes `cpw` output channels of E consecutive input rows.
+constexpr int kCompTerms = 2 * kDim / kWave;     // 18 terms per lane
+constexpr int kDppRowShl = 0x100;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_shl(float v)
 {
-    __shared__ float4 u_s[NE][2 * kDim / 4];
-    __shared__ const float *src_s[NE][2];
-    const int lane = threadIdx.x, rb = blockIdx.y;
-    const int64_t r0 = (int64_t)blockIdx.x * NE;
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
 
-    bool act = false;
-    if (lane < NE && r0 + lane < a.total_new) {
-        const int64_t r = r0 + lane;
-        const RowInfo ri = row_info<true>(a, r);
-        if (ri.entry >= 0) {
-            act = true;
-            src_s[lane][0] = ri.partner >= 0 ? a.tokens + (size_t)ri.partner * kDim
-                                             : a.c.pending + (size_t)ri.b * kDim;
-            src_s[lane][1] = a.tokens + (size_t)r * kDim;
+template <int E>
+__global__ __launch_bounds__(kWave) void compress_kernel(AppendArgs a, int cpw)
+{
+    const int lane = threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.y * E;
+    const int c0 = blockIdx.x * cpw;
+    const int c1 = c0 + cpw < kDim ? c0 + cpw : kDim;
+
+    // u's terms of this lane's block for every row of the group that
+    // completes an entry; lanes 0-31 hold x_even, lanes 32-63 x_odd
+    float u[E][kCompTerms];
+    uint32_t act = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int64_t r = r0 + e;
+        RowInfo ri{0, -1, -1};
+        if (r < a.total_new) ri = row_info<true>(a, r);
+        const bool on = ri.entry >= 0;
+        act |= (uint32_t)on << e;
+        // rows that complete no entry read row 0 (always present) and drop it
+        const float *src = !on ? a.tokens
+                         : lane < kWave / 2
+                               ? (ri.partner >= 0 ? a.tokens + (size_t)ri.partner * kDim
+                                                  : a.c.pending + (size_t)ri.b * kDim) + kCompTerms * lane
+                               : a.tokens + (size_t)r * kDim + kCompTerms * (lane - kWave / 2);
+#pragma unroll
+        for (int t = 0; t < kCompTerms / 2; ++t) {
+            const float2 x = reinterpret_cast<const float2 *>(src)[t];
+            const float2 v = on ? x : make_float2(0.f, 0.f);
+            u[e][2 * t] = v.x;
+            u[e][2 * t + 1] = v.y;
         }
     }
-    const uint64_t am = __ballot(act);
-    if (am == 0) return;
-    __syncthreads();
+    if (act == 0) return;
 
-    // stage u of every active row: 2 x 144 float4 per row
-#pragma unroll 1
-    for (int e = 0; e < NE; ++e) {
-        if (!((am >> e) & 1ull)) continue;
-        const float4 *xe = reinterpret_cast<const float4 *>(src_s[e][0]);
-        const float4 *xo = reinterpret_cast<const float4 *>(src_s[e][1]);
-        for (int i = lane; i < kDim / 4; i += kWave) {
-            u_s[e][i] = xe[i];
-            u_s[e][kDim / 4 + i] = xo[i];
-        }
-    }
-    __syncthreads();
-
-    const int ch = kWave * rb + lane;
-    const float4 *wrow = reinterpret_cast<const float4 *>(a.w_comp + (size_t)ch * 2 * kDim);
-    float acc[NE];
+    const float2 *wl = reinterpret_cast<const float2 *>(a.w_comp) + (kCompTerms / 2) * lane;
+    float2 wn[kCompTerms / 2];
 #pragma unroll
-    for (int e = 0; e < NE; ++e) acc[e] = 0.0f;
-    constexpr int kQ = 2 * kDim / 4;       // 288 float4 per W row
-    constexpr int kU = 8;                  // float4 per step
-    float4 wcur[kU], wnext[kU];
+    for (int t = 0; t < kCompTerms / 2; ++t) wn[t] = wl[(size_t)c0 * kDim + t];
+    for (int c = c0; c < c1; ++c) {
+        float2 w[kCompTerms / 2];
 #pragma unroll
-    for (int i = 0; i < kU; ++i) wcur[i] = wrow[i];
-    for (int j0 = 0; j0 < kQ; j0 += kU) {
-        if (j0 + kU < kQ) {
+        for (int t = 0; t < kCompTerms / 2; ++t) w[t] = wn[t];
+        if (c + 1 < c1) {
 #pragma unroll
-            for (int i = 0; i < kU; ++i) wnext[i] = wrow[j0 + kU + i];
+            for (int t = 0; t < kCompTerms / 2; ++t) wn[t] = wl[(size_t)(c + 1) * kDim + t];
         }
 #pragma unroll
-        for (int e = 0; e < NE; ++e) {
-            if ((am >> e) & 1ull) {
-                float x = acc[e];
+        for (int e = 0; e < E; ++e) {
+            if (!((act >> e) & 1u)) continue;
+            float acc = 0.0f;
 #pragma unroll
-                for (int i = 0; i < kU; ++i) {
-                    const float4 u = u_s[e][j0 + i];
-                    x = fmaf(wcur[i].x, u.x, x);
-                    x = fmaf(wcur[i].y, u.y, x);
-                    x = fmaf(wcur[i].z, u.z, x);
-                    x = fmaf(wcur[i].w, u.w, x);
-                }
-                acc[e] = x;
+            for (int t = 0; t < kCompTerms / 2; ++t) {
+                acc = fmaf(w[t].x, u[e][2 * t], acc);
+                acc = fmaf(w[t].y, u[e][2 * t + 1], acc);
             }
+            acc = acc + dpp_shl<kDppRowShl | 1>(acc);
+            acc = acc + dpp_shl<kDppRowShl | 2>(acc);
+            acc = acc + dpp_shl<kDppRowShl | 4>(acc);
+            acc = acc + dpp_shl<kDppRowShl | 8>(acc);
+            const float q0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 0));
+            const float q1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 16));
+            const float q2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 32));
+            const float q3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 48));
+            const float res = (q0 + q1) + (q2 + q3);
+            if (lane == e) a.ent[(size_t)(r0 + e) * kDim + c] = res;
         }
-#pragma unroll
-        for (int i = 0; i < kU; ++i) wcur[i] = wnext[i];
     }
-#pragma unroll
-    for (int e = 0; e < NE; ++e)
-        if ((am >> e) & 1ull) a.ent[(size_t)(r0 + e) * kDim + ch] = acc[e];
 }
 
 // ---------------------------------------------------------------- quantiser
@@ -298,14 +306,13 @@ hipError_t launch_kv_append(const cskv_cache &c, const float *tokens, const int3
     AppendArgs a{c, tokens, cu_new, w_comp, idx_rows, static_cast<float *>(ws), total_new};
     const TimedLaunch tl = timer_take(CSKV_KERNEL_APPEND);
     if (w_comp) {
-        // decode-sized appends: one row per wave (shortest chains); large
-        // chunks: 8 rows per wave share each W row read
-        if (total_new <= 1024)
-            launch_kernel(compress_kernel<1>, dim3((unsigned)total_new, kDim / kWave), dim3(kWave), s, tl.start,
-                          nullptr, a);
-        else
-            launch_kernel(compress_kernel<8>, dim3((unsigned)((total_new + 7) / 8), kDim / kWave), dim3(kWave), s,
-                          tl.start, nullptr, a);
+        // about 1024 waves: groups of 8 input rows x runs of output channels
+        constexpr int kE = 8;
+        const int groups = (total_new + kE - 1) / kE;
+        const int runs = groups >= 1024 ? 1 : (1024 / groups < kDim ? 1024 / groups : kDim);
+        const int cpw = (kDim + runs - 1) / runs;
+        launch_kernel(compress_kernel<kE>, dim3((unsigned)((kDim + cpw - 1) / cpw), (unsigned)groups), dim3(kWave),
+                      s, tl.start, nullptr, a, cpw);
         launch_kernel(quantize_kernel<true>, dim3((unsigned)total_new), dim3(kAppendThreads), s, nullptr, nullptr, a);
         launch_kernel(append_finalize_kernel<true>, dim3((unsigned)c.batch), dim3(kWave), s, nullptr, tl.stop, a);
     } else {

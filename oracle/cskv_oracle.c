@@ -101,16 +101,28 @@ uint16_t orc_bf16_from_f32(float x)
 
 /* ------------------------------------------------------------ compress */
 
+#define ORC_COMPRESS_BLOCKS 64
+
 void orc_compress_pair(const float *W, const float *x_even, const float *x_odd,
                        int dim, float *e)
 {
+    const int n = 2 * dim;
+    assert(n % ORC_COMPRESS_BLOCKS == 0);
+    const int per = n / ORC_COMPRESS_BLOCKS;
     for (int r = 0; r < dim; ++r) {
-        float acc = 0.0f;
-        for (int j = 0; j < 2 * dim; ++j) {
-            float u = (j < dim) ? x_even[j] : x_odd[j - dim];
-            acc = fmaf(W[(size_t)r * 2 * dim + j], u, acc);
+        float part[ORC_COMPRESS_BLOCKS];
+        for (int p = 0; p < ORC_COMPRESS_BLOCKS; ++p) {       /* block sums */
+            float acc = 0.0f;
+            for (int j = p * per; j < (p + 1) * per; ++j) {
+                float u = (j < dim) ? x_even[j] : x_odd[j - dim];
+                acc = fmaf(W[(size_t)r * n + j], u, acc);
+            }
+            part[p] = acc;
         }
-        e[r] = acc;
+        for (int w = 1; w < ORC_COMPRESS_BLOCKS; w *= 2)      /* pairwise tree */
+            for (int p = 0; p < ORC_COMPRESS_BLOCKS; p += 2 * w)
+                part[p] = part[p] + part[p + w];
+        e[r] = part[0];
     }
 }
 

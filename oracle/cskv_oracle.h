@@ -71,11 +71,15 @@ double orc_bf16_value(uint16_t h);
 /* ---------------- compress, quantise, append ----------------------------- */
 
 /* Stand-in for the learned 2->1 compressor [P2 "突破四"; P1 §3.2]:
- * e[r] = sum_j W[r][j] * u[j], u = x_even || x_odd, accumulated in fp32 from
- * j = 0 upward with one fused multiply-add per term, starting from +0.
+ * e[r] = sum_j W[r][j] * u[j], u = x_even || x_odd, in a fixed fp32 order:
+ * the 2D terms are cut into 64 contiguous blocks of 2D/64; each block is
+ * folded from its first term upward with one fused multiply-add per term,
+ * starting from +0; the 64 block sums are then added as a pairwise tree
+ * (blocks 2i and 2i+1, then adjacent pairs of those, and so on).
  * The pages' compressor is trained and not given: parity with it is
- * unpinned.  The fp32 chain itself is pinned against an fp64 evaluation
- * within the forward-error bound of a length-2D dot product. */
+ * unpinned.  The order is pinned by cases that round differently under
+ * other groupings, and the result against an fp64 evaluation within the
+ * forward-error bound of this order (2D/64 + 6 roundings per term). */
 void orc_compress_pair(const float *W, const float *x_even, const float *x_odd,
                        int dim, float *e);
 

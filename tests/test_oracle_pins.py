@@ -232,25 +232,51 @@ def test_compress_selects_rows():
     assert e[3] == np.float32(np.float32(2 * xe[7]) - xo[7]) and np.all(np.delete(e, 3) == 0)
 
 
-def test_compress_sequential_fma_order():
-    """The fold runs j = 0..2D-1 in order: 1e8 + 1 rounds to 1e8 in fp32, so
-    (1e8 + 1) - 1e8 = 0, while any regrouping that adds 1 last gives 1."""
+def test_compress_fma_order_within_a_block():
+    """Inside a block of 2D/64 terms the fold runs upward: 1e8 + 1 rounds to
+    1e8 in fp32, so (1e8 + 1) - 1e8 = 0, while any regrouping that adds 1
+    last gives 1."""
     import oracle as orc
-    D = 4
+    D = 576                                   # blocks of 18 terms
     W = np.zeros((D, 2 * D), np.float32)
     W[0, :3] = 1.0
-    xe = np.array([1e8, 1.0, -1e8, 0.0], np.float32)
+    xe = np.zeros(D, np.float32)
+    xe[:3] = [1e8, 1.0, -1e8]
     assert orc.compress_pair(W, xe, np.zeros(D, np.float32))[0] == 0.0
-    W[1, [0, 2, 1]] = 1.0
-    xe2 = np.array([1e8, 1.0, -1e8, 0], np.float32)
-    assert orc.compress_pair(W, xe2, np.zeros(D, np.float32))[1] == 0.0
     # a single rounding per term: after acc = -1, fma(1/3f, 3, acc) keeps the
     # product's low bits (a separate multiply would round 3 * (1/3f) to 1 first)
     W[:] = 0
     W[2, 0], W[2, 1] = -1.0, np.float32(1.0 / 3.0)
-    xe3 = np.array([1.0, 3.0, 0, 0], np.float32)
+    xe3 = np.zeros(D, np.float32)
+    xe3[:2] = [1.0, 3.0]
     exact = np.float64(np.float32(1.0 / 3.0)) * 3.0 - 1.0
     assert orc.compress_pair(W, xe3, np.zeros(D, np.float32))[2] == np.float32(exact)
+
+
+def test_compress_blocks_of_18_and_pairwise_tree():
+    """Block sums [1e8, 0, 4, 4]: the tree adds (4 + 4) before meeting 1e8 and
+    gets 1e8 + 8 exactly; a fold over j (or blocks joined left to right)
+    rounds 1e8 + 4 back to 1e8 twice.  Terms at j = 17 and j = 18 fall in
+    different blocks: with blocks of 16, 4 + 4 would meet first."""
+    import oracle as orc
+    D = 576
+    z = np.zeros(D, np.float32)
+    W = np.zeros((D, 2 * D), np.float32)
+    u = np.zeros(D, np.float32)
+    W[5, [0, 36, 54]] = 1.0                   # blocks 0, 2, 3
+    u[[0, 36, 54]] = [1e8, 4.0, 4.0]
+    assert orc.compress_pair(W, u, z)[5] == np.float32(100000008.0)
+    W[:] = 0
+    u[:] = 0
+    W[6, [0, 17, 18]] = 1.0                   # block 0 holds j = 0..17, block 1 starts at 18
+    u[[0, 17, 18]] = [1e8, 4.0, 4.0]
+    assert orc.compress_pair(W, u, z)[6] == np.float32(1e8)
+    # the second half of u (x_odd) is blocks 32..63: x_odd[0] meets x_even's
+    # block sums only at the last level of the tree
+    W[:] = 0
+    W[7, [0, D]] = 1.0
+    assert orc.compress_pair(W, np.full(D, 1e8, np.float32) * (np.arange(D) == 0),
+                             np.full(D, -1e8, np.float32) * (np.arange(D) == 0))[7] == 0.0
 
 
 def test_compress_within_forward_error_bound():
@@ -262,7 +288,9 @@ def test_compress_within_forward_error_bound():
     e = orc.compress_pair(W, xe, xo).astype(np.float64)
     u = np.concatenate([xe, xo]).astype(np.float64)
     ref = W.astype(np.float64) @ u
-    n, uu = 2 * D, 2.0 ** -24
+    # every term passes through at most 18 fused multiply-adds of its block
+    # and 6 additions of the tree
+    n, uu = 2 * D // 64 + 6, 2.0 ** -24
     gamma = n * uu / (1 - n * uu)
     bound = gamma * (np.abs(W.astype(np.float64)) @ np.abs(u))
     assert np.all(np.abs(e - ref) <= bound)
