@@ -289,13 +289,16 @@ int cskv_layer_group_decode(const cskv_cache *cache, const cskv_layer *layers, i
     hipError_t e;
     for (int i = 0; i < n_layers; ++i) {
         const cskv_layer &L = layers[i];
+        bool window_done = false;
         if (L.mode == CSKV_MODE_FULL && new_tokens && !appended) {
+            // the append also writes this layer's window row
             e = cskv::launch_kv_append(*cache, new_tokens, nullptr, cache->batch, w_comp, new_idx_rows, ws,
-                                       stream);
+                                       stream, L.swa_row ? L.swa : nullptr, L.swa_row, window);
             if (e != hipSuccess) return hip_fail(e, "layer group: append");
             appended = true;
+            window_done = L.swa_row != nullptr;
         }
-        if (L.swa_row) {
+        if (L.swa_row && !window_done) {
             e = cskv::launch_swa_append(L.swa, cache->batch, window, cache->dim, L.swa_row, nullptr,
                                         cache->batch, cache->n_tokens, stream);
             if (e != hipSuccess) return hip_fail(e, "layer group: window append");

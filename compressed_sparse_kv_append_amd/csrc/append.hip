@@ -21,6 +21,10 @@ struct AppendArgs {
     const uint16_t *idx_rows;
     float *ent;          // compressor output, [total_new][dim] (rows that complete an entry)
     int64_t total_new;
+    // one row per sequence only: this row's window entry, written with the append
+    uint16_t *swa_ring;  // [batch][swa_window][dim] bf16, or null
+    const float *swa_rows;
+    int swa_window;
 };
 
 // Rows of sequence b are [row0, row0 + m).  A malformed cu_new (decreasing,
@@ -197,10 +201,51 @@ __device__ void quantize_channel(float x, int t, int n, int g, uint8_t *codes_ro
     if (live && (t % g) == 0) scales_row[t / g] = s;
 }
 
+// Sequence b after its rows are quantised: store the trailing odd token,
+// advance n_tokens, or flag a rejected sequence.  p is n_tokens[b] as the
+// append found it.  Returns the sequence's token count afterwards.
+template <bool kCompress>
+__device__ int64_t finalize_seq(const AppendArgs &a, int b, int64_t p, int t, int nthreads)
+{
+    const cskv_cache &c = a.c;
+    const int64_t row0 = a.cu_new ? a.cu_new[b] : b;
+    const int64_t m = a.cu_new ? (int64_t)a.cu_new[b + 1] - row0 : 1;
+    if (m == 0) return p;
+    if (p < 0 || !rows_ok(row0, m, a.total_new)) {
+        if (t == 0) atomicOr(c.status, CSKV_STATUS_BAD_STATE);
+        return p;
+    }
+    if (kCompress) {
+        if ((p + m) / 2 > c.capacity) {
+            if (t == 0) atomicOr(c.status, CSKV_STATUS_OVERFLOW);
+            return p;
+        }
+        if (((p + m) & 1) != 0) {
+            const float *last = a.tokens + (size_t)(row0 + m - 1) * kDim;
+            for (int i = t; i < kDim; i += nthreads) c.pending[(size_t)b * kDim + i] = last[i];
+        }
+        if (t == 0) c.n_tokens[b] = (int32_t)(p + m);
+        return p + m;
+    } else {
+        if ((p & 1) != 0) {
+            if (t == 0) atomicOr(c.status, CSKV_STATUS_ODD_ENTRY_APPEND);
+            return p;
+        }
+        if (p / 2 + m > c.capacity) {
+            if (t == 0) atomicOr(c.status, CSKV_STATUS_OVERFLOW);
+            return p;
+        }
+        if (t == 0) c.n_tokens[b] = (int32_t)(p + 2 * m);
+        return p + 2 * m;
+    }
+}
+
 // One block per input row.  A block whose row completes an entry quantises
 // that entry (compressor mode: from the compressor's output; entries mode:
-// the row itself) and writes its codes, scales and indexer key.
-template <bool kCompress>
+// the row itself) and writes its codes, scales and indexer key.  kFinalize
+// (one row per sequence): the block then also finalises its sequence and
+// writes the row's window entry when a window ring is given.
+template <bool kCompress, bool kFinalize>
 __global__ __launch_bounds__(kAppendThreads) void quantize_kernel(AppendArgs a)
 {
     __shared__ float wave_max[kAppendThreads / kWave];
@@ -208,55 +253,37 @@ __global__ __launch_bounds__(kAppendThreads) void quantize_kernel(AppendArgs a)
     const int64_t r = blockIdx.x;
     const int t = threadIdx.x;
     const RowInfo ri = row_info<kCompress>(a, r);
-    if (ri.entry < 0) return;
-    const float e = kCompress ? a.ent[(size_t)r * kDim + t] : a.tokens[(size_t)r * kDim + t];
-    const size_t slot = (size_t)ri.b * c.capacity + (size_t)ri.entry;
-    quantize_channel(e, t, kDim, c.k_group, c.k_codes + slot * (kDim / 2),
-                     c.k_scales + slot * (kDim / c.k_group), wave_max);
-    if (c.v_group > 0) {
-        const int dv = c.dim - c.rope_dim;
-        quantize_channel(e, t, dv, c.v_group, c.v_codes + slot * (dv / 2),
-                         c.v_scales + slot * (dv / c.v_group), wave_max);
+    if (ri.entry >= 0) {
+        const float e = kCompress ? a.ent[(size_t)r * kDim + t] : a.tokens[(size_t)r * kDim + t];
+        const size_t slot = (size_t)ri.b * c.capacity + (size_t)ri.entry;
+        quantize_channel(e, t, kDim, c.k_group, c.k_codes + slot * (kDim / 2),
+                         c.k_scales + slot * (kDim / c.k_group), wave_max);
+        if (c.v_group > 0) {
+            const int dv = c.dim - c.rope_dim;
+            quantize_channel(e, t, dv, c.v_group, c.v_codes + slot * (dv / 2),
+                             c.v_scales + slot * (dv / c.v_group), wave_max);
+        }
+        if (t < c.idx_dim) c.idx_keys[slot * c.idx_dim + t] = a.idx_rows[(size_t)r * c.idx_dim + t];
     }
-    if (t < c.idx_dim) c.idx_keys[slot * c.idx_dim + t] = a.idx_rows[(size_t)r * c.idx_dim + t];
+    if (kFinalize) {
+        const int b = (int)r;
+        const int64_t p = c.n_tokens[b];
+        __syncthreads();                            // every thread has read n_tokens[b]
+        const int64_t end = finalize_seq<kCompress>(a, b, p, t, kAppendThreads);
+        if (a.swa_ring && end >= 1) {
+            const int64_t pos = end - 1;            // the position of this row's token
+            uint16_t *dst = a.swa_ring + ((size_t)b * a.swa_window + (size_t)(pos % a.swa_window)) * kDim;
+            dst[t] = (uint16_t)bf16_bits_rne(a.swa_rows[(size_t)b * kDim + t]);
+        }
+    }
 }
 
-// One wave per sequence, after the quantiser: stores the trailing odd token,
-// advances n_tokens, or flags a rejected sequence.
+// One wave per sequence, after the quantiser (several rows per sequence).
 template <bool kCompress>
 __global__ __launch_bounds__(kWave) void append_finalize_kernel(AppendArgs a)
 {
-    const cskv_cache &c = a.c;
-    const int b = blockIdx.x, t = threadIdx.x;
-    const int64_t row0 = a.cu_new ? a.cu_new[b] : b;
-    const int64_t m = a.cu_new ? (int64_t)a.cu_new[b + 1] - row0 : 1;
-    const int64_t p = c.n_tokens[b];
-    if (m == 0) return;
-    if (p < 0 || !rows_ok(row0, m, a.total_new)) {
-        if (t == 0) atomicOr(c.status, CSKV_STATUS_BAD_STATE);
-        return;
-    }
-    if (kCompress) {
-        if ((p + m) / 2 > c.capacity) {
-            if (t == 0) atomicOr(c.status, CSKV_STATUS_OVERFLOW);
-            return;
-        }
-        if (((p + m) & 1) != 0) {
-            const float *last = a.tokens + (size_t)(row0 + m - 1) * kDim;
-            for (int i = t; i < kDim; i += kWave) c.pending[(size_t)b * kDim + i] = last[i];
-        }
-        if (t == 0) c.n_tokens[b] = (int32_t)(p + m);
-    } else {
-        if ((p & 1) != 0) {
-            if (t == 0) atomicOr(c.status, CSKV_STATUS_ODD_ENTRY_APPEND);
-            return;
-        }
-        if (p / 2 + m > c.capacity) {
-            if (t == 0) atomicOr(c.status, CSKV_STATUS_OVERFLOW);
-            return;
-        }
-        if (t == 0) c.n_tokens[b] = (int32_t)(p + 2 * m);
-    }
+    const int b = blockIdx.x;
+    (void)finalize_seq<kCompress>(a, b, a.c.n_tokens[b], threadIdx.x, kWave);
 }
 
 struct SwaArgs {
@@ -300,11 +327,16 @@ size_t append_workspace_bytes(int total_new)
 
 hipError_t launch_kv_append(const cskv_cache &c, const float *tokens, const int32_t *cu_new,
                             int total_new, const float *w_comp, const uint16_t *idx_rows,
-                            void *ws, hipStream_t s)
+                            void *ws, hipStream_t s, uint16_t *swa_ring, const float *swa_rows,
+                            int swa_window)
 {
     if (total_new == 0) return hipSuccess;
-    AppendArgs a{c, tokens, cu_new, w_comp, idx_rows, static_cast<float *>(ws), total_new};
+    AppendArgs a{c, tokens, cu_new, w_comp, idx_rows, static_cast<float *>(ws), total_new,
+                 cu_new ? nullptr : swa_ring, swa_rows, swa_window};
     const TimedLaunch tl = timer_take(CSKV_KERNEL_APPEND);
+    // one row per sequence: the quantiser also finalises (one launch less)
+    const bool fused = cu_new == nullptr;
+    const dim3 qgrid((unsigned)total_new), qblock(kAppendThreads);
     if (w_comp) {
         // about 1024 waves: groups of 8 input rows x runs of output channels
         constexpr int kE = 8;
@@ -313,11 +345,16 @@ hipError_t launch_kv_append(const cskv_cache &c, const float *tokens, const int3
         const int cpw = (kDim + runs - 1) / runs;
         launch_kernel(compress_kernel<kE>, dim3((unsigned)((kDim + cpw - 1) / cpw), (unsigned)groups), dim3(kWave),
                       s, tl.start, nullptr, a, cpw);
-        launch_kernel(quantize_kernel<true>, dim3((unsigned)total_new), dim3(kAppendThreads), s, nullptr, nullptr, a);
-        launch_kernel(append_finalize_kernel<true>, dim3((unsigned)c.batch), dim3(kWave), s, nullptr, tl.stop, a);
+        if (fused) {
+            launch_kernel(quantize_kernel<true, true>, qgrid, qblock, s, nullptr, tl.stop, a);
+        } else {
+            launch_kernel(quantize_kernel<true, false>, qgrid, qblock, s, nullptr, nullptr, a);
+            launch_kernel(append_finalize_kernel<true>, dim3((unsigned)c.batch), dim3(kWave), s, nullptr, tl.stop, a);
+        }
+    } else if (fused) {
+        launch_kernel(quantize_kernel<false, true>, qgrid, qblock, s, tl.start, tl.stop, a);
     } else {
-        launch_kernel(quantize_kernel<false>, dim3((unsigned)total_new), dim3(kAppendThreads), s, tl.start, nullptr,
-                      a);
+        launch_kernel(quantize_kernel<false, false>, qgrid, qblock, s, tl.start, nullptr, a);
         launch_kernel(append_finalize_kernel<false>, dim3((unsigned)c.batch), dim3(kWave), s, nullptr, tl.stop, a);
     }
     return hipGetLastError();

@@ -25,9 +25,13 @@ int topk_slices(const cskv_cache &c);
 
 // Compressor output rows (fp32) staged between the compressor and the quantiser.
 size_t append_workspace_bytes(int total_new);
+// With cu_new == nullptr (one row per sequence) the quantiser also finalises
+// each sequence and, when swa_ring is given, writes swa_rows[b] into that
+// ring at the row's token position (what launch_swa_append would do).
 hipError_t launch_kv_append(const cskv_cache &c, const float *tokens, const int32_t *cu_new,
                             int total_new, const float *w_comp, const uint16_t *idx_rows,
-                            void *ws, hipStream_t s);
+                            void *ws, hipStream_t s, uint16_t *swa_ring = nullptr,
+                            const float *swa_rows = nullptr, int swa_window = 0);
 hipError_t launch_swa_append(uint16_t *ring, int batch, int window, int dim, const float *rows,
                              const int32_t *cu_new, int total_new, const int32_t *end_pos,
                              hipStream_t s);
