@@ -64,27 +64,6 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     const int col = lane & 15, grp = lane >> 4;
 
-    // Indexer query as MFMA A operands: row = head, contraction slots
-    // 8*grp..8*grp+7 of each 32-dim step.  Missing heads: zero rows, weight 0.
-    u32x4_t qa[MT][kSteps];
-    float hw[MT][4];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int head = 16 * mt + col;
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (head < a.heads)
-                v = *reinterpret_cast<const u32x4_t *>(a.q + ((size_t)b * a.heads + head) * DI + 32 * s + 8 * grp);
-            qa[mt][s] = v;
-        }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int hrow = 16 * mt + 4 * grp + v;
-            hw[mt][v] = hrow < a.heads ? (a.head_w ? a.head_w[(size_t)b * a.heads + hrow] : 1.0f) : 0.0f;
-        }
-    }
-
     const int n_tiles = (int)((e_end - e_begin + 15) / 16);
     const int my_n = n_tiles > w ? (n_tiles - w + kScanWaves - 1) / kScanWaves : 0;
     const uint8_t *kb = reinterpret_cast<const uint8_t *>(a.keys + (size_t)b * a.capacity * DI);
@@ -113,6 +92,29 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
 
 #pragma unroll
     for (int i = 0; i < kRing; ++i) issue(i);
+
+    // the query is loaded while the first tiles are in flight
+    // Indexer query as MFMA A operands: row = head, contraction slots
+    // 8*grp..8*grp+7 of each 32-dim step.  Missing heads: zero rows, weight 0.
+    u32x4_t qa[MT][kSteps];
+    float hw[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int head = 16 * mt + col;
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            if (head < a.heads)
+                v = *reinterpret_cast<const u32x4_t *>(a.q + ((size_t)b * a.heads + head) * DI + 32 * s + 8 * grp);
+            qa[mt][s] = v;
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int hrow = 16 * mt + 4 * grp + v;
+            hw[mt][v] = hrow < a.heads ? (a.head_w ? a.head_w[(size_t)b * a.heads + hrow] : 1.0f) : 0.0f;
+        }
+    }
+
     for (int i = 0; i < my_n; ++i) {
         // tile i has landed once at most the later tiles' loads are pending
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(kInst * (kRing - 1)));
