@@ -661,33 +661,51 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a)
 }
 
 // Merge of the S partial softmaxes of one (sequence, head group): block of
-// 256 threads, thread t -> head t / 16, dims (t % 16) * 32 .. + 31.
+// 256 threads, thread t -> head t / 16, dims (t % 16) * 32 .. + 31.  The
+// partial outputs of two splits are loaded together with their (m, l), so
+// the common two-split case costs one round trip to memory.
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a)
 {
     const int HG = a.heads / kHG;
     const int bh = blockIdx.x, b = bh / HG, hg = bh % HG;
     const int t = threadIdx.x, h = t >> 4, d0 = (t & 15) * 32;
     const size_t p0 = ((size_t)b * HG + hg) * a.splits;
-    float M = -INFINITY;
-    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.part_ml[(p0 + s) * 2 * kHG + h]);
-    float L = 0.f;
+    float M = -INFINITY, L = 0.f;
     float acc[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] = 0.f;
-    if (M > -INFINITY) {
-        for (int s = 0; s < a.splits; ++s) {
-            const float ms = a.part_ml[(p0 + s) * 2 * kHG + h];
-            if (ms == -INFINITY) continue;
-            const float f = exp2f(ms - M);
-            L += f * a.part_ml[(p0 + s) * 2 * kHG + kHG + h];
+    // splits two at a time, with a running maximum (one pass when S = 2)
+    for (int s0 = 0; s0 < a.splits; s0 += 2) {
+        float4 x[2][8];
+        float ms[2], ls[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int s = s0 + j < a.splits ? s0 + j : s0;
+            ms[j] = a.part_ml[(p0 + s) * 2 * kHG + h];
+            ls[j] = a.part_ml[(p0 + s) * 2 * kHG + kHG + h];
             const float4 *src = reinterpret_cast<const float4 *>(a.part_o + ((p0 + s) * kHG + h) * kDv + d0);
 #pragma unroll
+            for (int i = 0; i < 8; ++i) x[j][i] = src[i];
+        }
+        if (s0 + 1 >= a.splits) ms[1] = -INFINITY;
+        const float Mn = fmaxf(M, fmaxf(ms[0], ms[1]));
+        if (Mn == -INFINITY) continue;                 // nothing in these splits yet
+        const float r = exp2f(M - Mn);                 // 0 while M is -inf
+        L *= r;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) acc[i] *= r;
+        M = Mn;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (ms[j] == -INFINITY) continue;
+            const float f = exp2f(ms[j] - M);
+            L += f * ls[j];
+#pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float4 x = src[i];
-                acc[4 * i] = fmaf(f, x.x, acc[4 * i]);
-                acc[4 * i + 1] = fmaf(f, x.y, acc[4 * i + 1]);
-                acc[4 * i + 2] = fmaf(f, x.z, acc[4 * i + 2]);
-                acc[4 * i + 3] = fmaf(f, x.w, acc[4 * i + 3]);
+                acc[4 * i] = fmaf(f, x[j][i].x, acc[4 * i]);
+                acc[4 * i + 1] = fmaf(f, x[j][i].y, acc[4 * i + 1]);
+                acc[4 * i + 2] = fmaf(f, x[j][i].z, acc[4 * i + 2]);
+                acc[4 * i + 3] = fmaf(f, x[j][i].w, acc[4 * i + 3]);
             }
         }
     }
