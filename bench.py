@@ -137,10 +137,19 @@ def cpu_baseline(synth, w, nseq: int):
     dt = time.perf_counter() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     per_full_step = dt * w.batch / nseq
+    cpu = "unknown CPU"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": 1.0 / per_full_step, "unit": "steps/s", "cores": min(threads, nseq),
             "kind": "oracle",
             "sample": f"{nseq} of {w.batch} sequences at full length ({w.entries} entries), one Full-layer "
-                      f"decode step ({dt:.2f} s), scaled by {w.batch}/{nseq}; cache build untimed"}
+                      f"decode step ({dt:.2f} s), scaled by {w.batch}/{nseq}; cache build untimed; "
+                      f"OpenMP over sequences on {cpu}"}
 
 
 def pmc_traffic():
@@ -178,7 +187,8 @@ def main():
     w = synth.WORKLOADS[a.workload]
     assert w.entries is not None and len(w.layers) == 1, "bench steps fixed-length single-layer workloads"
     timer_steps = min(a.steps, 100)
-    total_steps = a.warmup + timer_steps + a.steps + a.replicas
+    dist_steps = min(a.steps, 100)
+    total_steps = a.warmup + timer_steps + dist_steps + a.steps + a.replicas
     per_rep = (total_steps + a.replicas - 1) // a.replicas
     cap = w.entries + (per_rep + 1) // 2 + 16
 
@@ -256,6 +266,18 @@ def main():
         ck.timer_disable_all()
     ent_after = np.mean([r.n_tokens.float().mean().item() for r in reps]) / 2
 
+    # per-step distribution: events around each step of a separate pass
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(dist_steps)]
+    torch.cuda.synchronize()
+    for ev0, ev1 in evs:
+        ev0.record()
+        step(i)
+        ev1.record()
+        i += 1
+    torch.cuda.synchronize()
+    per_step = np.array([ev0.elapsed_time(ev1) * 1000.0 for ev0, ev1 in evs])
+
     # per-kernel breakdown: separate eager pass with every timer on
     for kd in kinds.values():
         ck.timer_enable(kd, timer_steps)
@@ -305,6 +327,10 @@ def main():
                      "timed_launches": scan["launches"],
                      "timing": ("hip events in the timed region, 1 step in %d" % every) if live is not None
                      else "hip events, separate eager pass"},
+        "step_us": {"p10": round(float(np.percentile(per_step, 10)), 2),
+                    "p50": round(float(np.percentile(per_step, 50)), 2),
+                    "p90": round(float(np.percentile(per_step, 90)), 2),
+                    "steps": int(dist_steps), "timing": "hip events around each step, separate pass"},
         "step_bytes": round(sb["total"]),
         "step_hbm_frac": round(sb["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
