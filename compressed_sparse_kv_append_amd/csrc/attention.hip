@@ -6,13 +6,15 @@
 //
 // Work decomposition.  The keys of a sequence are the k selected entries,
 // cut into chunks of 128, and the window rows, cut into chunks of 64.  A
-// split is a run of chunks of one kind; one block of 8 waves takes 16 query
-// heads and one split, and a second kernel merges the partial softmaxes of
-// each head by their log-sum-exp (skipped when there is one split).  The
-// blocks that share a split's keys (one per head group) are numbered so that
-// they land on the same XCD and read the gathered rows through one L2.
-// Keeping a block to one kind lets each loop hold its own prefetch registers
-// and makes every load in it unconditional.
+// split is a run of entry chunks and/or a run of window chunks; one block of
+// 8 waves takes 16 query heads and one split, and a second kernel merges the
+// partial softmaxes of each head by their log-sum-exp (skipped when there is
+// one split).  A split may mix the kinds so that every block of a launch
+// carries about the same work.  The blocks that share a split's keys (one
+// per head group) are numbered so that they land on the same XCD and read
+// the gathered rows through one L2.  Each kind has a loop of its own, run one
+// after the other with one softmax state, so that each loop holds its own
+// prefetch registers and every load in it is unconditional.
 //
 // Per chunk.  The gathered rows stay E2M1 codes in LDS: the key plane row-
 // major (MFMA B operand of Q.K^T: 8 consecutive dims of one key = one 32-bit
@@ -93,14 +95,14 @@ struct AttnArgs {
     float *part_ml;     // [B][HG][S][2][16] partial max (log2 units) and sum
     int heads, k, window;
     int n_sparse, n_win;
-    int sparse_splits, per_sparse, per_win, splits;
+    int win_split0, per_sparse, per_win, splits;
     float scale_log2;   // softmax_scale * log2(e)
 };
 
 // Per-block constants shared by the chunk loop.
 struct Ctx {
     int t, lane, w, col, grp;
-    int nloc;           // chunks of this block
+    int ne, nw;         // entry chunks, then window chunks, of this block
     int G;              // key groups per row
     size_t row0;        // first cache row of the sequence
     const uint16_t *ring;
@@ -518,16 +520,17 @@ __device__ __forceinline__ void chunk_pv(const AttnSmem &sm, const Ctx &x, f32x4
 // The chunk loop of one block: the next chunk's HBM reads are in flight
 // while the current chunk is computed.
 template <bool SPARSE, bool SPLIT, int VGS, int KG>
-__device__ __forceinline__ void run_chunks(const AttnArgs &a, AttnSmem &sm, const Ctx &x, f32x4_t (&o)[4])
+__device__ __forceinline__ void run_chunks(const AttnArgs &a, AttnSmem &sm, const Ctx &x, int first, int end,
+                                           f32x4_t (&o)[4])
 {
     if (SPARSE) {
         SparseRegs r;
-        fetch_sparse<SPLIT, VGS>(a, sm, x, 0, r);
-        for (int lc = 0; lc < x.nloc; ++lc) {
+        fetch_sparse<SPLIT, VGS>(a, sm, x, first, r);
+        for (int lc = first; lc < end; ++lc) {
             __syncthreads();                               // previous chunk fully consumed
             store_sparse<SPLIT, VGS>(sm, x, r);
             __syncthreads();
-            if (lc + 1 < x.nloc) fetch_sparse<SPLIT, VGS>(a, sm, x, lc + 1, r);
+            if (lc + 1 < end) fetch_sparse<SPLIT, VGS>(a, sm, x, lc + 1, r);
             chunk_logits<true, KG>(sm, x);
             __syncthreads();
             chunk_softmax<true>(sm, x, lc, a.scale_log2);
@@ -536,12 +539,12 @@ __device__ __forceinline__ void run_chunks(const AttnArgs &a, AttnSmem &sm, cons
         }
     } else {
         WindowRegs r;
-        fetch_window(a, sm, x, 0, r);
-        for (int lc = 0; lc < x.nloc; ++lc) {
+        fetch_window(a, sm, x, first, r);
+        for (int lc = first; lc < end; ++lc) {
             __syncthreads();
             store_window(sm, x, r);
             __syncthreads();
-            if (lc + 1 < x.nloc) fetch_window(a, sm, x, lc + 1, r);
+            if (lc + 1 < end) fetch_window(a, sm, x, lc + 1, r);
             chunk_logits<false, KG>(sm, x);
             __syncthreads();
             chunk_softmax<false>(sm, x, lc, a.scale_log2);
@@ -568,9 +571,10 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a)
     const int hg = rest % HG, u = (rest / HG) * 8 + xcd;
     if (u >= U) return;
     const int b = u / a.splits, split = u % a.splits;
-    const bool sparse = split < a.sparse_splits;
-    const int c0 = sparse ? split * a.per_sparse : (split - a.sparse_splits) * a.per_win;
-    const int c1 = sparse ? min(a.n_sparse, c0 + a.per_sparse) : min(a.n_win, c0 + a.per_win);
+    // entry chunks [e0, e1) and window chunks [w0, w1) of this split
+    const int e0 = min(split * a.per_sparse, a.n_sparse), e1 = min(e0 + a.per_sparse, a.n_sparse);
+    const int ws = split - a.win_split0;
+    const int w0 = ws < 0 ? 0 : min(ws * a.per_win, a.n_win), w1 = ws < 0 ? 0 : min(w0 + a.per_win, a.n_win);
 
     Ctx x;
     x.t = threadIdx.x;
@@ -578,7 +582,8 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a)
     x.w = x.t / kWave;
     x.col = x.lane & 15;
     x.grp = x.lane >> 4;
-    x.nloc = c1 - c0;
+    x.ne = e1 - e0;
+    x.nw = w1 - w0;
     x.G = kD / KG;
     x.row0 = (size_t)b * c.capacity;
     x.ring = a.swa + (size_t)b * a.window * kD;
@@ -587,8 +592,10 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a)
     nswa = nswa < 0 ? 0 : (nswa > a.window ? a.window : nswa);
 
     // ---- key sources of every chunk of the split
-    for (int i = x.t; i < x.nloc * kSK; i += kThreads) {
-        const int chunk = c0 + i / kSK, j = i % kSK;
+    for (int i = x.t; i < (x.ne + x.nw) * kSK; i += kThreads) {
+        const int lc = i / kSK, j = i % kSK;
+        const bool sparse = lc < x.ne;
+        const int chunk = sparse ? e0 + lc : w0 + lc - x.ne;
         int32_t s = -1;
         if (sparse) {
             const int jj = chunk * kSK + j;
@@ -621,10 +628,8 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a)
     for (int nt = 0; nt < 4; ++nt) o[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     __syncthreads();
 
-    if (x.nloc > 0) {
-        if (sparse) run_chunks<true, SPLIT, VGS, KG>(a, sm, x, o);
-        else run_chunks<false, SPLIT, VGS, KG>(a, sm, x, o);
-    }
+    if (x.ne > 0) run_chunks<true, SPLIT, VGS, KG>(a, sm, x, 0, x.ne, o);
+    if (x.nw > 0) run_chunks<false, SPLIT, VGS, KG>(a, sm, x, x.ne, x.ne + x.nw, o);
     __syncthreads();
 
     // ---- results: final (one split) or partial (merged by attn_merge_kernel)
@@ -723,10 +728,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a)
 
 AttnPlan attn_plan(const cskv_cache &c, int heads, int k, int window)
 {
-    // Blocks of 8 waves, one per CU (the staging takes most of the LDS).  The
-    // split is chosen from a rough cost per block -- setup, then per chunk a
-    // fixed cost that is about twice as high for 128 entries as for 64 window
-    // rows -- times the rounds of 256 blocks, plus the merge when splitting.
+    // Blocks of 8 waves, one per CU (the staging takes most of the LDS).  A
+    // split takes per_sparse entry chunks and per_win window chunks; in the
+    // kind-pure layout the entry splits come first and each split holds one
+    // kind, in the mixed layout split i holds entry chunks and window chunks
+    // both (one softmax state across the two loops).  The layout and split
+    // sizes are chosen from a rough cost per block -- setup, then per chunk
+    // a fixed cost about twice as high for 128 entries as for 64 window rows
+    // -- times the rounds of 256 blocks, plus the merge when splitting.
     AttnPlan p;
     p.n_sparse = (k + kSK - 1) / kSK;
     p.n_win = (window + kWK - 1) / kWK;
@@ -734,16 +743,24 @@ AttnPlan attn_plan(const cskv_cache &c, int heads, int k, int window)
     double best = 1e300;
     p.per_sparse = p.n_sparse;
     p.per_win = p.n_win;
-    for (int ps = 1; ps <= p.n_sparse && ps <= kMaxSplitChunks; ++ps)
-        for (int pw = 1; pw <= p.n_win && pw <= kMaxSplitChunks; ++pw) {
-            const int ss = (p.n_sparse + ps - 1) / ps, sw = (p.n_win + pw - 1) / pw;
-            const double blocks = (double)units * (ss + sw);
-            const double rounds = ceil(blocks / 256.0);
-            const double cost = rounds * (3.0 + fmax(2.0 * ps, 1.0 * pw)) + (ss + sw > 1 ? 4.0 : 0.0);
-            if (cost < best - 1e-9) { best = cost; p.per_sparse = ps; p.per_win = pw; }
-        }
-    p.sparse_splits = (p.n_sparse + p.per_sparse - 1) / p.per_sparse;
-    p.splits = p.sparse_splits + (p.n_win + p.per_win - 1) / p.per_win;
+    p.win_split0 = 1;
+    for (int mixed = 0; mixed < 2; ++mixed)
+        for (int ps = 1; ps <= p.n_sparse && ps <= kMaxSplitChunks; ++ps)
+            for (int pw = 1; pw <= p.n_win && pw <= kMaxSplitChunks; ++pw) {
+                if (mixed && ps + pw > kMaxSplitChunks) continue;
+                const int ss = (p.n_sparse + ps - 1) / ps, sw = (p.n_win + pw - 1) / pw;
+                const int splits = mixed ? (ss > sw ? ss : sw) : ss + sw;
+                const double rounds = ceil((double)units * splits / 256.0);
+                const double chain = mixed ? 2.0 * ps + pw + 0.5 : fmax(2.0 * ps, 1.0 * pw);
+                const double cost = rounds * (3.0 + chain) + (splits > 1 ? 4.0 : 0.0);
+                if (cost < best - 1e-9) {
+                    best = cost;
+                    p.per_sparse = ps;
+                    p.per_win = pw;
+                    p.win_split0 = mixed ? 0 : ss;
+                    p.splits = splits;
+                }
+            }
     const size_t parts = (size_t)units * p.splits;
     p.ws_bytes = p.splits > 1 ? parts * kHG * (kDv + 2) * sizeof(float) + 256 : 0;
     return p;
@@ -759,7 +776,7 @@ hipError_t launch_sparse_attn(const cskv_cache &c, const float *q, int heads, co
     float *part_o = p.splits > 1 ? static_cast<float *>(ws) : nullptr;
     float *part_ml = p.splits > 1 ? part_o + units * kHG * kDv : nullptr;
     AttnArgs a{c, q, idx, swa, swa_len, out, lse, part_o, part_ml, heads, k, window,
-               p.n_sparse, p.n_win, p.sparse_splits, p.per_sparse, p.per_win, p.splits,
+               p.n_sparse, p.n_win, p.win_split0, p.per_sparse, p.per_win, p.splits,
                (float)((double)scale * 1.4426950408889634)};
     const int U = c.batch * p.splits;
     const unsigned blocks = (unsigned)(8 * hg * ((U + 7) / 8));

@@ -43,13 +43,15 @@ hipError_t launch_indexer_topk(const cskv_cache &c, const uint16_t *q_idx, int h
                                const float *head_w, int k, int32_t *out_idx, void *ws,
                                hipStream_t s);
 // Split of the keys of one (sequence, head group) over blocks: selected
-// entries in chunks of 128, window rows in chunks of 64; a split holds chunks
-// of one kind only.  Splits [0, sparse_splits) take per_sparse entry chunks
-// each, the rest per_win window chunks each.  ws_bytes: partial results
-// when splits > 1.
+// entries in chunks of 128, window rows in chunks of 64.  Split i takes entry
+// chunks [i per_sparse, (i + 1) per_sparse) and window chunks
+// [(i - win_split0) per_win, (i - win_split0 + 1) per_win), each clipped to
+// what exists (none for i < win_split0).  win_split0 = 0 mixes both kinds in
+// one split; win_split0 = the number of entry splits keeps each split to one
+// kind.  ws_bytes: partial results when splits > 1.
 struct AttnPlan {
     int n_sparse, n_win;
-    int sparse_splits, per_sparse, per_win, splits;
+    int win_split0, per_sparse, per_win, splits;
     size_t ws_bytes;
 };
 AttnPlan attn_plan(const cskv_cache &c, int heads, int k, int window);

@@ -66,3 +66,31 @@ def load_entries(g: ck.Cache, h: orc.Cache, entries_per_seq, idx_keys_per_seq):
     keys = np.concatenate(idx_keys_per_seq).astype(np.uint16)
     ck.kv_append_fp4(g, dev(rows), dev(cu), None, dev(keys))
     orc.kv_append(h, rows, cu, None, keys)
+
+
+def lse_tol(h: orc.Cache, q: np.ndarray, idx: np.ndarray, ring: np.ndarray, swa_len: np.ndarray,
+            scale: float) -> np.ndarray:
+    """Per (sequence, head) bound on |lse - lse_ref| from the arithmetic of the
+    logits: q enters the bf16 products as a high + low bf16 pair (relative
+    error <= 2^-17 per element) and the 576-term sums accumulate in fp32
+    (<= 576 * 2^-24 relative to the sum of |terms|), the keys being exact
+    (E2M1 codes times fp32 group scales, bf16 window rows).  A softmax-
+    weighted mean of logit errors is at most the largest, so
+      |d lse| <= 2^-14 * scale * max_j sum_d |q_d| |k_jd| + 1e-5
+    (2^-14 > 2^-17 + 576 * 2^-24; 1e-5 covers the fp32 log-sum-exp itself)."""
+    B, H, D = q.shape
+    tol = np.full((B, H), 1e-5)
+    for b in range(B):
+        E = int(min(h.n_tokens[b] // 2, h.capacity))
+        keys = []
+        for e in idx[b]:
+            if 0 <= e < E:
+                keys.append(orc.dequantize_row(h.k_codes[b, e], h.k_scales[b, e], D, h.k_group))
+        nw = int(min(swa_len[b], ring.shape[1]))
+        if nw:
+            keys.append((ring[b, :nw].astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+        if not keys:
+            continue
+        K = np.abs(np.vstack(keys))
+        tol[b] += 2.0 ** -14 * scale * (np.abs(q[b].astype(np.float64)) @ K.T).max(axis=1)
+    return tol
