@@ -43,10 +43,12 @@ namespace {
 
 constexpr int kBins = 2048;
 constexpr int kDigit = 11;
-constexpr int kSliceThreads = 256;                      // slice blocks: 4 waves
+constexpr int kSliceThreads = 512;                      // slice blocks: 8 waves
 constexpr int kSlicePer = kSliceKeys / kSliceThreads;   // keys per thread in a slice (16)
-constexpr int kMergeThreads = 256;
-constexpr int kMergePer = 36;                           // candidates per thread per merge round
+constexpr int kMergeThreads = 512;                      // merge blocks: 8 waves
+constexpr int kMergeContigPer = kSliceKeys / kMergeThreads;  // a sequence of one slice (8)
+constexpr int kMergePerSmall = 10;                      // up to 5120 candidates in one round
+constexpr int kMergePer = 36;                           // more: 18432 per round
 
 // Items of one selection, in ascending index order: a contiguous key array
 // (the item at position p has index base + p; positions < n are valid), or
@@ -144,7 +146,7 @@ __device__ __forceinline__ uint64_t load_keys(const Items &it, int64_t r, uint32
 {
     const int64_t p0 = r * (int64_t)(THREADS * PER) + (int64_t)PER * threadIdx.x;
     uint64_t vm = 0;
-    if (!kList) {
+    if constexpr (!kList) {
         static_assert(PER % 4 == 0, "contiguous keys load as uint4");
 #pragma unroll
         for (int i = 0; i < PER; i += 4) {
@@ -383,13 +385,16 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(SelectArgs a)
     }
     if (E <= kSliceKeys) {
         Items it{a.keys + (size_t)b * a.key_stride, nullptr, E, 0};
-        select_topk<false, false, kMergeThreads, kMergePer>(sm, it, a.k, out, nullptr);
+        select_topk<false, false, kMergeThreads, kMergeContigPer>(sm, it, a.k, out, nullptr);
         return;
     }
+    // every list is full but the last slice's, whose first min(k, its
+    // entries) slots are valid: the padding after them is not read
     const int64_t used = (E + kSliceKeys - 1) / kSliceKeys;
-    Items it{nullptr, a.cand + (size_t)b * a.cand_stride, used * a.k, 0};
-    if (it.n <= kMergeThreads * kSlicePer)     // one round of 16 candidates per thread
-        select_topk<true, false, kMergeThreads, kSlicePer>(sm, it, a.k, out, nullptr);
+    const int64_t last = E - (used - 1) * kSliceKeys;
+    Items it{nullptr, a.cand + (size_t)b * a.cand_stride, (used - 1) * a.k + (last < a.k ? last : a.k), 0};
+    if (it.n <= kMergeThreads * kMergePerSmall)
+        select_topk<true, false, kMergeThreads, kMergePerSmall>(sm, it, a.k, out, nullptr);
     else
         select_topk<true, false, kMergeThreads, kMergePer>(sm, it, a.k, out, nullptr);
 }

@@ -168,15 +168,26 @@ def test_indexer_topk_exact_ragged(ck, orc, idx_dim, heads):
 
 
 def test_indexer_topk_long_sequences_merge_slices(ck, orc):
-    """Sequences longer than one select round (36,864 keys) go through the
-    per-slice candidate lists and the merge; short ones in the same batch
-    take the direct path."""
+    """Sequences longer than one slice (4096 keys) go through the per-slice
+    candidate lists and the merge, while short ones in the same batch are
+    selected from their keys directly."""
     lens = [36864, 36865, 80000, 700, 0]
     _indexer_case(ck, orc, lens, 128, 64, 512, seed=40)
     _indexer_case(ck, orc, [50000, 36900], 64, 4, 2048, seed=41)
     zero = lambda g, n: np.zeros((n, 64), np.uint16)
     got = _indexer_case(ck, orc, [90000, 40000], 64, 4, 512, seed=42, key_fn=zero)
     assert np.array_equal(got[0], np.arange(512)) and np.array_equal(got[1], np.arange(512))
+
+
+def test_indexer_topk_merge_candidate_counts(ck, orc):
+    """Slices hold 4096 entries; the merge reads k candidates per full slice
+    and min(k, entries) of the last one.  Lengths put the last slice at 1,
+    k, k + 1 and 4096 entries and the candidate count on both sides of 5120,
+    where the merge changes from 10 to 36 candidates per thread."""
+    s = 4096
+    lens = [8 * s + 1, 8 * s + 512, 8 * s + 513, 10 * s, 10 * s + 1, 10 * s + 511]
+    _indexer_case(ck, orc, lens, 64, 4, 512, seed=43)
+    _indexer_case(ck, orc, [s + 100, 2 * s + 2047, 2 * s + 2048, 2 * s + 2049], 64, 4, 2048, seed=44)
 
 
 def test_indexer_topk_head_weights_and_small_k(ck, orc):
