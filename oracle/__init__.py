@@ -90,6 +90,16 @@ def _declare(L):
     L.orc_indexer_topk.restype = None
     L.orc_indexer_topk.argtypes = [P(_Cache), P(C.c_uint16), C.c_int, P(C.c_float), C.c_int,
                                    P(i32)]
+    L.orc_pool_blocks.restype = None
+    L.orc_pool_blocks.argtypes = [P(f64), i64, C.c_int, C.c_int, P(i32)]
+    L.orc_topk_in_pool.restype = None
+    L.orc_topk_in_pool.argtypes = [P(f64), i64, P(i32), C.c_int, C.c_int, C.c_int, P(i32)]
+    L.orc_indexer_pool.restype = None
+    L.orc_indexer_pool.argtypes = [P(_Cache), P(C.c_uint16), C.c_int, P(C.c_float), C.c_int,
+                                   C.c_int, P(i32)]
+    L.orc_indexer_topk_in_pool.restype = None
+    L.orc_indexer_topk_in_pool.argtypes = [P(_Cache), P(C.c_uint16), C.c_int, P(C.c_float), P(i32),
+                                           C.c_int, C.c_int, C.c_int, P(i32)]
     L.orc_sparse_attn.restype = None
     L.orc_sparse_attn.argtypes = [P(_Cache), P(C.c_float), C.c_int, P(i32), C.c_int,
                                   P(C.c_uint16), C.c_int, P(i32), f64, P(f64), P(f64)]
@@ -180,6 +190,25 @@ def topk(scores, k) -> np.ndarray:
     return out
 
 
+def pool_blocks(scores, block, nb) -> np.ndarray:
+    """Candidate pool of the hierarchical indexer: the nb best blocks of
+    `block` entries by block maximum (ties: lower block), ascending, -1 padded."""
+    s = np.ascontiguousarray(scores, np.float64)
+    out = np.empty(nb, np.int32)
+    lib().orc_pool_blocks(_p(s, C.c_double), s.shape[0], block, nb, _p(out, C.c_int32))
+    return out
+
+
+def topk_in_pool(scores, pool, block, k) -> np.ndarray:
+    """Exact top-k among the entries of the pooled blocks, ascending, -1 padded."""
+    s = np.ascontiguousarray(scores, np.float64)
+    pl = np.ascontiguousarray(pool, np.int32)
+    out = np.empty(k, np.int32)
+    lib().orc_topk_in_pool(_p(s, C.c_double), s.shape[0], _p(pl, C.c_int32), pl.shape[0], block, k,
+                           _p(out, C.c_int32))
+    return out
+
+
 # ------------------------------------------------------------------ cache
 
 @dataclass
@@ -258,6 +287,27 @@ def indexer_topk(cache: Cache, q_idx, k, head_w=None) -> np.ndarray:
     return out
 
 
+def indexer_pool(cache: Cache, q_idx, block, nb, head_w=None) -> np.ndarray:
+    q = np.ascontiguousarray(q_idx, np.uint16)
+    hw = None if head_w is None else _f32(head_w)
+    out = np.empty((cache.batch, nb), np.int32)
+    c = cache._c()
+    lib().orc_indexer_pool(C.byref(c), _p(q, C.c_uint16), q.shape[1], _p(hw, C.c_float), block, nb,
+                           _p(out, C.c_int32))
+    return out
+
+
+def indexer_topk_in_pool(cache: Cache, q_idx, pool, block, k, head_w=None) -> np.ndarray:
+    q = np.ascontiguousarray(q_idx, np.uint16)
+    hw = None if head_w is None else _f32(head_w)
+    pl = np.ascontiguousarray(pool, np.int32)
+    out = np.empty((cache.batch, k), np.int32)
+    c = cache._c()
+    lib().orc_indexer_topk_in_pool(C.byref(c), _p(q, C.c_uint16), q.shape[1], _p(hw, C.c_float),
+                                   _p(pl, C.c_int32), pl.shape[1], block, k, _p(out, C.c_int32))
+    return out
+
+
 def sparse_attn(cache: Cache, q, idx, swa, scale, swa_len=None):
     q = _f32(q)
     B, H, D = q.shape
@@ -276,24 +326,32 @@ def sparse_attn(cache: Cache, q, idx, swa, scale, swa_len=None):
 
 
 def layer_group_decode(cache: Cache, modes, new_token, new_idx_row, w_comp, q, q_idx,
-                       swa_rings, swa_rows, k, scale, head_w=None):
+                       swa_rings, swa_rows, k, scale, head_w=None, pool=None):
     """One CSA2 layer-group decode step over a shared cache.
 
     new_token fp32 [B, dim] (appended by the full layer, or None);
     q / q_idx / swa_rings / swa_rows: per-layer lists (q_idx None for reuse).
+    pool = (block, nb): the hierarchical indexer -- the first full layer's
+    scores give the candidate pool and later reindex layers select inside it.
     swa_rings are updated in place.  Returns (outs, lses, idx_lists) per layer.
     """
     B = cache.batch
     cu = np.arange(B + 1, dtype=np.int32)
     outs, lses, idxs = [], [], []
     last_idx = None
+    cand = None
     for li, mode in enumerate(modes):
         if mode == "full" and new_token is not None:
             kv_append(cache, new_token, cu, w_comp, new_idx_row)
         swa_append(swa_rings[li], swa_rows[li], cu, cache.n_tokens)
         if mode in ("full", "reindex"):
             hw = None if head_w is None else head_w[li]
-            last_idx = indexer_topk(cache, q_idx[li], k, hw)
+            if mode == "reindex" and cand is not None:
+                last_idx = indexer_topk_in_pool(cache, q_idx[li], cand, pool[0], k, hw)
+            else:
+                last_idx = indexer_topk(cache, q_idx[li], k, hw)
+            if mode == "full" and pool is not None and cand is None:
+                cand = indexer_pool(cache, q_idx[li], pool[0], pool[1], hw)
         elif last_idx is None:
             raise ValueError("reuse layer with no preceding full/reindex layer")
         o, l = sparse_attn(cache, q[li], last_idx, swa_rings[li], scale)

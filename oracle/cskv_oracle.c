@@ -303,6 +303,77 @@ void orc_indexer_topk(const orc_cache *c, const uint16_t *q, int heads,
     }
 }
 
+/* ------------------------------------------------------------ candidate pool */
+
+void orc_pool_blocks(const double *scores, int64_t E, int block, int nb, int32_t *pool)
+{
+    int64_t nblocks = E > 0 ? (E + block - 1) / block : 0;
+    double *bmax = (double *)malloc(sizeof(double) * (size_t)(nblocks > 0 ? nblocks : 1));
+    for (int64_t i = 0; i < nblocks; ++i) {
+        double m = -INFINITY;
+        for (int64_t j = i * block; j < (i + 1) * block && j < E; ++j)
+            if (scores[j] > m) m = scores[j];
+        bmax[i] = m;
+    }
+    orc_topk(bmax, nblocks, nb, pool);
+    free(bmax);
+}
+
+void orc_topk_in_pool(const double *scores, int64_t E, const int32_t *pool, int nb, int block,
+                      int k, int32_t *out)
+{
+    /* the pooled entries in ascending order, and their scores */
+    int64_t *ent = (int64_t *)malloc(sizeof(int64_t) * (size_t)nb * block + 1);
+    double *sub = (double *)malloc(sizeof(double) * (size_t)nb * block + 1);
+    int64_t n = 0;
+    for (int i = 0; i < nb; ++i) {
+        if (pool[i] < 0) continue;
+        for (int64_t j = (int64_t)pool[i] * block; j < ((int64_t)pool[i] + 1) * block && j < E; ++j) {
+            ent[n] = j;
+            sub[n] = scores[j];
+            ++n;
+        }
+    }
+    /* positions in `sub` ascend with the entry index, so the top-k tie rule
+     * on positions is the tie rule on entries */
+    orc_topk(sub, n, k, out);
+    for (int i = 0; i < k; ++i)
+        if (out[i] >= 0) out[i] = (int32_t)ent[out[i]];
+    free(ent);
+    free(sub);
+}
+
+void orc_indexer_pool(const orc_cache *c, const uint16_t *q, int heads, const float *head_w,
+                      int block, int nb, int32_t *pool)
+{
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < c->batch; ++b) {
+        int64_t E = entries_of(c, b);
+        double *s = (double *)malloc(sizeof(double) * (size_t)(E > 0 ? E : 1));
+        orc_indexer_scores(c->idx_keys + (size_t)b * c->capacity * c->idx_dim, E, c->idx_dim,
+                           q + (size_t)b * heads * c->idx_dim, heads,
+                           head_w ? head_w + (size_t)b * heads : NULL, s);
+        orc_pool_blocks(s, E, block, nb, pool + (size_t)b * nb);
+        free(s);
+    }
+}
+
+void orc_indexer_topk_in_pool(const orc_cache *c, const uint16_t *q, int heads,
+                              const float *head_w, const int32_t *pool, int nb, int block, int k,
+                              int32_t *out)
+{
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < c->batch; ++b) {
+        int64_t E = entries_of(c, b);
+        double *s = (double *)malloc(sizeof(double) * (size_t)(E > 0 ? E : 1));
+        orc_indexer_scores(c->idx_keys + (size_t)b * c->capacity * c->idx_dim, E, c->idx_dim,
+                           q + (size_t)b * heads * c->idx_dim, heads,
+                           head_w ? head_w + (size_t)b * heads : NULL, s);
+        orc_topk_in_pool(s, E, pool + (size_t)b * nb, nb, block, k, out + (size_t)b * k);
+        free(s);
+    }
+}
+
 /* ------------------------------------------------------------ attention */
 
 void orc_sparse_attn(const orc_cache *c, const float *q, int heads, const int32_t *idx,

@@ -150,6 +150,39 @@ void orc_topk(const double *scores, int64_t E, int k, int32_t *out);
 void orc_indexer_topk(const orc_cache *c, const uint16_t *q, int heads,
                       const float *head_w, int k, int32_t *out);
 
+/* ---------------- hierarchical indexer: the candidate pool ---------------- */
+
+/* Candidate pool [P2 "层级稀疏索引器：后面的层只在候选池里找": the first Full
+ * layer scores every position, each block of 8 positions keeps its highest
+ * score, the 2048 best blocks form a 16,384-position pool].  Positions are
+ * the E entries; block i holds entries [block*i, block*i + block) that are
+ * < E (the last block may be short); its score is the highest score among
+ * them.  The pool is the first min(nb, blocks) blocks ordered by (block
+ * score descending, block index ascending) -- the top-k tie rule applied to
+ * blocks -- output ascending by block index, padded with -1.
+ * Pinned: brute force over all block subsets on tiny inputs, hand-built
+ * cases, and the closed forms stated in orc_topk_in_pool. */
+void orc_pool_blocks(const double *scores, int64_t E, int block, int nb, int32_t *pool);
+
+/* Top-k inside a pool [same passage: later Reindex layers score only inside
+ * the pool]: among the entries of the pooled blocks (those < E), order by
+ * (score descending, entry index ascending), take the first min(k, count),
+ * output ascending by entry index, pad with -1.
+ * Pinned: brute force on tiny inputs; when every block is pooled the result
+ * is orc_topk's; with the pool's own scores, distinct scores and k <= nb it
+ * is orc_topk's as well (each of the k best entries lies in a block whose
+ * maximum is among the k best block maxima). */
+void orc_topk_in_pool(const double *scores, int64_t E, const int32_t *pool, int nb, int block,
+                      int k, int32_t *out);
+
+/* Whole-batch forms on a cache, scores as orc_indexer_scores: pool [B][nb];
+ * out [B][k]. */
+void orc_indexer_pool(const orc_cache *c, const uint16_t *q, int heads, const float *head_w,
+                      int block, int nb, int32_t *pool);
+void orc_indexer_topk_in_pool(const orc_cache *c, const uint16_t *q, int heads,
+                              const float *head_w, const int32_t *pool, int nb, int block, int k,
+                              int32_t *out);
+
 /* ---------------- attention ---------------------------------------------- */
 
 /* One joint softmax per query head over the selected compressed entries and

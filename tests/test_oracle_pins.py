@@ -451,6 +451,105 @@ def test_topk_exhaustive_tiny(orc):
             _valid_topk(s, k, orc.topk(s, k))
 
 
+# ---------------------------------------------------------------- candidate pool
+
+def _pool_by_subsets(s, block, nb):
+    """The pool found by trying every set of blocks: the unique set of
+    min(nb, blocks) blocks in which every member beats every non-member
+    on (block maximum, then lower block index)."""
+    import itertools
+    E = len(s)
+    nblk = -(-E // block)
+    bm = [max(s[i * block:(i + 1) * block]) for i in range(nblk)]
+    m = min(nb, nblk)
+    found = []
+    for S in itertools.combinations(range(nblk), m):
+        inside = set(S)
+        if all(bm[i] > bm[j] or (bm[i] == bm[j] and i < j)
+               for i in inside for j in range(nblk) if j not in inside):
+            found.append(list(S))
+    assert len(found) == 1
+    return found[0] + [-1] * (nb - m)
+
+
+def test_pool_blocks_brute_force_tiny(orc):
+    g = np.random.default_rng(21)
+    for trial in range(400):
+        E = int(g.integers(0, 13))
+        block = int(g.integers(1, 4))
+        nb = int(g.integers(1, 6))
+        s = g.integers(0, 3, E).astype(np.float64) if trial % 2 else g.standard_normal(E)
+        assert list(orc.pool_blocks(s, block, nb)) == _pool_by_subsets(list(s), block, nb)
+
+
+def test_pool_blocks_hand_built(orc):
+    # blocks of 8 over 27 entries: maxima 5 (block 0), 9 (block 1), 5 (block 2),
+    # 7 (block 3, the short one: entries 24..26)
+    s = np.zeros(27)
+    s[3], s[12], s[20], s[26] = 5, 9, 5, 7
+    assert list(orc.pool_blocks(s, 8, 2)) == [1, 3]
+    assert list(orc.pool_blocks(s, 8, 3)) == [0, 1, 3]        # tie 5 = 5: block 0 before block 2
+    assert list(orc.pool_blocks(s, 8, 6)) == [0, 1, 2, 3, -1, -1]
+    assert list(orc.pool_blocks(np.zeros(0), 8, 2)) == [-1, -1]
+    # within the pool, selection follows the entry scores, not the block maxima
+    pool = np.array([1, 3], np.int32)
+    assert list(orc.topk_in_pool(s, pool, 8, 3)) == [8, 12, 26]   # 9, 7, then the lowest 0 (entry 8)
+    assert list(orc.topk_in_pool(s, pool, 8, 12)) == list(range(8, 16)) + [24, 25, 26, -1]
+
+
+def test_topk_in_pool_brute_force_tiny(orc):
+    g = np.random.default_rng(22)
+    for trial in range(300):
+        E = int(g.integers(0, 14))
+        block = int(g.integers(1, 4))
+        nb = int(g.integers(1, 5))
+        k = int(g.integers(1, 8))
+        s = g.integers(0, 3, E).astype(np.float64) if trial % 2 else g.standard_normal(E)
+        pool = orc.pool_blocks(s, block, nb)
+        q = g.integers(0, 3, E).astype(np.float64)        # a second query's scores
+        out = orc.topk_in_pool(q, pool, block, k)
+        ent = [j for b in pool if b >= 0 for j in range(b * block, min((b + 1) * block, E))]
+        n = min(k, len(ent))
+        sel = list(out[:n])
+        assert all(x == -1 for x in out[n:]) and sel == sorted(sel) and set(sel) <= set(ent)
+        for i in sel:
+            for j in ent:
+                if j not in sel:
+                    assert q[i] > q[j] or (q[i] == q[j] and i < j)
+
+
+def test_topk_in_pool_closed_forms(orc):
+    g = np.random.default_rng(23)
+    # every block pooled: the pool changes nothing
+    s = g.integers(0, 4, 500).astype(np.float64)
+    pool = orc.pool_blocks(s, 8, 2048)
+    assert list(pool[:63]) == list(range(63)) and np.all(pool[63:] == -1)
+    assert np.array_equal(orc.topk_in_pool(s, pool, 8, 64), orc.topk(s, 64))
+    # the pool's own scores, all distinct, k <= nb: the k best entries lie in
+    # the k best blocks, so the pooled top-k is the top-k
+    for E, nb, k in ((4000, 64, 64), (4003, 100, 37), (20000, 2048, 512)):
+        s = g.permutation(E).astype(np.float64)
+        pool = orc.pool_blocks(s, 8, nb)
+        assert np.array_equal(orc.topk_in_pool(s, pool, 8, k), orc.topk(s, k))
+
+
+def test_pool_on_a_cache_matches_the_score_form(orc):
+    cache = _small_cache(orc, B=2, cap=300)
+    g = np.random.default_rng(24)
+    for b, n in enumerate((300, 131)):
+        keys = _bf16_int(g.integers(-8, 9, (n, 64)))
+        orc.kv_append(cache, np.zeros((n, 576), np.float32), np.array([0] * (b + 1) + [n] * (2 - b), np.int32),
+                      None, keys)
+    q = _bf16_int(g.integers(-8, 9, (2, 4, 64)))
+    q2 = _bf16_int(g.integers(-8, 9, (2, 4, 64)))
+    pool = orc.indexer_pool(cache, q, 8, 16)
+    out = orc.indexer_topk_in_pool(cache, q2, pool, 8, 50)
+    for b, n in enumerate((300, 131)):
+        keys = cache.idx_keys[b, :n]
+        assert np.array_equal(pool[b], orc.pool_blocks(orc.indexer_scores(keys, q[b]), 8, 16))
+        assert np.array_equal(out[b], orc.topk_in_pool(orc.indexer_scores(keys, q2[b]), pool[b], 8, 50))
+
+
 # ---------------------------------------------------------------- attention
 
 def _attn_cache(orc, entries, group=32):
@@ -552,3 +651,34 @@ def test_modes_reindex_and_reuse_reproduce_full(orc):
     assert np.array_equal(outs[2], outs[0]) and np.array_equal(lses[2], lses[0])
     assert not np.array_equal(outs[1], outs[0])
     assert list(cache.n_tokens) == [601, 601]
+
+
+def test_modes_with_candidate_pool(orc):
+    """The layer group with the hierarchical indexer: a pool holding every
+    block changes nothing; a small pool confines the reindex layer's
+    selection to the full layer's pool blocks."""
+    import synth
+    w = synth.scaled(synth.WORKLOADS["tiny_t4096"], batch=2, entries=300, prefill_tokens=None,
+                     entry_law="normal", layers=("full", "reindex", "reuse"))
+    ents = np.concatenate([synth.cache_entries(w, b) for b in range(2)])
+    keys = np.concatenate([synth.cache_idx_keys(w, b) for b in range(2)])
+    st = synth.step_inputs(w)
+    Wc = synth.w_comp(w)
+    res = {}
+    for name, pool in (("none", None), ("all", (8, 2048)), ("small", (8, 6))):
+        cache = orc.Cache.empty(2, 310, 576, 64, 32, 0, 64)
+        orc.kv_append(cache, ents, np.array([0, 300, 600], np.int32), None, keys)
+        rings = [r.copy() for r in st.swa_ring]
+        res[name] = orc.layer_group_decode(cache, w.layers, st.token, st.idx_row, Wc, st.q, st.q_idx,
+                                           rings, st.swa_row, 40, 1 / 24, pool=pool)
+        if name == "small":
+            cand = orc.indexer_pool(cache, st.q_idx[0], 8, 6)
+    for a, b in zip(res["none"][2], res["all"][2]):
+        assert np.array_equal(a, b)
+    assert np.array_equal(res["small"][2][0], res["none"][2][0])          # full layer: unchanged
+    assert not np.array_equal(res["small"][2][1], res["none"][2][1])
+    for b in range(2):
+        allowed = {8 * int(p) + r for p in cand[b] if p >= 0 for r in range(8)}
+        sel = res["small"][2][1][b]
+        assert set(sel[sel >= 0].tolist()) <= allowed and np.sum(sel >= 0) == 40
+
