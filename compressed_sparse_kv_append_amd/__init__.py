@@ -31,10 +31,12 @@ STATUS_BAD_STATE = 4
 MODE_FULL, MODE_REINDEX, MODE_REUSE = 0, 1, 2
 MODES = {"full": MODE_FULL, "reindex": MODE_REINDEX, "reuse": MODE_REUSE}
 KERNEL_APPEND, KERNEL_SWA_APPEND, KERNEL_INDEXER_SCAN, KERNEL_TOPK_SELECT, KERNEL_ATTENTION = 1, 2, 3, 4, 5
-OP_INDEXER_TOPK, OP_SPARSE_ATTN, OP_LAYER_GROUP = 1, 2, 3
+OP_INDEXER_TOPK, OP_SPARSE_ATTN, OP_LAYER_GROUP, OP_INDEXER_POOL, OP_INDEXER_IN_POOL = 1, 2, 3, 4, 5
 
-EXPORTS = ("cskv_kv_append_fp4", "cskv_append_workspace_bytes", "cskv_swa_append", "cskv_indexer_topk", "cskv_sparse_attn_decode",
-           "cskv_layer_group_decode", "cskv_workspace_bytes", "cskv_entry_bytes", "cskv_last_error",
+EXPORTS = ("cskv_kv_append_fp4", "cskv_append_workspace_bytes", "cskv_swa_append", "cskv_indexer_topk",
+           "cskv_indexer_topk_pool", "cskv_indexer_topk_in_pool", "cskv_sparse_attn_decode",
+           "cskv_layer_group_decode", "cskv_layer_group_decode_pooled", "cskv_workspace_bytes",
+           "cskv_workspace_bytes_pool", "cskv_entry_bytes", "cskv_last_error",
            "cskv_timer_enable", "cskv_timer_pause", "cskv_timer_read", "cskv_timer_disable_all")
 
 
@@ -80,16 +82,23 @@ def lib():
                                               vp]
         L.cskv_layer_group_decode.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, C.c_float,
                                               vp, sz, vp]
+        L.cskv_layer_group_decode_pooled.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, C.c_float,
+                                                     i32, i32, vp, sz, vp]
+        L.cskv_indexer_topk_pool.argtypes = [vp, vp, i32, vp, i32, vp, i32, i32, vp, vp, sz, vp]
+        L.cskv_indexer_topk_in_pool.argtypes = [vp, vp, i32, vp, i32, vp, i32, i32, vp, vp, sz, vp]
         L.cskv_workspace_bytes.argtypes = [vp, i32, i32, i32, i32]
         L.cskv_workspace_bytes.restype = sz
+        L.cskv_workspace_bytes_pool.argtypes = [vp, i32, i32, i32, i32, i32, i32]
+        L.cskv_workspace_bytes_pool.restype = sz
         L.cskv_entry_bytes.argtypes = [i32] * 5
         L.cskv_entry_bytes.restype = sz
         L.cskv_last_error.restype = C.c_char_p
         L.cskv_timer_enable.argtypes = [i32, i32]
         L.cskv_timer_pause.argtypes = [i32, i32]
         L.cskv_timer_read.argtypes = [i32, C.POINTER(C.c_double), C.POINTER(C.c_int32)]
-        for f in ("cskv_kv_append_fp4", "cskv_swa_append", "cskv_indexer_topk", "cskv_sparse_attn_decode",
-                  "cskv_layer_group_decode", "cskv_timer_enable", "cskv_timer_pause", "cskv_timer_read",
+        for f in ("cskv_kv_append_fp4", "cskv_swa_append", "cskv_indexer_topk", "cskv_indexer_topk_pool",
+                  "cskv_indexer_topk_in_pool", "cskv_sparse_attn_decode", "cskv_layer_group_decode",
+                  "cskv_layer_group_decode_pooled", "cskv_timer_enable", "cskv_timer_pause", "cskv_timer_read",
                   "cskv_timer_disable_all"):
             getattr(L, f).restype = C.c_int
         _lib = L
@@ -180,9 +189,17 @@ def workspace_bytes(cache: Cache, k: int, op: int = OP_INDEXER_TOPK, n_heads: in
 
 
 def workspace(cache: Cache, k: int, op: int = OP_INDEXER_TOPK, n_heads: int = 0,
-              window: int = 0) -> torch.Tensor:
-    return torch.empty(workspace_bytes(cache, k, op, n_heads, window), dtype=torch.uint8,
-                       device=cache.k_codes.device)
+              window: int = 0, pool=None) -> torch.Tensor:
+    """Device workspace for an operation; pool = (pool_blocks, pool_block) for the
+    hierarchical indexer's operations."""
+    if pool is None:
+        n = workspace_bytes(cache, k, op, n_heads, window)
+    else:
+        d = cache.desc()
+        n = lib().cskv_workspace_bytes_pool(C.byref(d), op, n_heads, k, window, pool[0], pool[1])
+        if n == 0:
+            raise CskvError(EINVAL, lib().cskv_last_error().decode())
+    return torch.empty(int(n), dtype=torch.uint8, device=cache.k_codes.device)
 
 
 def entry_bytes(dim, rope_dim, k_group, v_group, idx_dim) -> int:
@@ -234,6 +251,46 @@ def indexer_topk(cache: Cache, q_idx: torch.Tensor, k: int, head_w: Optional[tor
     return out
 
 
+def indexer_topk_pool(cache: Cache, q_idx: torch.Tensor, k: int, pool_blocks: int, pool_block: int,
+                      head_w: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                      out_pool: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                      stream=None):
+    """indexer_topk plus the hierarchical indexer's candidate pool [B, pool_blocks]."""
+    B, H, Di = q_idx.shape
+    if out is None:
+        out = torch.empty(B, k, dtype=torch.int32, device=q_idx.device)
+    if out_pool is None:
+        out_pool = torch.empty(B, pool_blocks, dtype=torch.int32, device=q_idx.device)
+    if ws is None:
+        ws = workspace(cache, k, OP_INDEXER_POOL, pool=(pool_blocks, pool_block))
+    d = cache.desc()
+    _check(lib().cskv_indexer_topk_pool(
+        C.byref(d), _ptr(q_idx, B16, "q_idx", (cache.batch, H, cache.idx_dim)), H,
+        _ptr(head_w, F32, "head_w", (cache.batch, H)), k, _ptr(out, I32, "out", (cache.batch, k)),
+        pool_blocks, pool_block, _ptr(out_pool, I32, "out_pool", (cache.batch, pool_blocks)),
+        _ptr(ws, U8, "ws"), ws.numel(), _stream(stream)))
+    return out, out_pool
+
+
+def indexer_topk_in_pool(cache: Cache, q_idx: torch.Tensor, k: int, pool: torch.Tensor, pool_block: int,
+                         head_w: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                         ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Top-k of this query's indexer scores among the entries of the pooled blocks."""
+    B, H, Di = q_idx.shape
+    nb = pool.shape[1]
+    if out is None:
+        out = torch.empty(B, k, dtype=torch.int32, device=q_idx.device)
+    if ws is None:
+        ws = workspace(cache, k, OP_INDEXER_IN_POOL, pool=(nb, pool_block))
+    d = cache.desc()
+    _check(lib().cskv_indexer_topk_in_pool(
+        C.byref(d), _ptr(q_idx, B16, "q_idx", (cache.batch, H, cache.idx_dim)), H,
+        _ptr(head_w, F32, "head_w", (cache.batch, H)), k, _ptr(pool, I32, "pool", (cache.batch, nb)),
+        nb, pool_block, _ptr(out, I32, "out", (cache.batch, k)), _ptr(ws, U8, "ws"), ws.numel(),
+        _stream(stream)))
+    return out
+
+
 def sparse_attn_decode(cache: Cache, q: torch.Tensor, idx: torch.Tensor, swa: torch.Tensor,
                        softmax_scale: float, swa_len: Optional[torch.Tensor] = None,
                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
@@ -275,12 +332,14 @@ class Layer:
 def layer_group_decode(cache: Cache, layers: Sequence[Layer], new_tokens: Optional[torch.Tensor],
                        w_comp: Optional[torch.Tensor], new_idx_rows: Optional[torch.Tensor],
                        k: int, window: int, softmax_scale: float, ws: Optional[torch.Tensor] = None,
-                       stream=None) -> None:
+                       stream=None, pool=None) -> None:
+    """One decode step of a layer group; pool = (pool_blocks, pool_block) turns on
+    the hierarchical indexer (cskv_layer_group_decode_pooled)."""
     B = cache.batch
     n_heads = layers[0].q.shape[1]
     n_idx_heads = next((L.q_idx.shape[1] for L in layers if L.q_idx is not None), 1)
     if ws is None:
-        ws = workspace(cache, k, OP_LAYER_GROUP, n_heads, window)
+        ws = workspace(cache, k, OP_LAYER_GROUP, n_heads, window, pool=pool)
     arr = (LayerDesc * len(layers))()
     for i, L in enumerate(layers):
         dv = cache.dim - cache.rope_dim
@@ -293,11 +352,15 @@ def layer_group_decode(cache: Cache, layers: Sequence[Layer], new_tokens: Option
                            _ptr(L.out, F32, "out", (B, n_heads, dv)),
                            _ptr(L.lse, F32, "lse", (B, n_heads)))
     d = cache.desc()
-    _check(lib().cskv_layer_group_decode(
-        C.byref(d), arr, len(layers), _ptr(new_tokens, F32, "new_tokens", (B, cache.dim)),
-        _ptr(w_comp, F32, "w_comp", (cache.dim, 2 * cache.dim)),
-        _ptr(new_idx_rows, B16, "new_idx_rows", (B, cache.idx_dim)), n_idx_heads, n_heads, k,
-        window, float(softmax_scale), _ptr(ws, U8, "ws"), ws.numel(), _stream(stream)))
+    args = (C.byref(d), arr, len(layers), _ptr(new_tokens, F32, "new_tokens", (B, cache.dim)),
+            _ptr(w_comp, F32, "w_comp", (cache.dim, 2 * cache.dim)),
+            _ptr(new_idx_rows, B16, "new_idx_rows", (B, cache.idx_dim)), n_idx_heads, n_heads, k,
+            window, float(softmax_scale))
+    if pool is None:
+        _check(lib().cskv_layer_group_decode(*args, _ptr(ws, U8, "ws"), ws.numel(), _stream(stream)))
+    else:
+        _check(lib().cskv_layer_group_decode_pooled(*args, pool[0], pool[1], _ptr(ws, U8, "ws"), ws.numel(),
+                                                    _stream(stream)))
 
 
 # ---------------------------------------------------------------- timers

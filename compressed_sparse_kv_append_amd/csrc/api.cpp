@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -113,6 +114,38 @@ int attn_args(const cskv_cache *c, const float *q, int32_t heads, const int32_t 
     return CSKV_OK;
 }
 
+int pool_args(const cskv_cache *c, int32_t k, int32_t pool_blocks, int32_t pool_block)
+{
+    REQUIRE(pool_block == 2 || pool_block == 4 || pool_block == 8 || pool_block == 16, CSKV_EUNSUPPORTED,
+            "pool_block %d: 2, 4, 8 or 16", pool_block);
+    REQUIRE(pool_blocks >= 1 && pool_blocks <= 2048, CSKV_EUNSUPPORTED, "pool_blocks %d out of [1, 2048]",
+            pool_blocks);
+    REQUIRE((int64_t)pool_blocks * pool_block >= (int64_t)k + pool_block, CSKV_EUNSUPPORTED,
+            "pool of %d x %d positions too small for k = %d", pool_blocks, pool_block, k);
+    (void)c;
+    return CSKV_OK;
+}
+
+// Layer-group workspace: the candidate pool (when used) at offset 0, then a
+// region shared in turn by the append, each layer's top-k and attention.
+size_t group_pool_bytes(const cskv_cache &c, int pool_blocks)
+{
+    return pool_blocks > 0 ? ((size_t)c.batch * pool_blocks * sizeof(int32_t) + 255) / 256 * 256 : 0;
+}
+
+size_t group_ws_bytes(const cskv_cache &c, int heads, int k, int window, int pool_blocks, int pool_block)
+{
+    size_t need = cskv::topk_workspace(c, k).total;
+    if (pool_blocks > 0) {
+        const cskv::PoolWorkspace pw = cskv::pool_workspace(c, k, pool_blocks, pool_block);
+        need = std::max(need, std::max(pw.build_total, pw.inpool_total));
+    }
+    need = std::max(need, cskv::attn_plan(c, heads, k, window).ws_bytes);
+    need = std::max(need, cskv::append_workspace_bytes(c.batch));   // one new token per sequence
+    need = std::max(need, (size_t)256);
+    return group_pool_bytes(c, pool_blocks) + need;
+}
+
 // ---------------------------------------------------------------- timers
 
 struct Timer {
@@ -182,12 +215,30 @@ size_t cskv_workspace_bytes(const cskv_cache *cache, int32_t op, int32_t n_heads
         fail(CSKV_EINVAL, "unknown workspace op %d", op);
         return 0;
     }
-    size_t need = topk > attn ? topk : attn;
-    if (op == CSKV_OP_LAYER_GROUP) {
-        const size_t app = cskv::append_workspace_bytes(cache->batch);   // one new token per sequence
-        need = need > app ? need : app;
-    }
+    if (op == CSKV_OP_LAYER_GROUP) return group_ws_bytes(*cache, n_heads, k, window, 0, 0);
+    const size_t need = topk > attn ? topk : attn;
     return need > 256 ? need : 256;
+}
+
+size_t cskv_workspace_bytes_pool(const cskv_cache *cache, int32_t op, int32_t n_heads, int32_t k,
+                                 int32_t window, int32_t pool_blocks, int32_t pool_block)
+{
+    if (op == CSKV_OP_INDEXER_POOL || op == CSKV_OP_INDEXER_IN_POOL) {
+        if (check_cache(cache) != CSKV_OK) return 0;
+        if (k < 1 || k > 2048) {
+            fail(CSKV_EUNSUPPORTED, "k %d out of [1, 2048]", k);
+            return 0;
+        }
+        if (pool_args(cache, k, pool_blocks, pool_block) != CSKV_OK) return 0;
+        const cskv::PoolWorkspace pw = cskv::pool_workspace(*cache, k, pool_blocks, pool_block);
+        return std::max(op == CSKV_OP_INDEXER_POOL ? pw.build_total : pw.inpool_total, (size_t)256);
+    }
+    if (op == CSKV_OP_LAYER_GROUP && pool_blocks != 0) {
+        if (cskv_workspace_bytes(cache, op, n_heads, k, window) == 0) return 0;
+        if (pool_args(cache, k, pool_blocks, pool_block) != CSKV_OK) return 0;
+        return group_ws_bytes(*cache, n_heads, k, window, pool_blocks, pool_block);
+    }
+    return cskv_workspace_bytes(cache, op, n_heads, k, window);
 }
 
 size_t cskv_append_workspace_bytes(int32_t total_new, const float *w_comp)
@@ -242,6 +293,43 @@ int cskv_indexer_topk(const cskv_cache *cache, const uint16_t *q_idx, int32_t n_
     return e == hipSuccess ? CSKV_OK : hip_fail(e, "indexer_topk launch");
 }
 
+int cskv_indexer_topk_pool(const cskv_cache *cache, const uint16_t *q_idx, int32_t n_idx_heads,
+                           const float *head_w, int32_t k, int32_t *out_idx, int32_t pool_blocks,
+                           int32_t pool_block, int32_t *out_pool, void *ws, size_t ws_bytes,
+                           hipStream_t stream)
+{
+    int rc = check_cache(cache);
+    if (rc) return rc;
+    if ((rc = topk_args(cache, q_idx, n_idx_heads, k, out_idx, ws, ws_bytes))) return rc;
+    if ((rc = pool_args(cache, k, pool_blocks, pool_block))) return rc;
+    REQUIRE(out_pool, CSKV_EINVAL, "out_pool is NULL");
+    const size_t need = cskv::pool_workspace(*cache, k, pool_blocks, pool_block).build_total;
+    REQUIRE(ws_bytes >= need, CSKV_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    const cskv::PoolBuild pb{pool_blocks, pool_block, out_pool};
+    hipError_t e = cskv::launch_indexer_topk(*cache, q_idx, n_idx_heads, head_w, k, out_idx, ws, stream, &pb);
+    return e == hipSuccess ? CSKV_OK : hip_fail(e, "indexer_topk_pool launch");
+}
+
+int cskv_indexer_topk_in_pool(const cskv_cache *cache, const uint16_t *q_idx, int32_t n_idx_heads,
+                              const float *head_w, int32_t k, const int32_t *pool, int32_t pool_blocks,
+                              int32_t pool_block, int32_t *out_idx, void *ws, size_t ws_bytes,
+                              hipStream_t stream)
+{
+    int rc = check_cache(cache);
+    if (rc) return rc;
+    if ((rc = pool_args(cache, k, pool_blocks, pool_block))) return rc;
+    REQUIRE(q_idx && aligned(q_idx, 16), CSKV_EINVAL, "q_idx NULL or not 16-byte aligned");
+    REQUIRE(n_idx_heads >= 1 && n_idx_heads <= 64, CSKV_EUNSUPPORTED, "n_idx_heads %d out of [1, 64]",
+            n_idx_heads);
+    REQUIRE(out_idx && pool && aligned(pool, 4), CSKV_EINVAL, "out_idx or pool is NULL");
+    const size_t need = cskv::pool_workspace(*cache, k, pool_blocks, pool_block).inpool_total;
+    REQUIRE(ws && aligned(ws, 256), CSKV_EWORKSPACE, "workspace NULL or not 256-byte aligned");
+    REQUIRE(ws_bytes >= need, CSKV_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    hipError_t e = cskv::launch_indexer_topk_in_pool(*cache, q_idx, n_idx_heads, head_w, k, pool, pool_blocks,
+                                                     pool_block, out_idx, ws, stream);
+    return e == hipSuccess ? CSKV_OK : hip_fail(e, "indexer_topk_in_pool launch");
+}
+
 int cskv_sparse_attn_decode(const cskv_cache *cache, const float *q, int32_t n_heads,
                             const int32_t *idx, int32_t k, const uint16_t *swa, int32_t window,
                             const int32_t *swa_len, float softmax_scale, float *out, float *lse,
@@ -255,17 +343,26 @@ int cskv_sparse_attn_decode(const cskv_cache *cache, const float *q, int32_t n_h
     return e == hipSuccess ? CSKV_OK : hip_fail(e, "sparse_attn_decode launch");
 }
 
-int cskv_layer_group_decode(const cskv_cache *cache, const cskv_layer *layers, int32_t n_layers,
-                            const float *new_tokens, const float *w_comp,
-                            const uint16_t *new_idx_rows, int32_t n_idx_heads, int32_t n_heads,
-                            int32_t k, int32_t window, float softmax_scale, void *ws,
-                            size_t ws_bytes, hipStream_t stream)
+static int layer_group(const cskv_cache *cache, const cskv_layer *layers, int32_t n_layers,
+                       const float *new_tokens, const float *w_comp, const uint16_t *new_idx_rows,
+                       int32_t n_idx_heads, int32_t n_heads, int32_t k, int32_t window,
+                       float softmax_scale, int32_t pool_blocks, int32_t pool_block, void *ws,
+                       size_t ws_bytes, hipStream_t stream)
 {
     int rc = check_cache(cache);
     if (rc) return rc;
     REQUIRE(layers && n_layers >= 1 && n_layers <= 256, CSKV_EINVAL, "need 1..256 layers");
     REQUIRE(!new_tokens || (aligned(new_tokens, 16) && new_idx_rows), CSKV_EINVAL,
             "new_tokens must be 16-byte aligned and come with new_idx_rows");
+    if (pool_blocks != 0 && (rc = pool_args(cache, k, pool_blocks, pool_block))) return rc;
+    // the pool (if any) at the start of ws; each step below uses what follows
+    REQUIRE(ws && aligned(ws, 256), CSKV_EWORKSPACE, "workspace NULL or not 256-byte aligned");
+    const size_t need = group_ws_bytes(*cache, n_heads, k, window, pool_blocks, pool_block);
+    REQUIRE(ws_bytes >= need, CSKV_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    const size_t pool_bytes = group_pool_bytes(*cache, pool_blocks);
+    int32_t *pool = pool_blocks > 0 ? static_cast<int32_t *>(ws) : nullptr;
+    void *work = static_cast<char *>(ws) + pool_bytes;
+    const size_t work_bytes = ws_bytes - pool_bytes;
     // check every layer before enqueueing anything [P2 四、"CSA2：三种模式"]
     bool have_index = false;
     for (int i = 0; i < n_layers; ++i) {
@@ -273,18 +370,18 @@ int cskv_layer_group_decode(const cskv_cache *cache, const cskv_layer *layers, i
         REQUIRE(L.mode == CSKV_MODE_FULL || L.mode == CSKV_MODE_REINDEX || L.mode == CSKV_MODE_REUSE,
                 CSKV_EINVAL, "layer %d: unknown mode %d", i, L.mode);
         if ((rc = attn_args(cache, L.q, n_heads, L.idx, L.mode != CSKV_MODE_REUSE, k, L.swa, window, L.out,
-                            L.lse, ws, ws_bytes)))
+                            L.lse, work, work_bytes)))
             return fail(rc, "layer %d: %s", i, g_error.c_str());
         REQUIRE(!L.swa_row || aligned(L.swa_row, 16), CSKV_EINVAL, "layer %d: swa_row not 16-byte aligned", i);
         if (L.mode == CSKV_MODE_REUSE) {
             REQUIRE(have_index, CSKV_EINVAL, "layer %d: REUSE with no FULL/REINDEX layer before it", i);
         } else {
-            if ((rc = topk_args(cache, L.q_idx, n_idx_heads, k, L.idx, ws, ws_bytes)))
+            if ((rc = topk_args(cache, L.q_idx, n_idx_heads, k, L.idx, work, work_bytes)))
                 return fail(rc, "layer %d: %s", i, g_error.c_str());
             have_index = true;
         }
     }
-    bool appended = false;
+    bool appended = false, pooled = false;
     const int32_t *last_idx = nullptr;
     hipError_t e;
     for (int i = 0; i < n_layers; ++i) {
@@ -292,7 +389,7 @@ int cskv_layer_group_decode(const cskv_cache *cache, const cskv_layer *layers, i
         bool window_done = false;
         if (L.mode == CSKV_MODE_FULL && new_tokens && !appended) {
             // the append also writes this layer's window row
-            e = cskv::launch_kv_append(*cache, new_tokens, nullptr, cache->batch, w_comp, new_idx_rows, ws,
+            e = cskv::launch_kv_append(*cache, new_tokens, nullptr, cache->batch, w_comp, new_idx_rows, work,
                                        stream, L.swa_row ? L.swa : nullptr, L.swa_row, window);
             if (e != hipSuccess) return hip_fail(e, "layer group: append");
             appended = true;
@@ -303,16 +400,46 @@ int cskv_layer_group_decode(const cskv_cache *cache, const cskv_layer *layers, i
                                         cache->batch, cache->n_tokens, stream);
             if (e != hipSuccess) return hip_fail(e, "layer group: window append");
         }
-        if (L.mode != CSKV_MODE_REUSE) {
-            e = cskv::launch_indexer_topk(*cache, L.q_idx, n_idx_heads, L.head_w, k, L.idx, ws, stream);
+        if (L.mode == CSKV_MODE_REINDEX && pooled) {
+            // hierarchical indexer: select inside the first FULL layer's pool
+            e = cskv::launch_indexer_topk_in_pool(*cache, L.q_idx, n_idx_heads, L.head_w, k, pool, pool_blocks,
+                                                  pool_block, L.idx, work, stream);
+            if (e != hipSuccess) return hip_fail(e, "layer group: pooled indexer");
+            last_idx = L.idx;
+        } else if (L.mode != CSKV_MODE_REUSE) {
+            const bool build = pool && L.mode == CSKV_MODE_FULL && !pooled;
+            const cskv::PoolBuild pb{pool_blocks, pool_block, pool};
+            e = cskv::launch_indexer_topk(*cache, L.q_idx, n_idx_heads, L.head_w, k, L.idx, work, stream,
+                                          build ? &pb : nullptr);
             if (e != hipSuccess) return hip_fail(e, "layer group: indexer");
+            pooled = pooled || build;
             last_idx = L.idx;
         }
         e = cskv::launch_sparse_attn(*cache, L.q, n_heads, last_idx, k, L.swa, window, nullptr,
-                                     softmax_scale, L.out, L.lse, ws, stream);
+                                     softmax_scale, L.out, L.lse, work, stream);
         if (e != hipSuccess) return hip_fail(e, "layer group: attention");
     }
     return CSKV_OK;
+}
+
+int cskv_layer_group_decode(const cskv_cache *cache, const cskv_layer *layers, int32_t n_layers,
+                            const float *new_tokens, const float *w_comp,
+                            const uint16_t *new_idx_rows, int32_t n_idx_heads, int32_t n_heads,
+                            int32_t k, int32_t window, float softmax_scale, void *ws,
+                            size_t ws_bytes, hipStream_t stream)
+{
+    return layer_group(cache, layers, n_layers, new_tokens, w_comp, new_idx_rows, n_idx_heads, n_heads, k,
+                       window, softmax_scale, 0, 0, ws, ws_bytes, stream);
+}
+
+int cskv_layer_group_decode_pooled(const cskv_cache *cache, const cskv_layer *layers,
+                                   int32_t n_layers, const float *new_tokens, const float *w_comp,
+                                   const uint16_t *new_idx_rows, int32_t n_idx_heads, int32_t n_heads,
+                                   int32_t k, int32_t window, float softmax_scale, int32_t pool_blocks,
+                                   int32_t pool_block, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return layer_group(cache, layers, n_layers, new_tokens, w_comp, new_idx_rows, n_idx_heads, n_heads, k,
+                       window, softmax_scale, pool_blocks, pool_block, ws, ws_bytes, stream);
 }
 
 int cskv_timer_enable(int32_t kind, int32_t max_launches)

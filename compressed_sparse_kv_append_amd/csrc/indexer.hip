@@ -37,6 +37,20 @@ TopkWorkspace topk_workspace(const cskv_cache &c, int k)
     return w;
 }
 
+PoolWorkspace pool_workspace(const cskv_cache &c, int k, int pool_blocks, int block)
+{
+    PoolWorkspace w;
+    const size_t items = ((size_t)c.capacity + block - 1) / block;
+    w.bkey_stride = (items + 63) / 64 * 64;
+    w.bslices = (int)((items + kSliceKeys - 1) / kSliceKeys);
+    w.bcand_stride = ((size_t)w.bslices * pool_blocks + 1) & ~(size_t)1;
+    w.bkeys_off = topk_workspace(c, k).total;
+    w.bcand_off = align_up(w.bkeys_off + sizeof(uint32_t) * w.bkey_stride * c.batch, 256);
+    w.build_total = align_up(w.bcand_off + (w.bslices > 1 ? sizeof(uint2) * w.bcand_stride * c.batch : 0), 256);
+    w.inpool_total = align_up(sizeof(uint2) * (size_t)pool_blocks * block * c.batch, 256);
+    return w;
+}
+
 namespace {
 
 // ---------------------------------------------------------------- select
@@ -70,7 +84,14 @@ struct SelectArgs {
     int32_t *out;           // [B][k]
     int capacity, k, slices;
     size_t key_stride, cand_stride;
+    int group;              // entries per item: a sequence of E entries has ceil(E / group) items
 };
+
+// Items of sequence b: its entries, or its blocks of `group` entries.
+__device__ __forceinline__ int64_t items_of(const SelectArgs &a, int b)
+{
+    return (entries_of(a.n_tokens, b, a.capacity) + a.group - 1) / a.group;
+}
 
 template <int THREADS>
 struct SelectSmem {
@@ -338,7 +359,7 @@ __global__ __launch_bounds__(kSliceThreads) void topk_slice_kernel(SelectArgs a)
 {
     __shared__ SelectSmem<kSliceThreads> sm;
     const int b = blockIdx.y, s = blockIdx.x;
-    const int64_t E = entries_of(a.n_tokens, b, a.capacity);
+    const int64_t E = items_of(a, b);
     if (E <= a.k || E <= kSliceKeys) return;         // the merge reads the keys directly
     uint2 *out = a.cand + (size_t)b * a.cand_stride + (size_t)s * a.k;
     const int64_t first = (int64_t)s * kSliceKeys;
@@ -360,7 +381,7 @@ __global__ __launch_bounds__(kSliceThreads) void topk_select_kernel(SelectArgs a
 {
     __shared__ SelectSmem<kSliceThreads> sm;
     const int b = blockIdx.x;
-    const int64_t E = entries_of(a.n_tokens, b, a.capacity);
+    const int64_t E = items_of(a, b);
     int32_t *out = a.out + (size_t)b * a.k;
     if (E <= a.k) {
         for (int i = threadIdx.x; i < a.k; i += kSliceThreads) out[i] = i < E ? i : -1;
@@ -377,7 +398,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(SelectArgs a)
 {
     __shared__ SelectSmem<kMergeThreads> sm;
     const int b = blockIdx.x;
-    const int64_t E = entries_of(a.n_tokens, b, a.capacity);
+    const int64_t E = items_of(a, b);
     int32_t *out = a.out + (size_t)b * a.k;
     if (E <= a.k) {
         for (int i = threadIdx.x; i < a.k; i += kMergeThreads) out[i] = i < E ? i : -1;
@@ -399,28 +420,78 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(SelectArgs a)
         select_topk<true, false, kMergeThreads, kMergePer>(sm, it, a.k, out, nullptr);
 }
 
+// Top-k among the pooled entries of sequence b, from the pooled scan's
+// (key, entry) pairs in pool order (ascending entries; key 0 = no entry).
+// A sequence of at most k entries has them all in the pool.
+__global__ __launch_bounds__(kMergeThreads) void topk_pool_select_kernel(SelectArgs a)
+{
+    __shared__ SelectSmem<kMergeThreads> sm;
+    const int b = blockIdx.x;
+    const int64_t E = entries_of(a.n_tokens, b, a.capacity);
+    int32_t *out = a.out + (size_t)b * a.k;
+    if (E <= a.k) {
+        for (int i = threadIdx.x; i < a.k; i += kMergeThreads) out[i] = i < E ? i : -1;
+        return;
+    }
+    Items it{nullptr, a.cand + (size_t)b * a.cand_stride, (int64_t)a.cand_stride, 0};
+    if (it.n <= kMergeThreads * kMergePerSmall)
+        select_topk<true, false, kMergeThreads, kMergePerSmall>(sm, it, a.k, out, nullptr);
+    else
+        select_topk<true, false, kMergeThreads, kMergePer>(sm, it, a.k, out, nullptr);
+}
+
+// Select (slices + merge, or one select) of the k best items per sequence.
+void launch_select(const SelectArgs &se, int batch, hipStream_t s, const TimedLaunch &tk)
+{
+    if (se.slices > 1) {
+        launch_kernel(topk_slice_kernel, dim3((unsigned)se.slices, (unsigned)batch), dim3(kSliceThreads), s,
+                      tk.start, nullptr, se);
+        launch_kernel(topk_merge_kernel, dim3((unsigned)batch), dim3(kMergeThreads), s, nullptr, tk.stop, se);
+    } else {
+        launch_kernel(topk_select_kernel, dim3((unsigned)batch), dim3(kSliceThreads), s, tk.start, tk.stop, se);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_indexer_topk(const cskv_cache &c, const uint16_t *q_idx, int heads,
                                const float *head_w, int k, int32_t *out_idx, void *ws,
-                               hipStream_t s)
+                               hipStream_t s, const PoolBuild *pool)
 {
     const TopkWorkspace lay = topk_workspace(c, k);
     uint32_t *keys = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + lay.keys_off);
     uint2 *cand = reinterpret_cast<uint2 *>(static_cast<char *>(ws) + lay.cand_off);
-
-    launch_indexer_scan(c, q_idx, heads, head_w, keys, s);
-
-    const int slices = topk_slices(c);
-    SelectArgs se{keys, cand, c.n_tokens, out_idx, c.capacity, k, slices, score_key_stride(c), cand_stride(c, k)};
-    const TimedLaunch tk = timer_take(CSKV_KERNEL_TOPK_SELECT);
-    if (slices > 1) {
-        launch_kernel(topk_slice_kernel, dim3((unsigned)slices, (unsigned)c.batch), dim3(kSliceThreads), s,
-                      tk.start, nullptr, se);
-        launch_kernel(topk_merge_kernel, dim3((unsigned)c.batch), dim3(kMergeThreads), s, nullptr, tk.stop, se);
-    } else {
-        launch_kernel(topk_select_kernel, dim3((unsigned)c.batch), dim3(kSliceThreads), s, tk.start, tk.stop, se);
+    uint32_t *bkeys = nullptr;
+    PoolWorkspace pw{};
+    if (pool) {
+        pw = pool_workspace(c, k, pool->blocks, pool->block);
+        bkeys = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + pw.bkeys_off);
     }
+
+    launch_indexer_scan(c, q_idx, heads, head_w, keys, s, bkeys, pw.bkey_stride, pool ? pool->block : 1);
+
+    const SelectArgs se{keys, cand, c.n_tokens, out_idx, c.capacity, k, topk_slices(c), score_key_stride(c),
+                        cand_stride(c, k), 1};
+    launch_select(se, c.batch, s, timer_take(CSKV_KERNEL_TOPK_SELECT));
+    if (pool) {
+        // the pool: the best pool->blocks blocks by their largest key
+        uint2 *bcand = reinterpret_cast<uint2 *>(static_cast<char *>(ws) + pw.bcand_off);
+        const SelectArgs sb{bkeys, bcand, c.n_tokens, pool->out, c.capacity, pool->blocks, pw.bslices,
+                            pw.bkey_stride, pw.bcand_stride, pool->block};
+        launch_select(sb, c.batch, s, TimedLaunch{});
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_indexer_topk_in_pool(const cskv_cache &c, const uint16_t *q_idx, int heads,
+                                       const float *head_w, int k, const int32_t *pool, int pool_blocks,
+                                       int block, int32_t *out_idx, void *ws, hipStream_t s)
+{
+    uint2 *pairs = static_cast<uint2 *>(ws);
+    launch_pool_scan(c, q_idx, heads, head_w, pool, pool_blocks, block, pairs, s);
+    const SelectArgs se{nullptr, pairs, c.n_tokens, out_idx, c.capacity, k, 1, 0,
+                        (size_t)pool_blocks * block, 1};
+    launch_kernel(topk_pool_select_kernel, dim3((unsigned)c.batch), dim3(kMergeThreads), s, nullptr, nullptr, se);
     return hipGetLastError();
 }
 

@@ -36,12 +36,40 @@ hipError_t launch_swa_append(uint16_t *ring, int batch, int window, int dim, con
                              const int32_t *cu_new, int total_new, const int32_t *end_pos,
                              hipStream_t s);
 // Indexer scan (scan.hip): one score key per valid entry into keys
-// [batch][score_key_stride].
+// [batch][score_key_stride]; with block_keys, also the largest key of each
+// block of `block` entries (block divides 16) into block_keys
+// [batch][block_stride].
 void launch_indexer_scan(const cskv_cache &c, const uint16_t *q_idx, int heads, const float *head_w,
-                         uint32_t *keys, hipStream_t s);
+                         uint32_t *keys, hipStream_t s, uint32_t *block_keys = nullptr,
+                         size_t block_stride = 0, int block = 1);
+// Pooled scan (scan.hip): (score key, entry) pairs of the entries of the
+// pooled blocks, pairs [batch][pool_blocks * block] in pool order; key 0 and
+// entry ~0 where a position holds no entry.
+void launch_pool_scan(const cskv_cache &c, const uint16_t *q_idx, int heads, const float *head_w,
+                      const int32_t *pool, int pool_blocks, int block, uint2 *pairs, hipStream_t s);
+// Candidate pool of the hierarchical indexer, built from the same scan as a
+// layer's top-k: the best `blocks` blocks of `block` entries by their best
+// score, ascending block indices into out [batch][blocks], -1 padded.
+struct PoolBuild {
+    int blocks, block;
+    int32_t *out;
+};
+// Workspace of the pool: block keys and the block select's candidate lists
+// after the top-k's own region (build_total in all), or the pooled scan's
+// (key, entry) pairs from offset 0 (inpool_total).
+struct PoolWorkspace {
+    size_t bkeys_off, bkey_stride, bcand_off, bcand_stride, build_total, inpool_total;
+    int bslices;
+};
+PoolWorkspace pool_workspace(const cskv_cache &c, int k, int pool_blocks, int block);
 hipError_t launch_indexer_topk(const cskv_cache &c, const uint16_t *q_idx, int heads,
                                const float *head_w, int k, int32_t *out_idx, void *ws,
-                               hipStream_t s);
+                               hipStream_t s, const PoolBuild *pool = nullptr);
+// Top-k among the entries of the pooled blocks (a later layer of the
+// hierarchical indexer); ws holds pool_workspace().inpool_total bytes.
+hipError_t launch_indexer_topk_in_pool(const cskv_cache &c, const uint16_t *q_idx, int heads,
+                                       const float *head_w, int k, const int32_t *pool, int pool_blocks,
+                                       int block, int32_t *out_idx, void *ws, hipStream_t s);
 // Split of the keys of one (sequence, head group) over blocks: selected
 // entries in chunks of 128, window rows in chunks of 64.  Split i takes entry
 // chunks [i per_sparse, (i + 1) per_sparse) and window chunks

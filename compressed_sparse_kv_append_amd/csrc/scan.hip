@@ -11,6 +11,13 @@
 // registers.  One round of blocks covers the chip.  The only output is one
 // order-preserving uint32 key per entry, which the top-k select consumes.
 //
+// Hierarchical indexer [P2 "层级稀疏索引器：后面的层只在候选池里找"]: the
+// scan of the layer that builds the candidate pool also writes, per block of
+// `block` entries, the largest key of the block (the key order is the score
+// order).  The pooled scan of a later layer reads only the rows of the
+// pooled blocks -- a block's rows are contiguous -- and writes (key, entry)
+// pairs in pool order, which is ascending entry order.
+//
 // Sources cited as [P2]:
 //   P2  "DeepSeek V1 到 V4.1-Flash，单 token 的 global KV 如何从 389,000 B 压缩到 890 B的？"
 #include "device.hpp"
@@ -30,9 +37,18 @@ struct ScanArgs {
     const int32_t *n_tokens;
     const uint16_t *q;         // [B][H][Di]
     const float *head_w;       // [B][H] or null
-    uint32_t *out_keys;        // [B][key_stride]
+    uint32_t *out_keys;        // [B][key_stride] (full scan)
     int capacity, heads, chunk;
     size_t key_stride;
+    // full scan: per-block maximum keys [B][block_stride], or null
+    uint32_t *block_keys;
+    size_t block_stride;
+    int block;                 // entries per pool block (divides 16)
+    // pooled scan: pool [B][pool_blocks] ascending block indices (-1 unused);
+    // output pairs [B][pool_blocks * block] (key 0 = no entry)
+    const int32_t *pool;
+    int pool_blocks;
+    uint2 *out_pairs;
 };
 
 typedef __attribute__((address_space(1))) void global_void_t;
@@ -44,9 +60,12 @@ constexpr int waitcnt_vm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (7
 constexpr int kWaitLgkm0 = 0xF | (3 << 14) | (7 << 4);
 constexpr int kNonTemporal = 2;     // cache policy of the streaming loads
 
-// One block: a run of `chunk` entries of one sequence; wave w takes 16-key
-// tiles w, w + 4, ...  MT: 16-head row tiles of the query (1..4).
-template <int DI, int MT>
+constexpr int kPoolChunkMax = 4096;   // pool positions per block of the pooled scan
+
+// One block: a run of `chunk` entries of one sequence (POOL: of pool
+// positions); wave w takes 16-key tiles w, w + 4, ...  MT: 16-head row tiles
+// of the query (1..4).
+template <int DI, int MT, bool POOL>
 __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
 {
     constexpr int kSteps = DI / 32;            // MFMA contraction steps per key
@@ -55,14 +74,29 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
     constexpr int kTileBytes = 16 * kRowBytes;
     constexpr int kInst = kTileBytes / 1024;   // loads per tile (64 lanes x 16 B)
     __shared__ __attribute__((aligned(16))) uint8_t ring[kScanWaves][kRing][kTileBytes];
+    __shared__ int32_t pool_rows[POOL ? kPoolChunkMax : 1];   // entry of each position of the run
 
     const int b = blockIdx.y;
     const int64_t E = entries_of(a.n_tokens, b, a.capacity);
+    // the positions scanned: entries, or pool positions
+    const int64_t N = POOL ? (E > 0 ? (int64_t)a.pool_blocks * a.block : 0) : E;
     const int64_t e_begin = (int64_t)blockIdx.x * a.chunk;
-    if (e_begin >= E) return;
-    const int64_t e_end = E < e_begin + a.chunk ? E : e_begin + a.chunk;
+    if (e_begin >= N) return;
+    const int64_t e_end = N < e_begin + a.chunk ? N : e_begin + a.chunk;
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     const int col = lane & 15, grp = lane >> 4;
+    if constexpr (POOL) {
+        // entry of every position of this block's run (-1: none); rows
+        // without an entry read row 0 and are dropped
+        const int32_t *pl = a.pool + (size_t)b * a.pool_blocks;
+        for (int i = threadIdx.x; i < e_end - e_begin; i += kScanThreads) {
+            const int64_t p = e_begin + i;
+            const int32_t blk = pl[p / a.block];
+            const int64_t e = blk >= 0 ? (int64_t)blk * a.block + p % a.block : -1;
+            pool_rows[i] = e < E ? (int32_t)e : -1;
+        }
+        __syncthreads();
+    }
 
     const int n_tiles = (int)((e_end - e_begin + 15) / 16);
     const int my_n = n_tiles > w ? (n_tiles - w + kScanWaves - 1) / kScanWaves : 0;
@@ -85,6 +119,10 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
             const int u = 64 * s + lane, r = u / kChunks, p = u % kChunks, c = p ^ (r % kChunks);
             int64_t e = t0 + r;
             if (tail) e = e < e_end ? e : e_end - 1;
+            if constexpr (POOL) {
+                const int32_t pe = pool_rows[e - e_begin];
+                e = pe >= 0 ? pe : 0;
+            }
             __builtin_amdgcn_global_load_lds((global_void_t *)(kb + (size_t)e * kRowBytes + 16 * c),
                                              (lds_void_t *)(slot + 1024 * s), 16, 0, kNonTemporal);
         }
@@ -142,7 +180,24 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
         part += __shfl_xor(part, 16);
         part += __shfl_xor(part, 32);
         const int64_t e = e_begin + (int64_t)(w + kScanWaves * i) * 16 + lane;
-        if (lane < 16 && e < e_end) ok[e] = score_key(part);
+        if constexpr (POOL) {
+            if (lane < 16 && e < e_end) {
+                const int32_t pe = pool_rows[e - e_begin];
+                a.out_pairs[(size_t)b * a.pool_blocks * a.block + e] =
+                    pe >= 0 ? make_uint2(score_key(part), (uint32_t)pe) : make_uint2(0u, 0xFFFFFFFFu);
+            }
+        } else {
+            const uint32_t key = score_key(part);
+            if (lane < 16 && e < e_end) ok[e] = key;
+            if (a.block_keys) {
+                // largest key of each pool block in the tile (tiles start on
+                // block boundaries; entries past the end count as key 0)
+                uint32_t m = e < e_end ? key : 0u;
+                for (int off = 1; off < a.block; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+                if (lane < 16 && e < e_end && lane % a.block == 0)
+                    a.block_keys[(size_t)b * a.block_stride + e / a.block] = m;
+            }
+        }
     }
     // no LDS write may land after the block's LDS is handed to another block
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -150,11 +205,11 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
 
 }  // namespace
 
-void launch_indexer_scan(const cskv_cache &c, const uint16_t *q_idx, int heads, const float *head_w,
-                         uint32_t *keys, hipStream_t s)
+// Blocks per sequence and positions per block for n positions per sequence:
+// one round of blocks that fills every CU, runs a multiple of 64 (and at
+// most `cap`).
+static int scan_chunk(int batch, size_t n, size_t cap)
 {
-    // One round of blocks that fills every CU: entries per block chosen so
-    // that batch x blocks-per-sequence <= resident slots, a multiple of 64.
     static int cus = 0;
     if (cus == 0) {
         int dev = 0;
@@ -162,26 +217,50 @@ void launch_indexer_scan(const cskv_cache &c, const uint16_t *q_idx, int heads, 
             cus = 256;
     }
     const int slots = kScanBlocksPerCU * cus;
-    const int per_seq = c.batch >= slots ? 1 : slots / c.batch;
-    size_t chunk = ((size_t)c.capacity + per_seq - 1) / per_seq;
+    const int per_seq = batch >= slots ? 1 : slots / batch;
+    size_t chunk = (n + per_seq - 1) / per_seq;
     chunk = (chunk + 63) / 64 * 64;
-    ScanArgs sa{c.idx_keys, c.n_tokens, q_idx, head_w, keys, c.capacity, heads, (int)chunk,
-                score_key_stride(c)};
-    dim3 grid((unsigned)(((size_t)c.capacity + chunk - 1) / chunk), (unsigned)c.batch);
+    return (int)(chunk < cap ? chunk : cap);
+}
+
+template <bool POOL>
+static void scan_dispatch(const cskv_cache &c, int heads, const ScanArgs &sa, dim3 grid, hipStream_t s)
+{
     const int mt = (heads + 15) / 16;
     const TimedLaunch ts = timer_take(CSKV_KERNEL_INDEXER_SCAN);
     auto scan = [&](auto kernel) { launch_kernel(kernel, grid, dim3(kScanThreads), s, ts.start, ts.stop, sa); };
     if (c.idx_dim == 128) {
-        if (mt == 4) scan(indexer_scan_kernel<128, 4>);
-        else if (mt == 3) scan(indexer_scan_kernel<128, 3>);
-        else if (mt == 2) scan(indexer_scan_kernel<128, 2>);
-        else scan(indexer_scan_kernel<128, 1>);
+        if (mt == 4) scan(indexer_scan_kernel<128, 4, POOL>);
+        else if (mt == 3) scan(indexer_scan_kernel<128, 3, POOL>);
+        else if (mt == 2) scan(indexer_scan_kernel<128, 2, POOL>);
+        else scan(indexer_scan_kernel<128, 1, POOL>);
     } else {
-        if (mt == 4) scan(indexer_scan_kernel<64, 4>);
-        else if (mt == 3) scan(indexer_scan_kernel<64, 3>);
-        else if (mt == 2) scan(indexer_scan_kernel<64, 2>);
-        else scan(indexer_scan_kernel<64, 1>);
+        if (mt == 4) scan(indexer_scan_kernel<64, 4, POOL>);
+        else if (mt == 3) scan(indexer_scan_kernel<64, 3, POOL>);
+        else if (mt == 2) scan(indexer_scan_kernel<64, 2, POOL>);
+        else scan(indexer_scan_kernel<64, 1, POOL>);
     }
+}
+
+void launch_indexer_scan(const cskv_cache &c, const uint16_t *q_idx, int heads, const float *head_w,
+                         uint32_t *keys, hipStream_t s, uint32_t *block_keys, size_t block_stride, int block)
+{
+    const int chunk = scan_chunk(c.batch, (size_t)c.capacity, (size_t)1 << 30);
+    ScanArgs sa{c.idx_keys, c.n_tokens, q_idx, head_w, keys, c.capacity, heads, chunk, score_key_stride(c),
+                block_keys, block_stride, block, nullptr, 0, nullptr};
+    dim3 grid((unsigned)(((size_t)c.capacity + chunk - 1) / chunk), (unsigned)c.batch);
+    scan_dispatch<false>(c, heads, sa, grid, s);
+}
+
+void launch_pool_scan(const cskv_cache &c, const uint16_t *q_idx, int heads, const float *head_w,
+                      const int32_t *pool, int pool_blocks, int block, uint2 *pairs, hipStream_t s)
+{
+    const size_t n = (size_t)pool_blocks * block;
+    const int chunk = scan_chunk(c.batch, n, kPoolChunkMax);
+    ScanArgs sa{c.idx_keys, c.n_tokens, q_idx, head_w, nullptr, c.capacity, heads, chunk, 0,
+                nullptr, 0, block, pool, pool_blocks, pairs};
+    dim3 grid((unsigned)((n + chunk - 1) / chunk), (unsigned)c.batch);
+    scan_dispatch<true>(c, heads, sa, grid, s);
 }
 
 }  // namespace cskv

@@ -13,7 +13,9 @@
  *      all query heads together with the window rows in one softmax
  *      (cskv_sparse_attn_decode);
  *   and the Full / Reindex / Reuse layer modes of one layer group over a
- *   shared cache (cskv_layer_group_decode).
+ *   shared cache (cskv_layer_group_decode), optionally with the hierarchical
+ *   indexer's candidate pool (cskv_indexer_topk_pool,
+ *   cskv_indexer_topk_in_pool, cskv_layer_group_decode_pooled).
  *
  * Sources cited as [P1]/[P2]/[P3] (page title, then the section):
  *   P1  "DeepSeek V4.1 Flash KV Cache压缩实战：FP4+CSA2+CED将显存降至1/4"
@@ -219,14 +221,68 @@ int cskv_layer_group_decode(const cskv_cache *cache, const cskv_layer *layers, i
                             int32_t k, int32_t window, float softmax_scale, void *ws,
                             size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Hierarchical sparse indexer [P2 "层级稀疏索引器：后面的层只在候选池里找":
+ * after the first Full layer has scored every position, each block of 8
+ * positions keeps its best score and the 2048 best blocks, 16,384 positions,
+ * form a candidate pool; later Reindex layers score only inside it].
+ * Positions are the cache entries; block i holds entries [block*i,
+ * block*i + block) below the sequence's entry count.
+ *
+ * cskv_indexer_topk_pool: cskv_indexer_topk, and from the same scores the
+ * pool: the pool_blocks best blocks by their best score (ties: lower block
+ * index), ascending block indices in out_pool [batch][pool_blocks], -1
+ * padded (fewer blocks than pool_blocks: all of them).
+ * cskv_indexer_topk_in_pool: the exact top-k of a layer's own indexer scores
+ * restricted to the entries of the pooled blocks (ties: lower entry index),
+ * ascending, -1 padded; pool as written by cskv_indexer_topk_pool on the
+ * same cache state.
+ * pool_block in {2, 4, 8, 16}; 1 <= pool_blocks <= 2048 and
+ * pool_blocks * pool_block >= k + pool_block (so a pool of more than k
+ * entries exists whenever the sequence has more than k).  Other arguments as
+ * for cskv_indexer_topk.  ws: cskv_workspace_bytes_pool(cache,
+ * CSKV_OP_INDEXER_POOL or CSKV_OP_INDEXER_IN_POOL, 0, k, 0, pool_blocks,
+ * pool_block) bytes, 256-byte aligned.
+ */
+int cskv_indexer_topk_pool(const cskv_cache *cache, const uint16_t *q_idx, int32_t n_idx_heads,
+                           const float *head_w, int32_t k, int32_t *out_idx, int32_t pool_blocks,
+                           int32_t pool_block, int32_t *out_pool, void *ws, size_t ws_bytes,
+                           hipStream_t stream);
+int cskv_indexer_topk_in_pool(const cskv_cache *cache, const uint16_t *q_idx, int32_t n_idx_heads,
+                              const float *head_w, int32_t k, const int32_t *pool, int32_t pool_blocks,
+                              int32_t pool_block, int32_t *out_idx, void *ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/*
+ * cskv_layer_group_decode with the hierarchical indexer: the first FULL
+ * layer also builds the candidate pool (pool_blocks blocks of pool_block
+ * entries), and every REINDEX layer after it selects inside the pool
+ * (cskv_indexer_topk_in_pool); a REINDEX layer before any FULL layer scans
+ * every entry.  pool_blocks = 0 is cskv_layer_group_decode.  ws:
+ * cskv_workspace_bytes_pool(cache, CSKV_OP_LAYER_GROUP, n_heads, k, window,
+ * pool_blocks, pool_block) bytes; the pool itself lives in it.
+ */
+int cskv_layer_group_decode_pooled(const cskv_cache *cache, const cskv_layer *layers,
+                                   int32_t n_layers, const float *new_tokens, const float *w_comp,
+                                   const uint16_t *new_idx_rows, int32_t n_idx_heads, int32_t n_heads,
+                                   int32_t k, int32_t window, float softmax_scale, int32_t pool_blocks,
+                                   int32_t pool_block, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Device workspace bytes an operation needs (at least 256); 0 on invalid
  * arguments (see cskv_last_error).  op: CSKV_OP_INDEXER_TOPK (uses k),
- * CSKV_OP_SPARSE_ATTN (n_heads, k, window), CSKV_OP_LAYER_GROUP (all). */
+ * CSKV_OP_SPARSE_ATTN (n_heads, k, window), CSKV_OP_LAYER_GROUP (all).
+ * cskv_workspace_bytes_pool also takes the pool's size, for
+ * CSKV_OP_INDEXER_POOL, CSKV_OP_INDEXER_IN_POOL (k and the pool) and
+ * CSKV_OP_LAYER_GROUP (all; pool_blocks = 0: no pool). */
 #define CSKV_OP_INDEXER_TOPK 1
 #define CSKV_OP_SPARSE_ATTN 2
 #define CSKV_OP_LAYER_GROUP 3
+#define CSKV_OP_INDEXER_POOL 4
+#define CSKV_OP_INDEXER_IN_POOL 5
 size_t cskv_workspace_bytes(const cskv_cache *cache, int32_t op, int32_t n_heads, int32_t k,
                             int32_t window);
+size_t cskv_workspace_bytes_pool(const cskv_cache *cache, int32_t op, int32_t n_heads, int32_t k,
+                                 int32_t window, int32_t pool_blocks, int32_t pool_block);
 
 /* Bytes one entry occupies across all planes (codes, scales, indexer key)
  * [P2 四、"890 字节是怎么算出来的"]. */

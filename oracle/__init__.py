@@ -331,8 +331,9 @@ def layer_group_decode(cache: Cache, modes, new_token, new_idx_row, w_comp, q, q
 
     new_token fp32 [B, dim] (appended by the full layer, or None);
     q / q_idx / swa_rings / swa_rows: per-layer lists (q_idx None for reuse).
-    pool = (block, nb): the hierarchical indexer -- the first full layer's
-    scores give the candidate pool and later reindex layers select inside it.
+    pool = (nb, block): the hierarchical indexer -- the first full layer's
+    scores give a candidate pool of nb blocks of `block` entries, and later
+    reindex layers select inside it.
     swa_rings are updated in place.  Returns (outs, lses, idx_lists) per layer.
     """
     B = cache.batch
@@ -347,11 +348,11 @@ def layer_group_decode(cache: Cache, modes, new_token, new_idx_row, w_comp, q, q
         if mode in ("full", "reindex"):
             hw = None if head_w is None else head_w[li]
             if mode == "reindex" and cand is not None:
-                last_idx = indexer_topk_in_pool(cache, q_idx[li], cand, pool[0], k, hw)
+                last_idx = indexer_topk_in_pool(cache, q_idx[li], cand, pool[1], k, hw)
             else:
                 last_idx = indexer_topk(cache, q_idx[li], k, hw)
             if mode == "full" and pool is not None and cand is None:
-                cand = indexer_pool(cache, q_idx[li], pool[0], pool[1], hw)
+                cand = indexer_pool(cache, q_idx[li], pool[1], pool[0], hw)
         elif last_idx is None:
             raise ValueError("reuse layer with no preceding full/reindex layer")
         o, l = sparse_attn(cache, q[li], last_idx, swa_rings[li], scale)

@@ -132,3 +132,34 @@ def test_layer_group_checks_every_layer_first(L):
     rc = L.cskv_layer_group_decode(C.byref(d), layers, 2, None, None, None, 4, 16, 512, 128,
                                    C.c_float(0.04), vp(0xB0000), ws, None)
     assert rc == ck.EINVAL and "mode" in _err(L)
+
+
+def test_pool_arguments_rejected_before_launch(L):
+    d = _desc()
+    vp = C.c_void_p
+    ws = L.cskv_workspace_bytes_pool(C.byref(d), ck.OP_INDEXER_POOL, 0, 512, 0, 2048, 8)
+    assert ws > L.cskv_workspace_bytes(C.byref(d), ck.OP_INDEXER_TOPK, 0, 512, 0)
+    assert L.cskv_workspace_bytes_pool(C.byref(d), ck.OP_INDEXER_IN_POOL, 0, 512, 0, 2048, 8) >= 2 * 2048 * 8 * 8
+    # block size, pool size, pool too small for k
+    for nb, blk, text in ((2048, 3, "pool_block"), (0, 8, "pool_blocks"), (4096, 8, "pool_blocks"),
+                          (64, 8, "too small")):
+        assert L.cskv_workspace_bytes_pool(C.byref(d), ck.OP_INDEXER_POOL, 0, 512, 0, nb, blk) == 0
+        assert text in _err(L)
+        rc = L.cskv_indexer_topk_pool(C.byref(d), vp(0xA0000), 4, None, 512, vp(0x90000), nb, blk,
+                                      vp(0x98000), vp(0xB0000), ws, None)
+        assert rc == ck.EUNSUPPORTED and text in _err(L), (rc, _err(L))
+    # missing pool output, workspace too small
+    assert L.cskv_indexer_topk_pool(C.byref(d), vp(0xA0000), 4, None, 512, vp(0x90000), 2048, 8, None,
+                                    vp(0xB0000), ws, None) == ck.EINVAL
+    assert L.cskv_indexer_topk_pool(C.byref(d), vp(0xA0000), 4, None, 512, vp(0x90000), 2048, 8,
+                                    vp(0x98000), vp(0xB0000), ws - 1, None) == ck.EWORKSPACE
+    wi = L.cskv_workspace_bytes_pool(C.byref(d), ck.OP_INDEXER_IN_POOL, 0, 512, 0, 2048, 8)
+    assert L.cskv_indexer_topk_in_pool(C.byref(d), vp(0xA0000), 4, None, 512, None, 2048, 8, vp(0x90000),
+                                       vp(0xB0000), wi, None) == ck.EINVAL
+    assert L.cskv_indexer_topk_in_pool(C.byref(d), vp(0xA0000), 4, None, 512, vp(0x98000), 2048, 8,
+                                       vp(0x90000), vp(0xB0000), wi - 1, None) == ck.EWORKSPACE
+    # the pooled layer group needs more workspace than the plain one
+    g0 = L.cskv_workspace_bytes(C.byref(d), ck.OP_LAYER_GROUP, 16, 512, 128)
+    g1 = L.cskv_workspace_bytes_pool(C.byref(d), ck.OP_LAYER_GROUP, 16, 512, 128, 2048, 8)
+    assert g1 > g0 and L.cskv_workspace_bytes_pool(C.byref(d), ck.OP_LAYER_GROUP, 16, 512, 128, 0, 0) == g0
+

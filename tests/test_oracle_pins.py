@@ -665,7 +665,7 @@ def test_modes_with_candidate_pool(orc):
     st = synth.step_inputs(w)
     Wc = synth.w_comp(w)
     res = {}
-    for name, pool in (("none", None), ("all", (8, 2048)), ("small", (8, 6))):
+    for name, pool in (("none", None), ("all", (2048, 8)), ("small", (6, 8))):
         cache = orc.Cache.empty(2, 310, 576, 64, 32, 0, 64)
         orc.kv_append(cache, ents, np.array([0, 300, 600], np.int32), None, keys)
         rings = [r.copy() for r in st.swa_ring]
