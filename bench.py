@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--graph", action="store_true", help="time HIP graph replays of the step")
     p.add_argument("--scan-sample-every", type=int, default=4)
     p.add_argument("--copy-probe", type=int, default=0, help="MiB copied by a plain device copy")
+    p.add_argument("--pool", default="", help="pool_blocks,pool_block: the hierarchical indexer's candidate "
+                   "pool in a layer-group workload (reindex layers select inside it)")
     return p.parse_args()
 
 
@@ -89,21 +91,43 @@ def build_replicas(ck, synth, w, cap, dev, n):
     return reps
 
 
-def step_bytes(w, entries: float) -> dict:
+def scans_per_step(w, pool):
+    """(full scans, pooled scans) one layer-group step runs."""
+    full = pooled = 0
+    have_pool = False
+    for mode in w.layers:
+        if mode == "full":
+            full += 1
+            have_pool = have_pool or pool is not None
+        elif mode == "reindex":
+            if have_pool:
+                pooled += 1
+            else:
+                full += 1
+    return full, pooled
+
+
+def step_bytes(w, entries: float, pool=None) -> dict:
     """Algorithmic bytes of one step (whole batch): every plane read or written
-    once by the method's definition; score arrays are not counted."""
+    once by the method's definition; score arrays are not counted.  Scans: the
+    whole indexer-key plane per full scan, the pooled positions' keys per
+    pooled scan."""
     B, D, Dv, Di = w.batch, w.dim, w.vdim, w.idx_dim
     entry_fp4 = D // 2 + 4 * (D // w.k_group)
     if w.v_group:
         entry_fp4 += Dv // 2 + 4 * (Dv // w.v_group)
+    full, pooled = scans_per_step(w, pool)
+    L = len(w.layers)
+    sel = sum(1 for m in w.layers if m != "reuse")
+    pool_pos = min(entries, pool[0] * pool[1]) if pool else 0
     parts = {
-        "indexer_keys": B * entries * Di * 2,
-        "indexer_q": B * w.idx_heads * Di * 2,
-        "gather": B * min(w.topk, entries) * entry_fp4,
-        "window": B * w.window * D * 2,
-        "q": B * w.q_heads * D * 4,
-        "out": B * w.q_heads * (Dv + 1) * 4,
-        "indices": B * w.topk * 4 * 2,
+        "indexer_keys": B * (full * entries + pooled * pool_pos) * Di * 2,
+        "indexer_q": B * sel * w.idx_heads * Di * 2,
+        "gather": L * B * min(w.topk, entries) * entry_fp4,
+        "window": L * B * w.window * D * 2,
+        "q": L * B * w.q_heads * D * 4,
+        "out": L * B * w.q_heads * (Dv + 1) * 4,
+        "indices": (sel + L) * B * w.topk * 4,
         # one token per sequence; a pair completes every other step, then the
         # compressor weights are read and one entry + indexer key written
         "append": B * (D * 4 * 2 + 0.5 * (entry_fp4 + Di * 2)) + 0.5 * D * 2 * D * 4,
@@ -112,7 +136,7 @@ def step_bytes(w, entries: float) -> dict:
     return parts
 
 
-def cpu_baseline(synth, w, nseq: int):
+def cpu_baseline(synth, w, nseq: int, pool=None):
     """The oracle, as it is, on a bounded sample: nseq of the batch's sequences,
     full-length caches, one Full-layer decode step; the cache build is untimed."""
     import oracle as orc
@@ -133,7 +157,7 @@ def cpu_baseline(synth, w, nseq: int):
     rings = [r.copy() for r in st.swa_ring]
     t0 = time.perf_counter()
     orc.layer_group_decode(hc, sub.layers, st.token, st.idx_row, W, st.q, st.q_idx, rings,
-                           st.swa_row, w.topk, 1 / math.sqrt(w.dim))
+                           st.swa_row, w.topk, 1 / math.sqrt(w.dim), pool=pool)
     dt = time.perf_counter() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     per_full_step = dt * w.batch / nseq
@@ -147,8 +171,8 @@ def cpu_baseline(synth, w, nseq: int):
         pass
     return {"value": 1.0 / per_full_step, "unit": "steps/s", "cores": min(threads, nseq),
             "kind": "oracle",
-            "sample": f"{nseq} of {w.batch} sequences at full length ({w.entries} entries), one Full-layer "
-                      f"decode step ({dt:.2f} s), scaled by {w.batch}/{nseq}; cache build untimed; "
+            "sample": f"{nseq} of {w.batch} sequences at full length ({w.entries} entries), one "
+                      f"{'+'.join(w.layers)} decode step ({dt:.2f} s), scaled by {w.batch}/{nseq}; cache build untimed; "
                       f"OpenMP over sequences on {cpu}"}
 
 
@@ -185,7 +209,8 @@ def main():
 
     ck.lib()
     w = synth.WORKLOADS[a.workload]
-    assert w.entries is not None and len(w.layers) == 1, "bench steps fixed-length single-layer workloads"
+    assert w.entries is not None, "bench steps fixed-length workloads"
+    pool = tuple(int(x) for x in a.pool.split(",")) if a.pool else None
     timer_steps = min(a.steps, 100)
     dist_steps = min(a.steps, 100)
     total_steps = a.warmup + timer_steps + dist_steps + a.steps + a.replicas
@@ -206,19 +231,25 @@ def main():
     B = w.batch
     per_rep_io = []
     for r in range(a.replicas):
-        per_rep_io.append(dict(
-            layers=[ck.Layer(mode="full", q=dev(st.q[0]), q_idx=dev(st.q_idx[0]), swa=dev(st.swa_ring[0]),
-                             swa_row=dev(st.swa_row[0]),
-                             idx=torch.empty(B, w.topk, dtype=torch.int32, device="cuda"),
-                             out=torch.empty(B, w.q_heads, w.vdim, device="cuda"),
-                             lse=torch.empty(B, w.q_heads, device="cuda"))],
-            ws=ck.workspace(reps[r], w.topk, ck.OP_LAYER_GROUP, w.q_heads, w.window)))
+        layers = []
+        for li, mode in enumerate(w.layers):
+            layers.append(ck.Layer(mode=mode, q=dev(st.q[li]),
+                                   q_idx=None if st.q_idx[li] is None else dev(st.q_idx[li]),
+                                   swa=dev(st.swa_ring[li]), swa_row=dev(st.swa_row[li]),
+                                   idx=torch.empty(B, w.topk, dtype=torch.int32, device="cuda")
+                                   if mode != "reuse" else None,
+                                   out=torch.empty(B, w.q_heads, w.vdim, device="cuda"),
+                                   lse=torch.empty(B, w.q_heads, device="cuda")))
+        per_rep_io.append(dict(layers=layers,
+                               ws=ck.workspace(reps[r], w.topk, ck.OP_LAYER_GROUP, w.q_heads, w.window,
+                                               pool=pool)))
     tok, irow = dev(st.token), dev(st.idx_row)
 
     def step(i):
         r = i % a.replicas
         io = per_rep_io[r]
-        ck.layer_group_decode(reps[r], io["layers"], tok, W, irow, w.topk, w.window, scale, ws=io["ws"])
+        ck.layer_group_decode(reps[r], io["layers"], tok, W, irow, w.topk, w.window, scale, ws=io["ws"],
+                              pool=pool)
 
     kinds = {"append": ck.KERNEL_APPEND, "swa_append": ck.KERNEL_SWA_APPEND,
              "indexer_scan": ck.KERNEL_INDEXER_SCAN, "topk_select": ck.KERNEL_TOPK_SELECT,
@@ -295,8 +326,9 @@ def main():
 
     # mean entries per sequence over the timed steps
     entries_mean = float(0.5 * (ent_before + ent_after))
-    sb = step_bytes(w, entries_mean)
-    scan_bytes = sb["indexer_keys"] + sb["indexer_q"]
+    sb = step_bytes(w, entries_mean, pool)
+    n_full, n_pooled = scans_per_step(w, pool)
+    scan_bytes = (sb["indexer_keys"] + sb["indexer_q"]) / (n_full + n_pooled)   # per launch, averaged
     scan = live if live is not None else kern["indexer_scan"]
     scan_us = scan["avg_us"]
     achieved = scan_bytes / (scan_us * 1e-6) / 1e9
@@ -318,13 +350,14 @@ def main():
                    "entries_per_seq": w.entries, "k_group": w.k_group, "storage": "e2m1+fp32 scales",
                    "idx_heads": w.idx_heads, "idx_dim": w.idx_dim, "q_heads": w.q_heads,
                    "topk": w.topk, "window": w.window, "replicas": a.replicas,
-                   "launch": "hip_graph" if a.graph else "eager",
+                   "launch": "hip_graph" if a.graph else "eager", "layers": list(w.layers),
+                   "pool": list(pool) if pool else None,
                    "tokens_per_s": round(steps_per_s * B, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": pmc_traffic(), "kernel": "indexer_scan",
                      "bytes_per_launch": round(scan_bytes), "avg_us": round(scan_us, 2),
-                     "timed_launches": scan["launches"],
+                     "timed_launches": scan["launches"], "scans_per_step": [n_full, n_pooled],
                      "timing": ("hip events in the timed region, 1 step in %d" % every) if live is not None
                      else "hip events, separate eager pass"},
         "step_us": {"p10": round(float(np.percentile(per_step, 10)), 2),
@@ -337,7 +370,7 @@ def main():
     }
     if not a.no_cpu_baseline:
         log("timing the oracle on a CPU sample ...")
-        result["cpu_baseline"] = cpu_baseline(synth, w, a.cpu_baseline_seqs)
+        result["cpu_baseline"] = cpu_baseline(synth, w, a.cpu_baseline_seqs, pool)
     print(json.dumps(result), flush=True)
 
 

@@ -85,8 +85,9 @@ def _build(ck, orc, w, cap, sampled):
     return gc, mirrors
 
 
-def _step(ck, orc, w, gc, mirrors, st, W_h):
-    """One layer-group step on the device, then the oracle per sampled sequence."""
+def _step(ck, orc, w, gc, mirrors, st, W_h, pool=None):
+    """One layer-group step on the device, then the oracle per sampled sequence
+    (pool: the hierarchical indexer's (pool_blocks, pool_block))."""
     B = w.batch
     scale = 1 / math.sqrt(w.dim)
     layers = []
@@ -98,9 +99,9 @@ def _step(ck, orc, w, gc, mirrors, st, W_h):
                                lse=torch.empty(B, w.q_heads, device="cuda"),
                                idx=torch.empty(B, w.topk, dtype=torch.int32, device="cuda")
                                if mode != "reuse" else None))
-    ws = ck.workspace(gc, w.topk, ck.OP_LAYER_GROUP, w.q_heads, w.window)
+    ws = ck.workspace(gc, w.topk, ck.OP_LAYER_GROUP, w.q_heads, w.window, pool=pool)
     ck.layer_group_decode(gc, layers, dev(st.token), dev(W_h), dev(st.idx_row), w.topk, w.window,
-                          scale, ws=ws)
+                          scale, ws=ws, pool=pool)
     torch.cuda.synchronize()
     assert int(host(gc.status)[0]) == 0
 
@@ -125,7 +126,7 @@ def _step(ck, orc, w, gc, mirrors, st, W_h):
         outs, lses, idxs = orc.layer_group_decode(
             hc, w.layers, st.token[sl], st.idx_row[sl], W_h, [q[sl] for q in st.q],
             [None if qi is None else qi[sl] for qi in st.q_idx], rings,
-            [r[sl] for r in st.swa_row], w.topk, scale)
+            [r[sl] for r in st.swa_row], w.topk, scale, pool=pool)
         e = int(hc.entries()[0])
         assert int(host(gc.n_tokens)[b]) == int(hc.n_tokens[0])
         for name in ("k_codes", "k_scales", "v_codes", "v_scales", "idx_keys"):
@@ -164,6 +165,26 @@ def test_full_group_128k_b64(ck, orc):
     w = synth.WORKLOADS["group_128k_b64"]
     gc, mirrors = _build(ck, orc, w, w.entries + 8, sampled={0, 41, 63})
     _step(ck, orc, w, gc, mirrors, synth.step_inputs(w, 0), synth.w_comp(w))
+
+
+def test_full_group_128k_b64_pooled(ck, orc):
+    """The same layer group with the hierarchical indexer at the pages' size:
+    the full layer's pool of 2048 blocks of 8 entries, the reindex layer
+    selecting inside it."""
+    w = synth.WORKLOADS["group_128k_b64"]
+    gc, mirrors = _build(ck, orc, w, w.entries + 8, sampled={5, 62})
+    st = synth.step_inputs(w, 0)
+    layers = _step(ck, orc, w, gc, mirrors, st, synth.w_comp(w), pool=(2048, 8))
+    # every sequence: the reindex layer's entries lie in the full layer's pool,
+    # rebuilt here from the same cache state and the full layer's query
+    fi, ri = w.layers.index("full"), w.layers.index("reindex")
+    idx, pool = ck.indexer_topk_pool(gc, dev(st.q_idx[fi]), w.topk, 2048, 8)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, layers[fi].idx)
+    pool, sel = host(pool), host(layers[ri].idx)
+    for b in range(w.batch):
+        s = sel[b][sel[b] >= 0]
+        assert len(s) == w.topk and set((s // 8).tolist()) <= set(pool[b].tolist()), f"seq {b}"
 
 
 def test_full_mixed_ragged_b256(ck, orc):
