@@ -51,7 +51,8 @@ class _Cache(C.Structure):
                 ("k_codes", C.POINTER(C.c_uint8)), ("k_scales", C.POINTER(C.c_float)),
                 ("v_codes", C.POINTER(C.c_uint8)), ("v_scales", C.POINTER(C.c_float)),
                 ("idx_keys", C.POINTER(C.c_uint16)), ("n_tokens", C.POINTER(C.c_int32)),
-                ("pending", C.POINTER(C.c_float)), ("status", C.POINTER(C.c_int32))]
+                ("pending", C.POINTER(C.c_float)), ("status", C.POINTER(C.c_int32)),
+                ("idx_format", C.c_int32), ("idx_scales", C.POINTER(C.c_uint8))]
 
 
 def _declare(L):
@@ -71,6 +72,12 @@ def _declare(L):
     L.orc_bf16_from_f32.argtypes = [C.c_float]
     L.orc_bf16_value.restype = f64
     L.orc_bf16_value.argtypes = [C.c_uint16]
+    L.orc_e8m0_value.restype = f64
+    L.orc_e8m0_value.argtypes = [C.c_uint8]
+    L.orc_quantize_mx16.restype = None
+    L.orc_quantize_mx16.argtypes = [P(C.c_uint16), C.c_int, P(C.c_uint8), P(C.c_uint8)]
+    L.orc_dequantize_mx16.restype = None
+    L.orc_dequantize_mx16.argtypes = [P(C.c_uint8), P(C.c_uint8), C.c_int, P(f64)]
     L.orc_compress_pair.restype = None
     L.orc_compress_pair.argtypes = [P(C.c_float)] * 3 + [C.c_int, P(C.c_float)]
     L.orc_quantize_row.restype = None
@@ -190,6 +197,28 @@ def topk(scores, k) -> np.ndarray:
     return out
 
 
+def e8m0_value(s: int) -> float:
+    return float(lib().orc_e8m0_value(s))
+
+
+def quantize_mx16(x_bf16):
+    """FP4 indexer key: E2M1 codes (low nibble first) and E8M0 scales per 16 dims."""
+    x = np.ascontiguousarray(x_bf16, np.uint16)
+    n = x.shape[0]
+    codes = np.empty(n // 2, np.uint8)
+    scales = np.empty(n // 16, np.uint8)
+    lib().orc_quantize_mx16(_p(x, C.c_uint16), n, _p(codes, C.c_uint8), _p(scales, C.c_uint8))
+    return codes, scales
+
+
+def dequantize_mx16(codes, scales, n) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    out = np.empty(n, np.float64)
+    lib().orc_dequantize_mx16(_p(codes, C.c_uint8), _p(scales, C.c_uint8), n, _p(out, C.c_double))
+    return out
+
+
 def pool_blocks(scores, block, nb) -> np.ndarray:
     """Candidate pool of the hierarchical indexer: the nb best blocks of
     `block` entries by block maximum (ties: lower block), ascending, -1 padded."""
@@ -225,22 +254,28 @@ class Cache:
     k_scales: np.ndarray
     v_codes: Optional[np.ndarray]
     v_scales: Optional[np.ndarray]
-    idx_keys: np.ndarray
+    idx_keys: np.ndarray       # bf16 [B][cap][Di], or E2M1 codes u8 [B][cap][Di/2] (idx_format 1)
     n_tokens: np.ndarray
     pending: np.ndarray
     status: np.ndarray
+    idx_format: int = 0
+    idx_scales: Optional[np.ndarray] = None   # E8M0 u8 [B][cap][Di/16] (idx_format 1)
 
     @classmethod
-    def empty(cls, batch, capacity, dim=576, rope_dim=64, k_group=32, v_group=0, idx_dim=128):
+    def empty(cls, batch, capacity, dim=576, rope_dim=64, k_group=32, v_group=0, idx_dim=128,
+              idx_format=0):
         Dv = dim - rope_dim
+        fp4 = idx_format == 1
         return cls(batch, capacity, dim, rope_dim, k_group, v_group, idx_dim,
                    np.zeros((batch, capacity, dim // 2), np.uint8),
                    np.zeros((batch, capacity, dim // k_group), np.float32),
                    np.zeros((batch, capacity, Dv // 2), np.uint8) if v_group else None,
                    np.zeros((batch, capacity, Dv // v_group), np.float32) if v_group else None,
-                   np.zeros((batch, capacity, idx_dim), np.uint16),
+                   np.zeros((batch, capacity, idx_dim // 2), np.uint8) if fp4
+                   else np.zeros((batch, capacity, idx_dim), np.uint16),
                    np.zeros(batch, np.int32), np.zeros((batch, dim), np.float32),
-                   np.zeros(1, np.int32))
+                   np.zeros(1, np.int32), idx_format,
+                   np.zeros((batch, capacity, idx_dim // 16), np.uint8) if fp4 else None)
 
     def _c(self) -> _Cache:
         return _Cache(self.batch, self.capacity, self.dim, self.rope_dim, self.k_group,
@@ -248,7 +283,8 @@ class Cache:
                       _p(self.k_codes, C.c_uint8), _p(self.k_scales, C.c_float),
                       _p(self.v_codes, C.c_uint8), _p(self.v_scales, C.c_float),
                       _p(self.idx_keys, C.c_uint16), _p(self.n_tokens, C.c_int32),
-                      _p(self.pending, C.c_float), _p(self.status, C.c_int32))
+                      _p(self.pending, C.c_float), _p(self.status, C.c_int32),
+                      self.idx_format, _p(self.idx_scales, C.c_uint8))
 
     def entries(self) -> np.ndarray:
         return np.clip(self.n_tokens // 2, 0, self.capacity)

@@ -163,6 +163,49 @@ void orc_dequantize_row(const uint8_t *packed, const float *scales, int n, int g
 
 /* ------------------------------------------------------------ cache append */
 
+/* ------------------------------------------------------------ FP4 indexer key */
+
+double orc_e8m0_value(uint8_t s)
+{
+    return ldexp(1.0, (int)s - 127);
+}
+
+void orc_quantize_mx16(const uint16_t *x_bf16, int n, uint8_t *codes, uint8_t *scales)
+{
+    for (int g = 0; g < n / 16; ++g) {
+        double a = 0.0;
+        for (int i = 0; i < 16; ++i) {
+            double v = fabs(orc_bf16_value(x_bf16[16 * g + i]));
+            if (v > a) a = v;
+        }
+        int e = -127;
+        if (a > 0.0) {
+            int ex;
+            (void)frexp(a, &ex);          /* a = m * 2^ex, 0.5 <= m < 1: floor(log2 a) = ex - 1 */
+            e = ex - 1 - 2;
+            if (e < -127) e = -127;
+            if (e > 127) e = 127;
+        }
+        scales[g] = (uint8_t)(e + 127);
+        for (int i = 0; i < 16; i += 2) {
+            unsigned c0 = 0, c1 = 0;
+            if (a > 0.0) {
+                c0 = orc_e2m1_encode((float)ldexp(orc_bf16_value(x_bf16[16 * g + i]), -e));
+                c1 = orc_e2m1_encode((float)ldexp(orc_bf16_value(x_bf16[16 * g + i + 1]), -e));
+            }
+            codes[(16 * g + i) / 2] = (uint8_t)(c0 | (c1 << 4));
+        }
+    }
+}
+
+void orc_dequantize_mx16(const uint8_t *codes, const uint8_t *scales, int n, double *out)
+{
+    for (int i = 0; i < n; ++i) {
+        unsigned c = (codes[i / 2] >> (4 * (i % 2))) & 15u;
+        out[i] = orc_e2m1_value(c) * orc_e8m0_value(scales[i / 16]);
+    }
+}
+
 static void store_entry(orc_cache *c, int b, int64_t i, const float *e, const uint16_t *idx_row)
 {
     const int D = c->dim, Dv = c->dim - c->rope_dim;
@@ -172,7 +215,11 @@ static void store_entry(orc_cache *c, int b, int64_t i, const float *e, const ui
     if (c->v_group > 0)
         orc_quantize_row(e, Dv, c->v_group, c->v_codes + row * (Dv / 2),
                          c->v_scales + row * (Dv / c->v_group));
-    memcpy(c->idx_keys + row * c->idx_dim, idx_row, sizeof(uint16_t) * (size_t)c->idx_dim);
+    if (c->idx_format == 1)
+        orc_quantize_mx16(idx_row, c->idx_dim, (uint8_t *)c->idx_keys + row * (c->idx_dim / 2),
+                          c->idx_scales + row * (c->idx_dim / 16));
+    else
+        memcpy(c->idx_keys + row * c->idx_dim, idx_row, sizeof(uint16_t) * (size_t)c->idx_dim);
 }
 
 static void raise_status(orc_cache *c, int32_t bit)
@@ -280,6 +327,32 @@ void orc_topk(const double *scores, int64_t E, int k, int32_t *out)
     free(all);
 }
 
+/* The indexer scores of sequence b's first E entries from its stored keys:
+ * bf16 keys directly, FP4 keys dequantised to their exact values. */
+static void cache_scores(const orc_cache *c, int b, int64_t E, const uint16_t *q, int heads,
+                         const float *head_w, double *scores)
+{
+    const int Di = c->idx_dim;
+    if (c->idx_format != 1) {
+        orc_indexer_scores(c->idx_keys + (size_t)b * c->capacity * Di, E, Di, q, heads, head_w, scores);
+        return;
+    }
+    double *k = (double *)malloc(sizeof(double) * (size_t)Di);
+    for (int64_t j = 0; j < E; ++j) {
+        size_t row = (size_t)b * c->capacity + (size_t)j;
+        orc_dequantize_mx16((const uint8_t *)c->idx_keys + row * (Di / 2), c->idx_scales + row * (Di / 16), Di, k);
+        double sc = 0.0;
+        for (int h = 0; h < heads; ++h) {
+            double dot = 0.0;
+            for (int d = 0; d < Di; ++d) dot += orc_bf16_value(q[(size_t)h * Di + d]) * k[d];
+            double w = head_w ? (double)head_w[h] : 1.0;
+            sc += w * (dot > 0.0 ? dot : 0.0);
+        }
+        scores[j] = sc;
+    }
+    free(k);
+}
+
 static int64_t entries_of(const orc_cache *c, int b)
 {
     int64_t e = c->n_tokens[b] / 2;
@@ -295,9 +368,8 @@ void orc_indexer_topk(const orc_cache *c, const uint16_t *q, int heads,
     for (int b = 0; b < c->batch; ++b) {
         int64_t E = entries_of(c, b);
         double *s = (double *)malloc(sizeof(double) * (size_t)(E > 0 ? E : 1));
-        orc_indexer_scores(c->idx_keys + (size_t)b * c->capacity * c->idx_dim, E, c->idx_dim,
-                           q + (size_t)b * heads * c->idx_dim, heads,
-                           head_w ? head_w + (size_t)b * heads : NULL, s);
+        cache_scores(c, b, E, q + (size_t)b * heads * c->idx_dim, heads,
+                     head_w ? head_w + (size_t)b * heads : NULL, s);
         orc_topk(s, E, k, out + (size_t)b * k);
         free(s);
     }
@@ -350,9 +422,8 @@ void orc_indexer_pool(const orc_cache *c, const uint16_t *q, int heads, const fl
     for (int b = 0; b < c->batch; ++b) {
         int64_t E = entries_of(c, b);
         double *s = (double *)malloc(sizeof(double) * (size_t)(E > 0 ? E : 1));
-        orc_indexer_scores(c->idx_keys + (size_t)b * c->capacity * c->idx_dim, E, c->idx_dim,
-                           q + (size_t)b * heads * c->idx_dim, heads,
-                           head_w ? head_w + (size_t)b * heads : NULL, s);
+        cache_scores(c, b, E, q + (size_t)b * heads * c->idx_dim, heads,
+                     head_w ? head_w + (size_t)b * heads : NULL, s);
         orc_pool_blocks(s, E, block, nb, pool + (size_t)b * nb);
         free(s);
     }
@@ -366,9 +437,8 @@ void orc_indexer_topk_in_pool(const orc_cache *c, const uint16_t *q, int heads,
     for (int b = 0; b < c->batch; ++b) {
         int64_t E = entries_of(c, b);
         double *s = (double *)malloc(sizeof(double) * (size_t)(E > 0 ? E : 1));
-        orc_indexer_scores(c->idx_keys + (size_t)b * c->capacity * c->idx_dim, E, c->idx_dim,
-                           q + (size_t)b * heads * c->idx_dim, heads,
-                           head_w ? head_w + (size_t)b * heads : NULL, s);
+        cache_scores(c, b, E, q + (size_t)b * heads * c->idx_dim, heads,
+                     head_w ? head_w + (size_t)b * heads : NULL, s);
         orc_topk_in_pool(s, E, pool + (size_t)b * nb, nb, block, k, out + (size_t)b * k);
         free(s);
     }

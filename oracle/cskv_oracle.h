@@ -100,10 +100,13 @@ typedef struct {
     float *k_scales;    /* [B][cap][dim/k_group]           */
     uint8_t *v_codes;   /* [B][cap][(dim-rope)/2] or NULL  */
     float *v_scales;    /* [B][cap][(dim-rope)/v_group]    */
-    uint16_t *idx_keys; /* [B][cap][idx_dim] bf16          */
+    uint16_t *idx_keys; /* [B][cap][idx_dim] bf16 (format 0) or E2M1 codes,
+                           idx_dim/2 bytes per row (format 1) */
     int32_t *n_tokens;  /* [B] tokens seen                 */
     float *pending;     /* [B][dim] odd token awaiting its pair */
     int32_t *status;    /* [1] bit flags                   */
+    int32_t idx_format; /* 0: bf16 indexer keys; 1: E2M1 + E8M0 per 16 dims */
+    uint8_t *idx_scales;/* [B][cap][idx_dim/16] E8M0 bytes (format 1) */
 } orc_cache;
 
 #define ORC_STATUS_OVERFLOW 1
@@ -127,6 +130,22 @@ void orc_kv_append(orc_cache *c, const float *tokens, const int32_t *cu_new,
 void orc_swa_append(uint16_t *ring, int batch, int W, int dim, const float *rows,
                     const int32_t *cu_new, const int32_t *end_pos);
 
+/* ---------------- FP4 indexer key ---------------------------------------- */
+
+/* The pages' indexer-key format [P2 四、"890 字节是怎么算出来的" (a 128-dim
+ * indexer key stored in FP4 takes 72 B); P2 四、"P4 main KV" (E2M1, one 8-bit
+ * scale per 16 channels, the OCP MXFP4 family)]: E2M1 codes (low nibble =
+ * even dim) and one E8M0 scale per 16 consecutive dims.  E8M0 byte s is the
+ * power of two 2^(s-127).  Scale of a group with largest magnitude a > 0:
+ * 2^(floor(log2 a) - 2) (the MX rule, 2 being E2M1's largest exponent);
+ * a = 0 gives byte 0 and zero codes.  Codes: orc_e2m1_encode(x / scale), the
+ * division by a power of two being exact.  Pinned: the E8M0 values, the scale
+ * rule at binade edges, exact round trips, the hand-derived mapping of the
+ * integers -8..8, and 72 B per 128 dims. */
+double orc_e8m0_value(uint8_t s);
+void orc_quantize_mx16(const uint16_t *x_bf16, int n, uint8_t *codes, uint8_t *scales);
+void orc_dequantize_mx16(const uint8_t *codes, const uint8_t *scales, int n, double *out);
+
 /* ---------------- indexer + top-k ---------------------------------------- */
 
 /* s_j = sum_h w_h * max(0, sum_d q[h][d] K[j][d]) in fp64, over j < E
@@ -145,8 +164,9 @@ void orc_indexer_scores(const uint16_t *keys, int64_t E, int idx_dim,
 void orc_topk(const double *scores, int64_t E, int k, int32_t *out);
 
 /* Whole-batch indexer + top-k on a cache: sequence b scores its first
- * n_tokens[b]/2 entries (capped at capacity). q [B][H][Di], head_w [B][H]
- * or NULL, out [B][k]. */
+ * n_tokens[b]/2 entries (capped at capacity) with its stored indexer keys
+ * (bf16, or the dequantised FP4 keys of format 1). q [B][H][Di], head_w
+ * [B][H] or NULL, out [B][k]. */
 void orc_indexer_topk(const orc_cache *c, const uint16_t *q, int heads,
                       const float *head_w, int k, int32_t *out);
 

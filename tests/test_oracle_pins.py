@@ -451,6 +451,71 @@ def test_topk_exhaustive_tiny(orc):
             _valid_topk(s, k, orc.topk(s, k))
 
 
+# ---------------------------------------------------------------- FP4 indexer key
+
+def test_e8m0_values(orc):
+    assert orc.e8m0_value(127) == 1.0 and orc.e8m0_value(128) == 2.0 and orc.e8m0_value(125) == 0.25
+    assert orc.e8m0_value(0) == 2.0 ** -127 and orc.e8m0_value(254) == 2.0 ** 127
+
+
+def _mx_group(orc, vals):
+    x = _bf16_int(np.asarray(vals, np.float32))
+    codes, scales = orc.quantize_mx16(x)
+    return codes, scales, orc.dequantize_mx16(codes, scales, len(vals))
+
+
+def test_mx16_scale_rule_at_binade_edges(orc):
+    # largest magnitude a: scale 2^(floor(log2 a) - 2)
+    for a, e in ((1.0, -2), (1.99, -2), (2.0, -1), (6.0, 0), (7.0, 0), (8.0, 1), (0.375, -4), (1000.0, 7)):
+        a = float(np.float32(a))
+        vals = [0.0] * 15 + [a]
+        codes, scales, deq = _mx_group(orc, vals)
+        assert scales[0] == e + 127, (a, scales[0])
+    # 7 / 1 is past 6: it saturates to 6 (the MX rule clamps)
+    assert _mx_group(orc, [0.0] * 15 + [7.0])[2][15] == 6.0
+    # an all-zero group: byte 0, zero codes
+    codes, scales, deq = _mx_group(orc, [0.0] * 16)
+    assert scales[0] == 0 and not codes.any() and not deq.any()
+
+
+def test_mx16_integers_and_round_trip(orc):
+    # a group holding -8..8 has scale 2: x / 2 in steps of 0.5, nearest E2M1
+    # value with ties to the even code, worked out by hand
+    ints = np.arange(-8, 8).astype(np.float32)               # -8..7: one group, largest magnitude 8
+    codes, scales, deq = _mx_group(orc, ints)
+    want = {0: 0, 1: 1, 2: 2, 3: 3, 4: 4, 5: 4, 6: 6, 7: 8, 8: 8}
+    assert scales[0] == 128
+    assert [deq[i] for i in range(16)] == [float(np.sign(v)) * want[abs(int(v))] for v in ints]
+    # values already on the grid of their group survive exactly
+    g = np.random.default_rng(30)
+    for _ in range(200):
+        e = int(g.integers(-6, 6))
+        grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
+        v = g.choice(grid, 16) * g.choice([-1, 1], 16) * 2.0 ** e
+        v[0] = 6 * 2.0 ** e                                  # pins the group's scale
+        assert np.array_equal(_mx_group(orc, v)[2], v)
+    # 128 dims take 64 code bytes + 8 scale bytes = 72 B, the pages' figure
+    codes, scales = orc.quantize_mx16(_bf16_int(np.ones(128, np.float32)))
+    assert codes.nbytes + scales.nbytes == 72 == orc.fp4_row_bytes(128, 16, 1)
+
+
+def test_fp4_cache_scores_use_the_dequantised_keys(orc):
+    g = np.random.default_rng(31)
+    n, Di = 300, 64
+    keys = _bf16_int(g.integers(-8, 9, (n, Di)))
+    c = orc.Cache.empty(1, n, 576, 64, 32, 0, Di, idx_format=1)
+    orc.kv_append(c, np.zeros((n, 576), np.float32), np.array([0, n], np.int32), None, keys)
+    for j in (0, 7, 299):
+        codes, scales = orc.quantize_mx16(keys[j])
+        assert np.array_equal(c.idx_keys[0, j], codes) and np.array_equal(c.idx_scales[0, j], scales)
+    # the dequantised keys are bf16-exact: scoring them as a bf16 plane gives the same ranking
+    deq = np.stack([orc.dequantize_mx16(c.idx_keys[0, j], c.idx_scales[0, j], Di) for j in range(n)])
+    q = _bf16_int(g.integers(-8, 9, (1, 4, Di)))
+    b16 = _bf16_int(deq.astype(np.float32))
+    assert np.array_equal(orc.indexer_topk(c, q, 50)[0], orc.topk(orc.indexer_scores(b16, q[0]), 50))
+    assert not np.array_equal(orc.indexer_topk(c, q, 50)[0], orc.topk(orc.indexer_scores(keys, q[0]), 50))
+
+
 # ---------------------------------------------------------------- candidate pool
 
 def _pool_by_subsets(s, block, nb):
