@@ -57,6 +57,11 @@ int check_cache(const cskv_cache *c)
             CSKV_EINVAL, "cache plane pointer is NULL");
     REQUIRE((c->v_group > 0) == (c->v_codes != nullptr) && (c->v_group > 0) == (c->v_scales != nullptr),
             CSKV_EINVAL, "value plane pointers must be set exactly when v_group > 0");
+    REQUIRE(c->idx_format == CSKV_IDX_BF16 || c->idx_format == CSKV_IDX_FP4, CSKV_EUNSUPPORTED,
+            "idx_format %d: CSKV_IDX_BF16 or CSKV_IDX_FP4", c->idx_format);
+    REQUIRE((c->idx_format == CSKV_IDX_FP4) == (c->idx_scales != nullptr), CSKV_EINVAL,
+            "idx_scales must be set exactly for CSKV_IDX_FP4");
+    REQUIRE(!c->idx_scales || aligned(c->idx_scales, 16), CSKV_EINVAL, "idx_scales must be 16-byte aligned");
     REQUIRE(aligned(c->k_codes, 16) && aligned(c->k_scales, 16) && aligned(c->idx_keys, 16) &&
                 aligned(c->n_tokens, 16) && aligned(c->pending, 16) && aligned(c->status, 4) &&
                 (!c->v_codes || aligned(c->v_codes, 16)) && (!c->v_scales || aligned(c->v_scales, 16)),

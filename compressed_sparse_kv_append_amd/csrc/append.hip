@@ -201,6 +201,32 @@ __device__ void quantize_channel(float x, int t, int n, int g, uint8_t *codes_ro
     if (live && (t % g) == 0) scales_row[t / g] = s;
 }
 
+// Indexer key in the pages' FP4 form [P2 四、"890 字节是怎么算出来的" (72 B per
+// 128-dim key); P2 四、"P4 main KV" (E2M1, one 8-bit scale per 16 channels)]:
+// thread t < Di holds dim t of the bf16 row.  Each 16-dim group takes the
+// E8M0 scale 2^(floor(log2 amax) - 2) (byte 0 and zero codes when amax = 0);
+// codes are the nearest E2M1 of x / scale (exact: a power of two).  Called by
+// whole waves (Di is a multiple of 64).
+__device__ void quantize_idx_fp4(float x, int t, uint8_t *codes_row, uint8_t *scales_row)
+{
+    float a = fabsf(x);
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) a = fmaxf(a, __shfl_xor(a, off));
+    int e = -127;
+    if (a > 0.0f) {
+        int ex;
+        (void)frexpf(a, &ex);                      // a = m 2^ex, 0.5 <= m < 1
+        e = ex - 1 - 2;
+        e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    }
+    uint32_t code = a > 0.0f ? e2m1_code(ldexpf(x, -e)) : 0u;
+    code |= __shfl_down(code, 1) << 4;             // 2 codes (even t)
+    code |= __shfl_down(code, 2) << 8;             // 4 codes
+    code |= __shfl_down(code, 4) << 16;            // 8 codes
+    if ((t & 7) == 0) *reinterpret_cast<uint32_t *>(codes_row + (t >> 1)) = code;
+    if ((t & 15) == 0) scales_row[t >> 4] = (uint8_t)(e + 127);
+}
+
 // Sequence b after its rows are quantised: store the trailing odd token,
 // advance n_tokens, or flag a rejected sequence.  p is n_tokens[b] as the
 // append found it.  Returns the sequence's token count afterwards.
@@ -263,7 +289,14 @@ __global__ __launch_bounds__(kAppendThreads) void quantize_kernel(AppendArgs a)
             quantize_channel(e, t, dv, c.v_group, c.v_codes + slot * (dv / 2),
                              c.v_scales + slot * (dv / c.v_group), wave_max);
         }
-        if (t < c.idx_dim) c.idx_keys[slot * c.idx_dim + t] = a.idx_rows[(size_t)r * c.idx_dim + t];
+        if (c.idx_format == CSKV_IDX_FP4) {
+            if (t < c.idx_dim)                      // whole waves: idx_dim is 64 or 128
+                quantize_idx_fp4(bf16_bits_to_f32(a.idx_rows[(size_t)r * c.idx_dim + t]), t,
+                                 reinterpret_cast<uint8_t *>(c.idx_keys) + slot * (c.idx_dim / 2),
+                                 c.idx_scales + slot * (c.idx_dim / 16));
+        } else if (t < c.idx_dim) {
+            c.idx_keys[slot * c.idx_dim + t] = a.idx_rows[(size_t)r * c.idx_dim + t];
+        }
     }
     if (kFinalize) {
         const int b = (int)r;

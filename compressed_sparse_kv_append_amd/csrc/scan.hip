@@ -49,6 +49,9 @@ struct ScanArgs {
     const int32_t *pool;
     int pool_blocks;
     uint2 *out_pairs;
+    // FP4 indexer keys: keys holds E2M1 codes (DI/2 bytes per row), scales
+    // one E8M0 byte per 16 dims
+    const uint8_t *idx_scales;
 };
 
 typedef __attribute__((address_space(1))) void global_void_t;
@@ -203,6 +206,195 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
+// E8M0 byte -> the fp32 power of two it encodes (byte 0: 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b)
+{
+    return __uint_as_float(b ? b << 23 : 0x00400000u);
+}
+
+// Eight E2M1 codes (one word, low nibble first) times a power of two ->
+// eight bf16 values; exact, E2M1 values having at most two significant bits.
+__device__ __forceinline__ u32x4_t fp4x8_scaled_to_bf16x8(uint32_t w, float scale)
+{
+    u32x4_t r;
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+    return r;
+}
+
+// The scan over FP4 indexer keys (E2M1 codes + one E8M0 scale per 16 dims,
+// the pages' 72-byte key at DI = 128).  Tiles of 64 keys: a tile's codes
+// (DI/2 bytes per key, XOR-swizzled 16-byte chunks as in the bf16 scan) and
+// scales (DI/16 bytes per key) go by DMA into the wave's LDS slot.  The
+// contraction order is permuted: at step s, lane group g holds dims
+// 8 (kSteps g + s) .. + 7, so a lane's code words for all steps are one
+// contiguous piece of the key row (one LDS read) and its scale bytes are
+// adjacent; the query is loaded in the same order.  Each 16-key column tile
+// is converted to bf16 by the hardware FP4 conversion, which applies the
+// group's power-of-two scale exactly, and goes through the same bf16 MFMA
+// and epilogue as the bf16 scan.
+template <int DI, int MT, bool POOL>
+__global__ __launch_bounds__(kScanThreads) void indexer_scan_fp4_kernel(ScanArgs a)
+{
+    constexpr int kSteps = DI / 32;
+    constexpr int kTileKeys = 64;
+    constexpr int kCodeBytes = DI / 2;                   // per key
+    constexpr int kScaleBytes = DI / 16;                 // per key
+    constexpr int kChunks = kCodeBytes / 16;             // 16-byte chunks per key row
+    constexpr int kTileCode = kTileKeys * kCodeBytes;
+    constexpr int kTileScale = kTileKeys * kScaleBytes;
+    constexpr int kInstC = kTileCode / 1024;             // 16-byte DMA per lane
+    constexpr int kInstS = kTileScale / 256;             // 4-byte DMA per lane
+    constexpr int kPiece = 4 * kSteps;                   // bytes of a lane's code piece
+    static_assert(kInstC >= 1 && kInstS >= 1, "tile sizes");
+    __shared__ __attribute__((aligned(16))) uint8_t ring[kScanWaves][kRing][kTileCode + kTileScale];
+    __shared__ int32_t pool_rows[POOL ? kPoolChunkMax : 1];   // entry of each position of the run
+    __shared__ __attribute__((aligned(16))) float hws[16 * MT];  // head weights (0 past the heads)
+
+    const int b = blockIdx.y;
+    const int64_t E = entries_of(a.n_tokens, b, a.capacity);
+    const int64_t N = POOL ? (E > 0 ? (int64_t)a.pool_blocks * a.block : 0) : E;
+    const int64_t e_begin = (int64_t)blockIdx.x * a.chunk;
+    if (e_begin >= N) return;
+    const int64_t e_end = N < e_begin + a.chunk ? N : e_begin + a.chunk;
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    const int col = lane & 15, grp = lane >> 4;
+    if constexpr (POOL) {
+        const int32_t *pl = a.pool + (size_t)b * a.pool_blocks;
+        for (int i = threadIdx.x; i < e_end - e_begin; i += kScanThreads) {
+            const int64_t p = e_begin + i;
+            const int32_t blk = pl[p / a.block];
+            const int64_t e = blk >= 0 ? (int64_t)blk * a.block + p % a.block : -1;
+            pool_rows[i] = e < E ? (int32_t)e : -1;
+        }
+    }
+    if (threadIdx.x < 16 * MT) {
+        const int h = threadIdx.x;
+        hws[h] = h < a.heads ? (a.head_w ? a.head_w[(size_t)b * a.heads + h] : 1.0f) : 0.0f;
+    }
+    __syncthreads();
+
+    const int n_tiles = (int)((e_end - e_begin + kTileKeys - 1) / kTileKeys);
+    const int my_n = n_tiles > w ? (n_tiles - w + kScanWaves - 1) / kScanWaves : 0;
+    const uint8_t *kb = reinterpret_cast<const uint8_t *>(a.keys) + (size_t)b * a.capacity * kCodeBytes;
+    const uint8_t *sb = a.idx_scales + (size_t)b * a.capacity * kScaleBytes;
+
+    // cache row of position e (clamped into the run; positions without an
+    // entry read row 0 and are dropped)
+    auto row_of = [&](int64_t e) -> int64_t {
+        e = e < e_end ? e : e_end - 1;
+        if constexpr (POOL) {
+            const int32_t pe = pool_rows[e - e_begin];
+            return pe >= 0 ? pe : 0;
+        } else {
+            return e;
+        }
+    };
+    auto issue = [&](int i) {
+        const int64_t t0 = e_begin + (int64_t)(w + kScanWaves * i) * kTileKeys;
+        uint8_t *slot = &ring[w][i % kRing][0];
+#pragma unroll
+        for (int s = 0; s < kInstC; ++s) {
+            const int u = 64 * s + lane, r = u / kChunks, p = u % kChunks, c = p ^ (r % kChunks);
+            __builtin_amdgcn_global_load_lds((global_void_t *)(kb + (size_t)row_of(t0 + r) * kCodeBytes + 16 * c),
+                                             (lds_void_t *)(slot + 1024 * s), 16, 0, kNonTemporal);
+        }
+#pragma unroll
+        for (int s = 0; s < kInstS; ++s) {
+            const int u = 4 * (64 * s + lane), r = u / kScaleBytes, o = u % kScaleBytes;
+            __builtin_amdgcn_global_load_lds((global_void_t *)(sb + (size_t)row_of(t0 + r) * kScaleBytes + o),
+                                             (lds_void_t *)(slot + kTileCode + 256 * s), 4, 0, kNonTemporal);
+        }
+    };
+
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) issue(i);
+
+    u32x4_t qa[MT][kSteps];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int head = 16 * mt + col;
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            if (head < a.heads)
+                v = *reinterpret_cast<const u32x4_t *>(a.q + ((size_t)b * a.heads + head) * DI +
+                                                       8 * (kSteps * grp + s));
+            qa[mt][s] = v;
+        }
+    }
+
+    uint32_t *ok = a.out_keys ? a.out_keys + (size_t)b * a.key_stride : nullptr;
+    for (int i = 0; i < my_n; ++i) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm((kInstC + kInstS) * (kRing - 1)));
+        const uint8_t *slot = &ring[w][i % kRing][0];
+        uint32_t cw[4][kSteps];
+        uint32_t sw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int key = 16 * j + col;
+            const int byte0 = kPiece * grp, p = (byte0 >> 4) ^ (key % kChunks);
+            const uint8_t *src = slot + key * kCodeBytes + 16 * p + (byte0 & 15);
+            if constexpr (kSteps == 4) {
+                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(src);
+                cw[j][0] = v[0]; cw[j][1] = v[1]; cw[j][2] = v[2]; cw[j][3] = v[3];
+            } else {
+                const uint2 v = *reinterpret_cast<const uint2 *>(src);
+                cw[j][0] = v.x; cw[j][1] = v.y;
+            }
+            const uint8_t *ss = slot + kTileCode + key * kScaleBytes;
+            sw[j] = kSteps == 4 ? (uint32_t)*reinterpret_cast<const uint16_t *>(ss + 2 * grp) : (uint32_t)ss[grp];
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);      // slot read before it is refilled
+        issue(i + kRing);
+        const int64_t t0 = e_begin + (int64_t)(w + kScanWaves * i) * kTileKeys;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f32x4_t acc[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < kSteps; ++s) {
+                const uint32_t byte = kSteps == 4 ? (sw[j] >> (8 * (s >> 1))) & 0xFFu : sw[j];
+                const u32x4_t bop = fp4x8_scaled_to_bf16x8(cw[j][s], e8m0_to_f32(byte));
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16x16x32(qa[mt][s], bop, acc[mt]);
+            }
+            float part = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const float4 hw = *reinterpret_cast<const float4 *>(&hws[16 * mt + 4 * grp]);
+                part += hw.x * fmaxf(acc[mt][0], 0.f);
+                part += hw.y * fmaxf(acc[mt][1], 0.f);
+                part += hw.z * fmaxf(acc[mt][2], 0.f);
+                part += hw.w * fmaxf(acc[mt][3], 0.f);
+            }
+            part += __shfl_xor(part, 16);
+            part += __shfl_xor(part, 32);
+            const int64_t e = t0 + 16 * j + lane;
+            if constexpr (POOL) {
+                if (lane < 16 && e < e_end) {
+                    const int32_t pe = pool_rows[e - e_begin];
+                    a.out_pairs[(size_t)b * a.pool_blocks * a.block + e] =
+                        pe >= 0 ? make_uint2(score_key(part), (uint32_t)pe) : make_uint2(0u, 0xFFFFFFFFu);
+                }
+            } else {
+                const uint32_t key = score_key(part);
+                if (lane < 16 && e < e_end) ok[e] = key;
+                if (a.block_keys) {
+                    uint32_t m = e < e_end ? key : 0u;
+                    for (int off = 1; off < a.block; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+                    if (lane < 16 && e < e_end && lane % a.block == 0)
+                        a.block_keys[(size_t)b * a.block_stride + e / a.block] = m;
+                }
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+}
+
 }  // namespace
 
 // Blocks per sequence and positions per block for n positions per sequence:
@@ -229,6 +421,20 @@ static void scan_dispatch(const cskv_cache &c, int heads, const ScanArgs &sa, di
     const int mt = (heads + 15) / 16;
     const TimedLaunch ts = timer_take(CSKV_KERNEL_INDEXER_SCAN);
     auto scan = [&](auto kernel) { launch_kernel(kernel, grid, dim3(kScanThreads), s, ts.start, ts.stop, sa); };
+    if (c.idx_format == CSKV_IDX_FP4) {
+        if (c.idx_dim == 128) {
+            if (mt == 4) scan(indexer_scan_fp4_kernel<128, 4, POOL>);
+            else if (mt == 3) scan(indexer_scan_fp4_kernel<128, 3, POOL>);
+            else if (mt == 2) scan(indexer_scan_fp4_kernel<128, 2, POOL>);
+            else scan(indexer_scan_fp4_kernel<128, 1, POOL>);
+        } else {
+            if (mt == 4) scan(indexer_scan_fp4_kernel<64, 4, POOL>);
+            else if (mt == 3) scan(indexer_scan_fp4_kernel<64, 3, POOL>);
+            else if (mt == 2) scan(indexer_scan_fp4_kernel<64, 2, POOL>);
+            else scan(indexer_scan_fp4_kernel<64, 1, POOL>);
+        }
+        return;
+    }
     if (c.idx_dim == 128) {
         if (mt == 4) scan(indexer_scan_kernel<128, 4, POOL>);
         else if (mt == 3) scan(indexer_scan_kernel<128, 3, POOL>);
@@ -247,7 +453,7 @@ void launch_indexer_scan(const cskv_cache &c, const uint16_t *q_idx, int heads, 
 {
     const int chunk = scan_chunk(c.batch, (size_t)c.capacity, (size_t)1 << 30);
     ScanArgs sa{c.idx_keys, c.n_tokens, q_idx, head_w, keys, c.capacity, heads, chunk, score_key_stride(c),
-                block_keys, block_stride, block, nullptr, 0, nullptr};
+                block_keys, block_stride, block, nullptr, 0, nullptr, c.idx_scales};
     dim3 grid((unsigned)(((size_t)c.capacity + chunk - 1) / chunk), (unsigned)c.batch);
     scan_dispatch<false>(c, heads, sa, grid, s);
 }
@@ -258,7 +464,7 @@ void launch_pool_scan(const cskv_cache &c, const uint16_t *q_idx, int heads, con
     const size_t n = (size_t)pool_blocks * block;
     const int chunk = scan_chunk(c.batch, n, kPoolChunkMax);
     ScanArgs sa{c.idx_keys, c.n_tokens, q_idx, head_w, nullptr, c.capacity, heads, chunk, 0,
-                nullptr, 0, block, pool, pool_blocks, pairs};
+                nullptr, 0, block, pool, pool_blocks, pairs, c.idx_scales};
     dim3 grid((unsigned)((n + chunk - 1) / chunk), (unsigned)c.batch);
     scan_dispatch<true>(c, heads, sa, grid, s);
 }

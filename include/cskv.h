@@ -72,8 +72,19 @@ extern "C" {
  *   v_codes  u8  [batch][capacity][(dim-rope_dim)/2]
  *   v_scales f32 [batch][capacity][(dim-rope_dim)/v_group]
  * otherwise values are read from the key plane (v_codes/v_scales NULL).
- * The indexer key of each entry [P2 四、"CSA2：三种模式"] is kept in bf16:
+ * The indexer key of each entry [P2 四、"CSA2：三种模式"] is kept in bf16
+ * (idx_format CSKV_IDX_BF16):
  *   idx_keys bf16 [batch][capacity][idx_dim]
+ * or in the pages' FP4 form (idx_format CSKV_IDX_FP4) [P2 四、"890 字节是怎么
+ * 算出来的" (a 128-dim indexer key in FP4 is 72 B); P2 四、"P4 main KV" (E2M1
+ * with one 8-bit scale per 16 channels, OCP MXFP4)]: E2M1 codes and one E8M0
+ * scale byte (the power of two 2^(byte-127)) per 16 dims,
+ *   idx_keys   u8 [batch][capacity][idx_dim/2]   (the pointer reinterpreted)
+ *   idx_scales u8 [batch][capacity][idx_dim/16]
+ * scale = 2^(floor(log2 amax) - 2) of the group's bf16 inputs (byte 0 and
+ * zero codes for an all-zero group), codes = nearest E2M1 of x / scale,
+ * ties to even, saturating at 6.  Appends take bf16 indexer rows in both
+ * formats; scores use the dequantised keys.
  * Sequence state:
  *   n_tokens i32 [batch]  tokens appended so far; entries = n_tokens / 2
  *   pending  f32 [batch][dim]  the odd token waiting for its pair
@@ -81,6 +92,8 @@ extern "C" {
  * Supported here: dim 576, rope_dim 64, k_group 32 or 64, v_group 0, 32, 64
  * or 128, idx_dim 64 or 128, capacity <= 2^26.
  */
+#define CSKV_IDX_BF16 0
+#define CSKV_IDX_FP4 1
 typedef struct cskv_cache {
     int32_t batch, capacity, dim, rope_dim, k_group, v_group, idx_dim;
     uint8_t *k_codes;
@@ -91,6 +104,8 @@ typedef struct cskv_cache {
     int32_t *n_tokens;
     float *pending;
     int32_t *status;
+    int32_t idx_format;      /* CSKV_IDX_BF16 or CSKV_IDX_FP4 */
+    uint8_t *idx_scales;     /* CSKV_IDX_FP4 only, else NULL */
 } cskv_cache;
 
 /*

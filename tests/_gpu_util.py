@@ -23,10 +23,10 @@ def host(t: torch.Tensor) -> np.ndarray:
     return a.view(np.uint16) if a.dtype == np.int16 else a
 
 
-def pair(batch, capacity, k_group, v_group, idx_dim):
+def pair(batch, capacity, k_group, v_group, idx_dim, idx_format=0):
     """An empty device cache and its empty host mirror with the same shape."""
-    g = ck.Cache.allocate(batch, capacity, k_group, v_group, idx_dim)
-    h = orc.Cache.empty(batch, capacity, 576, 64, k_group, v_group, idx_dim)
+    g = ck.Cache.allocate(batch, capacity, k_group, v_group, idx_dim, idx_format=idx_format)
+    h = orc.Cache.empty(batch, capacity, 576, 64, k_group, v_group, idx_dim, idx_format=idx_format)
     return g, h
 
 
@@ -37,7 +37,7 @@ def assert_cache_equal(g: ck.Cache, h: orc.Cache, seqs=None, check_pending=True)
     assert np.array_equal(nt[seqs], h.n_tokens[seqs]), (nt[seqs], h.n_tokens[seqs])
     for b in seqs:
         e = int(min(h.n_tokens[b] // 2, h.capacity))
-        for name in ("k_codes", "k_scales", "v_codes", "v_scales", "idx_keys"):
+        for name in ("k_codes", "k_scales", "v_codes", "v_scales", "idx_keys", "idx_scales"):
             gt = getattr(g, name)
             if gt is None:
                 continue

@@ -129,7 +129,7 @@ def _step(ck, orc, w, gc, mirrors, st, W_h, pool=None):
             [r[sl] for r in st.swa_row], w.topk, scale, pool=pool)
         e = int(hc.entries()[0])
         assert int(host(gc.n_tokens)[b]) == int(hc.n_tokens[0])
-        for name in ("k_codes", "k_scales", "v_codes", "v_scales", "idx_keys"):
+        for name in ("k_codes", "k_scales", "v_codes", "v_scales", "idx_keys", "idx_scales"):
             gt = getattr(gc, name)
             if gt is None:
                 continue
