@@ -61,6 +61,8 @@ def parse():
     p.add_argument("--graph", action="store_true", help="time HIP graph replays of the step")
     p.add_argument("--scan-sample-every", type=int, default=4)
     p.add_argument("--copy-probe", type=int, default=0, help="MiB copied by a plain device copy")
+    p.add_argument("--idx-format", choices=("bf16", "fp4"), default="bf16",
+                   help="indexer-key storage: bf16, or the pages' FP4 form (E2M1 + E8M0 per 16 dims)")
     p.add_argument("--pool", default="", help="pool_blocks,pool_block: the hierarchical indexer's candidate "
                    "pool in a layer-group workload (reindex layers select inside it)")
     return p.parse_args()
@@ -77,11 +79,12 @@ def copy_probe(mib: int):
     print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
 
 
-def build_replicas(ck, synth, w, cap, dev, n):
+def build_replicas(ck, synth, w, cap, dev, n, idx_format=0):
     """Entries-mode build of n identical cache replicas, one sequence at a time
     (each sequence's entries are drawn once and appended to every replica)."""
     import torch
-    reps = [ck.Cache.allocate(w.batch, cap, w.k_group, w.v_group, w.idx_dim) for _ in range(n)]
+    reps = [ck.Cache.allocate(w.batch, cap, w.k_group, w.v_group, w.idx_dim, idx_format=idx_format)
+            for _ in range(n)]
     for b in range(w.batch):
         ents = dev(synth.cache_entries(w, b))
         keys = dev(synth.cache_idx_keys(w, b))
@@ -110,7 +113,7 @@ def scans_per_step(w, pool):
     return full, pooled
 
 
-def step_bytes(w, entries: float, pool=None) -> dict:
+def step_bytes(w, entries: float, pool=None, idx_fp4=False) -> dict:
     """Algorithmic bytes of one step (whole batch): every plane read or written
     once by the method's definition; score arrays are not counted.  Scans: the
     whole indexer-key plane per full scan, the pooled positions' keys per
@@ -123,8 +126,9 @@ def step_bytes(w, entries: float, pool=None) -> dict:
     L = len(w.layers)
     sel = sum(1 for m in w.layers if m != "reuse")
     pool_pos = min(entries, pool[0] * pool[1]) if pool else 0
+    key_bytes = Di // 2 + Di // 16 if idx_fp4 else 2 * Di
     parts = {
-        "indexer_keys": B * (full * entries + pooled * pool_pos) * Di * 2,
+        "indexer_keys": B * (full * entries + pooled * pool_pos) * key_bytes,
         "indexer_q": B * sel * w.idx_heads * Di * 2,
         "gather": L * B * min(w.topk, entries) * entry_fp4,
         "window": L * B * w.window * D * 2,
@@ -133,7 +137,7 @@ def step_bytes(w, entries: float, pool=None) -> dict:
         "indices": (sel + L) * B * w.topk * 4,
         # one token per sequence; a pair completes every other step, then the
         # compressor weights are read and one entry + indexer key written
-        "append": B * (D * 4 * 2 + 0.5 * (entry_fp4 + Di * 2)) + 0.5 * D * 2 * D * 4,
+        "append": B * (D * 4 * 2 + 0.5 * (entry_fp4 + key_bytes)) + 0.5 * D * 2 * D * 4,
     }
     parts["total"] = sum(parts.values())
     return parts
@@ -233,9 +237,9 @@ def main():
         return torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).cuda()
 
     t0 = time.time()
-    reps = build_replicas(ck, synth, w, cap, dev, a.replicas)
-    log(f"built {a.replicas} cache replicas in {time.time() - t0:.1f}s "
-        f"({reps[0].entry_bytes()} B/entry incl. indexer key)")
+    idx_fp4 = a.idx_format == "fp4"
+    reps = build_replicas(ck, synth, w, cap, dev, a.replicas, ck.IDX_FP4 if idx_fp4 else ck.IDX_BF16)
+    log(f"built {a.replicas} cache replicas in {time.time() - t0:.1f}s (indexer keys {a.idx_format})")
     st = synth.step_inputs(w, 0)
     W = dev(synth.w_comp(w))
     scale = 1 / math.sqrt(w.dim)
@@ -337,7 +341,7 @@ def main():
 
     # mean entries per sequence over the timed steps
     entries_mean = float(0.5 * (ent_before + ent_after))
-    sb = step_bytes(w, entries_mean, pool)
+    sb = step_bytes(w, entries_mean, pool, idx_fp4)
     n_full, n_pooled = scans_per_step(w, pool)
     scan_bytes = (sb["indexer_keys"] + sb["indexer_q"]) / (n_full + n_pooled)   # per launch, averaged
     scan = live if live is not None else kern["indexer_scan"]
@@ -362,11 +366,13 @@ def main():
                    "idx_heads": w.idx_heads, "idx_dim": w.idx_dim, "q_heads": w.q_heads,
                    "topk": w.topk, "window": w.window, "replicas": a.replicas,
                    "launch": "hip_graph" if a.graph else "eager", "layers": list(w.layers),
+                   "idx_storage": "e2m1+e8m0/16" if idx_fp4 else "bf16",
                    "pool": list(pool) if pool else None,
                    "tokens_per_s": round(steps_per_s * B, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": pmc_traffic(), "kernel": "indexer_scan",
+                     "traffic": pmc_traffic() if (w.name == "decode_64k_b32" and not idx_fp4 and pool is None)
+                     else None, "kernel": "indexer_scan",
                      "bytes_per_launch": round(scan_bytes), "avg_us": round(scan_us, 2),
                      "timed_launches": scan["launches"], "scans_per_step": [n_full, n_pooled],
                      "timing": ("hip events in the timed region, 1 step in %d" % every) if live is not None

@@ -76,8 +76,15 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
     constexpr int kChunks = kRowBytes / 16;    // 16-byte chunks per key row
     constexpr int kTileBytes = 16 * kRowBytes;
     constexpr int kInst = kTileBytes / 1024;   // loads per tile (64 lanes x 16 B)
-    __shared__ __attribute__((aligned(16))) uint8_t ring[kScanWaves][kRing][kTileBytes];
-    __shared__ int32_t pool_rows[POOL ? kPoolChunkMax : 1];   // entry of each position of the run
+    // One LDS array: the wave rings, then (POOL) the entry of each position of
+    // the run.  Reads of a different LDS object inside the loop would make the
+    // compiler wait for every outstanding LDS DMA (vmcnt(0)) before them, which
+    // serialises the ring; reads of the DMA's own object are left to the
+    // explicit waits below.
+    constexpr int kRingBytes = kScanWaves * kRing * kTileBytes;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kRingBytes + (POOL ? 4 * kPoolChunkMax : 0)];
+    auto ring = reinterpret_cast<uint8_t (*)[kRing][kTileBytes]>(lds);
+    int32_t *pool_rows = reinterpret_cast<int32_t *>(lds + kRingBytes);
 
     const int b = blockIdx.y;
     const int64_t E = entries_of(a.n_tokens, b, a.capacity);
@@ -249,9 +256,13 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_fp4_kernel(ScanArgs
     constexpr int kInstS = kTileScale / 256;             // 4-byte DMA per lane
     constexpr int kPiece = 4 * kSteps;                   // bytes of a lane's code piece
     static_assert(kInstC >= 1 && kInstS >= 1, "tile sizes");
-    __shared__ __attribute__((aligned(16))) uint8_t ring[kScanWaves][kRing][kTileCode + kTileScale];
-    __shared__ int32_t pool_rows[POOL ? kPoolChunkMax : 1];   // entry of each position of the run
-    __shared__ __attribute__((aligned(16))) float hws[16 * MT];  // head weights (0 past the heads)
+    // One LDS array (see the bf16 scan): the wave rings, the head weights (0
+    // past the heads), then (POOL) the entry of each position of the run.
+    constexpr int kRingBytes = kScanWaves * kRing * (kTileCode + kTileScale);
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kRingBytes + 64 * MT + (POOL ? 4 * kPoolChunkMax : 0)];
+    auto ring = reinterpret_cast<uint8_t (*)[kRing][kTileCode + kTileScale]>(lds);
+    float *hws = reinterpret_cast<float *>(lds + kRingBytes);
+    int32_t *pool_rows = reinterpret_cast<int32_t *>(lds + kRingBytes + 64 * MT);
 
     const int b = blockIdx.y;
     const int64_t E = entries_of(a.n_tokens, b, a.capacity);
