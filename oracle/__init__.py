@@ -52,7 +52,8 @@ class _Cache(C.Structure):
                 ("v_codes", C.POINTER(C.c_uint8)), ("v_scales", C.POINTER(C.c_float)),
                 ("idx_keys", C.POINTER(C.c_uint16)), ("n_tokens", C.POINTER(C.c_int32)),
                 ("pending", C.POINTER(C.c_float)), ("status", C.POINTER(C.c_int32)),
-                ("idx_format", C.c_int32), ("idx_scales", C.POINTER(C.c_uint8))]
+                ("idx_format", C.c_int32), ("idx_scales", C.POINTER(C.c_uint8)),
+                ("swa_format", C.c_int32)]
 
 
 def _declare(L):
@@ -72,6 +73,12 @@ def _declare(L):
     L.orc_bf16_from_f32.argtypes = [C.c_float]
     L.orc_bf16_value.restype = f64
     L.orc_bf16_value.argtypes = [C.c_uint16]
+    L.orc_e4m3_value.restype = f64
+    L.orc_e4m3_value.argtypes = [C.c_uint8]
+    L.orc_e4m3_encode.restype = C.c_uint8
+    L.orc_e4m3_encode.argtypes = [C.c_float]
+    L.orc_swa_append_fp8.restype = None
+    L.orc_swa_append_fp8.argtypes = [P(C.c_uint8), C.c_int, C.c_int, C.c_int, P(C.c_float), P(i32), P(i32)]
     L.orc_e8m0_value.restype = f64
     L.orc_e8m0_value.argtypes = [C.c_uint8]
     L.orc_quantize_mx16.restype = None
@@ -260,10 +267,11 @@ class Cache:
     status: np.ndarray
     idx_format: int = 0
     idx_scales: Optional[np.ndarray] = None   # E8M0 u8 [B][cap][Di/16] (idx_format 1)
+    swa_format: int = 0                        # window rings used with this cache: 0 bf16, 1 FP8 E4M3
 
     @classmethod
     def empty(cls, batch, capacity, dim=576, rope_dim=64, k_group=32, v_group=0, idx_dim=128,
-              idx_format=0):
+              idx_format=0, swa_format=0):
         Dv = dim - rope_dim
         fp4 = idx_format == 1
         return cls(batch, capacity, dim, rope_dim, k_group, v_group, idx_dim,
@@ -275,7 +283,7 @@ class Cache:
                    else np.zeros((batch, capacity, idx_dim), np.uint16),
                    np.zeros(batch, np.int32), np.zeros((batch, dim), np.float32),
                    np.zeros(1, np.int32), idx_format,
-                   np.zeros((batch, capacity, idx_dim // 16), np.uint8) if fp4 else None)
+                   np.zeros((batch, capacity, idx_dim // 16), np.uint8) if fp4 else None, swa_format)
 
     def _c(self) -> _Cache:
         return _Cache(self.batch, self.capacity, self.dim, self.rope_dim, self.k_group,
@@ -284,7 +292,7 @@ class Cache:
                       _p(self.v_codes, C.c_uint8), _p(self.v_scales, C.c_float),
                       _p(self.idx_keys, C.c_uint16), _p(self.n_tokens, C.c_int32),
                       _p(self.pending, C.c_float), _p(self.status, C.c_int32),
-                      self.idx_format, _p(self.idx_scales, C.c_uint8))
+                      self.idx_format, _p(self.idx_scales, C.c_uint8), self.swa_format)
 
     def entries(self) -> np.ndarray:
         return np.clip(self.n_tokens // 2, 0, self.capacity)
@@ -302,14 +310,26 @@ def kv_append(cache: Cache, tokens, cu_new, w_comp, idx_rows) -> None:
 
 
 def swa_append(ring, rows, cu_new, end_pos) -> None:
-    """ring: bf16 bits [B, W, dim] updated in place."""
-    assert ring.dtype == np.uint16 and ring.flags.c_contiguous
+    """ring: bf16 bits (uint16) or FP8 E4M3 bytes (uint8) [B, W, dim], updated in place."""
+    assert ring.dtype in (np.uint16, np.uint8) and ring.flags.c_contiguous
     B, W, D = ring.shape
     rows = _f32(rows).reshape(-1, D)
     cu = np.ascontiguousarray(cu_new, np.int32)
     ep = np.ascontiguousarray(end_pos, np.int32)
-    lib().orc_swa_append(_p(ring, C.c_uint16), B, W, D, _p(rows, C.c_float), _p(cu, C.c_int32),
-                         _p(ep, C.c_int32))
+    if ring.dtype == np.uint8:
+        lib().orc_swa_append_fp8(_p(ring, C.c_uint8), B, W, D, _p(rows, C.c_float), _p(cu, C.c_int32),
+                                 _p(ep, C.c_int32))
+    else:
+        lib().orc_swa_append(_p(ring, C.c_uint16), B, W, D, _p(rows, C.c_float), _p(cu, C.c_int32),
+                             _p(ep, C.c_int32))
+
+
+def e4m3_value(v: int) -> float:
+    return float(lib().orc_e4m3_value(v))
+
+
+def e4m3_encode(x: float) -> int:
+    return int(lib().orc_e4m3_encode(float(x)))
 
 
 def indexer_topk(cache: Cache, q_idx, k, head_w=None) -> np.ndarray:
@@ -349,14 +369,14 @@ def sparse_attn(cache: Cache, q, idx, swa, scale, swa_len=None):
     B, H, D = q.shape
     idx = np.ascontiguousarray(idx, np.int32)
     k = idx.shape[1]
-    swa = np.ascontiguousarray(swa, np.uint16)
+    swa = np.ascontiguousarray(swa, np.uint8 if cache.swa_format == 1 else np.uint16)
     W = swa.shape[1]
     sl = None if swa_len is None else np.ascontiguousarray(swa_len, np.int32)
     out = np.empty((B, H, cache.dim - cache.rope_dim), np.float64)
     lse = np.empty((B, H), np.float64)
     c = cache._c()
     lib().orc_sparse_attn(C.byref(c), _p(q, C.c_float), H, _p(idx, C.c_int32), k,
-                          _p(swa, C.c_uint16), W, _p(sl, C.c_int32), float(scale),
+                          swa.ctypes.data_as(C.POINTER(C.c_uint16)), W, _p(sl, C.c_int32), float(scale),
                           _p(out, C.c_double), _p(lse, C.c_double))
     return out, lse
 

@@ -163,6 +163,51 @@ void orc_dequantize_row(const uint8_t *packed, const float *scales, int n, int g
 
 /* ------------------------------------------------------------ cache append */
 
+/* ------------------------------------------------------------ FP8 window rows */
+
+double orc_e4m3_value(uint8_t v)
+{
+    const int sign = v >> 7, ex = (v >> 3) & 15, man = v & 7;
+    if (ex == 15 && man == 7) return NAN;
+    double mag = ex == 0 ? ldexp((double)man, -9) : ldexp(1.0 + man / 8.0, ex - 7);
+    return sign ? -mag : mag;
+}
+
+uint8_t orc_e4m3_encode(float x)
+{
+    assert(isfinite(x));
+    const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    double mag = fabs((double)x);
+    if (mag >= 448.0) return sign | 0x7E;
+    /* the nearest of the 127 non-negative finite values; on a tie the even
+       mantissa (the two candidates of a tie are neighbours) */
+    unsigned best = 0;
+    double best_d = INFINITY;
+    for (unsigned c = 0; c < 0x7F; ++c) {
+        double d = fabs(mag - orc_e4m3_value((uint8_t)c));
+        if (d < best_d || (d == best_d && (c & 1u) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return sign | (uint8_t)best;
+}
+
+void orc_swa_append_fp8(uint8_t *ring, int batch, int W, int dim, const float *rows,
+                        const int32_t *cu_new, const int32_t *end_pos)
+{
+    for (int b = 0; b < batch; ++b) {
+        int64_t m = cu_new[b + 1] - cu_new[b];
+        for (int64_t q = 0; q < m; ++q) {
+            int64_t pos = (int64_t)end_pos[b] - m + q;
+            if (pos < 0 || pos < (int64_t)end_pos[b] - W) continue;
+            const float *x = rows + (size_t)(cu_new[b] + q) * dim;
+            uint8_t *dst = ring + ((size_t)b * W + (size_t)(pos % W)) * dim;
+            for (int d = 0; d < dim; ++d) dst[d] = orc_e4m3_encode(x[d]);
+        }
+    }
+}
+
 /* ------------------------------------------------------------ FP4 indexer key */
 
 double orc_e8m0_value(uint8_t s)
@@ -475,10 +520,15 @@ void orc_sparse_attn(const orc_cache *c, const float *q, int heads, const int32_
                 memcpy(V + nk * Dv, K + nk * D, sizeof(double) * (size_t)Dv);
             ++nk;
         }
-        /* keys from the sliding window (bf16 rows; values are the first Dv dims) */
+        /* keys from the sliding window (bf16 or FP8 rows; values are the first Dv dims) */
         for (int64_t s = 0; s < nswa; ++s) {
-            const uint16_t *r = swa + ((size_t)b * W + (size_t)s) * D;
-            for (int d = 0; d < D; ++d) K[nk * D + d] = orc_bf16_value(r[d]);
+            if (c->swa_format == 1) {
+                const uint8_t *r = (const uint8_t *)swa + ((size_t)b * W + (size_t)s) * D;
+                for (int d = 0; d < D; ++d) K[nk * D + d] = orc_e4m3_value(r[d]);
+            } else {
+                const uint16_t *r = swa + ((size_t)b * W + (size_t)s) * D;
+                for (int d = 0; d < D; ++d) K[nk * D + d] = orc_bf16_value(r[d]);
+            }
             memcpy(V + nk * Dv, K + nk * D, sizeof(double) * (size_t)Dv);
             ++nk;
         }

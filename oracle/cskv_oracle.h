@@ -107,6 +107,7 @@ typedef struct {
     int32_t *status;    /* [1] bit flags                   */
     int32_t idx_format; /* 0: bf16 indexer keys; 1: E2M1 + E8M0 per 16 dims */
     uint8_t *idx_scales;/* [B][cap][idx_dim/16] E8M0 bytes (format 1) */
+    int32_t swa_format; /* window rings used with this cache: 0 bf16, 1 FP8 E4M3 */
 } orc_cache;
 
 #define ORC_STATUS_OVERFLOW 1
@@ -145,6 +146,21 @@ void orc_swa_append(uint16_t *ring, int batch, int W, int dim, const float *rows
 double orc_e8m0_value(uint8_t s);
 void orc_quantize_mx16(const uint16_t *x_bf16, int n, uint8_t *codes, uint8_t *scales);
 void orc_dequantize_mx16(const uint8_t *codes, const uint8_t *scales, int n, double *out);
+
+/* ---------------- FP8 window rows ---------------------------------------- */
+
+/* The pages keep the sliding-window rows in FP8 [P2 四、"P4 main KV" (the
+ * window is stored in FP8); P2 三、"突破四" (the 128-token window)].  Format:
+ * OCP E4M3 -- 1 sign, 4 exponent bits (bias 7), 3 mantissa bits, no
+ * infinities, 0x7F/0xFF NaN, largest finite 448, subnormals k * 2^-9.
+ * Encoding: the nearest E4M3 value, ties to the even mantissa, magnitudes
+ * past 448 saturate to 448, sign kept (so -0 is 0x80).  Pinned: all 254
+ * finite values from their fields, round trips, midpoints, saturation. */
+double orc_e4m3_value(uint8_t v);
+uint8_t orc_e4m3_encode(float x);
+/* orc_swa_append with an FP8 ring */
+void orc_swa_append_fp8(uint8_t *ring, int batch, int W, int dim, const float *rows,
+                        const int32_t *cu_new, const int32_t *end_pos);
 
 /* ---------------- indexer + top-k ---------------------------------------- */
 
@@ -211,7 +227,8 @@ void orc_indexer_topk_in_pool(const orc_cache *c, const uint16_t *q, int heads,
  * Keys: K = dequantised key plane (all dim dims); values: the value plane if
  * present, else K's first dim-rope dims.  Indices < 0 or >= the sequence's
  * entry count are skipped.  No keys: out = 0, lse = -inf.
- * q fp32 [B][Hq][dim]; idx [B][k]; swa bf16 [B][W][dim]; swa_len [B]
+ * q fp32 [B][Hq][dim]; idx [B][k]; swa bf16 [B][W][dim] (FP8 E4M3 bytes when
+ * the cache's swa_format is 1, the pointer reinterpreted); swa_len [B]
  * (NULL: min(n_tokens, W)); out [B][Hq][dim-rope]; lse [B][Hq].
  * Pinned: equal logits -> mean of values, a dominant logit -> its value,
  * single key, LSE merge of the two branches, permutation invariance. */

@@ -451,6 +451,63 @@ def test_topk_exhaustive_tiny(orc):
             _valid_topk(s, k, orc.topk(s, k))
 
 
+# ---------------------------------------------------------------- FP8 window rows
+
+def _e4m3_by_fields(v):
+    s, e, m = v >> 7, (v >> 3) & 15, v & 7
+    mag = m / 8 * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+    return -mag if s else mag
+
+
+def test_e4m3_values_and_round_trip(orc):
+    vals = []
+    for v in range(256):
+        if v & 0x7F == 0x7F:
+            assert math.isnan(orc.e4m3_value(v))
+            continue
+        x = orc.e4m3_value(v)
+        assert x == _e4m3_by_fields(v)
+        assert orc.e4m3_encode(x) == v                 # every finite value encodes to itself
+        vals.append(x)
+    assert max(vals) == 448.0 and min(v for v in vals if v > 0) == 2.0 ** -9
+    assert len(set(vals)) == 253                         # +0 and -0 compare equal
+
+
+def test_e4m3_rounding_ties_and_saturation(orc):
+    pos = sorted({orc.e4m3_value(v) for v in range(0x7F)})
+    for a, b in zip(pos, pos[1:]):
+        mid = (a + b) / 2
+        ca, cb = orc.e4m3_encode(a), orc.e4m3_encode(b)
+        assert orc.e4m3_encode(mid) == (ca if ca % 2 == 0 else cb)      # ties to the even mantissa
+        assert orc.e4m3_encode(np.nextafter(np.float32(mid), np.float32(0))) == ca
+        assert orc.e4m3_encode(np.nextafter(np.float32(mid), np.float32(1e9))) == cb
+    assert orc.e4m3_encode(448.0) == 0x7E and orc.e4m3_encode(1e30) == 0x7E
+    assert orc.e4m3_encode(-500.0) == 0xFE and orc.e4m3_encode(-0.0) == 0x80
+    assert orc.e4m3_encode(2.0 ** -11) == 0x00 and orc.e4m3_encode(-(2.0 ** -10) * 1.01) == 0x81
+
+
+def test_attention_with_fp8_window_is_the_decoded_rows(orc):
+    g = np.random.default_rng(40)
+    n = 20
+    c8 = orc.Cache.empty(1, n, 576, 64, 32, 0, 64, swa_format=1)
+    c16 = orc.Cache.empty(1, n, 576, 64, 32, 0, 64)
+    ents = g.standard_normal((n, 576)).astype(np.float32)
+    for c in (c8, c16):
+        orc.kv_append(c, ents, np.array([0, n], np.int32), None, np.zeros((n, 64), np.uint16))
+    rows = g.standard_normal((6, 576)).astype(np.float32)
+    ring8 = np.zeros((1, 8, 576), np.uint8)
+    orc.swa_append(ring8, rows, np.array([0, 6], np.int32), np.array([6], np.int32))
+    assert ring8[0, 3, 7] == orc.e4m3_encode(rows[3, 7]) and not ring8[0, 6:].any()
+    # the same rows as bf16 (exact: E4M3 values have 4 significant bits)
+    dec = np.vectorize(orc.e4m3_value)(ring8).astype(np.float32)
+    ring16 = _bf16_int(dec)
+    q = g.standard_normal((1, 16, 576)).astype(np.float32)
+    idx = np.array([[0, 5, 19, -1]], np.int32)
+    o8, l8 = orc.sparse_attn(c8, q, idx, ring8, 0.04, swa_len=np.array([6], np.int32))
+    o16, l16 = orc.sparse_attn(c16, q, idx, ring16, 0.04, swa_len=np.array([6], np.int32))
+    assert np.array_equal(o8, o16) and np.array_equal(l8, l16)
+
+
 # ---------------------------------------------------------------- FP4 indexer key
 
 def test_e8m0_values(orc):
