@@ -30,11 +30,13 @@ STATUS_ODD_ENTRY_APPEND = 2
 STATUS_BAD_STATE = 4
 MODE_FULL, MODE_REINDEX, MODE_REUSE = 0, 1, 2
 IDX_BF16, IDX_FP4 = 0, 1
+SWA_BF16, SWA_FP8 = 0, 1
 MODES = {"full": MODE_FULL, "reindex": MODE_REINDEX, "reuse": MODE_REUSE}
 KERNEL_APPEND, KERNEL_SWA_APPEND, KERNEL_INDEXER_SCAN, KERNEL_TOPK_SELECT, KERNEL_ATTENTION = 1, 2, 3, 4, 5
 OP_INDEXER_TOPK, OP_SPARSE_ATTN, OP_LAYER_GROUP, OP_INDEXER_POOL, OP_INDEXER_IN_POOL = 1, 2, 3, 4, 5
 
-EXPORTS = ("cskv_kv_append_fp4", "cskv_append_workspace_bytes", "cskv_swa_append", "cskv_indexer_topk",
+EXPORTS = ("cskv_kv_append_fp4", "cskv_append_workspace_bytes", "cskv_swa_append", "cskv_swa_append_fp8",
+           "cskv_indexer_topk",
            "cskv_indexer_topk_pool", "cskv_indexer_topk_in_pool", "cskv_sparse_attn_decode",
            "cskv_layer_group_decode", "cskv_layer_group_decode_pooled", "cskv_workspace_bytes",
            "cskv_workspace_bytes_pool", "cskv_entry_bytes", "cskv_last_error",
@@ -54,7 +56,7 @@ class CacheDesc(C.Structure):
                 ("k_codes", C.c_void_p), ("k_scales", C.c_void_p), ("v_codes", C.c_void_p),
                 ("v_scales", C.c_void_p), ("idx_keys", C.c_void_p), ("n_tokens", C.c_void_p),
                 ("pending", C.c_void_p), ("status", C.c_void_p), ("idx_format", C.c_int32),
-                ("idx_scales", C.c_void_p)]
+                ("idx_scales", C.c_void_p), ("swa_format", C.c_int32)]
 
 
 class LayerDesc(C.Structure):
@@ -79,6 +81,7 @@ def lib():
         L.cskv_append_workspace_bytes.argtypes = [i32, vp]
         L.cskv_append_workspace_bytes.restype = sz
         L.cskv_swa_append.argtypes = [vp, i32, i32, i32, vp, vp, i32, vp, vp]
+        L.cskv_swa_append_fp8.argtypes = [vp, i32, i32, i32, vp, vp, i32, vp, vp]
         L.cskv_indexer_topk.argtypes = [vp, vp, i32, vp, i32, vp, vp, sz, vp]
         L.cskv_sparse_attn_decode.argtypes = [vp, vp, i32, vp, i32, vp, i32, vp, C.c_float, vp, vp, vp, sz,
                                               vp]
@@ -98,7 +101,8 @@ def lib():
         L.cskv_timer_enable.argtypes = [i32, i32]
         L.cskv_timer_pause.argtypes = [i32, i32]
         L.cskv_timer_read.argtypes = [i32, C.POINTER(C.c_double), C.POINTER(C.c_int32)]
-        for f in ("cskv_kv_append_fp4", "cskv_swa_append", "cskv_indexer_topk", "cskv_indexer_topk_pool",
+        for f in ("cskv_kv_append_fp4", "cskv_swa_append", "cskv_swa_append_fp8", "cskv_indexer_topk",
+                  "cskv_indexer_topk_pool",
                   "cskv_indexer_topk_in_pool", "cskv_sparse_attn_decode", "cskv_layer_group_decode",
                   "cskv_layer_group_decode_pooled", "cskv_timer_enable", "cskv_timer_pause", "cskv_timer_read",
                   "cskv_timer_disable_all"):
@@ -157,10 +161,11 @@ class Cache:
     rope_dim: int = 64
     idx_format: int = 0                          # IDX_BF16, or IDX_FP4 (idx_keys u8 codes + idx_scales)
     idx_scales: Optional[torch.Tensor] = None
+    swa_format: int = 0                          # window rings used with it: SWA_BF16, or SWA_FP8 (uint8 rings)
 
     @classmethod
     def allocate(cls, batch, capacity, k_group=32, v_group=0, idx_dim=128, dim=576, rope_dim=64,
-                 device="cuda", idx_format=0):
+                 device="cuda", idx_format=0, swa_format=0):
         dv = dim - rope_dim
         z = lambda *s, dt: torch.zeros(*s, dtype=dt, device=device)
         fp4 = idx_format == IDX_FP4
@@ -173,14 +178,15 @@ class Cache:
                    else z(batch, capacity, idx_dim, dt=torch.int16),
                    z(batch, dt=torch.int32), z(batch, dim, dt=torch.float32),
                    z(4, dt=torch.int32), dim, rope_dim, idx_format,
-                   z(batch, capacity, idx_dim // 16, dt=torch.uint8) if fp4 else None)
+                   z(batch, capacity, idx_dim // 16, dt=torch.uint8) if fp4 else None, swa_format)
 
     def desc(self) -> CacheDesc:
         p = lambda t: None if t is None else t.data_ptr()
         return CacheDesc(self.batch, self.capacity, self.dim, self.rope_dim, self.k_group,
                          self.v_group, self.idx_dim, p(self.k_codes), p(self.k_scales),
                          p(self.v_codes), p(self.v_scales), p(self.idx_keys), p(self.n_tokens),
-                         p(self.pending), p(self.status), self.idx_format, p(self.idx_scales))
+                         p(self.pending), p(self.status), self.idx_format, p(self.idx_scales),
+                         self.swa_format)
 
     def entry_bytes(self) -> int:
         return entry_bytes(self.dim, self.rope_dim, self.k_group, self.v_group, self.idx_dim)
@@ -235,11 +241,15 @@ def kv_append_fp4(cache: Cache, tokens: torch.Tensor, cu_new: Optional[torch.Ten
 
 def swa_append(ring: torch.Tensor, rows: torch.Tensor, cu_new: Optional[torch.Tensor],
                end_pos: torch.Tensor, stream=None) -> None:
+    """Window rows into a ring: bf16 rings (cskv_swa_append) or FP8 E4M3 rings
+    given as uint8 tensors (cskv_swa_append_fp8)."""
     B, W, D = ring.shape
     n = rows.shape[0]
-    _check(lib().cskv_swa_append(_ptr(ring, B16, "ring"), B, W, D, _ptr(rows, F32, "rows", (n, D)),
-                                 _ptr(cu_new, I32, "cu_new", (B + 1,)), n,
-                                 _ptr(end_pos, I32, "end_pos", (B,)), _stream(stream)))
+    fp8 = ring.dtype == torch.uint8
+    fn = lib().cskv_swa_append_fp8 if fp8 else lib().cskv_swa_append
+    _check(fn(_ptr(ring, U8 if fp8 else B16, "ring"), B, W, D, _ptr(rows, F32, "rows", (n, D)),
+              _ptr(cu_new, I32, "cu_new", (B + 1,)), n,
+              _ptr(end_pos, I32, "end_pos", (B,)), _stream(stream)))
 
 
 def indexer_topk(cache: Cache, q_idx: torch.Tensor, k: int, head_w: Optional[torch.Tensor] = None,
@@ -315,7 +325,7 @@ def sparse_attn_decode(cache: Cache, q: torch.Tensor, idx: torch.Tensor, swa: to
     d = cache.desc()
     _check(lib().cskv_sparse_attn_decode(
         C.byref(d), _ptr(q, F32, "q", (cache.batch, H, cache.dim)), H,
-        _ptr(idx, I32, "idx", (cache.batch, k)), k, _ptr(swa, B16, "swa", (cache.batch, W, cache.dim)), W,
+        _ptr(idx, I32, "idx", (cache.batch, k)), k, _ptr(swa, U8 if cache.swa_format == SWA_FP8 else B16, "swa", (cache.batch, W, cache.dim)), W,
         _ptr(swa_len, I32, "swa_len", (cache.batch,)), float(softmax_scale),
         _ptr(out, F32, "out", (cache.batch, H, dv)), _ptr(lse, F32, "lse", (cache.batch, H)),
         _ptr(ws, U8, "ws"), ws.numel(), _stream(stream)))
@@ -353,7 +363,7 @@ def layer_group_decode(cache: Cache, layers: Sequence[Layer], new_tokens: Option
         arr[i] = LayerDesc(MODES[L.mode], _ptr(L.q, F32, "q", (B, n_heads, cache.dim)),
                            _ptr(L.q_idx, B16, "q_idx", (B, n_idx_heads, cache.idx_dim)),
                            _ptr(L.head_w, F32, "head_w", (B, n_idx_heads)),
-                           _ptr(L.swa, B16, "swa", (B, window, cache.dim)),
+                           _ptr(L.swa, U8 if cache.swa_format == SWA_FP8 else B16, "swa", (B, window, cache.dim)),
                            _ptr(L.swa_row, F32, "swa_row", (B, cache.dim)),
                            _ptr(L.idx, I32, "idx", (B, k)),
                            _ptr(L.out, F32, "out", (B, n_heads, dv)),

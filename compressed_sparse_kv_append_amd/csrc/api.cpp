@@ -62,6 +62,8 @@ int check_cache(const cskv_cache *c)
     REQUIRE((c->idx_format == CSKV_IDX_FP4) == (c->idx_scales != nullptr), CSKV_EINVAL,
             "idx_scales must be set exactly for CSKV_IDX_FP4");
     REQUIRE(!c->idx_scales || aligned(c->idx_scales, 16), CSKV_EINVAL, "idx_scales must be 16-byte aligned");
+    REQUIRE(c->swa_format == CSKV_SWA_BF16 || c->swa_format == CSKV_SWA_FP8, CSKV_EUNSUPPORTED,
+            "swa_format %d: CSKV_SWA_BF16 or CSKV_SWA_FP8", c->swa_format);
     REQUIRE(aligned(c->k_codes, 16) && aligned(c->k_scales, 16) && aligned(c->idx_keys, 16) &&
                 aligned(c->n_tokens, 16) && aligned(c->pending, 16) && aligned(c->status, 4) &&
                 (!c->v_codes || aligned(c->v_codes, 16)) && (!c->v_scales || aligned(c->v_scales, 16)),
@@ -287,6 +289,22 @@ int cskv_swa_append(uint16_t *ring, int32_t batch, int32_t window, int32_t dim, 
     return e == hipSuccess ? CSKV_OK : hip_fail(e, "swa_append launch");
 }
 
+int cskv_swa_append_fp8(uint8_t *ring, int32_t batch, int32_t window, int32_t dim, const float *rows,
+                        const int32_t *cu_new, int32_t total_new, const int32_t *end_pos,
+                        hipStream_t stream)
+{
+    REQUIRE(ring && aligned(ring, 16), CSKV_EINVAL, "ring NULL or not 16-byte aligned");
+    REQUIRE(batch >= 1, CSKV_EINVAL, "batch %d < 1", batch);
+    REQUIRE(window >= 1 && window <= (1 << 20), CSKV_EINVAL, "window %d out of [1, 2^20]", window);
+    REQUIRE(dim > 0 && dim % 16 == 0, CSKV_EUNSUPPORTED, "dim %d must be a positive multiple of 16", dim);
+    REQUIRE(end_pos, CSKV_EINVAL, "end_pos is NULL");
+    int rc = check_rows(rows, cu_new, total_new, batch);
+    if (rc) return rc;
+    hipError_t e = cskv::launch_swa_append(reinterpret_cast<uint16_t *>(ring), batch, window, dim, rows, cu_new,
+                                           total_new, end_pos, stream, true);
+    return e == hipSuccess ? CSKV_OK : hip_fail(e, "swa_append_fp8 launch");
+}
+
 int cskv_indexer_topk(const cskv_cache *cache, const uint16_t *q_idx, int32_t n_idx_heads,
                       const float *head_w, int32_t k, int32_t *out_idx, void *ws, size_t ws_bytes,
                       hipStream_t stream)
@@ -402,7 +420,8 @@ static int layer_group(const cskv_cache *cache, const cskv_layer *layers, int32_
         }
         if (L.swa_row && !window_done) {
             e = cskv::launch_swa_append(L.swa, cache->batch, window, cache->dim, L.swa_row, nullptr,
-                                        cache->batch, cache->n_tokens, stream);
+                                        cache->batch, cache->n_tokens, stream,
+                                        cache->swa_format == CSKV_SWA_FP8);
             if (e != hipSuccess) return hip_fail(e, "layer group: window append");
         }
         if (L.mode == CSKV_MODE_REINDEX && pooled) {

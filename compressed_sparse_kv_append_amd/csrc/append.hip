@@ -201,6 +201,27 @@ __device__ void quantize_channel(float x, int t, int n, int g, uint8_t *codes_ro
     if (live && (t % g) == 0) scales_row[t / g] = s;
 }
 
+// fp32 -> OCP E4M3 byte [P2 四、"P4 main KV" (window rows kept in FP8)]: the
+// nearest E4M3 value, ties to the even mantissa, magnitudes past 448
+// saturating to 448, sign kept.  Normal results round the fp32 mantissa to 3
+// bits; below 2^-6 the value is a multiple of 2^-9, rounded with rintf.
+__device__ __forceinline__ uint32_t e4m3_bits(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const float a = fabsf(x);
+    if (!(a < 448.0f)) return sign | 0x7Eu;
+    if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);     // 0..8 (8 = 2^-6, code 0x08)
+    const uint32_t au = __float_as_uint(a);
+    uint32_t e = (au >> 23) - 127 + 7, m = (au >> 20) & 7u;
+    const uint32_t rem = au & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) {
+        if (++m == 8u) { m = 0; ++e; }
+    }
+    const uint32_t code = (e << 3) | m;
+    return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
 // Indexer key in the pages' FP4 form [P2 四、"890 字节是怎么算出来的" (72 B per
 // 128-dim key); P2 四、"P4 main KV" (E2M1, one 8-bit scale per 16 channels)]:
 // thread t < Di holds dim t of the bf16 row.  Each 16-dim group takes the
@@ -305,8 +326,12 @@ __global__ __launch_bounds__(kAppendThreads) void quantize_kernel(AppendArgs a)
         const int64_t end = finalize_seq<kCompress>(a, b, p, t, kAppendThreads);
         if (a.swa_ring && end >= 1) {
             const int64_t pos = end - 1;            // the position of this row's token
-            uint16_t *dst = a.swa_ring + ((size_t)b * a.swa_window + (size_t)(pos % a.swa_window)) * kDim;
-            dst[t] = (uint16_t)bf16_bits_rne(a.swa_rows[(size_t)b * kDim + t]);
+            const size_t row = (size_t)b * a.swa_window + (size_t)(pos % a.swa_window);
+            const float x = a.swa_rows[(size_t)b * kDim + t];
+            if (c.swa_format == CSKV_SWA_FP8)
+                reinterpret_cast<uint8_t *>(a.swa_ring)[row * kDim + t] = (uint8_t)e4m3_bits(x);
+            else
+                a.swa_ring[row * kDim + t] = (uint16_t)bf16_bits_rne(x);
         }
     }
 }
@@ -328,8 +353,9 @@ struct SwaArgs {
     int64_t total_new;
 };
 
-// One wave per row: fp32 -> bf16 (nearest even) into ring slot pos % window
-// when the row is among the last `window` positions.
+// One wave per row: fp32 -> bf16 (nearest even) or E4M3 (FP8) into ring slot
+// pos % window when the row is among the last `window` positions.
+template <bool FP8>
 __global__ __launch_bounds__(kWave) void swa_append_kernel(SwaArgs a)
 {
     const int r = blockIdx.x, t = threadIdx.x;
@@ -341,13 +367,22 @@ __global__ __launch_bounds__(kWave) void swa_append_kernel(SwaArgs a)
     if (!rows_ok(row0, m, a.total_new) || r - row0 >= m) return;
     if (pos < 0 || pos < end - a.window) return;
     const float4 *src = reinterpret_cast<const float4 *>(a.rows + (size_t)r * a.dim);
-    uint2 *dst = reinterpret_cast<uint2 *>(a.ring + ((size_t)b * a.window + (size_t)(pos % a.window)) * a.dim);
-    for (int i = t; i < a.dim / 4; i += kWave) {
-        const float4 x = src[i];
-        uint2 o;
-        o.x = bf16_bits_rne(x.x) | (bf16_bits_rne(x.y) << 16);
-        o.y = bf16_bits_rne(x.z) | (bf16_bits_rne(x.w) << 16);
-        dst[i] = o;
+    const size_t slot = (size_t)b * a.window + (size_t)(pos % a.window);
+    if (FP8) {
+        uint32_t *dst = reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(a.ring) + slot * a.dim);
+        for (int i = t; i < a.dim / 4; i += kWave) {
+            const float4 x = src[i];
+            dst[i] = e4m3_bits(x.x) | (e4m3_bits(x.y) << 8) | (e4m3_bits(x.z) << 16) | (e4m3_bits(x.w) << 24);
+        }
+    } else {
+        uint2 *dst = reinterpret_cast<uint2 *>(a.ring + slot * a.dim);
+        for (int i = t; i < a.dim / 4; i += kWave) {
+            const float4 x = src[i];
+            uint2 o;
+            o.x = bf16_bits_rne(x.x) | (bf16_bits_rne(x.y) << 16);
+            o.y = bf16_bits_rne(x.z) | (bf16_bits_rne(x.w) << 16);
+            dst[i] = o;
+        }
     }
 }
 
@@ -395,12 +430,15 @@ hipError_t launch_kv_append(const cskv_cache &c, const float *tokens, const int3
 
 hipError_t launch_swa_append(uint16_t *ring, int batch, int window, int dim, const float *rows,
                              const int32_t *cu_new, int total_new, const int32_t *end_pos,
-                             hipStream_t s)
+                             hipStream_t s, bool fp8)
 {
     if (total_new == 0) return hipSuccess;
     SwaArgs a{ring, batch, window, dim, rows, cu_new, end_pos, total_new};
     const TimedLaunch tl = timer_take(CSKV_KERNEL_SWA_APPEND);
-    launch_kernel(swa_append_kernel, dim3((unsigned)total_new), dim3(kWave), s, tl.start, tl.stop, a);
+    if (fp8)
+        launch_kernel(swa_append_kernel<true>, dim3((unsigned)total_new), dim3(kWave), s, tl.start, tl.stop, a);
+    else
+        launch_kernel(swa_append_kernel<false>, dim3((unsigned)total_new), dim3(kWave), s, tl.start, tl.stop, a);
     return hipGetLastError();
 }
 

@@ -33,6 +33,8 @@
 //   P2  "DeepSeek V1 到 V4.1-Flash，单 token 的 global KV 如何从 389,000 B 压缩到 890 B的？"
 #include <math.h>
 
+#include <type_traits>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -105,7 +107,7 @@ struct Ctx {
     int ne, nw;         // entry chunks, then window chunks, of this block
     int G;              // key groups per row
     size_t row0;        // first cache row of the sequence
-    const uint16_t *ring;
+    const uint8_t *ring;    // this sequence's window rows (bf16, or FP8 E4M3 bytes)
 };
 
 __device__ __forceinline__ u32x4_t lds16(const void *p) { return *reinterpret_cast<const u32x4_t *>(p); }
@@ -308,25 +310,45 @@ __device__ __forceinline__ void store_sparse(AttnSmem &sm, const Ctx &x, const S
     }
 }
 
+// Window rows: task (row, p) is dims 8p .. 8p+7 of a row, 16 bytes in bf16
+// or 8 bytes in FP8 (W8); FP8 rows are widened to bf16 on the way to LDS
+// (exact: E4M3 values have 4 significant bits), so the staged rows are bf16
+// either way.
+template <bool W8>
 __device__ __forceinline__ void fetch_window(const AttnArgs &a, const AttnSmem &sm, const Ctx &x, int lc,
                                              WindowRegs &r)
 {
+    constexpr uint32_t kRowBytes = W8 ? kD : kD * 2;
     const int32_t *src = sm.src + lc * kSK;
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(x.ring, (uint32_t)a.window * (kD * 2));
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(x.ring, (uint32_t)a.window * kRowBytes);
 #pragma unroll
     for (int i = 0; i < 9; ++i) {
         const int task = x.t + kThreads * i, row = task / 72, p = task % 72;
-        const uint32_t off = row_off(src[row], kD * 2) + 16 * p;
-        r.p[i] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)off, 0, 0);
+        const uint32_t off = row_off(src[row], kRowBytes) + (W8 ? 8 : 16) * p;
+        if (W8) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(wr, (int)off, 0, 0);
+            r.p[i][0] = v[0];
+            r.p[i][1] = v[1];
+        } else {
+            r.p[i] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)off, 0, 0);
+        }
     }
 }
 
+template <bool W8>
 __device__ __forceinline__ void store_window(AttnSmem &sm, const Ctx &x, const WindowRegs &r)
 {
 #pragma unroll
     for (int i = 0; i < 9; ++i) {
         const int task = x.t + kThreads * i, row = task / 72, p = task % 72;
-        *reinterpret_cast<u32x4_t *>(&sm.st.win.kr[row][8 * p]) = r.p[i];
+        u32x4_t v = r.p[i];
+        if (W8) {
+            v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.p[i][0], 1.0f, false));
+            v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.p[i][0], 1.0f, true));
+            v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.p[i][1], 1.0f, false));
+            v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.p[i][1], 1.0f, true));
+        }
+        *reinterpret_cast<u32x4_t *>(&sm.st.win.kr[row][8 * p]) = v;
     }
 }
 
@@ -519,7 +541,7 @@ __device__ __forceinline__ void chunk_pv(const AttnSmem &sm, const Ctx &x, f32x4
 
 // The chunk loop of one block: the next chunk's HBM reads are in flight
 // while the current chunk is computed.
-template <bool SPARSE, bool SPLIT, int VGS, int KG>
+template <bool SPARSE, bool SPLIT, int VGS, int KG, bool W8>
 __device__ __forceinline__ void run_chunks(const AttnArgs &a, AttnSmem &sm, const Ctx &x, int first, int end,
                                            f32x4_t (&o)[4])
 {
@@ -539,12 +561,12 @@ __device__ __forceinline__ void run_chunks(const AttnArgs &a, AttnSmem &sm, cons
         }
     } else {
         WindowRegs r;
-        fetch_window(a, sm, x, first, r);
+        fetch_window<W8>(a, sm, x, first, r);
         for (int lc = first; lc < end; ++lc) {
             __syncthreads();
-            store_window(sm, x, r);
+            store_window<W8>(sm, x, r);
             __syncthreads();
-            if (lc + 1 < end) fetch_window(a, sm, x, lc + 1, r);
+            if (lc + 1 < end) fetch_window<W8>(a, sm, x, lc + 1, r);
             chunk_logits<false, KG>(sm, x);
             __syncthreads();
             chunk_softmax<false>(sm, x, lc, a.scale_log2);
@@ -557,7 +579,8 @@ __device__ __forceinline__ void run_chunks(const AttnArgs &a, AttnSmem &sm, cons
 // VGS: the value group size in effect (the value plane's group, else the key
 // plane's): 32, 64 or 128.  SPLIT: the cache has a separate value plane.
 // KG: the key plane's group, 32 or 64.
-template <int VGS, bool SPLIT, int KG>
+// W8: the window rows are FP8 (E4M3).
+template <int VGS, bool SPLIT, int KG, bool W8>
 __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a)
 {
     __shared__ AttnSmem sm;
@@ -586,7 +609,7 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a)
     x.nw = w1 - w0;
     x.G = kD / KG;
     x.row0 = (size_t)b * c.capacity;
-    x.ring = a.swa + (size_t)b * a.window * kD;
+    x.ring = reinterpret_cast<const uint8_t *>(a.swa) + (size_t)b * a.window * kD * (W8 ? 1 : 2);
     const int64_t E = entries_of(c.n_tokens, b, c.capacity);
     int64_t nswa = a.swa_len ? (int64_t)a.swa_len[b] : (int64_t)c.n_tokens[b];
     nswa = nswa < 0 ? 0 : (nswa > a.window ? a.window : nswa);
@@ -628,8 +651,8 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a)
     for (int nt = 0; nt < 4; ++nt) o[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     __syncthreads();
 
-    if (x.ne > 0) run_chunks<true, SPLIT, VGS, KG>(a, sm, x, 0, x.ne, o);
-    if (x.nw > 0) run_chunks<false, SPLIT, VGS, KG>(a, sm, x, x.ne, x.ne + x.nw, o);
+    if (x.ne > 0) run_chunks<true, SPLIT, VGS, KG, W8>(a, sm, x, 0, x.ne, o);
+    if (x.nw > 0) run_chunks<false, SPLIT, VGS, KG, W8>(a, sm, x, x.ne, x.ne + x.nw, o);
     __syncthreads();
 
     // ---- results: final (one split) or partial (merged by attn_merge_kernel)
@@ -784,20 +807,25 @@ hipError_t launch_sparse_attn(const cskv_cache &c, const float *q, int heads, co
     const TimedLaunch tl = timer_take(CSKV_KERNEL_ATTENTION);
     hipEvent_t stop_main = p.splits > 1 ? nullptr : tl.stop;
     auto attn = [&](auto kernel) { launch_kernel(kernel, dim3(blocks), dim3(kThreads), s, tl.start, stop_main, a); };
-    if (c.v_group > 0) {
-        if (c.k_group == 32) {
-            if (vgs == 32) attn(sparse_attn_kernel<32, true, 32>);
-            else if (vgs == 64) attn(sparse_attn_kernel<64, true, 32>);
-            else attn(sparse_attn_kernel<128, true, 32>);
+    auto pick = [&](auto w8) {
+        constexpr bool W8 = decltype(w8)::value;
+        if (c.v_group > 0) {
+            if (c.k_group == 32) {
+                if (vgs == 32) attn(sparse_attn_kernel<32, true, 32, W8>);
+                else if (vgs == 64) attn(sparse_attn_kernel<64, true, 32, W8>);
+                else attn(sparse_attn_kernel<128, true, 32, W8>);
+            } else {
+                if (vgs == 32) attn(sparse_attn_kernel<32, true, 64, W8>);
+                else if (vgs == 64) attn(sparse_attn_kernel<64, true, 64, W8>);
+                else attn(sparse_attn_kernel<128, true, 64, W8>);
+            }
         } else {
-            if (vgs == 32) attn(sparse_attn_kernel<32, true, 64>);
-            else if (vgs == 64) attn(sparse_attn_kernel<64, true, 64>);
-            else attn(sparse_attn_kernel<128, true, 64>);
+            if (c.k_group == 32) attn(sparse_attn_kernel<32, false, 32, W8>);
+            else attn(sparse_attn_kernel<64, false, 64, W8>);
         }
-    } else {
-        if (c.k_group == 32) attn(sparse_attn_kernel<32, false, 32>);
-        else attn(sparse_attn_kernel<64, false, 64>);
-    }
+    };
+    if (c.swa_format == CSKV_SWA_FP8) pick(std::true_type{});
+    else pick(std::false_type{});
     if (p.splits > 1)
         launch_kernel(attn_merge_kernel, dim3((unsigned)(c.batch * hg)), dim3(256), s, nullptr, tl.stop, a);
     return hipGetLastError();

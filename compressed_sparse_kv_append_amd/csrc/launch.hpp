@@ -32,9 +32,11 @@ hipError_t launch_kv_append(const cskv_cache &c, const float *tokens, const int3
                             int total_new, const float *w_comp, const uint16_t *idx_rows,
                             void *ws, hipStream_t s, uint16_t *swa_ring = nullptr,
                             const float *swa_rows = nullptr, int swa_window = 0);
+// fp8: the ring holds E4M3 bytes (dim a multiple of 16), else bf16 (dim a
+// multiple of 4).
 hipError_t launch_swa_append(uint16_t *ring, int batch, int window, int dim, const float *rows,
                              const int32_t *cu_new, int total_new, const int32_t *end_pos,
-                             hipStream_t s);
+                             hipStream_t s, bool fp8 = false);
 // Indexer scan (scan.hip): one score key per valid entry into keys
 // [batch][score_key_stride]; with block_keys, also the largest key of each
 // block of `block` entries (block divides 16) into block_keys

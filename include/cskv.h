@@ -94,6 +94,13 @@ extern "C" {
  */
 #define CSKV_IDX_BF16 0
 #define CSKV_IDX_FP4 1
+/* Window rings used with a cache (cskv_sparse_attn_decode, the layer group):
+ * bf16 rows, or the pages' FP8 rows [P2 四、"P4 main KV" (the window is kept in
+ * FP8)]: OCP E4M3 bytes [batch][window][dim] (the uint16_t pointers of the
+ * entry points reinterpreted), written as the nearest E4M3 value, ties to
+ * the even mantissa, saturating at +-448, sign kept. */
+#define CSKV_SWA_BF16 0
+#define CSKV_SWA_FP8 1
 typedef struct cskv_cache {
     int32_t batch, capacity, dim, rope_dim, k_group, v_group, idx_dim;
     uint8_t *k_codes;
@@ -106,6 +113,7 @@ typedef struct cskv_cache {
     int32_t *status;
     int32_t idx_format;      /* CSKV_IDX_BF16 or CSKV_IDX_FP4 */
     uint8_t *idx_scales;     /* CSKV_IDX_FP4 only, else NULL */
+    int32_t swa_format;      /* CSKV_SWA_BF16 or CSKV_SWA_FP8 */
 } cskv_cache;
 
 /*
@@ -157,6 +165,10 @@ size_t cskv_append_workspace_bytes(int32_t total_new, const float *w_comp);
 int cskv_swa_append(uint16_t *ring, int32_t batch, int32_t window, int32_t dim,
                     const float *rows, const int32_t *cu_new, int32_t total_new,
                     const int32_t *end_pos, hipStream_t stream);
+/* cskv_swa_append into an FP8 ring (CSKV_SWA_FP8): ring u8 [batch][window][dim]. */
+int cskv_swa_append_fp8(uint8_t *ring, int32_t batch, int32_t window, int32_t dim, const float *rows,
+                        const int32_t *cu_new, int32_t total_new, const int32_t *end_pos,
+                        hipStream_t stream);
 
 /*
  * Indexer scoring and exact top-k [P2 三、"突破四" (a light indexer scores all

@@ -23,10 +23,12 @@ def host(t: torch.Tensor) -> np.ndarray:
     return a.view(np.uint16) if a.dtype == np.int16 else a
 
 
-def pair(batch, capacity, k_group, v_group, idx_dim, idx_format=0):
+def pair(batch, capacity, k_group, v_group, idx_dim, idx_format=0, swa_format=0):
     """An empty device cache and its empty host mirror with the same shape."""
-    g = ck.Cache.allocate(batch, capacity, k_group, v_group, idx_dim, idx_format=idx_format)
-    h = orc.Cache.empty(batch, capacity, 576, 64, k_group, v_group, idx_dim, idx_format=idx_format)
+    g = ck.Cache.allocate(batch, capacity, k_group, v_group, idx_dim, idx_format=idx_format,
+                          swa_format=swa_format)
+    h = orc.Cache.empty(batch, capacity, 576, 64, k_group, v_group, idx_dim, idx_format=idx_format,
+                        swa_format=swa_format)
     return g, h
 
 
@@ -87,7 +89,9 @@ def lse_tol(h: orc.Cache, q: np.ndarray, idx: np.ndarray, ring: np.ndarray, swa_
             if 0 <= e < E:
                 keys.append(orc.dequantize_row(h.k_codes[b, e], h.k_scales[b, e], D, h.k_group))
         nw = int(min(swa_len[b], ring.shape[1]))
-        if nw:
+        if nw and ring.dtype == np.uint8:          # FP8 E4M3 rows
+            keys.append(np.vectorize(orc.e4m3_value)(ring[b, :nw]).astype(np.float64))
+        elif nw:
             keys.append((ring[b, :nw].astype(np.uint32) << 16).view(np.float32).astype(np.float64))
         if not keys:
             continue

@@ -48,7 +48,7 @@ def test_entry_bytes(L):
 def _desc(**over):
     d = dict(batch=2, capacity=64, dim=576, rope_dim=64, k_group=32, v_group=0, idx_dim=64,
              k_codes=0x10000, k_scales=0x20000, v_codes=None, v_scales=None, idx_keys=0x30000,
-             n_tokens=0x40000, pending=0x50000, status=0x60000, idx_format=0, idx_scales=None)
+             n_tokens=0x40000, pending=0x50000, status=0x60000, idx_format=0, idx_scales=None, swa_format=0)
     d.update(over)
     return ck.CacheDesc(*[d[f] for f, _ in ck.CacheDesc._fields_])
 
@@ -71,6 +71,7 @@ def _err(L):
     (dict(idx_format=1), ck.EINVAL, "idx_scales"),
     (dict(idx_scales=0x68000), ck.EINVAL, "idx_scales"),
     (dict(idx_format=1, idx_scales=0x68004), ck.EINVAL, "aligned"),
+    (dict(swa_format=2), ck.EUNSUPPORTED, "swa_format"),
 ])
 def test_cache_descriptor_rejected_before_launch(L, over, code, text):
     d = _desc(**over)
@@ -117,8 +118,9 @@ def test_call_arguments_rejected_before_launch(L):
     assert L.cskv_sparse_attn_decode(C.byref(big), vp(0xC0000), 16, vp(0xD0000), 512, vp(0xE0000), 128,
                                      None, C.c_float(0.04), vp(0xF0000), None, vp(0xB0000), bws,
                                      None) == ck.EUNSUPPORTED and "capacity" in _err(L)
-    # window append: dim not a multiple of 4
+    # window append: dim not a multiple of 4 (bf16) or of 16 (FP8)
     assert L.cskv_swa_append(vp(0x100000), 2, 128, 578, vp(0x70000), None, 2, vp(0x40000), None) == ck.EUNSUPPORTED
+    assert L.cskv_swa_append_fp8(vp(0x100000), 2, 128, 580, vp(0x70000), None, 2, vp(0x40000), None) == ck.EUNSUPPORTED
 
 
 def test_layer_group_checks_every_layer_first(L):
