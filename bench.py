@@ -63,6 +63,8 @@ def parse():
     p.add_argument("--copy-probe", type=int, default=0, help="MiB copied by a plain device copy")
     p.add_argument("--idx-format", choices=("bf16", "fp4"), default="bf16",
                    help="indexer-key storage: bf16, or the pages' FP4 form (E2M1 + E8M0 per 16 dims)")
+    p.add_argument("--swa-format", choices=("bf16", "fp8"), default="bf16",
+                   help="window rows: bf16, or the pages' FP8 (E4M3)")
     p.add_argument("--pool", default="", help="pool_blocks,pool_block: the hierarchical indexer's candidate "
                    "pool in a layer-group workload (reindex layers select inside it)")
     return p.parse_args()
@@ -79,12 +81,12 @@ def copy_probe(mib: int):
     print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
 
 
-def build_replicas(ck, synth, w, cap, dev, n, idx_format=0):
+def build_replicas(ck, synth, w, cap, dev, n, idx_format=0, swa_format=0):
     """Entries-mode build of n identical cache replicas, one sequence at a time
     (each sequence's entries are drawn once and appended to every replica)."""
     import torch
-    reps = [ck.Cache.allocate(w.batch, cap, w.k_group, w.v_group, w.idx_dim, idx_format=idx_format)
-            for _ in range(n)]
+    reps = [ck.Cache.allocate(w.batch, cap, w.k_group, w.v_group, w.idx_dim, idx_format=idx_format,
+                              swa_format=swa_format) for _ in range(n)]
     for b in range(w.batch):
         ents = dev(synth.cache_entries(w, b))
         keys = dev(synth.cache_idx_keys(w, b))
@@ -113,7 +115,7 @@ def scans_per_step(w, pool):
     return full, pooled
 
 
-def step_bytes(w, entries: float, pool=None, idx_fp4=False) -> dict:
+def step_bytes(w, entries: float, pool=None, idx_fp4=False, swa_fp8=False) -> dict:
     """Algorithmic bytes of one step (whole batch): every plane read or written
     once by the method's definition; score arrays are not counted.  Scans: the
     whole indexer-key plane per full scan, the pooled positions' keys per
@@ -131,7 +133,7 @@ def step_bytes(w, entries: float, pool=None, idx_fp4=False) -> dict:
         "indexer_keys": B * (full * entries + pooled * pool_pos) * key_bytes,
         "indexer_q": B * sel * w.idx_heads * Di * 2,
         "gather": L * B * min(w.topk, entries) * entry_fp4,
-        "window": L * B * w.window * D * 2,
+        "window": L * B * w.window * D * (1 if swa_fp8 else 2),
         "q": L * B * w.q_heads * D * 4,
         "out": L * B * w.q_heads * (Dv + 1) * 4,
         "indices": (sel + L) * B * w.topk * 4,
@@ -238,8 +240,23 @@ def main():
 
     t0 = time.time()
     idx_fp4 = a.idx_format == "fp4"
-    reps = build_replicas(ck, synth, w, cap, dev, a.replicas, ck.IDX_FP4 if idx_fp4 else ck.IDX_BF16)
-    log(f"built {a.replicas} cache replicas in {time.time() - t0:.1f}s (indexer keys {a.idx_format})")
+    swa_fp8 = a.swa_format == "fp8"
+    reps = build_replicas(ck, synth, w, cap, dev, a.replicas, ck.IDX_FP4 if idx_fp4 else ck.IDX_BF16,
+                          ck.SWA_FP8 if swa_fp8 else ck.SWA_BF16)
+    log(f"built {a.replicas} cache replicas in {time.time() - t0:.1f}s (indexer keys {a.idx_format}, "
+        f"window {a.swa_format})")
+
+    def ring_of(r16):
+        """A layer's window ring: the bf16 ring, or the same rows written in FP8
+        by the library's own window append."""
+        if not swa_fp8:
+            return dev(r16)
+        Bw, Ww, Dw = r16.shape
+        rows = (r16.astype(np.uint32) << 16).view(np.float32).reshape(Bw * Ww, Dw)
+        ring = torch.zeros(Bw, Ww, Dw, dtype=torch.uint8, device="cuda")
+        ck.swa_append(ring, dev(rows), dev((np.arange(Bw + 1) * Ww).astype(np.int32)),
+                      dev(np.full(Bw, Ww, np.int32)))
+        return ring
     st = synth.step_inputs(w, 0)
     W = dev(synth.w_comp(w))
     scale = 1 / math.sqrt(w.dim)
@@ -250,7 +267,7 @@ def main():
         for li, mode in enumerate(w.layers):
             layers.append(ck.Layer(mode=mode, q=dev(st.q[li]),
                                    q_idx=None if st.q_idx[li] is None else dev(st.q_idx[li]),
-                                   swa=dev(st.swa_ring[li]), swa_row=dev(st.swa_row[li]),
+                                   swa=ring_of(st.swa_ring[li]), swa_row=dev(st.swa_row[li]),
                                    idx=torch.empty(B, w.topk, dtype=torch.int32, device="cuda")
                                    if mode != "reuse" else None,
                                    out=torch.empty(B, w.q_heads, w.vdim, device="cuda"),
@@ -341,7 +358,7 @@ def main():
 
     # mean entries per sequence over the timed steps
     entries_mean = float(0.5 * (ent_before + ent_after))
-    sb = step_bytes(w, entries_mean, pool, idx_fp4)
+    sb = step_bytes(w, entries_mean, pool, idx_fp4, swa_fp8)
     n_full, n_pooled = scans_per_step(w, pool)
     scan_bytes = (sb["indexer_keys"] + sb["indexer_q"]) / (n_full + n_pooled)   # per launch, averaged
     scan = live if live is not None else kern["indexer_scan"]
@@ -367,11 +384,13 @@ def main():
                    "topk": w.topk, "window": w.window, "replicas": a.replicas,
                    "launch": "hip_graph" if a.graph else "eager", "layers": list(w.layers),
                    "idx_storage": "e2m1+e8m0/16" if idx_fp4 else "bf16",
+                   "window_storage": "e4m3" if swa_fp8 else "bf16",
                    "pool": list(pool) if pool else None,
                    "tokens_per_s": round(steps_per_s * B, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": pmc_traffic() if (w.name == "decode_64k_b32" and not idx_fp4 and pool is None)
+                     "traffic": pmc_traffic() if (w.name == "decode_64k_b32" and not idx_fp4 and pool is None
+                                                  and not swa_fp8)
                      else None, "kernel": "indexer_scan",
                      "bytes_per_launch": round(scan_bytes), "avg_us": round(scan_us, 2),
                      "timed_launches": scan["launches"], "scans_per_step": [n_full, n_pooled],
