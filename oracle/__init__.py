@@ -53,7 +53,7 @@ class _Cache(C.Structure):
                 ("idx_keys", C.POINTER(C.c_uint16)), ("n_tokens", C.POINTER(C.c_int32)),
                 ("pending", C.POINTER(C.c_float)), ("status", C.POINTER(C.c_int32)),
                 ("idx_format", C.c_int32), ("idx_scales", C.POINTER(C.c_uint8)),
-                ("swa_format", C.c_int32)]
+                ("swa_format", C.c_int32), ("k_format", C.c_int32)]
 
 
 def _declare(L):
@@ -83,6 +83,8 @@ def _declare(L):
     L.orc_e8m0_value.argtypes = [C.c_uint8]
     L.orc_quantize_mx16.restype = None
     L.orc_quantize_mx16.argtypes = [P(C.c_uint16), C.c_int, P(C.c_uint8), P(C.c_uint8)]
+    L.orc_quantize_mx16_f32.restype = None
+    L.orc_quantize_mx16_f32.argtypes = [P(C.c_float), C.c_int, P(C.c_uint8), P(C.c_uint8)]
     L.orc_dequantize_mx16.restype = None
     L.orc_dequantize_mx16.argtypes = [P(C.c_uint8), P(C.c_uint8), C.c_int, P(f64)]
     L.orc_compress_pair.restype = None
@@ -218,6 +220,16 @@ def quantize_mx16(x_bf16):
     return codes, scales
 
 
+def quantize_mx16_f32(x):
+    """Main-entry plane in the pages' form: E2M1 codes and E8M0 scales per 16 channels."""
+    x = _f32(x)
+    n = x.shape[0]
+    codes = np.empty(n // 2, np.uint8)
+    scales = np.empty(n // 16, np.uint8)
+    lib().orc_quantize_mx16_f32(_p(x, C.c_float), n, _p(codes, C.c_uint8), _p(scales, C.c_uint8))
+    return codes, scales
+
+
 def dequantize_mx16(codes, scales, n) -> np.ndarray:
     codes = np.ascontiguousarray(codes, np.uint8)
     scales = np.ascontiguousarray(scales, np.uint8)
@@ -268,22 +280,25 @@ class Cache:
     idx_format: int = 0
     idx_scales: Optional[np.ndarray] = None   # E8M0 u8 [B][cap][Di/16] (idx_format 1)
     swa_format: int = 0                        # window rings used with this cache: 0 bf16, 1 FP8 E4M3
+    k_format: int = 0                          # 1: E8M0 byte scales per 16 channels (k_group 16)
 
     @classmethod
     def empty(cls, batch, capacity, dim=576, rope_dim=64, k_group=32, v_group=0, idx_dim=128,
-              idx_format=0, swa_format=0):
+              idx_format=0, swa_format=0, k_format=0):
         Dv = dim - rope_dim
         fp4 = idx_format == 1
+        st = np.uint8 if k_format == 1 else np.float32
         return cls(batch, capacity, dim, rope_dim, k_group, v_group, idx_dim,
                    np.zeros((batch, capacity, dim // 2), np.uint8),
-                   np.zeros((batch, capacity, dim // k_group), np.float32),
+                   np.zeros((batch, capacity, dim // k_group), st),
                    np.zeros((batch, capacity, Dv // 2), np.uint8) if v_group else None,
-                   np.zeros((batch, capacity, Dv // v_group), np.float32) if v_group else None,
+                   np.zeros((batch, capacity, Dv // v_group), st) if v_group else None,
                    np.zeros((batch, capacity, idx_dim // 2), np.uint8) if fp4
                    else np.zeros((batch, capacity, idx_dim), np.uint16),
                    np.zeros(batch, np.int32), np.zeros((batch, dim), np.float32),
                    np.zeros(1, np.int32), idx_format,
-                   np.zeros((batch, capacity, idx_dim // 16), np.uint8) if fp4 else None, swa_format)
+                   np.zeros((batch, capacity, idx_dim // 16), np.uint8) if fp4 else None, swa_format,
+                   k_format)
 
     def _c(self) -> _Cache:
         return _Cache(self.batch, self.capacity, self.dim, self.rope_dim, self.k_group,
@@ -292,7 +307,7 @@ class Cache:
                       _p(self.v_codes, C.c_uint8), _p(self.v_scales, C.c_float),
                       _p(self.idx_keys, C.c_uint16), _p(self.n_tokens, C.c_int32),
                       _p(self.pending, C.c_float), _p(self.status, C.c_int32),
-                      self.idx_format, _p(self.idx_scales, C.c_uint8), self.swa_format)
+                      self.idx_format, _p(self.idx_scales, C.c_uint8), self.swa_format, self.k_format)
 
     def entries(self) -> np.ndarray:
         return np.clip(self.n_tokens // 2, 0, self.capacity)

@@ -243,6 +243,34 @@ void orc_quantize_mx16(const uint16_t *x_bf16, int n, uint8_t *codes, uint8_t *s
     }
 }
 
+void orc_quantize_mx16_f32(const float *x, int n, uint8_t *codes, uint8_t *scales)
+{
+    for (int g = 0; g < n / 16; ++g) {
+        double a = 0.0;
+        for (int i = 0; i < 16; ++i) {
+            double v = fabs((double)x[16 * g + i]);
+            if (v > a) a = v;
+        }
+        int e = -127;
+        if (a > 0.0) {
+            int ex;
+            (void)frexp(a, &ex);          /* floor(log2 a) = ex - 1 */
+            e = ex - 1 - 2;
+            if (e < -127) e = -127;
+            if (e > 127) e = 127;
+        }
+        scales[g] = (uint8_t)(e + 127);
+        for (int i = 0; i < 16; i += 2) {
+            unsigned c0 = 0, c1 = 0;
+            if (a > 0.0) {
+                c0 = orc_e2m1_encode((float)ldexp((double)x[16 * g + i], -e));
+                c1 = orc_e2m1_encode((float)ldexp((double)x[16 * g + i + 1], -e));
+            }
+            codes[(16 * g + i) / 2] = (uint8_t)(c0 | (c1 << 4));
+        }
+    }
+}
+
 void orc_dequantize_mx16(const uint8_t *codes, const uint8_t *scales, int n, double *out)
 {
     for (int i = 0; i < n; ++i) {
@@ -255,11 +283,17 @@ static void store_entry(orc_cache *c, int b, int64_t i, const float *e, const ui
 {
     const int D = c->dim, Dv = c->dim - c->rope_dim;
     size_t row = (size_t)b * c->capacity + (size_t)i;
-    orc_quantize_row(e, D, c->k_group, c->k_codes + row * (D / 2),
-                     c->k_scales + row * (D / c->k_group));
-    if (c->v_group > 0)
-        orc_quantize_row(e, Dv, c->v_group, c->v_codes + row * (Dv / 2),
-                         c->v_scales + row * (Dv / c->v_group));
+    if (c->k_format == 1) {
+        orc_quantize_mx16_f32(e, D, c->k_codes + row * (D / 2), (uint8_t *)c->k_scales + row * (D / 16));
+        if (c->v_group > 0)
+            orc_quantize_mx16_f32(e, Dv, c->v_codes + row * (Dv / 2), (uint8_t *)c->v_scales + row * (Dv / 16));
+    } else {
+        orc_quantize_row(e, D, c->k_group, c->k_codes + row * (D / 2),
+                         c->k_scales + row * (D / c->k_group));
+        if (c->v_group > 0)
+            orc_quantize_row(e, Dv, c->v_group, c->v_codes + row * (Dv / 2),
+                             c->v_scales + row * (Dv / c->v_group));
+    }
     if (c->idx_format == 1)
         orc_quantize_mx16(idx_row, c->idx_dim, (uint8_t *)c->idx_keys + row * (c->idx_dim / 2),
                           c->idx_scales + row * (c->idx_dim / 16));
@@ -510,14 +544,24 @@ void orc_sparse_attn(const orc_cache *c, const float *q, int heads, const int32_
             int64_t j = idx[(size_t)b * k + t];
             if (j < 0 || j >= E) continue;
             size_t row = (size_t)b * c->capacity + (size_t)j;
-            orc_dequantize_row(c->k_codes + row * (D / 2), c->k_scales + row * (D / c->k_group),
-                               D, c->k_group, K + nk * D);
-            if (c->v_group > 0)
-                orc_dequantize_row(c->v_codes + row * (Dv / 2),
-                                   c->v_scales + row * (Dv / c->v_group), Dv, c->v_group,
-                                   V + nk * Dv);
-            else
-                memcpy(V + nk * Dv, K + nk * D, sizeof(double) * (size_t)Dv);
+            if (c->k_format == 1) {
+                orc_dequantize_mx16(c->k_codes + row * (D / 2), (const uint8_t *)c->k_scales + row * (D / 16),
+                                    D, K + nk * D);
+                if (c->v_group > 0)
+                    orc_dequantize_mx16(c->v_codes + row * (Dv / 2),
+                                        (const uint8_t *)c->v_scales + row * (Dv / 16), Dv, V + nk * Dv);
+                else
+                    memcpy(V + nk * Dv, K + nk * D, sizeof(double) * (size_t)Dv);
+            } else {
+                orc_dequantize_row(c->k_codes + row * (D / 2), c->k_scales + row * (D / c->k_group),
+                                   D, c->k_group, K + nk * D);
+                if (c->v_group > 0)
+                    orc_dequantize_row(c->v_codes + row * (Dv / 2),
+                                       c->v_scales + row * (Dv / c->v_group), Dv, c->v_group,
+                                       V + nk * Dv);
+                else
+                    memcpy(V + nk * Dv, K + nk * D, sizeof(double) * (size_t)Dv);
+            }
             ++nk;
         }
         /* keys from the sliding window (bf16 or FP8 rows; values are the first Dv dims) */

@@ -108,6 +108,9 @@ typedef struct {
     int32_t idx_format; /* 0: bf16 indexer keys; 1: E2M1 + E8M0 per 16 dims */
     uint8_t *idx_scales;/* [B][cap][idx_dim/16] E8M0 bytes (format 1) */
     int32_t swa_format; /* window rings used with this cache: 0 bf16, 1 FP8 E4M3 */
+    int32_t k_format;   /* 0: fp32 scale per k_group/v_group channels; 1: one E8M0 byte
+                           per 16 channels in both planes (k_group 16, v_group 0 or 16;
+                           k_scales / v_scales reinterpreted as bytes) */
 } orc_cache;
 
 #define ORC_STATUS_OVERFLOW 1
@@ -146,6 +149,10 @@ void orc_swa_append(uint16_t *ring, int batch, int W, int dim, const float *rows
 double orc_e8m0_value(uint8_t s);
 void orc_quantize_mx16(const uint16_t *x_bf16, int n, uint8_t *codes, uint8_t *scales);
 void orc_dequantize_mx16(const uint8_t *codes, const uint8_t *scales, int n, double *out);
+/* The same form for a main-entry plane [P2 四、"P4 main KV" (E2M1, one 8-bit
+ * scale per 16 channels, OCP MXFP4)]: fp32 inputs, the MX scale rule on the
+ * group's largest fp32 magnitude, codes as above. */
+void orc_quantize_mx16_f32(const float *x, int n, uint8_t *codes, uint8_t *scales);
 
 /* ---------------- FP8 window rows ---------------------------------------- */
 

@@ -556,6 +556,49 @@ def test_mx16_integers_and_round_trip(orc):
     assert codes.nbytes + scales.nbytes == 72 == orc.fp4_row_bytes(128, 16, 1)
 
 
+def test_mx16_main_entry_form(orc):
+    g = np.random.default_rng(32)
+    # on bf16-representable inputs the fp32 form and the bf16 form agree
+    for _ in range(50):
+        x = _bf16_int(g.standard_normal(576).astype(np.float32) * 2.0 ** g.integers(-8, 8))
+        xf = (x.astype(np.uint32) << 16).view(np.float32)
+        c1, s1 = orc.quantize_mx16(x)
+        c2, s2 = orc.quantize_mx16_f32(xf)
+        assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    # fp32 inputs at a binade edge: 7.999 has floor(log2) 2 -> scale 1 -> saturates to 6
+    codes, scales = orc.quantize_mx16_f32(np.array([7.999] + [0.0] * 15, np.float32))
+    assert scales[0] == 127 and orc.dequantize_mx16(codes, scales, 16)[0] == 6.0
+    # on-grid groups survive exactly
+    grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
+    v = g.choice(grid, 576) * g.choice([-1, 1], 576)
+    v[::16] = 6.0
+    v = v * 2.0 ** np.repeat(g.integers(-5, 5, 36), 16)
+    codes, scales = orc.quantize_mx16_f32(v.astype(np.float32))
+    assert np.array_equal(orc.dequantize_mx16(codes, scales, 576), v)
+
+
+def test_attention_over_mx16_entries_is_attention_over_their_values(orc):
+    # rows on the E2M1 x 2^e grid of every 16-channel group dequantise exactly
+    # under both scale forms, so attention agrees bit for bit
+    g = np.random.default_rng(33)
+    n = 30
+    grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
+    ents = g.choice(grid, (n, 576)) * g.choice([-1, 1], (n, 576))
+    ents[:, ::16] = 6.0
+    ents = (ents * 2.0 ** np.repeat(g.integers(-3, 3, (n, 36)), 16, axis=1)).astype(np.float32)
+    cm = orc.Cache.empty(1, n, 576, 64, 16, 16, 64, k_format=1)
+    cf = orc.Cache.empty(1, n, 576, 64, 16, 16, 64)
+    for c in (cm, cf):
+        orc.kv_append(c, ents, np.array([0, n], np.int32), None, np.zeros((n, 64), np.uint16))
+    assert cm.k_scales.dtype == np.uint8 and cm.k_scales.shape == (1, n, 36) and cm.v_scales.shape == (1, n, 32)
+    q = g.standard_normal((1, 16, 576)).astype(np.float32)
+    idx = np.array([[0, 3, 29, 17, -1]], np.int32)
+    ring = _bf16_int(g.standard_normal((1, 4, 576)).astype(np.float32))
+    om, lm = orc.sparse_attn(cm, q, idx, ring, 0.04, swa_len=np.array([2], np.int32))
+    of, lf = orc.sparse_attn(cf, q, idx, ring, 0.04, swa_len=np.array([2], np.int32))
+    assert np.array_equal(om, of) and np.array_equal(lm, lf)
+
+
 def test_fp4_cache_scores_use_the_dequantised_keys(orc):
     g = np.random.default_rng(31)
     n, Di = 300, 64
