@@ -31,6 +31,7 @@ STATUS_BAD_STATE = 4
 MODE_FULL, MODE_REINDEX, MODE_REUSE = 0, 1, 2
 IDX_BF16, IDX_FP4 = 0, 1
 SWA_BF16, SWA_FP8 = 0, 1
+KV_F32, KV_MX16 = 0, 1
 MODES = {"full": MODE_FULL, "reindex": MODE_REINDEX, "reuse": MODE_REUSE}
 KERNEL_APPEND, KERNEL_SWA_APPEND, KERNEL_INDEXER_SCAN, KERNEL_TOPK_SELECT, KERNEL_ATTENTION = 1, 2, 3, 4, 5
 OP_INDEXER_TOPK, OP_SPARSE_ATTN, OP_LAYER_GROUP, OP_INDEXER_POOL, OP_INDEXER_IN_POOL = 1, 2, 3, 4, 5
@@ -56,7 +57,7 @@ class CacheDesc(C.Structure):
                 ("k_codes", C.c_void_p), ("k_scales", C.c_void_p), ("v_codes", C.c_void_p),
                 ("v_scales", C.c_void_p), ("idx_keys", C.c_void_p), ("n_tokens", C.c_void_p),
                 ("pending", C.c_void_p), ("status", C.c_void_p), ("idx_format", C.c_int32),
-                ("idx_scales", C.c_void_p), ("swa_format", C.c_int32)]
+                ("idx_scales", C.c_void_p), ("swa_format", C.c_int32), ("k_format", C.c_int32)]
 
 
 class LayerDesc(C.Structure):
@@ -162,23 +163,25 @@ class Cache:
     idx_format: int = 0                          # IDX_BF16, or IDX_FP4 (idx_keys u8 codes + idx_scales)
     idx_scales: Optional[torch.Tensor] = None
     swa_format: int = 0                          # window rings used with it: SWA_BF16, or SWA_FP8 (uint8 rings)
+    k_format: int = 0                            # KV_F32, or KV_MX16 (k_group 16, uint8 scale planes)
 
     @classmethod
     def allocate(cls, batch, capacity, k_group=32, v_group=0, idx_dim=128, dim=576, rope_dim=64,
-                 device="cuda", idx_format=0, swa_format=0):
+                 device="cuda", idx_format=0, swa_format=0, k_format=0):
         dv = dim - rope_dim
         z = lambda *s, dt: torch.zeros(*s, dtype=dt, device=device)
         fp4 = idx_format == IDX_FP4
+        st = torch.uint8 if k_format == KV_MX16 else torch.float32
         return cls(batch, capacity, k_group, v_group, idx_dim,
                    z(batch, capacity, dim // 2, dt=torch.uint8),
-                   z(batch, capacity, dim // k_group, dt=torch.float32),
+                   z(batch, capacity, dim // k_group, dt=st),
                    z(batch, capacity, dv // 2, dt=torch.uint8) if v_group else None,
-                   z(batch, capacity, dv // v_group, dt=torch.float32) if v_group else None,
+                   z(batch, capacity, dv // v_group, dt=st) if v_group else None,
                    z(batch, capacity, idx_dim // 2, dt=torch.uint8) if fp4
                    else z(batch, capacity, idx_dim, dt=torch.int16),
                    z(batch, dt=torch.int32), z(batch, dim, dt=torch.float32),
                    z(4, dt=torch.int32), dim, rope_dim, idx_format,
-                   z(batch, capacity, idx_dim // 16, dt=torch.uint8) if fp4 else None, swa_format)
+                   z(batch, capacity, idx_dim // 16, dt=torch.uint8) if fp4 else None, swa_format, k_format)
 
     def desc(self) -> CacheDesc:
         p = lambda t: None if t is None else t.data_ptr()
@@ -186,7 +189,7 @@ class Cache:
                          self.v_group, self.idx_dim, p(self.k_codes), p(self.k_scales),
                          p(self.v_codes), p(self.v_scales), p(self.idx_keys), p(self.n_tokens),
                          p(self.pending), p(self.status), self.idx_format, p(self.idx_scales),
-                         self.swa_format)
+                         self.swa_format, self.k_format)
 
     def entry_bytes(self) -> int:
         return entry_bytes(self.dim, self.rope_dim, self.k_group, self.v_group, self.idx_dim)

@@ -47,10 +47,17 @@ int check_cache(const cskv_cache *c)
             "capacity %d out of [1, 2^26]", c->capacity);
     REQUIRE(c->dim == 576 && c->rope_dim == 64, CSKV_EUNSUPPORTED,
             "dim %d / rope_dim %d: only 576 / 64 are built", c->dim, c->rope_dim);
-    REQUIRE(c->k_group == 32 || c->k_group == 64, CSKV_EUNSUPPORTED,
-            "k_group %d: 32 or 64 supported (must divide 576)", c->k_group);
-    REQUIRE(c->v_group == 0 || c->v_group == 32 || c->v_group == 64 || c->v_group == 128,
-            CSKV_EUNSUPPORTED, "v_group %d: 0, 32, 64 or 128 supported", c->v_group);
+    REQUIRE(c->k_format == CSKV_KV_F32 || c->k_format == CSKV_KV_MX16, CSKV_EUNSUPPORTED,
+            "k_format %d: CSKV_KV_F32 or CSKV_KV_MX16", c->k_format);
+    if (c->k_format == CSKV_KV_MX16) {
+        REQUIRE(c->k_group == 16 && (c->v_group == 0 || c->v_group == 16), CSKV_EUNSUPPORTED,
+                "k_group %d / v_group %d: CSKV_KV_MX16 takes 16 / 0 or 16", c->k_group, c->v_group);
+    } else {
+        REQUIRE(c->k_group == 32 || c->k_group == 64, CSKV_EUNSUPPORTED,
+                "k_group %d: 32 or 64 supported (must divide 576)", c->k_group);
+        REQUIRE(c->v_group == 0 || c->v_group == 32 || c->v_group == 64 || c->v_group == 128,
+                CSKV_EUNSUPPORTED, "v_group %d: 0, 32, 64 or 128 supported", c->v_group);
+    }
     REQUIRE(c->idx_dim == 64 || c->idx_dim == 128, CSKV_EUNSUPPORTED,
             "idx_dim %d: 64 or 128 supported", c->idx_dim);
     REQUIRE(c->k_codes && c->k_scales && c->idx_keys && c->n_tokens && c->pending && c->status,

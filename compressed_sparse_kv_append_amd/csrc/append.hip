@@ -248,6 +248,31 @@ __device__ void quantize_idx_fp4(float x, int t, uint8_t *codes_row, uint8_t *sc
     if ((t & 15) == 0) scales_row[t >> 4] = (uint8_t)(e + 127);
 }
 
+// The pages' main-entry form [P2 四、"P4 main KV" (E2M1, one 8-bit scale per
+// 16 channels)]: channel t of a row of n; each 16-channel group (inside one
+// wave) takes the E8M0 scale 2^(floor(log2 amax) - 2), byte 0 and zero codes
+// when amax = 0.  Called by all threads of the block.
+__device__ void quantize_channel_mx16(float x, int t, int n, uint8_t *codes_row, uint8_t *scales_row)
+{
+    const bool live = t < n;
+    float a = live ? fabsf(x) : 0.0f;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) a = fmaxf(a, __shfl_xor(a, off));
+    int e = -127;
+    if (a > 0.0f) {
+        int ex;
+        (void)frexpf(a, &ex);
+        e = ex - 1 - 2;
+        e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    }
+    uint32_t code = (live && a > 0.0f) ? e2m1_code(ldexpf(x, -e)) : 0u;
+    code |= __shfl_down(code, 1) << 4;
+    code |= __shfl_down(code, 2) << 8;
+    code |= __shfl_down(code, 4) << 16;
+    if (live && (t & 7) == 0) *reinterpret_cast<uint32_t *>(codes_row + (t >> 1)) = code;
+    if (live && (t & 15) == 0) scales_row[t >> 4] = (uint8_t)(e + 127);
+}
+
 // Sequence b after its rows are quantised: store the trailing odd token,
 // advance n_tokens, or flag a rejected sequence.  p is n_tokens[b] as the
 // append found it.  Returns the sequence's token count afterwards.
@@ -303,12 +328,22 @@ __global__ __launch_bounds__(kAppendThreads) void quantize_kernel(AppendArgs a)
     if (ri.entry >= 0) {
         const float e = kCompress ? a.ent[(size_t)r * kDim + t] : a.tokens[(size_t)r * kDim + t];
         const size_t slot = (size_t)ri.b * c.capacity + (size_t)ri.entry;
-        quantize_channel(e, t, kDim, c.k_group, c.k_codes + slot * (kDim / 2),
-                         c.k_scales + slot * (kDim / c.k_group), wave_max);
-        if (c.v_group > 0) {
-            const int dv = c.dim - c.rope_dim;
-            quantize_channel(e, t, dv, c.v_group, c.v_codes + slot * (dv / 2),
-                             c.v_scales + slot * (dv / c.v_group), wave_max);
+        if (c.k_format == CSKV_KV_MX16) {
+            quantize_channel_mx16(e, t, kDim, c.k_codes + slot * (kDim / 2),
+                                  reinterpret_cast<uint8_t *>(c.k_scales) + slot * (kDim / 16));
+            if (c.v_group > 0) {
+                const int dv = c.dim - c.rope_dim;
+                quantize_channel_mx16(e, t, dv, c.v_codes + slot * (dv / 2),
+                                      reinterpret_cast<uint8_t *>(c.v_scales) + slot * (dv / 16));
+            }
+        } else {
+            quantize_channel(e, t, kDim, c.k_group, c.k_codes + slot * (kDim / 2),
+                             c.k_scales + slot * (kDim / c.k_group), wave_max);
+            if (c.v_group > 0) {
+                const int dv = c.dim - c.rope_dim;
+                quantize_channel(e, t, dv, c.v_group, c.v_codes + slot * (dv / 2),
+                                 c.v_scales + slot * (dv / c.v_group), wave_max);
+            }
         }
         if (c.idx_format == CSKV_IDX_FP4) {
             if (t < c.idx_dim)                      // whole waves: idx_dim is 64 or 128

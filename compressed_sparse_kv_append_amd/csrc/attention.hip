@@ -202,7 +202,10 @@ __device__ __forceinline__ uint32_t row_off(int32_t e, uint32_t row_bytes)
     return e >= 0 ? (uint32_t)e * row_bytes : kMasked;
 }
 
-template <bool SPLIT, int VGS>
+// KG = 16: the pages' scale form (CSKV_KV_MX16): one E8M0 byte per 16
+// channels, key rows of 36 bytes and value rows of 32; the scale words are
+// loaded raw and spread to bytes in LDS ([group][key], in the ks / vs space).
+template <bool SPLIT, int VGS, int KG>
 __device__ __forceinline__ void fetch_sparse(const AttnArgs &a, const AttnSmem &sm, const Ctx &x, int lc,
                                              SparseRegs &r)
 {
@@ -242,6 +245,28 @@ __device__ __forceinline__ void fetch_sparse(const AttnArgs &a, const AttnSmem &
             r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, (int)off, 0, 0);
         }
     }
+    if constexpr (KG == 16) {
+        constexpr uint32_t kKRow = kD / 16, kVRow = kDv / 16;          // scale bytes per row
+        const __amdgpu_buffer_rsrc_t kb8 =
+            make_rsrc(reinterpret_cast<const uint8_t *>(c.k_scales) + x.row0 * kKRow, cap * kKRow);
+        const uint32_t so = row_off(es, kKRow);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {                      // dwords t / 128 + 4 i of 9
+            const int d = min((x.t >> 7) + 4 * i, (int)kKRow / 4 - 1);
+            r.sc[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(kb8, (int)(so + 4 * d), 0, 0));
+        }
+        if (SPLIT) {
+            const __amdgpu_buffer_rsrc_t vb8 =
+                make_rsrc(reinterpret_cast<const uint8_t *>(c.v_scales) + x.row0 * kVRow, cap * kVRow);
+            const uint32_t vo = row_off(es, kVRow);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {                  // dwords t / 128 + 4 i of 8
+                const int d = (x.t >> 7) + 4 * i;
+                r.sc[5 + i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vb8, (int)(vo + 4 * d), 0, 0));
+            }
+        }
+        return;
+    }
     const uint32_t so = row_off(es, 4 * x.G);
 #pragma unroll
     for (int i = 0; i < 5; ++i) {                          // key scales: group t / 128 + 4 i
@@ -259,7 +284,7 @@ __device__ __forceinline__ void fetch_sparse(const AttnArgs &a, const AttnSmem &
     }
 }
 
-template <bool SPLIT, int VGS>
+template <bool SPLIT, int VGS, int KG>
 __device__ __forceinline__ void store_sparse(AttnSmem &sm, const Ctx &x, const SparseRegs &r)
 {
     constexpr int VG = kDv / VGS;
@@ -296,6 +321,29 @@ __device__ __forceinline__ void store_sparse(AttnSmem &sm, const Ctx &x, const S
         }
     }
     const int key = x.t & (kSK - 1);
+    if constexpr (KG == 16) {
+        uint8_t *kb = reinterpret_cast<uint8_t *>(&sm.ks[0][0]);            // [36][kSK] bytes
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int d = (x.t >> 7) + 4 * i;
+            const uint32_t w = __float_as_uint(r.sc[i]);
+            if (d < kD / 64) {
+#pragma unroll
+                for (int by = 0; by < 4; ++by) kb[(4 * d + by) * kSK + key] = (uint8_t)(w >> (8 * by));
+            }
+        }
+        if (SPLIT) {
+            uint8_t *vb = reinterpret_cast<uint8_t *>(&sm.vs[0][0]);        // [32][kSK] bytes
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int d = (x.t >> 7) + 4 * i;
+                const uint32_t w = __float_as_uint(r.sc[5 + i]);
+#pragma unroll
+                for (int by = 0; by < 4; ++by) vb[(4 * d + by) * kSK + key] = (uint8_t)(w >> (8 * by));
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
         const int g = (x.t >> 7) + 4 * i;
@@ -366,6 +414,29 @@ __device__ __forceinline__ void sparse_logits_half(AttnSmem &sm, const Ctx &x)
     const uint32_t *k1 = sm.st.sp.kc + j1 * kKcRow + x.grp;
     f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     f32x4_t p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (KG == 16) {
+        // E8M0 scales per 16 channels: a code word (8 dims) lies inside one
+        // group, so the power-of-two scale goes into the conversion (exact)
+        // and the logits need no per-group scaling
+        const uint8_t *kb = reinterpret_cast<const uint8_t *>(&sm.ks[0][0]);
+#pragma unroll
+        for (int s = 0; s < kHalf; ++s) {
+            const int step = kHalf * HALF + s, g = 2 * step + (x.grp >> 1);
+            const u32x4_t qh = sm.q[step][0][x.lane], ql = sm.q[step][1][x.lane];
+            const u32x4_t kb0 = fp4x8_scaled_to_bf16x8(k0[4 * step], e8m0_to_f32(kb[g * kSK + j0]));
+            const u32x4_t kb1 = fp4x8_scaled_to_bf16x8(k1[4 * step], e8m0_to_f32(kb[g * kSK + j1]));
+            acc0 = mfma16x16x32(qh, kb0, acc0);
+            acc1 = mfma16x16x32(qh, kb1, acc1);
+            acc0 = mfma16x16x32(ql, kb0, acc0);
+            acc1 = mfma16x16x32(ql, kb1, acc1);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            sm.s[HALF][4 * x.grp + v][j0] = acc0[v];
+            sm.s[HALF][4 * x.grp + v][j1] = acc1[v];
+        }
+        return;
+    }
 #pragma unroll
     for (int s = 0; s < kHalf; ++s) {
         const int step = kHalf * HALF + s;
@@ -505,7 +576,16 @@ __device__ __forceinline__ void chunk_pv(const AttnSmem &sm, const Ctx &x, f32x4
 #pragma unroll
         for (int gi = 0; gi < (SPARSE ? kGroupsHere : 1); ++gi) {
             float pv[8];
-            if (SPARSE) {
+            if (SPARSE && VGS == 16) {
+                // E8M0 bytes [group][key] (value plane, else the key plane's
+                // first 32 groups)
+                const int gv = 4 * x.w + gi;
+                const uint8_t *vb = reinterpret_cast<const uint8_t *>(SPLIT ? &sm.vs[0][0] : &sm.ks[0][0]);
+                const uint2 sv = *reinterpret_cast<const uint2 *>(vb + gv * kSK + key0);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    pv[i] = pr[i] * e8m0_to_f32(((i < 4 ? sv.x : sv.y) >> (8 * (i & 3))) & 0xFFu);
+            } else if (SPARSE) {
                 const int gv = (64 * x.w) / VGS + gi;
                 const float *vsr = SPLIT ? &sm.vs[gv][key0] : &sm.ks[gv][key0];
                 const float4 v0 = *reinterpret_cast<const float4 *>(vsr);
@@ -547,12 +627,12 @@ __device__ __forceinline__ void run_chunks(const AttnArgs &a, AttnSmem &sm, cons
 {
     if (SPARSE) {
         SparseRegs r;
-        fetch_sparse<SPLIT, VGS>(a, sm, x, first, r);
+        fetch_sparse<SPLIT, VGS, KG>(a, sm, x, first, r);
         for (int lc = first; lc < end; ++lc) {
             __syncthreads();                               // previous chunk fully consumed
-            store_sparse<SPLIT, VGS>(sm, x, r);
+            store_sparse<SPLIT, VGS, KG>(sm, x, r);
             __syncthreads();
-            if (lc + 1 < end) fetch_sparse<SPLIT, VGS>(a, sm, x, lc + 1, r);
+            if (lc + 1 < end) fetch_sparse<SPLIT, VGS, KG>(a, sm, x, lc + 1, r);
             chunk_logits<true, KG>(sm, x);
             __syncthreads();
             chunk_softmax<true>(sm, x, lc, a.scale_log2);
@@ -809,6 +889,11 @@ hipError_t launch_sparse_attn(const cskv_cache &c, const float *q, int heads, co
     auto attn = [&](auto kernel) { launch_kernel(kernel, dim3(blocks), dim3(kThreads), s, tl.start, stop_main, a); };
     auto pick = [&](auto w8) {
         constexpr bool W8 = decltype(w8)::value;
+        if (c.k_format == CSKV_KV_MX16) {
+            if (c.v_group > 0) attn(sparse_attn_kernel<16, true, 16, W8>);
+            else attn(sparse_attn_kernel<16, false, 16, W8>);
+            return;
+        }
         if (c.v_group > 0) {
             if (c.k_group == 32) {
                 if (vgs == 32) attn(sparse_attn_kernel<32, true, 32, W8>);

@@ -213,24 +213,6 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
-// E8M0 byte -> the fp32 power of two it encodes (byte 0: 2^-127).
-__device__ __forceinline__ float e8m0_to_f32(uint32_t b)
-{
-    return __uint_as_float(b ? b << 23 : 0x00400000u);
-}
-
-// Eight E2M1 codes (one word, low nibble first) times a power of two ->
-// eight bf16 values; exact, E2M1 values having at most two significant bits.
-__device__ __forceinline__ u32x4_t fp4x8_scaled_to_bf16x8(uint32_t w, float scale)
-{
-    u32x4_t r;
-    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
-    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
-    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
-    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
-    return r;
-}
-
 // The scan over FP4 indexer keys (E2M1 codes + one E8M0 scale per 16 dims,
 // the pages' 72-byte key at DI = 128).  Tiles of 64 keys: a tile's codes
 // (DI/2 bytes per key, XOR-swizzled 16-byte chunks as in the bf16 scan) and

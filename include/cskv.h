@@ -90,7 +90,8 @@ extern "C" {
  *   pending  f32 [batch][dim]  the odd token waiting for its pair
  *   status   i32 [1]      CSKV_STATUS_* bits, sticky until the caller clears them
  * Supported here: dim 576, rope_dim 64, k_group 32 or 64, v_group 0, 32, 64
- * or 128, idx_dim 64 or 128, capacity <= 2^26.
+ * or 128 (CSKV_KV_MX16: k_group 16, v_group 0 or 16), idx_dim 64 or 128,
+ * capacity <= 2^26.
  */
 #define CSKV_IDX_BF16 0
 #define CSKV_IDX_FP4 1
@@ -101,6 +102,15 @@ extern "C" {
  * the even mantissa, saturating at +-448, sign kept. */
 #define CSKV_SWA_BF16 0
 #define CSKV_SWA_FP8 1
+/* Scale form of the key and value planes: one fp32 scale = absmax/6 per
+ * k_group / v_group channels (CSKV_KV_F32), or the pages' form
+ * (CSKV_KV_MX16) [P2 四、"P4 main KV" (E2M1 with one 8-bit scale per 16
+ * channels, OCP MXFP4)]: one E8M0 byte per 16 channels, scale =
+ * 2^(floor(log2 amax) - 2), codes = nearest E2M1 of x / scale; then k_group
+ * is 16, v_group 0 or 16, and k_scales / v_scales are byte planes
+ * [batch][capacity][dim/16] / [batch][capacity][(dim-rope_dim)/16]. */
+#define CSKV_KV_F32 0
+#define CSKV_KV_MX16 1
 typedef struct cskv_cache {
     int32_t batch, capacity, dim, rope_dim, k_group, v_group, idx_dim;
     uint8_t *k_codes;
@@ -114,6 +124,7 @@ typedef struct cskv_cache {
     int32_t idx_format;      /* CSKV_IDX_BF16 or CSKV_IDX_FP4 */
     uint8_t *idx_scales;     /* CSKV_IDX_FP4 only, else NULL */
     int32_t swa_format;      /* CSKV_SWA_BF16 or CSKV_SWA_FP8 */
+    int32_t k_format;        /* CSKV_KV_F32 or CSKV_KV_MX16 */
 } cskv_cache;
 
 /*

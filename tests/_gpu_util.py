@@ -23,12 +23,12 @@ def host(t: torch.Tensor) -> np.ndarray:
     return a.view(np.uint16) if a.dtype == np.int16 else a
 
 
-def pair(batch, capacity, k_group, v_group, idx_dim, idx_format=0, swa_format=0):
+def pair(batch, capacity, k_group, v_group, idx_dim, idx_format=0, swa_format=0, k_format=0):
     """An empty device cache and its empty host mirror with the same shape."""
     g = ck.Cache.allocate(batch, capacity, k_group, v_group, idx_dim, idx_format=idx_format,
-                          swa_format=swa_format)
+                          swa_format=swa_format, k_format=k_format)
     h = orc.Cache.empty(batch, capacity, 576, 64, k_group, v_group, idx_dim, idx_format=idx_format,
-                        swa_format=swa_format)
+                        swa_format=swa_format, k_format=k_format)
     return g, h
 
 
@@ -86,7 +86,9 @@ def lse_tol(h: orc.Cache, q: np.ndarray, idx: np.ndarray, ring: np.ndarray, swa_
         E = int(min(h.n_tokens[b] // 2, h.capacity))
         keys = []
         for e in idx[b]:
-            if 0 <= e < E:
+            if 0 <= e < E and h.k_format == 1:
+                keys.append(orc.dequantize_mx16(h.k_codes[b, e], h.k_scales[b, e], D))
+            elif 0 <= e < E:
                 keys.append(orc.dequantize_row(h.k_codes[b, e], h.k_scales[b, e], D, h.k_group))
         nw = int(min(swa_len[b], ring.shape[1]))
         if nw and ring.dtype == np.uint8:          # FP8 E4M3 rows

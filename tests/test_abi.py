@@ -48,7 +48,7 @@ def test_entry_bytes(L):
 def _desc(**over):
     d = dict(batch=2, capacity=64, dim=576, rope_dim=64, k_group=32, v_group=0, idx_dim=64,
              k_codes=0x10000, k_scales=0x20000, v_codes=None, v_scales=None, idx_keys=0x30000,
-             n_tokens=0x40000, pending=0x50000, status=0x60000, idx_format=0, idx_scales=None, swa_format=0)
+             n_tokens=0x40000, pending=0x50000, status=0x60000, idx_format=0, idx_scales=None, swa_format=0, k_format=0)
     d.update(over)
     return ck.CacheDesc(*[d[f] for f, _ in ck.CacheDesc._fields_])
 
@@ -72,6 +72,10 @@ def _err(L):
     (dict(idx_scales=0x68000), ck.EINVAL, "idx_scales"),
     (dict(idx_format=1, idx_scales=0x68004), ck.EINVAL, "aligned"),
     (dict(swa_format=2), ck.EUNSUPPORTED, "swa_format"),
+    (dict(k_format=2), ck.EUNSUPPORTED, "k_format"),
+    (dict(k_format=1), ck.EUNSUPPORTED, "k_group"),
+    (dict(k_group=16), ck.EUNSUPPORTED, "k_group"),
+    (dict(k_format=1, k_group=16, v_group=32), ck.EUNSUPPORTED, "v_group"),
 ])
 def test_cache_descriptor_rejected_before_launch(L, over, code, text):
     d = _desc(**over)
