@@ -65,6 +65,9 @@ def parse():
                    help="indexer-key storage: bf16, or the pages' FP4 form (E2M1 + E8M0 per 16 dims)")
     p.add_argument("--swa-format", choices=("bf16", "fp8"), default="bf16",
                    help="window rows: bf16, or the pages' FP8 (E4M3)")
+    p.add_argument("--kv-format", choices=("f32", "mx16"), default="f32",
+                   help="main entries: E2M1 with fp32 group scales, or the pages' form with one E8M0 "
+                   "byte per 16 channels (the workload's groups become 16)")
     p.add_argument("--pool", default="", help="pool_blocks,pool_block: the hierarchical indexer's candidate "
                    "pool in a layer-group workload (reindex layers select inside it)")
     return p.parse_args()
@@ -81,12 +84,12 @@ def copy_probe(mib: int):
     print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
 
 
-def build_replicas(ck, synth, w, cap, dev, n, idx_format=0, swa_format=0):
+def build_replicas(ck, synth, w, cap, dev, n, idx_format=0, swa_format=0, k_format=0):
     """Entries-mode build of n identical cache replicas, one sequence at a time
     (each sequence's entries are drawn once and appended to every replica)."""
     import torch
     reps = [ck.Cache.allocate(w.batch, cap, w.k_group, w.v_group, w.idx_dim, idx_format=idx_format,
-                              swa_format=swa_format) for _ in range(n)]
+                              swa_format=swa_format, k_format=k_format) for _ in range(n)]
     for b in range(w.batch):
         ents = dev(synth.cache_entries(w, b))
         keys = dev(synth.cache_idx_keys(w, b))
@@ -115,15 +118,16 @@ def scans_per_step(w, pool):
     return full, pooled
 
 
-def step_bytes(w, entries: float, pool=None, idx_fp4=False, swa_fp8=False) -> dict:
+def step_bytes(w, entries: float, pool=None, idx_fp4=False, swa_fp8=False, mx16=False) -> dict:
     """Algorithmic bytes of one step (whole batch): every plane read or written
     once by the method's definition; score arrays are not counted.  Scans: the
     whole indexer-key plane per full scan, the pooled positions' keys per
     pooled scan."""
     B, D, Dv, Di = w.batch, w.dim, w.vdim, w.idx_dim
-    entry_fp4 = D // 2 + 4 * (D // w.k_group)
+    sb = 1 if mx16 else 4                      # bytes per group scale
+    entry_fp4 = D // 2 + sb * (D // w.k_group)
     if w.v_group:
-        entry_fp4 += Dv // 2 + 4 * (Dv // w.v_group)
+        entry_fp4 += Dv // 2 + sb * (Dv // w.v_group)
     full, pooled = scans_per_step(w, pool)
     L = len(w.layers)
     sel = sum(1 for m in w.layers if m != "reuse")
@@ -145,7 +149,7 @@ def step_bytes(w, entries: float, pool=None, idx_fp4=False, swa_fp8=False) -> di
     return parts
 
 
-def cpu_baseline(synth, w, nseq: int, seconds: float, pool=None):
+def cpu_baseline(synth, w, nseq: int, seconds: float, pool=None, idx_format=0, swa_format=0, k_format=0):
     """The oracle, as it is, on a bounded sample: nseq of the batch's sequences
     at full length, consecutive decode steps until `seconds` have passed (at
     least one); the cache build is untimed."""
@@ -155,7 +159,8 @@ def cpu_baseline(synth, w, nseq: int, seconds: float, pool=None):
     sub = synth.scaled(w, batch=nseq)
     max_steps = 100
     cap = w.entries + max_steps // 2 + 8
-    hc = orc.Cache.empty(nseq, cap, w.dim, w.rope_dim, w.k_group, w.v_group, w.idx_dim)
+    hc = orc.Cache.empty(nseq, cap, w.dim, w.rope_dim, w.k_group, w.v_group, w.idx_dim,
+                         idx_format=idx_format, swa_format=swa_format, k_format=k_format)
     ents = np.concatenate([synth.cache_entries(w, b) for b in seqs])
     keys = np.concatenate([synth.cache_idx_keys(w, b) for b in seqs])
     cu = (np.arange(nseq + 1) * w.entries).astype(np.int32)
@@ -166,6 +171,15 @@ def cpu_baseline(synth, w, nseq: int, seconds: float, pool=None):
     st = synth.step_inputs(w, 0, seqs=seqs)
     W = synth.w_comp(w)
     rings = [r.copy() for r in st.swa_ring]
+    if swa_format:                             # the same rows in E4M3, written by the oracle
+        rings8 = []
+        for r in rings:
+            Bw, Ww, Dw = r.shape
+            r8 = np.zeros((Bw, Ww, Dw), np.uint8)
+            orc.swa_append(r8, (r.astype(np.uint32) << 16).view(np.float32).reshape(Bw * Ww, Dw),
+                           (np.arange(Bw + 1) * Ww).astype(np.int32), np.full(Bw, Ww, np.int32))
+            rings8.append(r8)
+        rings = rings8
     n_steps = 0
     t0 = time.perf_counter()
     while True:
@@ -227,6 +241,9 @@ def main():
     ck.lib()
     w = synth.WORKLOADS[a.workload]
     assert w.entries is not None, "bench steps fixed-length workloads"
+    mx16 = a.kv_format == "mx16"
+    if mx16:
+        w = synth.scaled(w, k_group=16, v_group=16 if w.v_group else 0)
     pool = tuple(int(x) for x in a.pool.split(",")) if a.pool else None
     timer_steps = min(a.steps, 100)
     dist_steps = min(a.steps, 100)
@@ -242,9 +259,9 @@ def main():
     idx_fp4 = a.idx_format == "fp4"
     swa_fp8 = a.swa_format == "fp8"
     reps = build_replicas(ck, synth, w, cap, dev, a.replicas, ck.IDX_FP4 if idx_fp4 else ck.IDX_BF16,
-                          ck.SWA_FP8 if swa_fp8 else ck.SWA_BF16)
+                          ck.SWA_FP8 if swa_fp8 else ck.SWA_BF16, ck.KV_MX16 if mx16 else ck.KV_F32)
     log(f"built {a.replicas} cache replicas in {time.time() - t0:.1f}s (indexer keys {a.idx_format}, "
-        f"window {a.swa_format})")
+        f"window {a.swa_format}, main entries {a.kv_format})")
 
     def ring_of(r16):
         """A layer's window ring: the bf16 ring, or the same rows written in FP8
@@ -358,7 +375,7 @@ def main():
 
     # mean entries per sequence over the timed steps
     entries_mean = float(0.5 * (ent_before + ent_after))
-    sb = step_bytes(w, entries_mean, pool, idx_fp4, swa_fp8)
+    sb = step_bytes(w, entries_mean, pool, idx_fp4, swa_fp8, mx16)
     n_full, n_pooled = scans_per_step(w, pool)
     scan_bytes = (sb["indexer_keys"] + sb["indexer_q"]) / (n_full + n_pooled)   # per launch, averaged
     scan = live if live is not None else kern["indexer_scan"]
@@ -379,7 +396,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; Student-t(3) cache entries, integer indexer inputs)",
         "config": {"workload": w.name, "batch": B, "context_tokens": 2 * w.entries,
-                   "entries_per_seq": w.entries, "k_group": w.k_group, "storage": "e2m1+fp32 scales",
+                   "entries_per_seq": w.entries, "k_group": w.k_group, "storage": "e2m1+e8m0/16" if mx16 else "e2m1+fp32 scales",
                    "idx_heads": w.idx_heads, "idx_dim": w.idx_dim, "q_heads": w.q_heads,
                    "topk": w.topk, "window": w.window, "replicas": a.replicas,
                    "launch": "hip_graph" if a.graph else "eager", "layers": list(w.layers),
@@ -390,7 +407,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": pmc_traffic() if (w.name == "decode_64k_b32" and not idx_fp4 and pool is None
-                                                  and not swa_fp8)
+                                                  and not swa_fp8 and not mx16)
                      else None, "kernel": "indexer_scan",
                      "bytes_per_launch": round(scan_bytes), "avg_us": round(scan_us, 2),
                      "timed_launches": scan["launches"], "scans_per_step": [n_full, n_pooled],
@@ -406,7 +423,8 @@ def main():
     }
     if not a.no_cpu_baseline:
         log("timing the oracle on a CPU sample ...")
-        result["cpu_baseline"] = cpu_baseline(synth, w, a.cpu_baseline_seqs, a.cpu_baseline_seconds, pool)
+        result["cpu_baseline"] = cpu_baseline(synth, w, a.cpu_baseline_seqs, a.cpu_baseline_seconds, pool,
+                                              int(idx_fp4), int(swa_fp8), int(mx16))
     print(json.dumps(result), flush=True)
 
 

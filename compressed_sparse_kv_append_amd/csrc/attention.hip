@@ -583,8 +583,8 @@ __device__ __forceinline__ void chunk_pv(const AttnSmem &sm, const Ctx &x, f32x4
                 const uint8_t *vb = reinterpret_cast<const uint8_t *>(SPLIT ? &sm.vs[0][0] : &sm.ks[0][0]);
                 const uint2 sv = *reinterpret_cast<const uint2 *>(vb + gv * kSK + key0);
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    pv[i] = pr[i] * e8m0_to_f32(((i < 4 ? sv.x : sv.y) >> (8 * (i & 3))) & 0xFFu);
+                for (int i = 0; i < 8; ++i)             // p * 2^(byte - 127), exact in one ldexp
+                    pv[i] = ldexpf(pr[i], (int)(((i < 4 ? sv.x : sv.y) >> (8 * (i & 3))) & 0xFFu) - 127);
             } else if (SPARSE) {
                 const int gv = (64 * x.w) / VGS + gi;
                 const float *vsr = SPLIT ? &sm.vs[gv][key0] : &sm.ks[gv][key0];
