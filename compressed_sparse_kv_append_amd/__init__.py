@@ -40,7 +40,7 @@ EXPORTS = ("cskv_kv_append_fp4", "cskv_append_workspace_bytes", "cskv_swa_append
            "cskv_indexer_topk",
            "cskv_indexer_topk_pool", "cskv_indexer_topk_in_pool", "cskv_sparse_attn_decode",
            "cskv_layer_group_decode", "cskv_layer_group_decode_pooled", "cskv_workspace_bytes",
-           "cskv_workspace_bytes_pool", "cskv_entry_bytes", "cskv_last_error",
+           "cskv_workspace_bytes_pool", "cskv_entry_bytes", "cskv_cache_entry_bytes", "cskv_last_error",
            "cskv_timer_enable", "cskv_timer_pause", "cskv_timer_read", "cskv_timer_disable_all")
 
 
@@ -98,6 +98,8 @@ def lib():
         L.cskv_workspace_bytes_pool.restype = sz
         L.cskv_entry_bytes.argtypes = [i32] * 5
         L.cskv_entry_bytes.restype = sz
+        L.cskv_cache_entry_bytes.argtypes = [vp]
+        L.cskv_cache_entry_bytes.restype = sz
         L.cskv_last_error.restype = C.c_char_p
         L.cskv_timer_enable.argtypes = [i32, i32]
         L.cskv_timer_pause.argtypes = [i32, i32]
@@ -192,7 +194,12 @@ class Cache:
                          self.swa_format, self.k_format)
 
     def entry_bytes(self) -> int:
-        return entry_bytes(self.dim, self.rope_dim, self.k_group, self.v_group, self.idx_dim)
+        """Bytes per entry in this cache's formats."""
+        d = self.desc()
+        n = lib().cskv_cache_entry_bytes(C.byref(d))
+        if n == 0:
+            raise CskvError(EINVAL, lib().cskv_last_error().decode())
+        return int(n)
 
 
 def workspace_bytes(cache: Cache, k: int, op: int = OP_INDEXER_TOPK, n_heads: int = 0,

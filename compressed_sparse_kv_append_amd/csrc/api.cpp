@@ -209,6 +209,20 @@ size_t cskv_entry_bytes(int32_t dim, int32_t rope_dim, int32_t k_group, int32_t 
     return b;
 }
 
+size_t cskv_cache_entry_bytes(const cskv_cache *cache)
+{
+    if (check_cache(cache) != CSKV_OK) return 0;
+    const cskv_cache &c = *cache;
+    const size_t per_scale = c.k_format == CSKV_KV_MX16 ? 1 : 4;
+    size_t b = (size_t)c.dim / 2 + per_scale * (size_t)(c.dim / c.k_group);
+    if (c.v_group > 0) {
+        const int dv = c.dim - c.rope_dim;
+        b += (size_t)dv / 2 + per_scale * (size_t)(dv / c.v_group);
+    }
+    b += c.idx_format == CSKV_IDX_FP4 ? (size_t)c.idx_dim / 2 + (size_t)c.idx_dim / 16 : 2 * (size_t)c.idx_dim;
+    return b;
+}
+
 size_t cskv_workspace_bytes(const cskv_cache *cache, int32_t op, int32_t n_heads, int32_t k,
                             int32_t window)
 {

@@ -327,6 +327,17 @@ size_t cskv_workspace_bytes_pool(const cskv_cache *cache, int32_t op, int32_t n_
 size_t cskv_entry_bytes(int32_t dim, int32_t rope_dim, int32_t k_group, int32_t v_group,
                         int32_t idx_dim);
 
+/* Bytes one entry of *cache occupies in the cache's own formats
+ * [P2 四、"P4 main KV" and "890 字节是怎么算出来的"]: key codes dim/2, key
+ * scales 4 B per k_group channels (CSKV_KV_F32) or 1 B per 16 (CSKV_KV_MX16),
+ * the value plane likewise when v_group > 0, and the indexer key: 2 B per
+ * dim (CSKV_IDX_BF16) or idx_dim/2 + idx_dim/16 (CSKV_IDX_FP4).  In the
+ * pages' formats with split planes the value row (512 latent dims) is 288 B
+ * and the indexer key 72 B.  Host only; the plane pointers are checked for
+ * presence and alignment but never read.  Returns 0 for a descriptor that
+ * every entry point would reject (cskv_last_error says why). */
+size_t cskv_cache_entry_bytes(const cskv_cache *cache);
+
 /* Thread-local description of the last error (host string, never NULL). */
 const char *cskv_last_error(void);
 

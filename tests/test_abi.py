@@ -57,6 +57,25 @@ def _err(L):
     return L.cskv_last_error().decode()
 
 
+def test_cache_entry_bytes_in_each_format(L):
+    n = lambda **o: L.cskv_cache_entry_bytes(C.byref(_desc(**o)))
+    # fp32 scales, bf16 indexer keys: the shape-only helper's figure
+    assert n(k_group=64, idx_dim=128) == ck.entry_bytes(576, 64, 64, 0, 128) == 288 + 36 + 256
+    assert n(k_group=32, v_group=128, v_codes=0x70000, v_scales=0x80000, idx_dim=64) == \
+        ck.entry_bytes(576, 64, 32, 128, 64)
+    # the pages' formats with split planes: the value row (512 latent dims,
+    # E2M1 + one byte per 16) is their 288 B main entry and the FP4 indexer
+    # key their 72 B; the key plane adds the 576-dim row with its RoPE dims
+    pages = dict(k_format=1, k_group=16, v_group=16, v_codes=0x70000, v_scales=0x80000, idx_dim=128,
+                 idx_format=1, idx_scales=0x90000)
+    key_row = 576 // 2 + 576 // 16
+    assert n(**pages) == key_row + 288 + 72
+    assert n(**pages) - key_row == 360
+    # shared planes: the key row carries the values
+    assert n(**dict(pages, v_group=0, v_codes=None, v_scales=None)) == 324 + 72
+    assert n(k_format=1, k_group=32) == 0 and "k_group" in _err(L)
+
+
 @pytest.mark.parametrize("over,code,text", [
     (dict(dim=512), ck.EUNSUPPORTED, "dim"),
     (dict(k_group=128), ck.EUNSUPPORTED, "k_group"),

@@ -217,3 +217,18 @@ def test_layer_group_mx16(ck, orc, v_group, fp8):
         if L.idx is not None:
             assert np.array_equal(host(L.idx), idxs[li])
         assert attn_rel_err(host(L.out), outs[li]).max() <= TOL
+
+
+def test_live_cache_rows_in_the_pages_formats(ck, orc):
+    # a device cache in the pages' formats, filled by the append: the value
+    # row (512 latent dims) is 288 B, the FP4 indexer key 72 B, and the
+    # library's per-entry figure is the sum of every plane's row
+    gc, hc = pair(2, 40, 16, 16, 128, idx_format=1, k_format=MX16)
+    g = np.random.default_rng(370)
+    load_entries(gc, hc, [synth.normal(g, (n, 576)) for n in (30, 7)], [synth.int_bf16(g, (n, 128)) for n in (30, 7)])
+    assert_cache_equal(gc, hc)
+    row = lambda t: t[0, 0].numel() * t.element_size()
+    assert row(gc.v_codes) + row(gc.v_scales) == 288
+    assert row(gc.idx_keys) + row(gc.idx_scales) == 72
+    planes = (gc.k_codes, gc.k_scales, gc.v_codes, gc.v_scales, gc.idx_keys, gc.idx_scales)
+    assert gc.entry_bytes() == sum(row(t) for t in planes) == 324 + 288 + 72
