@@ -53,7 +53,7 @@ class _Cache(C.Structure):
                 ("idx_keys", C.POINTER(C.c_uint16)), ("n_tokens", C.POINTER(C.c_int32)),
                 ("pending", C.POINTER(C.c_float)), ("status", C.POINTER(C.c_int32)),
                 ("idx_format", C.c_int32), ("idx_scales", C.POINTER(C.c_uint8)),
-                ("swa_format", C.c_int32), ("k_format", C.c_int32)]
+                ("swa_format", C.c_int32), ("k_format", C.c_int32), ("ratio", C.c_int32)]
 
 
 def _declare(L):
@@ -94,6 +94,8 @@ def _declare(L):
     L.orc_dequantize_row.restype = None
     L.orc_dequantize_row.argtypes = [P(C.c_uint8), P(C.c_float), C.c_int, C.c_int, P(f64)]
     L.orc_kv_append.restype = None
+    L.orc_ced_project.restype = None
+    L.orc_ced_project.argtypes = [P(C.c_uint16), i64, C.c_int, P(C.c_uint16), C.c_int, P(C.c_float)]
     L.orc_kv_append.argtypes = [P(_Cache), P(C.c_float), P(i32), P(C.c_float), P(C.c_uint16)]
     L.orc_swa_append.restype = None
     L.orc_swa_append.argtypes = [P(C.c_uint16), C.c_int, C.c_int, C.c_int, P(C.c_float),
@@ -281,10 +283,13 @@ class Cache:
     idx_scales: Optional[np.ndarray] = None   # E8M0 u8 [B][cap][Di/16] (idx_format 1)
     swa_format: int = 0                        # window rings used with this cache: 0 bf16, 1 FP8 E4M3
     k_format: int = 0                          # 1: E8M0 byte scales per 16 channels (k_group 16)
+    ratio: int = 2                             # tokens per entry: 2 (compressed pairs) or 1
 
     @classmethod
     def empty(cls, batch, capacity, dim=576, rope_dim=64, k_group=32, v_group=0, idx_dim=128,
-              idx_format=0, swa_format=0, k_format=0):
+              idx_format=0, swa_format=0, k_format=0, ratio=2):
+        if ratio not in (1, 2):
+            raise ValueError(f"ratio {ratio}: 1 or 2 tokens per entry")
         Dv = dim - rope_dim
         fp4 = idx_format == 1
         st = np.uint8 if k_format == 1 else np.float32
@@ -298,7 +303,7 @@ class Cache:
                    np.zeros(batch, np.int32), np.zeros((batch, dim), np.float32),
                    np.zeros(1, np.int32), idx_format,
                    np.zeros((batch, capacity, idx_dim // 16), np.uint8) if fp4 else None, swa_format,
-                   k_format)
+                   k_format, ratio)
 
     def _c(self) -> _Cache:
         return _Cache(self.batch, self.capacity, self.dim, self.rope_dim, self.k_group,
@@ -307,10 +312,11 @@ class Cache:
                       _p(self.v_codes, C.c_uint8), _p(self.v_scales, C.c_float),
                       _p(self.idx_keys, C.c_uint16), _p(self.n_tokens, C.c_int32),
                       _p(self.pending, C.c_float), _p(self.status, C.c_int32),
-                      self.idx_format, _p(self.idx_scales, C.c_uint8), self.swa_format, self.k_format)
+                      self.idx_format, _p(self.idx_scales, C.c_uint8), self.swa_format, self.k_format,
+                      self.ratio)
 
     def entries(self) -> np.ndarray:
-        return np.clip(self.n_tokens // 2, 0, self.capacity)
+        return np.clip(self.n_tokens // self.ratio, 0, self.capacity)
 
 
 def kv_append(cache: Cache, tokens, cu_new, w_comp, idx_rows) -> None:
@@ -319,6 +325,8 @@ def kv_append(cache: Cache, tokens, cu_new, w_comp, idx_rows) -> None:
     assert cu.shape == (cache.batch + 1,)
     irows = np.ascontiguousarray(idx_rows, np.uint16).reshape(-1, cache.idx_dim)
     W = None if w_comp is None else _f32(w_comp)
+    if W is not None and cache.ratio != 2:
+        raise ValueError("the 2->1 compressor needs a ratio-2 cache")
     c = cache._c()
     lib().orc_kv_append(C.byref(c), _p(tokens, C.c_float), _p(cu, C.c_int32),
                         _p(W, C.c_float), _p(irows, C.c_uint16))
@@ -431,3 +439,52 @@ def layer_group_decode(cache: Cache, modes, new_token, new_idx_row, w_comp, q, q
         lses.append(l)
         idxs.append(last_idx)
     return outs, lses, idxs
+
+
+# ---------------------------------------------------------------- CED and the 40-layer plan
+
+def ced_project(h_bits, w_bits) -> np.ndarray:
+    """The decoder's global KV rows from one hidden state [P2 四、"CED：上半段模型
+    的 KV 由下半段代算"]: h bf16 bits [rows, d_model], w bf16 bits [n_out,
+    d_model] (a row per output channel) -> fp32 [rows, n_out], each output the
+    fp64 sum of its d_model products rounded once."""
+    h = np.ascontiguousarray(h_bits, np.uint16)
+    w = np.ascontiguousarray(w_bits, np.uint16)
+    assert h.ndim == 2 and w.ndim == 2 and h.shape[1] == w.shape[1]
+    out = np.empty((h.shape[0], w.shape[0]), np.float32)
+    lib().orc_ced_project(_p(h, C.c_uint16), h.shape[0], h.shape[1], _p(w, C.c_uint16), w.shape[0],
+                          _p(out, C.c_float))
+    return out
+
+
+def csa2_plan():
+    """The pages' CSA2 layer plan [P2 四、"CSA2：三种模式，40 层只存 4 份"]: one
+    (name, tokens per entry, layer modes) per stored cache, in layer order.
+    Encoder: three groups of one Full and five Reuse layers, each group with
+    its own 2->1 cache.  Decoder: one cache read by its five groups, (Full +
+    3 Reuse) and then four times (Reindex + 3 Reuse); its entries are one per
+    token, computed by the CED projection.  The encoder's two layers outside
+    these groups have no mode in the pages and are not part of the plan."""
+    enc = [(f"encoder{i}", 2, ["full"] + ["reuse"] * 5) for i in range(3)]
+    dec = ("decoder", 1, ["full"] + ["reuse"] * 3 + (["reindex"] + ["reuse"] * 3) * 4)
+    return enc + [dec]
+
+
+def model_decode(groups, k, scale, pool=None):
+    """One decode step of every CSA2 layer in plan order.  groups: one dict
+    per cache with `cache`, `modes`, the per-layer lists `q`, `q_idx`,
+    `rings`, `swa_rows`, the new indexer-key rows `idx_row`, and the new
+    entries' source: `token` + `w_comp` (an encoder cache, 2->1 compressor)
+    or `ced_h` + `ced_w` (the decoder cache: one entry per token from the CED
+    projection).  pool = (nb, block) for groups with a Reindex layer.  Rings
+    are updated in place.  Returns (outs, lses, idxs) per group."""
+    res = []
+    for g in groups:
+        if g.get("ced_h") is not None:
+            new, w = ced_project(g["ced_h"], g["ced_w"]), None
+        else:
+            new, w = g["token"], g["w_comp"]
+        use_pool = pool if "reindex" in g["modes"] else None
+        res.append(layer_group_decode(g["cache"], g["modes"], new, g["idx_row"], w, g["q"], g["q_idx"],
+                                      g["rings"], g["swa_rows"], k, scale, pool=use_pool))
+    return res

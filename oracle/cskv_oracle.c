@@ -321,11 +321,12 @@ void orc_kv_append(orc_cache *c, const float *tokens, const int32_t *cu_new,
         const uint16_t *irows = idx_rows + (size_t)cu_new[b] * c->idx_dim;
         if (m == 0) { free(e); continue; }
         if (w_comp == NULL) {
-            if (p % 2 != 0) { raise_status(c, ORC_STATUS_ODD_ENTRY_APPEND); free(e); continue; }
-            if (p / 2 + m > c->capacity) { raise_status(c, ORC_STATUS_OVERFLOW); free(e); continue; }
+            const int r = c->ratio;                    /* tokens per entry */
+            if (p % r != 0) { raise_status(c, ORC_STATUS_ODD_ENTRY_APPEND); free(e); continue; }
+            if (p / r + m > c->capacity) { raise_status(c, ORC_STATUS_OVERFLOW); free(e); continue; }
             for (int64_t q = 0; q < m; ++q)
-                store_entry(c, b, p / 2 + q, rows + q * D, irows + q * c->idx_dim);
-            c->n_tokens[b] = (int32_t)(p + 2 * m);
+                store_entry(c, b, p / r + q, rows + q * D, irows + q * c->idx_dim);
+            c->n_tokens[b] = (int32_t)(p + (int64_t)r * m);
         } else {
             if ((p + m) / 2 > c->capacity) { raise_status(c, ORC_STATUS_OVERFLOW); free(e); continue; }
             for (int64_t q = 0; q < m; ++q) {
@@ -340,6 +341,20 @@ void orc_kv_append(orc_cache *c, const float *tokens, const int32_t *cu_new,
             c->n_tokens[b] = (int32_t)(p + m);
         }
         free(e);
+    }
+}
+
+void orc_ced_project(const uint16_t *h, int64_t rows, int d_model, const uint16_t *w, int n_out,
+                     float *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int n = 0; n < n_out; ++n) {
+            double s = 0.0;
+            for (int k = 0; k < d_model; ++k)
+                s += orc_bf16_value(h[r * d_model + k]) * orc_bf16_value(w[(int64_t)n * d_model + k]);
+            out[r * n_out + n] = (float)s;
+        }
     }
 }
 
@@ -434,7 +449,7 @@ static void cache_scores(const orc_cache *c, int b, int64_t E, const uint16_t *q
 
 static int64_t entries_of(const orc_cache *c, int b)
 {
-    int64_t e = c->n_tokens[b] / 2;
+    int64_t e = c->n_tokens[b] / c->ratio;
     if (e < 0) e = 0;
     if (e > c->capacity) e = c->capacity;
     return e;

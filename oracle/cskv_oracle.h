@@ -111,6 +111,10 @@ typedef struct {
     int32_t k_format;   /* 0: fp32 scale per k_group/v_group channels; 1: one E8M0 byte
                            per 16 channels in both planes (k_group 16, v_group 0 or 16;
                            k_scales / v_scales reinterpreted as bytes) */
+    int32_t ratio;      /* tokens per entry: 2 (token pairs compressed into one entry,
+                           the encoder caches) or 1 (one entry per token, the decoder
+                           cache fed by the CED projection) [P2 四、"CSA2：三种模式，
+                           40 层只存 4 份"; "890 字节是怎么算出来的"] */
 } orc_cache;
 
 #define ORC_STATUS_OVERFLOW 1
@@ -120,9 +124,9 @@ typedef struct {
  * tokens fp32 [total][dim]; cu_new [B+1] prefix sums of rows per sequence.
  * w_comp != NULL: rows are tokens, paired by absolute position (2i, 2i+1);
  *   an odd trailing token waits in pending[b]; entry i takes the indexer-key
- *   row of the token that completes it.
- * w_comp == NULL: rows are already entries (n_tokens += 2 per row); requires
- *   an even token count.
+ *   row of the token that completes it.  Ratio-2 caches only.
+ * w_comp == NULL: rows are already entries (n_tokens += ratio per row); a
+ *   ratio-2 cache requires an even token count.
  * A sequence whose entries would pass capacity is left untouched and raises
  * ORC_STATUS_OVERFLOW. */
 void orc_kv_append(orc_cache *c, const float *tokens, const int32_t *cu_new,
@@ -133,6 +137,18 @@ void orc_kv_append(orc_cache *c, const float *tokens, const int32_t *cu_new,
  * go to ring slot pos % W as bf16 [P2 "突破四"; "CSA2：三种模式"]. */
 void orc_swa_append(uint16_t *ring, int batch, int W, int dim, const float *rows,
                     const int32_t *cu_new, const int32_t *end_pos);
+
+/* ---------------- CED projection ----------------------------------------- */
+
+/* The decoder's global KV from one hidden state [P2 四、"CED：上半段模型的
+ * KV 由下半段代算" (the second half's KV is the first half's last output
+ * times a per-layer projection)]: out[r][n] = sum_k h[r][k] * w[n][k] over
+ * k < d_model, h bf16 [rows][d_model], w bf16 [n_out][d_model] (one row per
+ * output channel), summed in fp64 and rounded once to fp32.  Parity: pinned
+ * by closed forms (identity and rank-1 weights, linearity) and by exact
+ * integer brute force. */
+void orc_ced_project(const uint16_t *h, int64_t rows, int d_model, const uint16_t *w, int n_out,
+                     float *out);
 
 /* ---------------- FP4 indexer key ---------------------------------------- */
 

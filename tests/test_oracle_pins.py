@@ -847,3 +847,179 @@ def test_modes_with_candidate_pool(orc):
         sel = res["small"][2][1][b]
         assert set(sel[sel >= 0].tolist()) <= allowed and np.sum(sel >= 0) == 40
 
+
+
+# ---------------------------------------------------------------- CED projection and the layer plan
+
+def _bf16_bits(x):
+    """bf16 bits of values that bf16 holds exactly (small integers, powers of two)."""
+    a = np.asarray(x, np.float32)
+    bits = (a.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal((bits.astype(np.uint32) << 16).view(np.float32), a), "not exact in bf16"
+    return bits
+
+
+def test_ced_project_identity_and_one_hot(orc):
+    g = np.random.default_rng(500)
+    h = g.integers(-8, 9, (5, 600)).astype(np.float32)
+    eye = np.zeros((576, 600), np.float32)
+    eye[np.arange(576), np.arange(576)] = 1
+    assert np.array_equal(orc.ced_project(_bf16_bits(h), _bf16_bits(eye)), h[:, :576])
+    # a one-hot hidden state picks one input column of w: out[n] = w[n][j]
+    # (a transposed operand would pick row j instead)
+    w = g.integers(-4, 5, (576, 600)).astype(np.float32)
+    for j in (0, 17, 599):
+        e = np.zeros((1, 600), np.float32)
+        e[0, j] = 1
+        assert np.array_equal(orc.ced_project(_bf16_bits(e), _bf16_bits(w))[0], w[:, j])
+
+
+def test_ced_project_rank_one_and_linearity(orc):
+    g = np.random.default_rng(501)
+    dm = 256
+    a = g.integers(-3, 4, 576).astype(np.float32)
+    b = g.integers(-3, 4, dm).astype(np.float32)
+    h = g.integers(-8, 9, (4, dm)).astype(np.float32)
+    w = np.outer(a, b)                                 # w[n][k] = a[n] b[k]
+    got = orc.ced_project(_bf16_bits(h), _bf16_bits(w))
+    hb = [sum(int(x) * int(y) for x, y in zip(row, b)) for row in h]
+    assert np.array_equal(got, np.array([[float(s * int(an)) for an in a] for s in hb], np.float32))
+    h2 = g.integers(-8, 9, (4, dm)).astype(np.float32)
+    w2 = g.integers(-4, 5, (576, dm)).astype(np.float32)
+    lhs = orc.ced_project(_bf16_bits(h + h2), _bf16_bits(w2))
+    rhs = orc.ced_project(_bf16_bits(h), _bf16_bits(w2)) + orc.ced_project(_bf16_bits(h2), _bf16_bits(w2))
+    assert np.array_equal(lhs, rhs)
+
+
+def test_ced_project_brute_force_and_rounding(orc):
+    g = np.random.default_rng(502)
+    # tiny integer case against exact integer arithmetic
+    h = g.integers(-8, 9, (3, 40))
+    w = g.integers(-4, 5, (7, 40))
+    want = np.array([[sum(int(h[r, k]) * int(w[n, k]) for k in range(40)) for n in range(7)] for r in range(3)])
+    assert np.array_equal(orc.ced_project(_bf16_bits(h), _bf16_bits(w)), want.astype(np.float32))
+    # general bf16 inputs: within one fp32 rounding of the exact sum (math.fsum)
+    hb = (g.standard_normal((2, 300)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    wb = (g.standard_normal((5, 300)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    hv = (hb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    wv = (wb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    got = orc.ced_project(hb, wb)
+    for r in range(2):
+        for n in range(5):
+            terms = hv[r] * wv[n]
+            exact = math.fsum(terms)
+            bound = abs(exact) * 2.0 ** -24 + 300 * 2.0 ** -53 * np.abs(terms).sum()
+            assert abs(float(got[r, n]) - exact) <= bound
+
+
+def test_csa2_plan_matches_the_pages(orc):
+    g = GOLD["csa2_full_layers"]
+    plan = orc.csa2_plan()
+    enc, dec = plan[:3], plan[3]
+    assert len(plan) == 4                                       # 4 stored copies
+    assert all(m == g["encoder_group"] for _, _, m in enc)
+    assert dec[2] == g["decoder_first"] + g["decoder_rest"] * g["decoder_rest_groups"]
+    modes = [m for _, _, ms in plan for m in ms]
+    assert modes.count("full") == g["printed_full"] and len(modes) == 38
+    kv = GOLD["global_kv_per_token"]
+    assert [r for _, r, _ in plan] == [kv["encoder_ratio"]] * kv["encoder_copies"] + \
+        [kv["decoder_ratio"]] * kv["decoder_copies"]
+
+
+def test_plan_caches_in_the_pages_formats_hold_900_bytes_per_token(orc):
+    # live caches of the plan in the pages' formats (E2M1 + one E8M0 byte per
+    # 16 channels, split value plane; FP4 indexer keys): per token, each
+    # cache's value row (the 512 latent dims) and indexer key over its ratio
+    kv = GOLD["global_kv_per_token"]
+    total = 0.0
+    for _, ratio, _ in orc.csa2_plan():
+        c = orc.Cache.empty(1, 4, k_group=16, v_group=16, idx_dim=128, idx_format=1, k_format=1, ratio=ratio)
+        row = c.v_codes[0, 0].nbytes + c.v_scales[0, 0].nbytes + c.idx_keys[0, 0].nbytes + c.idx_scales[0, 0].nbytes
+        assert row == 360
+        total += row / ratio
+    assert total == kv["printed_estimate"]
+    assert abs(total - kv["printed_reported"]) / kv["printed_reported"] < 0.02
+
+
+def test_ratio_one_cache_stores_one_entry_per_token(orc):
+    # the same entries appended to a ratio-1 and a ratio-2 cache: identical
+    # planes, n_tokens m vs 2m; attention with the window length given is equal
+    g = np.random.default_rng(503)
+    rows = g.standard_normal((30, 576)).astype(np.float32)
+    keys = g.integers(-8, 9, (30, 64)).astype(np.float32)
+    keys = (keys.view(np.uint32) >> 16).astype(np.uint16)
+    c1 = orc.Cache.empty(1, 40, k_group=32, idx_dim=64, ratio=1)
+    c2 = orc.Cache.empty(1, 40, k_group=32, idx_dim=64, ratio=2)
+    cu = np.array([0, 30], np.int32)
+    orc.kv_append(c1, rows, cu, None, keys)
+    orc.kv_append(c2, rows, cu, None, keys)
+    assert c1.n_tokens[0] == 30 and c2.n_tokens[0] == 60
+    assert np.array_equal(c1.entries(), c2.entries())
+    for name in ("k_codes", "k_scales", "idx_keys"):
+        assert np.array_equal(getattr(c1, name), getattr(c2, name))
+    # a ratio-1 cache takes entries at any token count; the compressor is refused
+    orc.kv_append(c1, rows[:1], np.array([0, 1], np.int32), None, keys[:1])
+    assert c1.n_tokens[0] == 31 and c1.status[0] == 0
+    with pytest.raises(ValueError):
+        orc.kv_append(c1, rows[:2], np.array([0, 2], np.int32), np.zeros((576, 1152), np.float32), keys[:2])
+    q = g.standard_normal((1, 8, 576)).astype(np.float32)
+    idx = np.array([[0, 5, 29, -1]], np.int32)
+    ring = (g.standard_normal((1, 16, 576)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    sl = np.array([9], np.int32)
+    c1.n_tokens[0] = 30
+    o1, l1 = orc.sparse_attn(c1, q, idx, ring, 0.05, swa_len=sl)
+    o2, l2 = orc.sparse_attn(c2, q, idx, ring, 0.05, swa_len=sl)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # without swa_len the window length is the token count: 16 here (ring full)
+    o3, _ = orc.sparse_attn(c1, q, idx, ring, 0.05)
+    o4, _ = orc.sparse_attn(c1, q, idx, ring, 0.05, swa_len=np.array([16], np.int32))
+    assert np.array_equal(o3, o4)
+
+
+def test_model_decode_is_the_plan_of_layer_groups(orc):
+    # a tiny two-cache plan: an encoder group and the decoder group; each
+    # group's results are those of its own layer group, the decoder's new
+    # entry being the CED projection of the hidden state
+    g = np.random.default_rng(504)
+    B, dm = 2, 64
+    enc = orc.Cache.empty(B, 64, k_group=32, idx_dim=64)
+    dec = orc.Cache.empty(B, 64, k_group=32, idx_dim=64, ratio=1)
+    for c in (enc, dec):
+        orc.kv_append(c, g.standard_normal((B * 20, 576)).astype(np.float32), np.array([0, 20, 40], np.int32),
+                      None, (g.integers(-8, 9, (B * 20, 64)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16))
+    plan = [("encoder0", 2, ["full", "reuse"]), ("decoder", 1, ["full", "reuse", "reindex", "reuse"])]
+    W = (g.standard_normal((576, 1152)) * 0.02).astype(np.float32)
+    hid = _bf16_bits(g.integers(-8, 9, (B, dm)).astype(np.float32))
+    wced = _bf16_bits(g.integers(-4, 5, (576, dm)).astype(np.float32) * np.float32(2.0 ** -6))
+    groups, twins = [], []
+    for (name, ratio, modes), c in zip(plan, (enc, dec)):
+        n = len(modes)
+        grp = dict(cache=c, modes=modes, idx_row=(g.integers(-8, 9, (B, 64)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16),
+                   q=[g.standard_normal((B, 8, 576)).astype(np.float32) for _ in range(n)],
+                   q_idx=[None if m == "reuse" else (g.integers(-8, 9, (B, 2, 64)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16) for m in modes],
+                   rings=[np.zeros((B, 8, 576), np.uint16) for _ in range(n)],
+                   swa_rows=[g.standard_normal((B, 576)).astype(np.float32) for _ in range(n)])
+        if ratio == 1:
+            grp.update(ced_h=hid, ced_w=wced)
+        else:
+            grp.update(token=g.standard_normal((B, 576)).astype(np.float32), w_comp=W)
+        groups.append(grp)
+        twin = dict(grp, cache=orc.Cache(**{k: (v.copy() if isinstance(v, np.ndarray) else v)
+                                            for k, v in c.__dict__.items()}),
+                    rings=[r.copy() for r in grp["rings"]])
+        twins.append(twin)
+    res = orc.model_decode(groups, 16, 0.05, pool=(4, 2))
+    # the encoder group by itself
+    t = twins[0]
+    o, l, i = orc.layer_group_decode(t["cache"], t["modes"], t["token"], t["idx_row"], t["w_comp"], t["q"],
+                                     t["q_idx"], t["rings"], t["swa_rows"], 16, 0.05)
+    assert all(np.array_equal(a, b) for a, b in zip(o, res[0][0]))
+    # the decoder group: entries-mode append of the projected rows, pooled reindex
+    t = twins[1]
+    rows = orc.ced_project(hid, wced)
+    o, l, i = orc.layer_group_decode(t["cache"], t["modes"], rows, t["idx_row"], None, t["q"], t["q_idx"],
+                                     t["rings"], t["swa_rows"], 16, 0.05, pool=(4, 2))
+    assert all(np.array_equal(a, b) for a, b in zip(o, res[1][0]))
+    assert all(np.array_equal(a, b) for a, b in zip(i, res[1][2]))
+    assert dec.n_tokens.tolist() == [21, 21] and enc.n_tokens.tolist() == [41, 41]
+    assert np.array_equal(dec.k_codes, t["cache"].k_codes)
