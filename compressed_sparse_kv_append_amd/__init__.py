@@ -41,6 +41,7 @@ EXPORTS = ("cskv_kv_append_fp4", "cskv_append_workspace_bytes", "cskv_swa_append
            "cskv_indexer_topk_pool", "cskv_indexer_topk_in_pool", "cskv_sparse_attn_decode",
            "cskv_layer_group_decode", "cskv_layer_group_decode_pooled", "cskv_workspace_bytes",
            "cskv_workspace_bytes_pool", "cskv_entry_bytes", "cskv_cache_entry_bytes", "cskv_last_error",
+           "cskv_ced_project", "cskv_model_decode", "cskv_model_workspace_bytes",
            "cskv_timer_enable", "cskv_timer_pause", "cskv_timer_read", "cskv_timer_disable_all")
 
 
@@ -57,13 +58,21 @@ class CacheDesc(C.Structure):
                 ("k_codes", C.c_void_p), ("k_scales", C.c_void_p), ("v_codes", C.c_void_p),
                 ("v_scales", C.c_void_p), ("idx_keys", C.c_void_p), ("n_tokens", C.c_void_p),
                 ("pending", C.c_void_p), ("status", C.c_void_p), ("idx_format", C.c_int32),
-                ("idx_scales", C.c_void_p), ("swa_format", C.c_int32), ("k_format", C.c_int32)]
+                ("idx_scales", C.c_void_p), ("swa_format", C.c_int32), ("k_format", C.c_int32),
+                ("ratio", C.c_int32)]
 
 
 class LayerDesc(C.Structure):
     _fields_ = [("mode", C.c_int32), ("q", C.c_void_p), ("q_idx", C.c_void_p),
                 ("head_w", C.c_void_p), ("swa", C.c_void_p), ("swa_row", C.c_void_p),
                 ("idx", C.c_void_p), ("out", C.c_void_p), ("lse", C.c_void_p)]
+
+
+class GroupDesc(C.Structure):
+    _fields_ = [("cache", C.c_void_p), ("layers", C.c_void_p), ("n_layers", C.c_int32),
+                ("new_tokens", C.c_void_p), ("w_comp", C.c_void_p), ("ced_h", C.c_void_p),
+                ("ced_w", C.c_void_p), ("d_model", C.c_int32), ("new_idx_rows", C.c_void_p),
+                ("pool_blocks", C.c_int32), ("pool_block", C.c_int32)]
 
 
 _lib = None
@@ -99,6 +108,10 @@ def lib():
         L.cskv_entry_bytes.argtypes = [i32] * 5
         L.cskv_entry_bytes.restype = sz
         L.cskv_cache_entry_bytes.argtypes = [vp]
+        L.cskv_ced_project.argtypes = [vp, C.c_int64, i32, vp, i32, vp, vp]
+        L.cskv_model_decode.argtypes = [vp, i32, i32, i32, i32, i32, C.c_float, vp, sz, vp]
+        L.cskv_model_workspace_bytes.argtypes = [vp, i32, i32, i32, i32]
+        L.cskv_model_workspace_bytes.restype = sz
         L.cskv_cache_entry_bytes.restype = sz
         L.cskv_last_error.restype = C.c_char_p
         L.cskv_timer_enable.argtypes = [i32, i32]
@@ -107,7 +120,7 @@ def lib():
         for f in ("cskv_kv_append_fp4", "cskv_swa_append", "cskv_swa_append_fp8", "cskv_indexer_topk",
                   "cskv_indexer_topk_pool",
                   "cskv_indexer_topk_in_pool", "cskv_sparse_attn_decode", "cskv_layer_group_decode",
-                  "cskv_layer_group_decode_pooled", "cskv_timer_enable", "cskv_timer_pause", "cskv_timer_read",
+                  "cskv_layer_group_decode_pooled", "cskv_ced_project", "cskv_model_decode", "cskv_timer_enable", "cskv_timer_pause", "cskv_timer_read",
                   "cskv_timer_disable_all"):
             getattr(L, f).restype = C.c_int
         _lib = L
@@ -166,10 +179,11 @@ class Cache:
     idx_scales: Optional[torch.Tensor] = None
     swa_format: int = 0                          # window rings used with it: SWA_BF16, or SWA_FP8 (uint8 rings)
     k_format: int = 0                            # KV_F32, or KV_MX16 (k_group 16, uint8 scale planes)
+    ratio: int = 2                               # tokens per entry: 2 (compressed pairs) or 1
 
     @classmethod
     def allocate(cls, batch, capacity, k_group=32, v_group=0, idx_dim=128, dim=576, rope_dim=64,
-                 device="cuda", idx_format=0, swa_format=0, k_format=0):
+                 device="cuda", idx_format=0, swa_format=0, k_format=0, ratio=2):
         dv = dim - rope_dim
         z = lambda *s, dt: torch.zeros(*s, dtype=dt, device=device)
         fp4 = idx_format == IDX_FP4
@@ -183,7 +197,8 @@ class Cache:
                    else z(batch, capacity, idx_dim, dt=torch.int16),
                    z(batch, dt=torch.int32), z(batch, dim, dt=torch.float32),
                    z(4, dt=torch.int32), dim, rope_dim, idx_format,
-                   z(batch, capacity, idx_dim // 16, dt=torch.uint8) if fp4 else None, swa_format, k_format)
+                   z(batch, capacity, idx_dim // 16, dt=torch.uint8) if fp4 else None, swa_format, k_format,
+                   ratio)
 
     def desc(self) -> CacheDesc:
         p = lambda t: None if t is None else t.data_ptr()
@@ -191,7 +206,7 @@ class Cache:
                          self.v_group, self.idx_dim, p(self.k_codes), p(self.k_scales),
                          p(self.v_codes), p(self.v_scales), p(self.idx_keys), p(self.n_tokens),
                          p(self.pending), p(self.status), self.idx_format, p(self.idx_scales),
-                         self.swa_format, self.k_format)
+                         self.swa_format, self.k_format, self.ratio)
 
     def entry_bytes(self) -> int:
         """Bytes per entry in this cache's formats."""
@@ -388,6 +403,82 @@ def layer_group_decode(cache: Cache, layers: Sequence[Layer], new_tokens: Option
     else:
         _check(lib().cskv_layer_group_decode_pooled(*args, pool[0], pool[1], _ptr(ws, U8, "ws"), ws.numel(),
                                                     _stream(stream)))
+
+
+def ced_project(h: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """CED projection: out[r][n] = sum_k h[r][k] w[n][k]; h bf16 bits (int16)
+    [rows, d_model], w bf16 bits (int16) [n_out, d_model] -> fp32 [rows, n_out]."""
+    rows, dm = h.shape
+    n_out = w.shape[0]
+    if out is None:
+        out = torch.empty(rows, n_out, dtype=torch.float32, device=h.device)
+    _check(lib().cskv_ced_project(_ptr(h, B16, "h", (rows, dm)), rows, dm, _ptr(w, B16, "w", (n_out, dm)),
+                                  n_out, _ptr(out, F32, "out", (rows, n_out)), _stream(stream)))
+    return out
+
+
+@dataclass
+class Group:
+    """One group of the layer plan (cskv_group): the layers sharing `cache`
+    and the source of the step's new entries -- new_tokens (+ w_comp for
+    the 2->1 compressor) or the CED projection of ced_h by ced_w."""
+    cache: Cache
+    layers: Sequence[Layer]
+    new_idx_rows: Optional[torch.Tensor] = None
+    new_tokens: Optional[torch.Tensor] = None
+    w_comp: Optional[torch.Tensor] = None
+    ced_h: Optional[torch.Tensor] = None
+    ced_w: Optional[torch.Tensor] = None
+    pool: Optional[tuple] = None
+
+
+def _group_descs(groups: Sequence[Group], k: int, window: int):
+    """ctypes descriptors of the groups (kept alive by the returned list)."""
+    keep, descs = [], (GroupDesc * len(groups))()
+    n_heads = groups[0].layers[0].q.shape[1]
+    n_idx_heads = next((L.q_idx.shape[1] for g in groups for L in g.layers if L.q_idx is not None), 1)
+    for gi, g in enumerate(groups):
+        c, B = g.cache, g.cache.batch
+        d = c.desc()
+        arr = (LayerDesc * len(g.layers))()
+        dv = c.dim - c.rope_dim
+        for i, L in enumerate(g.layers):
+            arr[i] = LayerDesc(MODES[L.mode], _ptr(L.q, F32, "q", (B, n_heads, c.dim)),
+                               _ptr(L.q_idx, B16, "q_idx", (B, n_idx_heads, c.idx_dim)),
+                               _ptr(L.head_w, F32, "head_w", (B, n_idx_heads)),
+                               _ptr(L.swa, U8 if c.swa_format == SWA_FP8 else B16, "swa", (B, window, c.dim)),
+                               _ptr(L.swa_row, F32, "swa_row", (B, c.dim)),
+                               _ptr(L.idx, I32, "idx", (B, k)),
+                               _ptr(L.out, F32, "out", (B, n_heads, dv)),
+                               _ptr(L.lse, F32, "lse", (B, n_heads)))
+        dm = 0 if g.ced_h is None else g.ced_h.shape[1]
+        pb, pbk = g.pool if g.pool else (0, 0)
+        descs[gi] = GroupDesc(C.addressof(d), C.addressof(arr), len(g.layers),
+                              _ptr(g.new_tokens, F32, "new_tokens", (B, c.dim)),
+                              _ptr(g.w_comp, F32, "w_comp", (c.dim, 2 * c.dim)),
+                              _ptr(g.ced_h, B16, "ced_h", (B, dm)), _ptr(g.ced_w, B16, "ced_w", (c.dim, dm)), dm,
+                              _ptr(g.new_idx_rows, B16, "new_idx_rows", (B, c.idx_dim)), pb, pbk)
+        keep += [d, arr]
+    return descs, keep, n_idx_heads, n_heads
+
+
+def model_workspace(groups: Sequence[Group], k: int, window: int) -> torch.Tensor:
+    descs, keep, _, n_heads = _group_descs(groups, k, window)
+    n = lib().cskv_model_workspace_bytes(descs, len(groups), n_heads, k, window)
+    if n == 0:
+        raise CskvError(EINVAL, lib().cskv_last_error().decode())
+    return torch.empty(int(n), dtype=torch.uint8, device=groups[0].cache.k_codes.device)
+
+
+def model_decode(groups: Sequence[Group], k: int, window: int, softmax_scale: float,
+                 ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    """One decode step of every group of the layer plan (cskv_model_decode)."""
+    if ws is None:
+        ws = model_workspace(groups, k, window)
+    descs, keep, n_idx_heads, n_heads = _group_descs(groups, k, window)
+    _check(lib().cskv_model_decode(descs, len(groups), n_idx_heads, n_heads, k, window, float(softmax_scale),
+                                   _ptr(ws, U8, "ws"), ws.numel(), _stream(stream)))
 
 
 # ---------------------------------------------------------------- timers

@@ -71,6 +71,7 @@ int check_cache(const cskv_cache *c)
     REQUIRE(!c->idx_scales || aligned(c->idx_scales, 16), CSKV_EINVAL, "idx_scales must be 16-byte aligned");
     REQUIRE(c->swa_format == CSKV_SWA_BF16 || c->swa_format == CSKV_SWA_FP8, CSKV_EUNSUPPORTED,
             "swa_format %d: CSKV_SWA_BF16 or CSKV_SWA_FP8", c->swa_format);
+    REQUIRE(c->ratio == 1 || c->ratio == 2, CSKV_EUNSUPPORTED, "ratio %d: 1 or 2 tokens per entry", c->ratio);
     REQUIRE(aligned(c->k_codes, 16) && aligned(c->k_scales, 16) && aligned(c->idx_keys, 16) &&
                 aligned(c->n_tokens, 16) && aligned(c->pending, 16) && aligned(c->status, 4) &&
                 (!c->v_codes || aligned(c->v_codes, 16)) && (!c->v_scales || aligned(c->v_scales, 16)),
@@ -286,6 +287,7 @@ int cskv_kv_append_fp4(const cskv_cache *cache, const float *tokens, const int32
     REQUIRE(total_new == 0 || (idx_rows && aligned(idx_rows, 4)), CSKV_EINVAL,
             "idx_rows NULL or not 4-byte aligned");
     REQUIRE(!w_comp || aligned(w_comp, 16), CSKV_EINVAL, "w_comp must be 16-byte aligned");
+    REQUIRE(!w_comp || cache->ratio == 2, CSKV_EUNSUPPORTED, "the 2->1 compressor needs a ratio-2 cache");
     if (w_comp && total_new > 0) {
         const size_t need = cskv::append_workspace_bytes(total_new);
         REQUIRE(ws && aligned(ws, 256), CSKV_EWORKSPACE, "workspace NULL or not 256-byte aligned");
@@ -387,24 +389,24 @@ int cskv_sparse_attn_decode(const cskv_cache *cache, const float *q, int32_t n_h
     return e == hipSuccess ? CSKV_OK : hip_fail(e, "sparse_attn_decode launch");
 }
 
-static int layer_group(const cskv_cache *cache, const cskv_layer *layers, int32_t n_layers,
+// Every check of one layer-group step, before anything is enqueued.
+static int check_group(const cskv_cache *cache, const cskv_layer *layers, int32_t n_layers,
                        const float *new_tokens, const float *w_comp, const uint16_t *new_idx_rows,
                        int32_t n_idx_heads, int32_t n_heads, int32_t k, int32_t window,
-                       float softmax_scale, int32_t pool_blocks, int32_t pool_block, void *ws,
-                       size_t ws_bytes, hipStream_t stream)
+                       int32_t pool_blocks, int32_t pool_block, void *ws, size_t ws_bytes)
 {
     int rc = check_cache(cache);
     if (rc) return rc;
     REQUIRE(layers && n_layers >= 1 && n_layers <= 256, CSKV_EINVAL, "need 1..256 layers");
     REQUIRE(!new_tokens || (aligned(new_tokens, 16) && new_idx_rows), CSKV_EINVAL,
             "new_tokens must be 16-byte aligned and come with new_idx_rows");
+    REQUIRE(!new_tokens || !w_comp || (aligned(w_comp, 16) && cache->ratio == 2), CSKV_EINVAL,
+            "w_comp must be 16-byte aligned and the cache ratio 2");
     if (pool_blocks != 0 && (rc = pool_args(cache, k, pool_blocks, pool_block))) return rc;
-    // the pool (if any) at the start of ws; each step below uses what follows
     REQUIRE(ws && aligned(ws, 256), CSKV_EWORKSPACE, "workspace NULL or not 256-byte aligned");
     const size_t need = group_ws_bytes(*cache, n_heads, k, window, pool_blocks, pool_block);
     REQUIRE(ws_bytes >= need, CSKV_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
     const size_t pool_bytes = group_pool_bytes(*cache, pool_blocks);
-    int32_t *pool = pool_blocks > 0 ? static_cast<int32_t *>(ws) : nullptr;
     void *work = static_cast<char *>(ws) + pool_bytes;
     const size_t work_bytes = ws_bytes - pool_bytes;
     // check every layer before enqueueing anything [P2 四、"CSA2：三种模式"]
@@ -425,6 +427,19 @@ static int layer_group(const cskv_cache *cache, const cskv_layer *layers, int32_
             have_index = true;
         }
     }
+    return CSKV_OK;
+}
+
+// Enqueue one checked layer-group step.  The pool (if any) sits at the start
+// of ws; each step uses what follows.
+static int run_group(const cskv_cache *cache, const cskv_layer *layers, int32_t n_layers,
+                     const float *new_tokens, const float *w_comp, const uint16_t *new_idx_rows,
+                     int32_t n_idx_heads, int32_t n_heads, int32_t k, int32_t window, float softmax_scale,
+                     int32_t pool_blocks, int32_t pool_block, void *ws, hipStream_t stream)
+{
+    const size_t pool_bytes = group_pool_bytes(*cache, pool_blocks);
+    int32_t *pool = pool_blocks > 0 ? static_cast<int32_t *>(ws) : nullptr;
+    void *work = static_cast<char *>(ws) + pool_bytes;
     bool appended = false, pooled = false;
     const int32_t *last_idx = nullptr;
     hipError_t e;
@@ -467,6 +482,35 @@ static int layer_group(const cskv_cache *cache, const cskv_layer *layers, int32_
     return CSKV_OK;
 }
 
+static int layer_group(const cskv_cache *cache, const cskv_layer *layers, int32_t n_layers,
+                       const float *new_tokens, const float *w_comp, const uint16_t *new_idx_rows,
+                       int32_t n_idx_heads, int32_t n_heads, int32_t k, int32_t window,
+                       float softmax_scale, int32_t pool_blocks, int32_t pool_block, void *ws,
+                       size_t ws_bytes, hipStream_t stream)
+{
+    const int rc = check_group(cache, layers, n_layers, new_tokens, w_comp, new_idx_rows, n_idx_heads, n_heads,
+                               k, window, pool_blocks, pool_block, ws, ws_bytes);
+    if (rc) return rc;
+    return run_group(cache, layers, n_layers, new_tokens, w_comp, new_idx_rows, n_idx_heads, n_heads, k, window,
+                     softmax_scale, pool_blocks, pool_block, ws, stream);
+}
+
+static int ced_args(const uint16_t *h, int64_t rows, int32_t d_model, const uint16_t *w, int32_t n_out,
+                    const float *out)
+{
+    REQUIRE(rows >= 0 && rows <= (1 << 22), CSKV_EINVAL, "rows %lld out of [0, 2^22]", (long long)rows);
+    REQUIRE(d_model >= 128 && d_model <= 65536 && d_model % 128 == 0, CSKV_EUNSUPPORTED,
+            "d_model %d: a multiple of 128 in [128, 65536]", d_model);
+    REQUIRE(n_out >= 16 && n_out <= 65536 && n_out % 16 == 0, CSKV_EUNSUPPORTED,
+            "n_out %d: a multiple of 16 in [16, 65536]", n_out);
+    REQUIRE(rows == 0 || (h && w && out), CSKV_EINVAL, "h, w or out is NULL");
+    REQUIRE(aligned(h, 16) && aligned(w, 16) && aligned(out, 16), CSKV_EINVAL,
+            "h, w and out must be 16-byte aligned");
+    return CSKV_OK;
+}
+
+static size_t ced_rows_bytes(const cskv_cache &c) { return ((size_t)c.batch * c.dim * 4 + 255) / 256 * 256; }
+
 int cskv_layer_group_decode(const cskv_cache *cache, const cskv_layer *layers, int32_t n_layers,
                             const float *new_tokens, const float *w_comp,
                             const uint16_t *new_idx_rows, int32_t n_idx_heads, int32_t n_heads,
@@ -485,6 +529,95 @@ int cskv_layer_group_decode_pooled(const cskv_cache *cache, const cskv_layer *la
 {
     return layer_group(cache, layers, n_layers, new_tokens, w_comp, new_idx_rows, n_idx_heads, n_heads, k,
                        window, softmax_scale, pool_blocks, pool_block, ws, ws_bytes, stream);
+}
+
+int cskv_ced_project(const uint16_t *h, int64_t rows, int32_t d_model, const uint16_t *w, int32_t n_out,
+                     float *out, hipStream_t stream)
+{
+    const int rc = ced_args(h, rows, d_model, w, n_out, out);
+    if (rc) return rc;
+    const hipError_t e = cskv::launch_ced_project(h, rows, d_model, w, n_out, out, stream);
+    return e == hipSuccess ? CSKV_OK : hip_fail(e, "ced_project launch");
+}
+
+// Per group: the workspace its layer group needs after the CED rows.
+static size_t model_ws_bytes(const cskv_group *groups, int32_t n_groups, int32_t n_heads, int32_t k,
+                             int32_t window)
+{
+    size_t rows = 0, group = 0;
+    for (int g = 0; g < n_groups; ++g) {
+        const cskv_cache &c = *groups[g].cache;
+        if (groups[g].ced_h) rows = std::max(rows, ced_rows_bytes(c));
+        group = std::max(group, group_ws_bytes(c, n_heads, k, window, groups[g].pool_blocks, groups[g].pool_block));
+    }
+    return rows + group;
+}
+
+static int check_model(const cskv_group *groups, int32_t n_groups, int32_t n_heads, int32_t k, int32_t window)
+{
+    REQUIRE(groups && n_groups >= 1 && n_groups <= 64, CSKV_EINVAL, "need 1..64 groups");
+    for (int g = 0; g < n_groups; ++g) {
+        const cskv_group &G = groups[g];
+        int rc = check_cache(G.cache);
+        if (rc) return fail(rc, "group %d: %s", g, g_error.c_str());
+        REQUIRE(!(G.new_tokens && G.ced_h), CSKV_EINVAL, "group %d: new_tokens and ced_h are exclusive", g);
+        if (G.ced_h) {
+            REQUIRE(G.new_idx_rows, CSKV_EINVAL, "group %d: ced_h needs new_idx_rows", g);
+            float *dummy = reinterpret_cast<float *>(256);      // alignment-only stand-in for the rows
+            if ((rc = ced_args(G.ced_h, G.cache->batch, G.d_model, G.ced_w, G.cache->dim, dummy)))
+                return fail(rc, "group %d: %s", g, g_error.c_str());
+        }
+        if (G.pool_blocks != 0 && (rc = pool_args(G.cache, k, G.pool_blocks, G.pool_block)))
+            return fail(rc, "group %d: %s", g, g_error.c_str());
+    }
+    (void)n_heads;
+    (void)window;
+    return CSKV_OK;
+}
+
+size_t cskv_model_workspace_bytes(const cskv_group *groups, int32_t n_groups, int32_t n_heads, int32_t k,
+                                  int32_t window)
+{
+    if (check_model(groups, n_groups, n_heads, k, window) != CSKV_OK) return 0;
+    return model_ws_bytes(groups, n_groups, n_heads, k, window);
+}
+
+int cskv_model_decode(const cskv_group *groups, int32_t n_groups, int32_t n_idx_heads, int32_t n_heads,
+                      int32_t k, int32_t window, float softmax_scale, void *ws, size_t ws_bytes,
+                      hipStream_t stream)
+{
+    int rc = check_model(groups, n_groups, n_heads, k, window);
+    if (rc) return rc;
+    REQUIRE(ws && aligned(ws, 256), CSKV_EWORKSPACE, "workspace NULL or not 256-byte aligned");
+    const size_t need = model_ws_bytes(groups, n_groups, n_heads, k, window);
+    REQUIRE(ws_bytes >= need, CSKV_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    size_t rows_bytes = 0;
+    for (int g = 0; g < n_groups; ++g)
+        if (groups[g].ced_h) rows_bytes = std::max(rows_bytes, ced_rows_bytes(*groups[g].cache));
+    float *rows = reinterpret_cast<float *>(ws);
+    void *gws = static_cast<char *>(ws) + rows_bytes;
+    const size_t gws_bytes = ws_bytes - rows_bytes;
+    // every group is checked before anything is enqueued
+    for (int g = 0; g < n_groups; ++g) {
+        const cskv_group &G = groups[g];
+        const float *src = G.ced_h ? rows : G.new_tokens;
+        if ((rc = check_group(G.cache, G.layers, G.n_layers, src, G.ced_h ? nullptr : G.w_comp, G.new_idx_rows,
+                              n_idx_heads, n_heads, k, window, G.pool_blocks, G.pool_block, gws, gws_bytes)))
+            return fail(rc, "group %d: %s", g, g_error.c_str());
+    }
+    for (int g = 0; g < n_groups; ++g) {
+        const cskv_group &G = groups[g];
+        if (G.ced_h) {
+            const hipError_t e = cskv::launch_ced_project(G.ced_h, G.cache->batch, G.d_model, G.ced_w,
+                                                          G.cache->dim, rows, stream);
+            if (e != hipSuccess) return hip_fail(e, "model decode: CED projection");
+        }
+        if ((rc = run_group(G.cache, G.layers, G.n_layers, G.ced_h ? rows : G.new_tokens,
+                            G.ced_h ? nullptr : G.w_comp, G.new_idx_rows, n_idx_heads, n_heads, k, window,
+                            softmax_scale, G.pool_blocks, G.pool_block, gws, stream)))
+            return rc;
+    }
+    return CSKV_OK;
 }
 
 int cskv_timer_enable(int32_t kind, int32_t max_launches)

@@ -63,8 +63,9 @@ __device__ __forceinline__ RowInfo row_info(const AppendArgs &a, int64_t r)
         ri.entry = pos >> 1;
         ri.partner = q > 0 ? r - 1 : -1;
     } else {
-        if ((p & 1) != 0 || p / 2 + m > c.capacity) return ri;
-        ri.entry = p / 2 + q;
+        const int rt = c.ratio;                        // tokens per entry
+        if ((p % rt) != 0 || p / rt + m > c.capacity) return ri;
+        ri.entry = p / rt + q;
     }
     return ri;
 }
@@ -299,16 +300,17 @@ __device__ int64_t finalize_seq(const AppendArgs &a, int b, int64_t p, int t, in
         if (t == 0) c.n_tokens[b] = (int32_t)(p + m);
         return p + m;
     } else {
-        if ((p & 1) != 0) {
+        const int rt = c.ratio;
+        if ((p % rt) != 0) {
             if (t == 0) atomicOr(c.status, CSKV_STATUS_ODD_ENTRY_APPEND);
             return p;
         }
-        if (p / 2 + m > c.capacity) {
+        if (p / rt + m > c.capacity) {
             if (t == 0) atomicOr(c.status, CSKV_STATUS_OVERFLOW);
             return p;
         }
-        if (t == 0) c.n_tokens[b] = (int32_t)(p + 2 * m);
-        return p + 2 * m;
+        if (t == 0) c.n_tokens[b] = (int32_t)(p + rt * m);
+        return p + rt * m;
     }
 }
 

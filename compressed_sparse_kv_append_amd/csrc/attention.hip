@@ -690,7 +690,7 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a)
     x.G = kD / KG;
     x.row0 = (size_t)b * c.capacity;
     x.ring = reinterpret_cast<const uint8_t *>(a.swa) + (size_t)b * a.window * kD * (W8 ? 1 : 2);
-    const int64_t E = entries_of(c.n_tokens, b, c.capacity);
+    const int64_t E = entries_of(c.n_tokens, b, c.capacity, c.ratio);
     int64_t nswa = a.swa_len ? (int64_t)a.swa_len[b] : (int64_t)c.n_tokens[b];
     nswa = nswa < 0 ? 0 : (nswa > a.window ? a.window : nswa);
 

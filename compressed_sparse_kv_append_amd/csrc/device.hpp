@@ -163,9 +163,9 @@ __device__ __forceinline__ uint32_t score_key(float s)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ int64_t entries_of(const int32_t *n_tokens, int b, int capacity)
+__device__ __forceinline__ int64_t entries_of(const int32_t *n_tokens, int b, int capacity, int ratio)
 {
-    int64_t e = (int64_t)n_tokens[b] / 2;
+    int64_t e = (int64_t)n_tokens[b] / ratio;
     e = e < 0 ? 0 : e;
     return e > capacity ? capacity : e;
 }

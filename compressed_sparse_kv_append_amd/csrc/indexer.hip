@@ -85,12 +85,13 @@ struct SelectArgs {
     int capacity, k, slices;
     size_t key_stride, cand_stride;
     int group;              // entries per item: a sequence of E entries has ceil(E / group) items
+    int ratio;              // tokens per entry of the cache
 };
 
 // Items of sequence b: its entries, or its blocks of `group` entries.
 __device__ __forceinline__ int64_t items_of(const SelectArgs &a, int b)
 {
-    return (entries_of(a.n_tokens, b, a.capacity) + a.group - 1) / a.group;
+    return (entries_of(a.n_tokens, b, a.capacity, a.ratio) + a.group - 1) / a.group;
 }
 
 template <int THREADS>
@@ -427,7 +428,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_pool_select_kernel(SelectA
 {
     __shared__ SelectSmem<kMergeThreads> sm;
     const int b = blockIdx.x;
-    const int64_t E = entries_of(a.n_tokens, b, a.capacity);
+    const int64_t E = entries_of(a.n_tokens, b, a.capacity, a.ratio);
     int32_t *out = a.out + (size_t)b * a.k;
     if (E <= a.k) {
         for (int i = threadIdx.x; i < a.k; i += kMergeThreads) out[i] = i < E ? i : -1;
@@ -471,13 +472,13 @@ hipError_t launch_indexer_topk(const cskv_cache &c, const uint16_t *q_idx, int h
     launch_indexer_scan(c, q_idx, heads, head_w, keys, s, bkeys, pw.bkey_stride, pool ? pool->block : 1);
 
     const SelectArgs se{keys, cand, c.n_tokens, out_idx, c.capacity, k, topk_slices(c), score_key_stride(c),
-                        cand_stride(c, k), 1};
+                        cand_stride(c, k), 1, c.ratio};
     launch_select(se, c.batch, s, timer_take(CSKV_KERNEL_TOPK_SELECT));
     if (pool) {
         // the pool: the best pool->blocks blocks by their largest key
         uint2 *bcand = reinterpret_cast<uint2 *>(static_cast<char *>(ws) + pw.bcand_off);
         const SelectArgs sb{bkeys, bcand, c.n_tokens, pool->out, c.capacity, pool->blocks, pw.bslices,
-                            pw.bkey_stride, pw.bcand_stride, pool->block};
+                            pw.bkey_stride, pw.bcand_stride, pool->block, c.ratio};
         launch_select(sb, c.batch, s, TimedLaunch{});
     }
     return hipGetLastError();
@@ -490,7 +491,7 @@ hipError_t launch_indexer_topk_in_pool(const cskv_cache &c, const uint16_t *q_id
     uint2 *pairs = static_cast<uint2 *>(ws);
     launch_pool_scan(c, q_idx, heads, head_w, pool, pool_blocks, block, pairs, s);
     const SelectArgs se{nullptr, pairs, c.n_tokens, out_idx, c.capacity, k, 1, 0,
-                        (size_t)pool_blocks * block, 1};
+                        (size_t)pool_blocks * block, 1, c.ratio};
     launch_kernel(topk_pool_select_kernel, dim3((unsigned)c.batch), dim3(kMergeThreads), s, nullptr, nullptr, se);
     return hipGetLastError();
 }

@@ -34,6 +34,8 @@ hipError_t launch_kv_append(const cskv_cache &c, const float *tokens, const int3
                             const float *swa_rows = nullptr, int swa_window = 0);
 // fp8: the ring holds E4M3 bytes (dim a multiple of 16), else bf16 (dim a
 // multiple of 4).
+hipError_t launch_ced_project(const uint16_t *h, int64_t rows, int d_model, const uint16_t *w, int n_out,
+                              float *out, hipStream_t s);
 hipError_t launch_swa_append(uint16_t *ring, int batch, int window, int dim, const float *rows,
                              const int32_t *cu_new, int total_new, const int32_t *end_pos,
                              hipStream_t s, bool fp8 = false);

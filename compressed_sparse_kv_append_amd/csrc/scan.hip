@@ -52,6 +52,7 @@ struct ScanArgs {
     // FP4 indexer keys: keys holds E2M1 codes (DI/2 bytes per row), scales
     // one E8M0 byte per 16 dims
     const uint8_t *idx_scales;
+    int ratio;                 // tokens per entry of the cache
 };
 
 typedef __attribute__((address_space(1))) void global_void_t;
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
     int32_t *pool_rows = reinterpret_cast<int32_t *>(lds + kRingBytes);
 
     const int b = blockIdx.y;
-    const int64_t E = entries_of(a.n_tokens, b, a.capacity);
+    const int64_t E = entries_of(a.n_tokens, b, a.capacity, a.ratio);
     // the positions scanned: entries, or pool positions
     const int64_t N = POOL ? (E > 0 ? (int64_t)a.pool_blocks * a.block : 0) : E;
     const int64_t e_begin = (int64_t)blockIdx.x * a.chunk;
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_fp4_kernel(ScanArgs
     int32_t *pool_rows = reinterpret_cast<int32_t *>(lds + kRingBytes + 64 * MT);
 
     const int b = blockIdx.y;
-    const int64_t E = entries_of(a.n_tokens, b, a.capacity);
+    const int64_t E = entries_of(a.n_tokens, b, a.capacity, a.ratio);
     const int64_t N = POOL ? (E > 0 ? (int64_t)a.pool_blocks * a.block : 0) : E;
     const int64_t e_begin = (int64_t)blockIdx.x * a.chunk;
     if (e_begin >= N) return;
@@ -446,7 +447,7 @@ void launch_indexer_scan(const cskv_cache &c, const uint16_t *q_idx, int heads, 
 {
     const int chunk = scan_chunk(c.batch, (size_t)c.capacity, (size_t)1 << 30);
     ScanArgs sa{c.idx_keys, c.n_tokens, q_idx, head_w, keys, c.capacity, heads, chunk, score_key_stride(c),
-                block_keys, block_stride, block, nullptr, 0, nullptr, c.idx_scales};
+                block_keys, block_stride, block, nullptr, 0, nullptr, c.idx_scales, c.ratio};
     dim3 grid((unsigned)(((size_t)c.capacity + chunk - 1) / chunk), (unsigned)c.batch);
     scan_dispatch<false>(c, heads, sa, grid, s);
 }
@@ -457,7 +458,7 @@ void launch_pool_scan(const cskv_cache &c, const uint16_t *q_idx, int heads, con
     const size_t n = (size_t)pool_blocks * block;
     const int chunk = scan_chunk(c.batch, n, kPoolChunkMax);
     ScanArgs sa{c.idx_keys, c.n_tokens, q_idx, head_w, nullptr, c.capacity, heads, chunk, 0,
-                nullptr, 0, block, pool, pool_blocks, pairs, c.idx_scales};
+                nullptr, 0, block, pool, pool_blocks, pairs, c.idx_scales, c.ratio};
     dim3 grid((unsigned)((n + chunk - 1) / chunk), (unsigned)c.batch);
     scan_dispatch<true>(c, heads, sa, grid, s);
 }

@@ -125,6 +125,9 @@ typedef struct cskv_cache {
     uint8_t *idx_scales;     /* CSKV_IDX_FP4 only, else NULL */
     int32_t swa_format;      /* CSKV_SWA_BF16 or CSKV_SWA_FP8 */
     int32_t k_format;        /* CSKV_KV_F32 or CSKV_KV_MX16 */
+    int32_t ratio;           /* tokens per entry: 2 (token pairs compressed into one
+                                entry) or 1 (one entry per token, as the decoder cache
+                                fed by cskv_ced_project); entries = n_tokens / ratio */
 } cskv_cache;
 
 /*
@@ -321,6 +324,68 @@ size_t cskv_workspace_bytes(const cskv_cache *cache, int32_t op, int32_t n_heads
                             int32_t window);
 size_t cskv_workspace_bytes_pool(const cskv_cache *cache, int32_t op, int32_t n_heads, int32_t k,
                                  int32_t window, int32_t pool_blocks, int32_t pool_block);
+
+/*
+ * The CED projection [P2 四、"CED：上半段模型的 KV 由下半段代算" (the second
+ * half's global KV is the first half's last output times a per-layer
+ * projection)]: out[r][n] = sum_k h[r][k] * w[n][k] for r < rows, n < n_out.
+ *
+ * h     bf16 [rows][d_model] (device), the hidden states
+ * w     bf16 [n_out][d_model] (device), one row per output channel
+ * out   f32 [rows][n_out] (device), written; it may not overlap h or w
+ * d_model a multiple of 128 in [128, 65536]; n_out a multiple of 16; rows in
+ * [0, 2^22]; all pointers 16-byte aligned.  bf16 MFMA with fp32
+ * accumulation: each output is the sum of its products in a fixed order
+ * (exact whenever the inputs make every partial sum representable, e.g.
+ * small integers times a common power of two).  Enqueued on `stream`.
+ */
+int cskv_ced_project(const uint16_t *h, int64_t rows, int32_t d_model, const uint16_t *w, int32_t n_out,
+                     float *out, hipStream_t stream);
+
+/*
+ * One group of the layer plan: the layers that share one cache and the
+ * source of the step's new entry per sequence [P2 四、"CSA2：三种模式，40 层只存
+ * 4 份" (encoder groups of Full + 5 Reuse with 2->1 caches; the decoder's
+ * groups, Full + 3 Reuse and then Reindex + 3 Reuse, read one cache);
+ * "CED：上半段模型的 KV 由下半段代算"].
+ *
+ * new_tokens + w_comp: one new token per sequence through the 2->1
+ *   compressor (ratio-2 cache), as cskv_layer_group_decode; w_comp NULL:
+ *   new_tokens are entries.
+ * ced_h + ced_w + d_model: the new entry of each sequence is the CED
+ *   projection of ced_h (bf16 [batch][d_model]) by ced_w (bf16
+ *   [dim][d_model]), appended as an entry (one per token on a ratio-1 cache).
+ * Neither: no append.  new_idx_rows bf16 [batch][idx_dim] goes with either.
+ * pool_blocks, pool_block: the hierarchical indexer for this group's REINDEX
+ *   layers (0, 0: off).  layers: host array as for cskv_layer_group_decode.
+ */
+typedef struct cskv_group {
+    const cskv_cache *cache;
+    const cskv_layer *layers;
+    int32_t n_layers;
+    const float *new_tokens;
+    const float *w_comp;
+    const uint16_t *ced_h;
+    const uint16_t *ced_w;
+    int32_t d_model;
+    const uint16_t *new_idx_rows;
+    int32_t pool_blocks, pool_block;
+} cskv_group;
+
+/*
+ * One decode step of every group in order, each as cskv_layer_group_decode
+ * (cskv_layer_group_decode_pooled when its pool is set), after the CED
+ * projection for a group that has one.  Every group is checked before
+ * anything is enqueued; an error leaves every cache untouched.  groups is a
+ * host array of 1..64 groups sharing n_idx_heads, n_heads, k and window.
+ * ws: cskv_model_workspace_bytes bytes, 256-byte aligned, reused by the
+ * groups in turn.  Returns CSKV_OK or an error code.
+ */
+int cskv_model_decode(const cskv_group *groups, int32_t n_groups, int32_t n_idx_heads, int32_t n_heads,
+                      int32_t k, int32_t window, float softmax_scale, void *ws, size_t ws_bytes,
+                      hipStream_t stream);
+size_t cskv_model_workspace_bytes(const cskv_group *groups, int32_t n_groups, int32_t n_heads, int32_t k,
+                                  int32_t window);
 
 /* Bytes one entry occupies across all planes (codes, scales, indexer key)
  * [P2 四、"890 字节是怎么算出来的"]. */

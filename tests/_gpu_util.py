@@ -38,7 +38,7 @@ def assert_cache_equal(g: ck.Cache, h: orc.Cache, seqs=None, check_pending=True)
     nt = host(g.n_tokens)
     assert np.array_equal(nt[seqs], h.n_tokens[seqs]), (nt[seqs], h.n_tokens[seqs])
     for b in seqs:
-        e = int(min(h.n_tokens[b] // 2, h.capacity))
+        e = int(min(h.n_tokens[b] // h.ratio, h.capacity))
         for name in ("k_codes", "k_scales", "v_codes", "v_scales", "idx_keys", "idx_scales"):
             gt = getattr(g, name)
             if gt is None:
@@ -48,7 +48,7 @@ def assert_cache_equal(g: ck.Cache, h: orc.Cache, seqs=None, check_pending=True)
             if not np.array_equal(ga.view(np.uint8), ha.view(np.uint8)):
                 bad = np.argwhere(ga.view(np.uint8).reshape(e, -1) != ha.view(np.uint8).reshape(e, -1))
                 raise AssertionError(f"{name} differs for sequence {b}: first at {bad[:5].tolist()}")
-        if check_pending and h.n_tokens[b] % 2 == 1:
+        if check_pending and h.ratio == 2 and h.n_tokens[b] % 2 == 1:
             assert np.array_equal(host(g.pending[b]), h.pending[b]), f"pending differs, seq {b}"
     assert int(host(g.status)[0]) == int(h.status[0])
 
@@ -83,7 +83,7 @@ def lse_tol(h: orc.Cache, q: np.ndarray, idx: np.ndarray, ring: np.ndarray, swa_
     B, H, D = q.shape
     tol = np.full((B, H), 1e-5)
     for b in range(B):
-        E = int(min(h.n_tokens[b] // 2, h.capacity))
+        E = int(min(h.n_tokens[b] // h.ratio, h.capacity))
         keys = []
         for e in idx[b]:
             if 0 <= e < E and h.k_format == 1:

@@ -48,7 +48,7 @@ def test_entry_bytes(L):
 def _desc(**over):
     d = dict(batch=2, capacity=64, dim=576, rope_dim=64, k_group=32, v_group=0, idx_dim=64,
              k_codes=0x10000, k_scales=0x20000, v_codes=None, v_scales=None, idx_keys=0x30000,
-             n_tokens=0x40000, pending=0x50000, status=0x60000, idx_format=0, idx_scales=None, swa_format=0, k_format=0)
+             n_tokens=0x40000, pending=0x50000, status=0x60000, idx_format=0, idx_scales=None, swa_format=0, k_format=0, ratio=2)
     d.update(over)
     return ck.CacheDesc(*[d[f] for f, _ in ck.CacheDesc._fields_])
 
@@ -95,6 +95,8 @@ def test_cache_entry_bytes_in_each_format(L):
     (dict(k_format=1), ck.EUNSUPPORTED, "k_group"),
     (dict(k_group=16), ck.EUNSUPPORTED, "k_group"),
     (dict(k_format=1, k_group=16, v_group=32), ck.EUNSUPPORTED, "v_group"),
+    (dict(ratio=0), ck.EUNSUPPORTED, "ratio"),
+    (dict(ratio=3), ck.EUNSUPPORTED, "ratio"),
 ])
 def test_cache_descriptor_rejected_before_launch(L, over, code, text):
     d = _desc(**over)
@@ -102,6 +104,41 @@ def test_cache_descriptor_rejected_before_launch(L, over, code, text):
                               C.c_void_p(0x80000), None, 0, None)
     assert rc == code and text in _err(L), (rc, _err(L))
     assert L.cskv_workspace_bytes(C.byref(d), ck.OP_INDEXER_TOPK, 0, 512, 0) == 0
+
+
+def test_ced_and_model_arguments_rejected_before_launch(L):
+    vp = C.c_void_p
+    h, w, out = vp(0x100000), vp(0x200000), vp(0x300000)
+    # d_model a multiple of 128, n_out a multiple of 16, aligned pointers
+    assert L.cskv_ced_project(h, 32, 4000, w, 576, out, None) == ck.EUNSUPPORTED and "d_model" in _err(L)
+    assert L.cskv_ced_project(h, 32, 4096, w, 570, out, None) == ck.EUNSUPPORTED and "n_out" in _err(L)
+    assert L.cskv_ced_project(vp(0x100008), 32, 4096, w, 576, out, None) == ck.EINVAL
+    assert L.cskv_ced_project(None, 32, 4096, w, 576, out, None) == ck.EINVAL
+    assert L.cskv_ced_project(h, -1, 4096, w, 576, out, None) == ck.EINVAL
+    # the 2->1 compressor on a one-entry-per-token cache
+    d1 = _desc(ratio=1)
+    need = L.cskv_append_workspace_bytes(2, vp(0x110000))
+    assert L.cskv_kv_append_fp4(C.byref(d1), vp(0x70000), None, 2, vp(0x110000), vp(0x80000), vp(0xB0000),
+                                need, None) == ck.EUNSUPPORTED and "ratio" in _err(L)
+    # model decode: group checks come before any launch
+    d = _desc()
+    lay = ck.LayerDesc(ck.MODE_FULL, 0xC0000, 0xA0000, None, 0xE0000, None, 0x90000, 0xF0000, None)
+    g = ck.GroupDesc(C.addressof(d), C.addressof(lay), 1, 0x70000, None, 0x100000, 0x200000, 4096, 0x80000, 0, 0)
+    arr = (ck.GroupDesc * 1)(g)
+    assert L.cskv_model_decode(arr, 1, 4, 16, 512, 128, C.c_float(0.04), vp(0xB0000), 1 << 30,
+                               None) == ck.EINVAL and "exclusive" in _err(L)
+    assert L.cskv_model_decode(arr, 0, 4, 16, 512, 128, C.c_float(0.04), vp(0xB0000), 1 << 30, None) == ck.EINVAL
+    arr[0].new_tokens = None
+    arr[0].d_model = 1000
+    assert L.cskv_model_decode(arr, 1, 4, 16, 512, 128, C.c_float(0.04), vp(0xB0000), 1 << 30,
+                               None) == ck.EUNSUPPORTED and "d_model" in _err(L)
+    assert L.cskv_model_workspace_bytes(arr, 1, 16, 512, 128) == 0
+    arr[0].d_model = 4096
+    ws = L.cskv_model_workspace_bytes(arr, 1, 16, 512, 128)
+    group = L.cskv_workspace_bytes(C.byref(d), ck.OP_LAYER_GROUP, 16, 512, 128)
+    assert ws == group + 2 * 576 * 4            # the projected rows (4608 B, 256-aligned) + the group's
+    assert L.cskv_model_decode(arr, 1, 4, 16, 512, 128, C.c_float(0.04), vp(0xB0000), ws - 1,
+                               None) == ck.EWORKSPACE
 
 
 def test_call_arguments_rejected_before_launch(L):
