@@ -240,6 +240,8 @@ def main():
 
     ck.lib()
     w = synth.WORKLOADS[a.workload]
+    if w.chunk_tokens:
+        return main_mixed(a, ck, synth, torch)
     assert w.entries is not None, "bench steps fixed-length workloads"
     mx16 = a.kv_format == "mx16"
     if mx16:
@@ -425,6 +427,205 @@ def main():
         log("timing the oracle on a CPU sample ...")
         result["cpu_baseline"] = cpu_baseline(synth, w, a.cpu_baseline_seqs, a.cpu_baseline_seconds, pool,
                                               int(idx_fp4), int(swa_fp8), int(mx16))
+    print(json.dumps(result), flush=True)
+
+
+ALU_PEAK_TFLOPS = 157.3      # MI355X fp32 vector: 256 CUs x 256 FMA lanes x 2 x 2.4 GHz
+
+
+def build_ragged(ck, synth, w, cap, dev, torch):
+    """Entries-mode build of the ragged cache, one sequence per call; the
+    sequences' rows are drawn on host threads while earlier ones upload."""
+    import concurrent.futures as cf
+    E = synth.entry_counts(w)
+    gc = ck.Cache.allocate(w.batch, cap, w.k_group, w.v_group, w.idx_dim)
+
+    def draw(b):
+        return synth.cache_entries(w, b), synth.cache_idx_keys(w, b)
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        for b, (ents, keys) in enumerate(ex.map(draw, range(w.batch))):
+            cu = np.zeros(w.batch + 1, np.int32)
+            cu[b + 1:] = int(E[b])
+            ck.kv_append_fp4(gc, dev(ents), dev(cu), None, dev(keys))
+    torch.cuda.synchronize()
+    return gc
+
+
+def mixed_cpu_baseline(synth, w, seconds: float):
+    """The oracle on a bounded sample of the mixed step: the whole chunk append
+    of sequence 0 through the compressor, then the decode step of the first
+    nseq sequences (nseq grown until the sample takes about `seconds`); the
+    cache build is untimed."""
+    import oracle as orc
+    E = synth.entry_counts(w)
+    W = synth.w_comp(w)
+    n = w.chunk_tokens
+    toks, irows = synth.prefill_tokens(w, 0, n), synth.prefill_idx_rows(w, 0, n)
+    nseq = 16
+    cap = int(E[:nseq].max()) + n // 2 + 8
+    hc = orc.Cache.empty(nseq, cap, w.dim, w.rope_dim, w.k_group, w.v_group, w.idx_dim)
+    for b in range(nseq):
+        cu = np.zeros(nseq + 1, np.int32)
+        cu[b + 1:] = int(E[b])
+        orc.kv_append(hc, synth.cache_entries(w, b), cu, None, synth.cache_idx_keys(w, b))
+    cu = np.zeros(nseq + 1, np.int32)
+    cu[1:] = n
+    t0 = time.perf_counter()
+    orc.kv_append(hc, toks, cu, W, irows)
+    t_app = time.perf_counter() - t0
+    sub = synth.scaled(w, batch=nseq)
+    st = synth.step_inputs(w, 0, seqs=range(nseq))
+    rings = [r.copy() for r in st.swa_ring]
+    t0 = time.perf_counter()
+    orc.layer_group_decode(hc, sub.layers, st.token, st.idx_row, W, st.q, st.q_idx, rings, st.swa_row,
+                           w.topk, 1 / math.sqrt(w.dim))
+    t_dec = time.perf_counter() - t0
+    # decode time scales with the batch's entries (the scan dominates)
+    t_dec_full = t_dec * float(E.sum() + n // 2) / float(E[:nseq].sum() + n // 2)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": 1.0 / (t_app + t_dec_full), "unit": "steps/s", "cores": min(threads, nseq),
+            "kind": "oracle",
+            "sample": f"chunk append of {n} tokens through the compressor ({t_app:.1f} s, one thread: "
+                      f"one sequence), then the decode step of {nseq} of {w.batch} sequences "
+                      f"({t_dec:.1f} s), scaled to the batch's {int(E.sum())} entries by entry count; "
+                      "cache build untimed"}
+
+
+def main_mixed(a, ck, synth, torch):
+    """Mixed append + decode on the ragged batch: one step = the chunk of
+    w.chunk_tokens tokens appended to sequence 0 through the compressor
+    together with one token on every other sequence (one kv_append call),
+    then one Full-layer decode step of the whole batch.  The sequences'
+    token counts are restored between steps, outside the timed intervals, so
+    every step sees the same cache; each step is timed with HIP events on
+    the launch stream (append, decode, both)."""
+    w = synth.WORKLOADS[a.workload]
+    E = synth.entry_counts(w)
+    B, n = w.batch, w.chunk_tokens
+    cap = int(E.max()) + n // 2 + 16
+
+    def dev(x):
+        x = np.ascontiguousarray(x)
+        return torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).cuda()
+
+    t0 = time.time()
+    gc = build_ragged(ck, synth, w, cap, dev, torch)
+    log(f"built the ragged cache ({int(E.sum())} entries over {B} sequences) in {time.time() - t0:.1f}s")
+    lens = np.array([n] + [1] * (B - 1), np.int64)
+    cu_h = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    toks = torch.empty(int(cu_h[-1]), w.dim, device="cuda")
+    irows = torch.empty(int(cu_h[-1]), w.idx_dim, dtype=torch.int16, device="cuda")
+    toks[:n] = dev(synth.prefill_tokens(w, 0, n))
+    irows[:n] = dev(synth.prefill_idx_rows(w, 0, n))
+    for b in range(1, B):
+        toks[cu_h[b]:cu_h[b + 1]] = dev(synth.prefill_tokens(w, b, 1))
+        irows[cu_h[b]:cu_h[b + 1]] = dev(synth.prefill_idx_rows(w, b, 1))
+    cu = dev(cu_h)
+    W = dev(synth.w_comp(w))
+    app_ws = ck.append_workspace(int(cu_h[-1]), W)
+    st = synth.step_inputs(w, 0)
+    layers = [ck.Layer(mode="full", q=dev(st.q[0]), q_idx=dev(st.q_idx[0]), swa=dev(st.swa_ring[0]),
+                       swa_row=dev(st.swa_row[0]), idx=torch.empty(B, w.topk, dtype=torch.int32, device="cuda"),
+                       out=torch.empty(B, w.q_heads, w.vdim, device="cuda"),
+                       lse=torch.empty(B, w.q_heads, device="cuda"))]
+    tok, irow = dev(st.token), dev(st.idx_row)
+    scale = 1 / math.sqrt(w.dim)
+    n0 = gc.n_tokens.clone()
+    gws = ck.workspace(gc, w.topk, ck.OP_LAYER_GROUP, w.q_heads, w.window)
+
+    def append():
+        ck.kv_append_fp4(gc, toks, cu, W, irows, ws=app_ws)
+
+    def decode():
+        ck.layer_group_decode(gc, layers, tok, W, irow, w.topk, w.window, scale, ws=gws)
+
+    def reset():
+        gc.n_tokens.copy_(n0)
+
+    for _ in range(a.warmup):
+        append()
+        decode()
+        reset()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    for e in ev:
+        e[0].record()
+        append()
+        e[1].record()
+        decode()
+        e[2].record()
+        reset()
+    torch.cuda.synchronize()
+    t_app = np.array([e[0].elapsed_time(e[1]) * 1000.0 for e in ev])
+    t_dec = np.array([e[1].elapsed_time(e[2]) * 1000.0 for e in ev])
+    t_step = np.array([e[0].elapsed_time(e[2]) * 1000.0 for e in ev])
+
+    # per-kernel pass: the compressor alone, then the other kinds
+    kinds = {"compress": ck.KERNEL_COMPRESS, "append": ck.KERNEL_APPEND,
+             "indexer_scan": ck.KERNEL_INDEXER_SCAN, "topk_select": ck.KERNEL_TOPK_SELECT,
+             "attention": ck.KERNEL_ATTENTION}
+    reps = min(a.steps, 50)
+    for kd in kinds.values():
+        ck.timer_enable(kd, 2 * reps)
+    for _ in range(reps):
+        append()
+        decode()
+        reset()
+    torch.cuda.synchronize()
+    kern = {}
+    for name, kd in kinds.items():
+        tot, cnt = ck.timer_read(kd)
+        kern[name] = 1000 * tot / max(cnt, 1) * (cnt / reps)     # per step
+    ck.timer_disable_all()
+    status = int(gc.status[0].item())
+    assert status == 0, f"cache status flag raised: {status}"
+
+    # algorithmic work of one step.  The token counts start even, so the
+    # append completes the chunk's n/2 entries and leaves the other sequences'
+    # tokens pending; the decode step's token completes their pairs and waits
+    # in sequence 0.
+    D = w.dim
+    entry_b = D // 2 + 4 * (D // w.k_group) + w.vdim // 2 + 4 * (w.vdim // w.v_group)
+    key_b = 2 * w.idx_dim
+    comp_entries = n // 2 + (B - 1)
+    comp_flops = 2.0 * comp_entries * D * 2 * D
+    E_dec = float(E.sum() + n // 2 + B - 1)     # entries the decode scans
+    scan_bytes = E_dec * key_b + B * w.idx_heads * w.idx_dim * 2
+    dec_bytes = (scan_bytes + B * w.topk * entry_b + B * w.window * D * 2 + B * w.q_heads * D * 4
+                 + B * w.q_heads * (w.vdim + 1) * 4 + B * (D * 4 * 2 + key_b) + (B - 1) * (entry_b + key_b))
+    app_bytes = int(cu_h[-1]) * (D * 4 + key_b) + D * 2 * D * 4 + (n // 2) * (entry_b + key_b)
+    ms = float(t_step.mean()) / 1000.0
+    scan_us, comp_us = kern["indexer_scan"], kern["compress"]
+    comp_tflops = comp_flops / (comp_us * 1e-6) / 1e12
+    scan_gbps = scan_bytes / (scan_us * 1e-6) / 1e9
+    result = {
+        "metric": "CSA2 FP4 mixed append + decode: steps/s on the ragged batch",
+        "value": round(1000.0 / ms, 2), "unit": "steps/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32 compressor, bf16 scan and attention",
+        "data": "synthetic (seeded; N(0,1) tokens and entries with 1% x20 outliers, integer indexer inputs)",
+        "config": {"workload": w.name, "batch": B, "token_range": list(w.ragged_tokens),
+                   "entries_total": int(E.sum()), "chunk_tokens": n, "k_group": w.k_group,
+                   "v_group": w.v_group, "idx_heads": w.idx_heads, "idx_dim": w.idx_dim,
+                   "q_heads": w.q_heads, "topk": w.topk, "window": w.window, "launch": "eager",
+                   "layers": ["full"]},
+        "roofline": {"bound": "alu", "achieved": round(comp_tflops, 2), "peak": ALU_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(comp_tflops / ALU_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "compress", "flops_per_step": round(comp_flops), "avg_us": round(comp_us, 2),
+                     "timing": "hip events on the compressor's launch, separate eager pass"},
+        "roofline_scan": {"bound": "hbm", "achieved": round(scan_gbps, 1), "peak": HBM_PEAK_GBPS,
+                          "unit": "GB/s", "frac": round(scan_gbps / HBM_PEAK_GBPS, 4),
+                          "bytes_per_launch": round(scan_bytes), "avg_us": round(scan_us, 2)},
+        "step_us": {k: {"p10": round(float(np.percentile(v, 10)), 2), "p50": round(float(np.percentile(v, 50)), 2),
+                        "p90": round(float(np.percentile(v, 90)), 2)}
+                    for k, v in (("append", t_app), ("decode", t_dec), ("step", t_step))},
+        "append_bytes": round(app_bytes), "decode_bytes": round(dec_bytes),
+        "decode_hbm_frac": round(dec_bytes / (float(t_dec.mean()) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "kernels_us": {k: round(v, 2) for k, v in kern.items()},
+    }
+    if not a.no_cpu_baseline:
+        log("timing the oracle on a CPU sample ...")
+        result["cpu_baseline"] = mixed_cpu_baseline(synth, w, a.cpu_baseline_seconds)
     print(json.dumps(result), flush=True)
 
 

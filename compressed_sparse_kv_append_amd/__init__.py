@@ -34,6 +34,7 @@ SWA_BF16, SWA_FP8 = 0, 1
 KV_F32, KV_MX16 = 0, 1
 MODES = {"full": MODE_FULL, "reindex": MODE_REINDEX, "reuse": MODE_REUSE}
 KERNEL_APPEND, KERNEL_SWA_APPEND, KERNEL_INDEXER_SCAN, KERNEL_TOPK_SELECT, KERNEL_ATTENTION = 1, 2, 3, 4, 5
+KERNEL_COMPRESS = 6
 OP_INDEXER_TOPK, OP_SPARSE_ATTN, OP_LAYER_GROUP, OP_INDEXER_POOL, OP_INDEXER_IN_POOL = 1, 2, 3, 4, 5
 
 EXPORTS = ("cskv_kv_append_fp4", "cskv_append_workspace_bytes", "cskv_swa_append", "cskv_swa_append_fp8",

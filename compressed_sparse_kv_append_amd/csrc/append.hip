@@ -12,6 +12,9 @@ namespace {
 
 constexpr int kDim = 576;          // entry dims handled by these kernels (512 latent + 64 RoPE)
 constexpr int kAppendThreads = kDim;  // quantiser: one channel per thread, 9 waves
+// Appends with a compressor and at least this many rows (grouped by cu_new)
+// take the planned, tiled path; smaller ones the wave-per-output kernel.
+constexpr int kTiledMinRows = 512;
 
 struct AppendArgs {
     cskv_cache c;
@@ -314,6 +317,41 @@ __device__ int64_t finalize_seq(const AppendArgs &a, int b, int64_t p, int t, in
     }
 }
 
+// Quantise entry value e (channel t of the entry) into cache slot `slot`
+// (sequence-major row of every plane) and copy or quantise input row r's
+// indexer key there.  Called by all threads of a kAppendThreads block
+// (barriers inside).
+__device__ __forceinline__ void quantize_entry(const AppendArgs &a, float e, int t, size_t slot, int64_t r,
+                                               float *wave_max)
+{
+    const cskv_cache &c = a.c;
+    if (c.k_format == CSKV_KV_MX16) {
+        quantize_channel_mx16(e, t, kDim, c.k_codes + slot * (kDim / 2),
+                              reinterpret_cast<uint8_t *>(c.k_scales) + slot * (kDim / 16));
+        if (c.v_group > 0) {
+            const int dv = c.dim - c.rope_dim;
+            quantize_channel_mx16(e, t, dv, c.v_codes + slot * (dv / 2),
+                                  reinterpret_cast<uint8_t *>(c.v_scales) + slot * (dv / 16));
+        }
+    } else {
+        quantize_channel(e, t, kDim, c.k_group, c.k_codes + slot * (kDim / 2),
+                         c.k_scales + slot * (kDim / c.k_group), wave_max);
+        if (c.v_group > 0) {
+            const int dv = c.dim - c.rope_dim;
+            quantize_channel(e, t, dv, c.v_group, c.v_codes + slot * (dv / 2),
+                             c.v_scales + slot * (dv / c.v_group), wave_max);
+        }
+    }
+    if (c.idx_format == CSKV_IDX_FP4) {
+        if (t < c.idx_dim)                      // whole waves: idx_dim is 64 or 128
+            quantize_idx_fp4(bf16_bits_to_f32(a.idx_rows[(size_t)r * c.idx_dim + t]), t,
+                             reinterpret_cast<uint8_t *>(c.idx_keys) + slot * (c.idx_dim / 2),
+                             c.idx_scales + slot * (c.idx_dim / 16));
+    } else if (t < c.idx_dim) {
+        c.idx_keys[slot * c.idx_dim + t] = a.idx_rows[(size_t)r * c.idx_dim + t];
+    }
+}
+
 // One block per input row.  A block whose row completes an entry quantises
 // that entry (compressor mode: from the compressor's output; entries mode:
 // the row itself) and writes its codes, scales and indexer key.  kFinalize
@@ -329,32 +367,7 @@ __global__ __launch_bounds__(kAppendThreads) void quantize_kernel(AppendArgs a)
     const RowInfo ri = row_info<kCompress>(a, r);
     if (ri.entry >= 0) {
         const float e = kCompress ? a.ent[(size_t)r * kDim + t] : a.tokens[(size_t)r * kDim + t];
-        const size_t slot = (size_t)ri.b * c.capacity + (size_t)ri.entry;
-        if (c.k_format == CSKV_KV_MX16) {
-            quantize_channel_mx16(e, t, kDim, c.k_codes + slot * (kDim / 2),
-                                  reinterpret_cast<uint8_t *>(c.k_scales) + slot * (kDim / 16));
-            if (c.v_group > 0) {
-                const int dv = c.dim - c.rope_dim;
-                quantize_channel_mx16(e, t, dv, c.v_codes + slot * (dv / 2),
-                                      reinterpret_cast<uint8_t *>(c.v_scales) + slot * (dv / 16));
-            }
-        } else {
-            quantize_channel(e, t, kDim, c.k_group, c.k_codes + slot * (kDim / 2),
-                             c.k_scales + slot * (kDim / c.k_group), wave_max);
-            if (c.v_group > 0) {
-                const int dv = c.dim - c.rope_dim;
-                quantize_channel(e, t, dv, c.v_group, c.v_codes + slot * (dv / 2),
-                                 c.v_scales + slot * (dv / c.v_group), wave_max);
-            }
-        }
-        if (c.idx_format == CSKV_IDX_FP4) {
-            if (t < c.idx_dim)                      // whole waves: idx_dim is 64 or 128
-                quantize_idx_fp4(bf16_bits_to_f32(a.idx_rows[(size_t)r * c.idx_dim + t]), t,
-                                 reinterpret_cast<uint8_t *>(c.idx_keys) + slot * (c.idx_dim / 2),
-                                 c.idx_scales + slot * (c.idx_dim / 16));
-        } else if (t < c.idx_dim) {
-            c.idx_keys[slot * c.idx_dim + t] = a.idx_rows[(size_t)r * c.idx_dim + t];
-        }
+        quantize_entry(a, e, t, (size_t)ri.b * c.capacity + (size_t)ri.entry, r, wave_max);
     }
     if (kFinalize) {
         const int b = (int)r;
@@ -423,11 +436,272 @@ __global__ __launch_bounds__(kWave) void swa_append_kernel(SwaArgs a)
     }
 }
 
+// ---------------------------------------------------------- large appends
+//
+// An append of many rows (a prefill chunk) runs the same compressor order
+// as a tiled SIMT product.  A plan kernel first lists the rows that complete
+// an entry; the compressor then gives each block a tile of 64 listed entries
+// x 32 output channels and cuts each output's 64 term blocks into eight runs
+// of 8, one per wave.  A run of 8 consecutive blocks is exactly one level-3
+// node of the pairwise tree, so a wave folds its blocks and adds their sums
+// in tree order, and the block joins the eight run sums as the tree's top
+// three levels: ((r0 + r1) + (r2 + r3)) + ((r4 + r5) + (r6 + r7)).  The
+// result equals the wave-per-output kernel's bit for bit.
+
+constexpr int kPlanThreads = 1024;
+constexpr int kTcRows = 64;                        // listed entries per block
+constexpr int kTcCh = 32;                          // output channels per block
+constexpr int kTcRuns = 8;                         // waves; run w = term blocks 8w .. 8w + 7
+constexpr int kTcThreads = kTcRuns * kWave;
+constexpr int kTcRunBlocks = (2 * kDim / kCompTerms) / kTcRuns;   // 8 term blocks per run
+constexpr int kTcChTiles = kDim / kTcCh;           // 18
+constexpr int kTcOpFloats = kCompTerms * (kTcRows + kTcCh);        // one wave's operands
+constexpr int kTcLdsFloats = kTcRuns * (kTcOpFloats + kTcRows * kTcCh);   // operands, then run sums
+static_assert(kTcRunBlocks == 8 && kTcRows == 64 && kTcCh == 32, "tile shape assumed below");
+// Entries the plan can list: each sequence of m rows completes at most
+// ceil(m / 2), so at most (total_new + batch) / 2 in all, and never more
+// than total_new.
+__host__ __device__ inline int64_t plan_bound(int64_t total_new, int batch)
+{
+    const int64_t b = (total_new + batch + 1) / 2;
+    return b < total_new ? b : total_new;
+}
+
+// One block.  For every sequence (1024 at a time): the entries its rows
+// complete (none when row_info would reject the sequence), an exclusive
+// prefix over sequences, then one plan record per completed entry in
+// sequence order: {input row, sequence, row of x_even (-1: pending), entry}.
+// count receives the number of records.
+__global__ __launch_bounds__(kPlanThreads) void compress_plan_kernel(AppendArgs a, int4 *plan, int32_t *count)
+{
+    __shared__ int s_off[kPlanThreads], s_row0[kPlanThreads], s_p[kPlanThreads];
+    __shared__ int s_wave[kPlanThreads / kWave];
+    const cskv_cache &c = a.c;
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+    int carry = 0;
+    for (int b0 = 0; b0 < c.batch; b0 += kPlanThreads) {
+        const int b = b0 + t;
+        int cnt = 0, row0 = 0, p = 0;
+        if (b < c.batch) {
+            row0 = a.cu_new ? a.cu_new[b] : b;
+            const int64_t m = a.cu_new ? (int64_t)a.cu_new[b + 1] - row0 : 1;
+            p = c.n_tokens[b];
+            if (p >= 0 && rows_ok(row0, m, a.total_new) && (p + m) / 2 <= c.capacity)
+                cnt = (int)((p + m) / 2 - p / 2);
+        }
+        int x = cnt;                                // inclusive scan over the block
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int y = __shfl_up(x, o);
+            if (lane >= o) x += y;
+        }
+        if (lane == kWave - 1) s_wave[w] = x;
+        __syncthreads();
+        if (w == 0) {
+            int v = lane < kPlanThreads / kWave ? s_wave[lane] : 0;
+            for (int o = 1; o < kPlanThreads / kWave; o <<= 1) {
+                const int y = __shfl_up(v, o);
+                if (lane >= o) v += y;
+            }
+            if (lane < kPlanThreads / kWave) s_wave[lane] = v;
+        }
+        __syncthreads();
+        s_off[t] = x - cnt + (w > 0 ? s_wave[w - 1] : 0);
+        s_row0[t] = row0;
+        s_p[t] = p;
+        const int total = s_wave[kPlanThreads / kWave - 1];
+        __syncthreads();
+        const int nb = c.batch - b0 < kPlanThreads ? c.batch - b0 : kPlanThreads;
+        for (int k = t; k < total; k += kPlanThreads) {
+            int lo = 0, hi = nb - 1;                // the last sequence whose offset is <= k
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_off[mid] <= k) lo = mid; else hi = mid - 1;
+            }
+            const int ps = s_p[lo];
+            const int q = ((ps & 1) ? 0 : 1) + 2 * (k - s_off[lo]);   // rows at odd positions complete
+            const int r = s_row0[lo] + q;
+            plan[carry + k] = make_int4(r, b0 + lo, q > 0 ? r - 1 : -1, (ps + q) >> 1);
+        }
+        carry += total;
+        __syncthreads();                            // before the next round reuses the arrays
+    }
+    if (t == 0) *count = carry;
+}
+
+// Block i runs on XCD i % 8 (round-robin dispatch); that XCD's j-th block
+// takes row tile (i % 8) + 8 (j / 18) and channel tile j % 18, so an XCD
+// sweeps all channels of one row tile before the next and its L2 holds the
+// tile's token rows while every XCD reads the whole weight matrix once.
+// Lane (ty, tx) of wave w owns entries 8 ty .. 8 ty + 7 and channels
+// 4 tx .. 4 tx + 3 of the tile for run w.  Per term block each wave stages
+// u's 18 terms of its 64 entries ([term][entry]) and W's of its 32 channels
+// ([term][channel]) in its own LDS area, prefetching the next block into
+// registers while it computes.
+__global__ __launch_bounds__(kTcThreads) void compress_tiled_kernel(AppendArgs a, const int4 *plan,
+                                                                    const int32_t *count)
+{
+    __shared__ __attribute__((aligned(16))) float lds[kTcLdsFloats];
+    __shared__ int s_rows[kTcRows];
+    const int n = *count;
+    const int i = blockIdx.x, j = i >> 3;
+    const int rt = (i & 7) + 8 * (j / kTcChTiles), ct = j % kTcChTiles;
+    const int k0 = rt * kTcRows;
+    if (k0 >= n) return;
+    const int c0 = ct * kTcCh;
+    const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int ty = lane >> 3, tx = lane & 7;
+    float *U = lds + w * kTcOpFloats;               // [18][64]
+    float *Wt = U + kCompTerms * kTcRows;           // [18][32]
+    float *R = lds + kTcRuns * kTcOpFloats;         // run sums [8][64][32]
+
+    // staging sources of this lane: entry `lane` of the tile (run w's terms
+    // lie in x_even for w < 4, in x_odd after), and W row c0 + (lane & 31),
+    // half (lane >> 5) of each block's 18 terms.  Entries past the list
+    // read token row 0 and are never stored.
+    const int k = k0 + lane;
+    const float *usrc = a.tokens;
+    if (k < n) {
+        const int4 pl = plan[k];
+        usrc = w < kTcRuns / 2 ? (pl.z >= 0 ? a.tokens + (size_t)pl.z * kDim : a.c.pending + (size_t)pl.y * kDim)
+                               : a.tokens + (size_t)pl.x * kDim;
+        if (w == 0) s_rows[lane] = pl.x;
+    }
+    usrc += (w % (kTcRuns / 2)) * kTcRunBlocks * kCompTerms;
+    const float *wsrc = a.w_comp + (size_t)(c0 + (lane & 31)) * (2 * kDim) + w * kTcRunBlocks * kCompTerms
+                      + (lane >> 5) * (kCompTerms / 2);
+
+    float2 pu[kCompTerms / 2];
+    float pw[kCompTerms / 2];
+    auto fetch = [&](int lb) {
+        const float2 *u2 = reinterpret_cast<const float2 *>(usrc + lb * kCompTerms);
+#pragma unroll
+        for (int t = 0; t < kCompTerms / 2; ++t) pu[t] = u2[t];
+        const float *wp = wsrc + lb * kCompTerms;
+#pragma unroll
+        for (int t = 0; t < kCompTerms / 2; ++t) pw[t] = wp[t];
+    };
+
+    // one term block of the run: stage the prefetched operands, prefetch the
+    // next block, fold the 18 terms from +0 into acc
+    auto block = [&](int lb, float (&acc)[8][4]) {
+        __syncthreads();                            // the previous block's operands are read
+#pragma unroll
+        for (int t = 0; t < kCompTerms / 2; ++t) {
+            U[(2 * t) * kTcRows + lane] = pu[t].x;
+            U[(2 * t + 1) * kTcRows + lane] = pu[t].y;
+            Wt[((lane >> 5) * (kCompTerms / 2) + t) * kTcCh + (lane & 31)] = pw[t];
+        }
+        __syncthreads();
+        if (lb + 1 < kTcRunBlocks) fetch(lb + 1);
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[r][q] = 0.0f;
+#pragma unroll 2
+        for (int t = 0; t < kCompTerms; ++t) {
+            const float4 ua = *reinterpret_cast<const float4 *>(U + t * kTcRows + 8 * ty);
+            const float4 ub = *reinterpret_cast<const float4 *>(U + t * kTcRows + 8 * ty + 4);
+            const float4 wv = *reinterpret_cast<const float4 *>(Wt + t * kTcCh + 4 * tx);
+            const float uu[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
+            const float ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[r][q] = fmaf(ww[q], uu[r], acc[r][q]);
+        }
+    };
+    // x += y over the thread's outputs (fp32 addition is commutative, so the
+    // operand order within one addition does not matter)
+    auto add = [](float (&x)[8][4], const float (&y)[8][4]) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) x[r][q] = x[r][q] + y[r][q];
+    };
+
+    // the run's pairwise tree, written out.  The first half's sum waits in
+    // this lane's own slots of the run-sum area (same lane, same addresses:
+    // no barrier) so that three arrays are live at a time, not four.
+    float *mine = R + (w * kTcRows + 8 * ty) * kTcCh + 4 * tx;
+    float lv0[8][4], lv1[8][4], acc[8][4];
+    fetch(0);
+    block(0, lv0);
+    block(1, acc);
+    add(lv0, acc);                                  // b0 + b1
+    block(2, lv1);
+    block(3, acc);
+    add(lv1, acc);                                  // b2 + b3
+    add(lv0, lv1);                                  // (b0 + b1) + (b2 + b3)
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        *reinterpret_cast<float4 *>(mine + r * kTcCh) = make_float4(lv0[r][0], lv0[r][1], lv0[r][2], lv0[r][3]);
+    block(4, lv0);
+    block(5, acc);
+    add(lv0, acc);                                  // b4 + b5
+    block(6, lv1);
+    block(7, acc);
+    add(lv1, acc);                                  // b6 + b7
+    add(lv0, lv1);                                  // (b4 + b5) + (b6 + b7)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        float4 *m = reinterpret_cast<float4 *>(mine + r * kTcCh);
+        const float4 h = *m;
+        *m = make_float4(h.x + lv0[r][0], h.y + lv0[r][1], h.z + lv0[r][2], h.w + lv0[r][3]);
+    }
+    __syncthreads();
+    for (int o = threadIdx.x; o < kTcRows * kTcCh; o += kTcThreads) {
+        const int row = o / kTcCh, ch = o % kTcCh;
+        if (k0 + row >= n) break;                   // o grows with row
+        float P[kTcRuns];
+#pragma unroll
+        for (int p = 0; p < kTcRuns; ++p) P[p] = R[(p * kTcRows + row) * kTcCh + ch];
+        const float e = ((P[0] + P[1]) + (P[2] + P[3])) + ((P[4] + P[5]) + (P[6] + P[7]));
+        a.ent[(size_t)s_rows[row] * kDim + c0 + ch] = e;
+    }
+}
+
+// Quantiser of a planned append: kQPer listed entries per block, the
+// compressor's output read from the entry's input row.
+constexpr int kQPer = 4;
+__global__ __launch_bounds__(kAppendThreads) void quantize_planned_kernel(AppendArgs a, const int4 *plan,
+                                                                          const int32_t *count)
+{
+    __shared__ float wave_max[kAppendThreads / kWave];
+    const int n = *count;
+    const int k0 = blockIdx.x * kQPer;
+    if (k0 >= n) return;
+    const int t = threadIdx.x;
+    int4 pl[kQPer];
+    float e[kQPer];
+#pragma unroll
+    for (int i = 0; i < kQPer; ++i) pl[i] = k0 + i < n ? plan[k0 + i] : make_int4(-1, 0, -1, 0);
+#pragma unroll
+    for (int i = 0; i < kQPer; ++i) e[i] = pl[i].x >= 0 ? a.ent[(size_t)pl[i].x * kDim + t] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < kQPer; ++i)
+        if (pl[i].x >= 0)                           // uniform over the block
+            quantize_entry(a, e[i], t, (size_t)pl[i].y * a.c.capacity + (size_t)pl[i].w, pl[i].x, wave_max);
+}
+
+// Workspace of an append with the compressor: the compressor's fp32 rows,
+// then the plan records and their count.
+struct AppendWs {
+    size_t plan_off, count_off, total;
+};
+inline AppendWs append_ws_layout(int64_t total_new)
+{
+    AppendWs L;
+    L.plan_off = ((size_t)total_new * kDim * sizeof(float) + 255) / 256 * 256;
+    L.count_off = L.plan_off + ((size_t)total_new * sizeof(int4) + 255) / 256 * 256;
+    L.total = L.count_off + 256;
+    return L;
+}
+
 }  // namespace
 
 size_t append_workspace_bytes(int total_new)
 {
-    return (size_t)total_new * kDim * sizeof(float);
+    return append_ws_layout(total_new).total;
 }
 
 hipError_t launch_kv_append(const cskv_cache &c, const float *tokens, const int32_t *cu_new,
@@ -438,22 +712,44 @@ hipError_t launch_kv_append(const cskv_cache &c, const float *tokens, const int3
     if (total_new == 0) return hipSuccess;
     AppendArgs a{c, tokens, cu_new, w_comp, idx_rows, static_cast<float *>(ws), total_new,
                  cu_new ? nullptr : swa_ring, swa_rows, swa_window};
-    const TimedLaunch tl = timer_take(CSKV_KERNEL_APPEND);
+    TimedLaunch tl = timer_take(CSKV_KERNEL_APPEND);
     // one row per sequence: the quantiser also finalises (one launch less)
     const bool fused = cu_new == nullptr;
     const dim3 qgrid((unsigned)total_new), qblock(kAppendThreads);
-    if (w_comp) {
+    if (w_comp && cu_new && total_new >= kTiledMinRows) {
+        // a large append: plan, tiled compressor, planned quantiser, finalise
+        const TimedLaunch tc = timer_take(CSKV_KERNEL_COMPRESS);
+        hipEvent_t comp_start = tl.start;
+        if (tc.start) comp_start = tc.start;
+        else tl.start = nullptr;
+        const AppendWs L = append_ws_layout(total_new);
+        int4 *plan = reinterpret_cast<int4 *>(static_cast<char *>(ws) + L.plan_off);
+        int32_t *count = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + L.count_off);
+        const int64_t bound = plan_bound(total_new, c.batch);
+        const int64_t row_tiles8 = ((bound + kTcRows - 1) / kTcRows + 7) / 8 * 8;
+        launch_kernel(compress_plan_kernel, dim3(1), dim3(kPlanThreads), s, comp_start, nullptr, a, plan, count);
+        launch_kernel(compress_tiled_kernel, dim3((unsigned)(row_tiles8 * kTcChTiles)), dim3(kTcThreads), s,
+                      nullptr, tc.stop, a, (const int4 *)plan, (const int32_t *)count);
+        launch_kernel(quantize_planned_kernel, dim3((unsigned)((bound + kQPer - 1) / kQPer)), qblock, s, tl.start,
+                      nullptr, a, (const int4 *)plan, (const int32_t *)count);
+        launch_kernel(append_finalize_kernel<true>, dim3((unsigned)c.batch), dim3(kWave), s, nullptr, tl.stop, a);
+    } else if (w_comp) {
+        // the compressor timed alone: the append interval starts after it
+        const TimedLaunch tc = timer_take(CSKV_KERNEL_COMPRESS);
+        hipEvent_t comp_start = tl.start;
+        if (tc.start) comp_start = tc.start;
+        else tl.start = nullptr;
         // about 1024 waves: groups of 8 input rows x runs of output channels
         constexpr int kE = 8;
         const int groups = (total_new + kE - 1) / kE;
         const int runs = groups >= 1024 ? 1 : (1024 / groups < kDim ? 1024 / groups : kDim);
         const int cpw = (kDim + runs - 1) / runs;
         launch_kernel(compress_kernel<kE>, dim3((unsigned)((kDim + cpw - 1) / cpw), (unsigned)groups), dim3(kWave),
-                      s, tl.start, nullptr, a, cpw);
+                      s, comp_start, tc.stop, a, cpw);
         if (fused) {
-            launch_kernel(quantize_kernel<true, true>, qgrid, qblock, s, nullptr, tl.stop, a);
+            launch_kernel(quantize_kernel<true, true>, qgrid, qblock, s, tl.start, tl.stop, a);
         } else {
-            launch_kernel(quantize_kernel<true, false>, qgrid, qblock, s, nullptr, nullptr, a);
+            launch_kernel(quantize_kernel<true, false>, qgrid, qblock, s, tl.start, nullptr, a);
             launch_kernel(append_finalize_kernel<true>, dim3((unsigned)c.batch), dim3(kWave), s, nullptr, tl.stop, a);
         }
     } else if (fused) {

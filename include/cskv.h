@@ -161,8 +161,10 @@ int cskv_kv_append_fp4(const cskv_cache *cache, const float *tokens, const int32
                        int32_t total_new, const float *w_comp, const uint16_t *idx_rows,
                        void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes of cskv_kv_append_fp4 (total_new * dim * 4 with a
- * compressor, else a nominal 256). */
+/* Workspace bytes of cskv_kv_append_fp4: with a compressor, the fp32
+ * compressor rows (total_new * dim * 4), then one 16-byte record per row for
+ * the list of rows that complete an entry (used by appends of 512 rows or
+ * more) and a count, each region rounded up to 256 bytes; else a nominal 256. */
 size_t cskv_append_workspace_bytes(int32_t total_new, const float *w_comp);
 
 /*
@@ -415,13 +417,17 @@ const char *cskv_last_error(void);
  * and returns the summed milliseconds and the count.  cskv_timer_pause(kind,
  * 1) stops recording for that kind (launches run untimed) until
  * cskv_timer_pause(kind, 0), so a bench can time a sample of its steps.  Not
- * thread-safe; meant for benches.
+ * thread-safe; meant for benches.  CSKV_KERNEL_COMPRESS times the stand-in
+ * compressor's kernel of an append alone; when it and CSKV_KERNEL_APPEND are
+ * both on, the APPEND interval then starts at the quantiser (the kernel
+ * after the compressor).
  */
 #define CSKV_KERNEL_APPEND 1
 #define CSKV_KERNEL_SWA_APPEND 2
 #define CSKV_KERNEL_INDEXER_SCAN 3
 #define CSKV_KERNEL_TOPK_SELECT 4
 #define CSKV_KERNEL_ATTENTION 5
+#define CSKV_KERNEL_COMPRESS 6
 int cskv_timer_enable(int32_t kernel_kind, int32_t max_launches);
 int cskv_timer_pause(int32_t kernel_kind, int32_t paused);
 int cskv_timer_read(int32_t kernel_kind, double *total_ms, int32_t *count);

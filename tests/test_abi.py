@@ -148,7 +148,9 @@ def test_call_arguments_rejected_before_launch(L):
     assert L.cskv_kv_append_fp4(C.byref(d), vp(0x70000), None, 3, None, vp(0x80000), None, 0, None) == ck.EINVAL
     # a compressor append needs its workspace
     need = L.cskv_append_workspace_bytes(2, vp(0x110000))
-    assert need == 2 * 576 * 4 and L.cskv_append_workspace_bytes(2, None) == 256
+    # compressor rows (fp32), then one 16-byte plan record per row and a count,
+    # each region rounded to 256 bytes
+    assert need == 4608 + 256 + 256 and L.cskv_append_workspace_bytes(2, None) == 256
     assert L.cskv_kv_append_fp4(C.byref(d), vp(0x70000), None, 2, vp(0x110000), vp(0x80000), vp(0xB0000),
                                 need - 1, None) == ck.EWORKSPACE
     # top-k: k out of range, too many heads, workspace too small

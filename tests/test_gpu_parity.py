@@ -93,6 +93,58 @@ def test_append_compressor_pairs_pending_bitexact(ck, orc):
         assert_cache_equal(gc, hc)
 
 
+@pytest.mark.parametrize("k_group,v_group,idx_dim", [(32, 128, 128), (64, 0, 64)])
+def test_append_compressor_large_calls_bitexact(ck, orc, k_group, v_group, idx_dim):
+    """Appends of 512 rows or more take the planned, tiled compressor: more
+    than 1024 sequences (the plan covers them in rounds), empty sequences,
+    sequences that start on a pending token, long runs of both parities, and
+    one sequence whose rows would pass capacity (left untouched, flagged).
+    Everything must equal the oracle bit for bit, over three calls."""
+    W = synth.w_comp(synth.WORKLOADS["tiny_t4096"])
+    Wd = dev(W)
+    B, cap = 1100, 400
+    gc, hc = pair(B, cap, k_group, v_group, idx_dim)
+    g = np.random.default_rng(31 + k_group)
+    for call in range(3):
+        lens = g.integers(0, 3, size=B)
+        lens[g.integers(0, B, size=6)] = g.integers(100, 301, size=6)
+        lens[7] = 0
+        if call == 2:
+            lens[1099] = 2 * cap + 2      # past capacity whatever the parity: rejected
+        if call == 1:
+            lens[:] = np.minimum(lens, 1)
+            lens[:600] = 1                # a few hundred single rows; >= 512 rows in all
+        toks = synth.normal(g, (int(lens.sum()), 576))
+        toks[::5] *= np.float32(30.0)
+        irows = synth.int_bf16(g, (int(lens.sum()), idx_dim))
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        assert cu[-1] >= 512
+        ck.kv_append_fp4(gc, dev(toks), dev(cu), Wd, dev(irows))
+        orc.kv_append(hc, toks, cu, W, irows)
+        assert_cache_equal(gc, hc)
+    assert int(host(gc.status)[0]) == ck.STATUS_OVERFLOW
+
+
+@pytest.mark.parametrize("rows", [511, 512, 4097])
+def test_append_compressor_paths_agree(ck, orc, rows):
+    """One long sequence just below, at and above the row count where the
+    planned path starts, onto an odd token count (a pending partner)."""
+    W = synth.w_comp(synth.WORKLOADS["tiny_t4096"])
+    gc, hc = pair(2, 2200, 32, 0, 64)
+    g = np.random.default_rng(rows)
+    first = synth.normal(g, (1, 576))
+    ir0 = synth.int_bf16(g, (1, 64))
+    cu0 = np.array([0, 1, 1], np.int32)
+    ck.kv_append_fp4(gc, dev(first), dev(cu0), dev(W), dev(ir0))
+    orc.kv_append(hc, first, cu0, W, ir0)
+    toks = synth.normal(g, (rows, 576))
+    irows = synth.int_bf16(g, (rows, 64))
+    cu = np.array([0, rows, rows], np.int32)
+    ck.kv_append_fp4(gc, dev(toks), dev(cu), dev(W), dev(irows))
+    orc.kv_append(hc, toks, cu, W, irows)
+    assert_cache_equal(gc, hc)
+
+
 def test_append_one_row_per_sequence_and_overflow(ck, orc):
     w = synth.WORKLOADS["tiny_t4096"]
     W = synth.w_comp(w)
