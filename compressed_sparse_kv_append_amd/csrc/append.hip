@@ -583,15 +583,21 @@ __global__ __launch_bounds__(kTcThreads) void compress_tiled_kernel(AppendArgs a
 
     // one term block of the run: stage the prefetched operands, prefetch the
     // next block, fold the 18 terms from +0 into acc
+    // The operand area is the wave's own and one wave's LDS operations run
+    // in issue order, so the wave only fences its own accesses (the
+    // compiler may not move LDS reads across the writes), with no block
+    // barrier.
     auto block = [&](int lb, float (&acc)[8][4]) {
-        __syncthreads();                            // the previous block's operands are read
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int t = 0; t < kCompTerms / 2; ++t) {
             U[(2 * t) * kTcRows + lane] = pu[t].x;
             U[(2 * t + 1) * kTcRows + lane] = pu[t].y;
             Wt[((lane >> 5) * (kCompTerms / 2) + t) * kTcCh + (lane & 31)] = pw[t];
         }
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
         if (lb + 1 < kTcRunBlocks) fetch(lb + 1);
 #pragma unroll
         for (int r = 0; r < 8; ++r)
@@ -683,6 +689,78 @@ __global__ __launch_bounds__(kAppendThreads) void quantize_planned_kernel(Append
             quantize_entry(a, e[i], t, (size_t)pl[i].y * a.c.capacity + (size_t)pl[i].w, pl[i].x, wave_max);
 }
 
+// Quantiser of a planned append for caches with fp32 group scales and bf16
+// indexer keys: one wave per listed entry, no block barrier.  Lane l holds
+// the latent channels 8 l .. 8 l + 7 (it packs their codes into one word
+// itself) and RoPE channel 512 + l.  A group of g latent channels spans g/8
+// lanes; the RoPE channels (g = 32 or 64 inside 64 lanes) reduce and pack
+// with lane exchanges.  Same arithmetic as quantize_channel: absmax, s =
+// absmax / 6 by IEEE division, codes of x / s.
+constexpr int kQwWaves = 4;
+__device__ __forceinline__ float xor_max(float a, int lanes)
+{
+    for (int off = 1; off < lanes; off <<= 1) a = fmaxf(a, __shfl_xor(a, off));
+    return a;
+}
+
+// The code word of one lane's 8 latent channels with group g (g >= 8) into
+// plane row `codes` / `scales`.
+__device__ __forceinline__ void quantize_lane8(const float (&x)[8], int lane, int g, uint8_t *codes, float *scales)
+{
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
+    a = xor_max(a, g / 8);
+    const float s = a / 6.0f;                      // IEEE division (no fast-math)
+    uint32_t word = 0;
+    if (s != 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) word |= e2m1_code(x[i] / s) << (4 * i);
+    }
+    reinterpret_cast<uint32_t *>(codes)[lane] = word;
+    if ((lane % (g / 8)) == 0) scales[lane / (g / 8)] = s;
+}
+
+__global__ __launch_bounds__(kQwWaves * kWave) void quantize_planned_wave_kernel(AppendArgs a, const int4 *plan,
+                                                                                 const int32_t *count)
+{
+    const cskv_cache &c = a.c;
+    const int n = *count;
+    const int k = blockIdx.x * kQwWaves + threadIdx.x / kWave;
+    if (k >= n) return;                             // whole waves
+    const int lane = threadIdx.x & (kWave - 1);
+    const int4 pl = plan[k];
+    const float *row = a.ent + (size_t)pl.x * kDim;
+    const float4 lo = reinterpret_cast<const float4 *>(row)[2 * lane];
+    const float4 hi = reinterpret_cast<const float4 *>(row)[2 * lane + 1];
+    const float xr = row[8 * kWave + lane];
+    const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    const size_t slot = (size_t)pl.y * c.capacity + (size_t)pl.w;
+    const int kg = c.k_group;
+    uint8_t *kc = c.k_codes + slot * (kDim / 2);
+    float *ks = c.k_scales + slot * (kDim / kg);
+    quantize_lane8(x, lane, kg, kc, ks);
+    {   // RoPE channels 512 .. 575: groups of kg lanes
+        const float ar = xor_max(fabsf(xr), kg);
+        const float sr = ar / 6.0f;
+        uint32_t code = sr != 0.0f ? e2m1_code(xr / sr) : 0u;
+        code |= __shfl_down(code, 1) << 4;
+        code |= __shfl_down(code, 2) << 8;
+        code |= __shfl_down(code, 4) << 16;
+        if ((lane & 7) == 0) *reinterpret_cast<uint32_t *>(kc + 4 * kWave + lane / 2) = code;
+        if ((lane % kg) == 0) ks[(8 * kWave + lane) / kg] = sr;
+    }
+    if (c.v_group > 0) {
+        const int dv = c.dim - c.rope_dim;          // 512: the latent channels
+        quantize_lane8(x, lane, c.v_group, c.v_codes + slot * (dv / 2), c.v_scales + slot * (dv / c.v_group));
+    }
+    if (c.idx_dim == 2 * kWave)
+        reinterpret_cast<uint32_t *>(c.idx_keys + slot * c.idx_dim)[lane] =
+            reinterpret_cast<const uint32_t *>(a.idx_rows + (size_t)pl.x * c.idx_dim)[lane];
+    else
+        c.idx_keys[slot * c.idx_dim + lane] = a.idx_rows[(size_t)pl.x * c.idx_dim + lane];
+}
+
 // Workspace of an append with the compressor: the compressor's fp32 rows,
 // then the plan records and their count.
 struct AppendWs {
@@ -730,8 +808,13 @@ hipError_t launch_kv_append(const cskv_cache &c, const float *tokens, const int3
         launch_kernel(compress_plan_kernel, dim3(1), dim3(kPlanThreads), s, comp_start, nullptr, a, plan, count);
         launch_kernel(compress_tiled_kernel, dim3((unsigned)(row_tiles8 * kTcChTiles)), dim3(kTcThreads), s,
                       nullptr, tc.stop, a, (const int4 *)plan, (const int32_t *)count);
-        launch_kernel(quantize_planned_kernel, dim3((unsigned)((bound + kQPer - 1) / kQPer)), qblock, s, tl.start,
-                      nullptr, a, (const int4 *)plan, (const int32_t *)count);
+        if (c.k_format == CSKV_KV_F32 && c.idx_format == CSKV_IDX_BF16)
+            launch_kernel(quantize_planned_wave_kernel, dim3((unsigned)((bound + kQwWaves - 1) / kQwWaves)),
+                          dim3(kQwWaves * kWave), s, tl.start, nullptr, a, (const int4 *)plan,
+                          (const int32_t *)count);
+        else
+            launch_kernel(quantize_planned_kernel, dim3((unsigned)((bound + kQPer - 1) / kQPer)), qblock, s,
+                          tl.start, nullptr, a, (const int4 *)plan, (const int32_t *)count);
         launch_kernel(append_finalize_kernel<true>, dim3((unsigned)c.batch), dim3(kWave), s, nullptr, tl.stop, a);
     } else if (w_comp) {
         // the compressor timed alone: the append interval starts after it
