@@ -79,13 +79,16 @@ __device__ __forceinline__ RowInfo row_info(const AppendArgs &a, int64_t r)
 // e[ch] = sum_j W[ch][j] u[j], u = x_even || x_odd, in a fixed fp32 order:
 // the 1152 terms are cut into 64 blocks of 18, each folded upward from +0
 // with one fused multiply-add per term, and the 64 block sums are added as a
-// pairwise tree (blocks 2i and 2i+1 first).  Lane l of a wave owns block l:
-// it keeps u's 18 terms of E input rows in registers and reads
-// W[ch][18 l .. 18 l + 17], so the wave reads each W row contiguously once
-// for all E rows.  The tree is four DPP steps inside each row of 16 lanes
-// (lane p adds lane p + w) and one scalar step over the four row sums.  A
-// wave takes `cpw` output channels of E consecutive input rows.
-constexpr int kCompTerms = 2 * kDim / kWave;     // 18 terms per lane
+// pairwise tree (blocks 2i and 2i+1 first).  The tiled kernel of large appends
+// cuts the tree at its level-3 nodes instead (see there).
+constexpr int kCompTerms = 2 * kDim / kWave;     // 18 terms per block
+
+// Small appends (a decode step): lane l of a wave owns block l; it keeps
+// u's 18 terms of E input rows in registers and reads W[ch][18 l ..
+// 18 l + 17], so the wave reads each W row contiguously once for all E
+// rows.  The tree is four DPP steps inside each row of 16 lanes (lane p
+// adds lane p + w) and one scalar step over the four row sums.  A wave
+// takes `cpw` output channels of E consecutive input rows.
 constexpr int kDppRowShl = 0x100;
 
 template <int CTRL>
