@@ -239,6 +239,8 @@ def main():
     import synth
 
     ck.lib()
+    if a.workload == MODEL_PLAN:
+        return main_model(a, ck, synth, torch)
     w = synth.WORKLOADS[a.workload]
     if w.chunk_tokens:
         return main_mixed(a, ck, synth, torch)
@@ -430,7 +432,193 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-ALU_PEAK_TFLOPS = 157.3      # MI355X fp32 vector: 256 CUs x 256 FMA lanes x 2 x 2.4 GHz
+ALU_PEAK_TFLOPS = 157.3      # MI355X fp32 vector, packed FMAs: 256 CUs x 4 SIMDs x 16 lanes x 2 x 2 FLOP x 2.4 GHz
+ALU_PEAK_UNPACKED_TFLOPS = 78.6   # the same without packed fp32 (this build compiles it off)
+MODEL_PLAN = "model_plan_64k_b32"
+
+
+def filler_rows(torch, seed, n, dim, law):
+    """fp32 [n, dim] on the GPU, seeded, with the workload's value law."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    z = torch.randn(n, dim, generator=g, device="cuda")
+    if law == "t3":
+        chi = torch.randn(n, dim, 3, generator=g, device="cuda").square().sum(-1)
+        z = z / torch.sqrt(chi / 3)
+    return z.contiguous()
+
+
+def filler_keys(torch, seed, n, dim):
+    """bf16 bits [n, dim] of integers uniform in [-8, 8], on the GPU, seeded."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    return torch.randint(-8, 9, (n, dim), generator=g, device="cuda").to(torch.bfloat16).view(torch.int16).contiguous()
+
+
+def main_model(a, ck, synth, torch):
+    """One decode step of the pages' whole CSA2 layer plan at the 64K x 32
+    size: three encoder caches of 32,768 entries (2->1 compression, Full + 5
+    Reuse each) and the decoder cache of 65,536 entries (one per token, the
+    new entry from the CED projection of a 4096-wide hidden state), read by
+    Full + 3 Reuse and four Reindex + 3 Reuse groups: 38 layers, one
+    cskv_model_decode call per step.  Student-t(3) entries, integer indexer
+    keys and queries, N(0,1) queries and window rows, drawn on the GPU with
+    seeded generators (the caches are too large to draw on the host in
+    reasonable time); token counts are restored between steps outside the
+    timed region so every step sees the same caches."""
+    import oracle as orc
+    B, T, kg, Di, Hi, Hq, K, W, dm = 32, 65536, 64, 128, 64, 64, 512, 128, 4096
+    pool = tuple(int(x) for x in a.pool.split(",")) if a.pool else None
+    plan = orc.csa2_plan()
+    scale = 1 / math.sqrt(576)
+    t0 = time.time()
+    groups, seed = [], 7000
+    Wc = filler_rows(torch, seed, 576, 1152, "normal") * 0.02
+    n_layers = 0
+    for gi, (name, ratio, modes) in enumerate(plan):
+        E = T // ratio
+        c = ck.Cache.allocate(B, E + 64, kg, 0, Di, ratio=ratio)
+        for b in range(B):
+            seed += 1
+            cu = np.zeros(B + 1, np.int32)
+            cu[b + 1:] = E
+            ck.kv_append_fp4(c, filler_rows(torch, seed, E, 576, "t3"), torch.from_numpy(cu).cuda(), None,
+                             filler_keys(torch, seed + 500_000, E, Di))
+        layers = []
+        for li, m in enumerate(modes):
+            seed += 1
+            layers.append(ck.Layer(mode=m, q=filler_rows(torch, seed, B * Hq, 576, "normal").view(B, Hq, 576),
+                                   q_idx=None if m == "reuse" else filler_keys(torch, seed + 1, B * Hi, Di).view(B, Hi, Di),
+                                   swa=filler_rows(torch, seed + 2, B * W, 576, "normal").to(torch.bfloat16)
+                                   .view(torch.int16).view(B, W, 576).contiguous(),
+                                   swa_row=filler_rows(torch, seed + 3, B, 576, "normal"),
+                                   idx=None if m == "reuse" else torch.empty(B, K, dtype=torch.int32, device="cuda"),
+                                   out=torch.empty(B, Hq, 512, device="cuda"), lse=torch.empty(B, Hq, device="cuda")))
+        n_layers += len(modes)
+        grp = ck.Group(cache=c, layers=layers, new_idx_rows=filler_keys(torch, seed + 4, B, Di),
+                       pool=pool if "reindex" in modes else None)
+        if ratio == 1:
+            grp.ced_h = filler_rows(torch, seed + 5, B, dm, "normal").to(torch.bfloat16).view(torch.int16).contiguous()
+            grp.ced_w = (filler_rows(torch, seed + 6, 576, dm, "normal") * 0.02).to(torch.bfloat16).view(torch.int16).contiguous()
+        else:
+            grp.new_tokens, grp.w_comp = filler_rows(torch, seed + 5, B, 576, "normal"), Wc
+        groups.append(grp)
+    torch.cuda.synchronize()
+    log(f"built {len(plan)} caches for {n_layers} layers in {time.time() - t0:.1f}s")
+    n0 = [g.cache.n_tokens.clone() for g in groups]
+    ws = ck.model_workspace(groups, K, W)
+
+    def step():
+        ck.model_decode(groups, K, W, scale, ws=ws)
+
+    def reset():
+        for g, n in zip(groups, n0):
+            g.cache.n_tokens.copy_(n)
+
+    for _ in range(a.warmup):
+        step()
+        reset()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    for e0, e1 in ev:
+        e0.record()
+        step()
+        e1.record()
+        reset()
+    torch.cuda.synchronize()
+    t = np.array([e0.elapsed_time(e1) * 1000.0 for e0, e1 in ev])
+    kinds = {"append": ck.KERNEL_APPEND, "indexer_scan": ck.KERNEL_INDEXER_SCAN,
+             "topk_select": ck.KERNEL_TOPK_SELECT, "attention": ck.KERNEL_ATTENTION}
+    reps = min(a.steps, 20)
+    for kd in kinds.values():
+        ck.timer_enable(kd, 64 * reps)
+    for _ in range(reps):
+        step()
+        reset()
+    torch.cuda.synchronize()
+    kern, scan_launches = {}, 0
+    for name, kd in kinds.items():
+        tot, cnt = ck.timer_read(kd)
+        kern[name] = 1000 * tot / reps
+        if name == "indexer_scan":
+            scan_us, scan_launches = 1000 * tot / max(cnt, 1), cnt // reps
+    ck.timer_disable_all()
+    status = [int(g.cache.status[0].item()) for g in groups]
+    assert all(x == 0 for x in status), f"cache status flags raised: {status}"
+    # algorithmic bytes of the step's scans: every full scan reads its cache's
+    # indexer keys (entries after the append), pooled scans the pooled rows
+    full_bytes, pooled_bytes = 0.0, 0.0
+    for (name, ratio, modes), g in zip(plan, groups):
+        E = T // ratio + 1
+        have_pool = False
+        for m in modes:
+            if m == "full":
+                full_bytes += B * (E * 2 * Di + Hi * Di * 2)
+                have_pool = pool is not None
+            elif m == "reindex":
+                if have_pool:
+                    pooled_bytes += B * (min(E, pool[0] * pool[1]) * 2 * Di + Hi * Di * 2)
+                else:
+                    full_bytes += B * (E * 2 * Di + Hi * Di * 2)
+    scan_total = full_bytes + pooled_bytes
+    achieved = scan_total / scan_launches / (scan_us * 1e-6) / 1e9 if scan_launches else 0.0
+    ms = float(t.mean()) / 1000.0
+    result = {
+        "metric": "CSA2 FP4 layer-plan decode: steps/s (all 38 layers, 4 caches) at 64K ctx",
+        "value": round(1000.0 / ms, 2), "unit": "steps/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded GPU generators; Student-t(3) entries, integer indexer inputs)",
+        "config": {"workload": MODEL_PLAN, "batch": B, "context_tokens": T, "k_group": kg, "idx_heads": Hi,
+                   "idx_dim": Di, "q_heads": Hq, "topk": K, "window": W, "ced_d_model": dm,
+                   "caches": [[n, r, len(m)] for n, r, m in plan], "layers": n_layers,
+                   "pool": list(pool) if pool else None, "launch": "eager",
+                   "tokens_per_s": round(1000.0 / ms * B, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "indexer_scan",
+                     "bytes_per_step": round(scan_total), "scans_per_step": scan_launches,
+                     "avg_us": round(scan_us, 2), "timing": "hip events, separate eager pass"},
+        "step_us": {"p10": round(float(np.percentile(t, 10)), 2), "p50": round(float(np.percentile(t, 50)), 2),
+                    "p90": round(float(np.percentile(t, 90)), 2), "timing": "hip events around each step"},
+        "kernels_us_per_step": {k: round(v, 2) for k, v in kern.items()},
+    }
+    if not a.no_cpu_baseline:
+        log("timing the oracle on a CPU sample ...")
+        result["cpu_baseline"] = model_cpu_baseline(synth, plan, B, T, kg, Di, Hi, Hq, K, W, 512, pool)
+    print(json.dumps(result), flush=True)
+
+
+def model_cpu_baseline(synth, plan, B, T, kg, Di, Hi, Hq, K, W, dm, pool):
+    """The oracle's model decode on a bounded sample: 2 of the batch's
+    sequences at full length in every cache (drawn with the host generators),
+    one step, scaled by B / 2; the cache build is untimed.  The CED width is
+    512 on the host (its cost is negligible beside the scans)."""
+    import oracle as orc
+    nseq = 2
+    g = np.random.default_rng(7000)
+    hgroups = []
+    for name, ratio, modes in plan:
+        E = T // ratio
+        hc = orc.Cache.empty(nseq, E + 8, 576, 64, kg, 0, Di, ratio=ratio)
+        for b in range(nseq):
+            cu = np.zeros(nseq + 1, np.int32)
+            cu[b + 1:] = E
+            orc.kv_append(hc, synth.student_t3(g, (E, 576)), cu, None, synth.int_bf16(g, (E, Di)))
+        L = len(modes)
+        hg = dict(cache=hc, modes=modes, q=[synth.normal(g, (nseq, Hq, 576)) for _ in range(L)],
+                  q_idx=[None if m == "reuse" else synth.int_bf16(g, (nseq, Hi, Di)) for m in modes],
+                  rings=[synth.normal_bf16_trunc(g, (nseq, W, 576)) for _ in range(L)],
+                  swa_rows=[synth.normal(g, (nseq, 576)) for _ in range(L)], idx_row=synth.int_bf16(g, (nseq, Di)))
+        if ratio == 1:
+            hg.update(ced_h=synth.int_bf16(g, (nseq, dm)), ced_w=synth.int_bf16(g, (576, dm)))
+        else:
+            hg.update(token=synth.normal(g, (nseq, 576)), w_comp=(g.standard_normal((576, 1152)) * 0.02).astype(np.float32))
+        hgroups.append(hg)
+    t0 = time.perf_counter()
+    orc.model_decode(hgroups, K, 1 / math.sqrt(576), pool=pool)
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": 1.0 / (dt * B / nseq), "unit": "steps/s", "cores": min(threads, nseq), "kind": "oracle",
+            "sample": f"{nseq} of {B} sequences at full length in all {len(plan)} caches, one step of all layers "
+                      f"in {dt:.1f} s, scaled by {B}/{nseq}; cache build untimed"}
 
 
 def build_ragged(ck, synth, w, cap, dev, torch):
@@ -611,6 +799,8 @@ def main_mixed(a, ck, synth, torch):
                    "layers": ["full"]},
         "roofline": {"bound": "alu", "achieved": round(comp_tflops, 2), "peak": ALU_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(comp_tflops / ALU_PEAK_TFLOPS, 4), "traffic": None,
+                     "peak_unpacked": ALU_PEAK_UNPACKED_TFLOPS,
+                     "frac_unpacked": round(comp_tflops / ALU_PEAK_UNPACKED_TFLOPS, 4),
                      "kernel": "compress", "flops_per_step": round(comp_flops), "avg_us": round(comp_us, 2),
                      "timing": "hip events on the compressor's launch, separate eager pass"},
         "roofline_scan": {"bound": "hbm", "achieved": round(scan_gbps, 1), "peak": HBM_PEAK_GBPS,
