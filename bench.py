@@ -84,12 +84,24 @@ def copy_probe(mib: int):
     print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
 
 
-def build_replicas(ck, synth, w, cap, dev, n, idx_format=0, swa_format=0, k_format=0):
+def build_replicas(ck, synth, w, cap, dev, n, idx_format=0, swa_format=0, k_format=0, prefill=False):
     """Entries-mode build of n identical cache replicas, one sequence at a time
-    (each sequence's entries are drawn once and appended to every replica)."""
+    (each sequence's entries are drawn once and appended to every replica);
+    prefill: each sequence's prefill tokens through the compressor instead."""
     import torch
     reps = [ck.Cache.allocate(w.batch, cap, w.k_group, w.v_group, w.idx_dim, idx_format=idx_format,
                               swa_format=swa_format, k_format=k_format) for _ in range(n)]
+    if prefill:
+        W = dev(synth.w_comp(w))
+        for b in range(w.batch):
+            toks = dev(synth.prefill_tokens(w, b, w.prefill_tokens))
+            rows = dev(synth.prefill_idx_rows(w, b, w.prefill_tokens))
+            cu = np.zeros(w.batch + 1, np.int32)
+            cu[b + 1:] = w.prefill_tokens
+            for c in reps:
+                ck.kv_append_fp4(c, toks, dev(cu), W, rows)
+        torch.cuda.synchronize()
+        return reps
     for b in range(w.batch):
         ents = dev(synth.cache_entries(w, b))
         keys = dev(synth.cache_idx_keys(w, b))
@@ -161,11 +173,18 @@ def cpu_baseline(synth, w, nseq: int, seconds: float, pool=None, idx_format=0, s
     cap = w.entries + max_steps // 2 + 8
     hc = orc.Cache.empty(nseq, cap, w.dim, w.rope_dim, w.k_group, w.v_group, w.idx_dim,
                          idx_format=idx_format, swa_format=swa_format, k_format=k_format)
-    ents = np.concatenate([synth.cache_entries(w, b) for b in seqs])
-    keys = np.concatenate([synth.cache_idx_keys(w, b) for b in seqs])
-    cu = (np.arange(nseq + 1) * w.entries).astype(np.int32)
     t0 = time.time()
-    orc.kv_append(hc, ents, cu, None, keys)
+    if w.prefill_tokens:                       # through the compressor, as on the GPU
+        n = w.prefill_tokens
+        orc.kv_append(hc, np.concatenate([synth.prefill_tokens(w, b, n) for b in seqs]),
+                      (np.arange(nseq + 1) * n).astype(np.int32), synth.w_comp(w),
+                      np.concatenate([synth.prefill_idx_rows(w, b, n) for b in seqs]))
+        ents = None
+    else:
+        ents = np.concatenate([synth.cache_entries(w, b) for b in seqs])
+        keys = np.concatenate([synth.cache_idx_keys(w, b) for b in seqs])
+        cu = (np.arange(nseq + 1) * w.entries).astype(np.int32)
+        orc.kv_append(hc, ents, cu, None, keys)
     log(f"cpu baseline: oracle cache build {time.time() - t0:.1f}s (untimed)")
     del ents
     st = synth.step_inputs(w, 0, seqs=seqs)
@@ -244,6 +263,11 @@ def main():
     w = synth.WORKLOADS[a.workload]
     if w.chunk_tokens:
         return main_mixed(a, ck, synth, torch)
+    prefill = w.entries is None and w.prefill_tokens
+    if prefill:
+        # the tiny workload: its cache is built from prefill tokens through
+        # the compressor (an odd count: the last token waits as pending)
+        w = synth.scaled(w, entries=(w.prefill_tokens + 1) // 2)
     assert w.entries is not None, "bench steps fixed-length workloads"
     mx16 = a.kv_format == "mx16"
     if mx16:
@@ -263,7 +287,8 @@ def main():
     idx_fp4 = a.idx_format == "fp4"
     swa_fp8 = a.swa_format == "fp8"
     reps = build_replicas(ck, synth, w, cap, dev, a.replicas, ck.IDX_FP4 if idx_fp4 else ck.IDX_BF16,
-                          ck.SWA_FP8 if swa_fp8 else ck.SWA_BF16, ck.KV_MX16 if mx16 else ck.KV_F32)
+                          ck.SWA_FP8 if swa_fp8 else ck.SWA_BF16, ck.KV_MX16 if mx16 else ck.KV_F32,
+                          prefill=prefill)
     log(f"built {a.replicas} cache replicas in {time.time() - t0:.1f}s (indexer keys {a.idx_format}, "
         f"window {a.swa_format}, main entries {a.kv_format})")
 
@@ -398,7 +423,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded; Student-t(3) cache entries, integer indexer inputs)",
+        "data": "synthetic (seeded; %s cache entries, integer indexer inputs)"
+                % {"t3": "Student-t(3)", "normal": "N(0,1)", "outliers": "N(0,1) with 1% x20 outliers"}[w.entry_law]
+                + (", built from prefill tokens through the compressor" if prefill else ""),
         "config": {"workload": w.name, "batch": B, "context_tokens": 2 * w.entries,
                    "entries_per_seq": w.entries, "k_group": w.k_group, "storage": "e2m1+e8m0/16" if mx16 else "e2m1+fp32 scales",
                    "idx_heads": w.idx_heads, "idx_dim": w.idx_dim, "q_heads": w.q_heads,
@@ -425,6 +452,9 @@ def main():
         "step_hbm_frac": round(sb["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
     }
+    if prefill:
+        result["config"]["prefill_tokens"] = w.prefill_tokens
+        result["config"]["context_tokens"] = w.prefill_tokens + 1
     if not a.no_cpu_baseline:
         log("timing the oracle on a CPU sample ...")
         result["cpu_baseline"] = cpu_baseline(synth, w, a.cpu_baseline_seqs, a.cpu_baseline_seconds, pool,

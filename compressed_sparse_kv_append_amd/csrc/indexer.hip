@@ -26,6 +26,19 @@ int topk_slices(const cskv_cache &c) { return (int)((c.capacity + kSliceKeys - 1
 // Candidate pairs per sequence, rounded to even so each list is 16-byte aligned.
 static size_t cand_stride(const cskv_cache &c, int k) { return ((size_t)topk_slices(c) * k + 1) & ~(size_t)1; }
 
+// Caches of many slices merge in two levels: blocks of kGroupSlices slice
+// lists first (one block each, in parallel), then the groups' lists.  One
+// merge block over 122 lists of 512 (a 1M-token sequence) ran 4 rounds of
+// its select; two levels keep every select to one round.
+constexpr int kGroupSlices = 8;
+constexpr int kGroupMinSlices = 25;
+static int topk_groups(const cskv_cache &c, int k)
+{
+    const int s = topk_slices(c);
+    return s >= kGroupMinSlices && k < kSliceKeys ? (s + kGroupSlices - 1) / kGroupSlices : 0;
+}
+static size_t cand2_stride(const cskv_cache &c, int k) { return ((size_t)topk_groups(c, k) * k + 1) & ~(size_t)1; }
+
 TopkWorkspace topk_workspace(const cskv_cache &c, int k)
 {
     TopkWorkspace w;
@@ -33,7 +46,9 @@ TopkWorkspace topk_workspace(const cskv_cache &c, int k)
     w.cand_off = align_up(sizeof(uint32_t) * score_key_stride(c) * (size_t)c.batch, 256);
     const size_t slices = (size_t)topk_slices(c);
     const size_t cand = slices > 1 ? sizeof(uint32_t) * 2 * cand_stride(c, k) * c.batch : 0;
-    w.total = align_up(w.cand_off + cand, 256);
+    w.cand2_off = align_up(w.cand_off + cand, 256);
+    const size_t cand2 = topk_groups(c, k) > 0 ? sizeof(uint2) * cand2_stride(c, k) * c.batch : 0;
+    w.total = align_up(w.cand2_off + cand2, 256);
     return w;
 }
 
@@ -86,6 +101,11 @@ struct SelectArgs {
     size_t key_stride, cand_stride;
     int group;              // entries per item: a sequence of E entries has ceil(E / group) items
     int ratio;              // tokens per entry of the cache
+    // two-level merge (groups > 0): the group lists [B][cand2_stride],
+    // groups x k (key, index) pairs per sequence
+    uint2 *cand2 = nullptr;
+    size_t cand2_stride = 0;
+    int groups = 0;
 };
 
 // Items of sequence b: its entries, or its blocks of `group` entries.
@@ -414,11 +434,57 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(SelectArgs a)
     // entries) slots are valid: the padding after them is not read
     const int64_t used = (E + kSliceKeys - 1) / kSliceKeys;
     const int64_t last = E - (used - 1) * kSliceKeys;
+    if (a.groups > 0) {
+        // the group lists: a group of two or more slices holds exactly k
+        // valid pairs (its first slice is full, k < 4096), a one-slice
+        // group its slice's list (pads hold key 0, never valid)
+        const int64_t ug = (used + kGroupSlices - 1) / kGroupSlices;
+        const uint2 *gl = a.cand2 + (size_t)b * a.cand2_stride;
+        if (ug == 1) {                              // group 0 has >= 2 slices: its k pairs are the answer
+            for (int i = threadIdx.x; i < a.k; i += kMergeThreads) out[i] = (int32_t)gl[i].y;
+            return;
+        }
+        Items it{nullptr, gl, ug * a.k, 0};
+        if (it.n <= kMergeThreads * kMergePerSmall)
+            select_topk<true, false, kMergeThreads, kMergePerSmall>(sm, it, a.k, out, nullptr);
+        else
+            select_topk<true, false, kMergeThreads, kMergePer>(sm, it, a.k, out, nullptr);
+        return;
+    }
     Items it{nullptr, a.cand + (size_t)b * a.cand_stride, (used - 1) * a.k + (last < a.k ? last : a.k), 0};
     if (it.n <= kMergeThreads * kMergePerSmall)
         select_topk<true, false, kMergeThreads, kMergePerSmall>(sm, it, a.k, out, nullptr);
     else
         select_topk<true, false, kMergeThreads, kMergePer>(sm, it, a.k, out, nullptr);
+}
+
+// First level of the two-level merge: group g of sequence b, slices
+// [8 g, 8 g + 8) of those holding entries, to its top-k (key, index) pairs
+// in index order.  The union of the groups' top-k lists holds the
+// sequence's top-k, as the slices' lists do.
+__global__ __launch_bounds__(kMergeThreads) void topk_group_kernel(SelectArgs a)
+{
+    __shared__ SelectSmem<kMergeThreads> sm;
+    const int b = blockIdx.y, g = blockIdx.x;
+    const int64_t E = items_of(a, b);
+    if (E <= a.k || E <= kSliceKeys) return;         // the merge reads the keys directly
+    const int64_t used = (E + kSliceKeys - 1) / kSliceKeys;
+    const int64_t s0 = (int64_t)g * kGroupSlices;
+    if (s0 >= used) return;                          // the merge reads only the groups in use
+    const int64_t s1 = s0 + kGroupSlices < used ? s0 + kGroupSlices : used;
+    uint2 *out = a.cand2 + (size_t)b * a.cand2_stride + (size_t)g * a.k;
+    const uint2 *in = a.cand + (size_t)b * a.cand_stride + (size_t)s0 * a.k;
+    if (s1 - s0 == 1) {                              // one list: its own top-k already
+        for (int i = threadIdx.x; i < a.k; i += kMergeThreads) out[i] = in[i];
+        return;
+    }
+    // the group's first slice is full (4096 > k entries): more than k valid
+    const int64_t last = s1 == used ? E - (used - 1) * kSliceKeys : kSliceKeys;
+    Items it{nullptr, in, (s1 - s0 - 1) * a.k + (last < a.k ? last : a.k), 0};
+    if (it.n <= kMergeThreads * kMergePerSmall)
+        select_topk<true, true, kMergeThreads, kMergePerSmall>(sm, it, a.k, nullptr, out);
+    else
+        select_topk<true, true, kMergeThreads, kMergePer>(sm, it, a.k, nullptr, out);
 }
 
 // Top-k among the pooled entries of sequence b, from the pooled scan's
@@ -447,6 +513,9 @@ void launch_select(const SelectArgs &se, int batch, hipStream_t s, const TimedLa
     if (se.slices > 1) {
         launch_kernel(topk_slice_kernel, dim3((unsigned)se.slices, (unsigned)batch), dim3(kSliceThreads), s,
                       tk.start, nullptr, se);
+        if (se.groups > 0)
+            launch_kernel(topk_group_kernel, dim3((unsigned)se.groups, (unsigned)batch), dim3(kMergeThreads), s,
+                          nullptr, nullptr, se);
         launch_kernel(topk_merge_kernel, dim3((unsigned)batch), dim3(kMergeThreads), s, nullptr, tk.stop, se);
     } else {
         launch_kernel(topk_select_kernel, dim3((unsigned)batch), dim3(kSliceThreads), s, tk.start, tk.stop, se);
@@ -471,8 +540,11 @@ hipError_t launch_indexer_topk(const cskv_cache &c, const uint16_t *q_idx, int h
 
     launch_indexer_scan(c, q_idx, heads, head_w, keys, s, bkeys, pw.bkey_stride, pool ? pool->block : 1);
 
-    const SelectArgs se{keys, cand, c.n_tokens, out_idx, c.capacity, k, topk_slices(c), score_key_stride(c),
-                        cand_stride(c, k), 1, c.ratio};
+    SelectArgs se{keys, cand, c.n_tokens, out_idx, c.capacity, k, topk_slices(c), score_key_stride(c),
+                  cand_stride(c, k), 1, c.ratio};
+    se.groups = topk_groups(c, k);
+    se.cand2 = reinterpret_cast<uint2 *>(static_cast<char *>(ws) + lay.cand2_off);
+    se.cand2_stride = cand2_stride(c, k);
     launch_select(se, c.batch, s, timer_take(CSKV_KERNEL_TOPK_SELECT));
     if (pool) {
         // the pool: the best pool->blocks blocks by their largest key

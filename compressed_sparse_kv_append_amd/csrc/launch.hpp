@@ -15,7 +15,7 @@ namespace cskv {
 // uint32 score key per entry, and the per-slice candidate lists of sequences
 // longer than one select round.
 struct TopkWorkspace {
-    size_t keys_off, cand_off, total;
+    size_t keys_off, cand_off, cand2_off, total;
 };
 constexpr int kSliceKeys = 4096;  // keys per select slice (one block)
 // Score keys: one uint32 per cache row; a sequence's rows padded to 64.

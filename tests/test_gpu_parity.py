@@ -231,6 +231,20 @@ def test_indexer_topk_long_sequences_merge_slices(ck, orc):
     assert np.array_equal(got[0], np.arange(512)) and np.array_equal(got[1], np.arange(512))
 
 
+@pytest.mark.parametrize("distinct", [False, True])
+def test_indexer_topk_two_level_merge(ck, orc, distinct):
+    """Caches of 25 or more slices merge the slices' lists in groups of 8
+    first: a sequence spanning 27 slices (a last group of 3), 22 (a last
+    group of 6), 10 (groups of 8 and 2), 2 (one group: its list is the
+    answer), and short ones, with many tied scores or few."""
+    lens = [110000, 5000, 90000, 40000, 0, 300]
+    if distinct:
+        key_fn = None
+    else:
+        key_fn = lambda g, n: synth.int_bf16(g, (n, 64), -1, 1)
+    _indexer_case(ck, orc, lens, 64, 4, 512, seed=77 + distinct, key_fn=key_fn, cap=110003)
+
+
 def test_indexer_topk_merge_candidate_counts(ck, orc):
     """Slices hold 4096 entries; the merge reads k candidates per full slice
     and min(k, entries) of the last one.  Lengths put the last slice at 1,
