@@ -218,3 +218,87 @@ def test_full_mixed_ragged_b256(ck, orc):
         orc.kv_append(mirrors[b], t_h, np.array([0, len(t_h)], np.int32), W_h, i_h)
     torch.cuda.synchronize()
     _step(ck, orc, w, gc, mirrors, synth.step_inputs(w, 0), W_h)
+
+
+def test_full_model_plan_64k_b32(ck, orc):
+    """The pages' whole layer plan at the size bench.py times for it: 32
+    sequences x 64K tokens, three encoder caches of 32,768 entries (2->1,
+    Full + 5 Reuse each) and the decoder cache of 65,536 one-per-token
+    entries fed by the CED projection (Full + 3 Reuse, then four Reindex +
+    3 Reuse), one cskv_model_decode step.  Sequence 5 is drawn on the host
+    in every cache and checked against the oracle (cache rows, windows,
+    indices, outputs); the others are GPU filler checked by invariants."""
+    B, T, kg, Di, Hi, Hq, K, W, dm = 32, 65536, 64, 128, 64, 64, 512, 128, 512
+    sb = 5
+    plan = orc.csa2_plan()
+    g = np.random.default_rng(640)
+    scale = 1 / math.sqrt(576)
+    Wc = (g.standard_normal((576, 1152)) * 0.02).astype(np.float32)
+    dev_groups, host_groups = [], []
+    for gi, (name, ratio, modes) in enumerate(plan):
+        E = T // ratio
+        gc = ck.Cache.allocate(B, E + 8, kg, 0, Di, ratio=ratio)
+        hc = orc.Cache.empty(1, E + 8, 576, 64, kg, 0, Di, ratio=ratio)
+        for b in range(B):
+            cu = np.zeros(B + 1, np.int32)
+            cu[b + 1:] = E
+            if b == sb:
+                rows_h, keys_h = synth.student_t3(g, (E, 576)), synth.int_bf16(g, (E, Di))
+                orc.kv_append(hc, rows_h, np.array([0, E], np.int32), None, keys_h)
+                rows, keys = dev(rows_h), dev(keys_h)
+            else:
+                fw = synth.scaled(synth.WORKLOADS["decode_64k_b32"], seed=50 + gi)
+                rows, keys = _filler_rows(fw, b, E), _filler_keys(fw, b, E)
+            ck.kv_append_fp4(gc, rows, dev(cu), None, keys)
+        L = len(modes)
+        q = [synth.normal(g, (B, Hq, 576)) for _ in range(L)]
+        qi = [None if m == "reuse" else synth.int_bf16(g, (B, Hi, Di)) for m in modes]
+        rings = [synth.normal_bf16_trunc(g, (B, W, 576)) for _ in range(L)]
+        srows = [synth.normal(g, (B, 576)) for _ in range(L)]
+        irow = synth.int_bf16(g, (B, Di))
+        layers = [ck.Layer(mode=m, q=dev(q[i]), swa=dev(rings[i]), swa_row=dev(srows[i]),
+                           q_idx=None if qi[i] is None else dev(qi[i]),
+                           out=torch.empty(B, Hq, 512, device="cuda"), lse=torch.empty(B, Hq, device="cuda"),
+                           idx=torch.empty(B, K, dtype=torch.int32, device="cuda") if m != "reuse" else None)
+                  for i, m in enumerate(modes)]
+        dgrp = ck.Group(cache=gc, layers=layers, new_idx_rows=dev(irow))
+        sl = slice(sb, sb + 1)
+        hg = dict(cache=hc, modes=modes, q=[x[sl] for x in q], q_idx=[None if x is None else x[sl] for x in qi],
+                  rings=[r[sl].copy() for r in rings], swa_rows=[r[sl] for r in srows], idx_row=irow[sl])
+        if ratio == 1:
+            h = synth.int_bf16(g, (B, dm))
+            wc = synth.int_bf16(g, (576, dm))
+            dgrp.ced_h, dgrp.ced_w = dev(h), dev(wc)
+            hg.update(ced_h=h[sl], ced_w=wc)
+        else:
+            tok = synth.normal(g, (B, 576))
+            dgrp.new_tokens, dgrp.w_comp = dev(tok), dev(Wc)
+            hg.update(token=tok[sl], w_comp=Wc)
+        dev_groups.append(dgrp)
+        host_groups.append(hg)
+    ck.model_decode(dev_groups, K, W, scale)
+    res = orc.model_decode(host_groups, K, scale)
+    torch.cuda.synchronize()
+    for gi, (dg, hg, (outs, lses, idxs)) in enumerate(zip(dev_groups, host_groups, res)):
+        gc, hc = dg.cache, hg["cache"]
+        assert int(host(gc.status)[0]) == 0
+        nt = host(gc.n_tokens)
+        assert int(nt[sb]) == int(hc.n_tokens[0])
+        e = int(hc.entries()[0])
+        for name in ("k_codes", "k_scales", "idx_keys"):
+            assert np.array_equal(host(getattr(gc, name)[sb, :e]).view(np.uint8),
+                                  getattr(hc, name)[0, :e].view(np.uint8)), f"group {gi}: {name} differs"
+        E = np.clip(nt.astype(np.int64) // gc.ratio, 0, gc.capacity)
+        for li, L in enumerate(dg.layers):
+            assert np.isfinite(host(L.out)).all() and np.isfinite(host(L.lse)).all(), f"group {gi} layer {li}"
+            assert np.array_equal(host(L.swa[sb:sb + 1]).view(np.uint16), hg["rings"][li]), \
+                f"group {gi} layer {li}: window"
+            if L.idx is not None:
+                ix = host(L.idx)
+                for b in range(B):
+                    m = min(int(E[b]), K)
+                    assert np.all(ix[b, m:] == -1) and np.all(np.diff(ix[b, :m]) > 0) and ix[b, m - 1] < E[b]
+                assert np.array_equal(ix[sb:sb + 1], idxs[li]), f"group {gi} layer {li}: indices differ"
+            err = attn_rel_err(host(L.out[sb:sb + 1]), outs[li])
+            assert err.max() <= TOL, f"group {gi} layer {li}: max rel err {err.max():.3e}"
+            assert np.abs(host(L.lse[sb:sb + 1]) - lses[li]).max() < 1e-4, f"group {gi} layer {li}: lse"
