@@ -768,23 +768,26 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a)
     }
 }
 
-// Merge of the S partial softmaxes of one (sequence, head group): block of
-// 256 threads, thread t -> head t / 16, dims (t % 16) * 32 .. + 31.  The
-// partial outputs of two splits are loaded together with their (m, l), so
-// the common two-split case costs one round trip to memory.
+// Merge of the S partial softmaxes of 4 heads of one (sequence, head group):
+// block of 256 threads, thread t -> head t / 64 of the four, dims
+// (t % 64) * 8 .. + 7, so a wave reads one head's 2 KB row contiguously.
+// The partial outputs of two splits are loaded together with their (m, l),
+// so the common two-split case costs one round trip to memory.
+constexpr int kMergeHeads = 4;
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a)
 {
     const int HG = a.heads / kHG;
-    const int bh = blockIdx.x, b = bh / HG, hg = bh % HG;
-    const int t = threadIdx.x, h = t >> 4, d0 = (t & 15) * 32;
+    constexpr int kQuarters = kHG / kMergeHeads;
+    const int bh = blockIdx.x / kQuarters, b = bh / HG, hg = bh % HG;
+    const int t = threadIdx.x, h = (blockIdx.x % kQuarters) * kMergeHeads + t / 64, d0 = (t % 64) * 8;
     const size_t p0 = ((size_t)b * HG + hg) * a.splits;
     float M = -INFINITY, L = 0.f;
-    float acc[32];
+    float acc[8];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) acc[i] = 0.f;
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     // splits two at a time, with a running maximum (one pass when S = 2)
     for (int s0 = 0; s0 < a.splits; s0 += 2) {
-        float4 x[2][8];
+        float4 x[2][2];
         float ms[2], ls[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -792,8 +795,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a)
             ms[j] = a.part_ml[(p0 + s) * 2 * kHG + h];
             ls[j] = a.part_ml[(p0 + s) * 2 * kHG + kHG + h];
             const float4 *src = reinterpret_cast<const float4 *>(a.part_o + ((p0 + s) * kHG + h) * kDv + d0);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[j][i] = src[i];
+            x[j][0] = src[0];
+            x[j][1] = src[1];
         }
         if (s0 + 1 >= a.splits) ms[1] = -INFINITY;
         const float Mn = fmaxf(M, fmaxf(ms[0], ms[1]));
@@ -801,7 +804,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a)
         const float r = exp2f(M - Mn);                 // 0 while M is -inf
         L *= r;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) acc[i] *= r;
+        for (int i = 0; i < 8; ++i) acc[i] *= r;
         M = Mn;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -809,7 +812,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a)
             const float f = exp2f(ms[j] - M);
             L += f * ls[j];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 2; ++i) {
                 acc[4 * i] = fmaf(f, x[j][i].x, acc[4 * i]);
                 acc[4 * i + 1] = fmaf(f, x[j][i].y, acc[4 * i + 1]);
                 acc[4 * i + 2] = fmaf(f, x[j][i].z, acc[4 * i + 2]);
@@ -821,9 +824,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a)
     const size_t head = (size_t)b * a.heads + kHG * hg + h;
     float4 *dst = reinterpret_cast<float4 *>(a.out + head * kDv + d0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 2; ++i)
         dst[i] = make_float4(acc[4 * i] * inv, acc[4 * i + 1] * inv, acc[4 * i + 2] * inv, acc[4 * i + 3] * inv);
-    if (a.lse && (t & 15) == 0)
+    if (a.lse && (t & 63) == 0)
         a.lse[head] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
@@ -912,7 +915,8 @@ hipError_t launch_sparse_attn(const cskv_cache &c, const float *q, int heads, co
     if (c.swa_format == CSKV_SWA_FP8) pick(std::true_type{});
     else pick(std::false_type{});
     if (p.splits > 1)
-        launch_kernel(attn_merge_kernel, dim3((unsigned)(c.batch * hg)), dim3(256), s, nullptr, tl.stop, a);
+        launch_kernel(attn_merge_kernel, dim3((unsigned)(c.batch * hg * (kHG / kMergeHeads))), dim3(256), s,
+                      nullptr, tl.stop, a);
     return hipGetLastError();
 }
 
