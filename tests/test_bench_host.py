@@ -36,3 +36,18 @@ def test_cpu_baseline_runs_every_format(fmt):
     r = bench.cpu_baseline(synth, w, 0, 0.01, None, idx_format, swa_format, k_format)
     assert r["kind"] == "oracle" and r["unit"] == "steps/s" and np.isfinite(r["value"]) and r["value"] > 0
     assert r["cores"] >= 1
+
+
+def test_cpu_baseline_prefill_workload():
+    """The tiny workload's cache is built from prefill tokens through the
+    compressor on the oracle side too (an odd count leaves one pending)."""
+    w = synth.scaled(synth.WORKLOADS["tiny_t4096"], prefill_tokens=301, entries=151)
+    r = bench.cpu_baseline(synth, w, 0, 0.01)
+    assert r["kind"] == "oracle" and np.isfinite(r["value"]) and r["value"] > 0
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+    import sys
+    p = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True, timeout=60)
+    assert p.returncode == 2 and "one GPU" in p.stderr
