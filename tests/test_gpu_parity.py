@@ -93,8 +93,9 @@ def test_append_compressor_pairs_pending_bitexact(ck, orc):
         assert_cache_equal(gc, hc)
 
 
-@pytest.mark.parametrize("k_group,v_group,idx_dim", [(32, 128, 128), (64, 0, 64)])
-def test_append_compressor_large_calls_bitexact(ck, orc, k_group, v_group, idx_dim):
+@pytest.mark.parametrize("k_group,v_group,idx_dim,fmt", [(32, 128, 128, "f32"), (64, 0, 64, "f32"),
+                                                        (16, 16, 128, "mx16"), (32, 0, 128, "idx_fp4")])
+def test_append_compressor_large_calls_bitexact(ck, orc, k_group, v_group, idx_dim, fmt):
     """Appends of 512 rows or more take the planned, tiled compressor: more
     than 1024 sequences (the plan covers them in rounds), empty sequences,
     sequences that start on a pending token, long runs of both parities, and
@@ -103,7 +104,10 @@ def test_append_compressor_large_calls_bitexact(ck, orc, k_group, v_group, idx_d
     W = synth.w_comp(synth.WORKLOADS["tiny_t4096"])
     Wd = dev(W)
     B, cap = 1100, 400
-    gc, hc = pair(B, cap, k_group, v_group, idx_dim)
+    # the pages' 16-channel E8M0 entries and FP4 indexer keys take the
+    # planned path's block quantiser, fp32 scales with bf16 keys its wave one
+    gc, hc = pair(B, cap, k_group, v_group, idx_dim, idx_format=1 if fmt == "idx_fp4" else 0,
+                  k_format=1 if fmt == "mx16" else 0)
     g = np.random.default_rng(31 + k_group)
     for call in range(3):
         lens = g.integers(0, 3, size=B)
