@@ -226,6 +226,40 @@ def cpu_baseline(synth, w, nseq: int, seconds: float, pool=None, idx_format=0, s
                       + f"; cache build untimed; OpenMP over sequences on {cpu}"}
 
 
+def cpu_baseline_one_thread(workload: str, seconds: float):
+    """The oracle on one host thread: a child process with OMP_NUM_THREADS=1
+    runs cpu_baseline on one sequence of the workload (scaled to the batch)."""
+    import subprocess
+    code = ("import json, sys; sys.path.insert(0, %r); import bench, synth; w = synth.WORKLOADS[%r]\n"
+            "if w.entries is None and w.prefill_tokens: w = synth.scaled(w, entries=(w.prefill_tokens + 1) // 2)\n"
+            "print(json.dumps(bench.cpu_baseline(synth, w, 1, %r)))") % (ROOT, workload, seconds)
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    try:
+        p = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=600)
+        r = json.loads(p.stdout.strip().splitlines()[-1])
+        r["cores"] = 1
+        return r
+    except Exception as e:                      # reported, never fatal
+        return {"error": str(e)[:200]}
+
+
+def gpu_clocks(torch):
+    """Current shader and memory clock levels of GPU 0 from its sysfs entry
+    (best effort: None where they cannot be read)."""
+    try:
+        pr = torch.cuda.get_device_properties(0)
+        dev = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (getattr(pr, "pci_domain_id", 0), pr.pci_bus_id,
+                                                        pr.pci_device_id)
+        out = {}
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            with open(os.path.join(dev, name)) as f:
+                cur = [ln.split(":", 1)[1].strip().rstrip("*").strip() for ln in f if ln.strip().endswith("*")]
+            out[name[7:]] = cur[0] if cur else None
+        return out
+    except Exception:
+        return None
+
+
 def pmc_traffic():
     """HBM bytes per scan launch from the committed counter summary, if it was
     taken on the current scan source."""
@@ -455,10 +489,14 @@ def main():
     if prefill:
         result["config"]["prefill_tokens"] = w.prefill_tokens
         result["config"]["context_tokens"] = w.prefill_tokens + 1
+    result["gpu_clocks"] = gpu_clocks(torch)
     if not a.no_cpu_baseline:
         log("timing the oracle on a CPU sample ...")
         result["cpu_baseline"] = cpu_baseline(synth, w, a.cpu_baseline_seqs, a.cpu_baseline_seconds, pool,
                                               int(idx_fp4), int(swa_fp8), int(mx16))
+        if w.name in ("tiny_t4096", "decode_64k_b32") and not (idx_fp4 or swa_fp8 or mx16 or pool):
+            log("timing the oracle on one host thread ...")
+            result["cpu_baseline_1thread"] = cpu_baseline_one_thread(w.name, 3.0)
     print(json.dumps(result), flush=True)
 
 
