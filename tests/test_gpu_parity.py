@@ -238,15 +238,15 @@ def test_indexer_topk_long_sequences_merge_slices(ck, orc):
 @pytest.mark.parametrize("distinct", [False, True])
 def test_indexer_topk_two_level_merge(ck, orc, distinct):
     """Caches of 25 or more slices merge the slices' lists in groups of 8
-    first: a sequence spanning 27 slices (a last group of 3), 22 (a last
-    group of 6), 10 (groups of 8 and 2), 2 (one group: its list is the
-    answer), and short ones, with many tied scores or few."""
-    lens = [110000, 5000, 90000, 40000, 0, 300]
+    first: with 4096-key slices, a sequence spanning 52 slices (a last group
+    of 4), 44 (a last group of 4), 20 (groups of 8, 8 and 4), 3 (one group:
+    its list is the answer), and short ones, with many tied scores or few."""
+    lens = [210000, 9000, 180000, 80000, 0, 300]
     if distinct:
         key_fn = None
     else:
         key_fn = lambda g, n: synth.int_bf16(g, (n, 64), -1, 1)
-    _indexer_case(ck, orc, lens, 64, 4, 512, seed=77 + distinct, key_fn=key_fn, cap=110003)
+    _indexer_case(ck, orc, lens, 64, 4, 512, seed=77 + distinct, key_fn=key_fn, cap=210003)
 
 
 def test_indexer_topk_merge_candidate_counts(ck, orc):
