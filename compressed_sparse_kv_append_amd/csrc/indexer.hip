@@ -21,7 +21,21 @@ namespace cskv {
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int topk_slices(const cskv_cache &c) { return (int)((c.capacity + kSliceKeys - 1) / kSliceKeys); }
+// Keys per slice: caches of few sequences (whose slices alone leave most of
+// the chip idle) longer than one 4096-key slice take slices of 8192 keys on
+// 1024-thread blocks, which halves the lists to merge; others slices of 4096
+// keys on 512 threads.  (One 1M-token sequence: 85 -> 73 us per decode step;
+// at 32 sequences the larger slices were slower.)
+constexpr int kFewSeqs = 4;
+static int slice_keys_of(const cskv_cache &c)
+{
+    return c.batch <= kFewSeqs && c.capacity > kSliceKeys ? 2 * kSliceKeys : kSliceKeys;
+}
+int topk_slices(const cskv_cache &c)
+{
+    const int sk = slice_keys_of(c);
+    return (int)((c.capacity + sk - 1) / sk);
+}
 
 // Candidate pairs per sequence, rounded to even so each list is 16-byte aligned.
 static size_t cand_stride(const cskv_cache &c, int k) { return ((size_t)topk_slices(c) * k + 1) & ~(size_t)1; }
@@ -35,7 +49,7 @@ constexpr int kGroupMinSlices = 25;
 static int topk_groups(const cskv_cache &c, int k)
 {
     const int s = topk_slices(c);
-    return s >= kGroupMinSlices && k < kSliceKeys ? (s + kGroupSlices - 1) / kGroupSlices : 0;
+    return s >= kGroupMinSlices && k < slice_keys_of(c) ? (s + kGroupSlices - 1) / kGroupSlices : 0;
 }
 static size_t cand2_stride(const cskv_cache &c, int k) { return ((size_t)topk_groups(c, k) * k + 1) & ~(size_t)1; }
 
@@ -72,10 +86,8 @@ namespace {
 
 constexpr int kBins = 2048;
 constexpr int kDigit = 11;
-constexpr int kSliceThreads = 512;                      // slice blocks: 8 waves
-constexpr int kSlicePer = kSliceKeys / kSliceThreads;   // keys per thread in a slice (16)
+constexpr int kSliceThreads = 512;                      // slice blocks of kSliceKeys keys: 8 waves
 constexpr int kMergeThreads = 512;                      // merge blocks: 8 waves
-constexpr int kMergeContigPer = kSliceKeys / kMergeThreads;  // a sequence of one slice (8)
 constexpr int kMergePerSmall = 10;                      // up to 5120 candidates in one round
 constexpr int kMergePer = 36;                           // more: 18432 per round
 
@@ -101,6 +113,7 @@ struct SelectArgs {
     size_t key_stride, cand_stride;
     int group;              // entries per item: a sequence of E entries has ceil(E / group) items
     int ratio;              // tokens per entry of the cache
+    int slice_keys = kSliceKeys;  // keys per slice (the kernels' KEYS)
     // two-level merge (groups > 0): the group lists [B][cand2_stride],
     // groups x k (key, index) pairs per sequence
     uint2 *cand2 = nullptr;
@@ -372,49 +385,52 @@ __device__ __forceinline__ void select_topk(SelectSmem<THREADS> &sm, const Items
 }
 
 // Sequence b longer than one slice, slice s: the local top-k of keys
-// [s*kSliceKeys, (s+1)*kSliceKeys) as index-ordered (key, index) pairs; a
+// [s*KEYS, (s+1)*KEYS) as index-ordered (key, index) pairs; a
 // slice with at most k entries passes them all and pads its list with key 0.
 // The slices' lists contain the sequence's top-k (an entry beaten by fewer
 // than k entries overall is beaten by fewer than k in its slice).
-__global__ __launch_bounds__(kSliceThreads) void topk_slice_kernel(SelectArgs a)
+template <int KEYS, int THREADS>
+__global__ __launch_bounds__(THREADS) void topk_slice_kernel(SelectArgs a)
 {
-    __shared__ SelectSmem<kSliceThreads> sm;
+    __shared__ SelectSmem<THREADS> sm;
     const int b = blockIdx.y, s = blockIdx.x;
     const int64_t E = items_of(a, b);
-    if (E <= a.k || E <= kSliceKeys) return;         // the merge reads the keys directly
+    if (E <= a.k || E <= KEYS) return;         // the merge reads the keys directly
     uint2 *out = a.cand + (size_t)b * a.cand_stride + (size_t)s * a.k;
-    const int64_t first = (int64_t)s * kSliceKeys;
+    const int64_t first = (int64_t)s * KEYS;
     if (first >= E) return;
-    const int64_t n = E - first < kSliceKeys ? E - first : kSliceKeys;
+    const int64_t n = E - first < KEYS ? E - first : KEYS;
     if (n <= a.k) {
-        for (int i = threadIdx.x; i < a.k; i += kSliceThreads)
+        for (int i = threadIdx.x; i < a.k; i += THREADS)
             out[i] = i < n ? make_uint2(a.keys[(size_t)b * a.key_stride + first + i], (uint32_t)(first + i))
                            : make_uint2(0u, 0xFFFFFFFFu);
         return;
     }
     Items it{a.keys + (size_t)b * a.key_stride + first, nullptr, n, first};
-    select_topk<false, true, kSliceThreads, kSlicePer>(sm, it, a.k, nullptr, out);
+    select_topk<false, true, THREADS, KEYS / THREADS>(sm, it, a.k, nullptr, out);
 }
 
 // Sequence b of a cache that fits one slice: the final top-k from the key
 // array.
-__global__ __launch_bounds__(kSliceThreads) void topk_select_kernel(SelectArgs a)
+template <int KEYS, int THREADS>
+__global__ __launch_bounds__(THREADS) void topk_select_kernel(SelectArgs a)
 {
-    __shared__ SelectSmem<kSliceThreads> sm;
+    __shared__ SelectSmem<THREADS> sm;
     const int b = blockIdx.x;
     const int64_t E = items_of(a, b);
     int32_t *out = a.out + (size_t)b * a.k;
     if (E <= a.k) {
-        for (int i = threadIdx.x; i < a.k; i += kSliceThreads) out[i] = i < E ? i : -1;
+        for (int i = threadIdx.x; i < a.k; i += THREADS) out[i] = i < E ? i : -1;
         return;
     }
     Items it{a.keys + (size_t)b * a.key_stride, nullptr, E, 0};
-    select_topk<false, false, kSliceThreads, kSlicePer>(sm, it, a.k, out, nullptr);
+    select_topk<false, false, THREADS, KEYS / THREADS>(sm, it, a.k, out, nullptr);
 }
 
 // Sequence b of a cache whose capacity spans several slices: the final top-k
 // over the slices' candidate lists (index-ordered, so their concatenation is
 // too), or straight from the key array when the sequence fits one slice.
+template <int KEYS>
 __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(SelectArgs a)
 {
     __shared__ SelectSmem<kMergeThreads> sm;
@@ -425,15 +441,15 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(SelectArgs a)
         for (int i = threadIdx.x; i < a.k; i += kMergeThreads) out[i] = i < E ? i : -1;
         return;
     }
-    if (E <= kSliceKeys) {
+    if (E <= KEYS) {
         Items it{a.keys + (size_t)b * a.key_stride, nullptr, E, 0};
-        select_topk<false, false, kMergeThreads, kMergeContigPer>(sm, it, a.k, out, nullptr);
+        select_topk<false, false, kMergeThreads, KEYS / kMergeThreads>(sm, it, a.k, out, nullptr);
         return;
     }
     // every list is full but the last slice's, whose first min(k, its
     // entries) slots are valid: the padding after them is not read
-    const int64_t used = (E + kSliceKeys - 1) / kSliceKeys;
-    const int64_t last = E - (used - 1) * kSliceKeys;
+    const int64_t used = (E + KEYS - 1) / KEYS;
+    const int64_t last = E - (used - 1) * KEYS;
     if (a.groups > 0) {
         // the group lists: a group of two or more slices holds exactly k
         // valid pairs (its first slice is full, k < 4096), a one-slice
@@ -462,13 +478,14 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(SelectArgs a)
 // [8 g, 8 g + 8) of those holding entries, to its top-k (key, index) pairs
 // in index order.  The union of the groups' top-k lists holds the
 // sequence's top-k, as the slices' lists do.
+template <int KEYS>
 __global__ __launch_bounds__(kMergeThreads) void topk_group_kernel(SelectArgs a)
 {
     __shared__ SelectSmem<kMergeThreads> sm;
     const int b = blockIdx.y, g = blockIdx.x;
     const int64_t E = items_of(a, b);
-    if (E <= a.k || E <= kSliceKeys) return;         // the merge reads the keys directly
-    const int64_t used = (E + kSliceKeys - 1) / kSliceKeys;
+    if (E <= a.k || E <= KEYS) return;         // the merge reads the keys directly
+    const int64_t used = (E + KEYS - 1) / KEYS;
     const int64_t s0 = (int64_t)g * kGroupSlices;
     if (s0 >= used) return;                          // the merge reads only the groups in use
     const int64_t s1 = s0 + kGroupSlices < used ? s0 + kGroupSlices : used;
@@ -479,7 +496,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_group_kernel(SelectArgs a)
         return;
     }
     // the group's first slice is full (4096 > k entries): more than k valid
-    const int64_t last = s1 == used ? E - (used - 1) * kSliceKeys : kSliceKeys;
+    const int64_t last = s1 == used ? E - (used - 1) * KEYS : KEYS;
     Items it{nullptr, in, (s1 - s0 - 1) * a.k + (last < a.k ? last : a.k), 0};
     if (it.n <= kMergeThreads * kMergePerSmall)
         select_topk<true, true, kMergeThreads, kMergePerSmall>(sm, it, a.k, nullptr, out);
@@ -508,18 +525,28 @@ __global__ __launch_bounds__(kMergeThreads) void topk_pool_select_kernel(SelectA
 }
 
 // Select (slices + merge, or one select) of the k best items per sequence.
-void launch_select(const SelectArgs &se, int batch, hipStream_t s, const TimedLaunch &tk)
+template <int KEYS, int THREADS>
+void launch_select_t(const SelectArgs &se, int batch, hipStream_t s, const TimedLaunch &tk)
 {
     if (se.slices > 1) {
-        launch_kernel(topk_slice_kernel, dim3((unsigned)se.slices, (unsigned)batch), dim3(kSliceThreads), s,
-                      tk.start, nullptr, se);
+        launch_kernel(topk_slice_kernel<KEYS, THREADS>, dim3((unsigned)se.slices, (unsigned)batch), dim3(THREADS),
+                      s, tk.start, nullptr, se);
         if (se.groups > 0)
-            launch_kernel(topk_group_kernel, dim3((unsigned)se.groups, (unsigned)batch), dim3(kMergeThreads), s,
-                          nullptr, nullptr, se);
-        launch_kernel(topk_merge_kernel, dim3((unsigned)batch), dim3(kMergeThreads), s, nullptr, tk.stop, se);
+            launch_kernel(topk_group_kernel<KEYS>, dim3((unsigned)se.groups, (unsigned)batch), dim3(kMergeThreads),
+                          s, nullptr, nullptr, se);
+        launch_kernel(topk_merge_kernel<KEYS>, dim3((unsigned)batch), dim3(kMergeThreads), s, nullptr, tk.stop, se);
     } else {
-        launch_kernel(topk_select_kernel, dim3((unsigned)batch), dim3(kSliceThreads), s, tk.start, tk.stop, se);
+        launch_kernel(topk_select_kernel<KEYS, THREADS>, dim3((unsigned)batch), dim3(THREADS), s, tk.start,
+                      tk.stop, se);
     }
+}
+
+void launch_select(const SelectArgs &se, int batch, hipStream_t s, const TimedLaunch &tk)
+{
+    if (se.slice_keys == 2 * kSliceKeys)
+        launch_select_t<2 * kSliceKeys, 2 * kSliceThreads>(se, batch, s, tk);
+    else
+        launch_select_t<kSliceKeys, kSliceThreads>(se, batch, s, tk);
 }
 
 }  // namespace
@@ -542,6 +569,7 @@ hipError_t launch_indexer_topk(const cskv_cache &c, const uint16_t *q_idx, int h
 
     SelectArgs se{keys, cand, c.n_tokens, out_idx, c.capacity, k, topk_slices(c), score_key_stride(c),
                   cand_stride(c, k), 1, c.ratio};
+    se.slice_keys = slice_keys_of(c);
     se.groups = topk_groups(c, k);
     se.cand2 = reinterpret_cast<uint2 *>(static_cast<char *>(ws) + lay.cand2_off);
     se.cand2_stride = cand2_stride(c, k);
