@@ -825,8 +825,8 @@ hipError_t launch_kv_append(const cskv_cache &c, const float *tokens, const int3
         hipEvent_t comp_start = tl.start;
         if (tc.start) comp_start = tc.start;
         else tl.start = nullptr;
-        // about 1024 waves: groups of 8 input rows x runs of output channels
-        constexpr int kE = 8;
+        // about 1024 waves: groups of 4 input rows x runs of output channels
+        constexpr int kE = 4;
         const int groups = (total_new + kE - 1) / kE;
         const int runs = groups >= 1024 ? 1 : (1024 / groups < kDim ? 1024 / groups : kDim);
         const int cpw = (kDim + runs - 1) / runs;
