@@ -541,10 +541,17 @@ void launch_select_t(const SelectArgs &se, int batch, hipStream_t s, const Timed
     }
 }
 
+// Batches of kManySeqs sequences or more fill the chip with slices several
+// times over; their slices take 4-wave blocks (16 keys per thread), which
+// measured faster there (ragged 256-sequence batch: 27 -> 23 us) and slower
+// at 32 sequences (19.1 -> 19.8 us).
+constexpr int kManySeqs = 128;
 void launch_select(const SelectArgs &se, int batch, hipStream_t s, const TimedLaunch &tk)
 {
     if (se.slice_keys == 2 * kSliceKeys)
         launch_select_t<2 * kSliceKeys, 2 * kSliceThreads>(se, batch, s, tk);
+    else if (batch >= kManySeqs)
+        launch_select_t<kSliceKeys, kSliceThreads / 2>(se, batch, s, tk);
     else
         launch_select_t<kSliceKeys, kSliceThreads>(se, batch, s, tk);
 }

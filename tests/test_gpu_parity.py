@@ -249,6 +249,16 @@ def test_indexer_topk_two_level_merge(ck, orc, distinct):
     _indexer_case(ck, orc, lens, 64, 4, 512, seed=77 + distinct, key_fn=key_fn, cap=210003)
 
 
+def test_indexer_topk_many_sequences(ck, orc):
+    """Batches of 128 sequences or more select their slices with 4-wave
+    blocks: ragged lengths from empty to several slices, with ties."""
+    g = np.random.default_rng(91)
+    lens = [int(x) for x in g.integers(0, 14000, size=130)]
+    lens[:4] = [0, 1, 512, 4096 + 1]
+    key_fn = lambda g, n: synth.int_bf16(g, (n, 64), -2, 2)
+    _indexer_case(ck, orc, lens, 64, 4, 512, seed=92, key_fn=key_fn)
+
+
 def test_indexer_topk_merge_candidate_counts(ck, orc):
     """Slices hold 4096 entries; the merge reads k candidates per full slice
     and min(k, entries) of the last one.  Lengths put the last slice at 1,
