@@ -149,6 +149,29 @@ def test_append_compressor_paths_agree(ck, orc, rows):
     assert_cache_equal(gc, hc)
 
 
+def test_append_compressor_max_batch(ck, orc):
+    """The largest batch (65,535 sequences), two rows each through the
+    compressor in one call: the plan covers the sequences in 64 rounds and
+    the tiled kernel 1,024 row tiles.  Every sequence ends with one entry;
+    whole planes are compared with the oracle bit for bit."""
+    B = 65535
+    W = synth.w_comp(synth.WORKLOADS["tiny_t4096"])
+    gc, hc = pair(B, 2, 32, 0, 64)
+    g = np.random.default_rng(55)
+    toks = synth.normal(g, (2 * B, 576))
+    irows = synth.int_bf16(g, (2 * B, 64))
+    cu = (2 * np.arange(B + 1)).astype(np.int32)
+    ck.kv_append_fp4(gc, dev(toks), dev(cu), dev(W), dev(irows))
+    orc.kv_append(hc, toks, cu, W, irows)
+    torch.cuda.synchronize()
+    assert int(host(gc.status)[0]) == 0 == int(hc.status[0])
+    assert np.array_equal(host(gc.n_tokens), hc.n_tokens)
+    for name in ("k_codes", "k_scales", "idx_keys"):
+        got = host(getattr(gc, name)[:, :1]).view(np.uint8)
+        want = getattr(hc, name)[:, :1].view(np.uint8)
+        assert np.array_equal(got, want), f"{name} differs"
+
+
 def test_append_one_row_per_sequence_and_overflow(ck, orc):
     w = synth.WORKLOADS["tiny_t4096"]
     W = synth.w_comp(w)
