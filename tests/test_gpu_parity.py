@@ -259,17 +259,18 @@ def test_indexer_topk_long_sequences_merge_slices(ck, orc):
 
 
 @pytest.mark.parametrize("distinct", [False, True])
-def test_indexer_topk_two_level_merge(ck, orc, distinct):
+@pytest.mark.parametrize("lens", [[210000, 9000, 180000, 80000, 0, 300], [210000, 9000, 300]])
+def test_indexer_topk_two_level_merge(ck, orc, distinct, lens):
     """Caches of 25 or more slices merge the slices' lists in groups of 8
-    first: with 4096-key slices, a sequence spanning 52 slices (a last group
-    of 4), 44 (a last group of 4), 20 (groups of 8, 8 and 4), 3 (one group:
-    its list is the answer), and short ones, with many tied scores or few."""
-    lens = [210000, 9000, 180000, 80000, 0, 300]
+    first.  Six sequences (4096-key slices): 52 slices (a last group of 4),
+    44, 20 (groups of 8, 8 and 4), 3 (one group: its list is the answer) and
+    short ones.  Three sequences (8192-key slices on 1024-thread blocks): 26
+    slices (a last group of 2), 2 and a short one.  Many tied scores or few."""
     if distinct:
         key_fn = None
     else:
         key_fn = lambda g, n: synth.int_bf16(g, (n, 64), -1, 1)
-    _indexer_case(ck, orc, lens, 64, 4, 512, seed=77 + distinct, key_fn=key_fn, cap=210003)
+    _indexer_case(ck, orc, lens, 64, 4, 512, seed=77 + distinct + len(lens), key_fn=key_fn, cap=210003)
 
 
 def test_indexer_topk_many_sequences(ck, orc):
