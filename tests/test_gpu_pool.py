@@ -74,6 +74,17 @@ def test_pool_and_topk_in_pool_ragged(ck, orc):
     _pool_case(ck, orc, lens, 64, 4, 64, nb=96, block=8, seed=60)
 
 
+def test_pool_many_sequences(ck, orc):
+    """130 sequences: both the top-k and the pool's block select take the
+    4-wave slice blocks of large batches; ragged lengths up to several block
+    slices (> 4096 blocks of 8), with ties."""
+    g = np.random.default_rng(68)
+    lens = [int(x) for x in g.integers(0, 40000, size=130)]
+    lens[:5] = [0, 5, 700, 36000, 39000]
+    few = lambda g, n: synth.int_bf16(g, (n, 64), -2, 2)
+    _pool_case(ck, orc, lens, 64, 4, 64, nb=96, block=8, seed=69, key_fn=few)
+
+
 def test_pool_full_shape_blocks_of_8(ck, orc):
     # the pages' shape: 2048 blocks of 8 (16,384 positions), top-512, 64 x 128
     _pool_case(ck, orc, [70001, 20000, 16384, 16385], 128, 64, 512, nb=2048, block=8, seed=61)
