@@ -392,9 +392,19 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_fp4_kernel(ScanArgs
 }  // namespace
 
 // Blocks per sequence and positions per block for n positions per sequence:
-// one round of blocks that fills every CU, runs a multiple of 64 (and at
-// most `cap`).
-static int scan_chunk(int batch, size_t n, size_t cap)
+// one round of blocks, runs a multiple of 64 (and at most `cap`).  The bf16
+// keys of batches of fewer than 128 sequences size the round for 2 blocks
+// per CU (longer runs per wave; 64K x 32: 48.2 -> 47.2 us, 128K x 64: 191
+// -> 184 us); larger batches take 3 (a ragged 256-sequence batch: 116 us
+// with 3, 156 with 2, where fewer runs per sequence leave the long
+// sequences' blocks with most of the work), and so do FP4 keys, whose scan
+// is bound by its per-key arithmetic and wants every wave it can hold.
+constexpr int kScanManySeqs = 128;
+static int scan_blocks_per_cu(const cskv_cache &c)
+{
+    return c.batch >= kScanManySeqs || c.idx_format == CSKV_IDX_FP4 ? kScanBlocksPerCU : kScanBlocksPerCU - 1;
+}
+static int scan_chunk(int batch, size_t n, size_t cap, int per_cu)
 {
     static int cus = 0;
     if (cus == 0) {
@@ -402,7 +412,7 @@ static int scan_chunk(int batch, size_t n, size_t cap)
         if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
     }
-    const int slots = kScanBlocksPerCU * cus;
+    const int slots = per_cu * cus;
     const int per_seq = batch >= slots ? 1 : slots / batch;
     size_t chunk = (n + per_seq - 1) / per_seq;
     chunk = (chunk + 63) / 64 * 64;
@@ -445,7 +455,7 @@ static void scan_dispatch(const cskv_cache &c, int heads, const ScanArgs &sa, di
 void launch_indexer_scan(const cskv_cache &c, const uint16_t *q_idx, int heads, const float *head_w,
                          uint32_t *keys, hipStream_t s, uint32_t *block_keys, size_t block_stride, int block)
 {
-    const int chunk = scan_chunk(c.batch, (size_t)c.capacity, (size_t)1 << 30);
+    const int chunk = scan_chunk(c.batch, (size_t)c.capacity, (size_t)1 << 30, scan_blocks_per_cu(c));
     ScanArgs sa{c.idx_keys, c.n_tokens, q_idx, head_w, keys, c.capacity, heads, chunk, score_key_stride(c),
                 block_keys, block_stride, block, nullptr, 0, nullptr, c.idx_scales, c.ratio};
     dim3 grid((unsigned)(((size_t)c.capacity + chunk - 1) / chunk), (unsigned)c.batch);
@@ -456,7 +466,7 @@ void launch_pool_scan(const cskv_cache &c, const uint16_t *q_idx, int heads, con
                       const int32_t *pool, int pool_blocks, int block, uint2 *pairs, hipStream_t s)
 {
     const size_t n = (size_t)pool_blocks * block;
-    const int chunk = scan_chunk(c.batch, n, kPoolChunkMax);
+    const int chunk = scan_chunk(c.batch, n, kPoolChunkMax, scan_blocks_per_cu(c));
     ScanArgs sa{c.idx_keys, c.n_tokens, q_idx, head_w, nullptr, c.capacity, heads, chunk, 0,
                 nullptr, 0, block, pool, pool_blocks, pairs, c.idx_scales, c.ratio};
     dim3 grid((unsigned)((n + chunk - 1) / chunk), (unsigned)c.batch);
