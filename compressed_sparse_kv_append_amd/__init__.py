@@ -93,7 +93,7 @@ def lib():
         L.cskv_append_workspace_bytes.restype = sz
         L.cskv_swa_append.argtypes = [vp, i32, i32, i32, vp, vp, i32, vp, vp]
         L.cskv_swa_append_fp8.argtypes = [vp, i32, i32, i32, vp, vp, i32, vp, vp]
-        L.cskv_indexer_topk.argtypes = [vp, vp, i32, vp, i32, vp, vp, sz, vp]
+        L.cskv_indexer_topk.argtypes = [vp, vp, i32, vp, i32, vp, vp, vp, sz, vp]
         L.cskv_sparse_attn_decode.argtypes = [vp, vp, i32, vp, i32, vp, i32, vp, C.c_float, vp, vp, vp, sz,
                                               vp]
         L.cskv_layer_group_decode.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, C.c_float,
@@ -136,6 +136,18 @@ def _check(rc):
 def _stream(stream) -> C.c_void_p:
     s = torch.cuda.current_stream() if stream is None else stream
     return C.c_void_p(s.cuda_stream)
+
+
+def _keep_for(stream, *tensors) -> None:
+    """Tensors the binding allocated for a call enqueued on `stream`: tell the
+    caching allocator that stream uses them, so their memory is not handed
+    out again before that stream's work is done (a no-op on the current
+    stream)."""
+    if stream is None:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
 
 
 def _ptr(t: Optional[torch.Tensor], dtypes, name, shape=None):
@@ -254,8 +266,9 @@ def kv_append_fp4(cache: Cache, tokens: torch.Tensor, cu_new: Optional[torch.Ten
                   w_comp: Optional[torch.Tensor], idx_rows: torch.Tensor, ws: Optional[torch.Tensor] = None,
                   stream=None) -> None:
     n = tokens.shape[0]
+    tmp = None
     if ws is None and w_comp is not None:
-        ws = append_workspace(n, w_comp, tokens.device)
+        ws = tmp = append_workspace(n, w_comp, tokens.device)
     d = cache.desc()
     _check(lib().cskv_kv_append_fp4(
         C.byref(d), _ptr(tokens, F32, "tokens", (n, cache.dim)),
@@ -263,6 +276,7 @@ def kv_append_fp4(cache: Cache, tokens: torch.Tensor, cu_new: Optional[torch.Ten
         _ptr(w_comp, F32, "w_comp", (cache.dim, 2 * cache.dim)),
         _ptr(idx_rows, B16, "idx_rows", (n, cache.idx_dim)),
         _ptr(ws, U8, "ws"), 0 if ws is None else ws.numel(), _stream(stream)))
+    _keep_for(stream, tmp)
 
 
 def swa_append(ring: torch.Tensor, rows: torch.Tensor, cu_new: Optional[torch.Tensor],
@@ -280,17 +294,24 @@ def swa_append(ring: torch.Tensor, rows: torch.Tensor, cu_new: Optional[torch.Te
 
 def indexer_topk(cache: Cache, q_idx: torch.Tensor, k: int, head_w: Optional[torch.Tensor] = None,
                  out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                 stream=None) -> torch.Tensor:
+                 stream=None, scores: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Top-k indices [B, k]; with `scores` (f32 [B, capacity]) the score of
+    every live entry is written there too."""
     B, H, Di = q_idx.shape
+    tmp = []
     if out is None:
         out = torch.empty(B, k, dtype=torch.int32, device=q_idx.device)
+        tmp.append(out)
     if ws is None:
         ws = workspace(cache, k)
+        tmp.append(ws)
     d = cache.desc()
     _check(lib().cskv_indexer_topk(
         C.byref(d), _ptr(q_idx, B16, "q_idx", (cache.batch, H, cache.idx_dim)), H,
         _ptr(head_w, F32, "head_w", (cache.batch, H)), k, _ptr(out, I32, "out", (cache.batch, k)),
+        _ptr(scores, F32, "scores", (cache.batch, cache.capacity)),
         _ptr(ws, U8, "ws"), ws.numel(), _stream(stream)))
+    _keep_for(stream, *tmp)
     return out
 
 
@@ -300,18 +321,23 @@ def indexer_topk_pool(cache: Cache, q_idx: torch.Tensor, k: int, pool_blocks: in
                       stream=None):
     """indexer_topk plus the hierarchical indexer's candidate pool [B, pool_blocks]."""
     B, H, Di = q_idx.shape
+    tmp = []
     if out is None:
         out = torch.empty(B, k, dtype=torch.int32, device=q_idx.device)
+        tmp.append(out)
     if out_pool is None:
         out_pool = torch.empty(B, pool_blocks, dtype=torch.int32, device=q_idx.device)
+        tmp.append(out_pool)
     if ws is None:
         ws = workspace(cache, k, OP_INDEXER_POOL, pool=(pool_blocks, pool_block))
+        tmp.append(ws)
     d = cache.desc()
     _check(lib().cskv_indexer_topk_pool(
         C.byref(d), _ptr(q_idx, B16, "q_idx", (cache.batch, H, cache.idx_dim)), H,
         _ptr(head_w, F32, "head_w", (cache.batch, H)), k, _ptr(out, I32, "out", (cache.batch, k)),
         pool_blocks, pool_block, _ptr(out_pool, I32, "out_pool", (cache.batch, pool_blocks)),
         _ptr(ws, U8, "ws"), ws.numel(), _stream(stream)))
+    _keep_for(stream, *tmp)
     return out, out_pool
 
 
@@ -321,16 +347,20 @@ def indexer_topk_in_pool(cache: Cache, q_idx: torch.Tensor, k: int, pool: torch.
     """Top-k of this query's indexer scores among the entries of the pooled blocks."""
     B, H, Di = q_idx.shape
     nb = pool.shape[1]
+    tmp = []
     if out is None:
         out = torch.empty(B, k, dtype=torch.int32, device=q_idx.device)
+        tmp.append(out)
     if ws is None:
         ws = workspace(cache, k, OP_INDEXER_IN_POOL, pool=(nb, pool_block))
+        tmp.append(ws)
     d = cache.desc()
     _check(lib().cskv_indexer_topk_in_pool(
         C.byref(d), _ptr(q_idx, B16, "q_idx", (cache.batch, H, cache.idx_dim)), H,
         _ptr(head_w, F32, "head_w", (cache.batch, H)), k, _ptr(pool, I32, "pool", (cache.batch, nb)),
         nb, pool_block, _ptr(out, I32, "out", (cache.batch, k)), _ptr(ws, U8, "ws"), ws.numel(),
         _stream(stream)))
+    _keep_for(stream, *tmp)
     return out
 
 
@@ -342,12 +372,16 @@ def sparse_attn_decode(cache: Cache, q: torch.Tensor, idx: torch.Tensor, swa: to
     k = idx.shape[1]
     W = swa.shape[1]
     dv = cache.dim - cache.rope_dim
+    tmp = []
     if out is None:
         out = torch.empty(B, H, dv, dtype=torch.float32, device=q.device)
+        tmp.append(out)
     if lse is None:
         lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+        tmp.append(lse)
     if ws is None:
         ws = workspace(cache, k, OP_SPARSE_ATTN, H, W)
+        tmp.append(ws)
     d = cache.desc()
     _check(lib().cskv_sparse_attn_decode(
         C.byref(d), _ptr(q, F32, "q", (cache.batch, H, cache.dim)), H,
@@ -355,6 +389,7 @@ def sparse_attn_decode(cache: Cache, q: torch.Tensor, idx: torch.Tensor, swa: to
         _ptr(swa_len, I32, "swa_len", (cache.batch,)), float(softmax_scale),
         _ptr(out, F32, "out", (cache.batch, H, dv)), _ptr(lse, F32, "lse", (cache.batch, H)),
         _ptr(ws, U8, "ws"), ws.numel(), _stream(stream)))
+    _keep_for(stream, *tmp)
     return out, lse
 
 
@@ -381,8 +416,9 @@ def layer_group_decode(cache: Cache, layers: Sequence[Layer], new_tokens: Option
     B = cache.batch
     n_heads = layers[0].q.shape[1]
     n_idx_heads = next((L.q_idx.shape[1] for L in layers if L.q_idx is not None), 1)
+    tmp = None
     if ws is None:
-        ws = workspace(cache, k, OP_LAYER_GROUP, n_heads, window, pool=pool)
+        ws = tmp = workspace(cache, k, OP_LAYER_GROUP, n_heads, window, pool=pool)
     arr = (LayerDesc * len(layers))()
     for i, L in enumerate(layers):
         dv = cache.dim - cache.rope_dim
@@ -404,6 +440,7 @@ def layer_group_decode(cache: Cache, layers: Sequence[Layer], new_tokens: Option
     else:
         _check(lib().cskv_layer_group_decode_pooled(*args, pool[0], pool[1], _ptr(ws, U8, "ws"), ws.numel(),
                                                     _stream(stream)))
+    _keep_for(stream, tmp)
 
 
 def ced_project(h: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None,
@@ -412,10 +449,12 @@ def ced_project(h: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = 
     [rows, d_model], w bf16 bits (int16) [n_out, d_model] -> fp32 [rows, n_out]."""
     rows, dm = h.shape
     n_out = w.shape[0]
+    tmp = None
     if out is None:
-        out = torch.empty(rows, n_out, dtype=torch.float32, device=h.device)
+        out = tmp = torch.empty(rows, n_out, dtype=torch.float32, device=h.device)
     _check(lib().cskv_ced_project(_ptr(h, B16, "h", (rows, dm)), rows, dm, _ptr(w, B16, "w", (n_out, dm)),
                                   n_out, _ptr(out, F32, "out", (rows, n_out)), _stream(stream)))
+    _keep_for(stream, tmp)
     return out
 
 
@@ -475,11 +514,13 @@ def model_workspace(groups: Sequence[Group], k: int, window: int) -> torch.Tenso
 def model_decode(groups: Sequence[Group], k: int, window: int, softmax_scale: float,
                  ws: Optional[torch.Tensor] = None, stream=None) -> None:
     """One decode step of every group of the layer plan (cskv_model_decode)."""
+    tmp = None
     if ws is None:
-        ws = model_workspace(groups, k, window)
+        ws = tmp = model_workspace(groups, k, window)
     descs, keep, n_idx_heads, n_heads = _group_descs(groups, k, window)
     _check(lib().cskv_model_decode(descs, len(groups), n_idx_heads, n_heads, k, window, float(softmax_scale),
                                    _ptr(ws, U8, "ws"), ws.numel(), _stream(stream)))
+    _keep_for(stream, tmp)
 
 
 # ---------------------------------------------------------------- timers

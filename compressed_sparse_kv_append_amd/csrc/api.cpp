@@ -329,13 +329,15 @@ int cskv_swa_append_fp8(uint8_t *ring, int32_t batch, int32_t window, int32_t di
 }
 
 int cskv_indexer_topk(const cskv_cache *cache, const uint16_t *q_idx, int32_t n_idx_heads,
-                      const float *head_w, int32_t k, int32_t *out_idx, void *ws, size_t ws_bytes,
-                      hipStream_t stream)
+                      const float *head_w, int32_t k, int32_t *out_idx, float *out_scores, void *ws,
+                      size_t ws_bytes, hipStream_t stream)
 {
     int rc = check_cache(cache);
     if (rc) return rc;
     if ((rc = topk_args(cache, q_idx, n_idx_heads, k, out_idx, ws, ws_bytes))) return rc;
-    hipError_t e = cskv::launch_indexer_topk(*cache, q_idx, n_idx_heads, head_w, k, out_idx, ws, stream);
+    REQUIRE(!out_scores || aligned(out_scores, 4), CSKV_EINVAL, "out_scores must be 4-byte aligned");
+    hipError_t e = cskv::launch_indexer_topk(*cache, q_idx, n_idx_heads, head_w, k, out_idx, ws, stream,
+                                             nullptr, out_scores);
     return e == hipSuccess ? CSKV_OK : hip_fail(e, "indexer_topk launch");
 }
 

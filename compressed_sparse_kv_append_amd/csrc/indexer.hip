@@ -5,12 +5,18 @@
 //
 // Select: exact top-k per sequence by radix select on those keys.  The digit
 // windows adapt to the keys' actual range (the first window starts below the
-// common prefix of the smallest and largest key).  Work is spread over the
-// chip: a sequence is cut into slices of 4096 keys, one 4-wave block each,
+// common prefix of the smallest and largest key).  Caches of up to 128K
+// entries per sequence take the tile select: the scan also writes the
+// largest key of every 16-entry tile, and the k-th largest of those tile
+// maxima is a lower bound of the k-th largest key (k tiles each hold a key at
+// least that large).  One block per sequence finds that bound by radix select
+// over the tile maxima, keeps the keys at or above it (a few more than k for
+// scores without heavy ties) in index order, and selects the top k among
+// them.  Longer caches are cut into slices of 4096 keys, one block each,
 // whose local top-k lists (which must contain the global top-k) are merged by
 // one block per sequence; a sequence of at most one slice is selected
-// directly.  Each block holds its keys in LDS.  The output lists the selected indices
-// in ascending order; among equal scores the lower index wins.
+// directly.  The output lists the selected indices in ascending order; among
+// equal scores the lower index wins.
 //
 // Sources cited as [P2]:
 //   P2  "DeepSeek V1 到 V4.1-Flash，单 token 的 global KV 如何从 389,000 B 压缩到 890 B的？"
@@ -53,11 +59,34 @@ static int topk_groups(const cskv_cache &c, int k)
 }
 static size_t cand2_stride(const cskv_cache &c, int k) { return ((size_t)topk_groups(c, k) * k + 1) & ~(size_t)1; }
 
+// The bound select serves caches longer than one slice and at most
+// kTileMaxCap entries per sequence.
+constexpr int kTileMaxCap = 1 << 17;
+static bool topk_uses_tiles(const cskv_cache &c)
+{
+    return c.capacity > kSliceKeys && c.capacity <= kTileMaxCap;
+}
+static size_t tile_stride(const cskv_cache &c) { return ((size_t)c.capacity / 16 + 1 + 63) / 64 * 64; }
+static int bound_slices(const cskv_cache &c) { return (int)((c.capacity + kSliceKeys - 1) / kSliceKeys); }
+
 TopkWorkspace topk_workspace(const cskv_cache &c, int k)
 {
     TopkWorkspace w;
     w.keys_off = 0;
     w.cand_off = align_up(sizeof(uint32_t) * score_key_stride(c) * (size_t)c.batch, 256);
+    if (topk_uses_tiles(c)) {
+        // per sequence: one candidate list of up to kSliceKeys pairs per slice,
+        // the slices' counts, the tile maxima
+        w.tiles = true;
+        w.cand2_off = w.cand_off;
+        const size_t slices = (size_t)bound_slices(c);
+        w.tcand_off = w.cand_off;
+        const size_t tcount_off = align_up(w.tcand_off + sizeof(uint2) * slices * kSliceKeys * c.batch, 256);
+        w.tmax_off = align_up(tcount_off + sizeof(uint32_t) * slices * c.batch, 256);
+        w.tmax_stride = tile_stride(c);
+        w.total = align_up(w.tmax_off + sizeof(uint32_t) * w.tmax_stride * c.batch, 256);
+        return w;
+    }
     const size_t slices = (size_t)topk_slices(c);
     const size_t cand = slices > 1 ? sizeof(uint32_t) * 2 * cand_stride(c, k) * c.batch : 0;
     w.cand2_off = align_up(w.cand_off + cand, 256);
@@ -119,6 +148,11 @@ struct SelectArgs {
     uint2 *cand2 = nullptr;
     size_t cand2_stride = 0;
     int groups = 0;
+    // bound select (caches the tile select serves): the largest key of every
+    // 16-entry tile [B][tmax_stride]; the slices' candidate counts [B][slices]
+    const uint32_t *tmax = nullptr;
+    size_t tmax_stride = 0;
+    uint32_t *tcount = nullptr;
 };
 
 // Items of sequence b: its entries, or its blocks of `group` entries.
@@ -234,22 +268,27 @@ __device__ __forceinline__ uint64_t load_keys(const Items &it, int64_t r, uint32
     return vm;
 }
 
-// Exact top-k of `it`, which holds more than k valid items.  Thread t holds
-// PER consecutive positions in registers.  kPairsOut: write the selected
-// (key, index) pairs in index order; else the indices.  Exactly k items are
-// selected, so nothing is padded.
-template <bool kList, bool kPairsOut, int THREADS, int PER>
-__device__ __forceinline__ void select_topk(SelectSmem<THREADS> &sm, const Items &it, int k, int32_t *out_idx,
-                            uint2 *out_pairs)
+// Where the k-th largest valid key of `it` lies: items with key >> tshift
+// greater than T are among the k largest, and of those with key >> tshift ==
+// T the first `ties` in index order complete the set.  `it` holds at least k
+// valid items.  Thread t holds PER consecutive positions of each round in
+// key / idx (loaded here when there are several rounds).
+struct Threshold {
+    uint32_t T;
+    int tshift;
+    uint32_t ties;
+};
+
+// max_passes limits the histogram passes: when it stops the search early,
+// T << tshift is still a lower bound of the k-th largest key (that key has
+// prefix T at shift tshift).
+template <bool kList, int THREADS, int PER>
+__device__ __forceinline__ Threshold radix_threshold(SelectSmem<THREADS> &sm, const Items &it, int k,
+                                                     uint32_t (&key)[PER], uint32_t (&idx)[PER], uint64_t &vm,
+                                                     int64_t rounds, int max_passes = 64)
 {
-    constexpr int kRound = THREADS * PER;
     constexpr int kWaves = THREADS / kWave;
     const int t = threadIdx.x;
-    const int64_t rounds = (it.n + kRound - 1) / kRound;
-    uint32_t key[PER], idx[PER];
-    uint64_t vm = 0;
-    if (rounds == 1) vm = load_keys<kList, THREADS, PER>(it, 0, key, idx);
-
     // ---- range of the valid keys, and the bits in which any two differ
     uint32_t lo = 0xFFFFFFFFu, hi = 0u, orv = 0u, andv = 0xFFFFFFFFu;
     for (int64_t r = 0; r < rounds; ++r) {
@@ -321,7 +360,7 @@ __device__ __forceinline__ void select_topk(SelectSmem<THREADS> &sm, const Items
             // key >> shift of the threshold key
             prefix = pshift >= 32 ? bin + sub : (prefix << (pshift - shift)) | bin;
             need -= a2;
-            if (shift == low || cnt == need) {
+            if (shift == low || cnt == need || --max_passes == 0) {
                 T = prefix;
                 tshift = shift;
                 ties = need;
@@ -333,6 +372,26 @@ __device__ __forceinline__ void select_topk(SelectSmem<THREADS> &sm, const Items
             mask = (1u << (pshift - shift)) - 1u;
         }
     }
+    return Threshold{T, tshift, ties};
+}
+
+// Exact top-k of `it`, which holds more than k valid items.  Thread t holds
+// PER consecutive positions in registers.  kPairsOut: write the selected
+// (key, index) pairs in index order; else the indices.  Exactly k items are
+// selected, so nothing is padded.
+template <bool kList, bool kPairsOut, int THREADS, int PER>
+__device__ __forceinline__ void select_topk(SelectSmem<THREADS> &sm, const Items &it, int k, int32_t *out_idx,
+                            uint2 *out_pairs)
+{
+    constexpr int kRound = THREADS * PER;
+    const int t = threadIdx.x;
+    const int64_t rounds = (it.n + kRound - 1) / kRound;
+    uint32_t key[PER], idx[PER];
+    uint64_t vm = 0;
+    if (rounds == 1) vm = load_keys<kList, THREADS, PER>(it, 0, key, idx);
+    const Threshold th = radix_threshold<kList, THREADS, PER>(sm, it, k, key, idx, vm, rounds);
+    const uint32_t T = th.T, ties = th.ties;
+    const int tshift = th.tshift;
     // Items with key >> tshift == T: the first `ties` of them in index order
     // complete the set (all of them when the bin was taken whole).
 
@@ -425,6 +484,104 @@ __global__ __launch_bounds__(THREADS) void topk_select_kernel(SelectArgs a)
     }
     Items it{a.keys + (size_t)b * a.key_stride, nullptr, E, 0};
     select_topk<false, false, THREADS, KEYS / THREADS>(sm, it, a.k, out, nullptr);
+}
+
+// Bound select, first kernel: slice s of sequence b (a block of THREADS
+// threads, KEYS keys).  The bound V is the prefix bin, after one histogram
+// pass over the sequence's 16-entry tile maxima, that holds the k-th largest
+// tile maximum (every key when there are at most k tiles): at least k tiles
+// hold a key >= V, so the sequence's k largest keys are all >= V.  The
+// slice's keys >= V go to its candidate list as (key, index) pairs in index
+// order, with their count.
+template <int KEYS, int THREADS>
+__global__ __launch_bounds__(THREADS) void topk_bound_slice_kernel(SelectArgs a)
+{
+    __shared__ SelectSmem<THREADS> sm;
+    const int b = blockIdx.y, s = blockIdx.x, t = threadIdx.x;
+    const int64_t E = items_of(a, b);
+    const int64_t first = (int64_t)s * KEYS;
+    if (E <= a.k || first >= E) return;           // the final kernel pads or reads only used slices
+    const int64_t n = E - first < KEYS ? E - first : KEYS;
+    const int64_t nt = (E + 15) / 16;
+    uint32_t V = 0;
+    if (nt > a.k) {
+        constexpr int kPer = 16;                   // tile maxima per thread and round
+        const Items ti{a.tmax + (size_t)b * a.tmax_stride, nullptr, nt, 0};
+        const int64_t rounds = (nt + THREADS * kPer - 1) / (THREADS * kPer);
+        uint32_t key[kPer], idx[kPer];
+        uint64_t vm = 0;
+        if (rounds == 1) vm = load_keys<false, THREADS, kPer>(ti, 0, key, idx);
+        const Threshold th = radix_threshold<false, THREADS, kPer>(sm, ti, a.k, key, idx, vm, rounds, 1);
+        V = th.T << th.tshift;
+        __syncthreads();                           // sm is used again below
+    }
+    constexpr int PER = KEYS / THREADS;
+    const Items it{a.keys + (size_t)b * a.key_stride + first, nullptr, n, first};
+    uint32_t key[PER], idx[PER];
+    const uint64_t vm = load_keys<false, THREADS, PER>(it, 0, key, idx);
+    uint32_t in = 0, mine = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const bool c = ((vm >> i) & 1ull) && key[i] >= V;
+        in |= (uint32_t)c << i;
+        mine += c;
+    }
+    uint32_t total;
+    uint32_t pos = block_scan<THREADS>(mine, sm.wave_sum, &total) - mine;
+    uint2 *out = a.cand + (size_t)b * a.cand_stride + (size_t)s * KEYS;
+    const int64_t p0 = first + (int64_t)PER * t;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+        if ((in >> i) & 1u) out[pos++] = make_uint2(key[i], (uint32_t)(p0 + i));
+    if (t == 0) a.tcount[(size_t)b * a.slices + s] = total;
+}
+
+// Bound select, second kernel: sequence b's candidate lists (slice order is
+// index order) gathered into LDS, then the exact top-k among them; more
+// candidates than kFinalCap (heavily tied scores at the bound) select over
+// every key of the sequence instead.
+constexpr int kFinalThreads = 512;
+constexpr int kFinalPer = 12;
+constexpr int kFinalCap = kFinalThreads * kFinalPer;
+constexpr int kBoundMaxSlices = kTileMaxCap / kSliceKeys;
+__global__ __launch_bounds__(kFinalThreads) void topk_bound_final_kernel(SelectArgs a)
+{
+    __shared__ SelectSmem<kFinalThreads> sm;
+    __shared__ __attribute__((aligned(16))) uint2 lc[kFinalCap];
+    __shared__ uint32_t pre[kBoundMaxSlices + 1];
+    const int b = blockIdx.x, t = threadIdx.x;
+    const int64_t E = items_of(a, b);
+    int32_t *out = a.out + (size_t)b * a.k;
+    if (E <= a.k) {
+        for (int i = t; i < a.k; i += kFinalThreads) out[i] = i < E ? i : -1;
+        return;
+    }
+    const int used = (int)((E + kSliceKeys - 1) / kSliceKeys);
+    if (t < kWave) {                               // prefix of the used slices' counts (used <= 32)
+        const uint32_t c = t < used ? a.tcount[(size_t)b * a.slices + t] : 0u;
+        const uint32_t incl = wave_scan_add(c);
+        if (t <= used) pre[t] = incl - c;
+    }
+    __syncthreads();
+    const uint32_t total = pre[used];
+    if (total > (uint32_t)kFinalCap) {
+        const Items it{a.keys + (size_t)b * a.key_stride, nullptr, E, 0};
+        select_topk<false, false, kFinalThreads, 8>(sm, it, a.k, out, nullptr);
+        return;
+    }
+    const uint2 *cl = a.cand + (size_t)b * a.cand_stride;
+    for (uint32_t p = t; p < total; p += kFinalThreads) {
+        int s = 0;
+        while (pre[s + 1] <= p) ++s;
+        lc[p] = cl[(size_t)s * kSliceKeys + (p - pre[s])];
+    }
+    __syncthreads();
+    if (total == (uint32_t)a.k) {                  // exactly the k largest
+        for (int i = t; i < a.k; i += kFinalThreads) out[i] = (int32_t)lc[i].y;
+        return;
+    }
+    const Items it{nullptr, lc, (int64_t)total, 0};
+    select_topk<true, false, kFinalThreads, kFinalPer>(sm, it, a.k, out, nullptr);
 }
 
 // Sequence b of a cache whose capacity spans several slices: the final top-k
@@ -560,7 +717,7 @@ void launch_select(const SelectArgs &se, int batch, hipStream_t s, const TimedLa
 
 hipError_t launch_indexer_topk(const cskv_cache &c, const uint16_t *q_idx, int heads,
                                const float *head_w, int k, int32_t *out_idx, void *ws,
-                               hipStream_t s, const PoolBuild *pool)
+                               hipStream_t s, const PoolBuild *pool, float *out_scores)
 {
     const TopkWorkspace lay = topk_workspace(c, k);
     uint32_t *keys = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + lay.keys_off);
@@ -572,15 +729,32 @@ hipError_t launch_indexer_topk(const cskv_cache &c, const uint16_t *q_idx, int h
         bkeys = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + pw.bkeys_off);
     }
 
-    launch_indexer_scan(c, q_idx, heads, head_w, keys, s, bkeys, pw.bkey_stride, pool ? pool->block : 1);
+    uint32_t *tmax = lay.tiles ? reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + lay.tmax_off) : nullptr;
+    launch_indexer_scan(c, q_idx, heads, head_w, keys, s, bkeys, pw.bkey_stride, pool ? pool->block : 1,
+                        out_scores, tmax, lay.tmax_stride);
 
     SelectArgs se{keys, cand, c.n_tokens, out_idx, c.capacity, k, topk_slices(c), score_key_stride(c),
                   cand_stride(c, k), 1, c.ratio};
-    se.slice_keys = slice_keys_of(c);
-    se.groups = topk_groups(c, k);
-    se.cand2 = reinterpret_cast<uint2 *>(static_cast<char *>(ws) + lay.cand2_off);
-    se.cand2_stride = cand2_stride(c, k);
-    launch_select(se, c.batch, s, timer_take(CSKV_KERNEL_TOPK_SELECT));
+    if (lay.tiles) {
+        const TimedLaunch tk = timer_take(CSKV_KERNEL_TOPK_SELECT);
+        const int slices = bound_slices(c);
+        se.slices = slices;
+        se.cand = reinterpret_cast<uint2 *>(static_cast<char *>(ws) + lay.tcand_off);
+        se.cand_stride = (size_t)slices * kSliceKeys;
+        se.tmax = tmax;
+        se.tmax_stride = lay.tmax_stride;
+        se.tcount = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) +
+                                                 align_up(lay.tcand_off + sizeof(uint2) * se.cand_stride * c.batch, 256));
+        launch_kernel(topk_bound_slice_kernel<kSliceKeys, kSliceThreads>, dim3((unsigned)slices, (unsigned)c.batch),
+                      dim3(kSliceThreads), s, tk.start, nullptr, se);
+        launch_kernel(topk_bound_final_kernel, dim3((unsigned)c.batch), dim3(kFinalThreads), s, nullptr, tk.stop, se);
+    } else {
+        se.slice_keys = slice_keys_of(c);
+        se.groups = topk_groups(c, k);
+        se.cand2 = reinterpret_cast<uint2 *>(static_cast<char *>(ws) + lay.cand2_off);
+        se.cand2_stride = cand2_stride(c, k);
+        launch_select(se, c.batch, s, timer_take(CSKV_KERNEL_TOPK_SELECT));
+    }
     if (pool) {
         // the pool: the best pool->blocks blocks by their largest key
         uint2 *bcand = reinterpret_cast<uint2 *>(static_cast<char *>(ws) + pw.bcand_off);

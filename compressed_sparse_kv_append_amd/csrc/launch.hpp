@@ -13,9 +13,12 @@ namespace cskv {
 
 // Workspace layout of the indexer + top-k (offsets in bytes from ws): one
 // uint32 score key per entry, and the per-slice candidate lists of sequences
-// longer than one select round.
+// longer than one select round; or, for caches the tile select serves, the
+// largest key of every 16-entry tile and one candidate list per sequence.
 struct TopkWorkspace {
     size_t keys_off, cand_off, cand2_off, total;
+    bool tiles = false;
+    size_t tmax_off = 0, tmax_stride = 0, tcand_off = 0;
 };
 constexpr int kSliceKeys = 4096;  // keys per select slice (one block)
 // Score keys: one uint32 per cache row; a sequence's rows padded to 64.
@@ -42,10 +45,12 @@ hipError_t launch_swa_append(uint16_t *ring, int batch, int window, int dim, con
 // Indexer scan (scan.hip): one score key per valid entry into keys
 // [batch][score_key_stride]; with block_keys, also the largest key of each
 // block of `block` entries (block divides 16) into block_keys
-// [batch][block_stride].
+// [batch][block_stride]; with out_scores, the fp32 score of every live
+// entry into out_scores [batch][capacity].
 void launch_indexer_scan(const cskv_cache &c, const uint16_t *q_idx, int heads, const float *head_w,
                          uint32_t *keys, hipStream_t s, uint32_t *block_keys = nullptr,
-                         size_t block_stride = 0, int block = 1);
+                         size_t block_stride = 0, int block = 1, float *out_scores = nullptr,
+                         uint32_t *tile_max = nullptr, size_t tile_stride = 0);
 // Pooled scan (scan.hip): (score key, entry) pairs of the entries of the
 // pooled blocks, pairs [batch][pool_blocks * block] in pool order; key 0 and
 // entry ~0 where a position holds no entry.
@@ -68,7 +73,7 @@ struct PoolWorkspace {
 PoolWorkspace pool_workspace(const cskv_cache &c, int k, int pool_blocks, int block);
 hipError_t launch_indexer_topk(const cskv_cache &c, const uint16_t *q_idx, int heads,
                                const float *head_w, int k, int32_t *out_idx, void *ws,
-                               hipStream_t s, const PoolBuild *pool = nullptr);
+                               hipStream_t s, const PoolBuild *pool = nullptr, float *out_scores = nullptr);
 // Top-k among the entries of the pooled blocks (a later layer of the
 // hierarchical indexer); ws holds pool_workspace().inpool_total bytes.
 hipError_t launch_indexer_topk_in_pool(const cskv_cache &c, const uint16_t *q_idx, int heads,

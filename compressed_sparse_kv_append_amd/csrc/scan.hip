@@ -38,7 +38,9 @@ struct ScanArgs {
     const uint16_t *q;         // [B][H][Di]
     const float *head_w;       // [B][H] or null
     uint32_t *out_keys;        // [B][key_stride] (full scan)
-    int capacity, heads, chunk;
+    int capacity, heads;
+    int chunk;                 // positions per block (pooled scan); 0: the full scan sizes each
+                               // sequence's runs from its live entries over gridDim.x blocks
     size_t key_stride;
     // full scan: per-block maximum keys [B][block_stride], or null
     uint32_t *block_keys;
@@ -53,6 +55,9 @@ struct ScanArgs {
     // one E8M0 byte per 16 dims
     const uint8_t *idx_scales;
     int ratio;                 // tokens per entry of the cache
+    float *out_scores = nullptr;   // full scan: [B][capacity] fp32 score of every live entry, or null
+    uint32_t *tile_max = nullptr;  // full scan: [B][tile_stride] largest key of each 16-entry tile, or null
+    size_t tile_stride = 0;
 };
 
 typedef __attribute__((address_space(1))) void global_void_t;
@@ -66,9 +71,20 @@ constexpr int kNonTemporal = 2;     // cache policy of the streaming loads
 
 constexpr int kPoolChunkMax = 4096;   // pool positions per block of the pooled scan
 
-// One block: a run of `chunk` entries of one sequence (POOL: of pool
-// positions); wave w takes 16-key tiles w, w + 4, ...  MT: 16-head row tiles
-// of the query (1..4).
+// Run of block blockIdx.x over the n positions of its sequence: the pooled
+// scan's fixed run length, or (full scan) the sequence's live entries cut
+// into gridDim.x runs of a multiple of 64, so a cache allocated far beyond
+// what it holds still spreads its entries over every block of the sequence.
+__device__ __forceinline__ int64_t run_length(const ScanArgs &a, int64_t n)
+{
+    if (a.chunk > 0) return a.chunk;
+    const int64_t per = (n + gridDim.x - 1) / gridDim.x;
+    return (per + 63) / 64 * 64;
+}
+
+// One block: a run of entries of one sequence (POOL: of pool positions);
+// wave w takes 16-key tiles w, w + 4, ...  MT: 16-head row tiles of the
+// query (1..4).
 template <int DI, int MT, bool POOL>
 __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
 {
@@ -91,9 +107,10 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
     const int64_t E = entries_of(a.n_tokens, b, a.capacity, a.ratio);
     // the positions scanned: entries, or pool positions
     const int64_t N = POOL ? (E > 0 ? (int64_t)a.pool_blocks * a.block : 0) : E;
-    const int64_t e_begin = (int64_t)blockIdx.x * a.chunk;
+    const int64_t run = run_length(a, N);
+    const int64_t e_begin = (int64_t)blockIdx.x * run;
     if (e_begin >= N) return;
-    const int64_t e_end = N < e_begin + a.chunk ? N : e_begin + a.chunk;
+    const int64_t e_end = N < e_begin + run ? N : e_begin + run;
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     const int col = lane & 15, grp = lane >> 4;
     if constexpr (POOL) {
@@ -200,6 +217,13 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
         } else {
             const uint32_t key = score_key(part);
             if (lane < 16 && e < e_end) ok[e] = key;
+            if (a.out_scores && lane < 16 && e < e_end) a.out_scores[(size_t)b * a.capacity + e] = part + 0.0f;
+            if (a.tile_max) {
+                // largest key of the 16-entry tile (entries past the end count as key 0)
+                uint32_t m = lane < 16 && e < e_end ? key : 0u;
+                for (int off = 1; off < 16; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+                if (lane == 0) a.tile_max[(size_t)b * a.tile_stride + (e >> 4)] = m;
+            }
             if (a.block_keys) {
                 // largest key of each pool block in the tile (tiles start on
                 // block boundaries; entries past the end count as key 0)
@@ -250,9 +274,10 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_fp4_kernel(ScanArgs
     const int b = blockIdx.y;
     const int64_t E = entries_of(a.n_tokens, b, a.capacity, a.ratio);
     const int64_t N = POOL ? (E > 0 ? (int64_t)a.pool_blocks * a.block : 0) : E;
-    const int64_t e_begin = (int64_t)blockIdx.x * a.chunk;
+    const int64_t run = run_length(a, N);
+    const int64_t e_begin = (int64_t)blockIdx.x * run;
     if (e_begin >= N) return;
-    const int64_t e_end = N < e_begin + a.chunk ? N : e_begin + a.chunk;
+    const int64_t e_end = N < e_begin + run ? N : e_begin + run;
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     const int col = lane & 15, grp = lane >> 4;
     if constexpr (POOL) {
@@ -377,6 +402,12 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_fp4_kernel(ScanArgs
             } else {
                 const uint32_t key = score_key(part);
                 if (lane < 16 && e < e_end) ok[e] = key;
+                if (a.out_scores && lane < 16 && e < e_end) a.out_scores[(size_t)b * a.capacity + e] = part + 0.0f;
+                if (a.tile_max) {
+                    uint32_t m = lane < 16 && e < e_end ? key : 0u;
+                    for (int off = 1; off < 16; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+                    if (lane == 0) a.tile_max[(size_t)b * a.tile_stride + (e >> 4)] = m;
+                }
                 if (a.block_keys) {
                     uint32_t m = e < e_end ? key : 0u;
                     for (int off = 1; off < a.block; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
@@ -404,7 +435,7 @@ static int scan_blocks_per_cu(const cskv_cache &c)
 {
     return c.batch >= kScanManySeqs || c.idx_format == CSKV_IDX_FP4 ? kScanBlocksPerCU : kScanBlocksPerCU - 1;
 }
-static int scan_chunk(int batch, size_t n, size_t cap, int per_cu)
+static int scan_blocks_per_seq(int batch, int per_cu)
 {
     static int cus = 0;
     if (cus == 0) {
@@ -413,7 +444,11 @@ static int scan_chunk(int batch, size_t n, size_t cap, int per_cu)
             cus = 256;
     }
     const int slots = per_cu * cus;
-    const int per_seq = batch >= slots ? 1 : slots / batch;
+    return batch >= slots ? 1 : slots / batch;
+}
+static int scan_chunk(int batch, size_t n, size_t cap, int per_cu)
+{
+    const int per_seq = scan_blocks_per_seq(batch, per_cu);
     size_t chunk = (n + per_seq - 1) / per_seq;
     chunk = (chunk + 63) / 64 * 64;
     return (int)(chunk < cap ? chunk : cap);
@@ -453,12 +488,19 @@ static void scan_dispatch(const cskv_cache &c, int heads, const ScanArgs &sa, di
 }
 
 void launch_indexer_scan(const cskv_cache &c, const uint16_t *q_idx, int heads, const float *head_w,
-                         uint32_t *keys, hipStream_t s, uint32_t *block_keys, size_t block_stride, int block)
+                         uint32_t *keys, hipStream_t s, uint32_t *block_keys, size_t block_stride, int block,
+                         float *out_scores, uint32_t *tile_max, size_t tile_stride)
 {
-    const int chunk = scan_chunk(c.batch, (size_t)c.capacity, (size_t)1 << 30, scan_blocks_per_cu(c));
-    ScanArgs sa{c.idx_keys, c.n_tokens, q_idx, head_w, keys, c.capacity, heads, chunk, score_key_stride(c),
-                block_keys, block_stride, block, nullptr, 0, nullptr, c.idx_scales, c.ratio};
-    dim3 grid((unsigned)(((size_t)c.capacity + chunk - 1) / chunk), (unsigned)c.batch);
+    // per sequence one round's share of the chip's blocks, each run sized on
+    // the device from the sequence's live entries (never more blocks than
+    // 64-entry runs fit in the capacity)
+    const int per_seq = scan_blocks_per_seq(c.batch, scan_blocks_per_cu(c));
+    const size_t max_runs = ((size_t)c.capacity + 63) / 64;
+    const unsigned gx = (unsigned)((size_t)per_seq < max_runs ? (size_t)per_seq : max_runs);
+    ScanArgs sa{c.idx_keys, c.n_tokens, q_idx, head_w, keys, c.capacity, heads, 0, score_key_stride(c),
+                block_keys, block_stride, block, nullptr, 0, nullptr, c.idx_scales, c.ratio, out_scores,
+                tile_max, tile_stride};
+    dim3 grid(gx, (unsigned)c.batch);
     scan_dispatch<false>(c, heads, sa, grid, s);
 }
 

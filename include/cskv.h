@@ -141,7 +141,10 @@ typedef struct cskv_cache {
  * w_comp   f32 [dim][2*dim] stand-in compressor, or NULL.
  *   non-NULL: rows are tokens.  Tokens pair by absolute position (2i, 2i+1);
  *     the entry is e[r] = sum_j w_comp[r][j] * u[j] with u = x_2i || x_2i+1,
- *     folded in fp32 from j = 0 upward with one fused multiply-add per term.
+ *     in this fixed fp32 order: the 1152 terms form 64 contiguous blocks of
+ *     18, each folded from +0 upward with one fused multiply-add per term,
+ *     and the 64 block sums are added as a pairwise tree (blocks 2i and 2i+1
+ *     first, then adjacent pairs of those, up to one sum).
  *     A trailing odd token waits in pending[b].  Entry i takes the indexer-key
  *     row of token 2i+1 (the row that completes it); other key rows are unused.
  *   NULL: rows are already entries; each adds 2 tokens.  Requires an even
@@ -197,12 +200,15 @@ int cskv_swa_append_fp8(uint8_t *ring, int32_t batch, int32_t window, int32_t di
  * head_w   f32 [batch][n_idx_heads] or NULL (all weights 1)
  * out_idx  i32 [batch][k]: the k highest scores, ties to the lower index,
  *          listed in ascending index order; -1 pads when fewer than k entries.
+ * out_scores f32 [batch][capacity] or NULL (not written): the score s_j of
+ *          every entry j < entries of each sequence (a zero score is +0);
+ *          rows at and past a sequence's entry count are left untouched.
  * 1 <= k <= 2048.  ws: device workspace of at least
  * cskv_workspace_bytes(cache, CSKV_OP_INDEXER_TOPK, 0, k, 0) bytes, 256-byte
  * aligned (contents need not be initialised; they are overwritten).
  */
 int cskv_indexer_topk(const cskv_cache *cache, const uint16_t *q_idx, int32_t n_idx_heads,
-                      const float *head_w, int32_t k, int32_t *out_idx, void *ws,
+                      const float *head_w, int32_t k, int32_t *out_idx, float *out_scores, void *ws,
                       size_t ws_bytes, hipStream_t stream);
 
 /*

@@ -149,6 +149,21 @@ WORKLOADS = {
 }
 
 
+# The layer plan of the pages' model as workload layout: one (name, tokens per
+# entry, layer modes) per stored cache, in layer order [P2 四、"CSA2：三种模式，
+# 40 层只存 4 份"]: three encoder caches (2->1), each read by one Full and five
+# Reuse layers; one decoder cache (one entry per token) read by Full + 3 Reuse
+# and then four times Reindex + 3 Reuse.  The two encoder layers the page gives
+# no mode are not in it.  Mode strings and ratios only; the GPU workloads and
+# tests build their caches and layers from this table.
+CSA2_PLAN = (
+    ("encoder0", 2, ("full",) + ("reuse",) * 5),
+    ("encoder1", 2, ("full",) + ("reuse",) * 5),
+    ("encoder2", 2, ("full",) + ("reuse",) * 5),
+    ("decoder", 1, ("full",) + ("reuse",) * 3 + (("reindex",) + ("reuse",) * 3) * 4),
+)
+
+
 def scaled(w: Workload, **over) -> Workload:
     """A copy of a workload with some sizes replaced (small parity cases)."""
     d = {f: getattr(w, f) for f in w.__dataclass_fields__}

@@ -157,12 +157,14 @@ def test_call_arguments_rejected_before_launch(L):
     ws = L.cskv_workspace_bytes(C.byref(d), ck.OP_INDEXER_TOPK, 0, 512, 0)
     assert ws > 0
     out = vp(0x90000)
-    assert L.cskv_indexer_topk(C.byref(d), vp(0xA0000), 4, None, 0, out, vp(0xB0000), ws, None) == ck.EUNSUPPORTED
-    assert L.cskv_indexer_topk(C.byref(d), vp(0xA0000), 65, None, 512, out, vp(0xB0000), ws, None) == ck.EUNSUPPORTED
-    assert L.cskv_indexer_topk(C.byref(d), vp(0xA0000), 4, None, 512, out, vp(0xB0000), ws - 1, None) == ck.EWORKSPACE
-    assert L.cskv_indexer_topk(C.byref(d), vp(0xA0000), 4, None, 512, out, None, ws, None) == ck.EWORKSPACE
+    assert L.cskv_indexer_topk(C.byref(d), vp(0xA0000), 4, None, 0, out, None, vp(0xB0000), ws, None) == ck.EUNSUPPORTED
+    assert L.cskv_indexer_topk(C.byref(d), vp(0xA0000), 65, None, 512, out, None, vp(0xB0000), ws, None) == ck.EUNSUPPORTED
+    assert L.cskv_indexer_topk(C.byref(d), vp(0xA0000), 4, None, 512, out, None, vp(0xB0000), ws - 1, None) == ck.EWORKSPACE
+    assert L.cskv_indexer_topk(C.byref(d), vp(0xA0000), 4, None, 512, out, None, None, ws, None) == ck.EWORKSPACE
     # attention: heads not a multiple of 16, missing window, workspace too small
-    aws = L.cskv_workspace_bytes(C.byref(d), ck.OP_SPARSE_ATTN, 16, 512, 128)
+    # (k = 2048 with a 1024-row window is split over several blocks, whose
+    # partial softmaxes need workspace)
+    aws = L.cskv_workspace_bytes(C.byref(d), ck.OP_SPARSE_ATTN, 16, 2048, 1024)
     assert aws > 256
     assert L.cskv_sparse_attn_decode(C.byref(d), vp(0xC0000), 24, vp(0xD0000), 512, vp(0xE0000), 128,
                                      None, C.c_float(0.04), vp(0xF0000), None, vp(0xB0000), aws,
@@ -170,7 +172,7 @@ def test_call_arguments_rejected_before_launch(L):
     assert L.cskv_sparse_attn_decode(C.byref(d), vp(0xC0000), 16, vp(0xD0000), 512, None, 128,
                                      None, C.c_float(0.04), vp(0xF0000), None, vp(0xB0000), aws,
                                      None) == ck.EINVAL
-    assert L.cskv_sparse_attn_decode(C.byref(d), vp(0xC0000), 16, vp(0xD0000), 512, vp(0xE0000), 128,
+    assert L.cskv_sparse_attn_decode(C.byref(d), vp(0xC0000), 16, vp(0xD0000), 2048, vp(0xE0000), 1024,
                                      None, C.c_float(0.04), vp(0xF0000), None, vp(0xB0000), aws - 1,
                                      None) == ck.EWORKSPACE
     assert L.cskv_workspace_bytes(C.byref(d), 9, 16, 512, 128) == 0

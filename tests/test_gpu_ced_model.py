@@ -97,7 +97,7 @@ def test_ratio_one_cache_append_and_attention(ck, orc):
 
 def _plan_case(ck, orc, g, B, enc_entries, dec_entries, heads, iheads, dm, pool):
     """Device and host caches and step inputs for every group of the plan."""
-    plan = orc.csa2_plan()
+    plan = synth.CSA2_PLAN
     dev_groups, host_groups = [], []
     W = (g.standard_normal((576, 1152)) * 0.02).astype(np.float32)
     for name, ratio, modes in plan:

@@ -2,13 +2,19 @@
 point and launch configuration the bench times (one cskv_layer_group_decode
 step over the whole batch).
 
-The oracle recomputes sampled sequences one by one: their cache rows, step
-inputs and expected results come from the seeded generators in synth/.  The
-other sequences of the batch hold filler of the same value law drawn on the
-GPU with a seeded torch generator; they go through the same launches and are
-checked by properties that hold at any size (selected indices ascending,
-distinct and in range; outputs and log-sum-exps finite).  Sequences are
-independent, so the filler cannot change a sampled sequence's results.
+Every sequence is checked against the oracle.  Sequences with a complete
+host mirror are compared in everything the step produces: cache rows,
+window rings, top-k indices, attention outputs and log-sum-exps.  Their
+inputs come from the seeded generators in synth/, or are drawn on the GPU
+with a seeded torch generator and copied to the host before anything of the
+library touches them (the 64K x 32 batch: its 32 sequences of 32,768 entries
+would take minutes to draw on the host).  The other sequences of the large
+batches hold GPU-drawn cache entries and host-drawn indexer keys; an
+index-only mirror holds their keys (the oracle's append copies bf16 key rows
+verbatim, and zero entries quantise to zero codes and +0 scales, which is
+what the mirror's untouched planes hold), so their top-k indices are compared
+on every sequence.  The step's own inputs (new tokens, queries, windows) are
+host-drawn for every sequence.
 """
 import math
 
@@ -20,7 +26,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 import synth  # noqa: E402
-from tests._gpu_util import TOL, attn_rel_err, dev, host  # noqa: E402
+from tests._gpu_util import TOL, attn_rel_err, dev, host, lse_tol  # noqa: E402
 
 
 @pytest.fixture(scope="module")
@@ -40,7 +46,7 @@ def orc():
 
 
 def _filler_rows(w, b, n):
-    """fp32 [n, dim] on the GPU with the workload's value law (not the oracle's data)."""
+    """fp32 [n, dim] on the GPU with the workload's value law (a seeded torch generator)."""
     g = torch.Generator(device="cuda").manual_seed(1_000_003 * (w.seed + 1) + b)
     z = torch.randn(n, w.dim, generator=g, device="cuda")
     if w.entry_law == "t3":
@@ -57,36 +63,64 @@ def _filler_keys(w, b, n):
     return v.view(torch.int16).contiguous()
 
 
-def _build(ck, orc, w, cap, sampled):
+class Mirrors:
+    """Host mirrors of a device batch: `full` (sorted sequence ids) in one
+    complete oracle cache, every other sequence in an index-only cache."""
+
+    def __init__(self, orc, w, cap, full, batch):
+        self.full = sorted(full)
+        self.rest = [b for b in range(batch) if b not in set(full)]
+        self.hf = orc.Cache.empty(len(self.full), cap, w.dim, w.rope_dim, w.k_group, w.v_group, w.idx_dim)
+        self.hi = orc.Cache.empty(len(self.rest), cap, w.dim, w.rope_dim, w.k_group, w.v_group, w.idx_dim) \
+            if self.rest else None
+        self.pos_f = {b: i for i, b in enumerate(self.full)}
+        self.pos_i = {b: i for i, b in enumerate(self.rest)}
+
+
+def _build(ck, orc, w, cap, full, host_rows="synth"):
     """Device cache of the whole batch (entries mode, one sequence per call)
-    and a one-sequence host mirror for every sampled sequence."""
+    and its mirrors.  Sequences in `full` take synth rows and keys
+    (host_rows="synth") or GPU filler copied to the host ("filler"); the
+    others take GPU filler entries and synth keys."""
     gc = ck.Cache.allocate(w.batch, cap, w.k_group, w.v_group, w.idx_dim)
     E = synth.entry_counts(w)
-    mirrors = {}
+    m = Mirrors(orc, w, cap, full, w.batch)
+    full_rows, full_keys = {}, {}
     for b in range(w.batch):
         n = int(E[b])
-        if n == 0:
-            continue
-        if b in sampled:
+        if b in m.pos_f and host_rows == "synth":
             rows_h, keys_h = synth.cache_entries(w, b), synth.cache_idx_keys(w, b)
             rows, keys = dev(rows_h), dev(keys_h)
-            hc = orc.Cache.empty(1, cap, w.dim, w.rope_dim, w.k_group, w.v_group, w.idx_dim)
-            orc.kv_append(hc, rows_h, np.array([0, n], np.int32), None, keys_h)
-            mirrors[b] = hc
-        else:
+        elif b in m.pos_f:
             rows, keys = _filler_rows(w, b, n), _filler_keys(w, b, n)
-        cu = np.zeros(w.batch + 1, np.int32)
-        cu[b + 1:] = n
-        ck.kv_append_fp4(gc, rows, dev(cu), None, keys)
-    for b in sampled:
-        if b not in mirrors:
-            mirrors[b] = orc.Cache.empty(1, cap, w.dim, w.rope_dim, w.k_group, w.v_group, w.idx_dim)
+            rows_h, keys_h = host(rows), host(keys)
+        else:
+            rows, keys_h = _filler_rows(w, b, n), synth.cache_idx_keys(w, b)
+            keys = dev(keys_h)
+        if b in m.pos_f:
+            full_rows[b], full_keys[b] = rows_h, keys_h
+        else:
+            m.hi.idx_keys[m.pos_i[b], :n] = keys_h
+            m.hi.n_tokens[m.pos_i[b]] = 2 * n
+        if n:
+            cu = np.zeros(w.batch + 1, np.int32)
+            cu[b + 1:] = n
+            ck.kv_append_fp4(gc, rows, dev(cu), None, keys)
+    if m.full:
+        lens = [len(full_keys[b]) for b in m.full]
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        orc.kv_append(m.hf, np.concatenate([full_rows[b] for b in m.full]), cu, None,
+                      np.concatenate([full_keys[b] for b in m.full]))
     torch.cuda.synchronize()
-    return gc, mirrors
+    return gc, m
 
 
-def _step(ck, orc, w, gc, mirrors, st, W_h, pool=None):
-    """One layer-group step on the device, then the oracle per sampled sequence
+def _sub(x, seqs):
+    return None if x is None else np.ascontiguousarray(x[seqs])
+
+
+def _step(ck, orc, w, gc, m, st, W_h, pool=None):
+    """One layer-group step on the device, then the oracle on both mirrors
     (pool: the hierarchical indexer's (pool_blocks, pool_block))."""
     B = w.batch
     scale = 1 / math.sqrt(w.dim)
@@ -104,77 +138,91 @@ def _step(ck, orc, w, gc, mirrors, st, W_h, pool=None):
                           scale, ws=ws, pool=pool)
     torch.cuda.synchronize()
     assert int(host(gc.status)[0]) == 0
+    nt = host(gc.n_tokens)
 
-    # properties of every sequence
-    E = np.clip(host(gc.n_tokens).astype(np.int64) // 2, 0, gc.capacity)
+    for seqs, hc, whole in ((m.full, m.hf, True), (m.rest, m.hi, False)):
+        if not seqs:
+            continue
+        rings = [_sub(r, seqs).copy() for r in st.swa_ring]
+        outs, lses, idxs = orc.layer_group_decode(
+            hc, w.layers, _sub(st.token, seqs), _sub(st.idx_row, seqs), W_h, [_sub(q, seqs) for q in st.q],
+            [_sub(qi, seqs) for qi in st.q_idx], rings, [_sub(r, seqs) for r in st.swa_row], w.topk, scale,
+            pool=pool)
+        assert np.array_equal(nt[seqs], hc.n_tokens)
+        for li, L in enumerate(layers):
+            if L.idx is not None:
+                got = host(L.idx)[seqs]
+                bad = [seqs[i] for i in range(len(seqs)) if not np.array_equal(got[i], idxs[li][i])]
+                assert not bad, f"layer {li}: indices differ for sequences {bad[:8]}"
+        if not whole:
+            continue
+        for i, b in enumerate(seqs):
+            e = int(hc.entries()[i])
+            for name in ("k_codes", "k_scales", "v_codes", "v_scales", "idx_keys", "idx_scales"):
+                gt = getattr(gc, name)
+                if gt is None:
+                    continue
+                assert np.array_equal(host(gt[b, :e]).view(np.uint8), getattr(hc, name)[i, :e].view(np.uint8)), \
+                    f"seq {b}: {name} differs"
+        for li, L in enumerate(layers):
+            assert np.array_equal(host(L.swa)[seqs].view(np.uint16), rings[li]), f"layer {li}: window"
+            err = attn_rel_err(host(L.out)[seqs], outs[li])
+            assert err.max() <= TOL, f"layer {li}: max rel err {err.max():.3e} (seq {seqs[int(err.max(1).argmax())]})"
+            idx_l = idxs[li]
+            tol = lse_tol(hc, _sub(st.q[li], seqs), idx_l, rings[li], hc.n_tokens, scale)
+            d = np.abs(host(L.lse)[seqs] - lses[li])
+            assert (d <= tol).all(), f"layer {li}: lse error {d.max():.3e} over its bound"
+    # every output finite
     for li, L in enumerate(layers):
         assert np.isfinite(host(L.out)).all(), f"layer {li}: non-finite output"
-        lse = host(L.lse)
-        assert np.isfinite(lse[E > 0]).all(), f"layer {li}: non-finite lse"
-        if L.idx is not None:
-            ix = host(L.idx)
-            for b in range(B):
-                m = min(int(E[b]), w.topk)
-                row = ix[b]
-                assert np.all(row[m:] == -1) and np.all(row[:m] >= 0) and np.all(row[:m] < E[b])
-                assert np.all(np.diff(row[:m]) > 0), f"layer {li} seq {b}: indices not ascending"
-
-    # the oracle on each sampled sequence
-    for b, hc in mirrors.items():
-        sl = slice(b, b + 1)
-        rings = [r[sl].copy() for r in st.swa_ring]
-        outs, lses, idxs = orc.layer_group_decode(
-            hc, w.layers, st.token[sl], st.idx_row[sl], W_h, [q[sl] for q in st.q],
-            [None if qi is None else qi[sl] for qi in st.q_idx], rings,
-            [r[sl] for r in st.swa_row], w.topk, scale, pool=pool)
-        e = int(hc.entries()[0])
-        assert int(host(gc.n_tokens)[b]) == int(hc.n_tokens[0])
-        for name in ("k_codes", "k_scales", "v_codes", "v_scales", "idx_keys", "idx_scales"):
-            gt = getattr(gc, name)
-            if gt is None:
-                continue
-            assert np.array_equal(host(gt[b, :e]).view(np.uint8), getattr(hc, name)[0, :e].view(np.uint8)), \
-                f"seq {b}: {name} differs"
-        for li, L in enumerate(layers):
-            assert np.array_equal(host(L.swa[sl]).view(np.uint16), rings[li]), f"seq {b} layer {li}: window"
-            if L.idx is not None:
-                assert np.array_equal(host(L.idx[sl]), idxs[li]), f"seq {b} layer {li}: indices differ"
-            err = attn_rel_err(host(L.out[sl]), outs[li])
-            assert err.max() <= TOL, f"seq {b} layer {li}: max rel err {err.max():.3e}"
-            assert np.abs(host(L.lse[sl]) - lses[li]).max() < 1e-4
     return layers
 
 
 def test_full_decode_64k_b32(ck, orc):
-    """32 sequences x 32,768 entries (64K tokens), group 64, Student-t(3)."""
+    """32 sequences x 32,768 entries (64K tokens), group 64, Student-t(3):
+    every sequence in full, and the indexer's fp32 scores of every entry of
+    every sequence (out_scores) against the oracle's exact scores."""
     w = synth.WORKLOADS["decode_64k_b32"]
-    gc, mirrors = _build(ck, orc, w, w.entries + 8, sampled={0, 17, 31})
-    _step(ck, orc, w, gc, mirrors, synth.step_inputs(w, 0), synth.w_comp(w))
+    gc, m = _build(ck, orc, w, w.entries + 8, full=set(range(w.batch)), host_rows="filler")
+    st = synth.step_inputs(w, 0)
+    _step(ck, orc, w, gc, m, st, synth.w_comp(w))
+    # scores of the cache as the step left it, for the full layer's query
+    scores = torch.full((w.batch, gc.capacity), float("nan"), device="cuda")
+    ck.indexer_topk(gc, dev(st.q_idx[0]), w.topk, scores=scores)
+    torch.cuda.synchronize()
+    sc = host(scores)
+    E = m.hf.entries()
+    for b in range(w.batch):
+        want = orc.indexer_scores(m.hf.idx_keys[b, :E[b]], st.q_idx[0][b])
+        assert np.array_equal(sc[b, :E[b]].astype(np.float64), want), f"seq {b}: scores differ"
+        assert np.isnan(sc[b, E[b]:]).all(), f"seq {b}: rows past the entries were written"
 
 
 def test_full_decode_1m_b1(ck, orc):
     """One sequence of 500,000 entries (1M tokens), group 32: the scan and the
     top-k at full length, every output against the oracle."""
     w = synth.WORKLOADS["decode_1m_b1"]
-    gc, mirrors = _build(ck, orc, w, w.entries + 8, sampled={0})
-    _step(ck, orc, w, gc, mirrors, synth.step_inputs(w, 0), synth.w_comp(w))
+    gc, m = _build(ck, orc, w, w.entries + 8, full={0})
+    _step(ck, orc, w, gc, m, synth.step_inputs(w, 0), synth.w_comp(w))
 
 
 def test_full_group_128k_b64(ck, orc):
-    """Full + Reindex + 3 Reuse on a shared cache, 64 sequences x 65,536 entries."""
+    """Full + Reindex + 3 Reuse on a shared cache, 64 sequences x 65,536
+    entries: indices of both index-producing layers on every sequence,
+    everything on a seeded sample."""
     w = synth.WORKLOADS["group_128k_b64"]
-    gc, mirrors = _build(ck, orc, w, w.entries + 8, sampled={0, 41, 63})
-    _step(ck, orc, w, gc, mirrors, synth.step_inputs(w, 0), synth.w_comp(w))
+    gc, m = _build(ck, orc, w, w.entries + 8, full={0, 41, 63})
+    _step(ck, orc, w, gc, m, synth.step_inputs(w, 0), synth.w_comp(w))
 
 
 def test_full_group_128k_b64_pooled(ck, orc):
     """The same layer group with the hierarchical indexer at the pages' size:
     the full layer's pool of 2048 blocks of 8 entries, the reindex layer
-    selecting inside it."""
+    selecting inside it; indices on every sequence."""
     w = synth.WORKLOADS["group_128k_b64"]
-    gc, mirrors = _build(ck, orc, w, w.entries + 8, sampled={5, 62})
+    gc, m = _build(ck, orc, w, w.entries + 8, full={5, 62})
     st = synth.step_inputs(w, 0)
-    layers = _step(ck, orc, w, gc, mirrors, st, synth.w_comp(w), pool=(2048, 8))
+    layers = _step(ck, orc, w, gc, m, st, synth.w_comp(w), pool=(2048, 8))
     # every sequence: the reindex layer's entries lie in the full layer's pool,
     # rebuilt here from the same cache state and the full layer's query
     fi, ri = w.layers.index("full"), w.layers.index("reindex")
@@ -190,12 +238,13 @@ def test_full_group_128k_b64_pooled(ck, orc):
 def test_full_mixed_ragged_b256(ck, orc):
     """256 ragged sequences (2K-32K tokens) with split K (g32) / V (g128) planes:
     a 16,384-token prefill chunk through the compressor on sequence 0 and one
-    token on every other sequence in one append, then one decode step."""
+    token on every other sequence in one append, then one decode step;
+    indices on every sequence, everything on a seeded sample."""
     w = synth.WORKLOADS["mixed_ragged_b256"]
     E = synth.entry_counts(w)
     cap = int(E.max()) + w.chunk_tokens // 2 + 8
-    sampled = {0, 100, 255}
-    gc, mirrors = _build(ck, orc, w, cap, sampled)
+    full = {0, 100, 255}
+    gc, m = _build(ck, orc, w, cap, full)
     W_h = synth.w_comp(w)
     lens = [w.chunk_tokens] + [1] * (w.batch - 1)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
@@ -204,7 +253,7 @@ def test_full_mixed_ragged_b256(ck, orc):
     host_rows = {}
     for b in range(w.batch):
         n = lens[b]
-        if b in sampled:
+        if b in full:
             t_h, i_h = synth.prefill_tokens(w, b, n), synth.prefill_idx_rows(w, b, n)
             toks[cu[b]:cu[b + 1]] = dev(t_h)
             irows[cu[b]:cu[b + 1]] = dev(i_h)
@@ -214,10 +263,17 @@ def test_full_mixed_ragged_b256(ck, orc):
             irows[cu[b]:cu[b + 1]] = _filler_keys(w, 10_000 + b, n)
     W = dev(W_h)
     ck.kv_append_fp4(gc, toks, dev(cu), W, irows, ws=ck.append_workspace(int(cu[-1]), W))
-    for b, (t_h, i_h) in host_rows.items():
-        orc.kv_append(mirrors[b], t_h, np.array([0, len(t_h)], np.int32), W_h, i_h)
+    fl = [lens[b] for b in m.full]
+    orc.kv_append(m.hf, np.concatenate([host_rows[b][0] for b in m.full]),
+                  np.concatenate([[0], np.cumsum(fl)]).astype(np.int32), W_h,
+                  np.concatenate([host_rows[b][1] for b in m.full]))
+    # the index-only mirror: one token each (its values reach no indexer key:
+    # it waits as the pending half of the next pair)
+    nr = len(m.rest)
+    orc.kv_append(m.hi, np.zeros((nr, w.dim), np.float32), np.arange(nr + 1, dtype=np.int32), W_h,
+                  np.zeros((nr, w.idx_dim), np.uint16))
     torch.cuda.synchronize()
-    _step(ck, orc, w, gc, mirrors, synth.step_inputs(w, 0), W_h)
+    _step(ck, orc, w, gc, m, synth.step_inputs(w, 0), W_h)
 
 
 def test_full_model_plan_64k_b32(ck, orc):
@@ -230,7 +286,7 @@ def test_full_model_plan_64k_b32(ck, orc):
     indices, outputs); the others are GPU filler checked by invariants."""
     B, T, kg, Di, Hi, Hq, K, W, dm = 32, 65536, 64, 128, 64, 64, 512, 128, 512
     sb = 5
-    plan = orc.csa2_plan()
+    plan = synth.CSA2_PLAN
     g = np.random.default_rng(640)
     scale = 1 / math.sqrt(576)
     Wc = (g.standard_normal((576, 1152)) * 0.02).astype(np.float32)

@@ -294,6 +294,16 @@ def test_indexer_topk_merge_candidate_counts(ck, orc):
     _indexer_case(ck, orc, [s + 100, 2 * s + 2047, 2 * s + 2048, 2 * s + 2049], 64, 4, 2048, seed=44)
 
 
+def test_indexer_topk_capacity_far_beyond_entries(ck, orc):
+    """A cache allocated far beyond what it holds: the scan sizes each
+    sequence's runs from its live entries, not from the capacity, so every
+    block of a sequence shares its few thousand entries; the select paths
+    for capacities inside and past the bound select's range both stay exact."""
+    lens = [5000, 3000, 0, 4097, 700]
+    _indexer_case(ck, orc, lens, 128, 64, 512, seed=45, cap=100000)
+    _indexer_case(ck, orc, lens, 64, 4, 512, seed=46, cap=500000)
+
+
 def test_indexer_topk_head_weights_and_small_k(ck, orc):
     hw = synth.head_weights_int(5, 3, 64)
     _indexer_case(ck, orc, [3000, 64, 9000], 128, 64, 512, seed=11, head_w=hw)

@@ -926,6 +926,16 @@ def test_csa2_plan_matches_the_pages(orc):
         [kv["decoder_ratio"]] * kv["decoder_copies"]
 
 
+def test_synth_plan_is_the_oracle_plan(orc):
+    # the GPU workloads take the layer plan from synth; it must be the plan
+    # the oracle follows and the page's counts
+    import synth
+    g = GOLD["csa2_full_layers"]
+    assert [(n, r, list(m)) for n, r, m in synth.CSA2_PLAN] == [(n, r, list(m)) for n, r, m in orc.csa2_plan()]
+    modes = [m for _, _, ms in synth.CSA2_PLAN for m in ms]
+    assert modes.count("full") == g["printed_full"] and len(synth.CSA2_PLAN) == 4
+
+
 def test_plan_caches_in_the_pages_formats_hold_900_bytes_per_token(orc):
     # live caches of the plan in the pages' formats (E2M1 + one E8M0 byte per
     # 16 channels, split value plane; FP4 indexer keys): per token, each
