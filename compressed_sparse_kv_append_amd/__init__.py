@@ -40,7 +40,8 @@ OP_INDEXER_TOPK, OP_SPARSE_ATTN, OP_LAYER_GROUP, OP_INDEXER_POOL, OP_INDEXER_IN_
 EXPORTS = ("cskv_kv_append_fp4", "cskv_append_workspace_bytes", "cskv_swa_append", "cskv_swa_append_fp8",
            "cskv_indexer_topk",
            "cskv_indexer_topk_pool", "cskv_indexer_topk_in_pool", "cskv_sparse_attn_decode",
-           "cskv_layer_group_decode", "cskv_layer_group_decode_pooled", "cskv_workspace_bytes",
+           "cskv_layer_group_decode", "cskv_layer_group_decode_pooled", "cskv_layer_group_decode_noalloc",
+           "cskv_workspace_bytes",
            "cskv_workspace_bytes_pool", "cskv_entry_bytes", "cskv_cache_entry_bytes", "cskv_last_error",
            "cskv_ced_project", "cskv_model_decode", "cskv_model_workspace_bytes",
            "cskv_timer_enable", "cskv_timer_pause", "cskv_timer_read", "cskv_timer_disable_all")
@@ -100,6 +101,7 @@ def lib():
                                               vp, sz, vp]
         L.cskv_layer_group_decode_pooled.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, C.c_float,
                                                      i32, i32, vp, sz, vp]
+        L.cskv_layer_group_decode_noalloc.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, C.c_float, vp]
         L.cskv_indexer_topk_pool.argtypes = [vp, vp, i32, vp, i32, vp, i32, i32, vp, vp, sz, vp]
         L.cskv_indexer_topk_in_pool.argtypes = [vp, vp, i32, vp, i32, vp, i32, i32, vp, vp, sz, vp]
         L.cskv_workspace_bytes.argtypes = [vp, i32, i32, i32, i32]
@@ -121,7 +123,7 @@ def lib():
         for f in ("cskv_kv_append_fp4", "cskv_swa_append", "cskv_swa_append_fp8", "cskv_indexer_topk",
                   "cskv_indexer_topk_pool",
                   "cskv_indexer_topk_in_pool", "cskv_sparse_attn_decode", "cskv_layer_group_decode",
-                  "cskv_layer_group_decode_pooled", "cskv_ced_project", "cskv_model_decode", "cskv_timer_enable", "cskv_timer_pause", "cskv_timer_read",
+                  "cskv_layer_group_decode_pooled", "cskv_layer_group_decode_noalloc", "cskv_ced_project", "cskv_model_decode", "cskv_timer_enable", "cskv_timer_pause", "cskv_timer_read",
                   "cskv_timer_disable_all"):
             getattr(L, f).restype = C.c_int
         _lib = L
@@ -441,6 +443,33 @@ def layer_group_decode(cache: Cache, layers: Sequence[Layer], new_tokens: Option
         _check(lib().cskv_layer_group_decode_pooled(*args, pool[0], pool[1], _ptr(ws, U8, "ws"), ws.numel(),
                                                     _stream(stream)))
     _keep_for(stream, tmp)
+
+
+def layer_group_decode_noalloc(cache: Cache, layers: Sequence[Layer], new_tokens: Optional[torch.Tensor],
+                               w_comp: Optional[torch.Tensor], new_idx_rows: Optional[torch.Tensor],
+                               k: int, window: int, softmax_scale: float, stream=None) -> None:
+    """layer_group_decode without a workspace argument: the library's own
+    scratch (cskv_layer_group_decode_noalloc; nothing is allocated)."""
+    B = cache.batch
+    n_heads = layers[0].q.shape[1]
+    n_idx_heads = next((L.q_idx.shape[1] for L in layers if L.q_idx is not None), 1)
+    arr = (LayerDesc * len(layers))()
+    dv = cache.dim - cache.rope_dim
+    for i, L in enumerate(layers):
+        arr[i] = LayerDesc(MODES[L.mode], _ptr(L.q, F32, "q", (B, n_heads, cache.dim)),
+                           _ptr(L.q_idx, B16, "q_idx", (B, n_idx_heads, cache.idx_dim)),
+                           _ptr(L.head_w, F32, "head_w", (B, n_idx_heads)),
+                           _ptr(L.swa, U8 if cache.swa_format == SWA_FP8 else B16, "swa", (B, window, cache.dim)),
+                           _ptr(L.swa_row, F32, "swa_row", (B, cache.dim)),
+                           _ptr(L.idx, I32, "idx", (B, k)),
+                           _ptr(L.out, F32, "out", (B, n_heads, dv)),
+                           _ptr(L.lse, F32, "lse", (B, n_heads)))
+    d = cache.desc()
+    _check(lib().cskv_layer_group_decode_noalloc(
+        C.byref(d), arr, len(layers), _ptr(new_tokens, F32, "new_tokens", (B, cache.dim)),
+        _ptr(w_comp, F32, "w_comp", (cache.dim, 2 * cache.dim)),
+        _ptr(new_idx_rows, B16, "new_idx_rows", (B, cache.idx_dim)), n_idx_heads, n_heads, k, window,
+        float(softmax_scale), _stream(stream)))
 
 
 def ced_project(h: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None,

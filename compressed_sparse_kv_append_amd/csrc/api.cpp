@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -159,6 +160,35 @@ size_t group_ws_bytes(const cskv_cache &c, int heads, int k, int window, int poo
     need = std::max(need, cskv::append_workspace_bytes(c.batch));   // one new token per sequence
     need = std::max(need, (size_t)256);
     return group_pool_bytes(c, pool_blocks) + need;
+}
+
+// ---------------------------------------------------------------- scratch
+
+// The workspace of cskv_layer_group_decode_noalloc: a file-scope device
+// array, one copy per GPU, held until the process ends.  Host code never
+// uses its name as an address: each device's address is looked up once with
+// hipGetSymbolAddress (with that device current) and kept here.
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[CSKV_NOALLOC_SCRATCH_BYTES];
+void *g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+int scratch_of_current_device(void **ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    REQUIRE(dev >= 0 && dev < kMaxDevices, CSKV_EUNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        REQUIRE(p && aligned(p, 256), CSKV_EHIP, "scratch address not 256-byte aligned");
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return CSKV_OK;
 }
 
 // ---------------------------------------------------------------- timers
@@ -521,6 +551,33 @@ int cskv_layer_group_decode(const cskv_cache *cache, const cskv_layer *layers, i
 {
     return layer_group(cache, layers, n_layers, new_tokens, w_comp, new_idx_rows, n_idx_heads, n_heads, k,
                        window, softmax_scale, 0, 0, ws, ws_bytes, stream);
+}
+
+int cskv_layer_group_decode_noalloc(const cskv_cache *cache, const cskv_layer *layers, int32_t n_layers,
+                                    const float *new_tokens, const float *w_comp,
+                                    const uint16_t *new_idx_rows, int32_t n_idx_heads, int32_t n_heads,
+                                    int32_t k, int32_t window, float softmax_scale, hipStream_t stream)
+{
+    int rc = check_cache(cache);
+    if (rc) return rc;
+    REQUIRE(n_heads >= 16 && n_heads <= 1024 && n_heads % 16 == 0 && k >= 1 && k <= 2048 && window >= 1 &&
+                window <= 1024,
+            CSKV_EUNSUPPORTED, "n_heads %d, k %d or window %d outside the supported range", n_heads, k, window);
+    const size_t need = group_ws_bytes(*cache, n_heads, k, window, 0, 0);
+    REQUIRE(need <= (size_t)CSKV_NOALLOC_SCRATCH_BYTES, CSKV_EWORKSPACE,
+            "this step needs %zu bytes of workspace; the built-in scratch holds %zu "
+            "(use cskv_layer_group_decode with a caller workspace)",
+            need, (size_t)CSKV_NOALLOC_SCRATCH_BYTES);
+    // every argument is checked before the scratch is looked up (the check
+    // reads only the workspace's size and alignment, not its address)
+    void *const placeholder = reinterpret_cast<void *>((uintptr_t)256);
+    if ((rc = check_group(cache, layers, n_layers, new_tokens, w_comp, new_idx_rows, n_idx_heads, n_heads, k,
+                          window, 0, 0, placeholder, (size_t)CSKV_NOALLOC_SCRATCH_BYTES)))
+        return rc;
+    void *ws = nullptr;
+    if ((rc = scratch_of_current_device(&ws))) return rc;
+    return run_group(cache, layers, n_layers, new_tokens, w_comp, new_idx_rows, n_idx_heads, n_heads, k, window,
+                     softmax_scale, 0, 0, ws, stream);
 }
 
 int cskv_layer_group_decode_pooled(const cskv_cache *cache, const cskv_layer *layers,

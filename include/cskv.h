@@ -271,6 +271,26 @@ int cskv_layer_group_decode(const cskv_cache *cache, const cskv_layer *layers, i
                             size_t ws_bytes, hipStream_t stream);
 
 /*
+ * cskv_layer_group_decode for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same step with the same results, its workspace taken from
+ * a scratch array built into the library (one per GPU, CSKV_NOALLOC_SCRATCH_BYTES
+ * bytes, held until the process ends; its address is looked up on the first
+ * call on each device).  Nothing is allocated.  A step whose workspace
+ * (cskv_workspace_bytes(cache, CSKV_OP_LAYER_GROUP, n_heads, k, window)) is
+ * larger returns CSKV_EWORKSPACE before anything is enqueued.  Every call on
+ * one GPU shares that GPU's scratch: calls that may overlap on one GPU
+ * (different streams, different threads) race and must be serialised by the
+ * caller.  The scratch needs no initialisation; the step overwrites what it
+ * reads.  Arguments as for cskv_layer_group_decode.
+ */
+#define CSKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+int cskv_layer_group_decode_noalloc(const cskv_cache *cache, const cskv_layer *layers, int32_t n_layers,
+                                    const float *new_tokens, const float *w_comp,
+                                    const uint16_t *new_idx_rows, int32_t n_idx_heads, int32_t n_heads,
+                                    int32_t k, int32_t window, float softmax_scale, hipStream_t stream);
+
+/*
  * Hierarchical sparse indexer [P2 "层级稀疏索引器：后面的层只在候选池里找":
  * after the first Full layer has scored every position, each block of 8
  * positions keeps its best score and the 2048 best blocks, 16,384 positions,

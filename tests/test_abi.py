@@ -233,3 +233,20 @@ def test_pool_arguments_rejected_before_launch(L):
     g1 = L.cskv_workspace_bytes_pool(C.byref(d), ck.OP_LAYER_GROUP, 16, 512, 128, 2048, 8)
     assert g1 > g0 and L.cskv_workspace_bytes_pool(C.byref(d), ck.OP_LAYER_GROUP, 16, 512, 128, 0, 0) == g0
 
+
+
+def test_noalloc_step_beyond_its_scratch_is_refused(L):
+    # 32 sequences x 600K entries: the score keys alone (4 B per cache row)
+    # pass the built-in 64 MiB scratch; refused before any device call
+    d = _desc(batch=32, capacity=600000, k_group=64, idx_dim=128)
+    need = L.cskv_workspace_bytes(C.byref(d), ck.OP_LAYER_GROUP, 64, 512, 128)
+    assert need > (64 << 20)
+    rc = L.cskv_layer_group_decode_noalloc(C.byref(d), None, 1, None, None, None, 64, 64, 512, 128,
+                                           C.c_float(0.04), None)
+    assert rc == ck.EWORKSPACE and "scratch" in _err(L), (rc, _err(L))
+    # a step within the scratch passes this check; its arguments are checked
+    # before the scratch is looked up (no layer array: EINVAL, no device call)
+    small = _desc(batch=2, capacity=5000, k_group=64, idx_dim=128)
+    rc = L.cskv_layer_group_decode_noalloc(C.byref(small), None, 1, None, None, None, 64, 64, 512, 128,
+                                           C.c_float(0.04), None)
+    assert rc == ck.EINVAL and "layers" in _err(L), (rc, _err(L))
