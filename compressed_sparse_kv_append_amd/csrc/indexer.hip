@@ -492,37 +492,46 @@ __global__ __launch_bounds__(THREADS) void topk_select_kernel(SelectArgs a)
 // tile maximum (every key when there are at most k tiles): at least k tiles
 // hold a key >= V, so the sequence's k largest keys are all >= V.  The
 // slice's keys >= V go to its candidate list as (key, index) pairs in index
-// order, with their count.
+// order, with their count.  The slice's keys and the tile maxima are read
+// at once, bounded by the capacity, and masked by the entry count when it
+// arrives, so the block waits for memory once.
 template <int KEYS, int THREADS>
 __global__ __launch_bounds__(THREADS) void topk_bound_slice_kernel(SelectArgs a)
 {
     __shared__ SelectSmem<THREADS> sm;
+    constexpr int PER = KEYS / THREADS;
+    constexpr int kTPer = 16;                     // tile maxima per thread (the capacity bounds them)
     const int b = blockIdx.y, s = blockIdx.x, t = threadIdx.x;
-    const int64_t E = items_of(a, b);
     const int64_t first = (int64_t)s * KEYS;
+    const int64_t cap_items = a.capacity;
+    const int64_t ncap = cap_items - first < KEYS ? cap_items - first : KEYS;
+    const Items kit{a.keys + (size_t)b * a.key_stride + first, nullptr, ncap, first};
+    uint32_t key[PER], kidx[PER];
+    uint64_t kvm = load_keys<false, THREADS, PER>(kit, 0, key, kidx);
+    const int64_t nt_cap = (cap_items + 15) / 16;
+    const Items tit{a.tmax + (size_t)b * a.tmax_stride, nullptr, nt_cap, 0};
+    uint32_t tm[kTPer], tidx[kTPer];
+    uint64_t tvm = load_keys<false, THREADS, kTPer>(tit, 0, tm, tidx);
+    const int64_t E = items_of(a, b);
     if (E <= a.k || first >= E) return;           // the final kernel pads or reads only used slices
     const int64_t n = E - first < KEYS ? E - first : KEYS;
     const int64_t nt = (E + 15) / 16;
+    {                                              // positions past the entries hold stale data
+        const int64_t kv = n - (int64_t)PER * t, tv = nt - (int64_t)kTPer * t;
+        kvm &= kv >= PER ? ~0ull : (kv > 0 ? (1ull << kv) - 1ull : 0ull);
+        tvm &= tv >= kTPer ? ~0ull : (tv > 0 ? (1ull << tv) - 1ull : 0ull);
+    }
     uint32_t V = 0;
     if (nt > a.k) {
-        constexpr int kPer = 16;                   // tile maxima per thread and round
         const Items ti{a.tmax + (size_t)b * a.tmax_stride, nullptr, nt, 0};
-        const int64_t rounds = (nt + THREADS * kPer - 1) / (THREADS * kPer);
-        uint32_t key[kPer], idx[kPer];
-        uint64_t vm = 0;
-        if (rounds == 1) vm = load_keys<false, THREADS, kPer>(ti, 0, key, idx);
-        const Threshold th = radix_threshold<false, THREADS, kPer>(sm, ti, a.k, key, idx, vm, rounds, 1);
+        const Threshold th = radix_threshold<false, THREADS, kTPer>(sm, ti, a.k, tm, tidx, tvm, 1, 1);
         V = th.T << th.tshift;
         __syncthreads();                           // sm is used again below
     }
-    constexpr int PER = KEYS / THREADS;
-    const Items it{a.keys + (size_t)b * a.key_stride + first, nullptr, n, first};
-    uint32_t key[PER], idx[PER];
-    const uint64_t vm = load_keys<false, THREADS, PER>(it, 0, key, idx);
     uint32_t in = 0, mine = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const bool c = ((vm >> i) & 1ull) && key[i] >= V;
+        const bool c = ((kvm >> i) & 1ull) && key[i] >= V;
         in |= (uint32_t)c << i;
         mine += c;
     }
@@ -539,17 +548,30 @@ __global__ __launch_bounds__(THREADS) void topk_bound_slice_kernel(SelectArgs a)
 // Bound select, second kernel: sequence b's candidate lists (slice order is
 // index order) gathered into LDS, then the exact top-k among them; more
 // candidates than kFinalCap (heavily tied scores at the bound) select over
-// every key of the sequence instead.
+// every key of the sequence instead.  The entry count, the slices' counts
+// and the first kSpec pairs of every slice are read at once; a slice with
+// more candidates has the rest read afterwards.
 constexpr int kFinalThreads = 512;
 constexpr int kFinalPer = 12;
 constexpr int kFinalCap = kFinalThreads * kFinalPer;
 constexpr int kBoundMaxSlices = kTileMaxCap / kSliceKeys;
+constexpr int kSpec = 128;
 __global__ __launch_bounds__(kFinalThreads) void topk_bound_final_kernel(SelectArgs a)
 {
     __shared__ SelectSmem<kFinalThreads> sm;
     __shared__ __attribute__((aligned(16))) uint2 lc[kFinalCap];
     __shared__ uint32_t pre[kBoundMaxSlices + 1];
+    constexpr int kSpecPer = kBoundMaxSlices * kSpec / kFinalThreads;   // 8
     const int b = blockIdx.x, t = threadIdx.x;
+    const uint2 *cl = a.cand + (size_t)b * a.cand_stride;
+    // speculative reads: pair j of slice sl for every slice that may exist
+    uint2 sp[kSpecPer];
+#pragma unroll
+    for (int i = 0; i < kSpecPer; ++i) {
+        const int u = t + kFinalThreads * i, sl = u / kSpec, j = u % kSpec;
+        sp[i] = sl < a.slices ? cl[(size_t)sl * kSliceKeys + j] : make_uint2(0u, 0u);
+    }
+    const uint32_t cnt = t < a.slices ? a.tcount[(size_t)b * a.slices + t] : 0u;
     const int64_t E = items_of(a, b);
     int32_t *out = a.out + (size_t)b * a.k;
     if (E <= a.k) {
@@ -558,7 +580,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_bound_final_kernel(SelectA
     }
     const int used = (int)((E + kSliceKeys - 1) / kSliceKeys);
     if (t < kWave) {                               // prefix of the used slices' counts (used <= 32)
-        const uint32_t c = t < used ? a.tcount[(size_t)b * a.slices + t] : 0u;
+        const uint32_t c = t < used ? cnt : 0u;
         const uint32_t incl = wave_scan_add(c);
         if (t <= used) pre[t] = incl - c;
     }
@@ -569,11 +591,14 @@ __global__ __launch_bounds__(kFinalThreads) void topk_bound_final_kernel(SelectA
         select_topk<false, false, kFinalThreads, 8>(sm, it, a.k, out, nullptr);
         return;
     }
-    const uint2 *cl = a.cand + (size_t)b * a.cand_stride;
-    for (uint32_t p = t; p < total; p += kFinalThreads) {
-        int s = 0;
-        while (pre[s + 1] <= p) ++s;
-        lc[p] = cl[(size_t)s * kSliceKeys + (p - pre[s])];
+#pragma unroll
+    for (int i = 0; i < kSpecPer; ++i) {
+        const int u = t + kFinalThreads * i, sl = u / kSpec, j = u % kSpec;
+        if (sl < used && (uint32_t)j < pre[sl + 1] - pre[sl]) lc[pre[sl] + j] = sp[i];
+    }
+    for (int sl = 0; sl < used; ++sl) {            // slices with more than kSpec candidates
+        const uint32_t c = pre[sl + 1] - pre[sl];
+        for (uint32_t j = kSpec + t; j < c; j += kFinalThreads) lc[pre[sl] + j] = cl[(size_t)sl * kSliceKeys + j];
     }
     __syncthreads();
     if (total == (uint32_t)a.k) {                  // exactly the k largest
