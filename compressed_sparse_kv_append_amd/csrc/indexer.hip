@@ -228,44 +228,39 @@ __device__ __forceinline__ void find_threshold_bin_wave0(Smem &sm, int nbins, ui
 }
 
 // The keys of positions [PER t, PER t + PER) of round r, held by thread t,
-// and their validity bits.  List mode: an unused slot holds key 0.
+// and their validity bits (list mode: a position past n or a slot holding
+// key 0 is not valid).  Every load is issued before any is waited for (a
+// position past n reads position 0 instead, and is masked): a contiguous
+// array is read 16 bytes at a time and must be readable up to n rounded up
+// to a multiple of 4 (every key array here is padded to 64 per sequence);
+// lists are read one pair at a time.
 template <bool kList, int THREADS, int PER>
 __device__ __forceinline__ uint64_t load_keys(const Items &it, int64_t r, uint32_t (&key)[PER],
                                               uint32_t (&idx)[PER])
 {
     const int64_t p0 = r * (int64_t)(THREADS * PER) + (int64_t)PER * threadIdx.x;
-    uint64_t vm = 0;
+    const int64_t nv = it.n - p0;
+    const uint64_t vm = nv >= PER ? (PER == 64 ? ~0ull : (1ull << PER) - 1ull) : (nv > 0 ? (1ull << nv) - 1ull : 0ull);
     if constexpr (!kList) {
         static_assert(PER % 4 == 0, "contiguous keys load as uint4");
 #pragma unroll
         for (int i = 0; i < PER; i += 4) {
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (p0 + i + 3 < it.n) {
-                v = *reinterpret_cast<const uint4 *>(it.keys + p0 + i);
-            } else {
-                if (p0 + i + 0 < it.n) v.x = it.keys[p0 + i + 0];
-                if (p0 + i + 1 < it.n) v.y = it.keys[p0 + i + 1];
-                if (p0 + i + 2 < it.n) v.z = it.keys[p0 + i + 2];
-            }
+            const uint4 v = *reinterpret_cast<const uint4 *>(it.keys + (i < nv ? p0 + i : 0));
             key[i] = v.x; key[i + 1] = v.y; key[i + 2] = v.z; key[i + 3] = v.w;
         }
-        const int64_t nv = it.n - p0;
-        vm = nv >= PER ? (PER == 64 ? ~0ull : (1ull << PER) - 1ull) : (nv > 0 ? (1ull << nv) - 1ull : 0ull);
+        return vm;
     } else {
 #pragma unroll
-        for (int i = 0; i < PER; i += 2) {
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (p0 + i + 1 < it.n) v = *reinterpret_cast<const uint4 *>(it.pairs + p0 + i);
-            else if (p0 + i < it.n) { const uint2 u = it.pairs[p0 + i]; v.x = u.x; v.y = u.y; }
-            key[i] = v.x;
-            idx[i] = v.y;
-            key[i + 1] = v.z;
-            idx[i + 1] = v.w;
+        for (int i = 0; i < PER; ++i) {
+            const uint2 u = it.pairs[i < nv ? p0 + i : 0];
+            key[i] = u.x;
+            idx[i] = u.y;
         }
+        uint64_t lv = 0;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) vm |= (uint64_t)(key[i] != 0u) << i;
+        for (int i = 0; i < PER; ++i) lv |= (uint64_t)(key[i] != 0u) << i;
+        return vm & lv;
     }
-    return vm;
 }
 
 // Where the k-th largest valid key of `it` lies: items with key >> tshift
@@ -569,7 +564,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_bound_final_kernel(SelectA
 #pragma unroll
     for (int i = 0; i < kSpecPer; ++i) {
         const int u = t + kFinalThreads * i, sl = u / kSpec, j = u % kSpec;
-        sp[i] = sl < a.slices ? cl[(size_t)sl * kSliceKeys + j] : make_uint2(0u, 0u);
+        sp[i] = cl[(size_t)(sl < a.slices ? sl : 0) * kSliceKeys + j];     // unused when sl >= slices
     }
     const uint32_t cnt = t < a.slices ? a.tcount[(size_t)b * a.slices + t] : 0u;
     const int64_t E = items_of(a, b);
@@ -605,8 +600,12 @@ __global__ __launch_bounds__(kFinalThreads) void topk_bound_final_kernel(SelectA
         for (int i = t; i < a.k; i += kFinalThreads) out[i] = (int32_t)lc[i].y;
         return;
     }
+    // the select's work grows with its item slots: few candidates take few
     const Items it{nullptr, lc, (int64_t)total, 0};
-    select_topk<true, false, kFinalThreads, kFinalPer>(sm, it, a.k, out, nullptr);
+    if (total <= (uint32_t)(kFinalThreads * 2))
+        select_topk<true, false, kFinalThreads, 2>(sm, it, a.k, out, nullptr);
+    else
+        select_topk<true, false, kFinalThreads, kFinalPer>(sm, it, a.k, out, nullptr);
 }
 
 // Sequence b of a cache whose capacity spans several slices: the final top-k
