@@ -49,17 +49,16 @@ struct RowInfo {
     int64_t partner;     // compressor mode: input row of x_even, -1 = pending[b]
 };
 
+// (b is row r's sequence and p its token count, read by the caller so that
+// it can issue other loads before waiting for them.)
 template <bool kCompress>
-__device__ __forceinline__ RowInfo row_info(const AppendArgs &a, int64_t r)
+__device__ __forceinline__ RowInfo row_info(const AppendArgs &a, int64_t r, int b, int64_t p)
 {
     const cskv_cache &c = a.c;
-    RowInfo ri{0, -1, -1};
-    const int b = seq_of_row(a.cu_new, c.batch, (int)r);
-    ri.b = b;
+    RowInfo ri{b, -1, -1};
     const int64_t row0 = a.cu_new ? a.cu_new[b] : b;
     const int64_t m = a.cu_new ? (int64_t)a.cu_new[b + 1] - row0 : 1;
     const int64_t q = r - row0;
-    const int64_t p = c.n_tokens[b];
     if (p < 0 || !rows_ok(row0, m, a.total_new) || q < 0 || q >= m) return ri;
     if (kCompress) {
         const int64_t pos = p + q;
@@ -90,7 +89,10 @@ constexpr int kCompTerms = 2 * kDim / kWave;     // 18 terms per block
 // 18 l + 17], so the wave reads each W row contiguously once for all E
 // rows.  The tree is four DPP steps inside each row of 16 lanes (lane p
 // adds lane p + w) and one scalar step over the four row sums.  A wave
-// takes `cpw` output channels of E consecutive input rows.
+// takes `cpw` output channels of E consecutive input rows.  Its loads are
+// issued in three groups before any is waited for: the rows' token counts,
+// the W rows of up to kDepth channels (they depend on nothing), then the
+// token rows (their addresses depend on the counts).
 constexpr int kDppRowShl = 0x100;
 
 template <int CTRL>
@@ -102,69 +104,89 @@ __device__ __forceinline__ float dpp_shl(float v)
 template <int E>
 __global__ __launch_bounds__(kWave) void compress_kernel(AppendArgs a, int cpw)
 {
+    constexpr int kDepth = E <= 4 ? 6 : 3;         // W rows in flight per wave
+    constexpr int kH = kCompTerms / 2;
     const int lane = threadIdx.x;
     const int64_t r0 = (int64_t)blockIdx.y * E;
     const int c0 = blockIdx.x * cpw;
     const int c1 = c0 + cpw < kDim ? c0 + cpw : kDim;
 
+    int bs[E];
+    int64_t ps[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int64_t r = r0 + e < a.total_new ? r0 + e : r0;
+        bs[e] = seq_of_row(a.cu_new, a.c.batch, (int)r);
+        ps[e] = a.c.n_tokens[bs[e]];
+    }
+    const float2 *wl = reinterpret_cast<const float2 *>(a.w_comp) + kH * lane;
+    float2 w[kDepth][kH];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+        const int c = c0 + d < c1 ? c0 + d : c1 - 1;
+#pragma unroll
+        for (int t = 0; t < kH; ++t) w[d][t] = wl[(size_t)c * kDim + t];
+    }
+
     // u's terms of this lane's block for every row of the group that
-    // completes an entry; lanes 0-31 hold x_even, lanes 32-63 x_odd
+    // completes an entry; lanes 0-31 hold x_even, lanes 32-63 x_odd (rows
+    // that complete no entry read row 0 and are never used)
     float u[E][kCompTerms];
     uint32_t act = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const int64_t r = r0 + e;
         RowInfo ri{0, -1, -1};
-        if (r < a.total_new) ri = row_info<true>(a, r);
+        if (r < a.total_new) ri = row_info<true>(a, r, bs[e], ps[e]);
         const bool on = ri.entry >= 0;
         act |= (uint32_t)on << e;
-        // rows that complete no entry read row 0 (always present) and drop it
         const float *src = !on ? a.tokens
                          : lane < kWave / 2
                                ? (ri.partner >= 0 ? a.tokens + (size_t)ri.partner * kDim
                                                   : a.c.pending + (size_t)ri.b * kDim) + kCompTerms * lane
                                : a.tokens + (size_t)r * kDim + kCompTerms * (lane - kWave / 2);
 #pragma unroll
-        for (int t = 0; t < kCompTerms / 2; ++t) {
+        for (int t = 0; t < kH; ++t) {
             const float2 x = reinterpret_cast<const float2 *>(src)[t];
-            const float2 v = on ? x : make_float2(0.f, 0.f);
-            u[e][2 * t] = v.x;
-            u[e][2 * t + 1] = v.y;
+            u[e][2 * t] = x.x;
+            u[e][2 * t + 1] = x.y;
         }
     }
     if (act == 0) return;
 
-    const float2 *wl = reinterpret_cast<const float2 *>(a.w_comp) + (kCompTerms / 2) * lane;
-    float2 wn[kCompTerms / 2];
+    for (int cb = c0; cb < c1; cb += kDepth) {
+        if (cb != c0) {
 #pragma unroll
-    for (int t = 0; t < kCompTerms / 2; ++t) wn[t] = wl[(size_t)c0 * kDim + t];
-    for (int c = c0; c < c1; ++c) {
-        float2 w[kCompTerms / 2];
+            for (int d = 0; d < kDepth; ++d) {
+                const int c = cb + d < c1 ? cb + d : c1 - 1;
 #pragma unroll
-        for (int t = 0; t < kCompTerms / 2; ++t) w[t] = wn[t];
-        if (c + 1 < c1) {
-#pragma unroll
-            for (int t = 0; t < kCompTerms / 2; ++t) wn[t] = wl[(size_t)(c + 1) * kDim + t];
+                for (int t = 0; t < kH; ++t) w[d][t] = wl[(size_t)c * kDim + t];
+            }
         }
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            if (!((act >> e) & 1u)) continue;
-            float acc = 0.0f;
+        for (int d = 0; d < kDepth; ++d) {
+            const int c = cb + d;
+            if (c >= c1) break;
 #pragma unroll
-            for (int t = 0; t < kCompTerms / 2; ++t) {
-                acc = fmaf(w[t].x, u[e][2 * t], acc);
-                acc = fmaf(w[t].y, u[e][2 * t + 1], acc);
+            for (int e = 0; e < E; ++e) {
+                if (!((act >> e) & 1u)) continue;
+                float acc = 0.0f;
+#pragma unroll
+                for (int t = 0; t < kH; ++t) {
+                    acc = fmaf(w[d][t].x, u[e][2 * t], acc);
+                    acc = fmaf(w[d][t].y, u[e][2 * t + 1], acc);
+                }
+                acc = acc + dpp_shl<kDppRowShl | 1>(acc);
+                acc = acc + dpp_shl<kDppRowShl | 2>(acc);
+                acc = acc + dpp_shl<kDppRowShl | 4>(acc);
+                acc = acc + dpp_shl<kDppRowShl | 8>(acc);
+                const float q0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 0));
+                const float q1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 16));
+                const float q2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 32));
+                const float q3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 48));
+                const float res = (q0 + q1) + (q2 + q3);
+                if (lane == e) a.ent[(size_t)(r0 + e) * kDim + c] = res;
             }
-            acc = acc + dpp_shl<kDppRowShl | 1>(acc);
-            acc = acc + dpp_shl<kDppRowShl | 2>(acc);
-            acc = acc + dpp_shl<kDppRowShl | 4>(acc);
-            acc = acc + dpp_shl<kDppRowShl | 8>(acc);
-            const float q0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 0));
-            const float q1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 16));
-            const float q2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 32));
-            const float q3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 48));
-            const float res = (q0 + q1) + (q2 + q3);
-            if (lane == e) a.ent[(size_t)(r0 + e) * kDim + c] = res;
         }
     }
 }
@@ -323,10 +345,10 @@ __device__ int64_t finalize_seq(const AppendArgs &a, int b, int64_t p, int t, in
 }
 
 // Quantise entry value e (channel t of the entry) into cache slot `slot`
-// (sequence-major row of every plane) and copy or quantise input row r's
-// indexer key there.  Called by all threads of a kAppendThreads block
+// (sequence-major row of every plane) and copy or quantise the indexer key
+// there (key_t: dim t of the key row, for t < idx_dim).  Called by all threads of a kAppendThreads block
 // (barriers inside).
-__device__ __forceinline__ void quantize_entry(const AppendArgs &a, float e, int t, size_t slot, int64_t r,
+__device__ __forceinline__ void quantize_entry(const AppendArgs &a, float e, int t, size_t slot, uint16_t key_t,
                                                float *wave_max)
 {
     const cskv_cache &c = a.c;
@@ -349,11 +371,11 @@ __device__ __forceinline__ void quantize_entry(const AppendArgs &a, float e, int
     }
     if (c.idx_format == CSKV_IDX_FP4) {
         if (t < c.idx_dim)                      // whole waves: idx_dim is 64 or 128
-            quantize_idx_fp4(bf16_bits_to_f32(a.idx_rows[(size_t)r * c.idx_dim + t]), t,
+            quantize_idx_fp4(bf16_bits_to_f32(key_t), t,
                              reinterpret_cast<uint8_t *>(c.idx_keys) + slot * (c.idx_dim / 2),
                              c.idx_scales + slot * (c.idx_dim / 16));
     } else if (t < c.idx_dim) {
-        c.idx_keys[slot * c.idx_dim + t] = a.idx_rows[(size_t)r * c.idx_dim + t];
+        c.idx_keys[slot * c.idx_dim + t] = key_t;
     }
 }
 
@@ -369,20 +391,23 @@ __global__ __launch_bounds__(kAppendThreads) void quantize_kernel(AppendArgs a)
     const cskv_cache &c = a.c;
     const int64_t r = blockIdx.x;
     const int t = threadIdx.x;
-    const RowInfo ri = row_info<kCompress>(a, r);
-    if (ri.entry >= 0) {
-        const float e = kCompress ? a.ent[(size_t)r * kDim + t] : a.tokens[(size_t)r * kDim + t];
-        quantize_entry(a, e, t, (size_t)ri.b * c.capacity + (size_t)ri.entry, r, wave_max);
-    }
+    // every load of the block is issued before any is waited for (the
+    // entry row of a row that completes none is read and dropped)
+    const int b0 = seq_of_row(a.cu_new, c.batch, (int)r);
+    const int64_t p = c.n_tokens[b0];
+    const float ev = kCompress ? a.ent[(size_t)r * kDim + t] : a.tokens[(size_t)r * kDim + t];
+    const uint16_t key_t = a.idx_rows[(size_t)r * c.idx_dim + (t < c.idx_dim ? t : 0)];
+    const float xw = kFinalize && a.swa_ring ? a.swa_rows[(size_t)r * kDim + t] : 0.f;
+    const RowInfo ri = row_info<kCompress>(a, r, b0, p);
+    if (ri.entry >= 0) quantize_entry(a, ev, t, (size_t)ri.b * c.capacity + (size_t)ri.entry, key_t, wave_max);
     if (kFinalize) {
         const int b = (int)r;
-        const int64_t p = c.n_tokens[b];
         __syncthreads();                            // every thread has read n_tokens[b]
         const int64_t end = finalize_seq<kCompress>(a, b, p, t, kAppendThreads);
         if (a.swa_ring && end >= 1) {
             const int64_t pos = end - 1;            // the position of this row's token
             const size_t row = (size_t)b * a.swa_window + (size_t)(pos % a.swa_window);
-            const float x = a.swa_rows[(size_t)b * kDim + t];
+            const float x = xw;
             if (c.swa_format == CSKV_SWA_FP8)
                 reinterpret_cast<uint8_t *>(a.swa_ring)[row * kDim + t] = (uint8_t)e4m3_bits(x);
             else
@@ -684,14 +709,19 @@ __global__ __launch_bounds__(kAppendThreads) void quantize_planned_kernel(Append
     const int t = threadIdx.x;
     int4 pl[kQPer];
     float e[kQPer];
+    uint16_t key[kQPer];
 #pragma unroll
     for (int i = 0; i < kQPer; ++i) pl[i] = k0 + i < n ? plan[k0 + i] : make_int4(-1, 0, -1, 0);
 #pragma unroll
-    for (int i = 0; i < kQPer; ++i) e[i] = pl[i].x >= 0 ? a.ent[(size_t)pl[i].x * kDim + t] : 0.0f;
+    for (int i = 0; i < kQPer; ++i) {
+        const int64_t row = pl[i].x >= 0 ? pl[i].x : 0;
+        e[i] = a.ent[(size_t)row * kDim + t];
+        key[i] = a.idx_rows[(size_t)row * a.c.idx_dim + (t < a.c.idx_dim ? t : 0)];
+    }
 #pragma unroll
     for (int i = 0; i < kQPer; ++i)
         if (pl[i].x >= 0)                           // uniform over the block
-            quantize_entry(a, e[i], t, (size_t)pl[i].y * a.c.capacity + (size_t)pl[i].w, pl[i].x, wave_max);
+            quantize_entry(a, e[i], t, (size_t)pl[i].y * a.c.capacity + (size_t)pl[i].w, key[i], wave_max);
 }
 
 // Quantiser of a planned append for caches with fp32 group scales and bf16
