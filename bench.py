@@ -74,6 +74,10 @@ def parse():
                    "pool in a layer-group workload (reindex layers select inside it)")
     p.add_argument("--capacity", type=int, default=0, help="entries per sequence the caches are allocated "
                    "for (0: what the timed steps need); the same entries, in a larger allocation")
+    p.add_argument("--pmc-summary", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                   "COPY_WRITE_DIR", "COPY_MIB"), help="write the step's HBM-traffic summary from four "
+                   "rocprofv3 --pmc output folders (FETCH_SIZE and WRITE_SIZE of a default run and of "
+                   "--copy-probe COPY_MIB) to " + os.path.relpath(PMC_FILE, ROOT) + "; no GPU use")
     return p.parse_args()
 
 
@@ -86,6 +90,80 @@ def copy_probe(mib: int):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+
+
+# The kernels one decode step of the default workload launches, with launches
+# per step (a name, followed by its argument list, is looked for in the
+# profiler's kernel name).
+STEP_KERNELS = (("compress_kernel<4>", 1), ("quantize_kernel<true, true>", 1),
+                ("indexer_scan_kernel<128, 4, false>", 1), ("topk_bound_slice_kernel<4096, 512>", 1),
+                ("topk_bound_final_kernel", 1), ("sparse_attn_kernel<64, false, 64, false>", 1),
+                ("attn_merge_kernel", 1))
+SCAN_KERNEL = "indexer_scan_kernel<128, 4, false>"
+
+
+def _counter_means(folder: str, counter: str) -> dict:
+    """Mean Counter_Value per dispatch (summed over the rows of a dispatch) of
+    every kernel in the rocprofv3 counter-collection csv under folder."""
+    import csv
+    path = None
+    for root, _, files in os.walk(folder):
+        for f in files:
+            if f.endswith("counter_collection.csv"):
+                path = os.path.join(root, f)
+    if path is None:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    per = {}
+    with open(path) as fh:
+        for row in csv.DictReader(fh):
+            if row["Counter_Name"] != counter:
+                continue
+            key = (row["Kernel_Name"], row["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    sums = {}
+    for (name, _), v in per.items():
+        t, n = sums.get(name, (0.0, 0))
+        sums[name] = (t + v, n + 1)
+    return {name: (t / n, n) for name, (t, n) in sums.items()}
+
+
+def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib):
+    """HBM bytes per step of the default workload, from FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch) scaled by what they read for a plain copy of known size."""
+    copy_kib = int(copy_mib) * 1024
+    fetch, write = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
+    cf, cw = _counter_means(copy_fetch_dir, "FETCH_SIZE"), _counter_means(copy_write_dir, "WRITE_SIZE")
+
+    def copy_value(d):
+        vals = [v for name, (v, n) in d.items() if "copy" in name.lower()]
+        if not vals:
+            raise SystemExit("no copy kernel in the copy-probe counters")
+        return max(vals)
+
+    f_scale, w_scale = copy_kib / copy_value(cf), copy_kib / copy_value(cw)
+
+    def find(d, kname):
+        hits = [(name, v) for name, v in d.items() if kname + "(" in name]
+        if not hits:
+            raise SystemExit(f"kernel {kname} not in the counters")
+        return hits[0][1]
+
+    kernels, step = {}, 0.0
+    for kname, per_step in STEP_KERNELS:
+        (fv, fn), (wv, wn) = find(fetch, kname), find(write, kname)
+        b = (fv * f_scale + wv * w_scale) * 1024.0
+        kernels[kname] = {"fetch_kib": round(fv, 1), "write_kib": round(wv, 1), "dispatches": [fn, wn],
+                          "hbm_bytes": round(b), "per_step": per_step}
+        step += b * per_step
+    out = {"workload": "decode_64k_b32", "source_sha256": source_sha256(),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "copy_probe_mib": int(copy_mib),
+           "kernels": kernels, "step_traffic_bytes": round(step),
+           "scan_traffic_bytes": kernels[SCAN_KERNEL]["hbm_bytes"]}
+    with open(PMC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps({"step_traffic_bytes": out["step_traffic_bytes"],
+                      "scan_traffic_bytes": out["scan_traffic_bytes"]}))
 
 
 def build_replicas(ck, synth, w, cap, dev, n, idx_format=0, swa_format=0, k_format=0, prefill=False):
@@ -296,6 +374,9 @@ def main():
               "(the batch shards by sequence with no exchange, so N GPUs run N independent copies)",
               file=sys.stderr)
         sys.exit(2)
+    if a.pmc_summary:
+        pmc_summary(*a.pmc_summary)
+        return
     if a.copy_probe:
         copy_probe(a.copy_probe)
         return
