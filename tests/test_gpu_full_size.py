@@ -198,6 +198,40 @@ def test_full_decode_64k_b32(ck, orc):
         assert np.isnan(sc[b, E[b]:]).all(), f"seq {b}: rows past the entries were written"
 
 
+def test_full_decode_64k_b32_fp4_key_scores(ck, orc):
+    """The pages' FP4 indexer keys at 32 x 32,768: the appended codes and
+    E8M0 scales of every entry bit for bit against the oracle's quantisation
+    of the same key rows, and the scan's fp32 score of every entry
+    (out_scores) exactly against the oracle's scores over the keys it
+    quantised and dequantised itself (integer-valued inputs: exact sums).
+    The main entries are zero rows; the scores do not read them."""
+    w = synth.WORKLOADS["decode_64k_b32"]
+    n = w.entries
+    gc = ck.Cache.allocate(w.batch, n + 8, w.k_group, w.v_group, w.idx_dim, idx_format=1)
+    zeros = torch.zeros(n, w.dim, device="cuda")
+    keys_h = []
+    for b in range(w.batch):
+        kb = _filler_keys(w, b, n)
+        keys_h.append(host(kb))
+        cu = np.zeros(w.batch + 1, np.int32)
+        cu[b + 1:] = n
+        ck.kv_append_fp4(gc, zeros, dev(cu), None, kb)
+    st = synth.step_inputs(w, 0)
+    scores = torch.full((w.batch, gc.capacity), float("nan"), device="cuda")
+    ck.indexer_topk(gc, dev(st.q_idx[0]), w.topk, scores=scores)
+    torch.cuda.synchronize()
+    sc, codes_g, scales_g = host(scores), host(gc.idx_keys), host(gc.idx_scales)
+    for b in range(w.batch):
+        codes, scl = orc.quantize_mx16(keys_h[b].reshape(-1))
+        assert np.array_equal(codes_g[b, :n].reshape(-1), codes), f"seq {b}: FP4 key codes differ"
+        assert np.array_equal(scales_g[b, :n].reshape(-1), scl), f"seq {b}: E8M0 key scales differ"
+        deq = orc.dequantize_mx16(codes, scl, n * w.idx_dim)
+        kbits = (deq.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16).reshape(n, w.idx_dim)
+        want = orc.indexer_scores(kbits, st.q_idx[0][b])
+        assert np.array_equal(sc[b, :n].astype(np.float64), want), f"seq {b}: scores differ"
+        assert np.isnan(sc[b, n:]).all(), f"seq {b}: rows past the entries were written"
+
+
 def test_full_decode_1m_b1(ck, orc):
     """One sequence of 500,000 entries (1M tokens), group 32: the scan and the
     top-k at full length, every output against the oracle."""
