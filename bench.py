@@ -74,6 +74,9 @@ def parse():
                    "pool in a layer-group workload (reindex layers select inside it)")
     p.add_argument("--capacity", type=int, default=0, help="entries per sequence the caches are allocated "
                    "for (0: what the timed steps need); the same entries, in a larger allocation")
+    p.add_argument("--mfma-compressor", action="store_true", help="mixed workload: the prefill chunk "
+                   "through cskv_kv_append_fp4_mfma (matrix-core compressor, stated error bound) instead "
+                   "of the exact fixed-order compressor")
     p.add_argument("--pmc-summary", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                    "COPY_WRITE_DIR", "COPY_MIB"), help="write the step's HBM-traffic summary from four "
                    "rocprofv3 --pmc output folders (FETCH_SIZE and WRITE_SIZE of a default run and of "
@@ -613,6 +616,7 @@ def main():
 
 ALU_PEAK_TFLOPS = 157.3      # MI355X fp32 vector, packed FMAs: 256 CUs x 4 SIMDs x 16 lanes x 2 x 2 FLOP x 2.4 GHz
 ALU_PEAK_UNPACKED_TFLOPS = 78.6   # the same without packed fp32 (this build compiles it off)
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix cores
 MODEL_PLAN = "model_plan_64k_b32"
 
 
@@ -900,7 +904,7 @@ def main_mixed(a, ck, synth, torch):
     gws = ck.workspace(gc, w.topk, ck.OP_LAYER_GROUP, w.q_heads, w.window)
 
     def append():
-        ck.kv_append_fp4(gc, toks, cu, W, irows, ws=app_ws)
+        ck.kv_append_fp4(gc, toks, cu, W, irows, ws=app_ws, mfma=a.mfma_compressor)
 
     def decode():
         ck.layer_group_decode(gc, layers, tok, W, irow, w.topk, w.window, scale, ws=gws)
@@ -964,23 +968,35 @@ def main_mixed(a, ck, synth, torch):
     scan_us, comp_us = kern["indexer_scan"], kern["compress"]
     comp_tflops = comp_flops / (comp_us * 1e-6) / 1e12
     scan_gbps = scan_bytes / (scan_us * 1e-6) / 1e9
+    if a.mfma_compressor:
+        # algorithmic FLOP over the bf16 matrix peak; each term is issued as
+        # three bf16 products (hi*hi + hi*lo + lo*hi)
+        comp_roof = {"bound": "mfma", "achieved": round(comp_tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(comp_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "issued_flops_per_step": round(3 * comp_flops),
+                     "kernel": "compress_mfma", "flops_per_step": round(comp_flops), "avg_us": round(comp_us, 2),
+                     "timing": "hip events on the compressor's launch, separate eager pass"}
+    else:
+        comp_roof = {"bound": "alu", "achieved": round(comp_tflops, 2), "peak": ALU_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(comp_tflops / ALU_PEAK_TFLOPS, 4), "traffic": None,
+                     "peak_unpacked": ALU_PEAK_UNPACKED_TFLOPS,
+                     "frac_unpacked": round(comp_tflops / ALU_PEAK_UNPACKED_TFLOPS, 4),
+                     "kernel": "compress", "flops_per_step": round(comp_flops), "avg_us": round(comp_us, 2),
+                     "timing": "hip events on the compressor's launch, separate eager pass"}
     result = {
         "metric": "CSA2 FP4 mixed append + decode: steps/s on the ragged batch",
         "value": round(1000.0 / ms, 2), "unit": "steps/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32 compressor, bf16 scan and attention",
+        "vs_baseline": None,
+        "dtype": ("bf16x3 matrix-core compressor" if a.mfma_compressor else "f32 compressor")
+        + ", bf16 scan and attention",
         "data": "synthetic (seeded; N(0,1) tokens and entries with 1% x20 outliers, integer indexer inputs)",
         "config": {"workload": w.name, "batch": B, "token_range": list(w.ragged_tokens),
                    "entries_total": int(E.sum()), "chunk_tokens": n, "k_group": w.k_group,
                    "v_group": w.v_group, "idx_heads": w.idx_heads, "idx_dim": w.idx_dim,
                    "q_heads": w.q_heads, "topk": w.topk, "window": w.window, "launch": "eager",
-                   "layers": ["full"]},
-        "roofline": {"bound": "alu", "achieved": round(comp_tflops, 2), "peak": ALU_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(comp_tflops / ALU_PEAK_TFLOPS, 4), "traffic": None,
-                     "peak_unpacked": ALU_PEAK_UNPACKED_TFLOPS,
-                     "frac_unpacked": round(comp_tflops / ALU_PEAK_UNPACKED_TFLOPS, 4),
-                     "kernel": "compress", "flops_per_step": round(comp_flops), "avg_us": round(comp_us, 2),
-                     "timing": "hip events on the compressor's launch, separate eager pass"},
+                   "layers": ["full"], "compressor": "mfma" if a.mfma_compressor else "exact"},
+        "roofline": comp_roof,
         "roofline_scan": {"bound": "hbm", "achieved": round(scan_gbps, 1), "peak": HBM_PEAK_GBPS,
                           "unit": "GB/s", "frac": round(scan_gbps / HBM_PEAK_GBPS, 4),
                           "bytes_per_launch": round(scan_bytes), "avg_us": round(scan_us, 2)},

@@ -37,7 +37,7 @@ KERNEL_APPEND, KERNEL_SWA_APPEND, KERNEL_INDEXER_SCAN, KERNEL_TOPK_SELECT, KERNE
 KERNEL_COMPRESS = 6
 OP_INDEXER_TOPK, OP_SPARSE_ATTN, OP_LAYER_GROUP, OP_INDEXER_POOL, OP_INDEXER_IN_POOL = 1, 2, 3, 4, 5
 
-EXPORTS = ("cskv_kv_append_fp4", "cskv_append_workspace_bytes", "cskv_swa_append", "cskv_swa_append_fp8",
+EXPORTS = ("cskv_kv_append_fp4", "cskv_kv_append_fp4_mfma", "cskv_append_workspace_bytes", "cskv_swa_append", "cskv_swa_append_fp8",
            "cskv_indexer_topk",
            "cskv_indexer_topk_pool", "cskv_indexer_topk_in_pool", "cskv_sparse_attn_decode",
            "cskv_layer_group_decode", "cskv_layer_group_decode_pooled", "cskv_layer_group_decode_noalloc",
@@ -90,6 +90,7 @@ def lib():
         L = C.CDLL(_build.LIB)
         vp, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
         L.cskv_kv_append_fp4.argtypes = [vp, vp, vp, i32, vp, vp, vp, sz, vp]
+        L.cskv_kv_append_fp4_mfma.argtypes = [vp, vp, vp, i32, vp, vp, vp, sz, vp]
         L.cskv_append_workspace_bytes.argtypes = [i32, vp]
         L.cskv_append_workspace_bytes.restype = sz
         L.cskv_swa_append.argtypes = [vp, i32, i32, i32, vp, vp, i32, vp, vp]
@@ -266,13 +267,16 @@ def append_workspace(n_rows: int, w_comp: Optional[torch.Tensor], device="cuda")
 
 def kv_append_fp4(cache: Cache, tokens: torch.Tensor, cu_new: Optional[torch.Tensor],
                   w_comp: Optional[torch.Tensor], idx_rows: torch.Tensor, ws: Optional[torch.Tensor] = None,
-                  stream=None) -> None:
+                  stream=None, mfma: bool = False) -> None:
+    """cskv_kv_append_fp4, or with mfma=True cskv_kv_append_fp4_mfma (the
+    matrix-core compressor for appends of 512 rows or more)."""
     n = tokens.shape[0]
     tmp = None
     if ws is None and w_comp is not None:
         ws = tmp = append_workspace(n, w_comp, tokens.device)
     d = cache.desc()
-    _check(lib().cskv_kv_append_fp4(
+    fn = lib().cskv_kv_append_fp4_mfma if mfma else lib().cskv_kv_append_fp4
+    _check(fn(
         C.byref(d), _ptr(tokens, F32, "tokens", (n, cache.dim)),
         _ptr(cu_new, I32, "cu_new", (cache.batch + 1,)), n,
         _ptr(w_comp, F32, "w_comp", (cache.dim, 2 * cache.dim)),

@@ -307,9 +307,9 @@ size_t cskv_append_workspace_bytes(int32_t total_new, const float *w_comp)
     return need > 256 ? need : 256;
 }
 
-int cskv_kv_append_fp4(const cskv_cache *cache, const float *tokens, const int32_t *cu_new,
-                       int32_t total_new, const float *w_comp, const uint16_t *idx_rows,
-                       void *ws, size_t ws_bytes, hipStream_t stream)
+static int kv_append(const cskv_cache *cache, const float *tokens, const int32_t *cu_new,
+                     int32_t total_new, const float *w_comp, const uint16_t *idx_rows,
+                     void *ws, size_t ws_bytes, hipStream_t stream, bool mfma)
 {
     int rc = check_cache(cache);
     if (rc) return rc;
@@ -323,8 +323,23 @@ int cskv_kv_append_fp4(const cskv_cache *cache, const float *tokens, const int32
         REQUIRE(ws && aligned(ws, 256), CSKV_EWORKSPACE, "workspace NULL or not 256-byte aligned");
         REQUIRE(ws_bytes >= need, CSKV_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
     }
-    hipError_t e = cskv::launch_kv_append(*cache, tokens, cu_new, total_new, w_comp, idx_rows, ws, stream);
+    hipError_t e = cskv::launch_kv_append(*cache, tokens, cu_new, total_new, w_comp, idx_rows, ws, stream,
+                                          nullptr, nullptr, 0, mfma);
     return e == hipSuccess ? CSKV_OK : hip_fail(e, "kv_append_fp4 launch");
+}
+
+int cskv_kv_append_fp4(const cskv_cache *cache, const float *tokens, const int32_t *cu_new,
+                       int32_t total_new, const float *w_comp, const uint16_t *idx_rows,
+                       void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return kv_append(cache, tokens, cu_new, total_new, w_comp, idx_rows, ws, ws_bytes, stream, false);
+}
+
+int cskv_kv_append_fp4_mfma(const cskv_cache *cache, const float *tokens, const int32_t *cu_new,
+                            int32_t total_new, const float *w_comp, const uint16_t *idx_rows,
+                            void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return kv_append(cache, tokens, cu_new, total_new, w_comp, idx_rows, ws, ws_bytes, stream, true);
 }
 
 int cskv_swa_append(uint16_t *ring, int32_t batch, int32_t window, int32_t dim, const float *rows,

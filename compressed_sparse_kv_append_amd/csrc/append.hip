@@ -696,6 +696,125 @@ __global__ __launch_bounds__(kTcThreads) void compress_tiled_kernel(AppendArgs a
     }
 }
 
+// ------------------------------------------------- matrix-core compressor
+//
+// The same listed entries as a product on the matrix cores, for callers
+// that take a stated error instead of the fixed fp32 order [P1 §3.2: the
+// compressor is a learned projection; a chunk of them is one product
+// E = U W^T, U = the listed entries' x_even || x_odd rows].  Every fp32
+// operand is split into bf16 high and low parts (x = hi + lo + d,
+// |d| <= 2^-16 |x|) and each term is taken as hi*hi + hi*lo + lo*hi with
+// v_mfma_f32_16x16x32_bf16 (exact bf16 products, fp32 accumulation).  Per
+// output the dropped parts are at most 3.02 * 2^-16 sum_j |W_rj u_j| and an
+// fp32 sum of 3456 terms in any order adds at most 3455 * 2^-24 of the sum
+// of their magnitudes, so |e - sum_j W_rj u_j| <= 2.53e-4 sum_j |W_rj u_j|.
+//
+// W is split once per call into the workspace, in the MFMA's B-operand
+// order: for channel tile ct (16 channels) and contraction step s (32
+// terms), 64 lanes x 8 bf16, lane l holding channel 16 ct + l % 16, terms
+// 32 s + 8 (l / 16) .. + 7; the high part's 1 KB, then the low part's.  A
+// block of 4 waves takes 64 listed entries x 64 output channels; wave w owns
+// entries 16w .. 16w + 15 against all 64 channels (4 MFMA tiles): it reads
+// each W operand as one contiguous 1 KB load and splits its own U operand
+// (8 consecutive terms of its entry's row) with the hardware conversion.
+constexpr int kMcRows = 64;                        // listed entries per block
+constexpr int kMcCh = 64;                          // output channels per block
+constexpr int kMcThreads = 256;
+constexpr int kMcSteps = 2 * kDim / 32;            // 36 contraction steps of 32 terms
+constexpr int kMcChTiles = kDim / 16;              // 36 channel tiles of 16
+constexpr size_t kWsplitBytes = (size_t)kMcChTiles * kMcSteps * 2 * 1024;   // 2.65 MB
+
+typedef __bf16 mc_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float mc_f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((mc_f32x2_t{a, b}), mc_bf16x2_t));
+}
+
+// hi/lo bf16 split of 8 floats (round to nearest even both times)
+__device__ __forceinline__ void split_bf16x8(const float4 &x0, const float4 &x1, u32x4_t &hi, u32x4_t &lo)
+{
+    const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t h = cvt_bf16x2(xv[2 * i], xv[2 * i + 1]);
+        hi[i] = h;
+        lo[i] = cvt_bf16x2(xv[2 * i] - __uint_as_float(h << 16), xv[2 * i + 1] - __uint_as_float(h & 0xFFFF0000u));
+    }
+}
+
+// One thread per (channel tile, step, lane): 8 terms of one W row split.
+__global__ __launch_bounds__(256) void split_w_kernel(const float *w_comp, uint8_t *wsplit)
+{
+    const int g = blockIdx.x * 256 + threadIdx.x;
+    if (g >= kMcChTiles * kMcSteps * kWave) return;
+    const int lane = g & (kWave - 1), step = (g / kWave) % kMcSteps, ct = g / (kWave * kMcSteps);
+    const float *src = w_comp + (size_t)(16 * ct + (lane & 15)) * (2 * kDim) + 32 * step + 8 * (lane >> 4);
+    u32x4_t hi, lo;
+    split_bf16x8(*reinterpret_cast<const float4 *>(src), *reinterpret_cast<const float4 *>(src + 4), hi, lo);
+    uint8_t *dst = wsplit + ((size_t)ct * kMcSteps + step) * 2048 + 16 * lane;
+    *reinterpret_cast<u32x4_t *>(dst) = hi;
+    *reinterpret_cast<u32x4_t *>(dst + 1024) = lo;
+}
+
+__global__ __launch_bounds__(kMcThreads) void compress_mfma_kernel(AppendArgs a, const int4 *plan,
+                                                                   const int32_t *count, const uint8_t *wsplit)
+{
+    const int n = *count;
+    const int k0 = blockIdx.x * kMcRows;
+    if (k0 >= n) return;
+    const int ct0 = blockIdx.y * (kMcCh / 16);
+    const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int r16 = lane & 15, oct = lane >> 4;
+    // A operand rows: this lane's listed entry (row r16 of the wave's 16)
+    const int rec = k0 + 16 * w + r16;
+    const int4 pl = rec < n ? plan[rec] : make_int4(-1, 0, -1, 0);
+    const float *xe = pl.x < 0 ? a.tokens
+                    : pl.z >= 0 ? a.tokens + (size_t)pl.z * kDim : a.c.pending + (size_t)pl.y * kDim;
+    const float *xo = pl.x < 0 ? a.tokens : a.tokens + (size_t)pl.x * kDim;
+    const uint8_t *wb = wsplit + (size_t)ct0 * kMcSteps * 2048 + 16 * lane;
+    f32x4_t acc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float4 u0, u1;
+    u32x4_t wh[4], wl[4];
+    auto load = [&](int s) {
+        const int kk = 32 * s + 8 * oct;
+        const float *ua = kk < kDim ? xe + kk : xo + (kk - kDim);
+        u0 = *reinterpret_cast<const float4 *>(ua);
+        u1 = *reinterpret_cast<const float4 *>(ua + 4);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const uint8_t *p = wb + ((size_t)nt * kMcSteps + s) * 2048;
+            wh[nt] = *reinterpret_cast<const u32x4_t *>(p);
+            wl[nt] = *reinterpret_cast<const u32x4_t *>(p + 1024);
+        }
+    };
+    load(0);
+    for (int s = 0; s < kMcSteps; ++s) {
+        u32x4_t uh, ul, bh[4], bl[4];
+        split_bf16x8(u0, u1, uh, ul);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) { bh[nt] = wh[nt]; bl[nt] = wl[nt]; }
+        if (s + 1 < kMcSteps) load(s + 1);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            acc[nt] = mfma16x16x32(uh, bh[nt], acc[nt]);
+            acc[nt] = mfma16x16x32(uh, bl[nt], acc[nt]);
+            acc[nt] = mfma16x16x32(ul, bh[nt], acc[nt]);
+        }
+    }
+    // D layout: lane holds rows 4 oct .. 4 oct + 3 of column r16
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int rr = k0 + 16 * w + 4 * oct + v;
+        if (rr >= n) continue;
+        const int row = plan[rr].x;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) a.ent[(size_t)row * kDim + 16 * (ct0 + nt) + r16] = acc[nt][v];
+    }
+}
+
 // Quantiser of a planned append: kQPer listed entries per block, the
 // compressor's output read from the entry's input row.
 constexpr int kQPer = 4;
@@ -799,14 +918,15 @@ __global__ __launch_bounds__(kQwWaves * kWave) void quantize_planned_wave_kernel
 // Workspace of an append with the compressor: the compressor's fp32 rows,
 // then the plan records and their count.
 struct AppendWs {
-    size_t plan_off, count_off, total;
+    size_t plan_off, count_off, wsplit_off, total;
 };
 inline AppendWs append_ws_layout(int64_t total_new)
 {
     AppendWs L;
     L.plan_off = ((size_t)total_new * kDim * sizeof(float) + 255) / 256 * 256;
     L.count_off = L.plan_off + ((size_t)total_new * sizeof(int4) + 255) / 256 * 256;
-    L.total = L.count_off + 256;
+    L.wsplit_off = L.count_off + 256;
+    L.total = L.wsplit_off + (total_new >= kTiledMinRows ? kWsplitBytes : 0);
     return L;
 }
 
@@ -820,7 +940,7 @@ size_t append_workspace_bytes(int total_new)
 hipError_t launch_kv_append(const cskv_cache &c, const float *tokens, const int32_t *cu_new,
                             int total_new, const float *w_comp, const uint16_t *idx_rows,
                             void *ws, hipStream_t s, uint16_t *swa_ring, const float *swa_rows,
-                            int swa_window)
+                            int swa_window, bool mfma)
 {
     if (total_new == 0) return hipSuccess;
     AppendArgs a{c, tokens, cu_new, w_comp, idx_rows, static_cast<float *>(ws), total_new,
@@ -841,8 +961,17 @@ hipError_t launch_kv_append(const cskv_cache &c, const float *tokens, const int3
         const int64_t bound = plan_bound(total_new, c.batch);
         const int64_t row_tiles8 = ((bound + kTcRows - 1) / kTcRows + 7) / 8 * 8;
         launch_kernel(compress_plan_kernel, dim3(1), dim3(kPlanThreads), s, comp_start, nullptr, a, plan, count);
-        launch_kernel(compress_tiled_kernel, dim3((unsigned)(row_tiles8 * kTcChTiles)), dim3(kTcThreads), s,
-                      nullptr, tc.stop, a, (const int4 *)plan, (const int32_t *)count);
+        if (mfma) {
+            uint8_t *wsplit = static_cast<uint8_t *>(ws) + L.wsplit_off;
+            launch_kernel(split_w_kernel, dim3((unsigned)((kMcChTiles * kMcSteps * kWave + 255) / 256)), dim3(256),
+                          s, nullptr, nullptr, w_comp, wsplit);
+            launch_kernel(compress_mfma_kernel, dim3((unsigned)((bound + kMcRows - 1) / kMcRows), kDim / kMcCh),
+                          dim3(kMcThreads), s, nullptr, tc.stop, a, (const int4 *)plan, (const int32_t *)count,
+                          (const uint8_t *)wsplit);
+        }
+        else
+            launch_kernel(compress_tiled_kernel, dim3((unsigned)(row_tiles8 * kTcChTiles)), dim3(kTcThreads), s,
+                          nullptr, tc.stop, a, (const int4 *)plan, (const int32_t *)count);
         if (c.k_format == CSKV_KV_F32 && c.idx_format == CSKV_IDX_BF16)
             launch_kernel(quantize_planned_wave_kernel, dim3((unsigned)((bound + kQwWaves - 1) / kQwWaves)),
                           dim3(kQwWaves * kWave), s, tl.start, nullptr, a, (const int4 *)plan,

@@ -34,7 +34,7 @@ size_t append_workspace_bytes(int total_new);
 hipError_t launch_kv_append(const cskv_cache &c, const float *tokens, const int32_t *cu_new,
                             int total_new, const float *w_comp, const uint16_t *idx_rows,
                             void *ws, hipStream_t s, uint16_t *swa_ring = nullptr,
-                            const float *swa_rows = nullptr, int swa_window = 0);
+                            const float *swa_rows = nullptr, int swa_window = 0, bool mfma = false);
 // fp8: the ring holds E4M3 bytes (dim a multiple of 16), else bf16 (dim a
 // multiple of 4).
 hipError_t launch_ced_project(const uint16_t *h, int64_t rows, int d_model, const uint16_t *w, int n_out,

@@ -164,10 +164,34 @@ int cskv_kv_append_fp4(const cskv_cache *cache, const float *tokens, const int32
                        int32_t total_new, const float *w_comp, const uint16_t *idx_rows,
                        void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes of cskv_kv_append_fp4: with a compressor, the fp32
- * compressor rows (total_new * dim * 4), then one 16-byte record per row for
- * the list of rows that complete an entry (used by appends of 512 rows or
- * more) and a count, each region rounded up to 256 bytes; else a nominal 256. */
+/*
+ * cskv_kv_append_fp4 with the compressor on the matrix cores for large
+ * appends [P1 §3.2 (the compressor is a learned projection: for a prefill
+ * chunk, one product of the chunk's token pairs with W)].  Arguments,
+ * workspace, quantisation, pending tokens and status are those of
+ * cskv_kv_append_fp4, and so is the result of every append that the
+ * compressor-free or small-append paths serve (w_comp NULL, cu_new NULL, or
+ * fewer than 512 rows).  For an append of 512 rows or more with w_comp, the
+ * entry e[r] = sum_j w_comp[r][j] * u[j] is computed with every fp32 factor
+ * split into bf16 high and low parts, each term as hi*hi + hi*lo + lo*hi
+ * with fp32 accumulation in an unspecified order, so that
+ *   |e[r] - sum_j w_comp[r][j] u[j]| <= 2.53e-4 * sum_j |w_comp[r][j] u[j]|
+ * (instead of the fixed order of cskv_kv_append_fp4); the codes and scales
+ * are then exactly the quantisation of that e.  The fp32 entry rows are left
+ * in ws (row r of the append at float offset r * dim) for rows that
+ * complete an entry.
+ */
+int cskv_kv_append_fp4_mfma(const cskv_cache *cache, const float *tokens, const int32_t *cu_new,
+                            int32_t total_new, const float *w_comp, const uint16_t *idx_rows,
+                            void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes of cskv_kv_append_fp4 and cskv_kv_append_fp4_mfma: with a
+ * compressor, the fp32 compressor rows (total_new * dim * 4), then one
+ * 16-byte record per row for the list of rows that complete an entry (used
+ * by appends of 512 rows or more) and a count, each region rounded up to 256
+ * bytes, and for appends of 512 rows or more the compressor weight split
+ * into bf16 high and low parts for the matrix cores (dim * 2*dim * 4 bytes);
+ * else a nominal 256. */
 size_t cskv_append_workspace_bytes(int32_t total_new, const float *w_comp);
 
 /*

@@ -153,6 +153,11 @@ def test_call_arguments_rejected_before_launch(L):
     assert need == 4608 + 256 + 256 and L.cskv_append_workspace_bytes(2, None) == 256
     assert L.cskv_kv_append_fp4(C.byref(d), vp(0x70000), None, 2, vp(0x110000), vp(0x80000), vp(0xB0000),
                                 need - 1, None) == ck.EWORKSPACE
+    assert L.cskv_kv_append_fp4_mfma(C.byref(d), vp(0x70000), None, 2, vp(0x110000), vp(0x80000),
+                                     vp(0xB0000), need - 1, None) == ck.EWORKSPACE
+    # 512 rows and more: the same regions, then W split into bf16 high and
+    # low parts for the matrix-core compressor (576 x 1152 x 2 x 2 bytes)
+    assert L.cskv_append_workspace_bytes(512, vp(0x110000)) == 512 * 2304 + 512 * 16 + 256 + 576 * 1152 * 4
     # top-k: k out of range, too many heads, workspace too small
     ws = L.cskv_workspace_bytes(C.byref(d), ck.OP_INDEXER_TOPK, 0, 512, 0)
     assert ws > 0
