@@ -74,6 +74,8 @@ def parse():
                    "pool in a layer-group workload (reindex layers select inside it)")
     p.add_argument("--capacity", type=int, default=0, help="entries per sequence the caches are allocated "
                    "for (0: what the timed steps need); the same entries, in a larger allocation")
+    p.add_argument("--paged", type=int, default=0, metavar="PAGE", help="mixed workload: paged cache "
+                   "planes of PAGE entries, each sequence holding only the pages it needs")
     p.add_argument("--mfma-compressor", action="store_true", help="mixed workload: the prefill chunk "
                    "through cskv_kv_append_fp4_mfma (matrix-core compressor, stated error bound) instead "
                    "of the exact fixed-order compressor")
@@ -803,12 +805,26 @@ def model_cpu_baseline(synth, plan, B, T, kg, Di, Hi, Hq, K, W, dm, pool):
                       f"in {dt:.1f} s, scaled by {B}/{nseq}; cache build untimed"}
 
 
-def build_ragged(ck, synth, w, cap, dev, torch):
+def build_ragged(ck, synth, w, cap, dev, torch, page=0, need=None):
     """Entries-mode build of the ragged cache, one sequence per call; the
-    sequences' rows are drawn on host threads while earlier ones upload."""
+    sequences' rows are drawn on host threads while earlier ones upload.
+    page > 0: paged planes holding only the pages each sequence needs
+    (need[b] entries), handed out in sequence order; unmapped table entries
+    are -1."""
     import concurrent.futures as cf
     E = synth.entry_counts(w)
-    gc = ck.Cache.allocate(w.batch, cap, w.k_group, w.v_group, w.idx_dim)
+    if page:
+        max_pages = (cap + page - 1) // page
+        cap = max_pages * page
+        per = [(int(n) + page - 1) // page for n in need]
+        table = np.full((w.batch, max_pages), -1, np.int32)
+        nxt = 0
+        for b, k in enumerate(per):
+            table[b, :k] = np.arange(nxt, nxt + k)
+            nxt += k
+        gc = ck.Cache.allocate_paged(w.batch, cap, page, nxt, dev(table), w.k_group, w.v_group, w.idx_dim)
+    else:
+        gc = ck.Cache.allocate(w.batch, cap, w.k_group, w.v_group, w.idx_dim)
 
     def draw(b):
         return synth.cache_entries(w, b), synth.cache_idx_keys(w, b)
@@ -879,8 +895,15 @@ def main_mixed(a, ck, synth, torch):
         return torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).cuda()
 
     t0 = time.time()
-    gc = build_ragged(ck, synth, w, cap, dev, torch)
-    log(f"built the ragged cache ({int(E.sum())} entries over {B} sequences) in {time.time() - t0:.1f}s")
+    # entries each sequence reaches: the chunk's on sequence 0, then one per
+    # pair of decode tokens (a few spare)
+    need = E + 16
+    need[0] += n // 2
+    gc = build_ragged(ck, synth, w, cap, dev, torch, page=a.paged, need=need)
+    plane_bytes = sum(t.numel() * t.element_size() for t in (gc.k_codes, gc.k_scales, gc.v_codes, gc.v_scales,
+                                                              gc.idx_keys) if t is not None)
+    log(f"built the ragged cache ({int(E.sum())} entries over {B} sequences, "
+        f"{plane_bytes / 2**30:.2f} GiB of planes{', paged' if a.paged else ''}) in {time.time() - t0:.1f}s")
     lens = np.array([n] + [1] * (B - 1), np.int64)
     cu_h = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     toks = torch.empty(int(cu_h[-1]), w.dim, device="cuda")
@@ -995,7 +1018,8 @@ def main_mixed(a, ck, synth, torch):
                    "entries_total": int(E.sum()), "chunk_tokens": n, "k_group": w.k_group,
                    "v_group": w.v_group, "idx_heads": w.idx_heads, "idx_dim": w.idx_dim,
                    "q_heads": w.q_heads, "topk": w.topk, "window": w.window, "launch": "eager",
-                   "layers": ["full"], "compressor": "mfma" if a.mfma_compressor else "exact"},
+                   "layers": ["full"], "compressor": "mfma" if a.mfma_compressor else "exact",
+                   "page_size": a.paged, "plane_bytes": plane_bytes},
         "roofline": comp_roof,
         "roofline_scan": {"bound": "hbm", "achieved": round(scan_gbps, 1), "peak": HBM_PEAK_GBPS,
                           "unit": "GB/s", "frac": round(scan_gbps / HBM_PEAK_GBPS, 4),

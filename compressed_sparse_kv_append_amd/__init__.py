@@ -28,6 +28,7 @@ EHIP = -4
 STATUS_OVERFLOW = 1
 STATUS_ODD_ENTRY_APPEND = 2
 STATUS_BAD_STATE = 4
+STATUS_BAD_PAGE = 8
 MODE_FULL, MODE_REINDEX, MODE_REUSE = 0, 1, 2
 IDX_BF16, IDX_FP4 = 0, 1
 SWA_BF16, SWA_FP8 = 0, 1
@@ -61,7 +62,8 @@ class CacheDesc(C.Structure):
                 ("v_scales", C.c_void_p), ("idx_keys", C.c_void_p), ("n_tokens", C.c_void_p),
                 ("pending", C.c_void_p), ("status", C.c_void_p), ("idx_format", C.c_int32),
                 ("idx_scales", C.c_void_p), ("swa_format", C.c_int32), ("k_format", C.c_int32),
-                ("ratio", C.c_int32)]
+                ("ratio", C.c_int32), ("page_size", C.c_int32), ("max_pages", C.c_int32),
+                ("n_pages", C.c_int32), ("block_table", C.c_void_p)]
 
 
 class LayerDesc(C.Structure):
@@ -196,6 +198,25 @@ class Cache:
     swa_format: int = 0                          # window rings used with it: SWA_BF16, or SWA_FP8 (uint8 rings)
     k_format: int = 0                            # KV_F32, or KV_MX16 (k_group 16, uint8 scale planes)
     ratio: int = 2                               # tokens per entry: 2 (compressed pairs) or 1
+    page_size: int = 0                           # paged planes: entries per page (0: [batch][capacity])
+    n_pages: int = 0
+    block_table: Optional[torch.Tensor] = None   # paged: int32 [batch][capacity // page_size]
+
+    @classmethod
+    def allocate_paged(cls, batch, capacity, page_size, n_pages, block_table, k_group=32, v_group=0,
+                       idx_dim=128, dim=576, rope_dim=64, device="cuda", idx_format=0, swa_format=0,
+                       k_format=0, ratio=2):
+        """A cache whose planes are n_pages pages of page_size entries
+        ([n_pages][page_size][row]); block_table (int32 [batch][capacity //
+        page_size], caller-owned) names each sequence's page of every
+        page-sized run of its entries."""
+        c = cls.allocate(n_pages, page_size, k_group, v_group, idx_dim, dim, rope_dim, device, idx_format,
+                         swa_format, k_format, ratio)
+        c.batch, c.capacity = batch, capacity
+        z = lambda *s, dt: torch.zeros(*s, dtype=dt, device=device)
+        c.n_tokens, c.pending = z(batch, dt=torch.int32), z(batch, dim, dt=torch.float32)
+        c.page_size, c.n_pages, c.block_table = page_size, n_pages, block_table
+        return c
 
     @classmethod
     def allocate(cls, batch, capacity, k_group=32, v_group=0, idx_dim=128, dim=576, rope_dim=64,
@@ -222,7 +243,9 @@ class Cache:
                          self.v_group, self.idx_dim, p(self.k_codes), p(self.k_scales),
                          p(self.v_codes), p(self.v_scales), p(self.idx_keys), p(self.n_tokens),
                          p(self.pending), p(self.status), self.idx_format, p(self.idx_scales),
-                         self.swa_format, self.k_format, self.ratio)
+                         self.swa_format, self.k_format, self.ratio, self.page_size,
+                         self.capacity // self.page_size if self.page_size else 0, self.n_pages,
+                         p(self.block_table))
 
     def entry_bytes(self) -> int:
         """Bytes per entry in this cache's formats."""

@@ -73,6 +73,17 @@ int check_cache(const cskv_cache *c)
     REQUIRE(c->swa_format == CSKV_SWA_BF16 || c->swa_format == CSKV_SWA_FP8, CSKV_EUNSUPPORTED,
             "swa_format %d: CSKV_SWA_BF16 or CSKV_SWA_FP8", c->swa_format);
     REQUIRE(c->ratio == 1 || c->ratio == 2, CSKV_EUNSUPPORTED, "ratio %d: 1 or 2 tokens per entry", c->ratio);
+    REQUIRE(c->page_size >= 0, CSKV_EINVAL, "page_size %d < 0", c->page_size);
+    if (c->page_size > 0) {
+        REQUIRE(c->page_size >= 64 && (c->page_size & (c->page_size - 1)) == 0, CSKV_EUNSUPPORTED,
+                "page_size %d: a power of two of at least 64", c->page_size);
+        REQUIRE(c->max_pages >= 1 && (int64_t)c->max_pages * c->page_size == c->capacity, CSKV_EINVAL,
+                "capacity %d must equal max_pages %d x page_size %d", c->capacity, c->max_pages, c->page_size);
+        REQUIRE(c->n_pages >= 1 && c->block_table && aligned(c->block_table, 4), CSKV_EINVAL,
+                "a paged cache needs n_pages >= 1 and a 4-byte aligned block table");
+        REQUIRE((int64_t)c->n_pages * c->page_size * (c->dim / 2) < ((int64_t)1 << 31), CSKV_EUNSUPPORTED,
+                "paged planes of %d pages x %d entries pass 2 GiB", c->n_pages, c->page_size);
+    }
     REQUIRE(aligned(c->k_codes, 16) && aligned(c->k_scales, 16) && aligned(c->idx_keys, 16) &&
                 aligned(c->n_tokens, 16) && aligned(c->pending, 16) && aligned(c->status, 4) &&
                 (!c->v_codes || aligned(c->v_codes, 16)) && (!c->v_scales || aligned(c->v_scales, 16)),

@@ -399,7 +399,11 @@ __global__ __launch_bounds__(kAppendThreads) void quantize_kernel(AppendArgs a)
     const uint16_t key_t = a.idx_rows[(size_t)r * c.idx_dim + (t < c.idx_dim ? t : 0)];
     const float xw = kFinalize && a.swa_ring ? a.swa_rows[(size_t)r * kDim + t] : 0.f;
     const RowInfo ri = row_info<kCompress>(a, r, b0, p);
-    if (ri.entry >= 0) quantize_entry(a, ev, t, (size_t)ri.b * c.capacity + (size_t)ri.entry, key_t, wave_max);
+    if (ri.entry >= 0) {
+        const int64_t slot = plane_row(c, ri.b, ri.entry);
+        if (slot >= 0) quantize_entry(a, ev, t, (size_t)slot, key_t, wave_max);
+        else if (t == 0) atomicOr(c.status, CSKV_STATUS_BAD_PAGE);
+    }
     if (kFinalize) {
         const int b = (int)r;
         __syncthreads();                            // every thread has read n_tokens[b]
@@ -839,8 +843,11 @@ __global__ __launch_bounds__(kAppendThreads) void quantize_planned_kernel(Append
     }
 #pragma unroll
     for (int i = 0; i < kQPer; ++i)
-        if (pl[i].x >= 0)                           // uniform over the block
-            quantize_entry(a, e[i], t, (size_t)pl[i].y * a.c.capacity + (size_t)pl[i].w, key[i], wave_max);
+        if (pl[i].x >= 0) {                         // uniform over the block
+            const int64_t slot = plane_row(a.c, pl[i].y, pl[i].w);
+            if (slot >= 0) quantize_entry(a, e[i], t, (size_t)slot, key[i], wave_max);
+            else if (t == 0) atomicOr(a.c.status, CSKV_STATUS_BAD_PAGE);
+        }
 }
 
 // Quantiser of a planned append for caches with fp32 group scales and bf16
@@ -889,7 +896,12 @@ __global__ __launch_bounds__(kQwWaves * kWave) void quantize_planned_wave_kernel
     const float4 hi = reinterpret_cast<const float4 *>(row)[2 * lane + 1];
     const float xr = row[8 * kWave + lane];
     const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    const size_t slot = (size_t)pl.y * c.capacity + (size_t)pl.w;
+    const int64_t prow = plane_row(c, pl.y, pl.w);
+    if (prow < 0) {                                 // whole waves
+        if (lane == 0) atomicOr(c.status, CSKV_STATUS_BAD_PAGE);
+        return;
+    }
+    const size_t slot = (size_t)prow;
     const int kg = c.k_group;
     uint8_t *kc = c.k_codes + slot * (kDim / 2);
     float *ks = c.k_scales + slot * (kDim / kg);

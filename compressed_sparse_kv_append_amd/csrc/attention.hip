@@ -106,7 +106,8 @@ struct Ctx {
     int t, lane, w, col, grp;
     int ne, nw;         // entry chunks, then window chunks, of this block
     int G;              // key groups per row
-    size_t row0;        // first cache row of the sequence
+    size_t row0;        // first plane row of the sequence's buffer resources (0 for paged planes)
+    uint32_t rows;      // plane rows those resources cover (the capacity, or every paged row)
     const uint8_t *ring;    // this sequence's window rows (bf16, or FP8 E4M3 bytes)
 };
 
@@ -213,7 +214,7 @@ __device__ __forceinline__ void fetch_sparse(const AttnArgs &a, const AttnSmem &
     const int32_t *src = sm.src + lc * kSK;
     constexpr int VG = kDv / VGS;
     constexpr uint32_t kVRowBytes = SPLIT ? kDv / 2 : kD / 2;
-    const uint32_t cap = (uint32_t)c.capacity;
+    const uint32_t cap = x.rows;
     const __amdgpu_buffer_rsrc_t vr =
         make_rsrc((SPLIT ? c.v_codes : c.k_codes) + x.row0 * kVRowBytes, cap * kVRowBytes);
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(c.k_codes + x.row0 * (kD / 2), cap * (kD / 2));
@@ -688,7 +689,9 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a)
     x.ne = e1 - e0;
     x.nw = w1 - w0;
     x.G = kD / KG;
-    x.row0 = (size_t)b * c.capacity;
+    const bool paged = c.page_size > 0;
+    x.row0 = paged ? 0 : (size_t)b * c.capacity;
+    x.rows = paged ? (uint32_t)c.n_pages * (uint32_t)c.page_size : (uint32_t)c.capacity;
     x.ring = reinterpret_cast<const uint8_t *>(a.swa) + (size_t)b * a.window * kD * (W8 ? 1 : 2);
     const int64_t E = entries_of(c.n_tokens, b, c.capacity, c.ratio);
     int64_t nswa = a.swa_len ? (int64_t)a.swa_len[b] : (int64_t)c.n_tokens[b];
@@ -704,6 +707,7 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a)
             const int jj = chunk * kSK + j;
             const int32_t e = jj < a.k ? a.idx[(size_t)b * a.k + jj] : -1;
             s = (e >= 0 && e < E) ? e : -1;
+            if (paged && s >= 0) s = (int32_t)plane_row(c, b, s);    // a plane row; -1 (bad page): skipped
         } else if (j < kWK) {
             const int64_t slot = (int64_t)chunk * kWK + j;
             s = slot < nswa ? (int32_t)slot : -1;

@@ -5,6 +5,8 @@
 //   P2  "DeepSeek V1 到 V4.1-Flash，单 token 的 global KV 如何从 389,000 B 压缩到 890 B的？"
 #pragma once
 #include <hip/hip_runtime.h>
+
+#include "cskv.h"
 #include <stdint.h>
 
 namespace cskv {
@@ -161,6 +163,17 @@ __device__ __forceinline__ uint32_t score_key(float s)
     s = s + 0.0f;
     uint32_t u = __float_as_uint(s);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Plane row of entry e of sequence b: [batch][capacity] planes, or paged
+// planes [n_pages][page_size] through the sequence's block table (-1 for a
+// table entry outside [0, n_pages)).
+__device__ __forceinline__ int64_t plane_row(const cskv_cache &c, int b, int64_t e)
+{
+    if (c.page_size <= 0) return (int64_t)b * c.capacity + e;
+    const int sh = __builtin_ctz(c.page_size);
+    const int32_t pg = c.block_table[(size_t)b * c.max_pages + (e >> sh)];
+    return pg >= 0 && pg < c.n_pages ? ((int64_t)pg << sh) + (e & (c.page_size - 1)) : -1;
 }
 
 __device__ __forceinline__ int64_t entries_of(const int32_t *n_tokens, int b, int capacity, int ratio)

@@ -58,7 +58,24 @@ struct ScanArgs {
     float *out_scores = nullptr;   // full scan: [B][capacity] fp32 score of every live entry, or null
     uint32_t *tile_max = nullptr;  // full scan: [B][tile_stride] largest key of each 16-entry tile, or null
     size_t tile_stride = 0;
+    // paged planes (page_size > 0): [n_pages][page_size] rows through the
+    // block table [B][max_pages]
+    const int32_t *block_table = nullptr;
+    int page_size = 0, max_pages = 0, n_pages = 0;
 };
+
+// Paged scans resolve the pages of a block's run once, into kPageSlots
+// words of the block's LDS array (the first row of each page); the grid
+// keeps every run within kPageSlots - 2 pages.
+constexpr int kPageSlots = 64;
+
+// First plane row of page `lp` of sequence b (a table entry outside
+// [0, n_pages) reads page 0: the scan only reads).
+__device__ __forceinline__ int32_t page_row0(const ScanArgs &a, int b, int64_t lp)
+{
+    const int32_t pg = a.block_table[(size_t)b * a.max_pages + lp];
+    return (pg >= 0 && pg < a.n_pages ? pg : 0) * a.page_size;
+}
 
 typedef __attribute__((address_space(1))) void global_void_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -85,7 +102,7 @@ __device__ __forceinline__ int64_t run_length(const ScanArgs &a, int64_t n)
 // One block: a run of entries of one sequence (POOL: of pool positions);
 // wave w takes 16-key tiles w, w + 4, ...  MT: 16-head row tiles of the
 // query (1..4).
-template <int DI, int MT, bool POOL>
+template <int DI, int MT, bool POOL, bool PAGED>
 __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
 {
     constexpr int kSteps = DI / 32;            // MFMA contraction steps per key
@@ -99,9 +116,12 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
     // serialises the ring; reads of the DMA's own object are left to the
     // explicit waits below.
     constexpr int kRingBytes = kScanWaves * kRing * kTileBytes;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kRingBytes + (POOL ? 4 * kPoolChunkMax : 0)];
+    __shared__ __attribute__((aligned(16)))
+    uint8_t lds[kRingBytes + (POOL ? 4 * kPoolChunkMax : 0) + (PAGED && !POOL ? 4 * kPageSlots : 0)];
     auto ring = reinterpret_cast<uint8_t (*)[kRing][kTileBytes]>(lds);
     int32_t *pool_rows = reinterpret_cast<int32_t *>(lds + kRingBytes);
+    int32_t *pool_prow = pool_rows + kPoolChunkMax / 2;                     // PAGED and POOL
+    int32_t *page_rows = reinterpret_cast<int32_t *>(lds + kRingBytes);     // PAGED, not POOL
 
     const int b = blockIdx.y;
     const int64_t E = entries_of(a.n_tokens, b, a.capacity, a.ratio);
@@ -113,22 +133,33 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
     const int64_t e_end = N < e_begin + run ? N : e_begin + run;
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     const int col = lane & 15, grp = lane >> 4;
+    // PAGED: rows are plane rows; a tile's 16 entries lie in one page
+    const int sh = PAGED ? __builtin_ctz(a.page_size) : 0;
+    const int64_t first_page = e_begin >> sh;
     if constexpr (POOL) {
-        // entry of every position of this block's run (-1: none); rows
-        // without an entry read row 0 and are dropped
+        // entry of every position of this block's run (-1: none) and, PAGED,
+        // its plane row in the second half of the array (the run is at most
+        // half as long); rows without an entry read row 0 and are dropped
         const int32_t *pl = a.pool + (size_t)b * a.pool_blocks;
         for (int i = threadIdx.x; i < e_end - e_begin; i += kScanThreads) {
             const int64_t p = e_begin + i;
             const int32_t blk = pl[p / a.block];
             const int64_t e = blk >= 0 ? (int64_t)blk * a.block + p % a.block : -1;
             pool_rows[i] = e < E ? (int32_t)e : -1;
+            if constexpr (PAGED)
+                pool_prow[i] = e >= 0 && e < E ? page_row0(a, b, e >> sh) + (int32_t)(e & (a.page_size - 1)) : 0;
         }
+        __syncthreads();
+    } else if constexpr (PAGED) {
+        const int n_pg = (int)(((e_end - 1) >> sh) - first_page + 1);
+        for (int j = threadIdx.x; j < n_pg && j < kPageSlots; j += kScanThreads)
+            page_rows[j] = page_row0(a, b, first_page + j);
         __syncthreads();
     }
 
     const int n_tiles = (int)((e_end - e_begin + 15) / 16);
     const int my_n = n_tiles > w ? (n_tiles - w + kScanWaves - 1) / kScanWaves : 0;
-    const uint8_t *kb = reinterpret_cast<const uint8_t *>(a.keys + (size_t)b * a.capacity * DI);
+    const uint8_t *kb = reinterpret_cast<const uint8_t *>(a.keys + (PAGED ? 0 : (size_t)b * a.capacity * DI));
     uint32_t *ok = a.out_keys + (size_t)b * a.key_stride;
 
     // Tile i goes straight from HBM into LDS slot i % kRing with coalesced
@@ -147,9 +178,14 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
             const int u = 64 * s + lane, r = u / kChunks, p = u % kChunks, c = p ^ (r % kChunks);
             int64_t e = t0 + r;
             if (tail) e = e < e_end ? e : e_end - 1;
-            if constexpr (POOL) {
+            if constexpr (POOL && PAGED) {
+                e = pool_prow[e - e_begin];
+            } else if constexpr (POOL) {
                 const int32_t pe = pool_rows[e - e_begin];
                 e = pe >= 0 ? pe : 0;
+            } else if constexpr (PAGED) {
+                const int64_t j = (e >> sh) - first_page;
+                e = page_rows[j < kPageSlots ? j : kPageSlots - 1] + (e & (a.page_size - 1));
             }
             __builtin_amdgcn_global_load_lds((global_void_t *)(kb + (size_t)e * kRowBytes + 16 * c),
                                              (lds_void_t *)(slot + 1024 * s), 16, 0, kNonTemporal);
@@ -249,7 +285,7 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
 // is converted to bf16 by the hardware FP4 conversion, which applies the
 // group's power-of-two scale exactly, and goes through the same bf16 MFMA
 // and epilogue as the bf16 scan.
-template <int DI, int MT, bool POOL>
+template <int DI, int MT, bool POOL, bool PAGED>
 __global__ __launch_bounds__(kScanThreads) void indexer_scan_fp4_kernel(ScanArgs a)
 {
     constexpr int kSteps = DI / 32;
@@ -266,10 +302,13 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_fp4_kernel(ScanArgs
     // One LDS array (see the bf16 scan): the wave rings, the head weights (0
     // past the heads), then (POOL) the entry of each position of the run.
     constexpr int kRingBytes = kScanWaves * kRing * (kTileCode + kTileScale);
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kRingBytes + 64 * MT + (POOL ? 4 * kPoolChunkMax : 0)];
+    __shared__ __attribute__((aligned(16)))
+    uint8_t lds[kRingBytes + 64 * MT + (POOL ? 4 * kPoolChunkMax : 0) + (PAGED && !POOL ? 4 * kPageSlots : 0)];
     auto ring = reinterpret_cast<uint8_t (*)[kRing][kTileCode + kTileScale]>(lds);
     float *hws = reinterpret_cast<float *>(lds + kRingBytes);
     int32_t *pool_rows = reinterpret_cast<int32_t *>(lds + kRingBytes + 64 * MT);
+    int32_t *pool_prow = pool_rows + kPoolChunkMax / 2;                             // PAGED and POOL
+    int32_t *page_rows = reinterpret_cast<int32_t *>(lds + kRingBytes + 64 * MT);   // PAGED, not POOL
 
     const int b = blockIdx.y;
     const int64_t E = entries_of(a.n_tokens, b, a.capacity, a.ratio);
@@ -280,6 +319,9 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_fp4_kernel(ScanArgs
     const int64_t e_end = N < e_begin + run ? N : e_begin + run;
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     const int col = lane & 15, grp = lane >> 4;
+    // PAGED: rows are plane rows; a tile's 64 entries lie in one page
+    const int sh = PAGED ? __builtin_ctz(a.page_size) : 0;
+    const int64_t first_page = e_begin >> sh;
     if constexpr (POOL) {
         const int32_t *pl = a.pool + (size_t)b * a.pool_blocks;
         for (int i = threadIdx.x; i < e_end - e_begin; i += kScanThreads) {
@@ -287,7 +329,13 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_fp4_kernel(ScanArgs
             const int32_t blk = pl[p / a.block];
             const int64_t e = blk >= 0 ? (int64_t)blk * a.block + p % a.block : -1;
             pool_rows[i] = e < E ? (int32_t)e : -1;
+            if constexpr (PAGED)
+                pool_prow[i] = e >= 0 && e < E ? page_row0(a, b, e >> sh) + (int32_t)(e & (a.page_size - 1)) : 0;
         }
+    } else if constexpr (PAGED) {
+        const int n_pg = (int)(((e_end - 1) >> sh) - first_page + 1);
+        for (int j = threadIdx.x; j < n_pg && j < kPageSlots; j += kScanThreads)
+            page_rows[j] = page_row0(a, b, first_page + j);
     }
     if (threadIdx.x < 16 * MT) {
         const int h = threadIdx.x;
@@ -297,16 +345,21 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_fp4_kernel(ScanArgs
 
     const int n_tiles = (int)((e_end - e_begin + kTileKeys - 1) / kTileKeys);
     const int my_n = n_tiles > w ? (n_tiles - w + kScanWaves - 1) / kScanWaves : 0;
-    const uint8_t *kb = reinterpret_cast<const uint8_t *>(a.keys) + (size_t)b * a.capacity * kCodeBytes;
-    const uint8_t *sb = a.idx_scales + (size_t)b * a.capacity * kScaleBytes;
+    const uint8_t *kb = reinterpret_cast<const uint8_t *>(a.keys) + (PAGED ? 0 : (size_t)b * a.capacity * kCodeBytes);
+    const uint8_t *sb = a.idx_scales + (PAGED ? 0 : (size_t)b * a.capacity * kScaleBytes);
 
     // cache row of position e (clamped into the run; positions without an
     // entry read row 0 and are dropped)
     auto row_of = [&](int64_t e) -> int64_t {
         e = e < e_end ? e : e_end - 1;
-        if constexpr (POOL) {
+        if constexpr (POOL && PAGED) {
+            return pool_prow[e - e_begin];
+        } else if constexpr (POOL) {
             const int32_t pe = pool_rows[e - e_begin];
             return pe >= 0 ? pe : 0;
+        } else if constexpr (PAGED) {
+            const int64_t j = (e >> sh) - first_page;
+            return page_rows[j < kPageSlots ? j : kPageSlots - 1] + (e & (a.page_size - 1));
         } else {
             return e;
         }
@@ -454,37 +507,44 @@ static int scan_chunk(int batch, size_t n, size_t cap, int per_cu)
     return (int)(chunk < cap ? chunk : cap);
 }
 
-template <bool POOL>
-static void scan_dispatch(const cskv_cache &c, int heads, const ScanArgs &sa, dim3 grid, hipStream_t s)
+template <bool POOL, bool PAGED>
+static void scan_dispatch_t(const cskv_cache &c, int heads, const ScanArgs &sa, dim3 grid, hipStream_t s)
 {
     const int mt = (heads + 15) / 16;
     const TimedLaunch ts = timer_take(CSKV_KERNEL_INDEXER_SCAN);
     auto scan = [&](auto kernel) { launch_kernel(kernel, grid, dim3(kScanThreads), s, ts.start, ts.stop, sa); };
     if (c.idx_format == CSKV_IDX_FP4) {
         if (c.idx_dim == 128) {
-            if (mt == 4) scan(indexer_scan_fp4_kernel<128, 4, POOL>);
-            else if (mt == 3) scan(indexer_scan_fp4_kernel<128, 3, POOL>);
-            else if (mt == 2) scan(indexer_scan_fp4_kernel<128, 2, POOL>);
-            else scan(indexer_scan_fp4_kernel<128, 1, POOL>);
+            if (mt == 4) scan(indexer_scan_fp4_kernel<128, 4, POOL, PAGED>);
+            else if (mt == 3) scan(indexer_scan_fp4_kernel<128, 3, POOL, PAGED>);
+            else if (mt == 2) scan(indexer_scan_fp4_kernel<128, 2, POOL, PAGED>);
+            else scan(indexer_scan_fp4_kernel<128, 1, POOL, PAGED>);
         } else {
-            if (mt == 4) scan(indexer_scan_fp4_kernel<64, 4, POOL>);
-            else if (mt == 3) scan(indexer_scan_fp4_kernel<64, 3, POOL>);
-            else if (mt == 2) scan(indexer_scan_fp4_kernel<64, 2, POOL>);
-            else scan(indexer_scan_fp4_kernel<64, 1, POOL>);
+            if (mt == 4) scan(indexer_scan_fp4_kernel<64, 4, POOL, PAGED>);
+            else if (mt == 3) scan(indexer_scan_fp4_kernel<64, 3, POOL, PAGED>);
+            else if (mt == 2) scan(indexer_scan_fp4_kernel<64, 2, POOL, PAGED>);
+            else scan(indexer_scan_fp4_kernel<64, 1, POOL, PAGED>);
         }
         return;
     }
     if (c.idx_dim == 128) {
-        if (mt == 4) scan(indexer_scan_kernel<128, 4, POOL>);
-        else if (mt == 3) scan(indexer_scan_kernel<128, 3, POOL>);
-        else if (mt == 2) scan(indexer_scan_kernel<128, 2, POOL>);
-        else scan(indexer_scan_kernel<128, 1, POOL>);
+        if (mt == 4) scan(indexer_scan_kernel<128, 4, POOL, PAGED>);
+        else if (mt == 3) scan(indexer_scan_kernel<128, 3, POOL, PAGED>);
+        else if (mt == 2) scan(indexer_scan_kernel<128, 2, POOL, PAGED>);
+        else scan(indexer_scan_kernel<128, 1, POOL, PAGED>);
     } else {
-        if (mt == 4) scan(indexer_scan_kernel<64, 4, POOL>);
-        else if (mt == 3) scan(indexer_scan_kernel<64, 3, POOL>);
-        else if (mt == 2) scan(indexer_scan_kernel<64, 2, POOL>);
-        else scan(indexer_scan_kernel<64, 1, POOL>);
+        if (mt == 4) scan(indexer_scan_kernel<64, 4, POOL, PAGED>);
+        else if (mt == 3) scan(indexer_scan_kernel<64, 3, POOL, PAGED>);
+        else if (mt == 2) scan(indexer_scan_kernel<64, 2, POOL, PAGED>);
+        else scan(indexer_scan_kernel<64, 1, POOL, PAGED>);
     }
+}
+
+template <bool POOL>
+static void scan_dispatch(const cskv_cache &c, int heads, const ScanArgs &sa, dim3 grid, hipStream_t s)
+{
+    if (c.page_size > 0) scan_dispatch_t<POOL, true>(c, heads, sa, grid, s);
+    else scan_dispatch_t<POOL, false>(c, heads, sa, grid, s);
 }
 
 void launch_indexer_scan(const cskv_cache &c, const uint16_t *q_idx, int heads, const float *head_w,
@@ -496,10 +556,17 @@ void launch_indexer_scan(const cskv_cache &c, const uint16_t *q_idx, int heads, 
     // 64-entry runs fit in the capacity)
     const int per_seq = scan_blocks_per_seq(c.batch, scan_blocks_per_cu(c));
     const size_t max_runs = ((size_t)c.capacity + 63) / 64;
-    const unsigned gx = (unsigned)((size_t)per_seq < max_runs ? (size_t)per_seq : max_runs);
+    size_t gxs = (size_t)per_seq < max_runs ? (size_t)per_seq : max_runs;
+    if (c.page_size > 0) {
+        // paged: every run within kPageSlots - 2 pages (a run may start inside a page)
+        const size_t span = (size_t)(kPageSlots - 3) * c.page_size;
+        const size_t need = ((size_t)c.capacity + span - 1) / span;
+        gxs = gxs > need ? gxs : need;
+    }
+    const unsigned gx = (unsigned)gxs;
     ScanArgs sa{c.idx_keys, c.n_tokens, q_idx, head_w, keys, c.capacity, heads, 0, score_key_stride(c),
                 block_keys, block_stride, block, nullptr, 0, nullptr, c.idx_scales, c.ratio, out_scores,
-                tile_max, tile_stride};
+                tile_max, tile_stride, c.block_table, c.page_size, c.max_pages, c.n_pages};
     dim3 grid(gx, (unsigned)c.batch);
     scan_dispatch<false>(c, heads, sa, grid, s);
 }
@@ -508,9 +575,13 @@ void launch_pool_scan(const cskv_cache &c, const uint16_t *q_idx, int heads, con
                       const int32_t *pool, int pool_blocks, int block, uint2 *pairs, hipStream_t s)
 {
     const size_t n = (size_t)pool_blocks * block;
-    const int chunk = scan_chunk(c.batch, n, kPoolChunkMax, scan_blocks_per_cu(c));
+    // paged: half the positions per block, the other half of the block's
+    // position array holds their plane rows
+    const int chunk = scan_chunk(c.batch, n, c.page_size > 0 ? kPoolChunkMax / 2 : kPoolChunkMax,
+                                 scan_blocks_per_cu(c));
     ScanArgs sa{c.idx_keys, c.n_tokens, q_idx, head_w, nullptr, c.capacity, heads, chunk, 0,
-                nullptr, 0, block, pool, pool_blocks, pairs, c.idx_scales, c.ratio};
+                nullptr, 0, block, pool, pool_blocks, pairs, c.idx_scales, c.ratio, nullptr,
+                nullptr, 0, c.block_table, c.page_size, c.max_pages, c.n_pages};
     dim3 grid((unsigned)((n + chunk - 1) / chunk), (unsigned)c.batch);
     scan_dispatch<true>(c, heads, sa, grid, s);
 }

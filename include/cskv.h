@@ -56,6 +56,7 @@ extern "C" {
 #define CSKV_STATUS_OVERFLOW 1           /* an append would pass capacity       */
 #define CSKV_STATUS_ODD_ENTRY_APPEND 2   /* entries-mode append with a pending token */
 #define CSKV_STATUS_BAD_STATE 4          /* negative n_tokens or cu_new inconsistent with total_new */
+#define CSKV_STATUS_BAD_PAGE 8           /* an append met a block-table entry outside [0, n_pages) */
 
 /*
  * The shared cache of one layer group (device planes, caller-owned).
@@ -92,6 +93,24 @@ extern "C" {
  * Supported here: dim 576, rope_dim 64, k_group 32 or 64, v_group 0, 32, 64
  * or 128 (CSKV_KV_MX16: k_group 16, v_group 0 or 16), idx_dim 64 or 128,
  * capacity <= 2^26.
+ *
+ * Paged planes [P2 三、"突破六：系统层，不改模型改部署" (KV allocated in fixed-
+ * size pages, as PagedAttention does, so ragged sequences share one pool)]:
+ * with page_size > 0 every entry plane (k/v codes and scales, indexer keys
+ * and scales) is [n_pages][page_size][row] instead of [batch][capacity][row],
+ * and entry e of sequence b lives in row
+ *   block_table[b][e / page_size] * page_size + e % page_size
+ * of every plane.  page_size is a power of two, at least 64;
+ * capacity = max_pages * page_size (the logical entries per sequence);
+ * block_table is device i32 [batch][max_pages]; each plane must stay under
+ * 2 GiB.  The table must name a page in [0, n_pages) for every page an
+ * append writes or a read covers (entries below n_tokens / ratio); an append
+ * that meets any other value writes nothing for that entry and sets
+ * CSKV_STATUS_BAD_PAGE; a read through one is no error (the indexer scores
+ * the entry from page 0's rows, attention leaves the entry out).  The
+ * caller owns the table and may share pages between sequences only for
+ * entries that no append writes.  page_size 0: the dense layout above
+ * (max_pages, n_pages and block_table unused).
  */
 #define CSKV_IDX_BF16 0
 #define CSKV_IDX_FP4 1
@@ -128,6 +147,10 @@ typedef struct cskv_cache {
     int32_t ratio;           /* tokens per entry: 2 (token pairs compressed into one
                                 entry) or 1 (one entry per token, as the decoder cache
                                 fed by cskv_ced_project); entries = n_tokens / ratio */
+    int32_t page_size;       /* entries per page (a power of two >= 64), or 0: dense planes */
+    int32_t max_pages;       /* paged: block-table columns per sequence */
+    int32_t n_pages;         /* paged: pages in every plane */
+    const int32_t *block_table;  /* paged: device i32 [batch][max_pages] */
 } cskv_cache;
 
 /*

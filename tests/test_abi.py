@@ -48,7 +48,8 @@ def test_entry_bytes(L):
 def _desc(**over):
     d = dict(batch=2, capacity=64, dim=576, rope_dim=64, k_group=32, v_group=0, idx_dim=64,
              k_codes=0x10000, k_scales=0x20000, v_codes=None, v_scales=None, idx_keys=0x30000,
-             n_tokens=0x40000, pending=0x50000, status=0x60000, idx_format=0, idx_scales=None, swa_format=0, k_format=0, ratio=2)
+             n_tokens=0x40000, pending=0x50000, status=0x60000, idx_format=0, idx_scales=None, swa_format=0,
+             k_format=0, ratio=2, page_size=0, max_pages=0, n_pages=0, block_table=None)
     d.update(over)
     return ck.CacheDesc(*[d[f] for f, _ in ck.CacheDesc._fields_])
 
@@ -255,3 +256,21 @@ def test_noalloc_step_beyond_its_scratch_is_refused(L):
     rc = L.cskv_layer_group_decode_noalloc(C.byref(small), None, 1, None, None, None, 64, 64, 512, 128,
                                            C.c_float(0.04), None)
     assert rc == ck.EINVAL and "layers" in _err(L), (rc, _err(L))
+
+
+def test_paged_cache_descriptor_rejected_before_launch(L):
+    """A paged cache: a power-of-two page of at least 64 entries, capacity =
+    max_pages x page_size, a block table, and planes under 2 GiB."""
+    vp = C.c_void_p
+    ok = dict(capacity=256, page_size=64, max_pages=4, n_pages=8, block_table=0x70000)
+    tok, idx = vp(0x80000), vp(0x90000)
+    def append(**over):
+        d = _desc(**{**ok, **over})
+        return L.cskv_kv_append_fp4(C.byref(d), tok, None, 2, None, idx, None, 0, None)
+    assert append(page_size=48, max_pages=5, capacity=240) == ck.EUNSUPPORTED    # not a power of two
+    assert append(page_size=32, max_pages=8) == ck.EUNSUPPORTED                  # below 64
+    assert append(max_pages=3) == ck.EINVAL                                      # capacity != pages x size
+    assert append(block_table=None) == ck.EINVAL
+    assert append(n_pages=0) == ck.EINVAL
+    assert append(page_size=1 << 20, max_pages=1, capacity=1 << 20, n_pages=8) == ck.EUNSUPPORTED   # > 2 GiB
+    assert append(page_size=-64) == ck.EINVAL
