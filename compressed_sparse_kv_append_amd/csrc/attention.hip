@@ -190,14 +190,6 @@ struct WindowRegs {
     u32x4_t p[9];       // 64 rows x 72 pieces of 16 bytes
 };
 
-constexpr uint32_t kMasked = 0x80000000u;    // offset past the end of every resource
-constexpr int kRsrcWord3 = 0x00020000;       // raw 32-bit buffer, gfx9 family
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
-}
-
 __device__ __forceinline__ uint32_t row_off(int32_t e, uint32_t row_bytes)
 {
     return e >= 0 ? (uint32_t)e * row_bytes : kMasked;

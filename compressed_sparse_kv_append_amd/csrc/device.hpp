@@ -176,6 +176,17 @@ __device__ __forceinline__ int64_t plane_row(const cskv_cache &c, int b, int64_t
     return pg >= 0 && pg < c.n_pages ? ((int64_t)pg << sh) + (e & (c.page_size - 1)) : -1;
 }
 
+// Raw buffer resources: a load or store whose offset (plus its size) passes
+// num_records does not touch memory (a load returns zeros), so a lane can be
+// masked by its offset alone and every lane executes the same instructions.
+constexpr uint32_t kMasked = 0x80000000u;    // offset past the end of every resource
+constexpr int kRsrcWord3 = 0x00020000;       // raw 32-bit buffer, gfx9 family
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
+}
+
 __device__ __forceinline__ int64_t entries_of(const int32_t *n_tokens, int b, int capacity, int ratio)
 {
     int64_t e = (int64_t)n_tokens[b] / ratio;

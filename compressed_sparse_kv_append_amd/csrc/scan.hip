@@ -30,7 +30,7 @@ namespace {
 constexpr int kScanThreads = 256;   // 4 waves
 constexpr int kScanWaves = kScanThreads / kWave;
 constexpr int kRing = 2;            // 16-key tiles in flight per wave (LDS slots)
-constexpr int kScanBlocksPerCU = 3; // what registers (<= 168) and LDS (32 KB) allow
+constexpr int kScanBlocksPerCU = 3; // blocks per CU the kernels are built for (<= 168 registers a lane)
 
 struct ScanArgs {
     const uint16_t *keys;      // idx_keys plane
@@ -88,6 +88,123 @@ constexpr int kNonTemporal = 2;     // cache policy of the streaming loads
 
 constexpr int kPoolChunkMax = 4096;   // pool positions per block of the pooled scan
 
+// Vector memory counter.  On this GPU stores count in vmcnt beside loads, so
+// a ring wait that counts only the later tiles' loads would also wait for
+// the stores issued after them, and with them for the next tile.  Every
+// iteration of a scan loop therefore issues the same number of buffer stores
+// from every lane (a masked lane gets an offset past its resource, an unused
+// output a resource of no bytes).  With a ring of two, iteration i - 1
+// issues tile i + 1's loads and its own stores after tile i's loads, in
+// whichever order, so at the top of iteration i >= 1 tile i has landed once
+// at most loads + stores are pending; tile 0 is waited for before the loop.
+static_assert(kRing == 2, "the ring waits below count a ring of two tiles");
+constexpr int scan_wait(int loads_per_tile, int stores) { return loads_per_tile + stores; }
+
+__device__ __forceinline__ void store_b32(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+}
+
+// ReLU in one integer max: a float with its sign bit set (a negative value,
+// -0) has a negative bit pattern and becomes +0, any other stays as it is.
+// (fmaxf would first quiet a possible signalling NaN: two instructions.)
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Cross-lane reductions on the VALU (DPP and lane swaps, no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Largest value of each 16-lane row, in every lane of the row (rotations).
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t m)
+{
+    m = max(m, dpp_u32<0x128>(m));
+    m = max(m, dpp_u32<0x124>(m));
+    m = max(m, dpp_u32<0x122>(m));
+    return max(m, dpp_u32<0x121>(m));
+}
+
+// Largest value of each aligned group of g lanes (g = 0, 1, 2, 4, 8 or 16),
+// in every lane of the group: lane ^ 1 and lane ^ 2 by quad permutes, then
+// the other quad of the eight and the other eight of the row by mirrors.
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t m, int g)
+{
+    if (g >= 2) m = max(m, dpp_u32<0xB1>(m));
+    if (g >= 4) m = max(m, dpp_u32<0x4E>(m));
+    if (g >= 8) m = max(m, dpp_u32<0x141>(m));
+    if (g >= 16) m = max(m, dpp_u32<0x140>(m));
+    return m;
+}
+
+// (p_l + p_(l^16)) + (p_(l^32) + p_(l^48)): the sum over the four 16-lane
+// rows at each column, in every lane (two lane swaps).
+__device__ __forceinline__ float sum_rows(float p)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+    const float s2 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(s2), __float_as_uint(s2), false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// The outputs of a block's sequence as buffer resources (an unused output:
+// no bytes).
+struct ScanOut {
+    __amdgpu_buffer_rsrc_t keys, scores, tmax, bkeys;
+    int bsh;                    // log2 of the pool block (0 when none)
+};
+
+template <bool POOL>
+__device__ __forceinline__ ScanOut scan_out(const ScanArgs &a, int b)
+{
+    ScanOut o;
+    if constexpr (POOL) {
+        const size_t n = (size_t)a.pool_blocks * a.block;
+        o.keys = make_rsrc(a.out_pairs + (size_t)b * n, (uint32_t)(n * sizeof(uint2)));
+        o.scores = o.tmax = o.bkeys = o.keys;
+    } else {
+        o.keys = make_rsrc(a.out_keys ? a.out_keys + (size_t)b * a.key_stride : nullptr,
+                           a.out_keys ? (uint32_t)(a.key_stride * 4) : 0u);
+        o.scores = make_rsrc(a.out_scores ? a.out_scores + (size_t)b * a.capacity : nullptr,
+                             a.out_scores ? (uint32_t)a.capacity * 4u : 0u);
+        o.tmax = make_rsrc(a.tile_max ? a.tile_max + (size_t)b * a.tile_stride : nullptr,
+                           a.tile_max ? (uint32_t)(a.tile_stride * 4) : 0u);
+        o.bkeys = make_rsrc(a.block_keys ? a.block_keys + (size_t)b * a.block_stride : nullptr,
+                            a.block_keys ? (uint32_t)(a.block_stride * 4) : 0u);
+    }
+    o.bsh = a.block > 1 ? __builtin_ctz(a.block) : 0;
+    return o;
+}
+
+// The epilogue of one lane for entry (pool position) e of the block's run,
+// score p (live: e is a position of the run this lane reports; pe: the
+// pooled scan's entry at e, read from LDS before the ring's refill): kStores
+// buffer stores from every lane whatever is live (no branch around them).
+template <bool POOL>
+__device__ __forceinline__ void scan_store(const ScanArgs &a, const ScanOut &o, int32_t pe, int64_t e, bool live,
+                                           bool tile_lane, float p)
+{
+    if constexpr (POOL) {
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t v = pe >= 0 ? u32x2_t{score_key(p), (uint32_t)pe} : u32x2_t{0u, 0xFFFFFFFFu};
+        __builtin_amdgcn_raw_buffer_store_b64(v, o.keys, (int)(live ? (uint32_t)e * 8u : kMasked), 0, 0);
+    } else {
+        const uint32_t key = score_key(p);
+        const uint32_t off = live ? (uint32_t)e * 4u : kMasked;
+        store_b32(o.keys, off, key);
+        store_b32(o.scores, off, __float_as_uint(p + 0.0f));
+        // largest key of each 16-entry tile (entries past the end count as
+        // key 0), written by the tile's first lane
+        const uint32_t lk = live ? key : 0u;
+        store_b32(o.tmax, tile_lane ? (uint32_t)(e >> 4) * 4u : kMasked, row_max_u32(lk));
+        // largest key of each pool block (tiles start on block boundaries)
+        const bool first = live && (e & ((1 << o.bsh) - 1)) == 0;
+        store_b32(o.bkeys, first ? (uint32_t)(e >> o.bsh) * 4u : kMasked, group_max_u32(lk, a.block));
+    }
+}
+template <bool POOL> constexpr int kStores = POOL ? 1 : 4;
+
 // Run of block blockIdx.x over the n positions of its sequence: the pooled
 // scan's fixed run length, or (full scan) the sequence's live entries cut
 // into gridDim.x runs of a multiple of 64, so a cache allocated far beyond
@@ -103,7 +220,7 @@ __device__ __forceinline__ int64_t run_length(const ScanArgs &a, int64_t n)
 // wave w takes 16-key tiles w, w + 4, ...  MT: 16-head row tiles of the
 // query (1..4).
 template <int DI, int MT, bool POOL, bool PAGED>
-__global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
+__global__ __launch_bounds__(kScanThreads, kScanBlocksPerCU) void indexer_scan_kernel(ScanArgs a)
 {
     constexpr int kSteps = DI / 32;            // MFMA contraction steps per key
     constexpr int kRowBytes = 2 * DI;
@@ -160,7 +277,9 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
     const int n_tiles = (int)((e_end - e_begin + 15) / 16);
     const int my_n = n_tiles > w ? (n_tiles - w + kScanWaves - 1) / kScanWaves : 0;
     const uint8_t *kb = reinterpret_cast<const uint8_t *>(a.keys + (PAGED ? 0 : (size_t)b * a.capacity * DI));
-    uint32_t *ok = a.out_keys + (size_t)b * a.key_stride;
+    const ScanOut out = scan_out<POOL>(a, b);
+    constexpr int kS = kStores<POOL>;
+    constexpr int KI = kInst;                  // loads per tile
 
     // Tile i goes straight from HBM into LDS slot i % kRing with coalesced
     // 16-byte loads (instruction s covers bytes 1024 s .. 1024 s + 1023 of the
@@ -192,12 +311,10 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
         }
     };
 
-#pragma unroll
-    for (int i = 0; i < kRing; ++i) issue(i);
-
-    // the query is loaded while the first tiles are in flight
     // Indexer query as MFMA A operands: row = head, contraction slots
     // 8*grp..8*grp+7 of each 32-dim step.  Missing heads: zero rows, weight 0.
+    // It is loaded before the ring's first tiles are issued, so the wait for
+    // it leaves those tiles in flight.
     u32x4_t qa[MT][kSteps];
     float hw[MT][4];
 #pragma unroll
@@ -216,10 +333,12 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
             hw[mt][v] = hrow < a.heads ? (a.head_w ? a.head_w[(size_t)b * a.heads + hrow] : 1.0f) : 0.0f;
         }
     }
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) issue(i);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(KI * (kRing - 1)));             // tile 0 has landed
 
     for (int i = 0; i < my_n; ++i) {
-        // tile i has landed once at most the later tiles' loads are pending
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kInst * (kRing - 1)));
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(scan_wait(KI, kS)));       // tile i has landed
         const uint8_t *slot = &ring[w][i % kRing][0];
         u32x4_t bop[kSteps];
 #pragma unroll
@@ -227,6 +346,10 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
             const int p = (4 * s + grp) ^ (col % kChunks);
             bop[s] = *reinterpret_cast<const u32x4_t *>(slot + 16 * (col * kChunks + p));
         }
+        // lanes 0-15 report the tile's 16 entries
+        const int64_t e = e_begin + (int64_t)(w + kScanWaves * i) * 16 + lane;
+        const bool live = lane < 16 && e < e_end;
+        const int32_t pe = POOL ? pool_rows[live ? e - e_begin : 0] : 0;
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);      // slot read before it is refilled
         issue(i + kRing);
         f32x4_t acc[MT];
@@ -240,35 +363,9 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) part += hw[mt][v] * fmaxf(acc[mt][v], 0.f);
-        part += __shfl_xor(part, 16);
-        part += __shfl_xor(part, 32);
-        const int64_t e = e_begin + (int64_t)(w + kScanWaves * i) * 16 + lane;
-        if constexpr (POOL) {
-            if (lane < 16 && e < e_end) {
-                const int32_t pe = pool_rows[e - e_begin];
-                a.out_pairs[(size_t)b * a.pool_blocks * a.block + e] =
-                    pe >= 0 ? make_uint2(score_key(part), (uint32_t)pe) : make_uint2(0u, 0xFFFFFFFFu);
-            }
-        } else {
-            const uint32_t key = score_key(part);
-            if (lane < 16 && e < e_end) ok[e] = key;
-            if (a.out_scores && lane < 16 && e < e_end) a.out_scores[(size_t)b * a.capacity + e] = part + 0.0f;
-            if (a.tile_max) {
-                // largest key of the 16-entry tile (entries past the end count as key 0)
-                uint32_t m = lane < 16 && e < e_end ? key : 0u;
-                for (int off = 1; off < 16; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-                if (lane == 0) a.tile_max[(size_t)b * a.tile_stride + (e >> 4)] = m;
-            }
-            if (a.block_keys) {
-                // largest key of each pool block in the tile (tiles start on
-                // block boundaries; entries past the end count as key 0)
-                uint32_t m = e < e_end ? key : 0u;
-                for (int off = 1; off < a.block; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-                if (lane < 16 && e < e_end && lane % a.block == 0)
-                    a.block_keys[(size_t)b * a.block_stride + e / a.block] = m;
-            }
-        }
+            for (int v = 0; v < 4; ++v) part += hw[mt][v] * relu(acc[mt][v]);
+        part = sum_rows(part);
+        scan_store<POOL>(a, out, pe, e, live, lane == 0, part);
     }
     // no LDS write may land after the block's LDS is handed to another block
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -286,7 +383,7 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(ScanArgs a)
 // group's power-of-two scale exactly, and goes through the same bf16 MFMA
 // and epilogue as the bf16 scan.
 template <int DI, int MT, bool POOL, bool PAGED>
-__global__ __launch_bounds__(kScanThreads) void indexer_scan_fp4_kernel(ScanArgs a)
+__global__ __launch_bounds__(kScanThreads, kScanBlocksPerCU) void indexer_scan_fp4_kernel(ScanArgs a)
 {
     constexpr int kSteps = DI / 32;
     constexpr int kTileKeys = 64;
@@ -381,9 +478,14 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_fp4_kernel(ScanArgs
         }
     };
 
+    const ScanOut out = scan_out<POOL>(a, b);
+    constexpr int kS = kStores<POOL>;
+    constexpr int KI = kInstC + kInstS;        // loads per tile
+    // head weights of rows 4 grp .. 4 grp + 3 of each head tile, in registers
+    // (an LDS read after the ring's refill would wait for the refill)
+    float4 hw4[MT];
 #pragma unroll
-    for (int i = 0; i < kRing; ++i) issue(i);
-
+    for (int mt = 0; mt < MT; ++mt) hw4[mt] = *reinterpret_cast<const float4 *>(&hws[16 * mt + 4 * grp]);
     u32x4_t qa[MT][kSteps];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -397,10 +499,12 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_fp4_kernel(ScanArgs
             qa[mt][s] = v;
         }
     }
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) issue(i);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(KI * (kRing - 1)));             // tile 0 has landed
 
-    uint32_t *ok = a.out_keys ? a.out_keys + (size_t)b * a.key_stride : nullptr;
     for (int i = 0; i < my_n; ++i) {
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm((kInstC + kInstS) * (kRing - 1)));
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(scan_wait(KI, kS)));       // tile i has landed
         const uint8_t *slot = &ring[w][i % kRing][0];
         uint32_t cw[4][kSteps];
         uint32_t sw[4];
@@ -419,9 +523,14 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_fp4_kernel(ScanArgs
             const uint8_t *ss = slot + kTileCode + key * kScaleBytes;
             sw[j] = kSteps == 4 ? (uint32_t)*reinterpret_cast<const uint16_t *>(ss + 2 * grp) : (uint32_t)ss[grp];
         }
+        const int64_t t0 = e_begin + (int64_t)(w + kScanWaves * i) * kTileKeys;
+        // lane l reports entry t0 + l: column l % 16 of column tile l / 16
+        const int64_t e = t0 + lane;
+        const bool live = e < e_end;
+        const int32_t pe = POOL ? pool_rows[live ? e - e_begin : 0] : 0;
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);      // slot read before it is refilled
         issue(i + kRing);
-        const int64_t t0 = e_begin + (int64_t)(w + kScanWaves * i) * kTileKeys;
+        float pj[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             f32x4_t acc[MT];
@@ -437,38 +546,16 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_fp4_kernel(ScanArgs
             float part = 0.f;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const float4 hw = *reinterpret_cast<const float4 *>(&hws[16 * mt + 4 * grp]);
-                part += hw.x * fmaxf(acc[mt][0], 0.f);
-                part += hw.y * fmaxf(acc[mt][1], 0.f);
-                part += hw.z * fmaxf(acc[mt][2], 0.f);
-                part += hw.w * fmaxf(acc[mt][3], 0.f);
+                const float4 hw = hw4[mt];
+                part += hw.x * relu(acc[mt][0]);
+                part += hw.y * relu(acc[mt][1]);
+                part += hw.z * relu(acc[mt][2]);
+                part += hw.w * relu(acc[mt][3]);
             }
-            part += __shfl_xor(part, 16);
-            part += __shfl_xor(part, 32);
-            const int64_t e = t0 + 16 * j + lane;
-            if constexpr (POOL) {
-                if (lane < 16 && e < e_end) {
-                    const int32_t pe = pool_rows[e - e_begin];
-                    a.out_pairs[(size_t)b * a.pool_blocks * a.block + e] =
-                        pe >= 0 ? make_uint2(score_key(part), (uint32_t)pe) : make_uint2(0u, 0xFFFFFFFFu);
-                }
-            } else {
-                const uint32_t key = score_key(part);
-                if (lane < 16 && e < e_end) ok[e] = key;
-                if (a.out_scores && lane < 16 && e < e_end) a.out_scores[(size_t)b * a.capacity + e] = part + 0.0f;
-                if (a.tile_max) {
-                    uint32_t m = lane < 16 && e < e_end ? key : 0u;
-                    for (int off = 1; off < 16; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-                    if (lane == 0) a.tile_max[(size_t)b * a.tile_stride + (e >> 4)] = m;
-                }
-                if (a.block_keys) {
-                    uint32_t m = e < e_end ? key : 0u;
-                    for (int off = 1; off < a.block; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-                    if (lane < 16 && e < e_end && lane % a.block == 0)
-                        a.block_keys[(size_t)b * a.block_stride + e / a.block] = m;
-                }
-            }
+            pj[j] = sum_rows(part);
         }
+        const float pm = grp == 0 ? pj[0] : grp == 1 ? pj[1] : grp == 2 ? pj[2] : pj[3];
+        scan_store<POOL>(a, out, pe, e, live, col == 0, pm);
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
