@@ -716,16 +716,29 @@ __global__ __launch_bounds__(kTcThreads) void compress_tiled_kernel(AppendArgs a
 // W is split once per call into the workspace, in the MFMA's B-operand
 // order: for channel tile ct (16 channels) and contraction step s (32
 // terms), 64 lanes x 8 bf16, lane l holding channel 16 ct + l % 16, terms
-// 32 s + 8 (l / 16) .. + 7; the high part's 1 KB, then the low part's.  A
-// block of 4 waves takes 64 listed entries x 64 output channels; wave w owns
-// entries 16w .. 16w + 15 against all 64 channels (4 MFMA tiles): it reads
-// each W operand as one contiguous 1 KB load and splits its own U operand
-// (8 consecutive terms of its entry's row) with the hardware conversion.
-constexpr int kMcRows = 64;                        // listed entries per block
-constexpr int kMcCh = 64;                          // output channels per block
+// 32 s + 8 (l / 16) .. + 7; the high part's 1 KB, then the low part's.
+//
+// A block takes 128 listed entries x 128 output channels (the last column
+// of blocks covers channels 512 .. 575 and computes 64 more that it does not
+// store); its four waves, 2 x 2, take 64 entries x 64 channels each, 4 x 4
+// MFMA tiles.  Per contraction step the block stages in LDS, double-
+// buffered: A, its entries' 32 terms split into bf16 high and low parts in
+// the MFMA A-operand order (per 16-entry tile the high part's 64 lanes x
+// 16 B, then the low part's: 16 KB), and B, the 8 channel tiles' pre-split
+// W operands (16 KB) as the workspace holds them.  A wave reads its step's
+// 4 A and 4 B operand pairs into registers, issues the loads of the next
+// step's W and of the terms two steps ahead, runs its 48 MFMAs, writes the
+// next step's W and split terms into the other buffer and meets the block
+// at a barrier.  Each A and B operand thus serves 4 tiles (the former layout, a
+// wave of 16 entries x 64 channels reading its W operands from L2 every
+// step, was bound by that traffic).
+constexpr int kMcRows = 128;                       // listed entries per block
+constexpr int kMcCh = 128;                         // output channels per block
 constexpr int kMcThreads = 256;
 constexpr int kMcSteps = 2 * kDim / 32;            // 36 contraction steps of 32 terms
 constexpr int kMcChTiles = kDim / 16;              // 36 channel tiles of 16
+constexpr int kMcColBlocks = (kDim + kMcCh - 1) / kMcCh;   // 5
+constexpr int kMcHalf = 16384;                     // A (or B) bytes of one stage
 constexpr size_t kWsplitBytes = (size_t)kMcChTiles * kMcSteps * 2 * 1024;   // 2.65 MB
 
 typedef __bf16 mc_bf16x2_t __attribute__((ext_vector_type(2)));
@@ -761,62 +774,138 @@ __global__ __launch_bounds__(256) void split_w_kernel(const float *w_comp, uint8
     *reinterpret_cast<u32x4_t *>(dst + 1024) = lo;
 }
 
-__global__ __launch_bounds__(kMcThreads) void compress_mfma_kernel(AppendArgs a, const int4 *plan,
-                                                                   const int32_t *count, const uint8_t *wsplit)
+__global__ __launch_bounds__(kMcThreads, 2) void compress_mfma_kernel(AppendArgs a, const int4 *plan,
+                                                                      const int32_t *count, const uint8_t *wsplit)
 {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * 2 * kMcHalf];     // 2 stages x (A, B)
     const int n = *count;
     const int k0 = blockIdx.x * kMcRows;
     if (k0 >= n) return;
     const int ct0 = blockIdx.y * (kMcCh / 16);
-    const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int t = threadIdx.x, w = t / kWave, lane = t & (kWave - 1);
+    const int wr = w >> 1, wc = w & 1;             // the wave's 64 entries and 64 channels
     const int r16 = lane & 15, oct = lane >> 4;
-    // A operand rows: this lane's listed entry (row r16 of the wave's 16)
-    const int rec = k0 + 16 * w + r16;
+
+    // U loads: thread t takes entry lr of the block (terms 16 lh .. 16 lh +
+    // 15 of each step: two octets, all of x_even or all of x_odd)
+    const int lr = t >> 1, lh = t & 1;
+    const int rec = k0 + lr;
     const int4 pl = rec < n ? plan[rec] : make_int4(-1, 0, -1, 0);
     const float *xe = pl.x < 0 ? a.tokens
                     : pl.z >= 0 ? a.tokens + (size_t)pl.z * kDim : a.c.pending + (size_t)pl.y * kDim;
     const float *xo = pl.x < 0 ? a.tokens : a.tokens + (size_t)pl.x * kDim;
-    const uint8_t *wb = wsplit + (size_t)ct0 * kMcSteps * 2048 + 16 * lane;
-    f32x4_t acc[4];
+    // the terms of a step are loaded two steps ahead, into two register sets
+    // used in turn
+    float4 ua[4], ub[4];
+    auto load_u = [&](int s, float4 (&d)[4]) {
+        const int kk = 32 * s + 16 * lh;
+        const float *src = kk < kDim ? xe + kk : xo + (kk - kDim);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float4 u0, u1;
-    u32x4_t wh[4], wl[4];
-    auto load = [&](int s) {
-        const int kk = 32 * s + 8 * oct;
-        const float *ua = kk < kDim ? xe + kk : xo + (kk - kDim);
-        u0 = *reinterpret_cast<const float4 *>(ua);
-        u1 = *reinterpret_cast<const float4 *>(ua + 4);
+        for (int i = 0; i < 4; ++i) d[i] = *reinterpret_cast<const float4 *>(src + 4 * i);
+    };
+    auto store_u = [&](uint8_t *A, const float4 (&u)[4]) {
+        uint8_t *tile = A + (lr >> 4) * 2048;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            const uint8_t *p = wb + ((size_t)nt * kMcSteps + s) * 2048;
-            wh[nt] = *reinterpret_cast<const u32x4_t *>(p);
-            wl[nt] = *reinterpret_cast<const u32x4_t *>(p + 1024);
+        for (int o = 0; o < 2; ++o) {
+            u32x4_t hi, lo;
+            split_bf16x8(u[2 * o], u[2 * o + 1], hi, lo);
+            const int ln = (lr & 15) + 16 * (2 * lh + o);
+            *reinterpret_cast<u32x4_t *>(tile + 16 * ln) = hi;
+            *reinterpret_cast<u32x4_t *>(tile + 1024 + 16 * ln) = lo;
         }
     };
-    load(0);
-    for (int s = 0; s < kMcSteps; ++s) {
-        u32x4_t uh, ul, bh[4], bl[4];
-        split_bf16x8(u0, u1, uh, ul);
+    // W: 16 pieces of 1 KB (channel tile q / 2, its high or low part), wave
+    // w loading pieces 4w .. 4w + 3 into registers a step ahead; tiles past
+    // the channels re-read the last one (their results are not stored).
+    // (Through registers rather than LDS DMA: a block barrier's fence waits
+    // for outstanding LDS DMA, and with it for the term loads behind it.)
+    u32x4_t wv[4];
+    auto load_w = [&](int s) {
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) { bh[nt] = wh[nt]; bl[nt] = wl[nt]; }
-        if (s + 1 < kMcSteps) load(s + 1);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            acc[nt] = mfma16x16x32(uh, bh[nt], acc[nt]);
-            acc[nt] = mfma16x16x32(uh, bl[nt], acc[nt]);
-            acc[nt] = mfma16x16x32(ul, bh[nt], acc[nt]);
+        for (int i = 0; i < 4; ++i) {
+            const int q = 4 * w + i;
+            const int ct = ct0 + (q >> 1) < kMcChTiles ? ct0 + (q >> 1) : kMcChTiles - 1;
+            wv[i] = *reinterpret_cast<const u32x4_t *>(wsplit + ((size_t)ct * kMcSteps + s) * 2048 +
+                                                       1024 * (q & 1) + 16 * lane);
         }
-    }
-    // D layout: lane holds rows 4 oct .. 4 oct + 3 of column r16
+    };
+    auto store_w = [&](uint8_t *B) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int rr = k0 + 16 * w + 4 * oct + v;
-        if (rr >= n) continue;
-        const int row = plan[rr].x;
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t *>(B + 1024 * (4 * w + i) + 16 * lane) = wv[i];
+    };
+
+    f32x4_t acc[4][4];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) a.ent[(size_t)row * kDim + 16 * (ct0 + nt) + r16] = acc[nt][v];
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // Step s: products from stage s % 2; meanwhile W of step s + 1 is loaded
+    // and the terms of step s + 2 into `ld`; at the end W and the terms of
+    // step s + 1 (in `st`, loaded a step ago) go into the other stage.
+    auto step = [&](int s, const float4 (&st)[4], float4 (&ld)[4]) {
+        const uint8_t *cur = lds + (s & 1) * 2 * kMcHalf;
+        uint8_t *nxt = lds + ((s + 1) & 1) * 2 * kMcHalf;
+        u32x4_t ah[4], al[4], bh[4], bl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint8_t *pa = cur + (4 * wr + i) * 2048 + 16 * lane;
+            ah[i] = *reinterpret_cast<const u32x4_t *>(pa);
+            al[i] = *reinterpret_cast<const u32x4_t *>(pa + 1024);
+            const uint8_t *pb = cur + kMcHalf + (4 * wc + i) * 2048 + 16 * lane;
+            bh[i] = *reinterpret_cast<const u32x4_t *>(pb);
+            bl[i] = *reinterpret_cast<const u32x4_t *>(pb + 1024);
+        }
+        const bool more = s + 1 < kMcSteps, more2 = s + 2 < kMcSteps;
+        if (more) load_w(s + 1);
+        if (more2) load_u(s + 2, ld);
+        __builtin_amdgcn_sched_barrier(0);          // the loads go out before the products
+        // high x high for all 16 tiles, then high x low, then low x high, so
+        // that consecutive products of one accumulator are 16 apart
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(ah[i], bh[j], acc[i][j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(ah[i], bl[j], acc[i][j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(al[i], bh[j], acc[i][j]);
+        if (more) {
+            store_u(nxt, st);
+            store_w(nxt + kMcHalf);
+        }
+        __syncthreads();
+    };
+
+    load_w(0);
+    load_u(0, ub);
+    load_u(1, ua);
+    store_w(lds + kMcHalf);
+    store_u(lds, ub);
+    __syncthreads();
+    static_assert(kMcSteps % 2 == 0, "steps go in pairs");
+    for (int s = 0; s < kMcSteps; s += 2) {
+        step(s, ua, ub);                           // stores step s + 1 from ua, loads step s + 2 into ub
+        step(s + 1, ub, ua);
     }
+    // D layout: lane holds entries 4 oct .. 4 oct + 3 of column r16 of each tile
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int rr = k0 + 64 * wr + 16 * i + 4 * oct + v;
+            if (rr >= n) continue;
+            float *erow = a.ent + (size_t)plan[rr].x * kDim;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int ch = 16 * (ct0 + 4 * wc + j) + r16;
+                if (ch < kDim) erow[ch] = acc[i][j][v];
+            }
+        }
 }
 
 // Quantiser of a planned append: kQPer listed entries per block, the
@@ -977,7 +1066,7 @@ hipError_t launch_kv_append(const cskv_cache &c, const float *tokens, const int3
             uint8_t *wsplit = static_cast<uint8_t *>(ws) + L.wsplit_off;
             launch_kernel(split_w_kernel, dim3((unsigned)((kMcChTiles * kMcSteps * kWave + 255) / 256)), dim3(256),
                           s, nullptr, nullptr, w_comp, wsplit);
-            launch_kernel(compress_mfma_kernel, dim3((unsigned)((bound + kMcRows - 1) / kMcRows), kDim / kMcCh),
+            launch_kernel(compress_mfma_kernel, dim3((unsigned)((bound + kMcRows - 1) / kMcRows), kMcColBlocks),
                           dim3(kMcThreads), s, nullptr, tc.stop, a, (const int4 *)plan, (const int32_t *)count,
                           (const uint8_t *)wsplit);
         }
