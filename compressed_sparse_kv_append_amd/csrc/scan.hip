@@ -205,6 +205,32 @@ __device__ __forceinline__ void scan_store(const ScanArgs &a, const ScanOut &o, 
 }
 template <bool POOL> constexpr int kStores = POOL ? 1 : 4;
 
+// The query rows of the block's sequence (16 MT heads of DI bf16, zero rows
+// past the heads) and the head weights (0 past the heads), staged once per
+// block at the start of the LDS array, in the ring's space before any tile is
+// issued; the waves take their MFMA operands from there.  (Loaded by every
+// wave from L2 instead, 16 KB a wave, the start of a launch read some 32-50
+// MB at once.)  Rows are DI bf16 plus 16 bytes, so the 16-byte reads of 16
+// heads at one offset fall on distinct banks.
+template <int DI> constexpr int kQRow = 2 * DI + 16;
+template <int DI, int MT> constexpr int kQStage = 16 * MT * kQRow<DI> + 4 * 16 * MT;
+template <int DI, int MT>
+__device__ __forceinline__ void stage_query(const ScanArgs &a, int b, uint8_t *lds)
+{
+    constexpr int kPieces = DI / 8;                  // 16-byte pieces per row
+    for (int i = threadIdx.x; i < 16 * MT * kPieces; i += kScanThreads) {
+        const int h = i / kPieces, p = i % kPieces;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (h < a.heads) v = *reinterpret_cast<const u32x4_t *>(a.q + ((size_t)b * a.heads + h) * DI + 8 * p);
+        *reinterpret_cast<u32x4_t *>(lds + h * kQRow<DI> + 16 * p) = v;
+    }
+    float *hws = reinterpret_cast<float *>(lds + 16 * MT * kQRow<DI>);
+    if (threadIdx.x < 16 * MT) {
+        const int h = threadIdx.x;
+        hws[h] = h < a.heads ? (a.head_w ? a.head_w[(size_t)b * a.heads + h] : 1.0f) : 0.0f;
+    }
+}
+
 // Run of block blockIdx.x over the n positions of its sequence: the pooled
 // scan's fixed run length, or (full scan) the sequence's live entries cut
 // into gridDim.x runs of a multiple of 64, so a cache allocated far beyond
@@ -233,6 +259,7 @@ __global__ __launch_bounds__(kScanThreads, kScanBlocksPerCU) void indexer_scan_k
     // serialises the ring; reads of the DMA's own object are left to the
     // explicit waits below.
     constexpr int kRingBytes = kScanWaves * kRing * kTileBytes;
+    static_assert(kQStage<DI, MT> <= kRingBytes, "the query is staged in the ring's space");
     __shared__ __attribute__((aligned(16)))
     uint8_t lds[kRingBytes + (POOL ? 4 * kPoolChunkMax : 0) + (PAGED && !POOL ? 4 * kPageSlots : 0)];
     auto ring = reinterpret_cast<uint8_t (*)[kRing][kTileBytes]>(lds);
@@ -266,13 +293,13 @@ __global__ __launch_bounds__(kScanThreads, kScanBlocksPerCU) void indexer_scan_k
             if constexpr (PAGED)
                 pool_prow[i] = e >= 0 && e < E ? page_row0(a, b, e >> sh) + (int32_t)(e & (a.page_size - 1)) : 0;
         }
-        __syncthreads();
     } else if constexpr (PAGED) {
         const int n_pg = (int)(((e_end - 1) >> sh) - first_page + 1);
         for (int j = threadIdx.x; j < n_pg && j < kPageSlots; j += kScanThreads)
             page_rows[j] = page_row0(a, b, first_page + j);
-        __syncthreads();
     }
+    stage_query<DI, MT>(a, b, lds);
+    __syncthreads();
 
     const int n_tiles = (int)((e_end - e_begin + 15) / 16);
     const int my_n = n_tiles > w ? (n_tiles - w + kScanWaves - 1) / kScanWaves : 0;
@@ -312,27 +339,20 @@ __global__ __launch_bounds__(kScanThreads, kScanBlocksPerCU) void indexer_scan_k
     };
 
     // Indexer query as MFMA A operands: row = head, contraction slots
-    // 8*grp..8*grp+7 of each 32-dim step.  Missing heads: zero rows, weight 0.
-    // It is loaded before the ring's first tiles are issued, so the wait for
-    // it leaves those tiles in flight.
+    // 8*grp..8*grp+7 of each 32-dim step; head weights of rows 4 grp ..
+    // 4 grp + 3 of each head tile.  Missing heads: zero rows, weight 0.
     u32x4_t qa[MT][kSteps];
     float hw[MT][4];
+    const float *hws = reinterpret_cast<const float *>(lds + 16 * MT * kQRow<DI>);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int head = 16 * mt + col;
+        const uint8_t *qrow = lds + (16 * mt + col) * kQRow<DI>;
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (head < a.heads)
-                v = *reinterpret_cast<const u32x4_t *>(a.q + ((size_t)b * a.heads + head) * DI + 32 * s + 8 * grp);
-            qa[mt][s] = v;
-        }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int hrow = 16 * mt + 4 * grp + v;
-            hw[mt][v] = hrow < a.heads ? (a.head_w ? a.head_w[(size_t)b * a.heads + hrow] : 1.0f) : 0.0f;
-        }
+        for (int s = 0; s < kSteps; ++s) qa[mt][s] = *reinterpret_cast<const u32x4_t *>(qrow + 16 * (4 * s + grp));
+        const float4 h4 = *reinterpret_cast<const float4 *>(hws + 16 * mt + 4 * grp);
+        hw[mt][0] = h4.x; hw[mt][1] = h4.y; hw[mt][2] = h4.z; hw[mt][3] = h4.w;
     }
+    __syncthreads();                                // the ring may now overwrite the staged query
 #pragma unroll
     for (int i = 0; i < kRing; ++i) issue(i);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(KI * (kRing - 1)));             // tile 0 has landed
@@ -396,16 +416,16 @@ __global__ __launch_bounds__(kScanThreads, kScanBlocksPerCU) void indexer_scan_f
     constexpr int kInstS = kTileScale / 256;             // 4-byte DMA per lane
     constexpr int kPiece = 4 * kSteps;                   // bytes of a lane's code piece
     static_assert(kInstC >= 1 && kInstS >= 1, "tile sizes");
-    // One LDS array (see the bf16 scan): the wave rings, the head weights (0
-    // past the heads), then (POOL) the entry of each position of the run.
+    // One LDS array (see the bf16 scan): the wave rings, then (POOL) the
+    // entry of each position of the run.
     constexpr int kRingBytes = kScanWaves * kRing * (kTileCode + kTileScale);
+    static_assert(kQStage<DI, MT> <= kRingBytes, "the query is staged in the ring's space");
     __shared__ __attribute__((aligned(16)))
-    uint8_t lds[kRingBytes + 64 * MT + (POOL ? 4 * kPoolChunkMax : 0) + (PAGED && !POOL ? 4 * kPageSlots : 0)];
+    uint8_t lds[kRingBytes + (POOL ? 4 * kPoolChunkMax : 0) + (PAGED && !POOL ? 4 * kPageSlots : 0)];
     auto ring = reinterpret_cast<uint8_t (*)[kRing][kTileCode + kTileScale]>(lds);
-    float *hws = reinterpret_cast<float *>(lds + kRingBytes);
-    int32_t *pool_rows = reinterpret_cast<int32_t *>(lds + kRingBytes + 64 * MT);
-    int32_t *pool_prow = pool_rows + kPoolChunkMax / 2;                             // PAGED and POOL
-    int32_t *page_rows = reinterpret_cast<int32_t *>(lds + kRingBytes + 64 * MT);   // PAGED, not POOL
+    int32_t *pool_rows = reinterpret_cast<int32_t *>(lds + kRingBytes);
+    int32_t *pool_prow = pool_rows + kPoolChunkMax / 2;                     // PAGED and POOL
+    int32_t *page_rows = reinterpret_cast<int32_t *>(lds + kRingBytes);     // PAGED, not POOL
 
     const int b = blockIdx.y;
     const int64_t E = entries_of(a.n_tokens, b, a.capacity, a.ratio);
@@ -434,10 +454,7 @@ __global__ __launch_bounds__(kScanThreads, kScanBlocksPerCU) void indexer_scan_f
         for (int j = threadIdx.x; j < n_pg && j < kPageSlots; j += kScanThreads)
             page_rows[j] = page_row0(a, b, first_page + j);
     }
-    if (threadIdx.x < 16 * MT) {
-        const int h = threadIdx.x;
-        hws[h] = h < a.heads ? (a.head_w ? a.head_w[(size_t)b * a.heads + h] : 1.0f) : 0.0f;
-    }
+    stage_query<DI, MT>(a, b, lds);
     __syncthreads();
 
     const int n_tiles = (int)((e_end - e_begin + kTileKeys - 1) / kTileKeys);
@@ -482,23 +499,20 @@ __global__ __launch_bounds__(kScanThreads, kScanBlocksPerCU) void indexer_scan_f
     constexpr int kS = kStores<POOL>;
     constexpr int KI = kInstC + kInstS;        // loads per tile
     // head weights of rows 4 grp .. 4 grp + 3 of each head tile, in registers
-    // (an LDS read after the ring's refill would wait for the refill)
+    // (an LDS read after the ring's refill would wait for the refill), and the
+    // query in the permuted contraction order, both from the staged copy
+    const float *hws = reinterpret_cast<const float *>(lds + 16 * MT * kQRow<DI>);
     float4 hw4[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) hw4[mt] = *reinterpret_cast<const float4 *>(&hws[16 * mt + 4 * grp]);
     u32x4_t qa[MT][kSteps];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int head = 16 * mt + col;
+        hw4[mt] = *reinterpret_cast<const float4 *>(hws + 16 * mt + 4 * grp);
+        const uint8_t *qrow = lds + (16 * mt + col) * kQRow<DI>;
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (head < a.heads)
-                v = *reinterpret_cast<const u32x4_t *>(a.q + ((size_t)b * a.heads + head) * DI +
-                                                       8 * (kSteps * grp + s));
-            qa[mt][s] = v;
-        }
+        for (int s = 0; s < kSteps; ++s)
+            qa[mt][s] = *reinterpret_cast<const u32x4_t *>(qrow + 16 * (kSteps * grp + s));
     }
+    __syncthreads();                                // the ring may now overwrite the staged query
 #pragma unroll
     for (int i = 0; i < kRing; ++i) issue(i);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(KI * (kRing - 1)));             // tile 0 has landed
@@ -563,18 +577,19 @@ __global__ __launch_bounds__(kScanThreads, kScanBlocksPerCU) void indexer_scan_f
 }  // namespace
 
 // Blocks per sequence and positions per block for n positions per sequence:
-// one round of blocks, runs a multiple of 64 (and at most `cap`).  The bf16
-// keys of batches of fewer than 128 sequences size the round for 2 blocks
-// per CU (longer runs per wave; 64K x 32: 48.2 -> 47.2 us, 128K x 64: 191
-// -> 184 us); larger batches take 3 (a ragged 256-sequence batch: 116 us
-// with 3, 156 with 2, where fewer runs per sequence leave the long
-// sequences' blocks with most of the work), and so do FP4 keys, whose scan
-// is bound by its per-key arithmetic and wants every wave it can hold.
-constexpr int kScanManySeqs = 128;
-static int scan_blocks_per_cu(const cskv_cache &c)
-{
-    return c.batch >= kScanManySeqs || c.idx_format == CSKV_IDX_FP4 ? kScanBlocksPerCU : kScanBlocksPerCU - 1;
-}
+// one round of blocks, runs a multiple of 64 (and at most `cap`), 3 blocks
+// per CU (what registers and LDS allow).  With the query staged once per
+// block and 3 blocks per CU, the 64K x 32 step runs 1.3% faster than with
+// every wave loading the query and 2 blocks per CU (10,372 against 10,242
+// steps/s on one box), the 128K x 64 group 0.7% slower (1,616 against
+// 1,629: longer runs amortise the loads); with every wave loading it, 3
+// blocks per CU had been slower at 64K x 32 (the launch's start reading
+// 50 MB of queries from L2); a ragged
+// 256-sequence batch was faster with 3 either way (116 us against 156 with
+// 2, where fewer runs per sequence leave the long sequences' blocks with
+// most of the work), and so are FP4 keys, whose scan is bound by its per-key
+// arithmetic.
+static int scan_blocks_per_cu(const cskv_cache &) { return kScanBlocksPerCU; }
 static int scan_blocks_per_seq(int batch, int per_cu)
 {
     static int cus = 0;
