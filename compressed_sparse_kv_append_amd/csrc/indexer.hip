@@ -60,12 +60,15 @@ static int topk_groups(const cskv_cache &c, int k)
 static size_t cand2_stride(const cskv_cache &c, int k) { return ((size_t)topk_groups(c, k) * k + 1) & ~(size_t)1; }
 
 // The bound select serves caches longer than one slice and at most
-// kTileMaxCap entries per sequence.
-constexpr int kTileMaxCap = 1 << 17;
+// kTileMaxCap entries per sequence.  Its bound comes from at most 8192
+// maxima per sequence: the 16-entry tiles' up to 131,072 entries, beyond
+// that the maxima of groups of 2 or 4 consecutive tiles (tile_group).
+constexpr int kTileMaxCap = 1 << 19;
 static bool topk_uses_tiles(const cskv_cache &c)
 {
     return c.capacity > kSliceKeys && c.capacity <= kTileMaxCap;
 }
+static int tile_group(const cskv_cache &c) { return c.capacity <= (1 << 17) ? 1 : c.capacity <= (1 << 18) ? 2 : 4; }
 static size_t tile_stride(const cskv_cache &c) { return ((size_t)c.capacity / 16 + 1 + 63) / 64 * 64; }
 static int bound_slices(const cskv_cache &c) { return (int)((c.capacity + kSliceKeys - 1) / kSliceKeys); }
 
@@ -481,48 +484,62 @@ __global__ __launch_bounds__(THREADS) void topk_select_kernel(SelectArgs a)
     select_topk<false, false, THREADS, KEYS / THREADS>(sm, it, a.k, out, nullptr);
 }
 
-// Bound select, first kernel: slice s of sequence b (a block of THREADS
-// threads, KEYS keys).  The bound V is the prefix bin, after one histogram
-// pass over the sequence's 16-entry tile maxima, that holds the k-th largest
-// tile maximum (every key when there are at most k tiles): at least k tiles
-// hold a key >= V, so the sequence's k largest keys are all >= V.  The
-// slice's keys >= V go to its candidate list as (key, index) pairs in index
-// order, with their count.  The slice's keys and the tile maxima are read
-// at once, bounded by the capacity, and masked by the entry count when it
-// arrives, so the block waits for memory once.
-template <int KEYS, int THREADS>
-__global__ __launch_bounds__(THREADS) void topk_bound_slice_kernel(SelectArgs a)
+// Bound select, first kernel: the slices of sequence b (blocks of THREADS
+// threads, KEYS keys per slice).  The bound V is the prefix bin, after one
+// histogram pass over the sequence's group maxima (the largest key of each
+// group of consecutive 16-entry tiles), that holds the k-th largest of them
+// (every key when there are at most k groups): at least k groups hold a
+// key >= V, so the sequence's k largest keys are all >= V.  A slice's keys
+// >= V go to its candidate list as (key, index) pairs in index order, with
+// their count.
+//
+// A group is the fewest tiles that fit the sequence's tile maxima in one
+// block, 16 groups per thread: 1 tile up to 131,072 entries, then 2, then
+// up to G.  A sequence gets min(slices, max(32, 512 / batch)) blocks; block
+// x handles slices x, x + gridDim.x, ... that hold entries.  Its first
+// slice's keys and the ungrouped tile maxima are read at once with the
+// entry count, bounded by the capacity and masked by the entries when they
+// arrive, so a block of a sequence that fits ungrouped waits for memory
+// once; blocks past the entries leave.
+
+// Group maxima of thread t (groups 16 t .. 16 t + 15 of G tiles each, 0 for
+// groups past the entries) and the bound V from them.
+template <int THREADS, int G>
+__device__ __forceinline__ uint32_t bound_from_groups(SelectSmem<THREADS> &sm, const SelectArgs &a, int b,
+                                                      const uint32_t (&tl)[16 * G], uint64_t tlvm, int64_t nt)
 {
-    __shared__ SelectSmem<THREADS> sm;
-    constexpr int PER = KEYS / THREADS;
-    constexpr int kTPer = 16;                     // tile maxima per thread (the capacity bounds them)
-    const int b = blockIdx.y, s = blockIdx.x, t = threadIdx.x;
-    const int64_t first = (int64_t)s * KEYS;
-    const int64_t cap_items = a.capacity;
-    const int64_t ncap = cap_items - first < KEYS ? cap_items - first : KEYS;
-    const Items kit{a.keys + (size_t)b * a.key_stride + first, nullptr, ncap, first};
-    uint32_t key[PER], kidx[PER];
-    uint64_t kvm = load_keys<false, THREADS, PER>(kit, 0, key, kidx);
-    const int64_t nt_cap = (cap_items + 15) / 16;
-    const Items tit{a.tmax + (size_t)b * a.tmax_stride, nullptr, nt_cap, 0};
+    constexpr int kTPer = 16;
+    const int t = threadIdx.x;
+    {                                              // tiles past the entries hold stale data
+        const int64_t tv = nt - (int64_t)kTPer * G * t;
+        tlvm &= tv >= kTPer * G ? ~0ull : (tv > 0 ? (1ull << tv) - 1ull : 0ull);
+    }
     uint32_t tm[kTPer], tidx[kTPer];
-    uint64_t tvm = load_keys<false, THREADS, kTPer>(tit, 0, tm, tidx);
-    const int64_t E = items_of(a, b);
-    if (E <= a.k || first >= E) return;           // the final kernel pads or reads only used slices
-    const int64_t n = E - first < KEYS ? E - first : KEYS;
-    const int64_t nt = (E + 15) / 16;
-    {                                              // positions past the entries hold stale data
-        const int64_t kv = n - (int64_t)PER * t, tv = nt - (int64_t)kTPer * t;
-        kvm &= kv >= PER ? ~0ull : (kv > 0 ? (1ull << kv) - 1ull : 0ull);
-        tvm &= tv >= kTPer ? ~0ull : (tv > 0 ? (1ull << tv) - 1ull : 0ull);
+    uint64_t tvm = 0;
+#pragma unroll
+    for (int j = 0; j < kTPer; ++j) {
+        uint32_t m = 0u;
+#pragma unroll
+        for (int i = 0; i < G; ++i) m = max(m, ((tlvm >> (G * j + i)) & 1ull) ? tl[G * j + i] : 0u);
+        tm[j] = m;
+        tvm |= (uint64_t)((tlvm >> (G * j)) & 1ull) << j;   // a group holds entries iff its first tile does
     }
-    uint32_t V = 0;
-    if (nt > a.k) {
-        const Items ti{a.tmax + (size_t)b * a.tmax_stride, nullptr, nt, 0};
-        const Threshold th = radix_threshold<false, THREADS, kTPer>(sm, ti, a.k, tm, tidx, tvm, 1, 1);
-        V = th.T << th.tshift;
-        __syncthreads();                           // sm is used again below
-    }
+    const int64_t ng = (nt + G - 1) / G;          // groups holding entries
+    if (ng <= a.k) return 0u;                      // every key is a candidate
+    const Items ti{nullptr, nullptr, ng, 0};       // one round: the maxima are in registers
+    const Threshold th = radix_threshold<false, THREADS, kTPer>(sm, ti, a.k, tm, tidx, tvm, 1, 1);
+    __syncthreads();                               // sm is used again afterwards
+    return th.T << th.tshift;
+}
+
+// The keys >= V of slice s (keys already loaded, kvm masked to its entries)
+// to the slice's candidate list, with their count.
+template <int KEYS, int THREADS>
+__device__ __forceinline__ void bound_candidates(SelectSmem<THREADS> &sm, const SelectArgs &a, int b, int s,
+                                                 const uint32_t (&key)[KEYS / THREADS], uint64_t kvm, uint32_t V)
+{
+    constexpr int PER = KEYS / THREADS;
+    const int t = threadIdx.x;
     uint32_t in = 0, mine = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -533,38 +550,103 @@ __global__ __launch_bounds__(THREADS) void topk_bound_slice_kernel(SelectArgs a)
     uint32_t total;
     uint32_t pos = block_scan<THREADS>(mine, sm.wave_sum, &total) - mine;
     uint2 *out = a.cand + (size_t)b * a.cand_stride + (size_t)s * KEYS;
-    const int64_t p0 = first + (int64_t)PER * t;
+    const int64_t p0 = (int64_t)s * KEYS + (int64_t)PER * t;
 #pragma unroll
     for (int i = 0; i < PER; ++i)
         if ((in >> i) & 1u) out[pos++] = make_uint2(key[i], (uint32_t)(p0 + i));
     if (t == 0) a.tcount[(size_t)b * a.slices + s] = total;
 }
 
+// V from groups of GS tiles, read after the entry count.
+template <int THREADS, int GS>
+__device__ __forceinline__ uint32_t bound_grouped(SelectSmem<THREADS> &sm, const SelectArgs &a, int b, int64_t nt)
+{
+    static_assert(16 * GS <= 64, "tile maxima per thread");
+    const Items tit{a.tmax + (size_t)b * a.tmax_stride, nullptr, nt, 0};
+    uint32_t tl[16 * GS], tlidx[16 * GS];
+    const uint64_t tlvm = load_keys<false, THREADS, 16 * GS>(tit, 0, tl, tlidx);
+    return bound_from_groups<THREADS, GS>(sm, a, b, tl, tlvm, nt);
+}
+
+template <int KEYS, int THREADS, int G>
+__global__ __launch_bounds__(THREADS) void topk_bound_slice_kernel(SelectArgs a)
+{
+    __shared__ SelectSmem<THREADS> sm;
+    constexpr int PER = KEYS / THREADS;
+    constexpr int kTPer = 16;
+    const int b = blockIdx.y, t = threadIdx.x;
+    const int64_t first = (int64_t)blockIdx.x * KEYS;
+    const int64_t ncap = a.capacity - first < KEYS ? a.capacity - first : KEYS;
+    uint32_t key[PER], kidx[PER];
+    uint64_t kvm;
+    {
+        const Items kit{a.keys + (size_t)b * a.key_stride + first, nullptr, ncap, first};
+        kvm = load_keys<false, THREADS, PER>(kit, 0, key, kidx);
+    }
+    const Items tit{a.tmax + (size_t)b * a.tmax_stride, nullptr, (a.capacity + 15) / 16, 0};
+    uint32_t tl[kTPer], tlidx[kTPer];
+    const uint64_t tlvm = load_keys<false, THREADS, kTPer>(tit, 0, tl, tlidx);
+    const int64_t E = items_of(a, b);
+    if (E <= a.k || first >= E) return;           // the final kernel pads or reads only used slices
+    {                                              // positions past the entries hold stale data
+        const int64_t kv = (E - first < KEYS ? E - first : KEYS) - (int64_t)PER * t;
+        kvm &= kv >= PER ? ~0ull : (kv > 0 ? (1ull << kv) - 1ull : 0ull);
+    }
+    const int64_t nt = (E + 15) / 16;
+    uint32_t V;
+    if (G == 1 || nt <= kTPer * THREADS)
+        V = bound_from_groups<THREADS, 1>(sm, a, b, tl, tlvm, nt);
+    else if (G == 2 || nt <= 2 * kTPer * THREADS)
+        V = bound_grouped<THREADS, (G > 2 ? 2 : G)>(sm, a, b, nt);
+    else
+        V = bound_grouped<THREADS, G>(sm, a, b, nt);
+    for (int s = blockIdx.x;;) {
+        bound_candidates<KEYS, THREADS>(sm, a, b, s, key, kvm, V);
+        s += gridDim.x;
+        if ((int64_t)s * KEYS >= E) break;
+        __syncthreads();                           // sm.wave_sum is used again
+        const int64_t f = (int64_t)s * KEYS;
+        const Items kit{a.keys + (size_t)b * a.key_stride + f, nullptr, E - f < KEYS ? E - f : KEYS, f};
+        kvm = load_keys<false, THREADS, PER>(kit, 0, key, kidx);
+    }
+}
+
 // Bound select, second kernel: sequence b's candidate lists (slice order is
 // index order) gathered into LDS, then the exact top-k among them; more
 // candidates than kFinalCap (heavily tied scores at the bound) select over
 // every key of the sequence instead.  The entry count, the slices' counts
-// and the first kSpec pairs of every slice are read at once; a slice with
-// more candidates has the rest read afterwards.
+// (MAXS slices at most) and the first pairs of every slice are read at
+// once: 4096 / MAXS pairs of each slice and, past 32 slices, 128 more of
+// each of the first 32 (few long slices and many short ones both fit); the
+// pairs past those, if any, are read afterwards, all at once.
 constexpr int kFinalThreads = 512;
 constexpr int kFinalPer = 12;
 constexpr int kFinalCap = kFinalThreads * kFinalPer;
-constexpr int kBoundMaxSlices = kTileMaxCap / kSliceKeys;
-constexpr int kSpec = 128;
+constexpr int kSpec = 128, kSpecSlices = 32;
+template <int MAXS>
 __global__ __launch_bounds__(kFinalThreads) void topk_bound_final_kernel(SelectArgs a)
 {
+    static_assert(MAXS <= kFinalThreads && MAXS >= kSpecSlices, "one slice count per thread");
+    constexpr int kA = 4096 / MAXS;                // pairs of every slice
+    constexpr int kB = MAXS > kSpecSlices ? kSpec : 0;   // more pairs of the first kSpecSlices
+    constexpr int kSpecPer = 4096 / kFinalThreads, kSpecPerB = kB ? kSpecSlices * kB / kFinalThreads : 0;
+    auto covered = [](int sl) { return (uint32_t)(kA + (sl < kSpecSlices ? kB : 0)); };
     __shared__ SelectSmem<kFinalThreads> sm;
     __shared__ __attribute__((aligned(16))) uint2 lc[kFinalCap];
-    __shared__ uint32_t pre[kBoundMaxSlices + 1];
-    constexpr int kSpecPer = kBoundMaxSlices * kSpec / kFinalThreads;   // 8
+    __shared__ uint32_t pre[MAXS + 1];
     const int b = blockIdx.x, t = threadIdx.x;
     const uint2 *cl = a.cand + (size_t)b * a.cand_stride;
-    // speculative reads: pair j of slice sl for every slice that may exist
-    uint2 sp[kSpecPer];
+    // speculative reads, unused for slices past the entries or the capacity
+    uint2 sp[kSpecPer], spb[kSpecPerB ? kSpecPerB : 1];
 #pragma unroll
     for (int i = 0; i < kSpecPer; ++i) {
-        const int u = t + kFinalThreads * i, sl = u / kSpec, j = u % kSpec;
-        sp[i] = cl[(size_t)(sl < a.slices ? sl : 0) * kSliceKeys + j];     // unused when sl >= slices
+        const int u = t + kFinalThreads * i, sl = u / kA, j = u % kA;
+        sp[i] = cl[(size_t)(sl < a.slices ? sl : 0) * kSliceKeys + j];
+    }
+#pragma unroll
+    for (int i = 0; i < kSpecPerB; ++i) {
+        const int u = t + kFinalThreads * i, sl = u / kSpec, j = kA + u % kSpec;
+        spb[i] = cl[(size_t)(sl < a.slices ? sl : 0) * kSliceKeys + j];
     }
     const uint32_t cnt = t < a.slices ? a.tcount[(size_t)b * a.slices + t] : 0u;
     const int64_t E = items_of(a, b);
@@ -574,12 +656,13 @@ __global__ __launch_bounds__(kFinalThreads) void topk_bound_final_kernel(SelectA
         return;
     }
     const int used = (int)((E + kSliceKeys - 1) / kSliceKeys);
-    if (t < kWave) {                               // prefix of the used slices' counts (used <= 32)
+    {                                              // prefix of the used slices' counts
         const uint32_t c = t < used ? cnt : 0u;
-        const uint32_t incl = wave_scan_add(c);
+        uint32_t tot;
+        const uint32_t incl = block_scan<kFinalThreads>(c, sm.wave_sum, &tot);
         if (t <= used) pre[t] = incl - c;
     }
-    __syncthreads();
+    const bool spill = __syncthreads_or(t < used && cnt > covered(t));
     const uint32_t total = pre[used];
     if (total > (uint32_t)kFinalCap) {
         const Items it{a.keys + (size_t)b * a.key_stride, nullptr, E, 0};
@@ -588,12 +671,32 @@ __global__ __launch_bounds__(kFinalThreads) void topk_bound_final_kernel(SelectA
     }
 #pragma unroll
     for (int i = 0; i < kSpecPer; ++i) {
-        const int u = t + kFinalThreads * i, sl = u / kSpec, j = u % kSpec;
+        const int u = t + kFinalThreads * i, sl = u / kA, j = u % kA;
         if (sl < used && (uint32_t)j < pre[sl + 1] - pre[sl]) lc[pre[sl] + j] = sp[i];
     }
-    for (int sl = 0; sl < used; ++sl) {            // slices with more than kSpec candidates
-        const uint32_t c = pre[sl + 1] - pre[sl];
-        for (uint32_t j = kSpec + t; j < c; j += kFinalThreads) lc[pre[sl] + j] = cl[(size_t)sl * kSliceKeys + j];
+#pragma unroll
+    for (int i = 0; i < kSpecPerB; ++i) {
+        const int u = t + kFinalThreads * i, sl = u / kSpec, j = kA + u % kSpec;
+        if (sl < used && (uint32_t)j < pre[sl + 1] - pre[sl]) lc[pre[sl] + j] = spb[i];
+    }
+    if (spill) {                                   // pairs the speculative reads left out
+        uint2 rest[kFinalPer];
+        uint32_t need = 0;
+#pragma unroll
+        for (int i = 0; i < kFinalPer; ++i) {
+            const uint32_t p = t + kFinalThreads * i;
+            int sl = 0;                            // the last slice whose list starts at or before p
+#pragma unroll
+            for (int w = MAXS / 2; w > 0; w >>= 1)
+                if (sl + w < used && pre[sl + w] <= p) sl += w;
+            const uint32_t j = p - pre[sl];
+            const bool r = p < total && j >= covered(sl);
+            rest[i] = cl[(size_t)sl * kSliceKeys + (r ? j : 0u)];
+            need |= (uint32_t)r << i;
+        }
+#pragma unroll
+        for (int i = 0; i < kFinalPer; ++i)
+            if ((need >> i) & 1u) lc[t + kFinalThreads * i] = rest[i];
     }
     __syncthreads();
     if (total == (uint32_t)a.k) {                  // exactly the k largest
@@ -769,9 +872,23 @@ hipError_t launch_indexer_topk(const cskv_cache &c, const uint16_t *q_idx, int h
         se.tmax_stride = lay.tmax_stride;
         se.tcount = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) +
                                                  align_up(lay.tcand_off + sizeof(uint2) * se.cand_stride * c.batch, 256));
-        launch_kernel(topk_bound_slice_kernel<kSliceKeys, kSliceThreads>, dim3((unsigned)slices, (unsigned)c.batch),
-                      dim3(kSliceThreads), s, tk.start, nullptr, se);
-        launch_kernel(topk_bound_final_kernel, dim3((unsigned)c.batch), dim3(kFinalThreads), s, nullptr, tk.stop, se);
+        const int per = 512 / c.batch > 32 ? 512 / c.batch : 32;
+        const dim3 sg((unsigned)(slices < per ? slices : per), (unsigned)c.batch), fg((unsigned)c.batch);
+        const int g = tile_group(c);
+        if (g == 1) {
+            launch_kernel(topk_bound_slice_kernel<kSliceKeys, kSliceThreads, 1>, sg, dim3(kSliceThreads), s,
+                          tk.start, nullptr, se);
+            launch_kernel(topk_bound_final_kernel<32>, fg, dim3(kFinalThreads), s, nullptr, tk.stop, se);
+        } else {
+            if (g == 2)
+                launch_kernel(topk_bound_slice_kernel<kSliceKeys, kSliceThreads, 2>, sg, dim3(kSliceThreads), s,
+                              tk.start, nullptr, se);
+            else
+                launch_kernel(topk_bound_slice_kernel<kSliceKeys, kSliceThreads, 4>, sg, dim3(kSliceThreads), s,
+                              tk.start, nullptr, se);
+            launch_kernel(topk_bound_final_kernel<kTileMaxCap / kSliceKeys>, fg, dim3(kFinalThreads), s, nullptr,
+                          tk.stop, se);
+        }
     } else {
         se.slice_keys = slice_keys_of(c);
         se.groups = topk_groups(c, k);

@@ -261,16 +261,31 @@ def test_indexer_topk_long_sequences_merge_slices(ck, orc):
 @pytest.mark.parametrize("distinct", [False, True])
 @pytest.mark.parametrize("lens", [[210000, 9000, 180000, 80000, 0, 300], [210000, 9000, 300]])
 def test_indexer_topk_two_level_merge(ck, orc, distinct, lens):
-    """Caches of 25 or more slices merge the slices' lists in groups of 8
-    first.  Six sequences (4096-key slices): 52 slices (a last group of 4),
+    """Caches past the bound select's 524,288 entries select by slices and
+    merge; 25 or more slices merge the slices' lists in groups of 8 first.
+    Six sequences (4096-key slices): 52 slices in use (a last group of 4),
     44, 20 (groups of 8, 8 and 4), 3 (one group: its list is the answer) and
     short ones.  Three sequences (8192-key slices on 1024-thread blocks): 26
-    slices (a last group of 2), 2 and a short one.  Many tied scores or few."""
+    slices in use (a last group of 2), 2 and a short one.  Many tied scores
+    or few."""
     if distinct:
         key_fn = None
     else:
         key_fn = lambda g, n: synth.int_bf16(g, (n, 64), -1, 1)
-    _indexer_case(ck, orc, lens, 64, 4, 512, seed=77 + distinct + len(lens), key_fn=key_fn, cap=210003)
+    _indexer_case(ck, orc, lens, 64, 4, 512, seed=77 + distinct + len(lens), key_fn=key_fn, cap=530000)
+
+
+def test_indexer_topk_grouped_bound_select(ck, orc):
+    """Capacities from 131,073 to 524,288 entries: the bound comes from the
+    maxima of groups of 1, 2 or 4 consecutive 16-entry tiles, the smallest
+    group that fits the sequence's entries in one block, and the final
+    select gathers up to 128 slices' candidate lists, slices with more than
+    32 candidates in a second read.  Long sequences of each group size beside
+    short and empty ones; many tied scores with k = 2048."""
+    _indexer_case(ck, orc, [200000, 1000, 0, 5000], 64, 16, 512, seed=47, cap=250000)
+    ties = lambda g, n: synth.int_bf16(g, (n, 64), -1, 1)
+    _indexer_case(ck, orc, [300000, 130000, 600, 200000], 64, 16, 2048, seed=48, key_fn=ties, cap=400000)
+    _indexer_case(ck, orc, [524288, 4097], 64, 4, 512, seed=49, cap=524288)
 
 
 def test_indexer_topk_many_sequences(ck, orc):
@@ -284,14 +299,15 @@ def test_indexer_topk_many_sequences(ck, orc):
 
 
 def test_indexer_topk_merge_candidate_counts(ck, orc):
-    """Slices hold 4096 entries; the merge reads k candidates per full slice
-    and min(k, entries) of the last one.  Lengths put the last slice at 1,
+    """Capacities past the bound select's range: slices hold 4096 entries;
+    the merge reads k candidates per full slice and min(k, entries) of the
+    last one.  Lengths put the last slice at 1,
     k, k + 1 and 4096 entries and the candidate count on both sides of 5120,
     where the merge changes from 10 to 36 candidates per thread."""
     s = 4096
     lens = [8 * s + 1, 8 * s + 512, 8 * s + 513, 10 * s, 10 * s + 1, 10 * s + 511]
-    _indexer_case(ck, orc, lens, 64, 4, 512, seed=43)
-    _indexer_case(ck, orc, [s + 100, 2 * s + 2047, 2 * s + 2048, 2 * s + 2049], 64, 4, 2048, seed=44)
+    _indexer_case(ck, orc, lens, 64, 4, 512, seed=43, cap=530000)
+    _indexer_case(ck, orc, [s + 100, 2 * s + 2047, 2 * s + 2048, 2 * s + 2049], 64, 4, 2048, seed=44, cap=530000)
 
 
 def test_indexer_topk_capacity_far_beyond_entries(ck, orc):
