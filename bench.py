@@ -100,10 +100,9 @@ def copy_probe(mib: int):
 # The kernels one decode step of the default workload launches, with launches
 # per step (a name, followed by its argument list, is looked for in the
 # profiler's kernel name).
-STEP_KERNELS = (("compress_kernel<4>", 1), ("quantize_kernel<true, true>", 1),
-                ("indexer_scan_kernel<128, 4, false, false>", 1), ("topk_bound_slice_kernel<4096, 512, 1>", 1),
-                ("topk_bound_final_kernel<32>", 1), ("sparse_attn_kernel<64, false, 64, false>", 1),
-                ("attn_merge_kernel", 1))
+STEP_KERNELS = (("quantize_kernel<true, true, true>", 1), ("indexer_scan_kernel<128, 4, false, false>", 1),
+                ("topk_bound_slice_carry_kernel<4096, 512, 1>", 1), ("topk_bound_final_carry_kernel<32>", 1),
+                ("sparse_attn_kernel<64, false, 64, false>", 1), ("attn_merge_kernel", 1))
 SCAN_KERNEL = "indexer_scan_kernel<128, 4, false, false>"
 
 

@@ -154,10 +154,20 @@ int pool_args(const cskv_cache *c, int32_t k, int32_t pool_blocks, int32_t pool_
 }
 
 // Layer-group workspace: the candidate pool (when used) at offset 0, then a
-// region shared in turn by the append, each layer's top-k and attention.
+// region shared in turn by the append, each layer's top-k and attention.  A
+// decode step whose append rides on the first top-k keeps the compressed
+// entry and its cache rows past the top-k's (and the pool build's) part of
+// that region, from the append's head kernel until the top-k's last launch.
 size_t group_pool_bytes(const cskv_cache &c, int pool_blocks)
 {
     return pool_blocks > 0 ? ((size_t)c.batch * pool_blocks * sizeof(int32_t) + 255) / 256 * 256 : 0;
+}
+
+static size_t group_carry_off(const cskv_cache &c, int k, int pool_blocks, int pool_block)
+{
+    size_t off = cskv::topk_workspace(c, k).total;
+    if (pool_blocks > 0) off = std::max(off, cskv::pool_workspace(c, k, pool_blocks, pool_block).build_total);
+    return (off + 255) / 256 * 256;
 }
 
 size_t group_ws_bytes(const cskv_cache &c, int heads, int k, int window, int pool_blocks, int pool_block)
@@ -169,6 +179,8 @@ size_t group_ws_bytes(const cskv_cache &c, int heads, int k, int window, int poo
     }
     need = std::max(need, cskv::attn_plan(c, heads, k, window).ws_bytes);
     need = std::max(need, cskv::append_workspace_bytes(c.batch));   // one new token per sequence
+    if (cskv::topk_carries_entry(c, k))
+        need = std::max(need, group_carry_off(c, k, pool_blocks, pool_block) + cskv::deferred_entry_bytes(c.batch));
     need = std::max(need, (size_t)256);
     return group_pool_bytes(c, pool_blocks) + need;
 }
@@ -493,21 +505,37 @@ static int check_group(const cskv_cache *cache, const cskv_layer *layers, int32_
 static int run_group(const cskv_cache *cache, const cskv_layer *layers, int32_t n_layers,
                      const float *new_tokens, const float *w_comp, const uint16_t *new_idx_rows,
                      int32_t n_idx_heads, int32_t n_heads, int32_t k, int32_t window, float softmax_scale,
-                     int32_t pool_blocks, int32_t pool_block, void *ws, hipStream_t stream)
+                     int32_t pool_blocks, int32_t pool_block, void *ws, size_t ws_bytes, hipStream_t stream)
 {
     const size_t pool_bytes = group_pool_bytes(*cache, pool_blocks);
     int32_t *pool = pool_blocks > 0 ? static_cast<int32_t *>(ws) : nullptr;
     void *work = static_cast<char *>(ws) + pool_bytes;
     bool appended = false, pooled = false;
     const int32_t *last_idx = nullptr;
+    // A compressor append rides on the first FULL layer's top-k when the
+    // bound select serves the cache and the workspace holds the entry: the
+    // head kernel advances the cache before the scan, the top-k's launches
+    // compress and quantise the entry before attention reads it.
+    const size_t carry_off = group_carry_off(*cache, k, pool_blocks, pool_block);
+    const cskv::DeferredEntry carry =
+        cskv::deferred_entry_at(static_cast<char *>(work) + carry_off, cache->batch, new_tokens, w_comp);
+    const bool can_carry = w_comp && cskv::topk_carries_entry(*cache, k) &&
+                           ws_bytes >= pool_bytes + carry_off + cskv::deferred_entry_bytes(cache->batch);
+    const cskv::DeferredEntry *carried = nullptr;
     hipError_t e;
     for (int i = 0; i < n_layers; ++i) {
         const cskv_layer &L = layers[i];
         bool window_done = false;
         if (L.mode == CSKV_MODE_FULL && new_tokens && !appended) {
             // the append also writes this layer's window row
-            e = cskv::launch_kv_append(*cache, new_tokens, nullptr, cache->batch, w_comp, new_idx_rows, work,
-                                       stream, L.swa_row ? L.swa : nullptr, L.swa_row, window);
+            if (can_carry) {
+                e = cskv::launch_append_head(*cache, carry, new_idx_rows, stream, L.swa_row ? L.swa : nullptr,
+                                             L.swa_row, window);
+                carried = &carry;
+            } else {
+                e = cskv::launch_kv_append(*cache, new_tokens, nullptr, cache->batch, w_comp, new_idx_rows, work,
+                                           stream, L.swa_row ? L.swa : nullptr, L.swa_row, window);
+            }
             if (e != hipSuccess) return hip_fail(e, "layer group: append");
             appended = true;
             window_done = L.swa_row != nullptr;
@@ -528,8 +556,9 @@ static int run_group(const cskv_cache *cache, const cskv_layer *layers, int32_t 
             const bool build = pool && L.mode == CSKV_MODE_FULL && !pooled;
             const cskv::PoolBuild pb{pool_blocks, pool_block, pool};
             e = cskv::launch_indexer_topk(*cache, L.q_idx, n_idx_heads, L.head_w, k, L.idx, work, stream,
-                                          build ? &pb : nullptr);
+                                          build ? &pb : nullptr, nullptr, carried);
             if (e != hipSuccess) return hip_fail(e, "layer group: indexer");
+            carried = nullptr;
             pooled = pooled || build;
             last_idx = L.idx;
         }
@@ -550,7 +579,7 @@ static int layer_group(const cskv_cache *cache, const cskv_layer *layers, int32_
                                k, window, pool_blocks, pool_block, ws, ws_bytes);
     if (rc) return rc;
     return run_group(cache, layers, n_layers, new_tokens, w_comp, new_idx_rows, n_idx_heads, n_heads, k, window,
-                     softmax_scale, pool_blocks, pool_block, ws, stream);
+                     softmax_scale, pool_blocks, pool_block, ws, ws_bytes, stream);
 }
 
 static int ced_args(const uint16_t *h, int64_t rows, int32_t d_model, const uint16_t *w, int32_t n_out,
@@ -603,7 +632,7 @@ int cskv_layer_group_decode_noalloc(const cskv_cache *cache, const cskv_layer *l
     void *ws = nullptr;
     if ((rc = scratch_of_current_device(&ws))) return rc;
     return run_group(cache, layers, n_layers, new_tokens, w_comp, new_idx_rows, n_idx_heads, n_heads, k, window,
-                     softmax_scale, 0, 0, ws, stream);
+                     softmax_scale, 0, 0, ws, (size_t)CSKV_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int cskv_layer_group_decode_pooled(const cskv_cache *cache, const cskv_layer *layers,
@@ -699,7 +728,7 @@ int cskv_model_decode(const cskv_group *groups, int32_t n_groups, int32_t n_idx_
         }
         if ((rc = run_group(G.cache, G.layers, G.n_layers, G.ced_h ? rows : G.new_tokens,
                             G.ced_h ? nullptr : G.w_comp, G.new_idx_rows, n_idx_heads, n_heads, k, window,
-                            softmax_scale, G.pool_blocks, G.pool_block, gws, stream)))
+                            softmax_scale, G.pool_blocks, G.pool_block, gws, gws_bytes, stream)))
             return rc;
     }
     return CSKV_OK;

@@ -6,387 +6,27 @@
 //   P2  "DeepSeek V1 到 V4.1-Flash，单 token 的 global KV 如何从 389,000 B 压缩到 890 B的？"
 #include <type_traits>
 
+#include "append_dev.hpp"
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace cskv {
 namespace {
 
-constexpr int kDim = 576;          // entry dims handled by these kernels (512 latent + 64 RoPE)
-constexpr int kAppendThreads = kDim;  // quantiser: one channel per thread, 9 waves
-// Appends with a compressor and at least this many rows (grouped by cu_new)
-// take the planned, tiled path; smaller ones the wave-per-output kernel.
-constexpr int kTiledMinRows = 512;
-
-struct AppendArgs {
-    cskv_cache c;
-    const float *tokens;
-    const int32_t *cu_new;
-    const float *w_comp;
-    const uint16_t *idx_rows;
-    float *ent;          // compressor output, [total_new][dim] (rows that complete an entry)
-    int64_t total_new;
-    // one row per sequence only: this row's window entry, written with the append
-    uint16_t *swa_ring;  // [batch][swa_window][dim] bf16, or null
-    const float *swa_rows;
-    int swa_window;
-};
-
-// Rows of sequence b are [row0, row0 + m).  A malformed cu_new (decreasing,
-// or pointing past total_new) must not make any row be read or written out of
-// bounds: such a sequence is rejected as a whole.
-__device__ __forceinline__ bool rows_ok(int64_t row0, int64_t m, int64_t total)
-{
-    return row0 >= 0 && m >= 0 && row0 + m <= total;
-}
-
-// Where input row r lands: the cache slot of the entry it completes, or -1
-// when it completes none (first half of a pair, a rejected sequence, a bad
-// row).  Also the sequence and the row of its pair partner (-1: pending).
-struct RowInfo {
-    int b;
-    int64_t entry;       // entry index within the sequence, or -1
-    int64_t partner;     // compressor mode: input row of x_even, -1 = pending[b]
-};
-
-// (b is row r's sequence and p its token count, read by the caller so that
-// it can issue other loads before waiting for them.)
-template <bool kCompress>
-__device__ __forceinline__ RowInfo row_info(const AppendArgs &a, int64_t r, int b, int64_t p)
-{
-    const cskv_cache &c = a.c;
-    RowInfo ri{b, -1, -1};
-    const int64_t row0 = a.cu_new ? a.cu_new[b] : b;
-    const int64_t m = a.cu_new ? (int64_t)a.cu_new[b + 1] - row0 : 1;
-    const int64_t q = r - row0;
-    if (p < 0 || !rows_ok(row0, m, a.total_new) || q < 0 || q >= m) return ri;
-    if (kCompress) {
-        const int64_t pos = p + q;
-        if ((pos & 1) == 0) return ri;                 // first half of a pair
-        if ((p + m) / 2 > c.capacity) return ri;       // rejected sequence (finalize flags it)
-        ri.entry = pos >> 1;
-        ri.partner = q > 0 ? r - 1 : -1;
-    } else {
-        const int rt = c.ratio;                        // tokens per entry
-        if ((p % rt) != 0 || p / rt + m > c.capacity) return ri;
-        ri.entry = p / rt + q;
-    }
-    return ri;
-}
-
-// ---------------------------------------------------------------- compressor
-
-// Stand-in 2->1 compressor [P2 三、"突破四" (2 tokens -> 1 entry); P1 §3.2]:
-// e[ch] = sum_j W[ch][j] u[j], u = x_even || x_odd, in a fixed fp32 order:
-// the 1152 terms are cut into 64 blocks of 18, each folded upward from +0
-// with one fused multiply-add per term, and the 64 block sums are added as a
-// pairwise tree (blocks 2i and 2i+1 first).  The tiled kernel of large appends
-// cuts the tree at its level-3 nodes instead (see there).
-constexpr int kCompTerms = 2 * kDim / kWave;     // 18 terms per block
-
-// Small appends (a decode step): lane l of a wave owns block l; it keeps
-// u's 18 terms of E input rows in registers and reads W[ch][18 l ..
-// 18 l + 17], so the wave reads each W row contiguously once for all E
-// rows.  The tree is four DPP steps inside each row of 16 lanes (lane p
-// adds lane p + w) and one scalar step over the four row sums.  A wave
-// takes `cpw` output channels of E consecutive input rows.  Its loads are
-// issued in three groups before any is waited for: the rows' token counts,
-// the W rows of up to kDepth channels (they depend on nothing), then the
-// token rows (their addresses depend on the counts).
-constexpr int kDppRowShl = 0x100;
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_shl(float v)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-
-template <int E>
-__global__ __launch_bounds__(kWave) void compress_kernel(AppendArgs a, int cpw)
-{
-    constexpr int kDepth = E <= 4 ? 6 : 3;         // W rows in flight per wave
-    constexpr int kH = kCompTerms / 2;
-    const int lane = threadIdx.x;
-    const int64_t r0 = (int64_t)blockIdx.y * E;
-    const int c0 = blockIdx.x * cpw;
-    const int c1 = c0 + cpw < kDim ? c0 + cpw : kDim;
-
-    int bs[E];
-    int64_t ps[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int64_t r = r0 + e < a.total_new ? r0 + e : r0;
-        bs[e] = seq_of_row(a.cu_new, a.c.batch, (int)r);
-        ps[e] = a.c.n_tokens[bs[e]];
-    }
-    const float2 *wl = reinterpret_cast<const float2 *>(a.w_comp) + kH * lane;
-    float2 w[kDepth][kH];
-#pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-        const int c = c0 + d < c1 ? c0 + d : c1 - 1;
-#pragma unroll
-        for (int t = 0; t < kH; ++t) w[d][t] = wl[(size_t)c * kDim + t];
-    }
-
-    // u's terms of this lane's block for every row of the group that
-    // completes an entry; lanes 0-31 hold x_even, lanes 32-63 x_odd (rows
-    // that complete no entry read row 0 and are never used)
-    float u[E][kCompTerms];
-    uint32_t act = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int64_t r = r0 + e;
-        RowInfo ri{0, -1, -1};
-        if (r < a.total_new) ri = row_info<true>(a, r, bs[e], ps[e]);
-        const bool on = ri.entry >= 0;
-        act |= (uint32_t)on << e;
-        const float *src = !on ? a.tokens
-                         : lane < kWave / 2
-                               ? (ri.partner >= 0 ? a.tokens + (size_t)ri.partner * kDim
-                                                  : a.c.pending + (size_t)ri.b * kDim) + kCompTerms * lane
-                               : a.tokens + (size_t)r * kDim + kCompTerms * (lane - kWave / 2);
-#pragma unroll
-        for (int t = 0; t < kH; ++t) {
-            const float2 x = reinterpret_cast<const float2 *>(src)[t];
-            u[e][2 * t] = x.x;
-            u[e][2 * t + 1] = x.y;
-        }
-    }
-    if (act == 0) return;
-
-    for (int cb = c0; cb < c1; cb += kDepth) {
-        if (cb != c0) {
-#pragma unroll
-            for (int d = 0; d < kDepth; ++d) {
-                const int c = cb + d < c1 ? cb + d : c1 - 1;
-#pragma unroll
-                for (int t = 0; t < kH; ++t) w[d][t] = wl[(size_t)c * kDim + t];
-            }
-        }
-#pragma unroll
-        for (int d = 0; d < kDepth; ++d) {
-            const int c = cb + d;
-            if (c >= c1) break;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                if (!((act >> e) & 1u)) continue;
-                float acc = 0.0f;
-#pragma unroll
-                for (int t = 0; t < kH; ++t) {
-                    acc = fmaf(w[d][t].x, u[e][2 * t], acc);
-                    acc = fmaf(w[d][t].y, u[e][2 * t + 1], acc);
-                }
-                acc = acc + dpp_shl<kDppRowShl | 1>(acc);
-                acc = acc + dpp_shl<kDppRowShl | 2>(acc);
-                acc = acc + dpp_shl<kDppRowShl | 4>(acc);
-                acc = acc + dpp_shl<kDppRowShl | 8>(acc);
-                const float q0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 0));
-                const float q1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 16));
-                const float q2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 32));
-                const float q3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 48));
-                const float res = (q0 + q1) + (q2 + q3);
-                if (lane == e) a.ent[(size_t)(r0 + e) * kDim + c] = res;
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------- quantiser
-
-// Group absmax of the channel each thread holds (threads >= n hold 0).
-// Groups of g <= 64 channels lie inside one wave and reduce with lane
-// exchanges; g = 128 adds one combine of two wave results through LDS.
-__device__ float group_absmax(float a, int t, int n, int g, float *wave_max)
-{
-    const int span = g < kWave ? g : kWave;
-    for (int off = span >> 1; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
-    if (g > kWave) {
-        if ((t & (kWave - 1)) == 0) wave_max[t / kWave] = a;
-        __syncthreads();
-        const int per = g / kWave, first = (t / g) * per;
-        float m = 0.f;
-        if (t < n)                                  // groups of live channels only
-            for (int i = 0; i < per; ++i) m = fmaxf(m, wave_max[first + i]);
-        __syncthreads();
-        a = m;
-    }
-    return a;
-}
-
-// Quantise channel t of a row of n channels with group g into a packed plane
-// row [P1 §3.1 (per-group scale, values stored relative to it); P2 四、"P4 main
-// KV" (E2M1)].  Codes are gathered 8 per 32-bit word with lane exchanges so
-// that every eighth thread writes one word.  Called by all threads of the
-// block (it contains barriers).
-__device__ void quantize_channel(float x, int t, int n, int g, uint8_t *codes_row,
-                                 float *scales_row, float *wave_max)
-{
-    const bool live = t < n;
-    float a = group_absmax(live ? fabsf(x) : 0.f, t, n, g, wave_max);
-    const float s = a / 6.0f;                      // IEEE division (no fast-math)
-    uint32_t code = (live && s != 0.0f) ? e2m1_code(x / s) : 0u;
-    code |= __shfl_down(code, 1) << 4;             // 2 codes (even t)
-    code |= __shfl_down(code, 2) << 8;             // 4 codes (t % 4 == 0)
-    code |= __shfl_down(code, 4) << 16;            // 8 codes (t % 8 == 0)
-    if (live && (t & 7) == 0) *reinterpret_cast<uint32_t *>(codes_row + (t >> 1)) = code;
-    if (live && (t % g) == 0) scales_row[t / g] = s;
-}
-
-// fp32 -> OCP E4M3 byte [P2 四、"P4 main KV" (window rows kept in FP8)]: the
-// nearest E4M3 value, ties to the even mantissa, magnitudes past 448
-// saturating to 448, sign kept.  Normal results round the fp32 mantissa to 3
-// bits; below 2^-6 the value is a multiple of 2^-9, rounded with rintf.
-__device__ __forceinline__ uint32_t e4m3_bits(float x)
-{
-    const uint32_t u = __float_as_uint(x);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const float a = fabsf(x);
-    if (!(a < 448.0f)) return sign | 0x7Eu;
-    if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);     // 0..8 (8 = 2^-6, code 0x08)
-    const uint32_t au = __float_as_uint(a);
-    uint32_t e = (au >> 23) - 127 + 7, m = (au >> 20) & 7u;
-    const uint32_t rem = au & 0xFFFFFu;
-    if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) {
-        if (++m == 8u) { m = 0; ++e; }
-    }
-    const uint32_t code = (e << 3) | m;
-    return sign | (code > 0x7Eu ? 0x7Eu : code);
-}
-
-// Indexer key in the pages' FP4 form [P2 四、"890 字节是怎么算出来的" (72 B per
-// 128-dim key); P2 四、"P4 main KV" (E2M1, one 8-bit scale per 16 channels)]:
-// thread t < Di holds dim t of the bf16 row.  Each 16-dim group takes the
-// E8M0 scale 2^(floor(log2 amax) - 2) (byte 0 and zero codes when amax = 0);
-// codes are the nearest E2M1 of x / scale (exact: a power of two).  Called by
-// whole waves (Di is a multiple of 64).
-__device__ void quantize_idx_fp4(float x, int t, uint8_t *codes_row, uint8_t *scales_row)
-{
-    float a = fabsf(x);
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) a = fmaxf(a, __shfl_xor(a, off));
-    int e = -127;
-    if (a > 0.0f) {
-        int ex;
-        (void)frexpf(a, &ex);                      // a = m 2^ex, 0.5 <= m < 1
-        e = ex - 1 - 2;
-        e = e < -127 ? -127 : (e > 127 ? 127 : e);
-    }
-    uint32_t code = a > 0.0f ? e2m1_code(ldexpf(x, -e)) : 0u;
-    code |= __shfl_down(code, 1) << 4;             // 2 codes (even t)
-    code |= __shfl_down(code, 2) << 8;             // 4 codes
-    code |= __shfl_down(code, 4) << 16;            // 8 codes
-    if ((t & 7) == 0) *reinterpret_cast<uint32_t *>(codes_row + (t >> 1)) = code;
-    if ((t & 15) == 0) scales_row[t >> 4] = (uint8_t)(e + 127);
-}
-
-// The pages' main-entry form [P2 四、"P4 main KV" (E2M1, one 8-bit scale per
-// 16 channels)]: channel t of a row of n; each 16-channel group (inside one
-// wave) takes the E8M0 scale 2^(floor(log2 amax) - 2), byte 0 and zero codes
-// when amax = 0.  Called by all threads of the block.
-__device__ void quantize_channel_mx16(float x, int t, int n, uint8_t *codes_row, uint8_t *scales_row)
-{
-    const bool live = t < n;
-    float a = live ? fabsf(x) : 0.0f;
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) a = fmaxf(a, __shfl_xor(a, off));
-    int e = -127;
-    if (a > 0.0f) {
-        int ex;
-        (void)frexpf(a, &ex);
-        e = ex - 1 - 2;
-        e = e < -127 ? -127 : (e > 127 ? 127 : e);
-    }
-    uint32_t code = (live && a > 0.0f) ? e2m1_code(ldexpf(x, -e)) : 0u;
-    code |= __shfl_down(code, 1) << 4;
-    code |= __shfl_down(code, 2) << 8;
-    code |= __shfl_down(code, 4) << 16;
-    if (live && (t & 7) == 0) *reinterpret_cast<uint32_t *>(codes_row + (t >> 1)) = code;
-    if (live && (t & 15) == 0) scales_row[t >> 4] = (uint8_t)(e + 127);
-}
-
-// Sequence b after its rows are quantised: store the trailing odd token,
-// advance n_tokens, or flag a rejected sequence.  p is n_tokens[b] as the
-// append found it.  Returns the sequence's token count afterwards.
-template <bool kCompress>
-__device__ int64_t finalize_seq(const AppendArgs &a, int b, int64_t p, int t, int nthreads)
-{
-    const cskv_cache &c = a.c;
-    const int64_t row0 = a.cu_new ? a.cu_new[b] : b;
-    const int64_t m = a.cu_new ? (int64_t)a.cu_new[b + 1] - row0 : 1;
-    if (m == 0) return p;
-    if (p < 0 || !rows_ok(row0, m, a.total_new)) {
-        if (t == 0) atomicOr(c.status, CSKV_STATUS_BAD_STATE);
-        return p;
-    }
-    if (kCompress) {
-        if ((p + m) / 2 > c.capacity) {
-            if (t == 0) atomicOr(c.status, CSKV_STATUS_OVERFLOW);
-            return p;
-        }
-        if (((p + m) & 1) != 0) {
-            const float *last = a.tokens + (size_t)(row0 + m - 1) * kDim;
-            for (int i = t; i < kDim; i += nthreads) c.pending[(size_t)b * kDim + i] = last[i];
-        }
-        if (t == 0) c.n_tokens[b] = (int32_t)(p + m);
-        return p + m;
-    } else {
-        const int rt = c.ratio;
-        if ((p % rt) != 0) {
-            if (t == 0) atomicOr(c.status, CSKV_STATUS_ODD_ENTRY_APPEND);
-            return p;
-        }
-        if (p / rt + m > c.capacity) {
-            if (t == 0) atomicOr(c.status, CSKV_STATUS_OVERFLOW);
-            return p;
-        }
-        if (t == 0) c.n_tokens[b] = (int32_t)(p + rt * m);
-        return p + rt * m;
-    }
-}
-
-// Quantise entry value e (channel t of the entry) into cache slot `slot`
-// (sequence-major row of every plane) and copy or quantise the indexer key
-// there (key_t: dim t of the key row, for t < idx_dim).  Called by all threads of a kAppendThreads block
-// (barriers inside).
-__device__ __forceinline__ void quantize_entry(const AppendArgs &a, float e, int t, size_t slot, uint16_t key_t,
-                                               float *wave_max)
-{
-    const cskv_cache &c = a.c;
-    if (c.k_format == CSKV_KV_MX16) {
-        quantize_channel_mx16(e, t, kDim, c.k_codes + slot * (kDim / 2),
-                              reinterpret_cast<uint8_t *>(c.k_scales) + slot * (kDim / 16));
-        if (c.v_group > 0) {
-            const int dv = c.dim - c.rope_dim;
-            quantize_channel_mx16(e, t, dv, c.v_codes + slot * (dv / 2),
-                                  reinterpret_cast<uint8_t *>(c.v_scales) + slot * (dv / 16));
-        }
-    } else {
-        quantize_channel(e, t, kDim, c.k_group, c.k_codes + slot * (kDim / 2),
-                         c.k_scales + slot * (kDim / c.k_group), wave_max);
-        if (c.v_group > 0) {
-            const int dv = c.dim - c.rope_dim;
-            quantize_channel(e, t, dv, c.v_group, c.v_codes + slot * (dv / 2),
-                             c.v_scales + slot * (dv / c.v_group), wave_max);
-        }
-    }
-    if (c.idx_format == CSKV_IDX_FP4) {
-        if (t < c.idx_dim)                      // whole waves: idx_dim is 64 or 128
-            quantize_idx_fp4(bf16_bits_to_f32(key_t), t,
-                             reinterpret_cast<uint8_t *>(c.idx_keys) + slot * (c.idx_dim / 2),
-                             c.idx_scales + slot * (c.idx_dim / 16));
-    } else if (t < c.idx_dim) {
-        c.idx_keys[slot * c.idx_dim + t] = key_t;
-    }
-}
-
 // One block per input row.  A block whose row completes an entry quantises
 // that entry (compressor mode: from the compressor's output; entries mode:
 // the row itself) and writes its codes, scales and indexer key.  kFinalize
 // (one row per sequence): the block then also finalises its sequence and
-// writes the row's window entry when a window ring is given.
-template <bool kCompress, bool kFinalize>
+// writes the row's window entry when a window ring is given.  kHead (a
+// decode step, one row per sequence, compressor mode): the block writes only
+// the entry's indexer key and records its cache row in a.slots (-1: none);
+// the entry itself is compressed and quantised later (quantize_main_512),
+// by kernels that run after this one and read the record, so the token
+// counts can advance here.
+template <bool kCompress, bool kFinalize, bool kHead = false>
 __global__ __launch_bounds__(kAppendThreads) void quantize_kernel(AppendArgs a)
 {
+    static_assert(!kHead || (kCompress && kFinalize), "the head of a one-row compressor append");
     __shared__ float wave_max[kAppendThreads / kWave];
     const cskv_cache &c = a.c;
     const int64_t r = blockIdx.x;
@@ -395,15 +35,22 @@ __global__ __launch_bounds__(kAppendThreads) void quantize_kernel(AppendArgs a)
     // entry row of a row that completes none is read and dropped)
     const int b0 = seq_of_row(a.cu_new, c.batch, (int)r);
     const int64_t p = c.n_tokens[b0];
-    const float ev = kCompress ? a.ent[(size_t)r * kDim + t] : a.tokens[(size_t)r * kDim + t];
+    const float ev = kHead ? 0.f : kCompress ? a.ent[(size_t)r * kDim + t] : a.tokens[(size_t)r * kDim + t];
     const uint16_t key_t = a.idx_rows[(size_t)r * c.idx_dim + (t < c.idx_dim ? t : 0)];
     const float xw = kFinalize && a.swa_ring ? a.swa_rows[(size_t)r * kDim + t] : 0.f;
     const RowInfo ri = row_info<kCompress>(a, r, b0, p);
+    int64_t rec = -1;
     if (ri.entry >= 0) {
         const int64_t slot = plane_row(c, ri.b, ri.entry);
-        if (slot >= 0) quantize_entry(a, ev, t, (size_t)slot, key_t, wave_max);
-        else if (t == 0) atomicOr(c.status, CSKV_STATUS_BAD_PAGE);
+        if (slot >= 0) {
+            if (kHead) store_idx_key(a, t, (size_t)slot, key_t);
+            else quantize_entry(a, ev, t, (size_t)slot, key_t, wave_max);
+            rec = slot;
+        } else if (t == 0) {
+            atomicOr(c.status, CSKV_STATUS_BAD_PAGE);
+        }
     }
+    if (kHead && t == 0) a.slots[r] = rec;
     if (kFinalize) {
         const int b = (int)r;
         __syncthreads();                            // every thread has read n_tokens[b]
@@ -1112,6 +759,31 @@ hipError_t launch_kv_append(const cskv_cache &c, const float *tokens, const int3
         launch_kernel(quantize_kernel<false, false>, qgrid, qblock, s, tl.start, nullptr, a);
         launch_kernel(append_finalize_kernel<false>, dim3((unsigned)c.batch), dim3(kWave), s, nullptr, tl.stop, a);
     }
+    return hipGetLastError();
+}
+
+static size_t deferred_ent_bytes(int batch) { return ((size_t)batch * kDim * sizeof(float) + 255) / 256 * 256; }
+
+size_t deferred_entry_bytes(int batch)
+{
+    return deferred_ent_bytes(batch) + ((size_t)batch * sizeof(int64_t) + 255) / 256 * 256;
+}
+
+DeferredEntry deferred_entry_at(void *base, int batch, const float *tokens, const float *w_comp)
+{
+    char *p = static_cast<char *>(base);
+    return DeferredEntry{tokens, w_comp, reinterpret_cast<float *>(p),
+                         reinterpret_cast<int64_t *>(p + deferred_ent_bytes(batch))};
+}
+
+hipError_t launch_append_head(const cskv_cache &c, const DeferredEntry &d, const uint16_t *idx_rows,
+                              hipStream_t s, uint16_t *swa_ring, const float *swa_rows, int swa_window)
+{
+    const AppendArgs a{c, d.tokens, nullptr, d.w_comp, idx_rows, d.ent, c.batch, swa_ring, swa_rows, swa_window,
+                       d.slots};
+    const TimedLaunch tl = timer_take(CSKV_KERNEL_APPEND);
+    launch_kernel(quantize_kernel<true, true, true>, dim3((unsigned)c.batch), dim3(kAppendThreads), s, tl.start,
+                  tl.stop, a);
     return hipGetLastError();
 }
 

@@ -20,6 +20,9 @@
 //
 // Sources cited as [P2]:
 //   P2  "DeepSeek V1 到 V4.1-Flash，单 token 的 global KV 如何从 389,000 B 压缩到 890 B的？"
+#include <type_traits>
+
+#include "append_dev.hpp"
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -568,14 +571,14 @@ __device__ __forceinline__ uint32_t bound_grouped(SelectSmem<THREADS> &sm, const
     return bound_from_groups<THREADS, GS>(sm, a, b, tl, tlvm, nt);
 }
 
+// Block x of nx of sequence b.
 template <int KEYS, int THREADS, int G>
-__global__ __launch_bounds__(THREADS) void topk_bound_slice_kernel(SelectArgs a)
+__device__ __forceinline__ void bound_slice(SelectSmem<THREADS> &sm, const SelectArgs &a, int x, int nx, int b)
 {
-    __shared__ SelectSmem<THREADS> sm;
     constexpr int PER = KEYS / THREADS;
     constexpr int kTPer = 16;
-    const int b = blockIdx.y, t = threadIdx.x;
-    const int64_t first = (int64_t)blockIdx.x * KEYS;
+    const int t = threadIdx.x;
+    const int64_t first = (int64_t)x * KEYS;
     const int64_t ncap = a.capacity - first < KEYS ? a.capacity - first : KEYS;
     uint32_t key[PER], kidx[PER];
     uint64_t kvm;
@@ -600,15 +603,90 @@ __global__ __launch_bounds__(THREADS) void topk_bound_slice_kernel(SelectArgs a)
         V = bound_grouped<THREADS, (G > 2 ? 2 : G)>(sm, a, b, nt);
     else
         V = bound_grouped<THREADS, G>(sm, a, b, nt);
-    for (int s = blockIdx.x;;) {
+    for (int s = x;;) {
         bound_candidates<KEYS, THREADS>(sm, a, b, s, key, kvm, V);
-        s += gridDim.x;
+        s += nx;
         if ((int64_t)s * KEYS >= E) break;
         __syncthreads();                           // sm.wave_sum is used again
         const int64_t f = (int64_t)s * KEYS;
         const Items kit{a.keys + (size_t)b * a.key_stride + f, nullptr, E - f < KEYS ? E - f : KEYS, f};
         kvm = load_keys<false, THREADS, PER>(kit, 0, key, kidx);
     }
+}
+
+template <int KEYS, int THREADS, int G>
+__global__ __launch_bounds__(THREADS) void topk_bound_slice_kernel(SelectArgs a)
+{
+    __shared__ SelectSmem<THREADS> sm;
+    bound_slice<KEYS, THREADS, G>(sm, a, blockIdx.x, gridDim.x, blockIdx.y);
+}
+
+// The slice launch of a decode step that carries its deferred entry: plane
+// z = 0 of the grid holds the slice blocks; the blocks of the planes after
+// it hold the compressor's waves (compress_wave_slots: 4 rows by 2 channels
+// each, nx x ceil(batch / 4) of them), taken in order, 8 to a block.  A
+// block's kind follows from its index alone, so the slice blocks issue their
+// loads without waiting for an argument first.  The two kinds share no data.  Two blocks fit a CU (at most 128
+// registers a lane), so the compressor's blocks run beside the slice blocks
+// rather than after them.  Measured against 5 channels a wave and against
+// blocks that stage 8 rows in LDS for 16 channels, this shape adds the least
+// to the launch on the steps that complete entries (about 3 us at 64K x 32).
+constexpr int kCarryRows = 4, kCarryCpw = 2, kCarryWaves = kSliceThreads / kWave;
+constexpr int kCarryMaxBatch = 64;
+
+// What the carried compressor and quantiser read, and nothing more: kernel
+// arguments are copied into every launch's argument buffer and loaded by its
+// waves, and the full descriptors made both carrying launches measurably
+// slower (624 argument bytes against 128).
+struct CarriedEntry {
+    const float *tokens, *w_comp, *pending;
+    float *ent;
+    int64_t *slots;
+    uint8_t *k_codes, *v_codes;
+    float *k_scales, *v_scales;
+    int32_t batch, dim, rope_dim, k_group, v_group, k_format;
+};
+
+__device__ __forceinline__ AppendArgs append_args_of(const CarriedEntry &e)
+{
+    AppendArgs d{};
+    d.c.batch = e.batch;
+    d.c.dim = e.dim;
+    d.c.rope_dim = e.rope_dim;
+    d.c.k_group = e.k_group;
+    d.c.v_group = e.v_group;
+    d.c.k_format = e.k_format;
+    d.c.k_codes = e.k_codes;
+    d.c.k_scales = e.k_scales;
+    d.c.v_codes = e.v_codes;
+    d.c.v_scales = e.v_scales;
+    d.c.pending = const_cast<float *>(e.pending);
+    d.tokens = e.tokens;
+    d.w_comp = e.w_comp;
+    d.ent = e.ent;
+    d.total_new = e.batch;
+    d.slots = e.slots;
+    return d;
+}
+
+struct CarriedCompress {
+    CarriedEntry e;
+    int nx, waves;
+};
+
+template <int KEYS, int THREADS, int G>
+__global__ __launch_bounds__(THREADS, 2 * THREADS / 256) void topk_bound_slice_carry_kernel(SelectArgs a,
+                                                                                           CarriedCompress cc)
+{
+    static_assert(THREADS == kCarryWaves * kWave, "the compressor's block shape");
+    __shared__ SelectSmem<THREADS> sm;
+    if (blockIdx.z == 0) {
+        bound_slice<KEYS, THREADS, G>(sm, a, blockIdx.x, gridDim.x, blockIdx.y);
+        return;
+    }
+    const int cb = (((int)blockIdx.z - 1) * (int)gridDim.y + (int)blockIdx.y) * (int)gridDim.x + (int)blockIdx.x;
+    const int wi = cb * kCarryWaves + (int)(threadIdx.x / kWave);
+    if (wi < cc.waves) compress_wave_slots<kCarryRows, kCarryCpw>(append_args_of(cc.e), wi % cc.nx, wi / cc.nx);
 }
 
 // Bound select, second kernel: sequence b's candidate lists (slice order is
@@ -624,17 +702,24 @@ constexpr int kFinalPer = 12;
 constexpr int kFinalCap = kFinalThreads * kFinalPer;
 constexpr int kSpec = 128, kSpecSlices = 32;
 template <int MAXS>
-__global__ __launch_bounds__(kFinalThreads) void topk_bound_final_kernel(SelectArgs a)
+struct FinalSmem {
+    SelectSmem<kFinalThreads> sm;
+    alignas(16) uint2 lc[kFinalCap];
+    uint32_t pre[MAXS + 1];
+};
+
+template <int MAXS>
+__device__ __forceinline__ void bound_final(FinalSmem<MAXS> &f, const SelectArgs &a, int b)
 {
     static_assert(MAXS <= kFinalThreads && MAXS >= kSpecSlices, "one slice count per thread");
     constexpr int kA = 4096 / MAXS;                // pairs of every slice
     constexpr int kB = MAXS > kSpecSlices ? kSpec : 0;   // more pairs of the first kSpecSlices
     constexpr int kSpecPer = 4096 / kFinalThreads, kSpecPerB = kB ? kSpecSlices * kB / kFinalThreads : 0;
     auto covered = [](int sl) { return (uint32_t)(kA + (sl < kSpecSlices ? kB : 0)); };
-    __shared__ SelectSmem<kFinalThreads> sm;
-    __shared__ __attribute__((aligned(16))) uint2 lc[kFinalCap];
-    __shared__ uint32_t pre[MAXS + 1];
-    const int b = blockIdx.x, t = threadIdx.x;
+    SelectSmem<kFinalThreads> &sm = f.sm;
+    uint2 *const lc = f.lc;
+    uint32_t *const pre = f.pre;
+    const int t = threadIdx.x;
     const uint2 *cl = a.cand + (size_t)b * a.cand_stride;
     // speculative reads, unused for slices past the entries or the capacity
     uint2 sp[kSpecPer], spb[kSpecPerB ? kSpecPerB : 1];
@@ -709,6 +794,32 @@ __global__ __launch_bounds__(kFinalThreads) void topk_bound_final_kernel(SelectA
         select_topk<true, false, kFinalThreads, 2>(sm, it, a.k, out, nullptr);
     else
         select_topk<true, false, kFinalThreads, kFinalPer>(sm, it, a.k, out, nullptr);
+}
+
+template <int MAXS>
+__global__ __launch_bounds__(kFinalThreads) void topk_bound_final_kernel(SelectArgs a)
+{
+    __shared__ FinalSmem<MAXS> f;
+    bound_final<MAXS>(f, a, blockIdx.x);
+}
+
+// The final launch of a decode step that carries its deferred entry: block
+// (b, 0) selects for sequence b, block (b, 1) quantises its compressed entry
+// (if the head recorded one) into its cache row, before attention reads it.
+template <int MAXS>
+__global__ __launch_bounds__(kFinalThreads) void topk_bound_final_carry_kernel(SelectArgs a, CarriedEntry e)
+{
+    static_assert(kFinalThreads == 512, "quantize_main_512 takes the entry on 512 threads");
+    __shared__ FinalSmem<MAXS> f;
+    const int b = blockIdx.x;
+    if (blockIdx.y == 0) {
+        bound_final<MAXS>(f, a, b);
+        return;
+    }
+    const int64_t slot = e.slots[b];
+    if (slot >= 0)
+        quantize_main_512(append_args_of(e), e.ent + (size_t)b * kDim, threadIdx.x, (size_t)slot,
+                          reinterpret_cast<float *>(f.sm.bins));
 }
 
 // Sequence b of a cache whose capacity spans several slices: the final top-k
@@ -842,11 +953,18 @@ void launch_select(const SelectArgs &se, int batch, hipStream_t s, const TimedLa
 
 }  // namespace
 
+bool topk_carries_entry(const cskv_cache &c, int k)
+{
+    return c.batch <= kCarryMaxBatch && topk_workspace(c, k).tiles;
+}
+
 hipError_t launch_indexer_topk(const cskv_cache &c, const uint16_t *q_idx, int heads,
                                const float *head_w, int k, int32_t *out_idx, void *ws,
-                               hipStream_t s, const PoolBuild *pool, float *out_scores)
+                               hipStream_t s, const PoolBuild *pool, float *out_scores,
+                               const DeferredEntry *entry)
 {
     const TopkWorkspace lay = topk_workspace(c, k);
+    if (entry && !lay.tiles) return hipErrorInvalidValue;     // only the bound select carries an entry
     uint32_t *keys = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + lay.keys_off);
     uint2 *cand = reinterpret_cast<uint2 *>(static_cast<char *>(ws) + lay.cand_off);
     uint32_t *bkeys = nullptr;
@@ -875,7 +993,32 @@ hipError_t launch_indexer_topk(const cskv_cache &c, const uint16_t *q_idx, int h
         const int per = 512 / c.batch > 32 ? 512 / c.batch : 32;
         const dim3 sg((unsigned)(slices < per ? slices : per), (unsigned)c.batch), fg((unsigned)c.batch);
         const int g = tile_group(c);
-        if (g == 1) {
+        if (entry) {
+            // the step's deferred entry: compressed in the slice launch,
+            // quantised in the final launch (grid rows / blocks past the
+            // select's)
+            const CarriedEntry d{entry->tokens, entry->w_comp, c.pending, entry->ent, entry->slots,
+                                 c.k_codes, c.v_codes, c.k_scales, c.v_scales, c.batch,
+                                 c.dim, c.rope_dim, c.k_group, c.v_group, c.k_format};
+            const int nx = (kDim + kCarryCpw - 1) / kCarryCpw;
+            const CarriedCompress cc{d, nx, nx * ((c.batch + kCarryRows - 1) / kCarryRows)};
+            const int blocks = (cc.waves + kCarryWaves - 1) / kCarryWaves;
+            const int plane = (int)sg.x * c.batch;
+            const dim3 cg(sg.x, (unsigned)c.batch, (unsigned)(1 + (blocks + plane - 1) / plane));
+            auto slice_launch = [&](auto gg) {
+                launch_kernel(topk_bound_slice_carry_kernel<kSliceKeys, kSliceThreads, decltype(gg)::value>, cg,
+                              dim3(kSliceThreads), s, tk.start, nullptr, se, cc);
+            };
+            if (g == 1) slice_launch(std::integral_constant<int, 1>{});
+            else if (g == 2) slice_launch(std::integral_constant<int, 2>{});
+            else slice_launch(std::integral_constant<int, 4>{});
+            const dim3 qg((unsigned)c.batch, 2);
+            if (g == 1)
+                launch_kernel(topk_bound_final_carry_kernel<32>, qg, dim3(kFinalThreads), s, nullptr, tk.stop, se, d);
+            else
+                launch_kernel(topk_bound_final_carry_kernel<kTileMaxCap / kSliceKeys>, qg, dim3(kFinalThreads), s,
+                              nullptr, tk.stop, se, d);
+        } else if (g == 1) {
             launch_kernel(topk_bound_slice_kernel<kSliceKeys, kSliceThreads, 1>, sg, dim3(kSliceThreads), s,
                           tk.start, nullptr, se);
             launch_kernel(topk_bound_final_kernel<32>, fg, dim3(kFinalThreads), s, nullptr, tk.stop, se);

@@ -71,9 +71,31 @@ struct PoolWorkspace {
     int bslices;
 };
 PoolWorkspace pool_workspace(const cskv_cache &c, int k, int pool_blocks, int block);
+// A decode step's append (one new token per sequence, compressor mode)
+// spread over the step's first top-k: launch_append_head writes each
+// completed entry's indexer key, the pending tokens, the token counts and
+// the window row, and records the new entry's cache row in slots (-1: none);
+// launch_indexer_topk with `entry` then compresses the entry in its slice
+// launch and quantises it into the cache in its final launch, so attention,
+// which follows, reads it.  Only the bound select carries an entry, for at
+// most 64 sequences (topk_carries_entry).  ent and slots live beside the top-k's workspace
+// (deferred_entry_bytes).
+struct DeferredEntry {
+    const float *tokens;   // [batch][576] the step's tokens
+    const float *w_comp;   // [576][1152] compressor weights
+    float *ent;            // [batch][576] the compressor's output
+    int64_t *slots;        // [batch] the cache row of each new entry, -1: none
+};
+size_t deferred_entry_bytes(int batch);
+// ent and slots laid out from base (256-byte aligned, deferred_entry_bytes long).
+DeferredEntry deferred_entry_at(void *base, int batch, const float *tokens, const float *w_comp);
+hipError_t launch_append_head(const cskv_cache &c, const DeferredEntry &d, const uint16_t *idx_rows,
+                              hipStream_t s, uint16_t *swa_ring, const float *swa_rows, int swa_window);
+bool topk_carries_entry(const cskv_cache &c, int k);
 hipError_t launch_indexer_topk(const cskv_cache &c, const uint16_t *q_idx, int heads,
                                const float *head_w, int k, int32_t *out_idx, void *ws,
-                               hipStream_t s, const PoolBuild *pool = nullptr, float *out_scores = nullptr);
+                               hipStream_t s, const PoolBuild *pool = nullptr, float *out_scores = nullptr,
+                               const DeferredEntry *entry = nullptr);
 // Top-k among the entries of the pooled blocks (a later layer of the
 // hierarchical indexer); ws holds pool_workspace().inpool_total bytes.
 hipError_t launch_indexer_topk_in_pool(const cskv_cache &c, const uint16_t *q_idx, int heads,
