@@ -143,6 +143,12 @@ def test_encoders_exhaustive_all_fp32(orc, exhaustive_bin):
     r = subprocess.run([exhaustive_bin, ob.LIB, "0", str(1 << 32)], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "e2m1_mismatch=0 bf16_mismatch=0" in r.stdout
+    # the stored checksums the device encoders are checked against come
+    # from this same oracle run
+    with open(os.path.join(HERE, "golden", "encoder_checksums.json")) as f:
+        g = json.load(f)
+    assert f"e2m1_sum={g['e2m1_sum']} bf16_sum={g['bf16_sum']}" in r.stdout
+    assert f"tested={g['tested']} " in r.stdout
 
 
 # ---------------------------------------------------------------- quantiser
