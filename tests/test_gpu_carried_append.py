@@ -143,3 +143,36 @@ def test_carried_step_equals_separate_calls(ck, paged, kg, vg, idx_format, k_for
         assert np.array_equal(host(o_ref).view(np.uint32), host(o_got).view(np.uint32)), f"outputs, step {step}"
         assert np.array_equal(host(l_ref).view(np.uint32), host(l_got).view(np.uint32)), f"lse, step {step}"
     assert int(host(got.status)[0]) & ck.STATUS_OVERFLOW
+
+
+@pytest.mark.parametrize("batch,cap,lens_fn", [
+    # capacity past 262,144: groups of 4 tiles in the slice launch, the 128-slice final launch
+    (3, 300000, lambda g, B: [20000, 0, 4097]),
+    # the largest batch that carries its append, and the first that does not
+    (64, 5000, lambda g, B: [int(x) for x in g.integers(0, 5000, size=B)]),
+    (65, 5000, lambda g, B: [int(x) for x in g.integers(0, 5000, size=B)]),
+])
+def test_carried_step_limits_equal_separate_calls(ck, batch, cap, lens_fn):
+    """Steps at the carried path's limits against separate calls, bit for bit
+    over two steps (one holding a pending token, one completing entries)."""
+    g = np.random.default_rng(batch)
+    lens = lens_fn(g, batch)
+    lens[0] = min(max(lens[0], 4097), cap)         # one sequence past one slice
+    w = synth.scaled(synth.WORKLOADS["group_128k_b64"], batch=batch, entries=max(lens), layers=("full",))
+    W = dev(synth.w_comp(w))
+    ref, got = (ck.Cache.allocate(batch, cap, 64, 0, w.idx_dim) for _ in range(2))
+    rows = np.concatenate([synth.cache_entries(w, b, n) for b, n in enumerate(lens)])
+    keys = np.concatenate([synth.cache_idx_keys(w, b, n) for b, n in enumerate(lens)])
+    cu = dev(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+    for c in (ref, got):
+        ck.kv_append_fp4(c, dev(rows), cu, None, dev(keys))
+    for step in range(2):
+        st = synth.step_inputs(w, step)
+        ring_ref, ring_got = _ring(ref, w, st), _ring(got, w, st)
+        i_ref, o_ref, l_ref = _by_parts(ck, ref, w, st, ring_ref, W)
+        i_got, o_got, l_got = _by_group(ck, got, w, st, ring_got, W)
+        _same_planes(ref, got)
+        assert np.array_equal(host(ring_ref), host(ring_got)), f"window ring, step {step}"
+        assert np.array_equal(host(i_ref), host(i_got)), f"indices, step {step}"
+        assert np.array_equal(host(o_ref).view(np.uint32), host(o_got).view(np.uint32)), f"outputs, step {step}"
+        assert np.array_equal(host(l_ref).view(np.uint32), host(l_got).view(np.uint32)), f"lse, step {step}"
