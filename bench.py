@@ -616,7 +616,7 @@ def main():
 
 
 ALU_PEAK_TFLOPS = 157.3      # MI355X fp32 vector, packed FMAs: 256 CUs x 4 SIMDs x 16 lanes x 2 x 2 FLOP x 2.4 GHz
-ALU_PEAK_UNPACKED_TFLOPS = 78.6   # the same without packed fp32 (this build compiles it off)
+ALU_PEAK_UNPACKED_TFLOPS = 78.6   # the same without packed fp32 (the library compiles it off)
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix cores
 MODEL_PLAN = "model_plan_64k_b32"
 
