@@ -108,6 +108,19 @@ __device__ __forceinline__ void store_b32(__amdgpu_buffer_rsrc_t r, uint32_t off
 // ReLU in one integer max: a float with its sign bit set (a negative value,
 // -0) has a negative bit pattern and becomes +0, any other stays as it is.
 // (fmaxf would first quiet a possible signalling NaN: two instructions.)
+// A DMA of 16 or 4 bytes per lane from a buffer resource into LDS at dst
+// (+ bytes * lane), non-temporal; an offset past the resource reads zeros.
+// (Kept out of the kernels' bodies: the host compilation pass drops a kernel
+// template whose body calls this builtin directly.)
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint8_t *dst, uint32_t voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, voff, 0, 0, kNonTemporal);
+}
+__device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t r, uint8_t *dst, uint32_t voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 4, voff, 0, 0, kNonTemporal);
+}
+
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // Cross-lane reductions on the VALU (DPP and lane swaps, no LDS round trip).
@@ -402,9 +415,10 @@ __global__ __launch_bounds__(kScanThreads, kScanBlocksPerCU) void indexer_scan_k
 // is converted to bf16 by the hardware FP4 conversion, which applies the
 // group's power-of-two scale exactly, and goes through the same bf16 MFMA
 // and epilogue as the bf16 scan.
-template <int DI, int MT, bool POOL, bool PAGED>
+template <int DI, int MT, bool POOL, bool PAGED, bool DENSE = false>
 __global__ __launch_bounds__(kScanThreads, kScanBlocksPerCU) void indexer_scan_fp4_kernel(ScanArgs a)
 {
+    static_assert(!DENSE || (!POOL && !PAGED), "dense rows are neither pooled nor paged");
     constexpr int kSteps = DI / 32;
     constexpr int kTileKeys = 64;
     constexpr int kCodeBytes = DI / 2;                   // per key
@@ -478,9 +492,31 @@ __global__ __launch_bounds__(kScanThreads, kScanBlocksPerCU) void indexer_scan_f
             return e;
         }
     };
+    // DENSE (the host's choice for rows neither pooled nor paged whose run
+    // offsets fit 31 bits): codes and scales through two buffer resources
+    // over the block's run; a lane's offsets within a tile are fixed (load s
+    // adds 1024 s, or 256 s for the scales), one 32-bit add places the tile,
+    // and rows past the run lie outside the resources and read as zeros (their
+    // scores are dropped).  Otherwise each row comes from row_of.
+    const __amdgpu_buffer_rsrc_t crs =
+        make_rsrc(kb + (size_t)e_begin * kCodeBytes, DENSE ? (uint32_t)((e_end - e_begin) * kCodeBytes) : 0u);
+    const __amdgpu_buffer_rsrc_t srs =
+        make_rsrc(sb + (size_t)e_begin * kScaleBytes, DENSE ? (uint32_t)((e_end - e_begin) * kScaleBytes) : 0u);
+    const uint32_t coff = (uint32_t)((w * kTileKeys + lane / kChunks) * kCodeBytes +
+                                     16 * ((lane % kChunks) ^ ((lane / kChunks) % kChunks)));
+    const uint32_t soff = (uint32_t)((w * kTileKeys + 4 * lane / kScaleBytes) * kScaleBytes + (4 * lane) % kScaleBytes);
     auto issue = [&](int i) {
-        const int64_t t0 = e_begin + (int64_t)(w + kScanWaves * i) * kTileKeys;
         uint8_t *slot = &ring[w][i % kRing][0];
+        if constexpr (DENSE) {
+            const uint32_t tk = (uint32_t)(kScanWaves * i) * kTileKeys;
+#pragma unroll
+            for (int s = 0; s < kInstC; ++s) load_lds16(crs, slot + 1024 * s, coff + tk * kCodeBytes + 1024 * s);
+#pragma unroll
+            for (int s = 0; s < kInstS; ++s)
+                load_lds4(srs, slot + kTileCode + 256 * s, soff + tk * kScaleBytes + 256 * s);
+            return;
+        }
+        const int64_t t0 = e_begin + (int64_t)(w + kScanWaves * i) * kTileKeys;
 #pragma unroll
         for (int s = 0; s < kInstC; ++s) {
             const int u = 64 * s + lane, r = u / kChunks, p = u % kChunks, c = p ^ (r % kChunks);
@@ -616,6 +652,23 @@ static void scan_dispatch_t(const cskv_cache &c, int heads, const ScanArgs &sa, 
     const TimedLaunch ts = timer_take(CSKV_KERNEL_INDEXER_SCAN);
     auto scan = [&](auto kernel) { launch_kernel(kernel, grid, dim3(kScanThreads), s, ts.start, ts.stop, sa); };
     if (c.idx_format == CSKV_IDX_FP4) {
+        // dense rows whose byte offsets within a sequence fit 31 bits
+        constexpr bool kCanDense = !POOL && !PAGED;
+        if (kCanDense && (uint64_t)c.capacity * (uint64_t)(c.idx_dim / 2) < (1ull << 31)) {
+            constexpr bool D = kCanDense;
+            if (c.idx_dim == 128) {
+                if (mt == 4) scan(indexer_scan_fp4_kernel<128, 4, POOL, PAGED, D>);
+                else if (mt == 3) scan(indexer_scan_fp4_kernel<128, 3, POOL, PAGED, D>);
+                else if (mt == 2) scan(indexer_scan_fp4_kernel<128, 2, POOL, PAGED, D>);
+                else scan(indexer_scan_fp4_kernel<128, 1, POOL, PAGED, D>);
+            } else {
+                if (mt == 4) scan(indexer_scan_fp4_kernel<64, 4, POOL, PAGED, D>);
+                else if (mt == 3) scan(indexer_scan_fp4_kernel<64, 3, POOL, PAGED, D>);
+                else if (mt == 2) scan(indexer_scan_fp4_kernel<64, 2, POOL, PAGED, D>);
+                else scan(indexer_scan_fp4_kernel<64, 1, POOL, PAGED, D>);
+            }
+            return;
+        }
         if (c.idx_dim == 128) {
             if (mt == 4) scan(indexer_scan_fp4_kernel<128, 4, POOL, PAGED>);
             else if (mt == 3) scan(indexer_scan_fp4_kernel<128, 3, POOL, PAGED>);
