@@ -151,6 +151,24 @@ def test_encoders_exhaustive_all_fp32(orc, exhaustive_bin):
     assert f"tested={g['tested']} " in r.stdout
 
 
+def test_oracle_under_host_sanitizers(tmp_path):
+    """The oracle's C built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (every report fatal), driven through every entry point on small caches
+    whose planes are allocated at exactly their layout's size, in every
+    storage format and over the edge cases it handles (empty, full and
+    overflowing sequences, pending tokens, k past the entry count, -1 and
+    out-of-range indices, empty windows, padded pools)."""
+    import oracle.build as ob
+    exe = tmp_path / "sanitize_oracle"
+    flags = [f for f in ob.CFLAGS if f not in ("-O2", "-fPIC", "-shared", "-fopenmp")]
+    subprocess.run(["gcc", *flags, "-O1", "-g", "-fno-omit-frame-pointer", "-Wno-unknown-pragmas",
+                    "-fsanitize=address,undefined", "-fno-sanitize-recover=all", ob.SRC,
+                    os.path.join(HERE, "native", "sanitize_oracle.c"), "-lm", "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
+    assert r.stdout.rstrip().endswith("ok") and "runtime error" not in r.stderr, r.stderr[-4000:]
+
+
 # ---------------------------------------------------------------- quantiser
 
 def _codes(packed):
