@@ -208,21 +208,19 @@ __device__ __forceinline__ void compress_wave(const AppendArgs &a, int cpw, int 
 // The compressor of a decode step whose head kernel has advanced the token
 // counts (one row per sequence, a.slots recorded), one wave: a row completes
 // an entry exactly when its slot is recorded, its partner being the pending
-// token.  The wave takes rows [E by, E by + E) and output channels
-// [CPW bx, CPW bx + CPW); the slots, the W rows and the rows' terms are all
-// loaded before the first wait.  Same arithmetic as compress_wave
+// token.  The wave takes output channels [CPW bx, CPW bx + CPW) and RG groups
+// of E rows in turn, rows [E (RG by + g), E (RG by + g) + E) for g < RG: the
+// W rows are loaded once, then per group the slots and the rows' terms, all
+// before the group's first wait.  Same arithmetic as compress_wave
 // (compress_dot).
-template <int E, int CPW>
+template <int E, int CPW, int RG>
 __device__ __forceinline__ void compress_wave_slots(const AppendArgs &a, int bx, int by)
 {
     constexpr int kH = kCompTerms / 2;
     const int lane = threadIdx.x & (kWave - 1);
-    const int r0 = by * E, c0 = bx * CPW;
+    const int c0 = bx * CPW;
     // only the sign of a slot matters: its high word (little-endian int64)
     const int32_t *slot_hi = reinterpret_cast<const int32_t *>(a.slots) + 1;
-    int32_t sl[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) sl[e] = slot_hi[2 * (r0 + e < a.total_new ? r0 + e : r0)];
     const float2 *wl = reinterpret_cast<const float2 *>(a.w_comp) + kH * lane;
     float2 w[CPW][kH];
 #pragma unroll
@@ -231,29 +229,36 @@ __device__ __forceinline__ void compress_wave_slots(const AppendArgs &a, int bx,
 #pragma unroll
         for (int t = 0; t < kH; ++t) w[d][t] = wl[(size_t)c * kDim + t];
     }
-    float u[E][kCompTerms];
+    for (int g = 0; g < RG; ++g) {
+        const int r0 = (by * RG + g) * E;
+        if (r0 >= a.total_new) break;
+        int32_t sl[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int r = r0 + e < a.total_new ? r0 + e : r0;   // a row past the batch reads row r0, unused
-        const float *src = lane < kWave / 2 ? a.c.pending + (size_t)r * kDim + kCompTerms * lane
-                                            : a.tokens + (size_t)r * kDim + kCompTerms * (lane - kWave / 2);
+        for (int e = 0; e < E; ++e) sl[e] = slot_hi[2 * (r0 + e < a.total_new ? r0 + e : r0)];
+        float u[E][kCompTerms];
 #pragma unroll
-        for (int t = 0; t < kH; ++t) {
-            const float2 x = reinterpret_cast<const float2 *>(src)[t];
-            u[e][2 * t] = x.x;
-            u[e][2 * t + 1] = x.y;
+        for (int e = 0; e < E; ++e) {
+            const int r = r0 + e < a.total_new ? r0 + e : r0;   // a row past the batch reads row r0, unused
+            const float *src = lane < kWave / 2 ? a.c.pending + (size_t)r * kDim + kCompTerms * lane
+                                                : a.tokens + (size_t)r * kDim + kCompTerms * (lane - kWave / 2);
+#pragma unroll
+            for (int t = 0; t < kH; ++t) {
+                const float2 x = reinterpret_cast<const float2 *>(src)[t];
+                u[e][2 * t] = x.x;
+                u[e][2 * t + 1] = x.y;
+            }
         }
-    }
-    uint32_t act = 0;
+        uint32_t act = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) act |= (uint32_t)(r0 + e < a.total_new && sl[e] >= 0) << e;
+        for (int e = 0; e < E; ++e) act |= (uint32_t)(r0 + e < a.total_new && sl[e] >= 0) << e;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        if (!((act >> e) & 1u)) continue;
+        for (int e = 0; e < E; ++e) {
+            if (!((act >> e) & 1u)) continue;
 #pragma unroll
-        for (int d = 0; d < CPW; ++d) {
-            const float res = compress_dot(w[d], u[e]);
-            if (lane == 0 && c0 + d < kDim) a.ent[(size_t)(r0 + e) * kDim + c0 + d] = res;
+            for (int d = 0; d < CPW; ++d) {
+                const float res = compress_dot(w[d], u[e]);
+                if (lane == 0 && c0 + d < kDim) a.ent[(size_t)(r0 + e) * kDim + c0 + d] = res;
+            }
         }
     }
 }

@@ -623,15 +623,18 @@ __global__ __launch_bounds__(THREADS) void topk_bound_slice_kernel(SelectArgs a)
 
 // The slice launch of a decode step that carries its deferred entry: plane
 // z = 0 of the grid holds the slice blocks; the blocks of the planes after
-// it hold the compressor's waves (compress_wave_slots: 4 rows by 2 channels
-// each, nx x ceil(batch / 4) of them), taken in order, 8 to a block.  A
+// it hold the compressor's waves (compress_wave_slots: 2 channels by two
+// groups of 4 rows each, nx x ceil(batch / 8) of them), taken in order, 8 to
+// a block.  A
 // block's kind follows from its index alone, so the slice blocks issue their
 // loads without waiting for an argument first.  The two kinds share no data.  Two blocks fit a CU (at most 128
 // registers a lane), so the compressor's blocks run beside the slice blocks
-// rather than after them.  Measured against 5 channels a wave and against
-// blocks that stage 8 rows in LDS for 16 channels, this shape adds the least
-// to the launch on the steps that complete entries (about 3 us at 64K x 32).
-constexpr int kCarryRows = 4, kCarryCpw = 2, kCarryWaves = kSliceThreads / kWave;
+// rather than after them.  Measured against 5 channels a wave, against
+// blocks that stage 8 rows in LDS for 16 channels and against one, three or
+// four row groups a wave, this shape adds the least to the launch on the
+// steps that complete entries (about 2 us at 64K x 32: its 144 blocks and the
+// 288 slice blocks run in one round of two blocks a CU).
+constexpr int kCarryRows = 4, kCarryCpw = 2, kCarryGroups = 2, kCarryWaves = kSliceThreads / kWave;
 constexpr int kCarryMaxBatch = 64;
 
 // What the carried compressor and quantiser read, and nothing more: kernel
@@ -686,7 +689,8 @@ __global__ __launch_bounds__(THREADS, 2 * THREADS / 256) void topk_bound_slice_c
     }
     const int cb = (((int)blockIdx.z - 1) * (int)gridDim.y + (int)blockIdx.y) * (int)gridDim.x + (int)blockIdx.x;
     const int wi = cb * kCarryWaves + (int)(threadIdx.x / kWave);
-    if (wi < cc.waves) compress_wave_slots<kCarryRows, kCarryCpw>(append_args_of(cc.e), wi % cc.nx, wi / cc.nx);
+    if (wi < cc.waves)
+        compress_wave_slots<kCarryRows, kCarryCpw, kCarryGroups>(append_args_of(cc.e), wi % cc.nx, wi / cc.nx);
 }
 
 // Bound select, second kernel: sequence b's candidate lists (slice order is
@@ -1001,7 +1005,8 @@ hipError_t launch_indexer_topk(const cskv_cache &c, const uint16_t *q_idx, int h
                                  c.k_codes, c.v_codes, c.k_scales, c.v_scales, c.batch,
                                  c.dim, c.rope_dim, c.k_group, c.v_group, c.k_format};
             const int nx = (kDim + kCarryCpw - 1) / kCarryCpw;
-            const CarriedCompress cc{d, nx, nx * ((c.batch + kCarryRows - 1) / kCarryRows)};
+            constexpr int kRowsPerWave = kCarryRows * kCarryGroups;
+            const CarriedCompress cc{d, nx, nx * ((c.batch + kRowsPerWave - 1) / kRowsPerWave)};
             const int blocks = (cc.waves + kCarryWaves - 1) / kCarryWaves;
             const int plane = (int)sg.x * c.batch;
             const dim3 cg(sg.x, (unsigned)c.batch, (unsigned)(1 + (blocks + plane - 1) / plane));
